@@ -1,0 +1,280 @@
+/*
+ * NVFP4 two-level microscaling -- CPU ORACLE (test infrastructure only).
+ *
+ * This file is the slow, plain reference that the HIP library is checked
+ * against.  Only the test suite, the smoke check and the CPU-baseline leg of
+ * the benchmark may load it; the product library never links or calls it, and
+ * the two share no code, headers, tables or constants.
+ *
+ * What it computes, and where the pages fix it:
+ *  - E2M1 element values +-{0, 0.5, 1, 1.5, 2, 3, 4, 6}: 1 sign, 2 exponent,
+ *    1 mantissa bit (axbrief.com, "NVFP4: how NVIDIA pre-trained a 12B model
+ *    on 10 trillion tokens", section "E2M1 format and two-level scaling";
+ *    iwan.kr, "NVIDIA shrank GLM-5.2 to 4 bits", section 3 "Terminology:
+ *    quantization and NVFP4", which counts 15 distinct values).
+ *  - 16-element blocks sharing one E4M3 scale, plus one FP32 scale per tensor
+ *    (same two sections; theddari.com, "What is FP4 quantization? KV cache in
+ *    4 bits", format-comparison table).
+ *  - The tensor-level FP32 scale sets the overall range and the block scale
+ *    maps each block's amax close to the FP4 maximum (axbrief.com, section
+ *    "E2M1 format and two-level scaling").
+ * Where the pages are silent the recipe is the plainest reading:
+ *  g  = RN32(amax / (6*448))           (448 = E4M3 maximum, 6 = E2M1 maximum)
+ *  d6 = RN32(6*g)
+ *  s  = E4M3_RNE_SAT(RN32(block_amax / d6))     (0 when d6 == 0)
+ *  d  = RN32(s*g)
+ *  code = sign(x)<<3 | E2M1_RNE_SAT(RN32(|x| / d))   (signed zero when d == 0)
+ *  byte j of a row = code[2j] | code[2j+1] << 4
+ *  dequant: bf16_RNE(RN32((E2M1(code)*s) * g)), sign from code bit 3
+ * Every RN32 step is ONE IEEE-754 binary32 operation, round-to-nearest-even.
+ * Build with -O2 -ffp-contract=off, no fast-math, no FTZ/DAZ (x86-64 SSE
+ * float arithmetic is then exactly binary32 with one rounding per operation).
+ * Rounding onto the E2M1 and E4M3 grids is done by brute-force nearest search
+ * with ties to the even code -- the definition, not a shortcut.
+ * Inputs are required to be finite; non-finite inputs return an error.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* ---------- scalar formats ---------- */
+
+/* E2M1 magnitude for code bits 2..0 (exponent bias 1, one mantissa bit). */
+static const double kE2M1Mag[8] = {0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0};
+
+double orc_e2m1_value(int code) {
+  double m = kE2M1Mag[code & 7];
+  return (code & 8) ? -m : m;
+}
+
+/* Nearest E2M1 magnitude code for y >= 0, ties to the even code, saturating
+ * at 6 (the representable range ends at +-6; +inf from an overflowed quotient
+ * saturates too).  Returns -1 for NaN or negative input. */
+int orc_e2m1_encode(float y) {
+  if (!(y >= 0.0f)) return -1;
+  if (y > 6.0f) return 7;
+  int best = 0;
+  double bestd = fabs((double)y - kE2M1Mag[0]);
+  for (int k = 1; k < 8; ++k) {
+    double d = fabs((double)y - kE2M1Mag[k]);
+    if (d < bestd || (d == bestd && (k & 1) == 0)) { best = k; bestd = d; }
+  }
+  return best;
+}
+
+/* OCP E4M3FN value of a non-negative scale byte 0x00..0x7E:
+ * normal (1+m/8)*2^(e-7), subnormal m*2^-9; 0x7F (NaN) is never produced. */
+double orc_e4m3_value(int byte) {
+  int e = (byte >> 3) & 15, m = byte & 7;
+  if (e == 0) return ldexp((double)m, -9);
+  return ldexp(1.0 + m / 8.0, e - 7);
+}
+
+/* Nearest E4M3 byte for v >= 0, ties to the even mantissa, saturating at 448
+ * (+inf included).  Returns -1 for NaN or negative input. */
+int orc_e4m3_encode(float v) {
+  if (!(v >= 0.0f)) return -1;
+  if (v >= 448.0f) return 0x7E;
+  int best = 0;
+  double bestd = fabs((double)v);
+  for (int b = 1; b <= 0x7E; ++b) {
+    double d = fabs((double)v - orc_e4m3_value(b));
+    if (d < bestd || (d == bestd && (b & 1) == 0)) { best = b; bestd = d; }
+  }
+  return best;
+}
+
+float orc_bf16_to_f32(uint16_t h) {
+  uint32_t u = (uint32_t)h << 16;
+  float f;
+  memcpy(&f, &u, 4);
+  return f;
+}
+
+/* bf16 nearest to a finite f32, ties to even; overflow gives +-inf. */
+uint16_t orc_f32_to_bf16(float f) {
+  uint32_t u;
+  memcpy(&u, &f, 4);
+  uint16_t lo = (uint16_t)(u >> 16);          /* toward zero */
+  if (((uint32_t)lo << 16) == u) return lo;   /* exact */
+  uint16_t hi = (uint16_t)(lo + 1);           /* next magnitude up */
+  double a = fabs((double)f);
+  double vlo = fabs((double)orc_bf16_to_f32(lo));
+  double vhi = ((hi & 0x7F80) == 0x7F80) ? ldexp(1.0, 128) : fabs((double)orc_bf16_to_f32(hi));
+  double dlo = a - vlo, dhi = vhi - a;
+  if (dlo < dhi) return lo;
+  if (dhi < dlo) return hi;
+  return (lo & 1) ? hi : lo;
+}
+
+static int bf16_is_finite(uint16_t h) { return (h & 0x7F80) != 0x7F80; }
+static float bf16_abs(uint16_t h) { return fabsf(orc_bf16_to_f32(h)); }
+
+/* ---------- the two-level scales ---------- */
+
+/* Step 1-2: tensor amax and the FP32 tensor scale g = RN32(amax / 2688). */
+float orc_global_scale(float amax) { return amax / 2688.0f; }
+
+/* Step 3-4: block scale byte from block amax and g. */
+int orc_block_scale(float bamax, float g) {
+  float d6 = 6.0f * g;
+  if (d6 == 0.0f) return 0;
+  return orc_e4m3_encode(bamax / d6);
+}
+
+/* Step 5-6: one element's 4-bit code given g and its block's scale byte. */
+int orc_encode_element(uint16_t x, float g, int sbyte) {
+  int sign = (x >> 15) & 1;
+  float s = (float)orc_e4m3_value(sbyte);
+  float d = s * g;
+  if (d == 0.0f) return sign << 3;
+  float y = bf16_abs(x) / d;
+  return (sign << 3) | orc_e2m1_encode(y);
+}
+
+/* Encode one row of `cols` values (cols % 16 == 0) with tensor scale g. */
+static void encode_row(const uint16_t* x, int64_t cols, float g, uint8_t* q, uint8_t* sf) {
+  for (int64_t b = 0; b < cols / 16; ++b) {
+    const uint16_t* xb = x + 16 * b;
+    float bamax = 0.0f;
+    for (int i = 0; i < 16; ++i) bamax = fmaxf(bamax, bf16_abs(xb[i]));
+    int sbyte = orc_block_scale(bamax, g);
+    sf[b] = (uint8_t)sbyte;
+    for (int i = 0; i < 16; i += 2) {
+      int c0 = orc_encode_element(xb[i], g, sbyte);
+      int c1 = orc_encode_element(xb[i + 1], g, sbyte);
+      q[8 * b + i / 2] = (uint8_t)(c0 | (c1 << 4));   /* element 2j in the low nibble */
+    }
+  }
+}
+
+static void set_threads(int nthreads) {
+#ifdef _OPENMP
+  if (nthreads > 0) omp_set_num_threads(nthreads);
+#else
+  (void)nthreads;
+#endif
+}
+
+int orc_max_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}
+
+/* Full quantize: x [batch][rows][cols] bf16 -> q [batch][rows][cols/2],
+ * sf [batch][rows][cols/16], g [batch].  Returns 0, or -1 on bad shape or a
+ * non-finite input. */
+int orc_quantize(const uint16_t* x, int64_t batch, int64_t rows, int64_t cols,
+                 uint8_t* q, uint8_t* sf, float* g, int nthreads) {
+  if (batch < 0 || rows < 0 || cols < 0 || cols % 16) return -1;
+  set_threads(nthreads);
+  const int64_t n = rows * cols;
+  for (int64_t t = 0; t < batch; ++t) {
+    const uint16_t* xt = x + t * n;
+    float amax = 0.0f;
+    int bad = 0;
+#pragma omp parallel for reduction(max : amax) reduction(| : bad)
+    for (int64_t i = 0; i < n; ++i) {
+      if (!bf16_is_finite(xt[i])) bad = 1;
+      amax = fmaxf(amax, bf16_abs(xt[i]));
+    }
+    if (bad) return -1;
+    float gt = orc_global_scale(amax);
+    g[t] = gt;
+#pragma omp parallel for
+    for (int64_t r = 0; r < rows; ++r)
+      encode_row(xt + r * cols, cols, gt, q + (t * rows + r) * (cols / 2), sf + (t * rows + r) * (cols / 16));
+  }
+  return 0;
+}
+
+/* Quantize with caller-supplied tensor scales g[batch] (no amax pass). */
+int orc_quantize_with_scale(const uint16_t* x, int64_t batch, int64_t rows, int64_t cols,
+                            const float* g, uint8_t* q, uint8_t* sf, int nthreads) {
+  if (batch < 0 || rows < 0 || cols < 0 || cols % 16) return -1;
+  set_threads(nthreads);
+  const int64_t n = rows * cols;
+  for (int64_t t = 0; t < batch; ++t) {
+    if (!(g[t] >= 0.0f) || isinf(g[t])) return -1;
+    int bad = 0;
+#pragma omp parallel for reduction(| : bad)
+    for (int64_t i = 0; i < n; ++i)
+      if (!bf16_is_finite(x[t * n + i])) bad = 1;
+    if (bad) return -1;
+#pragma omp parallel for
+    for (int64_t r = 0; r < rows; ++r)
+      encode_row(x + t * n + r * cols, cols, g[t], q + (t * rows + r) * (cols / 2), sf + (t * rows + r) * (cols / 16));
+  }
+  return 0;
+}
+
+/* One element's decoded fp32 value: RN32((E2M1(code) * s) * g). */
+float orc_decode_element(int code, int sbyte, float g) {
+  float m = (float)kE2M1Mag[code & 7];
+  float s = (float)orc_e4m3_value(sbyte);
+  float v = (m * s) * g;      /* m*s is exact in fp32; one rounding for *g */
+  return (code & 8) ? -v : v;
+}
+
+/* Dequantize to bf16: y [batch][rows][cols]. */
+int orc_dequantize(const uint8_t* q, const uint8_t* sf, const float* g, int64_t batch, int64_t rows,
+                   int64_t cols, uint16_t* y, int nthreads) {
+  if (batch < 0 || rows < 0 || cols < 0 || cols % 16) return -1;
+  set_threads(nthreads);
+  for (int64_t t = 0; t < batch; ++t) {
+    const float gt = g[t];
+#pragma omp parallel for
+    for (int64_t r = 0; r < rows; ++r) {
+      const int64_t row = t * rows + r;
+      for (int64_t c = 0; c < cols; ++c) {
+        int byte = q[row * (cols / 2) + c / 2];
+        int code = (c & 1) ? (byte >> 4) : (byte & 15);
+        int sbyte = sf[row * (cols / 16) + c / 16];
+        y[row * cols + c] = orc_f32_to_bf16(orc_decode_element(code, sbyte, gt));
+      }
+    }
+  }
+  return 0;
+}
+
+/* Exact fp64 value E2M1(code) * s of every element, WITHOUT the tensor
+ * scale (the GEMM and decode-QK references apply g separately in fp64). */
+int orc_dequantize_f64_unscaled(const uint8_t* q, const uint8_t* sf, int64_t rows, int64_t cols,
+                                double* y, int nthreads) {
+  if (rows < 0 || cols < 0 || cols % 16) return -1;
+  set_threads(nthreads);
+#pragma omp parallel for
+  for (int64_t r = 0; r < rows; ++r)
+    for (int64_t c = 0; c < cols; ++c) {
+      int byte = q[r * (cols / 2) + c / 2];
+      int code = (c & 1) ? (byte >> 4) : (byte & 15);
+      y[r * cols + c] = orc_e2m1_value(code) * orc_e4m3_value(sf[r * (cols / 16) + c / 16]);
+    }
+  return 0;
+}
+
+/* Array helpers for the exhaustive self-tests. */
+void orc_e2m1_encode_array(const float* y, int64_t n, int8_t* out, int nthreads) {
+  set_threads(nthreads);
+#pragma omp parallel for
+  for (int64_t i = 0; i < n; ++i) out[i] = (int8_t)orc_e2m1_encode(y[i]);
+}
+
+void orc_e4m3_encode_array(const float* v, int64_t n, int16_t* out, int nthreads) {
+  set_threads(nthreads);
+#pragma omp parallel for
+  for (int64_t i = 0; i < n; ++i) out[i] = (int16_t)orc_e4m3_encode(v[i]);
+}
+
+void orc_f32_to_bf16_array(const float* f, int64_t n, uint16_t* out, int nthreads) {
+  set_threads(nthreads);
+#pragma omp parallel for
+  for (int64_t i = 0; i < n; ++i) out[i] = orc_f32_to_bf16(f[i]);
+}

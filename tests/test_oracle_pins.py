@@ -1,0 +1,504 @@
+"""Pins of the CPU oracle against what the pages and mathematics fix.
+
+Nothing here compares the oracle with itself: each check uses an independent
+formulation (closed-form threshold tables, numpy/torch library rounding,
+exact rational arithmetic, brute force on tiny inputs) or a number printed on
+the pages (tests/golden/*.json, each with its citation).
+"""
+import json
+import os
+from fractions import Fraction as F
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import exact
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def gold(name):
+    with open(os.path.join(GOLD, name)) as f:
+        return json.load(f)
+
+
+def bf16_bits(values):
+    t = torch.tensor(values, dtype=torch.float32).to(torch.bfloat16)
+    return t.view(torch.int16).numpy().view(np.uint16)
+
+
+def bits_to_f32(b):
+    return (np.asarray(b, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+# ------------------------------------------------------------------ E2M1 grid
+def test_e2m1_value_set_matches_pages():
+    gd = gold("e2m1_grid.json")
+    vals = [oracle.e2m1_value(c) for c in range(16)]
+    mags = sorted({abs(v) for v in vals})
+    assert mags == gd["magnitudes"]
+    assert sorted(v for v in vals if v > 0) == [m for m in gd["magnitudes"] if m > 0]
+    assert sorted(-v for v in vals if v < 0) == [m for m in gd["magnitudes"] if m > 0]
+    # 16 codes, +0 and -0 coincide as values: 15 distinct values
+    assert len(set(vals)) == gd["distinct_values"]
+    assert max(abs(v) for v in vals) == gd["max_magnitude"]
+    # S1E2M1 layout: sign is bit 3; code 8 is -0
+    assert np.signbit(oracle.e2m1_value(8)) and oracle.e2m1_value(8) == 0.0
+    for c in range(8):
+        e, m = c >> 1, c & 1
+        expect = m * 0.5 if e == 0 else (1 + m / 2) * 2.0 ** (e - 1)   # bias 1, 1 mantissa bit
+        assert oracle.e2m1_value(c) == expect
+
+
+def _e2m1_by_thresholds(y: np.ndarray) -> np.ndarray:
+    """RNE onto {0,.5,1,1.5,2,3,4,6} written as a threshold table: a midpoint
+    between two grid values goes to the neighbour whose code is even."""
+    k = np.zeros(y.shape, dtype=np.int8)
+    k += y > 0.25      # 0.25: midpoint of 0 (code 0) and 0.5 (code 1) -> 0
+    k += y >= 0.75     # 0.75: 0.5 (1) | 1 (2) -> 2
+    k += y > 1.25      # 1.25: 1 (2) | 1.5 (3) -> 2
+    k += y >= 1.75     # 1.75: 1.5 (3) | 2 (4) -> 4
+    k += y > 2.5       # 2.5: 2 (4) | 3 (5) -> 4
+    k += y >= 3.5      # 3.5: 3 (5) | 4 (6) -> 6
+    k += y > 5.0       # 5: 4 (6) | 6 (7) -> 6; above 6 saturates at 7
+    return k
+
+
+def test_e2m1_encode_exhaustive_up_to_8():
+    """Every non-negative float32 in [0, 8], then a sample of larger ones."""
+    hi = np.uint32(0x41000000)  # 8.0
+    step = 1 << 24
+    for start in range(0, int(hi) + 1, step):
+        bits = np.arange(start, min(start + step, int(hi) + 1), dtype=np.uint32)
+        y = bits.view(np.float32)
+        got = oracle.e2m1_encode_array(y)
+        want = _e2m1_by_thresholds(y)
+        bad = np.nonzero(got != want)[0]
+        assert bad.size == 0, f"first mismatch at y={y[bad[0]]!r}: {got[bad[0]]} vs {want[bad[0]]}"
+    rng = np.random.default_rng(1)
+    big = rng.integers(0x41000001, 0x7F800000, size=1 << 20, dtype=np.uint32).view(np.float32)
+    assert np.all(oracle.e2m1_encode_array(big) == 7)
+
+
+# ------------------------------------------------------------------ E4M3
+def _e4m3_closed_form(v: np.ndarray) -> np.ndarray:
+    """OCP E4M3FN (bias 7, max 448), RNE via np.rint on exactly scaled values."""
+    v = v.astype(np.float64)
+    out = np.zeros(v.shape, dtype=np.int16)
+    sub = v < 2.0 ** -6
+    out[sub] = np.rint(v[sub] * 512.0).astype(np.int16)       # m * 2^-9, m = 0..8 (8 == 2^-6 == 0x08)
+    nrm = ~sub
+    fr, e = np.frexp(v[nrm])                                  # v = fr * 2^e, fr in [0.5, 1)
+    m = np.rint(fr * 16.0).astype(np.int64)                   # 8..16
+    e = e.astype(np.int64) - 1 + (m == 16)
+    m = np.where(m == 16, 8, m)
+    code = ((e + 7) << 3) | (m - 8)
+    out[nrm] = np.minimum(code, 0x7E).astype(np.int16)        # saturate at 448
+    return out
+
+
+def test_e4m3_value_table():
+    vals = [oracle.e4m3_value(b) for b in range(0x7F)]
+    assert vals[0x7E] == 448.0 and vals[1] == 2.0 ** -9 and vals[8] == 2.0 ** -6
+    assert all(a < b for a, b in zip(vals, vals[1:]))          # strictly increasing, no NaN used
+
+
+def test_e4m3_encode_dense():
+    rng = np.random.default_rng(2)
+    # strided sweep over all floats in [0, 1024] plus dense windows around every
+    # grid value and every midpoint between neighbours
+    sweep = np.arange(0, 0x44800000, 97, dtype=np.uint32).view(np.float32)
+    grid = np.array([oracle.e4m3_value(b) for b in range(0x7F)], dtype=np.float64)
+    mids = (grid[:-1] + grid[1:]) / 2
+    pts = np.concatenate([grid, mids, [448.0, 464.0, 480.0, 2.0 ** -10]]).astype(np.float32)
+    win = (pts.view(np.uint32)[:, None].astype(np.int64) + np.arange(-300, 301)[None, :]).clip(0, 0x7F7FFFFF)
+    dense = win.astype(np.uint32).ravel().view(np.float32)
+    rnd = rng.uniform(0, 600, size=1 << 20).astype(np.float32)
+    for v in (sweep, dense, rnd):
+        got = oracle.e4m3_encode_array(v)
+        want = _e4m3_closed_form(v)
+        bad = np.nonzero(got != want)[0]
+        assert bad.size == 0, f"v={v[bad[0]]!r}: {got[bad[0]]:#x} vs {want[bad[0]]:#x}"
+
+
+def test_e4m3_documented_examples():
+    assert oracle.e4m3_encode(1.0625) == 0x38      # tie 1 | 1.125 -> even mantissa 1.0
+    assert oracle.e4m3_encode(1.1875) == 0x3A      # tie 1.125 | 1.25 -> 1.25
+    assert oracle.e4m3_encode(464.0) == 0x7E       # saturates at 448
+    assert oracle.e4m3_encode(2.0 ** -10) == 0     # tie 0 | 2^-9 -> 0
+    assert oracle.e4m3_encode(1.5 * 2.0 ** -10) == 1
+
+
+# ------------------------------------------------------------------ bf16 RNE
+def test_f32_to_bf16_matches_torch():
+    hi = np.arange(0, 0x10000, 131, dtype=np.uint32)
+    hi = hi[(hi & 0x7F80) != 0x7F80]
+    hi = np.unique(np.concatenate([hi, [0x3F80, 0x0000, 0x8000, 0x0001, 0x7F7F, 0xFF7F & 0xFFFF]]))
+    bits = (hi[:, None] << 16 | np.arange(0x10000, dtype=np.uint32)[None, :]).ravel()
+    f = bits.view(np.float32)
+    got = oracle.f32_to_bf16_array(f)
+    want = torch.from_numpy(f.copy()).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    bad = np.nonzero(got != want)[0]
+    assert bad.size == 0, f"f={f[bad[0]]!r}: {got[bad[0]]:#x} vs {want[bad[0]]:#x}"
+
+
+# ------------------------------------------------------------------ storage
+def test_storage_is_0p5625_bytes_per_value():
+    gs = gold("storage.json")
+    x = bf16_bits(np.random.default_rng(3).standard_normal((8, 64)))
+    q, sf, g = oracle.quantize(x)
+    n = x.size
+    assert q.nbytes + sf.nbytes == gs["bytes_per_value"] * n
+    assert 8 * (q.nbytes + sf.nbytes) / n == gs["bits_per_value"]
+    assert 16 / gs["bits_per_value"] == pytest.approx(gs["ratio_vs_fp16_about"], abs=0.1)
+    assert 8 / gs["bits_per_value"] == pytest.approx(gs["ratio_vs_fp8_about"], abs=0.05)
+    assert g.nbytes == 4          # one FP32 scale per tensor
+
+
+def test_kv_size_worked_example():
+    gk = gold("kv_size_example.json")
+    L, H, D, T = gk["layers"], gk["kv_heads"], gk["head_dim"], gk["context_tokens"]
+    assert 2 * L * H * D == gk["values_per_token"]
+    # encode one token of K and one of V through the oracle and count bytes
+    rng = np.random.default_rng(4)
+    k = bf16_bits(rng.standard_normal((L, 1, H, D)))
+    v = bf16_bits(rng.standard_normal((L, 1, H, D)))
+    gl = np.full((L, H), 0.01, dtype=np.float32)
+    kq, ksf = oracle.kv_encode(k, gl)
+    vq, vsf = oracle.kv_encode(v, gl)
+    per_token = kq.nbytes + ksf.nbytes + vq.nbytes + vsf.nbytes
+    assert per_token == gk["rows"]["nvfp4"]["per_token_KiB"] * 1024
+    assert per_token * T == gk["rows"]["nvfp4"]["per_context_GiB"] * 2 ** 30
+    for fmt in ("bf16", "fp8"):
+        row = gk["rows"][fmt]
+        assert gk["values_per_token"] * row["bytes_per_value"] == row["per_token_KiB"] * 1024
+        assert gk["values_per_token"] * row["bytes_per_value"] * T == row["per_context_GiB"] * 2 ** 30
+
+
+# ------------------------------------------------------------------ crafted tensors
+def _tensor_with_g1(blocks):
+    """Row of 16-value blocks; the last block holds 2688 so amax = 6*448 -> g = 1."""
+    row = [v for b in blocks for v in b] + [2688.0] + [0.0] * 15
+    return bf16_bits([row])
+
+
+@pytest.mark.parametrize("j", [-9, -3, 0, 2, 6])
+def test_e2m1_ties_go_to_even_code(j):
+    grid = gold("e2m1_grid.json")["magnitudes"]
+    mids = [(a + b) / 2 for a, b in zip(grid, grid[1:])]          # 0.25 .. 5
+    blk = [6.0 * 2 ** j] + [m * 2 ** j for m in mids] + [-m * 2 ** j for m in mids] + [-0.0]
+    assert len(blk) == 16
+    x = _tensor_with_g1([blk])
+    q, sf, g = oracle.quantize(x)
+    assert g[0] == 1.0
+    assert sf[0, 0] == oracle.e4m3_encode(2.0 ** j) and oracle.e4m3_value(sf[0, 0]) == 2.0 ** j
+    codes = np.stack([q[0] & 15, q[0] >> 4], axis=1).ravel()[:16]
+    even = [k if k % 2 == 0 else k + 1 for k in range(7)]        # midpoint k|k+1 -> even code
+    assert codes[0] == 7
+    assert list(codes[1:8]) == even
+    assert list(codes[8:15]) == [8 | c for c in even]
+    assert codes[15] == 8                                        # -0 keeps its sign
+    assert sf[0, 1] == 0x7E                                      # amax block: s = 448
+
+
+def test_e4m3_tie_in_block_scale():
+    x = _tensor_with_g1([[6.375] + [0.0] * 15])                  # 6.375 / 6 = 1.0625: tie -> 1.0
+    q, sf, g = oracle.quantize(x)
+    assert g[0] == 1.0 and sf[0, 0] == 0x38
+    assert (q[0, 0] & 15) == 7                                   # 6.375 / 1 saturates to 6
+
+
+def test_nibble_order_low_first():
+    x = _tensor_with_g1([[6.0, 0.5, 1.0, -1.5] + [0.0] * 12])
+    q, sf, g = oracle.quantize(x)
+    assert sf[0, 0] == 0x38                                      # s = 1
+    assert q[0, 0] == (7 | (1 << 4)) and q[0, 1] == (2 | (11 << 4))
+
+
+def test_all_zero_and_signed_zero():
+    x = bf16_bits([[0.0, -0.0] * 16])
+    q, sf, g = oracle.quantize(x)
+    assert g[0] == 0.0 and np.all(sf == 0)
+    assert np.all(q == 0x80)
+    y = oracle.dequantize(q, sf, g)
+    assert np.all(y == np.array([0x0000, 0x8000] * 16, dtype=np.uint16))
+
+
+def test_global_amax_element():
+    rng = np.random.default_rng(5)
+    for scale in (1e-3, 1.0, 37.0, 3e4):
+        x = bf16_bits(rng.standard_normal((16, 64)) * scale)
+        q, sf, g = oracle.quantize(x)
+        xf = bits_to_f32(x)
+        amax = np.abs(xf).max()
+        r, c = np.unravel_index(np.abs(xf).argmax(), xf.shape)
+        assert sf[r, c // 16] == 0x7E
+        code = (q[r, c // 2] >> (4 * (c % 2))) & 15
+        assert code & 7 == 7
+        back = oracle.f32_to_bf16_array(np.array([np.float32(2688.0) * g[0]], dtype=np.float32))
+        assert bits_to_f32(back)[0] == amax
+
+
+def test_block_amax_keeps_fp8_precision():
+    """The block max is carried by an E4M3 scale: in every normal-scale block the
+    largest element gets the top E2M1 code and 6*s*g is within 2^-4 of bamax
+    (axbrief.com, 'E2M1 format and two-level scaling': the block amax is kept at
+    FP8 precision; one of the 16 values)."""
+    rng = np.random.default_rng(6)
+    checked = 0
+    for dist in ("normal", "t3", "outlier"):
+        z = rng.standard_normal((64, 256))
+        if dist == "t3":
+            z = z / np.sqrt(rng.chisquare(3, z.shape) / 3)
+        if dist == "outlier":
+            z = z * 0.02 * np.where(rng.random(z.shape) < 0.01, 50, 1)
+        x = bf16_bits(z)
+        q, sf, g = oracle.quantize(x)
+        xf = np.abs(bits_to_f32(x)).reshape(64, -1, 16)
+        codes = np.stack([q & 15, q >> 4], axis=-1).reshape(64, -1, 16) & 7
+        for r in range(64):
+            for b in range(xf.shape[1]):
+                if sf[r, b] >= 0x08:                       # normal E4M3 scale
+                    assert codes[r, b].max() == 7
+                    deq_max = 6 * oracle.e4m3_value(sf[r, b]) * float(g[0])
+                    assert abs(deq_max - xf[r, b].max()) <= 2 ** -4 * xf[r, b].max() * 1.0001
+                    checked += 1
+    assert checked > 3000
+
+
+def test_idempotence_on_normal_scale_blocks():
+    rng = np.random.default_rng(7)
+    for scale in (1e-30, 1e-4, 1.0, 1e3, 1e30):
+        x = bf16_bits(rng.standard_normal((32, 128)) * scale)
+        q, sf, g = oracle.quantize(x)
+        y = oracle.dequantize(q, sf, g)
+        q2, sf2, g2 = oracle.quantize(y)
+        assert g2[0] == g[0]
+        ok = sf >= 0x08
+        assert ok.mean() > 0.99
+        assert np.array_equal(sf2[ok], sf[ok])
+        qb = np.repeat(ok, 8, axis=1)
+        assert np.array_equal(q2[qb], q[qb])
+
+
+def test_subnormal_scale_exception_is_real():
+    """Known exception to idempotence: a block whose E4M3 scale is subnormal and
+    whose largest code is below 6 re-quantizes to a different scale."""
+    bamax = 6 * 1.6 * 2.0 ** -9
+    x = _tensor_with_g1([[bamax] + [0.0] * 15])
+    q, sf, g = oracle.quantize(x)
+    # bamax/6 = 1.6*2^-9 rounds on the subnormal E4M3 grid to 2*2^-9 (byte 2);
+    # the element then sits at 6*1.6/2 = 4.8 -> code 6 (value 4), not the top code
+    assert sf[0, 0] == 2 and (q[0, 0] & 7) == 6
+    y = oracle.dequantize(q, sf, g)
+    q2, sf2, _ = oracle.quantize(y)
+    assert sf2[0, 0] != sf[0, 0]
+
+
+# ------------------------------------------------------------------ exact rationals
+def _rand_tensor(rng, rows, cols):
+    mode = rng.integers(0, 5)
+    if mode == 0:
+        z = rng.standard_normal((rows, cols))
+    elif mode == 1:
+        z = rng.standard_normal((rows, cols)) * 10.0 ** rng.uniform(-40, 38)
+    elif mode == 2:
+        z = rng.standard_normal((rows, cols)) * np.where(rng.random((rows, cols)) < 0.1, 1e4, 1)
+    elif mode == 3:                                          # bf16 subnormals mixed in
+        z = rng.standard_normal((rows, cols)) * 2.0 ** -128
+    else:                                                    # wide dynamic range per block
+        z = rng.standard_normal((rows, cols)) * 2.0 ** rng.integers(-20, 20, (rows, cols))
+    return bf16_bits(np.clip(z, -3e38, 3e38))
+
+
+def test_quantize_matches_exact_rationals():
+    rng = np.random.default_rng(8)
+    for trial in range(40):
+        x = _rand_tensor(rng, 3, 32)
+        q, sf, g = oracle.quantize(x)
+        codes, scales, ge = exact.quantize_rows(x.tolist())
+        assert F(float(g[0])) == ge
+        assert sf.tolist() == scales
+        qc = np.stack([q & 15, q >> 4], axis=-1).reshape(3, 32)
+        assert qc.tolist() == codes, f"trial {trial}"
+
+
+def test_quantize_with_scale_matches_exact_rationals():
+    rng = np.random.default_rng(9)
+    for trial in range(30):
+        x = _rand_tensor(rng, 2, 32)
+        gval = np.float32(abs(rng.standard_normal()) * 10.0 ** rng.uniform(-8, 3))
+        q, sf = oracle.quantize_with_scale(x[None], np.array([gval]))
+        codes, scales, _ = exact.quantize_rows(x.tolist(), g=F(float(gval)))
+        assert sf[0].tolist() == scales
+        assert np.stack([q[0] & 15, q[0] >> 4], -1).reshape(2, 32).tolist() == codes
+
+
+def _division_sensitive_cases(rng, n=2000):
+    """(x, d) pairs where RN32(x/d) and RN32(x * RN32(1/d)) land in different E2M1
+    cells -- an oracle that used a reciprocal instead of a division would fail."""
+    out = []
+    while len(out) < 8:
+        d = rng.uniform(0.5, 1.0, n).astype(np.float32)
+        for b in (0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0):
+            x = (np.float32(b) * d).astype(np.float32)
+            xb = bf16_bits(x)
+            xf = bits_to_f32(xb)
+            y_div = (xf / d).astype(np.float32)
+            y_rcp = (xf * (np.float32(1) / d).astype(np.float32)).astype(np.float32)
+            diff = _e2m1_by_thresholds(y_div) != _e2m1_by_thresholds(y_rcp)
+            for i in np.nonzero(diff)[0][:2]:
+                out.append((xb[i], float(d[i])))
+    return out
+
+
+def test_element_division_sensitive_cases():
+    rng = np.random.default_rng(10)
+    cases = _division_sensitive_cases(rng)
+    checked = 0
+    for xb, d in cases:
+        # quantize_with_scale with g = d and a block scale of exactly 1 (bamax = 6 d)
+        sixd = bf16_bits([6.0 * d])[0]
+        row = np.array([[sixd] + [xb] + [0] * 14], dtype=np.uint16)
+        gval = np.float32(d)
+        if oracle.block_scale(bits_to_f32([sixd])[0], gval) != 0x38:
+            continue
+        q, sf = oracle.quantize_with_scale(row[None], np.array([gval]))
+        codes, scales, _ = exact.quantize_rows(row.tolist(), g=F(float(gval)))
+        assert (q[0, 0, 0] >> 4) == codes[0][1]
+        checked += 1
+    assert checked >= 4
+
+
+def test_dequant_matches_fp64_product_and_exact():
+    rng = np.random.default_rng(11)
+    codes = rng.integers(0, 16, size=4096)
+    sbytes = rng.integers(0, 0x7F, size=4096)
+    gs = (np.abs(rng.standard_normal(4096)) * 10.0 ** rng.uniform(-30, 30, 4096)).astype(np.float32)
+    lut = np.array([oracle.e2m1_value(c) for c in range(16)])
+    sv = np.array([oracle.e4m3_value(b) for b in range(0x7F)])
+    exact64 = lut[codes] * sv[sbytes] * gs.astype(np.float64)       # exact: <= 30 significant bits
+    f32 = exact64.astype(np.float32)                                # one RNE rounding
+    for i in range(4096):
+        got = oracle.decode_element(int(codes[i]), int(sbytes[i]), float(gs[i]))
+        assert np.float32(got) == f32[i] or (got == 0 and f32[i] == 0)
+        if i < 300:
+            assert F(got) == exact.dequant_value(int(codes[i]), int(sbytes[i]), F(float(gs[i])))
+    # full tensor path: bf16 output equals torch's RNE of the same fp32 values
+    x = bf16_bits(rng.standard_normal((64, 128)) * 3)
+    q, sf, g = oracle.quantize(x)
+    y = oracle.dequantize(q, sf, g)
+    d64 = oracle.dequantize_f64_unscaled(q, sf) * float(g[0])
+    want = torch.from_numpy(d64.astype(np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(y, want)
+
+
+# ------------------------------------------------------------------ contractions
+def _exact_deq(q, sf, r, k):
+    code = (int(q[r, k // 2]) >> (4 * (k % 2))) & 15
+    return exact.E2M1[code & 7] * (-1 if code & 8 else 1) * exact.E4M3[int(sf[r, k // 16])]
+
+
+def test_gemm_f64_against_exact_triple_loop():
+    rng = np.random.default_rng(12)
+    M, N, K = 3, 4, 48
+    a = bf16_bits(rng.standard_normal((M, K)))
+    b = bf16_bits(rng.standard_normal((N, K)) * 5)
+    aq, asf, ag = oracle.quantize(a)
+    bq, bsf, bg = oracle.quantize(b)
+    C = oracle.gemm_f64(aq, asf, ag[0], bq, bsf, bg[0])
+    for m in range(M):
+        for n in range(N):
+            s = sum(_exact_deq(aq, asf, m, k) * _exact_deq(bq, bsf, n, k) for k in range(K))
+            want = F(float(ag[0])) * F(float(bg[0])) * s
+            assert abs(F(C[m, n]) - want) <= abs(want) * F(1, 2 ** 48) + F(1, 2 ** 1000)
+    # not symmetric in its operands: swapping A and B transposes C
+    Ct = oracle.gemm_f64(bq, bsf, bg[0], aq, asf, ag[0])
+    assert np.allclose(Ct, C.T, rtol=1e-15)
+
+
+def test_decode_qk_against_exact_sums():
+    rng = np.random.default_rng(13)
+    L, H, Hq, n, D = 2, 2, 8, 3, 32
+    k = bf16_bits(rng.standard_normal((L, n, H, D)))
+    qv = bf16_bits(rng.standard_normal((L, Hq, D)))
+    kg = np.array([[0.002, 0.0017], [0.0021, 0.001]], dtype=np.float32)
+    kq, ksf = oracle.kv_encode(k, kg)
+    logits = oracle.decode_qk_f64(qv, kq, ksf, kg)
+    for l in range(L):
+        for hq in range(Hq):
+            h = hq // (Hq // H)                                   # GQA: Hq/H query heads per KV head
+            for t in range(n):
+                s = F(0)
+                for d in range(D):
+                    s += exact.bf16_to_fraction(int(qv[l, hq, d])) * _exact_deq(kq[l, h], ksf[l, h], t, d)
+                want = s * F(float(kg[l, h]))
+                assert abs(F(logits[l, hq, t]) - want) <= abs(want) * F(1, 2 ** 45) + F(1, 2 ** 1000)
+
+
+def test_decode_qk_single_block_closed_form():
+    """head_dim 16: one block, logit = g * s * sum_d E2M1(code_d) * q_d."""
+    rng = np.random.default_rng(14)
+    k = bf16_bits(rng.standard_normal((1, 5, 1, 16)))
+    qv = bf16_bits(rng.standard_normal((1, 4, 16)))
+    kg = np.array([[0.0013]], dtype=np.float32)
+    kq, ksf = oracle.kv_encode(k, kg)
+    logits = oracle.decode_qk_f64(qv, kq, ksf, kg)
+    qf = bits_to_f32(qv).astype(np.float64)
+    for hq in range(4):
+        for t in range(5):
+            codes = [(int(kq[0, 0, t, j // 2]) >> (4 * (j % 2))) & 15 for j in range(16)]
+            dot = sum(oracle.e2m1_value(c) * qf[0, hq, j] for j, c in enumerate(codes))
+            want = float(kg[0, 0]) * oracle.e4m3_value(int(ksf[0, 0, t, 0])) * dot
+            assert logits[0, hq, t] == pytest.approx(want, rel=1e-14, abs=1e-300)
+
+
+def test_kv_encode_places_each_token_row():
+    rng = np.random.default_rng(15)
+    L, n, H, D = 3, 5, 2, 32
+    k = bf16_bits(rng.standard_normal((L, n, H, D)) * rng.uniform(0.1, 10, (L, n, H, 1)))
+    kg = (np.abs(rng.standard_normal((L, H))) * 0.01 + 1e-3).astype(np.float32)
+    kq, ksf = oracle.kv_encode(k, kg)
+    for l in range(L):
+        for h in range(H):
+            for t in range(n):
+                q1, s1 = oracle.quantize_with_scale(k[l, t, h][None, None], kg[l, h:h + 1])
+                assert np.array_equal(kq[l, h, t], q1[0, 0]) and np.array_equal(ksf[l, h, t], s1[0, 0])
+    back = oracle.kv_read(kq, ksf, kg)
+    assert back.shape == (L, H, n, D)
+    for l in range(L):
+        for h in range(H):
+            want = oracle.dequantize(kq[l, h][None], ksf[l, h][None], kg[l, h:h + 1])[0]
+            assert np.array_equal(back[l, h], want)
+
+
+def test_nonfinite_input_is_rejected():
+    x = bf16_bits([[1.0] * 15 + [float("inf")]])
+    with pytest.raises(ValueError):
+        oracle.quantize(x)
+
+
+def test_caller_scale_overflow_saturates():
+    """With a caller-supplied tensor scale the quotients can overflow binary32:
+    +inf saturates at the format maxima (448 for E4M3, 6 for E2M1); an infinite
+    d6 or d gives zero scales / signed-zero codes."""
+    x = bf16_bits([[3e38, -1.0] + [0.0] * 14])
+    q, sf = oracle.quantize_with_scale(x[None], np.array([1e-38], dtype=np.float32))
+    assert sf[0, 0, 0] == 0x7E
+    assert (q[0, 0, 0] & 15) == 7 and (q[0, 0, 0] >> 4) == 15
+    codes, scales, _ = exact.quantize_rows(x.tolist(), g=F(float(np.float32(1e-38))))
+    assert scales[0] == [0x7E] and codes[0][:2] == [7, 15]
+    q, sf = oracle.quantize_with_scale(x[None], np.array([3e38], dtype=np.float32))
+    assert sf[0, 0, 0] == 0 and q[0, 0, 0] == 0x80
+    codes, scales, _ = exact.quantize_rows(x.tolist(), g=F(float(np.float32(3e38))))
+    assert scales[0] == [0] and codes[0][:2] == [0, 8]
+
+
+def test_thread_count_does_not_change_results():
+    x = bf16_bits(np.random.default_rng(16).standard_normal((3, 64, 256)))
+    a = oracle.quantize(x, nthreads=1)
+    b = oracle.quantize(x, nthreads=0)
+    for u, v in zip(a, b):
+        assert np.array_equal(u, v)
