@@ -1,0 +1,181 @@
+/*
+ * libnvfp4 -- NVFP4 two-level microscaling on AMD Instinct MI355X (gfx950).
+ *
+ * NVFP4 stores each value as a 4-bit E2M1 float (1 sign, 2 exponent, 1
+ * mantissa bit: +-0, +-0.5, +-1, +-1.5, +-2, +-3, +-4, +-6); 16 consecutive
+ * values share one E4M3 block scale and the whole tensor has one FP32 scale,
+ * about 4.5 bits (0.5625 bytes) per value.  Sources: axbrief.com, "NVFP4: how
+ * NVIDIA pre-trained a 12B model on 10 trillion tokens", section "E2M1 format
+ * and two-level scaling"; iwan.kr, "NVIDIA shrank GLM-5.2 to 4 bits", section 3
+ * "Terminology: quantization and NVFP4"; theddari.com, "What is FP4
+ * quantization? KV cache in 4 bits", format-comparison table.
+ *
+ * Numeric recipe (the pages leave the formulas open; this is the plain
+ * reading that maps each block's amax onto the E2M1 maximum):
+ *   g  = RN32(amax / 2688)                 2688 = 6 (E2M1 max) * 448 (E4M3 max)
+ *   s  = E4M3_RNE_SAT(RN32(bamax / RN32(6 g)))            (0 when 6g == 0)
+ *   code = sign(x) << 3 | E2M1_RNE_SAT(RN32(|x| / RN32(s g)))
+ *          (a signed zero when s g == 0)
+ *   value = bf16_RNE(RN32((E2M1(code) * s) * g))
+ * RN32 is one IEEE binary32 rounding to nearest-even.  E4M3 is OCP E4M3FN
+ * (max 448, byte 0x7F never produced).  Ties on both grids go to the even
+ * code.  Results are bit-exact across every entry point and launch mode.
+ *
+ * Layouts (row-major, contiguous, no swizzle):
+ *   x  [batch][rows][cols] bf16 bit patterns (uint16_t), cols % 16 == 0
+ *   q  [batch][rows][cols/2] uint8, element 2j in the LOW nibble of byte j
+ *   sf [batch][rows][cols/16] uint8 E4M3 block-scale bytes
+ *   g  [batch] float, one tensor scale per batch item
+ *
+ * Conventions for every entry point:
+ *   - All tensor pointers are DEVICE pointers owned by the caller.  The
+ *     library never allocates, frees or synchronizes; every call enqueues
+ *     kernels on `stream` (a hipStream_t, NULL = the default stream) and
+ *     returns.  Device-side faults surface at the caller's next sync.
+ *   - Arguments are validated on the host before any launch.  On an error
+ *     code nothing is launched and no output byte is written.
+ *   - Inputs must be finite (not checked on the device; non-finite inputs give
+ *     unspecified codes but never out-of-bounds accesses).
+ *   - Tensor base pointers must be 16-byte aligned (NVFP4_EALIGN otherwise).
+ *   - Sizes are int64_t; negative sizes are NVFP4_EINVAL, zero sizes are a
+ *     successful no-op.
+ *   - Thread-safe; the only global state is a once-per-device architecture
+ *     check and a per-thread last-HIP-error slot.
+ */
+#ifndef NVFP4_H_
+#define NVFP4_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t nvfp4_status;
+
+enum {
+  NVFP4_OK = 0,
+  NVFP4_EINVAL = -1,     /* null pointer, bad dimension, cols % 16 != 0, range */
+  NVFP4_EALIGN = -2,     /* a tensor base pointer is not 16-byte aligned */
+  NVFP4_EWORKSPACE = -3, /* workspace missing or smaller than required */
+  NVFP4_ENOTSUP = -4,    /* current device is not gfx950, or unsupported flag */
+  NVFP4_EHIP = -5        /* a HIP runtime call failed; see nvfp4_last_hip_error */
+};
+
+/* Launch modes of nvfp4_quantize. */
+enum {
+  NVFP4_TWO_KERNEL = 0,  /* pass 1: per-tensor amax kernel; pass 2: encode kernel */
+  NVFP4_FUSED = 1        /* one persistent cooperative launch, amax then encode */
+};
+
+#define NVFP4_ABI_VERSION 1
+int32_t nvfp4_abi_version(void);
+
+/* Human-readable name of a status code (static storage, never NULL). */
+const char* nvfp4_status_string(nvfp4_status status);
+
+/* hipError_t of the last NVFP4_EHIP returned on the calling thread (0 if none). */
+int32_t nvfp4_last_hip_error(void);
+
+/* ------------------------------------------------------------------------
+ * Quantize: bf16 -> NVFP4 with the tensor scale computed from the tensor's
+ * own amax (activations; weights).  Two-level scaling of axbrief.com, "NVFP4:
+ * how NVIDIA pre-trained a 12B model on 10 trillion tokens", section "E2M1
+ * format and two-level scaling": the FP32 tensor scale sets the overall range
+ * and the E4M3 block scale maps each 16-value block's amax near the E2M1 max.
+ *
+ * x:  [batch][rows][cols] bf16 (read)     q:  [batch][rows][cols/2] (written)
+ * sf: [batch][rows][cols/16] (written)    g:  [batch] float (written)
+ * workspace: device scratch of at least nvfp4_quantize_workspace_bytes(...)
+ *   bytes, caller-owned.  It must be zero-filled once when allocated; the
+ *   library leaves it ready for the next call.  Calls that share one
+ *   workspace must be ordered on one stream.
+ * flags: NVFP4_TWO_KERNEL or NVFP4_FUSED (same bytes either way).
+ * Errors: EINVAL (null pointer with nonzero size, negative size, cols % 16),
+ *   EALIGN, EWORKSPACE, ENOTSUP (unknown flag / not gfx950), EHIP.
+ * ------------------------------------------------------------------------ */
+size_t nvfp4_quantize_workspace_bytes(int64_t batch, int64_t rows, int64_t cols);
+
+nvfp4_status nvfp4_quantize(const uint16_t* x, int64_t batch, int64_t rows, int64_t cols,
+                            uint8_t* q, uint8_t* sf, float* g,
+                            void* workspace, size_t workspace_bytes,
+                            uint32_t flags, void* stream);
+
+/* Quantize with caller-supplied tensor scales g[batch] (read, not written):
+ * a static or calibrated scale, no amax pass (theddari.com, "What is FP4
+ * quantization? KV cache in 4 bits", checklist item 2: KV scales come from
+ * calibration).  g must hold finite values >= 0. */
+nvfp4_status nvfp4_quantize_with_scale(const uint16_t* x, int64_t batch, int64_t rows, int64_t cols,
+                                       const float* g, uint8_t* q, uint8_t* sf, void* stream);
+
+/* Dequantize NVFP4 -> bf16: the runtime restores approximate values from the
+ * stored scales (omidsaffari.com, "LLM quantization guide", section "What is
+ * LLM quantization").  y: [batch][rows][cols] bf16 (written). */
+nvfp4_status nvfp4_dequantize(const uint8_t* q, const uint8_t* sf, const float* g,
+                              int64_t batch, int64_t rows, int64_t cols,
+                              uint16_t* y, void* stream);
+
+/* ------------------------------------------------------------------------
+ * NVFP4 KV cache (theddari.com, "What is FP4 quantization? KV cache in 4
+ * bits", sections "KV cache size example" and "how does 4-bit KV change
+ * inference cost": K and V are stored in NVFP4, 0.5625 bytes per value, and
+ * decoding re-reads the cache every step).  Each (layer, kv-head, token) K or
+ * V vector of head_dim values is one row of head_dim/16 blocks quantized with
+ * the (layer, head) tensor scale, which the caller fixes at cache creation.
+ * ------------------------------------------------------------------------ */
+typedef struct {
+  int32_t layers, kv_heads, head_dim;    /* head_dim % 16 == 0 */
+  int64_t capacity;                      /* maximum tokens */
+  uint8_t* k;                            /* [layers][kv_heads][capacity][head_dim/2]  */
+  uint8_t* v;                            /* [layers][kv_heads][capacity][head_dim/2]  */
+  uint8_t* k_sf;                         /* [layers][kv_heads][capacity][head_dim/16] */
+  uint8_t* v_sf;                         /* [layers][kv_heads][capacity][head_dim/16] */
+  const float* k_g;                      /* [layers][kv_heads] tensor scales (device) */
+  const float* v_g;                      /* [layers][kv_heads] tensor scales (device) */
+} nvfp4_kv_cache;
+
+/* Bytes of codes + block scales held by the cache:
+ * capacity * 2 * layers * kv_heads * head_dim * 0.5625 (tensor scales excluded).
+ * Returns 0 for an invalid descriptor. */
+size_t nvfp4_kv_bytes(const nvfp4_kv_cache* cache);
+
+/* Append n tokens at positions [start, start+n).  k_new, v_new:
+ * [layers][n][kv_heads][head_dim] bf16.  EINVAL if start < 0 or
+ * start + n > capacity.  The caller tracks the cache length. */
+nvfp4_status nvfp4_kv_append(const nvfp4_kv_cache* cache, int64_t start, int64_t n,
+                             const uint16_t* k_new, const uint16_t* v_new, void* stream);
+
+/* Dequantize tokens [t0, t0+n) of layers [layer0, layer0+nlayers) to bf16:
+ * k_out, v_out: [nlayers][kv_heads][n][head_dim] (either may be NULL to skip). */
+nvfp4_status nvfp4_kv_read(const nvfp4_kv_cache* cache, int32_t layer0, int32_t nlayers,
+                           int64_t t0, int64_t n, uint16_t* k_out, uint16_t* v_out, void* stream);
+
+/* One decode step's attention logits over the first n cached tokens:
+ * logits[l][hq][t] = sum_d q[l][hq][d] * Khat[l][hq / (q_heads/kv_heads)][t][d]
+ * (unscaled dot products, fp32 accumulation; Khat is the exact dequantized K).
+ * q: [layers][q_heads][head_dim] bf16; q_heads a multiple of kv_heads (GQA).
+ * logits: [layers][q_heads][n] float. */
+nvfp4_status nvfp4_kv_decode_qk(const nvfp4_kv_cache* cache, const uint16_t* q, int32_t q_heads,
+                                int64_t n, float* logits, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Block-scaled NVFP4 x NVFP4 GEMM for MoE expert linears, weights and
+ * activations both NVFP4 (iwan.kr, "NVIDIA shrank GLM-5.2 to 4 bits",
+ * section 1; FP4 GEMM speed, axbrief.com, section "36% token efficiency and
+ * Blackwell speed"):
+ *   C[m][n] = gA * gB * sum_k deq(A)[m][k] * deq(B)[n][k]        (TN, K-major)
+ * deq() = E2M1(code) * s, exact in bf16; fp32 accumulation; the tensor scales
+ * are applied once in the epilogue.  Both operands use the quantize layout:
+ * a_q [M][K/2], a_sf [M][K/16], b_q [N][K/2], b_sf [N][K/16]; a_g, b_g point
+ * to one float each (device).  c: [M][N] float.  K % 16 == 0.
+ * ------------------------------------------------------------------------ */
+nvfp4_status nvfp4_gemm(const uint8_t* a_q, const uint8_t* a_sf, const float* a_g,
+                        const uint8_t* b_q, const uint8_t* b_sf, const float* b_g,
+                        int64_t M, int64_t N, int64_t K, float* c, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NVFP4_H_ */

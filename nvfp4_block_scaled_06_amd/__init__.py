@@ -1,0 +1,238 @@
+"""Python binding for libnvfp4, the gfx950 NVFP4 two-level microscaling library.
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of libnvfp4.so (built in-tree by __graft_entry__.build()).  PyTorch
+provides device memory and the current HIP stream.  There is no CPU path:
+if the library is missing or the device is not gfx950, calls raise.
+
+Function names mirror the C-ABI in include/nvfp4.h.
+"""
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libnvfp4.so")
+
+TWO_KERNEL = 0
+FUSED = 1
+_FLAGS = {"two_kernel": TWO_KERNEL, "fused": FUSED, TWO_KERNEL: TWO_KERNEL, FUSED: FUSED}
+
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+_I32 = ctypes.c_int32
+_SZ = ctypes.c_size_t
+
+
+class NVFP4Error(RuntimeError):
+    def __init__(self, fn, status):
+        msg = _lib().nvfp4_status_string(status).decode()
+        if status == -5:
+            msg += f" (hipError {_lib().nvfp4_last_hip_error()})"
+        super().__init__(f"{fn}: {msg}")
+        self.status = status
+
+
+class KVCacheDesc(ctypes.Structure):
+    """Mirror of the C struct nvfp4_kv_cache."""
+    _fields_ = [
+        ("layers", _I32), ("kv_heads", _I32), ("head_dim", _I32),
+        ("capacity", _I64),
+        ("k", _P), ("v", _P), ("k_sf", _P), ("v_sf", _P),
+        ("k_g", _P), ("v_g", _P),
+    ]
+
+
+_SIGS = {
+    "nvfp4_abi_version": (_I32, []),
+    "nvfp4_status_string": (ctypes.c_char_p, [_I32]),
+    "nvfp4_last_hip_error": (_I32, []),
+    "nvfp4_quantize_workspace_bytes": (_SZ, [_I64, _I64, _I64]),
+    "nvfp4_quantize": (_I32, [_P, _I64, _I64, _I64, _P, _P, _P, _P, _SZ, ctypes.c_uint32, _P]),
+    "nvfp4_quantize_with_scale": (_I32, [_P, _I64, _I64, _I64, _P, _P, _P, _P]),
+    "nvfp4_dequantize": (_I32, [_P, _P, _P, _I64, _I64, _I64, _P, _P]),
+    "nvfp4_kv_bytes": (_SZ, [ctypes.POINTER(KVCacheDesc)]),
+    "nvfp4_kv_append": (_I32, [ctypes.POINTER(KVCacheDesc), _I64, _I64, _P, _P, _P]),
+    "nvfp4_kv_read": (_I32, [ctypes.POINTER(KVCacheDesc), _I32, _I32, _I64, _I64, _P, _P, _P]),
+    "nvfp4_kv_decode_qk": (_I32, [ctypes.POINTER(KVCacheDesc), _P, _I32, _I64, _P, _P]),
+    "nvfp4_gemm": (_I32, [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P, _P]),
+}
+
+_L = None
+
+
+def _lib():
+    global _L
+    if _L is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() (hipcc, gfx950)")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        _L = L
+    return _L
+
+
+def lib():
+    """The loaded ctypes library (raises if libnvfp4.so is not built)."""
+    return _lib()
+
+
+def _check(fn, status):
+    if status != 0:
+        raise NVFP4Error(fn, status)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _need(t, dtype, name):
+    if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+        raise ValueError(f"{name} must be a CUDA (HIP) tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _bits(t):
+    """bf16 tensors are passed as their uint16 bit patterns."""
+    return t
+
+
+# ---------------------------------------------------------------- codec
+def workspace_bytes(batch, rows, cols):
+    return int(_lib().nvfp4_quantize_workspace_bytes(batch, rows, cols))
+
+
+def make_workspace(batch, rows, cols, device="cuda"):
+    return torch.zeros(workspace_bytes(batch, rows, cols), dtype=torch.uint8, device=device)
+
+
+def _split(shape):
+    if len(shape) == 2:
+        return 1, shape[0], shape[1]
+    if len(shape) == 3:
+        return shape
+    raise ValueError("expected [rows, cols] or [batch, rows, cols]")
+
+
+def quantize(x, flags="two_kernel", workspace=None, out=None):
+    """x: bf16 [rows, cols] or [batch, rows, cols] -> (q uint8 [..., cols/2],
+    sf uint8 [..., cols/16], g float32 [batch])."""
+    _need(x, torch.bfloat16, "x")
+    b, r, c = _split(x.shape)
+    lead = tuple(x.shape[:-1])
+    if out is None:
+        q = torch.empty(lead + (c // 2,), dtype=torch.uint8, device=x.device)
+        sf = torch.empty(lead + (c // 16,), dtype=torch.uint8, device=x.device)
+        g = torch.empty((b,), dtype=torch.float32, device=x.device)
+    else:
+        q, sf, g = out
+    if workspace is None:
+        workspace = make_workspace(b, r, c, x.device)
+    _check("nvfp4_quantize", _lib().nvfp4_quantize(
+        _ptr(x), b, r, c, _ptr(q), _ptr(sf), _ptr(g), _ptr(workspace), workspace.numel(),
+        _FLAGS[flags], _stream(x.device)))
+    return q, sf, g
+
+
+def quantize_with_scale(x, g, out=None):
+    _need(x, torch.bfloat16, "x")
+    _need(g, torch.float32, "g")
+    b, r, c = _split(x.shape)
+    if g.numel() != b:
+        raise ValueError("g must hold one scale per batch item")
+    lead = tuple(x.shape[:-1])
+    if out is None:
+        q = torch.empty(lead + (c // 2,), dtype=torch.uint8, device=x.device)
+        sf = torch.empty(lead + (c // 16,), dtype=torch.uint8, device=x.device)
+    else:
+        q, sf = out
+    _check("nvfp4_quantize_with_scale", _lib().nvfp4_quantize_with_scale(
+        _ptr(x), b, r, c, _ptr(g), _ptr(q), _ptr(sf), _stream(x.device)))
+    return q, sf
+
+
+def dequantize(q, sf, g, out=None):
+    _need(q, torch.uint8, "q")
+    _need(sf, torch.uint8, "sf")
+    _need(g, torch.float32, "g")
+    c = q.shape[-1] * 2
+    b, r, _ = _split(tuple(q.shape[:-1]) + (c,))
+    y = out if out is not None else torch.empty(tuple(q.shape[:-1]) + (c,), dtype=torch.bfloat16, device=q.device)
+    _check("nvfp4_dequantize", _lib().nvfp4_dequantize(
+        _ptr(q), _ptr(sf), _ptr(g), b, r, c, _ptr(y), _stream(q.device)))
+    return y
+
+
+# ---------------------------------------------------------------- KV cache
+class KVCache:
+    """Caller-owned NVFP4 KV cache: K/V codes [L][H][capacity][D/2], block
+    scales [L][H][capacity][D/16] and fixed per-(layer, head) tensor scales."""
+
+    def __init__(self, layers, kv_heads, head_dim, capacity, k_g, v_g, device="cuda"):
+        self.layers, self.kv_heads, self.head_dim, self.capacity = layers, kv_heads, head_dim, capacity
+        shp = (layers, kv_heads, capacity)
+        self.k = torch.empty(shp + (head_dim // 2,), dtype=torch.uint8, device=device)
+        self.v = torch.empty_like(self.k)
+        self.k_sf = torch.empty(shp + (head_dim // 16,), dtype=torch.uint8, device=device)
+        self.v_sf = torch.empty_like(self.k_sf)
+        self.k_g = k_g.to(device=device, dtype=torch.float32).contiguous().reshape(layers, kv_heads)
+        self.v_g = v_g.to(device=device, dtype=torch.float32).contiguous().reshape(layers, kv_heads)
+        self.desc = KVCacheDesc(layers, kv_heads, head_dim, capacity,
+                                self.k.data_ptr(), self.v.data_ptr(), self.k_sf.data_ptr(),
+                                self.v_sf.data_ptr(), self.k_g.data_ptr(), self.v_g.data_ptr())
+
+    def nbytes(self):
+        return int(_lib().nvfp4_kv_bytes(ctypes.byref(self.desc)))
+
+    def append(self, start, k_new, v_new):
+        _need(k_new, torch.bfloat16, "k_new")
+        _need(v_new, torch.bfloat16, "v_new")
+        n = k_new.shape[1]
+        _check("nvfp4_kv_append", _lib().nvfp4_kv_append(
+            ctypes.byref(self.desc), start, n, _ptr(k_new), _ptr(v_new), _stream(k_new.device)))
+
+    def read(self, layer0, nlayers, t0, n, k_out=None, v_out=None, want_k=True, want_v=True):
+        shp = (nlayers, self.kv_heads, n, self.head_dim)
+        dev = self.k.device
+        if want_k and k_out is None:
+            k_out = torch.empty(shp, dtype=torch.bfloat16, device=dev)
+        if want_v and v_out is None:
+            v_out = torch.empty(shp, dtype=torch.bfloat16, device=dev)
+        _check("nvfp4_kv_read", _lib().nvfp4_kv_read(
+            ctypes.byref(self.desc), layer0, nlayers, t0, n, _ptr(k_out), _ptr(v_out), _stream(dev)))
+        return k_out, v_out
+
+    def decode_qk(self, q, n, out=None):
+        _need(q, torch.bfloat16, "q")
+        L, Hq, D = q.shape
+        logits = out if out is not None else torch.empty((L, Hq, n), dtype=torch.float32, device=q.device)
+        _check("nvfp4_kv_decode_qk", _lib().nvfp4_kv_decode_qk(
+            ctypes.byref(self.desc), _ptr(q), Hq, n, _ptr(logits), _stream(q.device)))
+        return logits
+
+
+# ---------------------------------------------------------------- GEMM
+def gemm(a_q, a_sf, a_g, b_q, b_sf, b_g, out=None):
+    """C[M][N] = gA*gB * sum_k deq(A)[m][k] deq(B)[n][k]; fp32 output."""
+    for t, n in ((a_q, "a_q"), (a_sf, "a_sf"), (b_q, "b_q"), (b_sf, "b_sf")):
+        _need(t, torch.uint8, n)
+    _need(a_g, torch.float32, "a_g")
+    _need(b_g, torch.float32, "b_g")
+    M, K2 = a_q.shape
+    N = b_q.shape[0]
+    c = out if out is not None else torch.empty((M, N), dtype=torch.float32, device=a_q.device)
+    _check("nvfp4_gemm", _lib().nvfp4_gemm(
+        _ptr(a_q), _ptr(a_sf), _ptr(a_g), _ptr(b_q), _ptr(b_sf), _ptr(b_g), M, N, 2 * K2, _ptr(c),
+        _stream(a_q.device)))
+    return c

@@ -1,0 +1,271 @@
+// NVFP4 KV cache: append (encode new K/V tokens into the cache layout), read
+// (dequantize a token range) and the decode-step QK sweep.
+//
+// The KV cache stores K and V in NVFP4 at 0.5625 bytes per value and decoding
+// re-reads it every step, so a smaller cache means fewer bytes per step
+// (theddari.com, "What is FP4 quantization? KV cache in 4 bits", sections "KV
+// cache size example" and "how does 4-bit KV change inference cost").
+//
+// Cache layout: codes [layers][kv_heads][capacity][head_dim/2], block scales
+// [layers][kv_heads][capacity][head_dim/16]; one (layer, head) owns a
+// contiguous run of tokens, so appends write and decode sweeps read long
+// contiguous stretches.  Each (layer, head) has its own fixed tensor scale
+// (k_g / v_g), so one workgroup serves one (layer, head, K|V) and builds that
+// scale's encode table once.
+#include <algorithm>
+
+#include "common.hpp"
+
+namespace nvfp4 {
+
+struct TensorScalesKV {
+  float g, d6, r6;
+  bool zero_all, exact_all;
+};
+
+__device__ __forceinline__ TensorScalesKV kv_scales(float g) {
+  TensorScalesKV ts;
+  ts.g = g;
+  ts.d6 = 6.0f * g;
+  ts.zero_all = ts.d6 == 0.0f;
+  ts.exact_all = !(ts.d6 >= 0x1p-125f && ts.d6 <= 0x1p125f);
+  ts.r6 = (ts.zero_all || ts.exact_all) ? 0.0f : 1.0f / ts.d6;
+  return ts;
+}
+
+// grid (tiles, kv_heads, 2*layers): z = 2*layer + (0: K, 1: V).
+__global__ void __launch_bounds__(kThreads) kv_append_kernel(nvfp4_kv_cache c, int64_t start, int64_t n,
+                                                             const u32x4* __restrict__ k_new,
+                                                             const u32x4* __restrict__ v_new) {
+  const int h = blockIdx.y;
+  const int l = blockIdx.z >> 1;
+  const bool is_v = blockIdx.z & 1;
+  const int H = c.kv_heads, D = c.head_dim, bpr = D / kBlock;
+  const float g = (is_v ? c.v_g : c.k_g)[l * H + h];
+  __shared__ Entry table[128];
+  for (uint32_t j = threadIdx.x; j < 127u; j += kThreads) table[j] = build_entry(j, g);
+  __syncthreads();
+  const TensorScalesKV ts = kv_scales(g);
+  const u32x4* src = is_v ? v_new : k_new;                     // [L][n][H][D] bf16, 2 x u32x4 per block
+  u32x2* dq = (u32x2*)(is_v ? c.v : c.k);                       // 8 bytes of codes per block
+  uint8_t* dsf = is_v ? c.v_sf : c.k_sf;
+  const int64_t row0 = ((int64_t)l * H + h) * c.capacity + start;   // cache row of token 0
+  const int64_t nblk = n * bpr;
+  for (int64_t b = (int64_t)blockIdx.x * kThreads + threadIdx.x; b < nblk; b += (int64_t)gridDim.x * kThreads) {
+    const int64_t t = b / bpr;
+    const int j = (int)(b - t * bpr);
+    const int64_t in_blk = (((int64_t)l * n + t) * H + h) * bpr + j;
+    uint32_t w[8];
+    const u32x4 a = src[2 * in_blk], bb = src[2 * in_blk + 1];
+    w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
+    w[4] = bb.x; w[5] = bb.y; w[6] = bb.z; w[7] = bb.w;
+    uint32_t am = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) am = pk_absmax(am, w[i]);
+    const uint32_t sbyte = block_scale_byte(halves_max(am), ts.d6, ts.r6, ts.exact_all, ts.zero_all);
+    uint32_t c0, c1;
+    encode_block(w, table[sbyte], sbyte, g, c0, c1);
+    const int64_t out_blk = (row0 + t) * bpr + j;
+    dq[out_blk] = u32x2{c0, c1};
+    dsf[out_blk] = (uint8_t)sbyte;
+  }
+}
+
+__device__ __forceinline__ uint32_t kv_dequant_pair(float2 f, float s, float g) {
+  const __bf16 ha = (__bf16)((f.x * s) * g), hb = (__bf16)((f.y * s) * g);
+  return (uint32_t)__builtin_bit_cast(uint16_t, ha) | ((uint32_t)__builtin_bit_cast(uint16_t, hb) << 16);
+}
+
+__device__ __forceinline__ u32x4 kv_dequant_half(uint32_t codes, float s, float g) {
+  u32x4 o;
+  f32x2 f0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 0);
+  f32x2 f1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 1);
+  f32x2 f2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 2);
+  f32x2 f3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 3);
+  o.x = kv_dequant_pair(make_float2(f0.x, f0.y), s, g);
+  o.y = kv_dequant_pair(make_float2(f1.x, f1.y), s, g);
+  o.z = kv_dequant_pair(make_float2(f2.x, f2.y), s, g);
+  o.w = kv_dequant_pair(make_float2(f3.x, f3.y), s, g);
+  return o;
+}
+
+// grid (tiles, kv_heads, 2*nlayers); out [nlayers][H][n][D] bf16.
+__global__ void __launch_bounds__(kThreads) kv_read_kernel(nvfp4_kv_cache c, int layer0, int64_t t0, int64_t n,
+                                                           u32x4* __restrict__ k_out, u32x4* __restrict__ v_out) {
+  const int h = blockIdx.y;
+  const int li = blockIdx.z >> 1;
+  const bool is_v = blockIdx.z & 1;
+  u32x4* out = is_v ? v_out : k_out;
+  if (!out) return;
+  const int l = layer0 + li;
+  const int H = c.kv_heads, bpr = c.head_dim / kBlock;
+  const float g = (is_v ? c.v_g : c.k_g)[l * H + h];
+  const u32x2* sq = (const u32x2*)(is_v ? c.v : c.k);
+  const uint8_t* ssf = is_v ? c.v_sf : c.k_sf;
+  const int64_t row0 = ((int64_t)l * H + h) * c.capacity + t0;
+  const int64_t orow0 = ((int64_t)li * H + h) * n;
+  const int64_t nblk = n * bpr;
+  for (int64_t b = (int64_t)blockIdx.x * kThreads + threadIdx.x; b < nblk; b += (int64_t)gridDim.x * kThreads) {
+    const u32x2 cw = sq[row0 * bpr + b];
+    const float s = e4m3_value(ssf[row0 * bpr + b]);
+    const int64_t o = orow0 * bpr + b;
+    out[2 * o] = kv_dequant_half(cw.x, s, g);
+    out[2 * o + 1] = kv_dequant_half(cw.y, s, g);
+  }
+}
+
+// Decode-step QK: grid (token tiles, kv_heads, layers).  The grp query heads
+// of one KV head (GQA) are staged in LDS as f32; each lane takes one
+// (token, block) pair, decodes its 16 K values exactly (E2M1 * s in f32) and
+// accumulates grp partial dot products, which the bpr lanes of a token then
+// sum with shuffles.  logit = g * sum (exact K products, fp32 accumulation).
+constexpr int kQKMaxLds = 16 * 256;   // grp * head_dim floats
+
+__global__ void __launch_bounds__(kThreads) kv_decode_qk_kernel(nvfp4_kv_cache c, const uint16_t* __restrict__ q,
+                                                                int q_heads, int64_t n, float* __restrict__ logits) {
+  const int h = blockIdx.y, l = blockIdx.z;
+  const int H = c.kv_heads, D = c.head_dim, bpr = D / kBlock;
+  const int grp = q_heads / H;
+  __shared__ float qs[kQKMaxLds];
+  for (int i = threadIdx.x; i < grp * D; i += kThreads) {
+    const int hq = h * grp + i / D;
+    qs[i] = __uint_as_float((uint32_t)q[((int64_t)l * q_heads + hq) * D + (i % D)] << 16);
+  }
+  __syncthreads();
+  const float g = c.k_g[l * H + h];
+  const u32x2* kq = (const u32x2*)c.k;
+  const int64_t row0 = ((int64_t)l * H + h) * c.capacity;
+  // bpr is a power of two dividing 64 (validated on the host), so every token's
+  // lanes sit in one wave and the tile loop keeps whole tokens per iteration.
+  const int64_t tokens_per_iter = kThreads / bpr;
+  for (int64_t t0 = (int64_t)blockIdx.x * tokens_per_iter; t0 < n; t0 += (int64_t)gridDim.x * tokens_per_iter) {
+    const int64_t t = t0 + threadIdx.x / bpr;
+    const int j = threadIdx.x % bpr;
+    float kv[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) kv[e] = 0.0f;
+    if (t < n) {
+      const u32x2 cw = kq[(row0 + t) * bpr + j];
+      const float s = e4m3_value(c.k_sf[(row0 + t) * bpr + j]);
+      const f32x2 f0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw.x, 1.0f, 0);
+      const f32x2 f1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw.x, 1.0f, 1);
+      const f32x2 f2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw.x, 1.0f, 2);
+      const f32x2 f3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw.x, 1.0f, 3);
+      const f32x2 f4 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw.y, 1.0f, 0);
+      const f32x2 f5 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw.y, 1.0f, 1);
+      const f32x2 f6 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw.y, 1.0f, 2);
+      const f32x2 f7 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw.y, 1.0f, 3);
+      kv[0] = f0.x * s; kv[1] = f0.y * s; kv[2] = f1.x * s; kv[3] = f1.y * s;
+      kv[4] = f2.x * s; kv[5] = f2.y * s; kv[6] = f3.x * s; kv[7] = f3.y * s;
+      kv[8] = f4.x * s; kv[9] = f4.y * s; kv[10] = f5.x * s; kv[11] = f5.y * s;
+      kv[12] = f6.x * s; kv[13] = f6.y * s; kv[14] = f7.x * s; kv[15] = f7.y * s;
+    }
+    for (int hq = 0; hq < grp; ++hq) {
+      float acc = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc = __builtin_fmaf(qs[hq * D + 16 * j + e], kv[e], acc);
+      for (int off = 1; off < bpr; off <<= 1) acc += __shfl_xor(acc, off, 64);
+      if (t < n && j == 0) logits[((int64_t)l * q_heads + h * grp + hq) * n + t] = acc * g;
+    }
+  }
+}
+
+}  // namespace nvfp4
+
+// ============================================================ host entry points
+namespace {
+
+using namespace nvfp4;
+
+nvfp4_status check_desc(const nvfp4_kv_cache* c) {
+  if (!c) return NVFP4_EINVAL;
+  if (c->layers <= 0 || c->kv_heads <= 0 || c->head_dim <= 0 || c->capacity < 0) return NVFP4_EINVAL;
+  if (c->head_dim % kBlock) return NVFP4_EINVAL;
+  if (c->kv_heads > 65535 || c->layers > 32767) return NVFP4_EINVAL;
+  if (!c->k || !c->v || !c->k_sf || !c->v_sf || !c->k_g || !c->v_g) return NVFP4_EINVAL;
+  if (!nvfp4host::aligned16(c->k) || !nvfp4host::aligned16(c->v) || !nvfp4host::aligned16(c->k_sf) ||
+      !nvfp4host::aligned16(c->v_sf))
+    return NVFP4_EALIGN;
+  if ((reinterpret_cast<uintptr_t>(c->k_g) & 3u) || (reinterpret_cast<uintptr_t>(c->v_g) & 3u)) return NVFP4_EALIGN;
+  return NVFP4_OK;
+}
+
+int tiles_for(int64_t blocks, int64_t other_wgs) {
+  const int64_t target = (int64_t)nvfp4host::num_cus() * 8;
+  int64_t per = std::max<int64_t>(1, (target + other_wgs - 1) / other_wgs);
+  const int64_t need = (blocks + kThreads - 1) / kThreads;
+  return (int)std::max<int64_t>(1, std::min<int64_t>(std::min(per, need), 65535));
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t nvfp4_kv_bytes(const nvfp4_kv_cache* c) {
+  if (!c || c->layers <= 0 || c->kv_heads <= 0 || c->head_dim <= 0 || c->capacity < 0 || c->head_dim % kBlock)
+    return 0;
+  const size_t per_row = (size_t)c->head_dim / 2 + (size_t)c->head_dim / kBlock;   // 0.5625 B per value
+  return 2 * (size_t)c->layers * (size_t)c->kv_heads * (size_t)c->capacity * per_row;
+}
+
+nvfp4_status nvfp4_kv_append(const nvfp4_kv_cache* c, int64_t start, int64_t n, const uint16_t* k_new,
+                             const uint16_t* v_new, void* stream) {
+  nvfp4_status st = check_desc(c);
+  if (st) return st;
+  if (start < 0 || n < 0 || start > c->capacity || n > c->capacity - start) return NVFP4_EINVAL;
+  if (n == 0) return NVFP4_OK;
+  if (!k_new || !v_new) return NVFP4_EINVAL;
+  if (!nvfp4host::aligned16(k_new) || !nvfp4host::aligned16(v_new)) return NVFP4_EALIGN;
+  if ((st = nvfp4host::check_device())) return st;
+  const int64_t blocks = n * (c->head_dim / kBlock);
+  const int64_t others = (int64_t)c->kv_heads * 2 * c->layers;
+  const int tiles = tiles_for(blocks, others);
+  kv_append_kernel<<<dim3(tiles, c->kv_heads, 2 * c->layers), kThreads, 0, (hipStream_t)stream>>>(
+      *c, start, n, (const u32x4*)k_new, (const u32x4*)v_new);
+  NVFP4_LAUNCH_CHECK();
+  return NVFP4_OK;
+}
+
+nvfp4_status nvfp4_kv_read(const nvfp4_kv_cache* c, int32_t layer0, int32_t nlayers, int64_t t0, int64_t n,
+                           uint16_t* k_out, uint16_t* v_out, void* stream) {
+  nvfp4_status st = check_desc(c);
+  if (st) return st;
+  if (layer0 < 0 || nlayers < 0 || layer0 > c->layers || nlayers > c->layers - layer0) return NVFP4_EINVAL;
+  if (t0 < 0 || n < 0 || t0 > c->capacity || n > c->capacity - t0) return NVFP4_EINVAL;
+  if (n == 0 || nlayers == 0 || (!k_out && !v_out)) return NVFP4_OK;
+  if (!nvfp4host::aligned16(k_out) || !nvfp4host::aligned16(v_out)) return NVFP4_EALIGN;
+  if ((st = nvfp4host::check_device())) return st;
+  const int64_t blocks = n * (c->head_dim / kBlock);
+  const int tiles = tiles_for(blocks, (int64_t)c->kv_heads * 2 * nlayers);
+  kv_read_kernel<<<dim3(tiles, c->kv_heads, 2 * nlayers), kThreads, 0, (hipStream_t)stream>>>(
+      *c, layer0, t0, n, (u32x4*)k_out, (u32x4*)v_out);
+  NVFP4_LAUNCH_CHECK();
+  return NVFP4_OK;
+}
+
+nvfp4_status nvfp4_kv_decode_qk(const nvfp4_kv_cache* c, const uint16_t* q, int32_t q_heads, int64_t n,
+                                float* logits, void* stream) {
+  nvfp4_status st = check_desc(c);
+  if (st) return st;
+  if (q_heads <= 0 || q_heads % c->kv_heads) return NVFP4_EINVAL;
+  const int grp = q_heads / c->kv_heads;
+  const int bpr = c->head_dim / kBlock;
+  if (grp > 16 || (int64_t)grp * c->head_dim > kQKMaxLds) return NVFP4_ENOTSUP;
+  if (bpr > 64 || (bpr & (bpr - 1))) return NVFP4_ENOTSUP;
+  if (n < 0 || n > c->capacity) return NVFP4_EINVAL;
+  if (n == 0) return NVFP4_OK;
+  if (!q || !logits) return NVFP4_EINVAL;
+  if (!nvfp4host::aligned16(q) || !nvfp4host::aligned16(logits)) return NVFP4_EALIGN;
+  if ((st = nvfp4host::check_device())) return st;
+  const int64_t tokens_per_iter = kThreads / bpr;
+  const int64_t need = (n + tokens_per_iter - 1) / tokens_per_iter;
+  const int tiles = (int)std::max<int64_t>(
+      1, std::min<int64_t>(need, std::max<int64_t>(1, (int64_t)nvfp4host::num_cus() * 8 /
+                                                           ((int64_t)c->kv_heads * c->layers))));
+  kv_decode_qk_kernel<<<dim3(tiles, c->kv_heads, c->layers), kThreads, 0, (hipStream_t)stream>>>(*c, q, q_heads, n,
+                                                                                                  logits);
+  NVFP4_LAUNCH_CHECK();
+  return NVFP4_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,109 @@
+"""GPU parity: NVFP4 KV cache append / read (bit-exact vs the oracle) and the
+decode-step QK sweep (relative Frobenius error <= 1e-5 vs the fp64 oracle)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from gpu_util import bits, np_, rel_frobenius
+
+pytestmark = pytest.mark.gpu
+
+nv = pytest.importorskip("nvfp4_block_scaled_06_amd")
+QK_TOL = 1e-5
+
+
+def _cache(L, H, D, cap, seed):
+    gen = torch.Generator().manual_seed(seed)
+    kg = (torch.rand((L, H), generator=gen) * 0.003 + 0.0005).float()
+    vg = (torch.rand((L, H), generator=gen) * 0.003 + 0.0005).float()
+    return nv.KVCache(L, H, D, cap, kg, vg, device="cuda"), np_(kg), np_(vg)
+
+
+@pytest.mark.parametrize("D,grp", [(128, 4), (64, 2), (32, 1), (256, 8), (16, 4)])
+def test_append_read_qk_small(D, grp):
+    print("case: kv small D", D, "grp", grp, flush=True)
+    L, H, cap = 3, 2, 300
+    cache, kg, vg = _cache(L, H, D, cap, D + grp)
+    gen = torch.Generator().manual_seed(11 * D + grp)
+    ks, vs = [], []
+    bounds = [0, 1, 8, 100, 257, 300]
+    for a, b in zip(bounds, bounds[1:]):
+        k = (torch.randn((L, b - a, H, D), generator=gen) * 2).to(torch.bfloat16)
+        v = torch.randn((L, b - a, H, D), generator=gen).to(torch.bfloat16)
+        cache.append(a, k.cuda(), v.cuda())
+        ks.append(bits(k))
+        vs.append(bits(v))
+    torch.cuda.synchronize()
+    kall = np.concatenate(ks, axis=1)
+    vall = np.concatenate(vs, axis=1)
+    okq, oks = oracle.kv_encode(kall, kg)
+    ovq, ovs = oracle.kv_encode(vall, vg)
+    assert np.array_equal(np_(cache.k), okq) and np.array_equal(np_(cache.k_sf), oks)
+    assert np.array_equal(np_(cache.v), ovq) and np.array_equal(np_(cache.v_sf), ovs)
+    # read a window of layers / tokens
+    kr, vr = cache.read(1, 2, 5, 250)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(kr), oracle.kv_read(okq[1:3, :, 5:255], oks[1:3, :, 5:255], kg[1:3]))
+    assert np.array_equal(bits(vr), oracle.kv_read(ovq[1:3, :, 5:255], ovs[1:3, :, 5:255], vg[1:3]))
+    # decode QK over the first n tokens
+    qv = torch.randn((L, H * grp, D), generator=gen).to(torch.bfloat16)
+    for n in (1, 77, 300):
+        logits = cache.decode_qk(qv.cuda(), n)
+        torch.cuda.synchronize()
+        want = oracle.decode_qk_f64(bits(qv), okq[:, :, :n], oks[:, :, :n], kg)
+        err = rel_frobenius(np_(logits), want)
+        assert err <= QK_TOL, f"n={n}: rel Frobenius {err:.3e}"
+
+
+def test_read_only_k_or_v():
+    cache, kg, vg = _cache(2, 2, 64, 40, 3)
+    k = torch.randn((2, 40, 2, 64)).to(torch.bfloat16)
+    v = torch.randn((2, 40, 2, 64)).to(torch.bfloat16)
+    cache.append(0, k.cuda(), v.cuda())
+    kr, vr = cache.read(0, 2, 0, 40, want_v=False)
+    torch.cuda.synchronize()
+    assert vr is None
+    okq, oks = oracle.kv_encode(bits(k), kg)
+    assert np.array_equal(bits(kr), oracle.kv_read(okq, oks, kg))
+
+
+def test_full_context_sampled():
+    """32 layers x 8 KV heads x 128 dims, 131072 tokens appended in 512 chunks of
+    256; sampled chunks checked byte for byte, decode QK for 32 query heads
+    (GQA 4:1) checked on sampled tokens against fp64."""
+    print("case: kv full context 32x8x128x131072", flush=True)
+    L, H, D, T, C = 32, 8, 128, 131072, 256
+    # tensor scales: amax/2688 of a calibration pass over the whole stream is
+    # replaced here by a fixed scale per (layer, head) near N(0,1)'s typical max
+    gen = torch.Generator().manual_seed(104)
+    kg = (torch.rand((L, H), generator=gen) * 0.0004 + 0.0018).float()
+    vg = (torch.rand((L, H), generator=gen) * 0.0004 + 0.0018).float()
+    cache = nv.KVCache(L, H, D, T, kg, vg, device="cuda")
+    for c in range(T // C):
+        k, v = synth.kv_chunk(c, device="cuda")
+        cache.append(c * C, k, v)
+    torch.cuda.synchronize()
+    kgn, vgn = np_(kg), np_(vg)
+    for c in (0, 1, 257, 511):
+        k, v = synth.kv_chunk(c, device="cuda")
+        okq, oks = oracle.kv_encode(bits(k), kgn)
+        ovq, ovs = oracle.kv_encode(bits(v), vgn)
+        sl = slice(c * C, (c + 1) * C)
+        assert np.array_equal(np_(cache.k[:, :, sl]), okq), f"chunk {c} K codes"
+        assert np.array_equal(np_(cache.k_sf[:, :, sl]), oks), f"chunk {c} K scales"
+        assert np.array_equal(np_(cache.v[:, :, sl]), ovq), f"chunk {c} V codes"
+        assert np.array_equal(np_(cache.v_sf[:, :, sl]), ovs), f"chunk {c} V scales"
+    qv = synth.kv_query(device="cuda")
+    logits = cache.decode_qk(qv, T)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(0)
+    toks = np.sort(rng.choice(T, 2048, replace=False))
+    kq = np_(cache.k[:, :, toks])
+    ks = np_(cache.k_sf[:, :, toks])
+    want = oracle.decode_qk_f64(bits(qv), kq, ks, kgn)
+    got = np_(logits[:, :, toks])
+    err = rel_frobenius(got, want)
+    assert err <= QK_TOL, f"rel Frobenius {err:.3e}"
+    del cache, logits
