@@ -1,0 +1,330 @@
+"""Benchmark of the NVFP4 hot path on one MI355X.
+
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extras] [--no-cpu]
+
+Headline step (one JSON line on stdout): NVFP4 quantize + dequantize of 64
+MoE expert weight matrices [2048 x 7168] bf16 (N(0, 0.02) with 0.1% x50
+outliers), one FP32 tensor scale per expert, inputs resident in HBM.
+value = algorithmic bytes of the step (each input byte read once, each
+output byte written once) / wall time per step, in GB/s.
+
+Extra records in the same line ("rows"): the single 1024x1024 tensor, the
+16384 x 7168 activation quantize (two-kernel and fused), the 32x8x128 KV
+cache (512 appends of 256 tokens, decode QK over 131072 tokens, 32 query
+heads), and the 8192 x 2048 x 7168 block-scaled GEMM in TFLOP/s -- each with
+its roofline fraction.  Every kernel time comes from HIP events recorded on
+the stream the kernels run on.
+
+cpu_baseline: the CPU oracle (the parity reference, not tuned) timed on a
+bounded sample of the headline workload on this host's cores.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--no-extras", action="store_true", help="headline step only")
+    p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    p.add_argument("--rows-only", default="", help="comma list of extra rows to run (single,acts,kv,gemm)")
+    return p.parse_args()
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+class EventTimer:
+    """Per-call HIP event pairs on the current stream; mean milliseconds."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.pairs = {}
+
+    def start(self, name):
+        e = self.torch.cuda.Event(enable_timing=True)
+        e.record()
+        self.pairs.setdefault(name, []).append([e, None])
+
+    def stop(self, name):
+        e = self.torch.cuda.Event(enable_timing=True)
+        e.record()
+        self.pairs[name][-1][1] = e
+
+    def mean_ms(self, name):
+        v = [a.elapsed_time(b) for a, b in self.pairs.get(name, [])]
+        return sum(v) / len(v) if v else None
+
+    def reset(self):
+        self.pairs = {}
+
+
+def source_hash():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "nvfp4_block_scaled_06_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_for(kernel):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken from the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_hash") != source_hash():
+        return None
+    k = t.get("kernels", {}).get(kernel)
+    return None if k is None else k.get("hbm_bytes_per_launch")
+
+
+# ----------------------------------------------------------------- workloads
+def bytes_quantize(n_elem, n_tensors):
+    return n_elem * 2 + n_elem // 2 + n_elem // 16 + 4 * n_tensors
+
+
+def bytes_dequant(n_elem, n_tensors):
+    return n_elem // 2 + n_elem // 16 + 4 * n_tensors + 2 * n_elem
+
+
+def run_headline(nv, synth, torch, steps, warmup):
+    E, R, C = 64, 2048, 7168
+    log(f"headline: experts {E}x{R}x{C}: generating inputs on the GPU")
+    x = synth.experts(E, R, C, device="cuda")
+    n = E * R * C
+    q = torch.empty((E, R, C // 2), dtype=torch.uint8, device="cuda")
+    sf = torch.empty((E, R, C // 16), dtype=torch.uint8, device="cuda")
+    g = torch.empty((E,), dtype=torch.float32, device="cuda")
+    y = torch.empty_like(x)
+    ws = nv.make_workspace(E, R, C)
+    flags = "fused" if _fused_ok(nv) else "two_kernel"
+    timer = EventTimer(torch)
+
+    def step():
+        timer.start("quantize")
+        nv.quantize(x, flags=flags, workspace=ws, out=(q, sf, g))
+        timer.stop("quantize")
+        timer.start("dequantize")
+        nv.dequantize(q, sf, g, out=y)
+        timer.stop("dequantize")
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    timer.reset()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / steps
+    bq, bd = bytes_quantize(n, E), bytes_dequant(n, E)
+    res = {
+        "ms_per_step": ms_step,
+        "value_gbs": (bq + bd) / (ms_step * 1e-3) / 1e9,
+        "quantize_ms": timer.mean_ms("quantize"),
+        "dequantize_ms": timer.mean_ms("dequantize"),
+        "quantize_bytes": bq,
+        "dequantize_bytes": bd,
+        "flags": flags,
+    }
+    del x, q, sf, g, y, ws
+    torch.cuda.empty_cache()
+    return res
+
+
+def _fused_ok(nv):
+    """True when the library accepts the persistent single-launch mode."""
+    import torch
+    x = torch.zeros((1, 16), dtype=torch.bfloat16, device="cuda")
+    try:
+        nv.quantize(x, flags="fused")
+        torch.cuda.synchronize()
+        return True
+    except nv.NVFP4Error:
+        return False
+
+
+def flush_caches(torch, buf):
+    buf.fill_(1)   # 512 MiB write: larger than the 256 MB Infinity Cache
+
+
+def timed(torch, fn, reps, flush=None, warm=2):
+    for _ in range(warm):
+        fn()
+    ms = []
+    for _ in range(reps):
+        if flush is not None:
+            flush()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        fn()
+        b.record()
+        torch.cuda.synchronize()
+        ms.append(a.elapsed_time(b))
+    ms.sort()
+    return ms[len(ms) // 2]
+
+
+def roof(bytes_or_flops, ms, peak, unit):
+    ach = bytes_or_flops / (ms * 1e-3) / (1e9 if unit == "GB/s" else 1e12)
+    return {"achieved": round(ach, 2), "peak": peak, "unit": unit, "frac": round(ach / peak, 4)}
+
+
+def run_extras(nv, synth, torch, which):
+    rows = {}
+    fbuf = torch.empty(512 * 2 ** 20, dtype=torch.uint8, device="cuda")
+    flush = lambda: flush_caches(torch, fbuf)
+    fused = _fused_ok(nv)
+    if "single" in which:
+        x = synth.single(device="cuda")
+        ws = nv.make_workspace(1, 1024, 1024)
+        q, sf, g = nv.quantize(x, workspace=ws)
+        n = 1024 * 1024
+        mq = timed(torch, lambda: nv.quantize(x, workspace=ws, out=(q, sf, g)), 50)
+        md = timed(torch, lambda: nv.dequantize(q, sf, g), 50)
+        rows["single_1024x1024"] = {
+            "note": "2.7 MB working set: launch-bound and cache-resident; warm medians",
+            "quantize": {"ms": mq, **roof(bytes_quantize(n, 1), mq, HBM_PEAK_GBS, "GB/s")},
+            "dequantize": {"ms": md, **roof(bytes_dequant(n, 1), md, HBM_PEAK_GBS, "GB/s")}}
+        del x, q, sf, g
+    if "acts" in which:
+        x = synth.activations(device="cuda")
+        n = x.numel()
+        ws = nv.make_workspace(1, 16384, 7168)
+        q, sf, g = nv.quantize(x, workspace=ws)
+        r = {}
+        for fl in (["two_kernel", "fused"] if fused else ["two_kernel"]):
+            m = timed(torch, lambda: nv.quantize(x, flags=fl, workspace=ws, out=(q, sf, g)), 20, flush)
+            r[fl] = {"ms": m, **roof(bytes_quantize(n, 1), m, HBM_PEAK_GBS, "GB/s")}
+        rows["activations_16384x7168_quantize"] = r
+        del x, q, sf, g
+    if "kv" in which:
+        L, H, D, T, C = 32, 8, 128, 131072, 256
+        log("kv: generating 512 chunks of K/V on the GPU (16 GiB bf16)")
+        chunks = [synth.kv_chunk(c, device="cuda") for c in range(T // C)]
+        gen = torch.Generator().manual_seed(104)
+        kg = (torch.rand((L, H), generator=gen) * 0.0004 + 0.0018).float()
+        cache = nv.KVCache(L, H, D, T, kg, kg.clone(), device="cuda")
+        qv = synth.kv_query(device="cuda")
+        logits = torch.empty((L, 4 * H, T), dtype=torch.float32, device="cuda")
+
+        def appends():
+            for c, (k, v) in enumerate(chunks):
+                cache.append(c * C, k, v)
+        ma = timed(torch, appends, 5, flush, warm=1)
+        mqk = timed(torch, lambda: cache.decode_qk(qv, T, out=logits), 20, flush)
+        nvals = L * H * D * T
+        app_bytes = 2 * nvals * 2 + 2 * (nvals // 2 + nvals // 16)
+        qk_bytes = nvals // 2 + nvals // 16 + L * 4 * H * T * 4 + qv.numel() * 2
+        rows["kv_32x8x128_131072"] = {
+            "append_512x256": {"ms": ma, "ms_per_chunk": ma / (T // C), **roof(app_bytes, ma, HBM_PEAK_GBS, "GB/s")},
+            "decode_qk_32q": {"ms": mqk, **roof(qk_bytes, mqk, HBM_PEAK_GBS, "GB/s")},
+            "cache_bytes": cache.nbytes()}
+        del chunks, cache, logits
+        torch.cuda.empty_cache()
+    if "gemm" in which:
+        a, b = synth.gemm_operands(device="cuda")
+        aq, asf, ag = nv.quantize(a)
+        bq, bsf, bg = nv.quantize(b)
+        c = torch.empty((8192, 2048), dtype=torch.float32, device="cuda")
+        m = timed(torch, lambda: nv.gemm(aq, asf, ag, bq, bsf, bg, out=c), 20)
+        flops = 2 * 8192 * 2048 * 7168
+        rows["gemm_8192x2048x7168"] = {"ms": m, "bound": "mfma",
+                                       **roof(flops, m, BF16_MFMA_PEAK_TFLOPS, "TFLOP/s")}
+        del a, b, aq, bq, c
+    del fbuf
+    torch.cuda.empty_cache()
+    return rows
+
+
+def cpu_baseline(synth, torch):
+    """The oracle, untouched, on 8 of the 64 expert matrices: quantize + dequantize
+    (about 10-15 s of CPU work on a 16-core host)."""
+    import numpy as np
+    import oracle
+    E = 8
+    x = synth.experts(E, 2048, 7168, device="cuda")
+    xb = x.cpu().view(torch.int16).numpy().view(np.uint16)
+    del x
+    n = E * 2048 * 7168
+    t0 = time.perf_counter()
+    q, sf, g = oracle.quantize(xb)
+    oracle.dequantize(q, sf, g)
+    dt = time.perf_counter() - t0
+    nbytes = bytes_quantize(n, E) + bytes_dequant(n, E)
+    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": oracle.max_threads(), "kind": "oracle",
+            "sample": f"quantize+dequantize of {E} of the 64 expert matrices ({E}x2048x7168), {dt:.2f} s wall"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported (the multi-GPU design "
+              "is documented, not built).", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import nvfp4_block_scaled_06_amd as nv
+    import synth
+    nv.lib()                       # fail loudly if the HIP library is missing
+    torch.cuda.set_device(0)
+    head = run_headline(nv, synth, torch, args.steps, args.warmup)
+    log("headline done:", json.dumps(head))
+    rows = {}
+    if not args.no_extras:
+        which = args.rows_only.split(",") if args.rows_only else ["single", "acts", "kv", "gemm"]
+        rows = run_extras(nv, synth, torch, which)
+        log("extras done")
+    cpu = None if args.no_cpu else cpu_baseline(synth, torch)
+    dom = "quantize" if head["quantize_ms"] >= head["dequantize_ms"] else "dequantize"
+    dom_bytes = head[f"{dom}_bytes"]
+    dom_ms = head[f"{dom}_ms"]
+    kname = {"quantize": "nvfp4_quantize (" + head["flags"] + ")", "dequantize": "dequant_kernel"}[dom]
+    r = roof(dom_bytes, dom_ms, HBM_PEAK_GBS, "GB/s")
+    line = {
+        "metric": "NVFP4 quantize/dequant GB/s (% of 8 TB/s HBM); block-scaled GEMM TFLOPS",
+        "value": round(head["value_gbs"], 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(head["ms_per_step"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded; N(0,0.02) with Bernoulli(0.001) x50 outliers)",
+        "config": {"workload": "moe_expert_weights_quantize_dequantize", "experts": 64, "rows": 2048,
+                   "cols": 7168, "block": 16, "quantize_flags": head["flags"], "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "kernel": kname, "achieved": r["achieved"], "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": r["frac"], "traffic": traffic_for(dom),
+                     "ms_per_launch": round(dom_ms, 4), "algorithmic_bytes_per_launch": dom_bytes},
+        "cpu_baseline": cpu,
+        "kernels_ms": {"quantize": round(head["quantize_ms"], 4), "dequantize": round(head["dequantize_ms"], 4)},
+        "rows": rows,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
