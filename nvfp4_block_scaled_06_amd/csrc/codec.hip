@@ -2,28 +2,38 @@
 //
 // Two-level microscaling (axbrief.com, "NVFP4: how NVIDIA pre-trained a 12B
 // model on 10 trillion tokens", section "E2M1 format and two-level scaling"):
-// pass 1 reduces the tensor amax (the FP32 tensor scale sets the overall
-// range), pass 2 derives each 16-value block's E4M3 scale from its amax and
-// rounds every element onto the E2M1 grid, packing two codes per byte.
+// a tensor amax pass (the FP32 tensor scale sets the overall range), then an
+// encode pass that derives each 16-value block's E4M3 scale from the block's
+// amax and rounds every element onto the E2M1 grid, two codes per byte.
 // Dequantization restores values from the scales (omidsaffari.com, "LLM
 // quantization guide", section "What is LLM quantization").
 //
-// Memory layout per tensor: a flat run of 16-value blocks (rows never split a
-// block because cols % 16 == 0): x block i at 32*i bytes, codes at 8*i,
-// scale byte at i.  One thread handles one block per iteration; consecutive
-// lanes take consecutive blocks, so every wave reads 2 KiB and writes 512 B
-// of codes contiguously.
+// Memory layout per tensor: a flat run of 16-value blocks (cols % 16 == 0,
+// so rows never split a block).  Kernels work in HALF blocks: half block h
+// is 16 bytes of bf16 at x + 16h, 4 code bytes at q + 4h, and shares the
+// scale byte sf[h/2] with its partner.  Lane i of a wave takes half block
+// base+i, so each load / store instruction covers one contiguous run.
+//
+// Launch modes of nvfp4_quantize:
+//  TWO_KERNEL  amax_partial_kernel (per-workgroup maxima, no atomics) then
+//              encode_kernel (reduces the partials, builds the table, encodes).
+//  FUSED       fused_quantize_kernel: one cooperative launch whose workgroups
+//              walk the batch tensor by tensor.  Each workgroup reduces its
+//              slice of tensor t, publishes it (agent-scope atomics), then
+//              encodes its slice of tensor t-1 -- data it read one step
+//              earlier, still in L2 / the Infinity Cache -- so HBM sees each
+//              input byte about once.
 #include <algorithm>
 
 #include "common.hpp"
 
 namespace nvfp4 {
 
+constexpr int kU = 4;   // half blocks per lane per loop trip (loads in flight)
+
 // ------------------------------------------------------------ pass 1: amax
 // grid (P, batch): workgroup p of tensor t reduces a strided share of the
-// tensor's 16-byte vectors and writes one partial maximum (bf16 magnitude
-// bits) to partial[t*P + p].  No atomics, no zero-fill: pass 2 reduces the P
-// partials itself.
+// tensor's 16-byte vectors into partial[t*P + p] (bf16 magnitude bits).
 __global__ void __launch_bounds__(kThreads) amax_partial_kernel(const u32x4* __restrict__ x, int64_t vec_per_tensor,
                                                                 uint32_t* __restrict__ partial) {
   const int t = blockIdx.y;
@@ -32,10 +42,7 @@ __global__ void __launch_bounds__(kThreads) amax_partial_kernel(const u32x4* __r
   uint32_t m0 = 0, m1 = 0;
   int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
   for (; i + 3 * stride < vec_per_tensor; i += 4 * stride) {
-    const u32x4 a = xt[i];
-    const u32x4 b = xt[i + stride];
-    const u32x4 c = xt[i + 2 * stride];
-    const u32x4 d = xt[i + 3 * stride];
+    const u32x4 a = xt[i], b = xt[i + stride], c = xt[i + 2 * stride], d = xt[i + 3 * stride];
     m0 = pk_absmax(pk_absmax(pk_absmax(pk_absmax(m0, a.x), a.y), a.z), a.w);
     m1 = pk_absmax(pk_absmax(pk_absmax(pk_absmax(m1, b.x), b.y), b.z), b.w);
     m0 = pk_absmax(pk_absmax(pk_absmax(pk_absmax(m0, c.x), c.y), c.z), c.w);
@@ -58,57 +65,67 @@ __global__ void __launch_bounds__(kThreads) amax_partial_kernel(const u32x4* __r
   }
 }
 
-// ------------------------------------------------------------ pass 2: encode
-// Shared prologue: the tensor scale g, d6 = RN32(6g), r6 = RN32(1/d6) and the
-// 127-entry encode table in LDS.
-struct TensorScales {
-  float g, d6, r6;
-  bool zero_all, exact_all;
-};
-
-__device__ __forceinline__ TensorScales make_scales(float g) {
-  TensorScales ts;
-  ts.g = g;
-  ts.d6 = 6.0f * g;
-  ts.zero_all = ts.d6 == 0.0f;
-  ts.exact_all = !(ts.d6 >= 0x1p-125f && ts.d6 <= 0x1p125f);
-  ts.r6 = (ts.zero_all || ts.exact_all) ? 0.0f : 1.0f / ts.d6;
-  return ts;
+// ------------------------------------------------------------ encode pieces
+// Per-tensor state of the encode pass: g, the reciprocal of d6 = RN32(6g) and
+// the fp64 reciprocal of every block divisor d = RN32(s g) in LDS.
+__device__ __forceinline__ void build_table(double* table, float g) {
+  for (uint32_t j = threadIdx.x; j < 127u; j += blockDim.x) table[j] = recip_entry(j, g);
 }
 
-__device__ __forceinline__ void build_table(Entry* table, float g) {
-  for (uint32_t j = threadIdx.x; j < 127u; j += kThreads) table[j] = build_entry(j, g);
+// Encodes one wave chunk of half blocks [base, base+64) clipped to [lo, hi)
+// (the ragged tail of a tensor or slice).  All lanes run it together, so the
+// DPP pair exchange is always well defined.
+__device__ __forceinline__ void encode_tail(const u32x4* __restrict__ xt, uint32_t* __restrict__ qt,
+                                            uint8_t* __restrict__ st, int64_t base, int64_t lo, int64_t hi,
+                                            double r6, const double* table) {
+  const int lane = threadIdx.x & 63;
+  const int64_t hb = base + lane;
+  const bool ok = hb >= lo && hb < hi;
+  const u32x4 v = ok ? xt[hb] : u32x4{0u, 0u, 0u, 0u};
+  const uint32_t sbyte = block_scale_byte(pair_max(half_absmax_bits(v)), r6);
+  const uint32_t code = encode_half(v, table[sbyte]);
+  if (ok) {
+    qt[hb] = code;
+    if ((lane & 1) == 0) st[hb >> 1] = (uint8_t)sbyte;
+  }
 }
 
-__device__ __forceinline__ void load_block(const u32x4* __restrict__ xb, uint32_t (&w)[8]) {
-  const u32x4 a = xb[0];
-  const u32x4 b = xb[1];
-  w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
-  w[4] = b.x; w[5] = b.y; w[6] = b.z; w[7] = b.w;
-}
-
-__device__ __forceinline__ void encode_store(const uint32_t (&w)[8], const TensorScales& ts, const Entry* table,
-                                             u32x2* __restrict__ qb, uint8_t* __restrict__ sb) {
-  uint32_t am = 0;
+// Encodes kU whole wave chunks (64 half blocks each, every one in range):
+// chunk u starts at half block c[u] (wave-uniform, a multiple of 64).  No
+// bounds checks: the loads and stores use a scalar base plus the lane offset.
+__device__ __forceinline__ void encode_chunks(const u32x4* __restrict__ xt, uint32_t* __restrict__ qt,
+                                              uint8_t* __restrict__ st, const int64_t (&c)[kU], double r6,
+                                              const double* table) {
+  const int lane = threadIdx.x & 63;
+  u32x4 v[kU];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) am = pk_absmax(am, w[i]);
-  const uint32_t sbyte = block_scale_byte(halves_max(am), ts.d6, ts.r6, ts.exact_all, ts.zero_all);
-  const Entry en = table[sbyte];
-  uint32_t c0, c1;
-  encode_block(w, en, sbyte, ts.g, c0, c1);
-  *qb = u32x2{c0, c1};
-  *sb = (uint8_t)sbyte;
+  for (int u = 0; u < kU; ++u) v[u] = (xt + c[u])[lane];
+  uint32_t sbyte[kU];
+#pragma unroll
+  for (int u = 0; u < kU; ++u) sbyte[u] = block_scale_byte(pair_max(half_absmax_bits(v[u])), r6);
+  double r[kU];
+#pragma unroll
+  for (int u = 0; u < kU; ++u) r[u] = table[sbyte[u]];
+#pragma unroll
+  for (int u = 0; u < kU; ++u) {
+    const uint32_t code = encode_half(v[u], r[u]);
+    __builtin_nontemporal_store(code, (qt + c[u]) + lane);
+    if ((lane & 1) == 0) (st + c[u] / 2)[lane >> 1] = (uint8_t)sbyte[u];
+  }
 }
 
+// ------------------------------------------------------------ pass 2 (two-kernel) / with_scale
 // grid (P, batch).  kFromPartials: g = RN32(amax/2688) from pass-1 partials;
 // otherwise g is read from gin[t] (quantize_with_scale).
 template <bool kFromPartials>
-__global__ void __launch_bounds__(kThreads) encode_kernel(const u32x4* __restrict__ x, int64_t blk_per_tensor,
+__global__ void __launch_bounds__(kThreads) encode_kernel(const u32x4* __restrict__ x, int64_t hb_per_tensor,
                                                           const uint32_t* __restrict__ partial, int npartial,
                                                           const float* __restrict__ gin, float* __restrict__ gout,
-                                                          u32x2* __restrict__ q, uint8_t* __restrict__ sf) {
-  const int t = blockIdx.y;
-  __shared__ Entry table[128];
+                                                          uint32_t* __restrict__ q, uint8_t* __restrict__ sf) {
+  // Tensors and chunks are walked in the reverse of pass 1's order, so the
+  // most recently read data -- still in the Infinity Cache -- is encoded first.
+  const int t = gridDim.y - 1 - blockIdx.y;
+  __shared__ double table[128];
   __shared__ uint32_t red[kThreads / 64];
   float g;
   if (kFromPartials) {
@@ -128,82 +145,343 @@ __global__ void __launch_bounds__(kThreads) encode_kernel(const u32x4* __restric
   } else {
     g = gin[t];
   }
-  const TensorScales ts = make_scales(g);
+  const double r6 = recip_d6(g);
   build_table(table, g);
   __syncthreads();
-
-  const int64_t base = (int64_t)t * blk_per_tensor;
-  const u32x4* xt = x + 2 * base;
-  u32x2* qt = q + base;
-  uint8_t* st = sf + base;
-  const int64_t stride = (int64_t)gridDim.x * kThreads;
-  int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  for (; i + stride < blk_per_tensor; i += 2 * stride) {
-    uint32_t w0[8], w1[8];
-    load_block(xt + 2 * i, w0);
-    load_block(xt + 2 * (i + stride), w1);
-    encode_store(w0, ts, table, qt + i, st + i);
-    encode_store(w1, ts, table, qt + i + stride, st + i + stride);
+  const int64_t off = (int64_t)t * hb_per_tensor;
+  const u32x4* xt = x + off;
+  uint32_t* qt = q + off;
+  uint8_t* st = sf + off / 2;
+  // whole 64-half-block chunks, kU per wave per trip, then the ragged rest
+  const int64_t nwaves = (int64_t)gridDim.x * (kThreads / 64);
+  const int64_t gw = (int64_t)blockIdx.x * (kThreads / 64) + wave_id();
+  const int64_t nchunks = (hb_per_tensor + 63) / 64;
+  const int64_t nfull = hb_per_tensor / 64;
+  if (gw == 0 && nfull < nchunks)                      // ragged last chunk first
+    encode_tail(xt, qt, st, nfull * 64, 0, hb_per_tensor, r6, table);
+  // chunk index counted from the end: j = nfull - 1 - k
+  int64_t k = gw;
+  for (; k + (kU - 1) * nwaves < nfull; k += kU * nwaves) {
+    int64_t c[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) c[u] = (nfull - 1 - (k + u * nwaves)) * 64;
+    encode_chunks(xt, qt, st, c, r6, table);
   }
-  for (; i < blk_per_tensor; i += stride) {
-    uint32_t w0[8];
-    load_block(xt + 2 * i, w0);
-    encode_store(w0, ts, table, qt + i, st + i);
+  for (; k < nfull; k += nwaves) encode_tail(xt, qt, st, (nfull - 1 - k) * 64, 0, hb_per_tensor, r6, table);
+}
+
+// ------------------------------------------------------------ fused persistent launch
+// Workspace header (zero-filled by the caller once; the kernel's last
+// workgroup restores it to zero).  Per tensor there is one 64-byte line per
+// arrival group {arrive, amax, go} and one top line {arrive, amax}: workgroup
+// w belongs to group w % kGroups, so no counter sees more than ~G/kGroups
+// atomics per tensor (same-address atomics serialize at the coherence point).
+constexpr int kGroups = 32;
+constexpr size_t kFusedHeaderBytes = 256;
+constexpr size_t kLineWords = 16;                      // 64-byte lines
+constexpr size_t kTensorWords = (kGroups + 1) * kLineWords;
+constexpr uint32_t kSpinLimit = 1u << 24;              // ~seconds: only a non-resident grid gets there
+
+struct FusedHeader {
+  uint32_t done;
+  uint32_t error;
+};
+
+__device__ __forceinline__ uint32_t* fused_line(uint32_t* ws, int t, int line) {
+  return ws + kFusedHeaderBytes / 4 + (size_t)t * kTensorWords + (size_t)line * kLineWords;
+}
+
+// Publishes this workgroup's maximum m of tensor t (thread 0 only).
+// Only atomic locations carry data between workgroups (the input is read-only
+// and outputs are not read back), so relaxed agent-scope atomics suffice;
+// acquire/release would write back and invalidate the whole L2 every time.
+// Each arrival is made data-dependent on the returned old maximum (always
+// < 2^15), so it is issued only after the maximum has been performed.
+__device__ __forceinline__ void fused_arrive(uint32_t* ws, int t, uint32_t m, int G) {
+  const int grp = blockIdx.x % kGroups;
+  const uint32_t members = (uint32_t)((G - grp + kGroups - 1) / kGroups);
+  const uint32_t ngroups = (uint32_t)(G < kGroups ? G : kGroups);
+  uint32_t* gl = fused_line(ws, t, grp);
+  const uint32_t om = __hip_atomic_fetch_max(gl + 1, m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const uint32_t oa = __hip_atomic_fetch_add(gl, 1u + (om >> 31), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (oa + 1 != members) return;
+  // last of its group: every member's maximum is in gl[1] (their arrivals,
+  // which follow their maxima, have all been counted)
+  const uint32_t gm = __hip_atomic_load(gl + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  uint32_t* top = fused_line(ws, t, kGroups);
+  const uint32_t om2 = __hip_atomic_fetch_max(top + 1, gm, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const uint32_t oa2 = __hip_atomic_fetch_add(top, 1u + (om2 >> 31), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (oa2 + 1 != ngroups) return;
+  // last group overall: release every group's waiters
+  const uint32_t tm = __hip_atomic_load(top + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  for (uint32_t k = 0; k < ngroups; ++k)
+    __hip_atomic_store(fused_line(ws, t, (int)k) + 2, 0x80000000u | tm, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Waits (thread 0 only) until tensor t's maximum is published to this
+// workgroup's group; returns it with bit 31 set, or 0 after the spin limit.
+__device__ __forceinline__ uint32_t fused_wait(uint32_t* ws, int t) {
+  uint32_t* go = fused_line(ws, t, blockIdx.x % kGroups) + 2;
+  for (uint32_t it = 0; it < kSpinLimit; ++it) {
+    const uint32_t v = __hip_atomic_load(go, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (v & 0x80000000u) return v;
+    __builtin_amdgcn_s_sleep(2);
+  }
+  __hip_atomic_store(&((FusedHeader*)ws)->error, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return 0u;
+}
+
+__global__ void __launch_bounds__(kThreads) fused_quantize_kernel(const u32x4* __restrict__ x, int batch,
+                                                                  int64_t hb_per_tensor, uint32_t* ws,
+                                                                  float* __restrict__ gout, uint32_t* __restrict__ q,
+                                                                  uint8_t* __restrict__ sf) {
+  __shared__ double table[128];
+  __shared__ uint32_t red[kThreads / 64];
+  __shared__ uint32_t sh_amax;
+  __shared__ uint32_t sh_last;
+  const int G = gridDim.x, w = blockIdx.x;
+  const int wave = threadIdx.x >> 6;
+  // this workgroup's contiguous slice of every tensor, in whole waves
+  const int64_t chunk = ((hb_per_tensor + G - 1) / G + 63) & ~(int64_t)63;
+  const int64_t lo = std::min<int64_t>((int64_t)w * chunk, hb_per_tensor);
+  const int64_t hi = std::min<int64_t>(lo + chunk, hb_per_tensor);
+  const int64_t step = kThreads;                       // the workgroup's waves tile 256 half blocks
+
+  for (int t = 0; t <= batch; ++t) {
+    if (t < batch) {                                   // pass 1 on tensor t
+      const u32x4* xt = x + (int64_t)t * hb_per_tensor;
+      uint32_t m0 = 0, m1 = 0;
+      int64_t i = lo + threadIdx.x;
+      for (; i + step < hi; i += 2 * step) {
+        const u32x4 a = xt[i], b = xt[i + step];
+        m0 = pk_absmax(pk_absmax(pk_absmax(pk_absmax(m0, a.x), a.y), a.z), a.w);
+        m1 = pk_absmax(pk_absmax(pk_absmax(pk_absmax(m1, b.x), b.y), b.z), b.w);
+      }
+      if (i < hi) {
+        const u32x4 a = xt[i];
+        m0 = pk_absmax(pk_absmax(pk_absmax(pk_absmax(m0, a.x), a.y), a.z), a.w);
+      }
+      uint32_t m = wave_max_u32(halves_max(pk_absmax(m0, m1)));
+      if ((threadIdx.x & 63) == 0) red[wave] = m;
+      __syncthreads();
+      if (threadIdx.x == 0) {
+        uint32_t r = red[0];
+#pragma unroll
+        for (int k = 1; k < kThreads / 64; ++k) r = r > red[k] ? r : red[k];
+        fused_arrive(ws, t, r, G);
+      }
+      __syncthreads();                                 // red[] is reused by the next tensor's pass 1
+    }
+    if (t >= 1) {                                      // pass 2 on tensor t-1
+      const int tp = t - 1;
+      if (threadIdx.x == 0) sh_amax = fused_wait(ws, tp);
+      __syncthreads();
+      const uint32_t v = sh_amax;
+      const float g = v ? __uint_as_float((v & 0x7fffu) << 16) / kGlobalDiv : __builtin_nanf("");
+      if (w == 0 && threadIdx.x == 0) gout[tp] = g;
+      const double r6 = recip_d6(g);
+      build_table(table, g);
+      __syncthreads();
+      // newest data first: walk the slice's 64-half-block chunks backwards,
+      // chunk k going to wave k % 4
+      const int64_t off = (int64_t)tp * hb_per_tensor;
+      const u32x4* xt = x + off;
+      uint32_t* qt = q + off;
+      uint8_t* st = sf + off / 2;
+      const int64_t nfull = (hi - lo) / 64;              // whole chunks of the slice
+      const int nw = kThreads / 64;
+      const int wv = wave_id();
+      int64_t k = nfull - 1 - wv;
+      for (; k - (kU - 1) * nw >= 0; k -= kU * nw) {
+        int64_t c[kU];
+#pragma unroll
+        for (int u = 0; u < kU; ++u) c[u] = lo + (k - u * nw) * 64;
+        encode_chunks(xt, qt, st, c, r6, table);
+      }
+      for (; k >= 0; k -= nw) encode_tail(xt, qt, st, lo + k * 64, lo, hi, r6, table);
+      if (wv == 0 && lo + nfull * 64 < hi)            // ragged end of the last slice
+        encode_tail(xt, qt, st, lo + nfull * 64, lo, hi, r6, table);
+      __syncthreads();                                 // the table is rebuilt for the next tensor
+    }
+  }
+  // The last workgroup out restores the header to zero for the next launch.
+  // Every counter read of this workgroup has returned (the values were used
+  // above), so a relaxed count is enough.
+  if (threadIdx.x == 0) {
+    const uint32_t old = __hip_atomic_fetch_add(&((FusedHeader*)ws)->done, 1u, __ATOMIC_RELAXED,
+                                                __HIP_MEMORY_SCOPE_AGENT);
+    sh_last = old == (uint32_t)G - 1;
+  }
+  __syncthreads();
+  if (sh_last) {
+    const size_t words = (size_t)batch * kTensorWords;
+    uint32_t* base = ws + kFusedHeaderBytes / 4;
+    for (size_t i = threadIdx.x; i < words; i += kThreads)
+      __hip_atomic_store(base + i, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (threadIdx.x == 0)
+      __hip_atomic_store(&((FusedHeader*)ws)->done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+// ------------------------------------------------------------ fused, tensor held on chip
+// When one tensor fits in the register files of the whole GPU (up to
+// kOnchipMaxPer half blocks per thread, one 512-thread workgroup per CU),
+// the persistent launch keeps it there.  Thread i of workgroup w owns half
+// blocks w*S + p*512 + i (p < kPer) of every tensor, S = 512*kPer, and three
+// register sets rotate through a three-stage pipeline: while the loads of
+// tensor t+2 are in flight, the workgroup reduces and publishes the maximum of
+// tensor t+1 and encodes tensor t, whose amax was published a whole step
+// earlier -- so the cross-workgroup wait and the atomics' round trips are
+// hidden behind a step of work, and HBM sees every input byte exactly once.
+constexpr int kOnchipThreads = 512;
+constexpr int kOnchipMaxPer = 14;   // 3 x 14 x 16 B per thread stays within 256 VGPRs
+
+// Loads this workgroup's slice of one tensor: the host only picks the on-chip
+// launch when every slice is whole (hb_per_tensor is a multiple of 512*kPer),
+// so there are no bounds checks.  Raw buffer loads address the slice with a
+// scalar resource plus a scalar per-p offset and one shared lane offset,
+// keeping the address arithmetic out of the vector registers that hold the
+// three tensors in flight.
+constexpr int kBufferWord3 = 0x00020000;   // gfx9 buffer resource word 3: 32-bit data format
+
+template <int kPer>
+__device__ __forceinline__ void onchip_load(const u32x4* __restrict__ xs, u32x4 (&v)[kPer]) {
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)xs, 0, kPer * kOnchipThreads * 16, kBufferWord3);
+#pragma unroll
+  for (int p = 0; p < kPer; ++p)
+    v[p] = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)threadIdx.x * 16, p * kOnchipThreads * 16, 0);
+}
+
+// Workgroup maximum of the held values, published for tensor t.
+template <int kPer>
+__device__ __forceinline__ void onchip_arrive(const u32x4 (&v)[kPer], uint32_t* red, uint32_t* ws, int t, int G) {
+  uint32_t m = 0;
+#pragma unroll
+  for (int p = 0; p < kPer; ++p) m = pk_absmax(pk_absmax(pk_absmax(pk_absmax(m, v[p].x), v[p].y), v[p].z), v[p].w);
+  m = wave_max_u32(halves_max(m));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t r = red[0];
+    for (int k = 1; k < kOnchipThreads / 64; ++k) r = r > red[k] ? r : red[k];
+    fused_arrive(ws, t, r, G);
+  }
+}
+
+// Waits for tensor t's amax, builds its table and encodes the held values.
+template <int kPer>
+__device__ __forceinline__ void onchip_encode(const u32x4 (&v)[kPer], int64_t lo, int t,
+                                              int64_t hb_per_tensor, uint32_t* ws, float* __restrict__ gout,
+                                              uint32_t* __restrict__ q, uint8_t* __restrict__ sf, double* table,
+                                              uint32_t* sh_amax) {
+  if (threadIdx.x == 0) *sh_amax = fused_wait(ws, t);
+  __syncthreads();
+  const uint32_t a = *sh_amax;
+  const float g = a ? __uint_as_float((a & 0x7fffu) << 16) / kGlobalDiv : __builtin_nanf("");
+  if (blockIdx.x == 0 && threadIdx.x == 0) gout[t] = g;
+  const double r6 = recip_d6(g);
+  build_table(table, g);
+  __syncthreads();
+  const int64_t off = (int64_t)t * hb_per_tensor + lo;
+  const __amdgpu_buffer_rsrc_t rq =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(q + off), 0, kPer * kOnchipThreads * 4, kBufferWord3);
+  const __amdgpu_buffer_rsrc_t rsf =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(sf + off / 2), 0, kPer * kOnchipThreads / 2, kBufferWord3);
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int p = 0; p < kPer; ++p) {
+    const uint32_t sbyte = block_scale_byte(pair_max(half_absmax_bits(v[p])), r6);
+    const uint32_t code = encode_half(v[p], table[sbyte]);
+    __builtin_amdgcn_raw_buffer_store_b32(code, rq, (int)threadIdx.x * 4, p * kOnchipThreads * 4, 0);
+    if ((lane & 1) == 0)
+      __builtin_amdgcn_raw_buffer_store_b8((uint8_t)sbyte, rsf, (int)threadIdx.x >> 1, p * (kOnchipThreads / 2), 0);
+    __builtin_amdgcn_sched_barrier(0);                 // one half block's temporaries at a time
+  }
+  __syncthreads();                                     // the table and sh_amax are reused by the next tensor
+}
+
+// One pipeline step: issue tensor t+2's loads into nw, publish tensor t+1's
+// maximum from nx, encode tensor t from cur.
+template <int kPer>
+__device__ __forceinline__ void onchip_step(const u32x4* __restrict__ x, int batch, int64_t hb_per_tensor, int64_t lo,
+                                            int t, const u32x4 (&cur)[kPer], const u32x4 (&nx)[kPer],
+                                            u32x4 (&nw)[kPer], uint32_t* ws, int G, float* __restrict__ gout,
+                                            uint32_t* __restrict__ q, uint8_t* __restrict__ sf, double* table,
+                                            uint32_t* red, uint32_t* sh_amax) {
+  // unconditional (tensor index clamped): a skipped load would keep the
+  // buffer's previous contents alive across the step and cost registers
+  const int tl = t + 2 < batch ? t + 2 : batch - 1;
+  onchip_load<kPer>(x + (int64_t)tl * hb_per_tensor + lo, nw);
+  if (t + 1 < batch) onchip_arrive<kPer>(nx, red, ws, t + 1, G);
+  onchip_encode<kPer>(cur, lo, t, hb_per_tensor, ws, gout, q, sf, table, sh_amax);
+}
+
+template <int kPer>
+__global__ void __launch_bounds__(kOnchipThreads) fused_onchip_kernel(const u32x4* __restrict__ x, int batch,
+                                                                      int64_t hb_per_tensor, uint32_t* ws,
+                                                                      float* __restrict__ gout,
+                                                                      uint32_t* __restrict__ q,
+                                                                      uint8_t* __restrict__ sf) {
+  __shared__ double table[128];
+  __shared__ uint32_t red[kOnchipThreads / 64];
+  __shared__ uint32_t sh_amax;
+  __shared__ uint32_t sh_last;
+  const int G = gridDim.x;
+  const int64_t lo = (int64_t)blockIdx.x * kPer * kOnchipThreads;
+  u32x4 a[kPer], b[kPer], c[kPer];
+  onchip_load<kPer>(x + lo, a);
+  onchip_load<kPer>(x + (batch > 1 ? hb_per_tensor : 0) + lo, b);
+  onchip_arrive<kPer>(a, red, ws, 0, G);
+  for (int t = 0; t < batch; t += 3) {
+    onchip_step<kPer>(x, batch, hb_per_tensor, lo, t, a, b, c, ws, G, gout, q, sf, table, red, &sh_amax);
+    if (t + 1 >= batch) break;
+    onchip_step<kPer>(x, batch, hb_per_tensor, lo, t + 1, b, c, a, ws, G, gout, q, sf, table, red, &sh_amax);
+    if (t + 2 >= batch) break;
+    onchip_step<kPer>(x, batch, hb_per_tensor, lo, t + 2, c, a, b, ws, G, gout, q, sf, table, red, &sh_amax);
+  }
+  // the last workgroup out restores the counters to zero (see fused_quantize_kernel)
+  if (threadIdx.x == 0) {
+    const uint32_t old = __hip_atomic_fetch_add(&((FusedHeader*)ws)->done, 1u, __ATOMIC_RELAXED,
+                                                __HIP_MEMORY_SCOPE_AGENT);
+    sh_last = old == (uint32_t)G - 1;
+  }
+  __syncthreads();
+  if (sh_last) {
+    const size_t words = (size_t)batch * kTensorWords;
+    uint32_t* base = ws + kFusedHeaderBytes / 4;
+    for (size_t i = threadIdx.x; i < words; i += kOnchipThreads)
+      __hip_atomic_store(base + i, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (threadIdx.x == 0)
+      __hip_atomic_store(&((FusedHeader*)ws)->done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
 // ------------------------------------------------------------ dequantize
-// Per block: 8 code bytes + 1 scale byte -> 16 bf16.  v = RN32((E2M1*s)*g):
-// the hardware decode gives the exact signed E2M1 value, E2M1*s is exact in
-// f32, one rounding for *g, then RNE to bf16.
-__device__ __forceinline__ uint32_t dequant_pair(uint32_t codes, int sel, float s, float g) {
-  f32x2 f;
-  switch (sel) {
-    case 0: f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 0); break;
-    case 1: f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 1); break;
-    case 2: f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 2); break;
-    default: f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 3); break;
-  }
-  const float a = (f.x * s) * g;
-  const float b = (f.y * s) * g;
-  const __bf16 ha = (__bf16)a, hb = (__bf16)b;
-  return (uint32_t)__builtin_bit_cast(uint16_t, ha) | ((uint32_t)__builtin_bit_cast(uint16_t, hb) << 16);
-}
-
-__device__ __forceinline__ void dequant_block(u32x2 c, uint8_t sbyte, float g, u32x4* __restrict__ yb) {
-  const float s = e4m3_value(sbyte);
-  u32x4 o0, o1;
-  o0.x = dequant_pair(c.x, 0, s, g);
-  o0.y = dequant_pair(c.x, 1, s, g);
-  o0.z = dequant_pair(c.x, 2, s, g);
-  o0.w = dequant_pair(c.x, 3, s, g);
-  o1.x = dequant_pair(c.y, 0, s, g);
-  o1.y = dequant_pair(c.y, 1, s, g);
-  o1.z = dequant_pair(c.y, 2, s, g);
-  o1.w = dequant_pair(c.y, 3, s, g);
-  yb[0] = o0;
-  yb[1] = o1;
-}
-
-__global__ void __launch_bounds__(kThreads) dequant_kernel(const u32x2* __restrict__ q, const uint8_t* __restrict__ sf,
-                                                           const float* __restrict__ gin, int64_t blk_per_tensor,
+__global__ void __launch_bounds__(kThreads) dequant_kernel(const uint32_t* __restrict__ q,
+                                                           const uint8_t* __restrict__ sf,
+                                                           const float* __restrict__ gin, int64_t hb_per_tensor,
                                                            u32x4* __restrict__ y) {
   const int t = blockIdx.y;
   const float g = gin[t];
-  const int64_t base = (int64_t)t * blk_per_tensor;
-  const u32x2* qt = q + base;
-  const uint8_t* st = sf + base;
-  u32x4* yt = y + 2 * base;
-  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  const int64_t off = (int64_t)t * hb_per_tensor;
+  const uint32_t* qt = q + off;
+  const uint8_t* st = sf + off / 2;
+  u32x4* yt = y + off;
+  const int64_t step = (int64_t)gridDim.x * kThreads;
   int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  for (; i + stride < blk_per_tensor; i += 2 * stride) {
-    const u32x2 c0 = qt[i];
-    const u32x2 c1 = qt[i + stride];
-    const uint8_t s0 = st[i], s1 = st[i + stride];
-    dequant_block(c0, s0, g, yt + 2 * i);
-    dequant_block(c1, s1, g, yt + 2 * (i + stride));
+  for (; i + (kU - 1) * step < hb_per_tensor; i += kU * step) {
+    uint32_t c[kU];
+    uint8_t s[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      c[u] = __builtin_nontemporal_load(qt + i + u * step);
+      s[u] = st[(i + u * step) >> 1];
+    }
+#pragma unroll
+    for (int u = 0; u < kU; ++u) yt[i + u * step] = dequant_half(c[u], e4m3_value(s[u]), g);
   }
-  for (; i < blk_per_tensor; i += stride) dequant_block(qt[i], st[i], g, yt + 2 * i);
+  for (; i < hb_per_tensor; i += step) yt[i] = dequant_half(qt[i], e4m3_value(st[i >> 1]), g);
 }
 
 }  // namespace nvfp4
@@ -213,23 +491,22 @@ namespace {
 
 using namespace nvfp4;
 
-// Workgroups per tensor for a streaming launch: enough to fill the GPU
-// (~8 workgroups per CU overall) but at least 16 blocks per thread.
-int wgs_per_tensor(int64_t batch, int64_t blk_per_tensor) {
-  const int64_t target = (int64_t)nvfp4host::num_cus() * 8;
+constexpr int kMaxPartials = 2048;
+
+// Workgroups per tensor for a streaming launch: ~16 workgroups per CU in all,
+// but at least kU half blocks per lane.
+int wgs_per_tensor(int64_t batch, int64_t hb_per_tensor) {
+  const int64_t target = (int64_t)nvfp4host::num_cus() * 16;
   int64_t per = (target + batch - 1) / batch;
-  const int64_t need = (blk_per_tensor + (int64_t)kThreads * 16 - 1) / ((int64_t)kThreads * 16);
-  per = std::min(per, need);
-  per = std::max<int64_t>(per, 1);
+  const int64_t need = (hb_per_tensor + (int64_t)kThreads * kU - 1) / ((int64_t)kThreads * kU);
+  per = std::max<int64_t>(std::min(per, need), 1);
   return (int)std::min<int64_t>(per, 65535);
 }
 
-constexpr int kMaxPartials = 2048;
-
 int amax_wgs_per_tensor(int64_t batch, int64_t vec_per_tensor) {
-  const int64_t target = (int64_t)nvfp4host::num_cus() * 8;
+  const int64_t target = (int64_t)nvfp4host::num_cus() * 32;
   int64_t per = (target + batch - 1) / batch;
-  const int64_t need = (vec_per_tensor + (int64_t)kThreads * 16 - 1) / ((int64_t)kThreads * 16);
+  const int64_t need = (vec_per_tensor + (int64_t)kThreads * 4 - 1) / ((int64_t)kThreads * 4);
   per = std::min<int64_t>(std::min(per, need), kMaxPartials);
   return (int)std::max<int64_t>(per, 1);
 }
@@ -241,6 +518,35 @@ nvfp4_status check_shape(int64_t batch, int64_t rows, int64_t cols) {
   return NVFP4_OK;
 }
 
+size_t fused_header_bytes(int64_t batch) { return kFusedHeaderBytes + (size_t)batch * kTensorWords * 4; }
+
+// Co-resident workgroups for the persistent launch (cached per device).
+int fused_grid(int64_t hb_per_tensor) {
+  static int per_cu = -1;
+  if (per_cu < 0) {
+    int nb = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, fused_quantize_kernel, kThreads, 0) != hipSuccess || nb < 1)
+      nb = 1;
+    per_cu = std::min(nb, 4);
+  }
+  int64_t g = (int64_t)nvfp4host::num_cus() * per_cu;
+  const int64_t need = std::max<int64_t>(1, (hb_per_tensor + 255) / 256);
+  return (int)std::max<int64_t>(1, std::min(g, need));
+}
+
+// Half blocks per thread for the on-chip persistent launch: the smallest
+// count whose 512-thread slices tile a tensor exactly with at most one
+// workgroup per CU, or 0 when no count does (the tensor is too large to hold
+// on chip, or its size does not divide) -- the streaming launch runs then.
+int onchip_per_thread(int64_t hb_per_tensor) {
+  const int64_t cus = nvfp4host::num_cus();
+  for (int per = 1; per <= kOnchipMaxPer; ++per) {
+    const int64_t slice = (int64_t)per * kOnchipThreads;
+    if (hb_per_tensor % slice == 0 && hb_per_tensor / slice <= cus) return per;
+  }
+  return 0;
+}
+
 }  // namespace
 
 extern "C" {
@@ -249,16 +555,16 @@ size_t nvfp4_quantize_workspace_bytes(int64_t batch, int64_t rows, int64_t cols)
   if (batch <= 0 || rows < 0 || cols < 0) return 0;
   (void)rows;
   (void)cols;
-  // per-tensor partial maxima of pass 1, plus one 256-byte header reserved
-  // for the persistent launch's counters.
-  return 256 + (size_t)batch * kMaxPartials * sizeof(uint32_t);
+  // fused header, then the two-kernel path's per-tensor partial maxima
+  const size_t head = (fused_header_bytes(batch) + 255) & ~(size_t)255;
+  return head + (size_t)batch * kMaxPartials * sizeof(uint32_t);
 }
 
 nvfp4_status nvfp4_quantize(const uint16_t* x, int64_t batch, int64_t rows, int64_t cols, uint8_t* q, uint8_t* sf,
                             float* g, void* workspace, size_t workspace_bytes, uint32_t flags, void* stream) {
   nvfp4_status st = check_shape(batch, rows, cols);
   if (st) return st;
-  if (flags != NVFP4_TWO_KERNEL) return NVFP4_ENOTSUP;   // the persistent launch is not built yet
+  if (flags != NVFP4_TWO_KERNEL && flags != NVFP4_FUSED) return NVFP4_ENOTSUP;
   if (batch == 0) return NVFP4_OK;
   if (!g) return NVFP4_EINVAL;
   const int64_t n = rows * cols;
@@ -269,14 +575,64 @@ nvfp4_status nvfp4_quantize(const uint16_t* x, int64_t batch, int64_t rows, int6
   if (!nvfp4host::aligned16(workspace)) return NVFP4_EALIGN;
   if ((st = nvfp4host::check_device())) return st;
   hipStream_t s = (hipStream_t)stream;
-  uint32_t* partial = (uint32_t*)((char*)workspace + 256);
-  const int64_t vec = n / 8, blk = n / kBlock;
+  const int64_t hb = n / 8;
+  if (flags == NVFP4_FUSED) {
+    const int onchip_per = onchip_per_thread(hb);
+    if (onchip_per > 0) {
+      const u32x4* xa = (const u32x4*)x;
+      int bt = (int)batch;
+      uint32_t* ws = (uint32_t*)workspace;
+      uint32_t* qa = (uint32_t*)q;
+      void* args[] = {&xa, &bt, (void*)&hb, &ws, &g, &qa, &sf};
+      const int64_t slice = (int64_t)onchip_per * kOnchipThreads;
+      const int G = (int)((hb + slice - 1) / slice);
+      const void* fn = nullptr;
+      const void* fns[kOnchipMaxPer] = {
+          (const void*)fused_onchip_kernel<1>,
+          (const void*)fused_onchip_kernel<2>,
+          (const void*)fused_onchip_kernel<3>,
+          (const void*)fused_onchip_kernel<4>,
+          (const void*)fused_onchip_kernel<5>,
+          (const void*)fused_onchip_kernel<6>,
+          (const void*)fused_onchip_kernel<7>,
+          (const void*)fused_onchip_kernel<8>,
+          (const void*)fused_onchip_kernel<9>,
+          (const void*)fused_onchip_kernel<10>,
+          (const void*)fused_onchip_kernel<11>,
+          (const void*)fused_onchip_kernel<12>,
+          (const void*)fused_onchip_kernel<13>,
+          (const void*)fused_onchip_kernel<14>,
+      };
+      fn = fns[onchip_per - 1];
+      hipError_t e = hipLaunchCooperativeKernel(fn, dim3(G), dim3(kOnchipThreads), args, 0, s);
+      if (e != hipSuccess) {
+        nvfp4host::set_hip_error(e);
+        return NVFP4_EHIP;
+      }
+      return NVFP4_OK;
+    }
+    const int G = fused_grid(hb);
+    const u32x4* xa = (const u32x4*)x;
+    int bt = (int)batch;
+    uint32_t* ws = (uint32_t*)workspace;
+    uint32_t* qa = (uint32_t*)q;
+    void* args[] = {&xa, &bt, (void*)&hb, &ws, &g, &qa, &sf};
+    hipError_t e = hipLaunchCooperativeKernel((const void*)fused_quantize_kernel, dim3(G), dim3(kThreads), args, 0, s);
+    if (e != hipSuccess) {
+      nvfp4host::set_hip_error(e);
+      return NVFP4_EHIP;
+    }
+    return NVFP4_OK;
+  }
+  const size_t head = (fused_header_bytes(batch) + 255) & ~(size_t)255;
+  uint32_t* partial = (uint32_t*)((char*)workspace + head);
+  const int64_t vec = hb;
   const int p1 = amax_wgs_per_tensor(batch, vec);
   amax_partial_kernel<<<dim3(p1, (unsigned)batch), kThreads, 0, s>>>((const u32x4*)x, vec, partial);
   NVFP4_LAUNCH_CHECK();
-  const int p2 = wgs_per_tensor(batch, blk);
-  encode_kernel<true><<<dim3(p2, (unsigned)batch), kThreads, 0, s>>>((const u32x4*)x, blk, partial, p1, nullptr, g,
-                                                                      (u32x2*)q, sf);
+  const int p2 = wgs_per_tensor(batch, hb);
+  encode_kernel<true><<<dim3(p2, (unsigned)batch), kThreads, 0, s>>>((const u32x4*)x, hb, partial, p1, nullptr, g,
+                                                                      (uint32_t*)q, sf);
   NVFP4_LAUNCH_CHECK();
   return NVFP4_OK;
 }
@@ -292,10 +648,10 @@ nvfp4_status nvfp4_quantize_with_scale(const uint16_t* x, int64_t batch, int64_t
   if ((reinterpret_cast<uintptr_t>(g) & 3u) != 0) return NVFP4_EALIGN;
   if ((st = nvfp4host::check_device())) return st;
   hipStream_t s = (hipStream_t)stream;
-  const int64_t blk = n / kBlock;
-  const int p2 = wgs_per_tensor(batch, blk);
-  encode_kernel<false><<<dim3(p2, (unsigned)batch), kThreads, 0, s>>>((const u32x4*)x, blk, nullptr, 0, g, nullptr,
-                                                                       (u32x2*)q, sf);
+  const int64_t hb = n / 8;
+  const int p2 = wgs_per_tensor(batch, hb);
+  encode_kernel<false><<<dim3(p2, (unsigned)batch), kThreads, 0, s>>>((const u32x4*)x, hb, nullptr, 0, g, nullptr,
+                                                                       (uint32_t*)q, sf);
   NVFP4_LAUNCH_CHECK();
   return NVFP4_OK;
 }
@@ -311,9 +667,9 @@ nvfp4_status nvfp4_dequantize(const uint8_t* q, const uint8_t* sf, const float* 
   if ((reinterpret_cast<uintptr_t>(g) & 3u) != 0) return NVFP4_EALIGN;
   if ((st = nvfp4host::check_device())) return st;
   hipStream_t s = (hipStream_t)stream;
-  const int64_t blk = n / kBlock;
-  const int p = wgs_per_tensor(batch, blk);
-  dequant_kernel<<<dim3(p, (unsigned)batch), kThreads, 0, s>>>((const u32x2*)q, sf, g, blk, (u32x4*)y);
+  const int64_t hb = n / 8;
+  const int p = wgs_per_tensor(batch, hb);
+  dequant_kernel<<<dim3(p, (unsigned)batch), kThreads, 0, s>>>((const uint32_t*)q, sf, g, hb, (u32x4*)y);
   NVFP4_LAUNCH_CHECK();
   return NVFP4_OK;
 }

@@ -7,8 +7,8 @@
 // (v_cvt_scalef32_pk_fp4_f32 rounds f32 to E2M1 to nearest-even with
 // saturation, keeping the sign of zeros and underflows; v_cvt_pk_fp8_f32
 // rounds to OCP E4M3 to nearest-even for inputs up to 464, so inputs are
-// clamped to 448 first) and through a per-tensor reciprocal table whose
-// exactness is established when the table is built (see build_entry).
+// clamped to 448 first) and through fp64 reciprocals of the per-block
+// divisors (see "exact quotients" below).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -29,8 +29,8 @@ typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kBlock = 16;          // values per E4M3 block scale
-constexpr int kThreads = 256;       // threads per workgroup of the streaming kernels
+constexpr int kBlock = 16;             // values per E4M3 block scale
+constexpr int kThreads = 256;          // threads per workgroup of the streaming kernels
 constexpr float kGlobalDiv = 2688.0f;  // 6 (E2M1 max) * 448 (E4M3 max)
 
 // ---------------------------------------------------------------- bf16 words
@@ -69,114 +69,91 @@ __device__ __forceinline__ uint32_t fp4_pair(uint32_t old, float a, float b) {
   return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, a, b, 1.0f, sel);
 }
 
-// ---------------------------------------------------------------- tables
-// Per-tensor encode table, one entry per block-scale byte (0..126).
+// ---------------------------------------------------------------- exact quotients
+// Every quotient of the recipe has the form RN32(a / d) with a a bf16 value
+// (8 significant bits) and d an fp32 value (24 significant bits): the block
+// scale quotient bamax / d6 and the element quotient |x| / d.  Such a
+// quotient is either exactly representable in fp32 or lies at least 2^-49
+// (relative) away from every fp32 rounding midpoint: writing a = A 2^i,
+// d = D 2^j with A, D odd, a/d is dyadic only when D divides A (and then has
+// at most 8 significant bits); otherwise, for a midpoint m 2^(e-24) of the
+// binade [2^e, 2^(e+1)), (a/d - m 2^(e-24)) D 2^j is a nonzero multiple of
+// 2^min(i, e-24+j), which bounds the gap below by 2^-49 (a/d) either way.
+// So y64 = RN64(a * RN64(1/d)), whose relative error is below 2^-52, rounds
+// once to exactly RN32(a / d) -- E2M1 / E4M3 ties included -- with no
+// division per element and no exception path.  fp64 multiplies and
+// conversions run at the full VALU rate on gfx950.
 //
-// Element code = E2M1(RN32(x / d)) with d = RN32(s*g).  The fast path uses
-// y' = RN32(x * r), r = RN32(1/d), which differs from RN32(x/d) by < 2^-22.9
-// relative.  E2M1 rounding of y only depends on where y lies against the
-// seven grid midpoints b (0.25 ... 5), so y' gives the same code unless
-// |x/d - b| <= 2^-22 b for some b.  Because x is bf16 (8 significant bits),
-// for a given d at most one bf16 magnitude lies in each such window: the
-// bf16 nearest to P = d*b (computed exactly in fp64).  build_entry records up
-// to two such "danger" magnitudes; blocks that contain one are re-encoded by
-// exact division.  Entries whose d is outside [2^-125, 2^125] (so 1/d could
-// lose precision) are marked fully slow (r < 0).  d == 0 or +inf gives r = 0:
-// x * 0 is a signed zero, which is exactly the recipe's code there.
-struct Entry {
-  float r;          // reciprocal of d (0: zero codes; < 0: exact division for the whole block)
-  uint32_t danger;  // two bf16 magnitude patterns (low, high half); 0xFFFF = none
-};
-
-__device__ inline Entry build_entry(uint32_t sbyte, float g) {
-  Entry e;
-  e.danger = 0xffffffffu;
-  const float s = e4m3_value(sbyte);
-  const float d = s * g;
-  if (d == 0.0f || __builtin_isinf(d)) { e.r = 0.0f; return e; }
-  if (!(d >= 0x1p-125f && d <= 0x1p125f)) { e.r = -1.0f; return e; }
-  e.r = 1.0f / d;   // correctly rounded (default HIP division)
-  const float bnd[7] = {0.25f, 0.75f, 1.25f, 1.75f, 2.5f, 3.5f, 5.0f};
-  int nd = 0;
-#pragma unroll
-  for (int k = 0; k < 7; ++k) {
-    const double P = (double)d * (double)bnd[k];       // exact (<= 27 significant bits)
-    const uint64_t u = (uint64_t)__double_as_longlong(P);
-    const int E = (int)((u >> 52) & 0x7ff) - 1023;
-    if (E < -126) { e.r = -1.0f; return e; }
-    const uint64_t low = u & ((1ull << 45) - 1);       // bits below the bf16 mantissa
-    const uint64_t dist = low < (1ull << 44) ? low : (1ull << 45) - low;
-    if (dist <= (1ull << 31)) {                        // a bf16 lies within 2^-22 of P
-      const uint64_t ur = u + (1ull << 44);            // nearest bf16 grid point
-      const int Er = (int)((ur >> 52) & 0x7ff) - 1023;
-      if (Er > 127) continue;                          // beyond the largest finite bf16
-      const uint32_t A = ((uint32_t)(Er + 127) << 7) | (uint32_t)((ur >> 45) & 0x7f);
-      if (nd == 2) { e.r = -1.0f; return e; }
-      e.danger = nd == 0 ? ((e.danger & 0xffff0000u) | A) : ((e.danger & 0xffffu) | (A << 16));
-      ++nd;
-    }
-  }
-  return e;
+// Per-tensor table: one fp64 reciprocal per block-scale byte (0..126).
+// d == 0 (or +inf, from a huge caller scale) stores 0: x * 0 is the signed
+// zero that the recipe prescribes there (x / inf = 0 too).
+__device__ inline double recip_entry(uint32_t sbyte, float g) {
+  const float d = e4m3_value(sbyte) * g;            // RN32(s * g)
+  if (d == 0.0f || __builtin_isinf(d)) return 0.0;
+  return 1.0 / (double)d;                           // RN64, correctly rounded
 }
 
-// Block-scale byte of a block from its amax (bf16 magnitude bits).
-// Exact recipe: s = E4M3_RNE_SAT(RN32(bamax / d6)).  Fast path: RN32(bamax*r6)
-// is within 2^-22.9 of the true quotient, so it rounds to the same E4M3 value
-// unless it lies within 16 ulps of an E4M3 midpoint (mantissa pattern
-// 1000...0 below the 3 kept bits) or in the subnormal E4M3 range; those take
-// the exact division.  `exact_all` forces division (d6 outside [2^-125,2^125]).
-__device__ __forceinline__ uint32_t block_scale_byte(uint32_t bam_bits, float d6, float r6, bool exact_all,
-                                                     bool zero_all) {
-  if (zero_all) return 0u;
+// RN32 of an fp64 value (one rounding; fp32 denormals are kept).
+__device__ __forceinline__ float rn32(double v) { return (float)v; }
+
+// Reciprocal of d6 = RN32(6 g) for the block-scale quotients; 0 when d6 is 0
+// (all scales zero) or +inf (bamax / inf = 0).
+__device__ __forceinline__ double recip_d6(float g) {
+  const float d6 = 6.0f * g;
+  if (d6 == 0.0f || __builtin_isinf(d6)) return 0.0;
+  return 1.0 / (double)d6;
+}
+
+// Block-scale byte from the block amax (bf16 magnitude bits):
+// s = E4M3_RNE_SAT(RN32(bamax / d6)).
+__device__ __forceinline__ uint32_t block_scale_byte(uint32_t bam_bits, double r6) {
   const float bam = __uint_as_float(bam_bits << 16);
-  float qv = bam * r6;
-  const uint32_t qb = __float_as_uint(qv);
-  const int mid = (int)(qb & 0xfffffu) - 0x80000;
-  const bool near = (mid >= -16 && mid <= 16) || (qv > 0.0f && qv < 0x1p-6f);
-  if (exact_all || near) qv = bam / d6;
-  return e4m3_rne_sat(qv);
+  return e4m3_rne_sat(rn32((double)bam * r6));
 }
 
-// Encodes one 16-value block held as 8 words (element 2i in the low half of
-// w[i]) given its table entry; returns the 8 code bytes as two words.
-__device__ __forceinline__ void encode_block(const uint32_t (&w)[8], const Entry& en, uint32_t sbyte, float g,
-                                             uint32_t& c0, uint32_t& c1) {
-  const float r = en.r;
-  if (r >= 0.0f) {
-    c0 = fp4_pair<0>(0u, bf16_lo(w[0]) * r, bf16_hi(w[0]) * r);
-    c0 = fp4_pair<1>(c0, bf16_lo(w[1]) * r, bf16_hi(w[1]) * r);
-    c0 = fp4_pair<2>(c0, bf16_lo(w[2]) * r, bf16_hi(w[2]) * r);
-    c0 = fp4_pair<3>(c0, bf16_lo(w[3]) * r, bf16_hi(w[3]) * r);
-    c1 = fp4_pair<0>(0u, bf16_lo(w[4]) * r, bf16_hi(w[4]) * r);
-    c1 = fp4_pair<1>(c1, bf16_lo(w[5]) * r, bf16_hi(w[5]) * r);
-    c1 = fp4_pair<2>(c1, bf16_lo(w[6]) * r, bf16_hi(w[6]) * r);
-    c1 = fp4_pair<3>(c1, bf16_lo(w[7]) * r, bf16_hi(w[7]) * r);
-  }
-  if (r < 0.0f || en.danger != 0xffffffffu) {
-    // exact path: y = RN32(x / d) for every element (fully slow), or only for
-    // the recorded danger magnitudes.
-    const float d = e4m3_value(sbyte) * g;
-    const bool all = r < 0.0f;
-    const uint32_t A0 = en.danger & 0xffffu, A1 = en.danger >> 16;
-    uint32_t out[2] = {c0, c1};
-    if (all) { out[0] = 0u; out[1] = 0u; }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const uint32_t xb = h ? (w[i] >> 16) : (w[i] & 0xffffu);
-        const uint32_t ab = xb & 0x7fffu;
-        if (all || ab == A0 || ab == A1) {
-          const float x = __uint_as_float(xb << 16);
-          const uint32_t code = fp4_pair<0>(0u, x / d, 0.0f) & 0xfu;
-          const int sh = 8 * (i & 3) + 4 * h;
-          out[i >> 2] = (out[i >> 2] & ~(0xfu << sh)) | (code << sh);
-        }
-      }
-    }
-    c0 = out[0];
-    c1 = out[1];
-  }
+// RN32(x / d) for the two bf16 halves of a word, sign kept.
+__device__ __forceinline__ float q_lo(uint32_t w, double r) { return rn32((double)bf16_lo(w) * r); }
+__device__ __forceinline__ float q_hi(uint32_t w, double r) { return rn32((double)bf16_hi(w) * r); }
+
+// ---------------------------------------------------------------- half blocks
+// Streaming kernels give each lane HALF a block (8 values = 16 bytes of bf16),
+// so consecutive lanes touch consecutive 16-byte chunks and every load and
+// store instruction of a wave covers one contiguous run.  Lanes 2j and 2j+1
+// hold the two halves of one block; they swap partial maxima with a DPP
+// quad permutation.
+__device__ __forceinline__ uint32_t half_absmax_bits(const u32x4 v) {
+  uint32_t m = pk_absmax(pk_absmax(pk_absmax(pk_absmax(0u, v.x), v.y), v.z), v.w);
+  return halves_max(m);
+}
+__device__ __forceinline__ uint32_t pair_max(uint32_t m) {
+  // quad_perm(1,0,3,2): lane i reads lane i^1
+  const uint32_t o = (uint32_t)__builtin_amdgcn_mov_dpp((int)m, 0xB1, 0xF, 0xF, false);
+  return m > o ? m : o;
+}
+
+// Encodes 8 values (one half block) into 4 code bytes (element 2i in the low
+// nibble of byte i) given the block's reciprocal r = RN64(1/d).
+__device__ __forceinline__ uint32_t encode_half(const u32x4 w, double r) {
+  uint32_t c = fp4_pair<0>(0u, q_lo(w.x, r), q_hi(w.x, r));
+  c = fp4_pair<1>(c, q_lo(w.y, r), q_hi(w.y, r));
+  c = fp4_pair<2>(c, q_lo(w.z, r), q_hi(w.z, r));
+  return fp4_pair<3>(c, q_lo(w.w, r), q_hi(w.w, r));
+}
+
+// Dequantizes 4 code bytes (8 values) with scale s and tensor scale g into 8
+// bf16: RN32((E2M1 * s) * g) -> bf16 RNE.  The hardware decode yields the
+// exact signed E2M1 value; E2M1 * s is exact in fp32.
+__device__ __forceinline__ uint32_t deq_pair_bits(f32x2 f, float s, float g) {
+  const __bf16 ha = (__bf16)((f.x * s) * g), hb = (__bf16)((f.y * s) * g);
+  return (uint32_t)__builtin_bit_cast(uint16_t, ha) | ((uint32_t)__builtin_bit_cast(uint16_t, hb) << 16);
+}
+__device__ __forceinline__ u32x4 dequant_half(uint32_t codes, float s, float g) {
+  u32x4 o;
+  o.x = deq_pair_bits(__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 0), s, g);
+  o.y = deq_pair_bits(__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 1), s, g);
+  o.z = deq_pair_bits(__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 2), s, g);
+  o.w = deq_pair_bits(__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 3), s, g);
+  return o;
 }
 
 // ---------------------------------------------------------------- reductions
@@ -188,6 +165,8 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
   }
   return v;
 }
+
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)); }
 
 }  // namespace nvfp4
 

@@ -18,56 +18,51 @@
 
 namespace nvfp4 {
 
-struct TensorScalesKV {
-  float g, d6, r6;
-  bool zero_all, exact_all;
-};
-
-__device__ __forceinline__ TensorScalesKV kv_scales(float g) {
-  TensorScalesKV ts;
-  ts.g = g;
-  ts.d6 = 6.0f * g;
-  ts.zero_all = ts.d6 == 0.0f;
-  ts.exact_all = !(ts.d6 >= 0x1p-125f && ts.d6 <= 0x1p125f);
-  ts.r6 = (ts.zero_all || ts.exact_all) ? 0.0f : 1.0f / ts.d6;
-  return ts;
-}
-
-// grid (tiles, kv_heads, 2*layers): z = 2*layer + (0: K, 1: V).
-__global__ void __launch_bounds__(kThreads) kv_append_kernel(nvfp4_kv_cache c, int64_t start, int64_t n,
+// grid (tiles, kv_heads, 2*layers): z = 2*layer + (0: K, 1: V).  Work unit:
+// half block j of the chunk's rows for this (layer, head), j in [0, n*R),
+// R = head_dim/8 half blocks per token row.  Lane j of a wave chunk maps to
+// token j / R, half block j % R (shifts when kPow2).  Input rows of one head
+// are head_dim*kv_heads apart; cache rows of consecutive tokens are
+// contiguous, so the code stores of a wave form one run.
+template <bool kPow2>
+__global__ void __launch_bounds__(kThreads) kv_append_kernel(nvfp4_kv_cache c, int64_t start, int64_t n, int log2r,
                                                              const u32x4* __restrict__ k_new,
                                                              const u32x4* __restrict__ v_new) {
   const int h = blockIdx.y;
   const int l = blockIdx.z >> 1;
   const bool is_v = blockIdx.z & 1;
-  const int H = c.kv_heads, D = c.head_dim, bpr = D / kBlock;
+  const int H = c.kv_heads;
+  const uint32_t R = (uint32_t)c.head_dim / 8;
   const float g = (is_v ? c.v_g : c.k_g)[l * H + h];
-  __shared__ Entry table[128];
-  for (uint32_t j = threadIdx.x; j < 127u; j += kThreads) table[j] = build_entry(j, g);
+  __shared__ double table[128];
+  for (uint32_t j = threadIdx.x; j < 127u; j += kThreads) table[j] = recip_entry(j, g);
   __syncthreads();
-  const TensorScalesKV ts = kv_scales(g);
-  const u32x4* src = is_v ? v_new : k_new;                     // [L][n][H][D] bf16, 2 x u32x4 per block
-  u32x2* dq = (u32x2*)(is_v ? c.v : c.k);                       // 8 bytes of codes per block
-  uint8_t* dsf = is_v ? c.v_sf : c.k_sf;
-  const int64_t row0 = ((int64_t)l * H + h) * c.capacity + start;   // cache row of token 0
-  const int64_t nblk = n * bpr;
-  for (int64_t b = (int64_t)blockIdx.x * kThreads + threadIdx.x; b < nblk; b += (int64_t)gridDim.x * kThreads) {
-    const int64_t t = b / bpr;
-    const int j = (int)(b - t * bpr);
-    const int64_t in_blk = (((int64_t)l * n + t) * H + h) * bpr + j;
-    uint32_t w[8];
-    const u32x4 a = src[2 * in_blk], bb = src[2 * in_blk + 1];
-    w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
-    w[4] = bb.x; w[5] = bb.y; w[6] = bb.z; w[7] = bb.w;
-    uint32_t am = 0;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) am = pk_absmax(am, w[i]);
-    const uint32_t sbyte = block_scale_byte(halves_max(am), ts.d6, ts.r6, ts.exact_all, ts.zero_all);
-    uint32_t c0, c1;
-    encode_block(w, table[sbyte], sbyte, g, c0, c1);
-    const int64_t out_blk = (row0 + t) * bpr + j;
-    dq[out_blk] = u32x2{c0, c1};
-    dsf[out_blk] = (uint8_t)sbyte;
+  const double r6 = recip_d6(g);
+  const u32x4* src = (is_v ? v_new : k_new) + ((int64_t)l * n * H + h) * R;    // token 0 of (l, h)
+  uint32_t* dq = (uint32_t*)(is_v ? c.v : c.k) + (((int64_t)l * H + h) * c.capacity + start) * R;
+  uint8_t* dsf = (is_v ? c.v_sf : c.k_sf) + (((int64_t)l * H + h) * c.capacity + start) * (R / 2);
+  const int64_t total = n * (int64_t)R;
+  const int lane = threadIdx.x & 63;
+  const int64_t in_stride = (int64_t)H * R;                                     // between tokens
+  for (int64_t base = ((int64_t)blockIdx.x * (kThreads / 64) + wave_id()) * 64; base < total;
+       base += (int64_t)gridDim.x * kThreads) {
+    const int64_t j = base + lane;
+    const bool ok = j < total;
+    uint32_t t, r;
+    if (kPow2) {
+      t = (uint32_t)(j >> log2r);
+      r = (uint32_t)j & (R - 1);
+    } else {
+      t = (uint32_t)j / R;
+      r = (uint32_t)j - t * R;
+    }
+    const u32x4 v = ok ? src[(int64_t)t * in_stride + r] : u32x4{0u, 0u, 0u, 0u};
+    const uint32_t sbyte = block_scale_byte(pair_max(half_absmax_bits(v)), r6);
+    const uint32_t code = encode_half(v, table[sbyte]);
+    if (ok) {
+      dq[j] = code;
+      if ((lane & 1) == 0) dsf[j >> 1] = (uint8_t)sbyte;
+    }
   }
 }
 
@@ -217,11 +212,20 @@ nvfp4_status nvfp4_kv_append(const nvfp4_kv_cache* c, int64_t start, int64_t n, 
   if (!k_new || !v_new) return NVFP4_EINVAL;
   if (!nvfp4host::aligned16(k_new) || !nvfp4host::aligned16(v_new)) return NVFP4_EALIGN;
   if ((st = nvfp4host::check_device())) return st;
-  const int64_t blocks = n * (c->head_dim / kBlock);
+  const int R = c->head_dim / 8;
+  if (n > INT32_MAX / R) return NVFP4_EINVAL;                      // 32-bit token index per lane
+  const int64_t halves = n * R;
   const int64_t others = (int64_t)c->kv_heads * 2 * c->layers;
-  const int tiles = tiles_for(blocks, others);
-  kv_append_kernel<<<dim3(tiles, c->kv_heads, 2 * c->layers), kThreads, 0, (hipStream_t)stream>>>(
-      *c, start, n, (const u32x4*)k_new, (const u32x4*)v_new);
+  const int tiles = tiles_for(halves / 2, others);
+  const bool pow2 = (R & (R - 1)) == 0;
+  const int log2r = __builtin_ctz((unsigned)R);
+  const dim3 grid(tiles, c->kv_heads, 2 * c->layers);
+  if (pow2)
+    kv_append_kernel<true><<<grid, kThreads, 0, (hipStream_t)stream>>>(*c, start, n, log2r, (const u32x4*)k_new,
+                                                                      (const u32x4*)v_new);
+  else
+    kv_append_kernel<false><<<grid, kThreads, 0, (hipStream_t)stream>>>(*c, start, n, log2r, (const u32x4*)k_new,
+                                                                       (const u32x4*)v_new);
   NVFP4_LAUNCH_CHECK();
   return NVFP4_OK;
 }

@@ -11,13 +11,14 @@ from gpu_util import Guarded, bits, bf16_from_floats, from_bits, np_
 pytestmark = pytest.mark.gpu
 
 nv = pytest.importorskip("nvfp4_block_scaled_06_amd")
-FLAGS = ["two_kernel"]
+FLAGS = ["two_kernel", "fused"]
 
 
 def assert_quantize_matches(x_gpu, flags="two_kernel", label=""):
     xb = bits(x_gpu)
     q, sf, g = nv.quantize(x_gpu, flags=flags)
     torch.cuda.synchronize()
+    assert not torch.isnan(g).any(), f"{label}: persistent launch reported a wait timeout"
     oq, osf, og = oracle.quantize(xb)
     assert np.array_equal(np_(g).view(np.uint32), og.view(np.uint32)), f"{label}: g {np_(g)} vs {og}"
     bad = np.argwhere(np_(sf) != osf)
@@ -201,3 +202,18 @@ def test_activations_full_size():
         assert np.array_equal(np_(sf), osf)
         assert np.array_equal(np_(q), oq)
         del q, sf
+
+
+def test_fused_workspace_is_left_clean():
+    """The persistent launch restores its counters to zero: many back-to-back
+    calls on one workspace, with different batch sizes, all give the two-kernel bytes."""
+    gen = torch.Generator().manual_seed(21)
+    ws = nv.make_workspace(8, 64, 512)
+    for it, b in enumerate([8, 3, 8, 1, 5] * 3):
+        x = (torch.randn((b, 64, 512), generator=gen) * (it + 1)).to(torch.bfloat16).cuda()
+        a = nv.quantize(x, flags="fused", workspace=ws[:nv.workspace_bytes(b, 64, 512)])
+        r = nv.quantize(x, flags="two_kernel")
+        for u, v in zip(a, r):
+            assert torch.equal(u, v), f"iteration {it}"
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(ws[:nv.workspace_bytes(8, 64, 512) - 8 * 2048 * 4]).item() == 0
