@@ -165,6 +165,110 @@ __global__ void __launch_bounds__(kThreads) kv_decode_qk_kernel(nvfp4_kv_cache c
   }
 }
 
+// Decode-step QK, register-resident queries.  Each token's head_dim K
+// values are split over LPT = head_dim/32 consecutive lanes (32 values = 16
+// code bytes + 2 scale bytes per lane), so a wave reads 64/LPT tokens' codes
+// as one contiguous run.  Every lane keeps its 32-value slice of the GRP
+// query heads of this KV head (GQA) in registers as bf16 pairs.  K is decoded
+// exactly to bf16 pairs (E2M1 values; v_cvt_scalef32_pk_bf16_fp4) and
+// contracted with v_dot2_f32_bf16 (bf16 x bf16 products are exact in fp32);
+// each 16-value block's partial is scaled by its s, the LPT lanes of a token
+// are summed with DPP butterflies, and g is applied once per logit.
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+template <int sel>
+__device__ __forceinline__ bf16x2 kpair(uint32_t codes) {
+  return __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, 1.0f, sel);
+}
+
+template <int LPT>
+__device__ __forceinline__ float lane_group_sum(float v) {
+  if (LPT >= 2) v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false));
+  if (LPT >= 4) v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false));
+  if (LPT >= 8) v += __shfl_xor(v, 4, 64);
+  return v;
+}
+
+template <int LPT, int GRP>
+__global__ void __launch_bounds__(kThreads) kv_qk_kernel(nvfp4_kv_cache c, const uint32_t* __restrict__ q,
+                                                         int q_heads, int64_t n, float* __restrict__ logits) {
+  constexpr int TPW = 64 / LPT;                        // tokens per wave
+  const int h = blockIdx.y, l = blockIdx.z;
+  const int H = c.kv_heads;
+  const int lane = threadIdx.x & 63;
+  const int j = lane % LPT;                            // 32-value chunk of the token
+  // query slices: q[l][h*GRP + g][32 j .. 32 j + 32) as 16 bf16 pairs per head
+  uint32_t qv[GRP][16];
+#pragma unroll
+  for (int g = 0; g < GRP; ++g) {
+    const u32x4* qp = (const u32x4*)(q + ((int64_t)l * q_heads + h * GRP + g) * (LPT * 16) + j * 16);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const u32x4 w = qp[i];
+      qv[g][4 * i] = w.x; qv[g][4 * i + 1] = w.y; qv[g][4 * i + 2] = w.z; qv[g][4 * i + 3] = w.w;
+    }
+  }
+  const float gk = c.k_g[l * H + h];
+  const int64_t row0 = ((int64_t)l * H + h) * c.capacity;
+  const u32x4* kc = (const u32x4*)c.k + row0 * LPT;                 // 16 code bytes per lane
+  const uint16_t* ks = (const uint16_t*)c.k_sf + row0 * LPT;         // 2 scale bytes per lane
+  float* out = logits + ((int64_t)l * q_heads + h * GRP) * n;
+  const int64_t tok_step = (int64_t)gridDim.x * (kThreads / 64) * TPW;
+  const int64_t t_lane = lane / LPT;
+  // two token groups per trip (independent dot chains); the next trip's codes
+  // and scales are already in flight while this trip is contracted
+  int64_t t = ((int64_t)blockIdx.x * (kThreads / 64) + wave_id()) * TPW + t_lane;
+  u32x4 cwn[2];
+  uint32_t swn[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int64_t tu = t + u * tok_step;
+    cwn[u] = tu < n ? kc[tu * LPT + j] : u32x4{0u, 0u, 0u, 0u};
+    swn[u] = tu < n ? ks[tu * LPT + j] : 0u;
+  }
+  for (; t - t_lane < n; t += 2 * tok_step) {
+    u32x4 cw[2];
+    uint32_t sw[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      cw[u] = cwn[u];
+      sw[u] = swn[u];
+      const int64_t tn = t + (2 + u) * tok_step;
+      cwn[u] = tn < n ? kc[tn * LPT + j] : u32x4{0u, 0u, 0u, 0u};
+      swn[u] = tn < n ? ks[tn * LPT + j] : 0u;
+    }
+    float acc[2][GRP];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const float s0 = e4m3_value(sw[u] & 0xffu), s1 = e4m3_value(sw[u] >> 8);
+      bf16x2 kp[16];
+      kp[0] = kpair<0>(cw[u].x); kp[1] = kpair<1>(cw[u].x); kp[2] = kpair<2>(cw[u].x); kp[3] = kpair<3>(cw[u].x);
+      kp[4] = kpair<0>(cw[u].y); kp[5] = kpair<1>(cw[u].y); kp[6] = kpair<2>(cw[u].y); kp[7] = kpair<3>(cw[u].y);
+      kp[8] = kpair<0>(cw[u].z); kp[9] = kpair<1>(cw[u].z); kp[10] = kpair<2>(cw[u].z); kp[11] = kpair<3>(cw[u].z);
+      kp[12] = kpair<0>(cw[u].w); kp[13] = kpair<1>(cw[u].w); kp[14] = kpair<2>(cw[u].w); kp[15] = kpair<3>(cw[u].w);
+#pragma unroll
+      for (int g = 0; g < GRP; ++g) {
+        float p0 = 0.0f, p1 = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          p0 = __builtin_amdgcn_fdot2_f32_bf16(kp[i], __builtin_bit_cast(bf16x2, qv[g][i]), p0, false);
+          p1 = __builtin_amdgcn_fdot2_f32_bf16(kp[8 + i], __builtin_bit_cast(bf16x2, qv[g][8 + i]), p1, false);
+        }
+        acc[u][g] = __builtin_fmaf(p1, s1, p0 * s0);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int64_t tu = t + u * tok_step;
+#pragma unroll
+      for (int g = 0; g < GRP; ++g) {
+        const float v = lane_group_sum<LPT>(acc[u][g]);
+        if (tu < n && g % LPT == j) out[(int64_t)g * n + tu] = v * gk;
+      }
+    }
+  }
+}
+
 }  // namespace nvfp4
 
 // ============================================================ host entry points
@@ -261,6 +365,39 @@ nvfp4_status nvfp4_kv_decode_qk(const nvfp4_kv_cache* c, const uint16_t* q, int3
   if (!q || !logits) return NVFP4_EINVAL;
   if (!nvfp4host::aligned16(q) || !nvfp4host::aligned16(logits)) return NVFP4_EALIGN;
   if ((st = nvfp4host::check_device())) return st;
+  const int lpt = c->head_dim / 32;
+  if (c->head_dim % 32 == 0 && (lpt == 1 || lpt == 2 || lpt == 4 || lpt == 8) &&
+      (grp == 1 || grp == 2 || grp == 4 || grp == 8)) {
+    const int64_t tpb = (kThreads / 64) * (64 / lpt);             // tokens per workgroup pass
+    const int64_t need = (n + tpb - 1) / tpb;
+    const int64_t per = std::max<int64_t>(1, (int64_t)nvfp4host::num_cus() * 8 / ((int64_t)c->kv_heads * c->layers));
+    const int tiles = (int)std::max<int64_t>(1, std::min<int64_t>(need, std::min<int64_t>(per, 65535)));
+    const dim3 grid(tiles, c->kv_heads, c->layers);
+    hipStream_t st = (hipStream_t)stream;
+    const uint32_t* qa = (const uint32_t*)q;
+#define NVFP4_QK(L, G) kv_qk_kernel<L, G><<<grid, kThreads, 0, st>>>(*c, qa, q_heads, n, logits)
+    switch (lpt * 16 + grp) {
+      case 1 * 16 + 1: NVFP4_QK(1, 1); break;
+      case 1 * 16 + 2: NVFP4_QK(1, 2); break;
+      case 1 * 16 + 4: NVFP4_QK(1, 4); break;
+      case 1 * 16 + 8: NVFP4_QK(1, 8); break;
+      case 2 * 16 + 1: NVFP4_QK(2, 1); break;
+      case 2 * 16 + 2: NVFP4_QK(2, 2); break;
+      case 2 * 16 + 4: NVFP4_QK(2, 4); break;
+      case 2 * 16 + 8: NVFP4_QK(2, 8); break;
+      case 4 * 16 + 1: NVFP4_QK(4, 1); break;
+      case 4 * 16 + 2: NVFP4_QK(4, 2); break;
+      case 4 * 16 + 4: NVFP4_QK(4, 4); break;
+      case 4 * 16 + 8: NVFP4_QK(4, 8); break;
+      case 8 * 16 + 1: NVFP4_QK(8, 1); break;
+      case 8 * 16 + 2: NVFP4_QK(8, 2); break;
+      case 8 * 16 + 4: NVFP4_QK(8, 4); break;
+      default: NVFP4_QK(8, 8); break;
+    }
+#undef NVFP4_QK
+    NVFP4_LAUNCH_CHECK();
+    return NVFP4_OK;
+  }
   const int64_t tokens_per_iter = kThreads / bpr;
   const int64_t need = (n + tokens_per_iter - 1) / tokens_per_iter;
   const int tiles = (int)std::max<int64_t>(
