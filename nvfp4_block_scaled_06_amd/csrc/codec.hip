@@ -342,7 +342,6 @@ constexpr int kOnchipMaxPer = 14;   // 3 x 14 x 16 B per thread stays within 256
 // scalar resource plus a scalar per-p offset and one shared lane offset,
 // keeping the address arithmetic out of the vector registers that hold the
 // three tensors in flight.
-constexpr int kBufferWord3 = 0x00020000;   // gfx9 buffer resource word 3: 32-bit data format
 
 template <int kPer>
 __device__ __forceinline__ void onchip_load(const u32x4* __restrict__ xs, u32x4 (&v)[kPer]) {

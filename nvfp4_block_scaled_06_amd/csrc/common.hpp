@@ -156,6 +156,10 @@ __device__ __forceinline__ u32x4 dequant_half(uint32_t codes, float s, float g) 
   return o;
 }
 
+// gfx9 buffer resource word 3 (32-bit data format) for raw buffer loads and
+// stores; accesses past the resource's extent read zero and write nothing.
+constexpr int kBufferWord3 = 0x00020000;
+
 // ---------------------------------------------------------------- reductions
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
 #pragma unroll

@@ -1,110 +1,235 @@
-// Block-scaled NVFP4 x NVFP4 GEMM on gfx950 bf16 MFMA.
+// Block-scaled NVFP4 x NVFP4 GEMM on gfx950 MFMA.
 //
 // NVFP4 serves both weights and activations of MoE expert linears (iwan.kr,
 // "NVIDIA shrank GLM-5.2 to 4 bits", section 1); the low-bit operands are
 // restored inside the compute kernel instead of being expanded in global
 // memory (omidsaffari.com, "LLM quantization guide", section "memory, speed
-// and quality").  gfx950 has no MFMA that consumes E4M3-per-16 block scales,
-// so each 16-value block is dequantized EXACTLY to bf16 (E2M1 * s has at most
-// 6 significant bits and lies in [2^-10, 2688]) in LDS, contracted on
-// v_mfma_f32_32x32x16_bf16 with fp32 accumulation, and the two FP32 tensor
-// scales are applied once in the epilogue.
+// and quality").
 //
-// C[m][n] = gA * gB * sum_k deq(A)[m][k] * deq(B)[n][k]   (both K-major)
+//   C[m][n] = gA * gB * sum_k deq(A)[m][k] * deq(B)[n][k]       (both K-major)
+//
+// gfx950 has no MFMA that consumes E4M3-per-16 block scales, so every 16-value
+// block is dequantized EXACTLY into f16 tiles in LDS: E2M1 * s has at most 6
+// significant bits and lies in [2^-10, 2688].  v_cvt_scalef32_pk_f16_fp4 with
+// the scale s applies s's power-of-two part (the instruction uses only the
+// scale's exponent), and one v_pk_mul_f16 by s's mantissa factor (1 + m/8,
+// at most 4 significant bits) finishes the exact product -- about one VALU
+// operation per element.  The tiles feed v_mfma_f32_32x32x16_f16 (fp32
+// accumulation); gA * gB is applied once in the epilogue.
+//
+// Tiling: 256 x 256 output per workgroup (the 8192 x 2048 problem is then one
+// workgroup per CU), 4 waves of 128 x 128 (4 x 4 MFMA tiles, 256 fp32
+// accumulators per lane), K step 64 (4 blocks).  LDS holds two f16 tile
+// pairs; the next K step's codes and scales are prefetched into registers
+// while the current step is contracted, one barrier per step.
 #include <algorithm>
 
 #include "common.hpp"
 
 namespace nvfp4 {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int GBM = 128, GBN = 128, GBK = 64;
-constexpr int GLDK = GBK + 8;          // LDS row stride in bf16 (pads away bank conflicts)
+constexpr int GTM = 256, GTN = 256, GTK = 64;
+constexpr int GLD = GTK + 8;                 // f16 per LDS row (padding spreads rows over banks)
+constexpr int GThreads = 256;
 
-// Dequantizes one 16-value block (8 code bytes, scale byte) into 16 bf16 at dst.
-__device__ __forceinline__ void deq16_to_lds(u32x2 c, uint32_t sbyte, __bf16* dst) {
-  const float s = e4m3_value(sbyte);
-  bf16x8 lo, hi;
-  f32x2 f;
-  f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c.x, 1.0f, 0); lo[0] = (__bf16)(f.x * s); lo[1] = (__bf16)(f.y * s);
-  f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c.x, 1.0f, 1); lo[2] = (__bf16)(f.x * s); lo[3] = (__bf16)(f.y * s);
-  f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c.x, 1.0f, 2); lo[4] = (__bf16)(f.x * s); lo[5] = (__bf16)(f.y * s);
-  f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c.x, 1.0f, 3); lo[6] = (__bf16)(f.x * s); lo[7] = (__bf16)(f.y * s);
-  f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c.y, 1.0f, 0); hi[0] = (__bf16)(f.x * s); hi[1] = (__bf16)(f.y * s);
-  f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c.y, 1.0f, 1); hi[2] = (__bf16)(f.x * s); hi[3] = (__bf16)(f.y * s);
-  f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c.y, 1.0f, 2); hi[4] = (__bf16)(f.x * s); hi[5] = (__bf16)(f.y * s);
-  f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c.y, 1.0f, 3); hi[6] = (__bf16)(f.x * s); hi[7] = (__bf16)(f.y * s);
-  *(bf16x8*)dst = lo;
-  *(bf16x8*)(dst + 8) = hi;
+// Raw operand data of one K step for one row: 32 code bytes, 4 scale bytes.
+struct RowRaw {
+  u32x4 c01, c23;                      // blocks 0,1 and 2,3 (8 bytes each)
+  uint32_t s;                          // scale byte of block b in bits 8b..8b+7
+};
+
+// One workgroup's rows [r0, r0 + 256) of a K-major NVFP4 operand, addressed
+// through buffer resources whose extent ends at the last row: reads of rows
+// past the matrix, and reads steered past the extent for K steps at or after
+// K, return zeros without a branch and without touching memory (K may be 0,
+// with zero-size buffers).  Every load is unconditional, so the compiler
+// counts them exactly and the two-steps-ahead prefetch below stays in flight.
+struct Operand {
+  __amdgpu_buffer_rsrc_t q, s;
+  uint32_t qrow, srow;                 // bytes per row: K/2, K/16
+};
+
+__device__ __forceinline__ Operand make_operand(const uint8_t* q, const uint8_t* sf, int64_t r0, int64_t rows,
+                                                int64_t K) {
+  Operand o;
+  const int64_t here = rows - r0 < GTM ? rows - r0 : GTM;
+  o.qrow = (uint32_t)(K / 2);
+  o.srow = (uint32_t)(K / 16);
+  o.q = __builtin_amdgcn_make_buffer_rsrc((void*)(q + r0 * (K / 2)), 0, (int)(here * (K / 2)), kBufferWord3);
+  o.s = __builtin_amdgcn_make_buffer_rsrc((void*)(sf + r0 * (K / 16)), 0, (int)(here * (K / 16)), kBufferWord3);
+  return o;
 }
 
-// Stages a GBM x GBK (or GBN x GBK) tile: 512 blocks of 16 values, 2 per thread.
-__device__ __forceinline__ void stage_tile(const uint8_t* __restrict__ q, const uint8_t* __restrict__ sf, int64_t rows,
-                                           int64_t K, int64_t r0, int64_t k0, __bf16 (*tile)[GLDK]) {
+constexpr uint32_t kOutside = 0x80000000u;  // offset beyond every extent (extents stay below 2^31)
+
+template <bool kAligned>
+__device__ __forceinline__ RowRaw load_row(const Operand& o, int lrow, int64_t K, int64_t k0) {
+  RowRaw r;
+  const bool in = k0 < K;
+  const uint32_t qo = in ? (uint32_t)lrow * o.qrow + (uint32_t)(k0 / 2) : kOutside;
+  const uint32_t so = in ? (uint32_t)lrow * o.srow + (uint32_t)(k0 / 16) : kOutside;
+  if (kAligned) {                      // K % 64 == 0: a step is wholly inside or outside
+    r.c01 = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(o.q, (int)qo, 0, 0));
+    r.c23 = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(o.q, (int)(in ? qo + 16 : kOutside), 0, 0));
+    r.s = __builtin_amdgcn_raw_buffer_load_b32(o.s, (int)so, 0, 0);
+  } else {                             // ragged last step: each block checked on its own
+    u32x2 c[4];
+    r.s = 0;
 #pragma unroll
-  for (int it = 0; it < 2; ++it) {
-    const int idx = threadIdx.x + it * kThreads;   // 0..511
-    const int r = idx >> 2, kb = idx & 3;
-    const int64_t gr = r0 + r, gk = k0 + 16 * kb;
-    u32x2 c = {0u, 0u};
-    uint32_t sb = 0;
-    if (gr < rows && gk < K) {
-      c = *(const u32x2*)(q + gr * (K / 2) + gk / 2);
-      sb = sf[gr * (K / 16) + gk / 16];
+    for (int b = 0; b < 4; ++b) {
+      const bool bin = k0 + 16 * b < K;
+      c[b] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(o.q, (int)(bin ? qo + 8 * b : kOutside), 0, 0));
+      r.s |= (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(o.s, (int)(bin ? so + b : kOutside), 0, 0) << (8 * b);
     }
-    deq16_to_lds(c, sb, &tile[r][16 * kb]);
+    r.c01 = u32x4{c[0].x, c[0].y, c[1].x, c[1].y};
+    r.c23 = u32x4{c[2].x, c[2].y, c[3].x, c[3].y};
+  }
+  return r;
+}
+
+template <int sel>
+__device__ __forceinline__ f16x2 deq_pair(uint32_t w, float s, f16x2 mf) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, s, sel) * mf;
+}
+
+// Dequantizes block b (16 values) of one row exactly into f16 and writes it
+// to LDS (dst points at the row).
+template <int b>
+__device__ __forceinline__ void deq_block_to_lds(const RowRaw& r, _Float16* dst) {
+  // s from its E4M3 byte (exact hardware decode, subnormals included)
+  const float s = __builtin_amdgcn_cvt_f32_fp8((int)r.s, b);
+  // mantissa factor of s in [1, 2): s / 2^floor(log2 s), exact
+  const float mfs = __uint_as_float((__float_as_uint(s) & 0x007fffffu) | 0x3f800000u);
+  const _Float16 mh = (_Float16)mfs;
+  const f16x2 mf = {mh, mh};
+  const uint32_t cx = b == 0 ? r.c01.x : b == 1 ? r.c01.z : b == 2 ? r.c23.x : r.c23.z;
+  const uint32_t cy = b == 0 ? r.c01.y : b == 1 ? r.c01.w : b == 2 ? r.c23.y : r.c23.w;
+  f16x8 lo, hi;
+  f16x2 p;
+  p = deq_pair<0>(cx, s, mf); lo[0] = p.x; lo[1] = p.y;
+  p = deq_pair<1>(cx, s, mf); lo[2] = p.x; lo[3] = p.y;
+  p = deq_pair<2>(cx, s, mf); lo[4] = p.x; lo[5] = p.y;
+  p = deq_pair<3>(cx, s, mf); lo[6] = p.x; lo[7] = p.y;
+  p = deq_pair<0>(cy, s, mf); hi[0] = p.x; hi[1] = p.y;
+  p = deq_pair<1>(cy, s, mf); hi[2] = p.x; hi[3] = p.y;
+  p = deq_pair<2>(cy, s, mf); hi[4] = p.x; hi[5] = p.y;
+  p = deq_pair<3>(cy, s, mf); hi[6] = p.x; hi[7] = p.y;
+  *(f16x8*)(dst + 16 * b) = lo;
+  *(f16x8*)(dst + 16 * b + 8) = hi;
+}
+
+// One 16-wide k substep: 16 MFMAs on the fragments in a/b while the next
+// substep's fragments load from LDS and block kk of the next K step is
+// dequantized into the other LDS buffer.  The scheduling groups interleave
+// one MFMA with a few VALU and LDS instructions, so the single wave on each
+// SIMD keeps its matrix core fed while it does the dequantization.
+template <int kk>
+__device__ __forceinline__ void substep(f32x16 (&acc)[4][4], f16x8 (&a)[4], f16x8 (&b)[4], const _Float16* Acur,
+                                        const _Float16* Bcur, const RowRaw& ra, const RowRaw& rb, _Float16* Anext,
+                                        _Float16* Bnext) {
+  __builtin_amdgcn_sched_barrier(0);               // each substep is its own scheduling region
+  f16x8 an[4], bn[4];
+  if (kk < 3) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) an[i] = *(const f16x8*)(Acur + i * 32 * GLD + 16 * (kk + 1));
+#pragma unroll
+    for (int j = 0; j < 4; ++j) bn[j] = *(const f16x8*)(Bcur + j * 32 * GLD + 16 * (kk + 1));
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], b[j], acc[i][j], 0, 0, 0);
+  deq_block_to_lds<kk>(ra, Anext);
+  deq_block_to_lds<kk>(rb, Bnext);
+  // 16 MFMA; about 40 VALU; 8 LDS reads (kk < 3) and 4 LDS writes
+#pragma unroll
+  for (int m = 0; m < 16; ++m) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);     // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);     // VALU
+    if (m < 8) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
+    else if (m < 12) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // DS write
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  if (kk < 3) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { a[i] = an[i]; b[i] = bn[i]; }
   }
 }
 
-__global__ void __launch_bounds__(kThreads) gemm_lds_kernel(const uint8_t* __restrict__ aq,
-                                                            const uint8_t* __restrict__ asf,
-                                                            const float* __restrict__ ag,
-                                                            const uint8_t* __restrict__ bq,
-                                                            const uint8_t* __restrict__ bsf,
-                                                            const float* __restrict__ bg, int64_t M, int64_t N,
-                                                            int64_t K, float* __restrict__ C) {
-  __shared__ __attribute__((aligned(16))) __bf16 As[GBM][GLDK];
-  __shared__ __attribute__((aligned(16))) __bf16 Bs[GBN][GLDK];
-  const int64_t m0 = (int64_t)blockIdx.y * GBM, n0 = (int64_t)blockIdx.x * GBN;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int wm = wave >> 1, wn = wave & 1;       // 2 x 2 waves, 64 x 64 each
-  f32x16 acc[2][2];
+template <bool kAligned>
+__global__ void __launch_bounds__(GThreads) gemm_kernel(const uint8_t* __restrict__ aq, const uint8_t* __restrict__ asf,
+                                                        const float* __restrict__ ag, const uint8_t* __restrict__ bq,
+                                                        const uint8_t* __restrict__ bsf, const float* __restrict__ bg,
+                                                        int64_t M, int64_t N, int64_t K, float* __restrict__ C) {
+  __shared__ __attribute__((aligned(16))) _Float16 As[2][GTM][GLD];
+  __shared__ __attribute__((aligned(16))) _Float16 Bs[2][GTN][GLD];
+  const int64_t m0 = (int64_t)blockIdx.y * GTM, n0 = (int64_t)blockIdx.x * GTN;
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int wm = wave >> 1, wn = wave & 1;       // 2 x 2 waves of 128 x 128
+  const Operand A = make_operand(aq, asf, m0, M, K), B = make_operand(bq, bsf, n0, N, K);
+
+  f32x16 acc[4][4];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
-  for (int64_t k0 = 0; k0 < K; k0 += GBK) {
-    stage_tile(aq, asf, M, K, m0, k0, As);
-    stage_tile(bq, bsf, N, K, n0, k0, Bs);
-    __syncthreads();
+  // Software pipeline over K steps: while the MFMAs of step k read LDS buffer
+  // k%2, each thread dequantizes its A row and B row of step k+1 into the
+  // other buffer (one block per substep) and the raw codes of step k+2 load.
+  // Steps past the last one read zeros and write an unread buffer.
+  const int64_t nk = (K + GTK - 1) / GTK;
+  RowRaw ra = load_row<kAligned>(A, tid, K, 0);
+  RowRaw rb = load_row<kAligned>(B, tid, K, 0);
+  deq_block_to_lds<0>(ra, &As[0][tid][0]);
+  deq_block_to_lds<1>(ra, &As[0][tid][0]);
+  deq_block_to_lds<2>(ra, &As[0][tid][0]);
+  deq_block_to_lds<3>(ra, &As[0][tid][0]);
+  deq_block_to_lds<0>(rb, &Bs[0][tid][0]);
+  deq_block_to_lds<1>(rb, &Bs[0][tid][0]);
+  deq_block_to_lds<2>(rb, &Bs[0][tid][0]);
+  deq_block_to_lds<3>(rb, &Bs[0][tid][0]);
+  ra = load_row<kAligned>(A, tid, K, GTK);
+  rb = load_row<kAligned>(B, tid, K, GTK);
+  __syncthreads();
+  const int arow = wm * 128 + (lane & 31), brow = wn * 128 + (lane & 31), kof = 8 * (lane >> 5);
+  for (int64_t kt = 0; kt < nk; ++kt) {
+    const int buf = (int)(kt & 1);
+    const RowRaw ra2 = load_row<kAligned>(A, tid, K, (kt + 2) * GTK);
+    const RowRaw rb2 = load_row<kAligned>(B, tid, K, (kt + 2) * GTK);
+    const _Float16* Acur = &As[buf][arow][kof];
+    const _Float16* Bcur = &Bs[buf][brow][kof];
+    _Float16* An = &As[buf ^ 1][tid][0];
+    _Float16* Bn = &Bs[buf ^ 1][tid][0];
+    f16x8 a[4], b[4];
 #pragma unroll
-    for (int kk = 0; kk < GBK; kk += 16) {
-      bf16x8 a[2], b[2];
+    for (int i = 0; i < 4; ++i) a[i] = *(const f16x8*)(Acur + i * 32 * GLD);
 #pragma unroll
-      for (int i = 0; i < 2; ++i) a[i] = *(const bf16x8*)&As[wm * 64 + i * 32 + (lane & 31)][kk + 8 * (lane >> 5)];
-#pragma unroll
-      for (int j = 0; j < 2; ++j) b[j] = *(const bf16x8*)&Bs[wn * 64 + j * 32 + (lane & 31)][kk + 8 * (lane >> 5)];
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
-    }
+    for (int j = 0; j < 4; ++j) b[j] = *(const f16x8*)(Bcur + j * 32 * GLD);
+    substep<0>(acc, a, b, Acur, Bcur, ra, rb, An, Bn);
+    substep<1>(acc, a, b, Acur, Bcur, ra, rb, An, Bn);
+    substep<2>(acc, a, b, Acur, Bcur, ra, rb, An, Bn);
+    substep<3>(acc, a, b, Acur, Bcur, ra, rb, An, Bn);
+    ra = ra2;
+    rb = rb2;
     __syncthreads();
   }
   const float gab = ag[0] * bg[0];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const int64_t row = m0 + wm * 64 + i * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
-        const int64_t col = n0 + wn * 64 + j * 32 + (lane & 31);
+        const int64_t row = m0 + wm * 128 + i * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+        const int64_t col = n0 + wn * 128 + j * 32 + (lane & 31);
         if (row < M && col < N) C[row * N + col] = acc[i][j][e] * gab;
       }
 }
@@ -119,13 +244,20 @@ extern "C" nvfp4_status nvfp4_gemm(const uint8_t* a_q, const uint8_t* a_sf, cons
   if (M == 0 || N == 0) return NVFP4_OK;
   if (!a_g || !b_g || !c) return NVFP4_EINVAL;
   if (K > 0 && (!a_q || !a_sf || !b_q || !b_sf)) return NVFP4_EINVAL;
-  if ((M + GBM - 1) / GBM > 65535 || (N + GBN - 1) / GBN > 2147483647LL) return NVFP4_EINVAL;
+  if ((M + GTM - 1) / GTM > 65535 || (N + GTN - 1) / GTN > 2147483647LL) return NVFP4_EINVAL;
+  // a workgroup's 256-row operand slab is addressed with 32-bit offsets
+  if (K > (1LL << 22)) return NVFP4_EINVAL;
   if (!nvfp4host::aligned16(a_q) || !nvfp4host::aligned16(b_q) || !nvfp4host::aligned16(c)) return NVFP4_EALIGN;
   if ((reinterpret_cast<uintptr_t>(a_g) & 3u) || (reinterpret_cast<uintptr_t>(b_g) & 3u)) return NVFP4_EALIGN;
   nvfp4_status st = nvfp4host::check_device();
   if (st) return st;
-  dim3 grid((unsigned)((N + GBN - 1) / GBN), (unsigned)((M + GBM - 1) / GBM));
-  gemm_lds_kernel<<<grid, kThreads, 0, (hipStream_t)stream>>>(a_q, a_sf, a_g, b_q, b_sf, b_g, M, N, K, c);
+  const dim3 grid((unsigned)((N + GTN - 1) / GTN), (unsigned)((M + GTM - 1) / GTM));
+  // aligned path: K a multiple of 64 and 4-byte aligned scale rows
+  const bool aligned = K % GTK == 0 && nvfp4host::aligned16(a_sf) && nvfp4host::aligned16(b_sf);
+  if (aligned)
+    gemm_kernel<true><<<grid, GThreads, 0, (hipStream_t)stream>>>(a_q, a_sf, a_g, b_q, b_sf, b_g, M, N, K, c);
+  else
+    gemm_kernel<false><<<grid, GThreads, 0, (hipStream_t)stream>>>(a_q, a_sf, a_g, b_q, b_sf, b_g, M, N, K, c);
   NVFP4_LAUNCH_CHECK();
   return NVFP4_OK;
 }

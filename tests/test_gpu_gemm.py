@@ -69,3 +69,47 @@ def test_gemm_full_size_sampled_rows():
     want = oracle.gemm_f64(np_(aq), np_(asf), np_(ag)[0], np_(bq), np_(bsf), np_(bg)[0], rows=rows)
     err = rel_frobenius(np_(c[torch.from_numpy(rows).cuda()]), want)
     assert err <= TOL, f"rel Frobenius {err:.3e}"
+
+
+@pytest.mark.parametrize("K", [2048, 2032])
+def test_gemm_every_scale_byte(K):
+    """Raw operands that walk every block-scale byte 0x00..0x7E (subnormal
+    E4M3 scales included) and every code nibble, against fp64; K = 2032 is
+    not a multiple of the 64-wide K step."""
+    print("case: gemm scale-byte sweep K", K, flush=True)
+    rng = np.random.default_rng(K)
+    M, N = 96, 80
+    aq = rng.integers(0, 256, (M, K // 2), dtype=np.uint8)
+    bq = rng.integers(0, 256, (N, K // 2), dtype=np.uint8)
+    asf = ((np.arange(M * (K // 16)).reshape(M, K // 16) * 5) % 127).astype(np.uint8)
+    bsf = ((np.arange(N * (K // 16)).reshape(N, K // 16) * 3 + 11) % 127).astype(np.uint8)
+    ag = np.array([1.0], np.float32)
+    bg = np.array([0.5], np.float32)
+    dev = [torch.from_numpy(t).cuda() for t in (aq, asf, ag, bq, bsf, bg)]
+    c = nv.gemm(*dev)
+    torch.cuda.synchronize()
+    want = oracle.gemm_f64(aq, asf, 1.0, bq, bsf, 0.5)
+    err = rel_frobenius(np_(c), want)
+    assert err <= TOL, f"rel Frobenius {err:.3e}"
+
+
+def test_gemm_picks_single_elements_exactly():
+    """B selects one element of A per column (code 1.0, scale byte 0x38 = 1.0,
+    gB = 1), so C[m][n] = E2M1(A[m][k_n]) * s(A) exactly: a per-element pin of
+    the in-kernel decode for every scale byte and code nibble."""
+    rng = np.random.default_rng(7)
+    M, K, N = 128, 2048, 128
+    aq = rng.integers(0, 256, (M, K // 2), dtype=np.uint8)
+    asf = ((np.arange(M * (K // 16)).reshape(M, K // 16) * 7 + 1) % 127).astype(np.uint8)
+    ks = np.array([16 * n + (n % 16) for n in range(N)])
+    bq = np.zeros((N, K // 2), np.uint8)
+    bsf = np.zeros((N, K // 16), np.uint8)
+    for n, k in enumerate(ks):
+        bq[n, k // 2] = 0x2 << (4 * (k % 2))        # E2M1 code 2 = 1.0
+        bsf[n, k // 16] = 0x38                      # E4M3 1.0
+    one = np.array([1.0], np.float32)
+    dev = [torch.from_numpy(t).cuda() for t in (aq, asf, one, bq, bsf, one)]
+    c = np_(nv.gemm(*dev))
+    torch.cuda.synchronize()
+    want = oracle.dequantize_f64_unscaled(aq, asf)[:, ks]
+    np.testing.assert_array_equal(c.astype(np.float64), want)
