@@ -17,12 +17,13 @@
 // Launch modes of nvfp4_quantize:
 //  TWO_KERNEL  amax_partial_kernel (per-workgroup maxima, no atomics) then
 //              encode_kernel (reduces the partials, builds the table, encodes).
-//  FUSED       fused_quantize_kernel: one cooperative launch whose workgroups
-//              walk the batch tensor by tensor.  Each workgroup reduces its
-//              slice of tensor t, publishes it (agent-scope atomics), then
-//              encodes its slice of tensor t-1 -- data it read one step
-//              earlier, still in L2 / the Infinity Cache -- so HBM sees each
-//              input byte about once.
+//  FUSED       one cooperative launch whose workgroups walk the batch
+//              tensor by tensor.  fused_onchip_kernel when a tensor fits on
+//              chip (registers + LDS of the whole GPU): every input byte is
+//              read from HBM once.  Otherwise fused_quantize_kernel: each
+//              workgroup reduces its slice of tensor t, publishes it
+//              (agent-scope atomics), then encodes its slice of tensor t-1,
+//              read again newest-first.
 #include <algorithm>
 
 #include "common.hpp"
@@ -324,135 +325,236 @@ __global__ void __launch_bounds__(kThreads) fused_quantize_kernel(const u32x4* _
 }
 
 // ------------------------------------------------------------ fused, tensor held on chip
-// When one tensor fits in the register files of the whole GPU (up to
-// kOnchipMaxPer half blocks per thread, one 512-thread workgroup per CU),
-// the persistent launch keeps it there.  Thread i of workgroup w owns half
-// blocks w*S + p*512 + i (p < kPer) of every tensor, S = 512*kPer, and three
-// register sets rotate through a three-stage pipeline: while the loads of
-// tensor t+2 are in flight, the workgroup reduces and publishes the maximum of
-// tensor t+1 and encodes tensor t, whose amax was published a whole step
-// earlier -- so the cross-workgroup wait and the atomics' round trips are
-// hidden behind a step of work, and HBM sees every input byte exactly once.
-constexpr int kOnchipThreads = 512;
-constexpr int kOnchipMaxPer = 14;   // 3 x 14 x 16 B per thread stays within 256 VGPRs
+// When one tensor fits on chip (up to kOnchipMaxPer half blocks per data
+// thread, one workgroup per CU), the persistent launch reads every input
+// byte from HBM exactly once.
+//
+// Each workgroup has kOnchipDataWaves data waves and one synchronization
+// wave.  Data thread i of workgroup w owns half blocks w*S + p*D + i
+// (p < kPer, D data threads, S = D*kPer) of every tensor.  Three tensors are
+// on chip at once: t in registers (waiting for its amax, then encoded),
+// t+1 in registers (its maximum published, its amax exchange in flight
+// while t is encoded) and t+2 streaming into an LDS buffer through direct
+// buffer-to-LDS loads, which hold no registers.  A step moves t+1 from LDS
+// into registers two pieces at a time, reissuing each freed LDS slot for
+// t+2 at once, so HBM always has a tensor's worth of loads queued.
+//
+// The cross-workgroup exchange of maxima runs in the synchronization wave:
+// each workgroup stores its maximum into its own slot of the tensor's line
+// set and every synchronization wave polls all slots -- plain agent-scope
+// stores and loads, no read-modify-write chains.  Waiting on those loads
+// never waits for the data waves' loads (each wave retires its vector
+// memory operations through its own in-order counter), and data and
+// synchronization waves meet at barriers that order LDS traffic only.
+//
+// The compiler tracks neither the completion of the buffer-to-LDS loads nor
+// reads of what they wrote piecewise, so the data waves wait for them with
+// explicit counts: a step always issues the same number of vector memory
+// operations in the same order (2*kPer stores, then kPer loads; tensors
+// past the batch and slices past a tensor use buffer resources of extent
+// zero or of the tensor's size, whose accesses read zeros and write
+// nothing).
+constexpr int kOnchipDataWaves = 7;
+constexpr int kOnchipData = 64 * kOnchipDataWaves;     // data threads per workgroup
+constexpr int kOnchipThreads = kOnchipData + 64;      // + the synchronization wave
+constexpr int kOnchipMaxPer = 16;                       // 2 x 16 x 16 B registers + 16 x 7 KiB LDS
 
-// Loads this workgroup's slice of one tensor: the host only picks the on-chip
-// launch when every slice is whole (hb_per_tensor is a multiple of 512*kPer),
-// so there are no bounds checks.  Raw buffer loads address the slice with a
-// scalar resource plus a scalar per-p offset and one shared lane offset,
-// keeping the address arithmetic out of the vector registers that hold the
-// three tensors in flight.
+typedef __attribute__((address_space(3))) void lds_void_t;
 
-template <int kPer>
-__device__ __forceinline__ void onchip_load(const u32x4* __restrict__ xs, u32x4 (&v)[kPer]) {
-  const __amdgpu_buffer_rsrc_t rs =
-      __builtin_amdgcn_make_buffer_rsrc((void*)xs, 0, kPer * kOnchipThreads * 16, kBufferWord3);
-#pragma unroll
-  for (int p = 0; p < kPer; ++p)
-    v[p] = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)threadIdx.x * 16, p * kOnchipThreads * 16, 0);
+// s_waitcnt with only the vector memory counter constrained (gfx9 encoding:
+// vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
+template <int kN>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(kN >= 0 && kN < 64, "vmcnt range");
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_waitcnt((kN & 0xF) | ((kN >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+  __builtin_amdgcn_sched_barrier(0);
 }
 
-// Workgroup maximum of the held values, published for tensor t.
+// Workgroup barrier ordering LDS only (the loads and stores in flight stay
+// in flight); the memory clobber keeps the compiler's LDS accesses on their
+// side of it.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// Two 16-byte LDS reads, complete on return.
+__device__ __forceinline__ void lds_read2(const u32x4* a, const u32x4* b, u32x4& ra, u32x4& rb) {
+  asm volatile("ds_read_b128 %0, %2\n\tds_read_b128 %1, %3\n\ts_waitcnt lgkmcnt(0)"
+               : "=&v"(ra), "=&v"(rb)
+               : "v"((uint32_t)(uintptr_t)a), "v"((uint32_t)(uintptr_t)b)
+               : "memory");
+}
+
+struct OnchipShared {
+  double table[128];                  // fp64 reciprocal of every block divisor of the tensor
+  double r6;                          // reciprocal of d6 = RN32(6 g)
+  uint32_t red[kOnchipDataWaves];     // per-data-wave maxima of the tensor
+};
+
+// Buffer resource over tensor t's range of a per-tensor array of `bytes`
+// bytes per tensor (t >= batch: extent zero, every access is a no-op).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tensor_rsrc(const void* base, int t, int batch, int64_t bytes) {
+  const int tc = t < batch ? t : batch - 1;
+  return __builtin_amdgcn_make_buffer_rsrc((void*)((const char*)base + (int64_t)tc * bytes), 0,
+                                           t < batch ? (int)bytes : 0, kBufferWord3);
+}
+
+// Issues the buffer-to-LDS loads of pieces [p0, p0 + n) of tensor t.
 template <int kPer>
-__device__ __forceinline__ void onchip_arrive(const u32x4 (&v)[kPer], uint32_t* red, uint32_t* ws, int t, int G) {
+__device__ __forceinline__ void onchip_dma(u32x4 (*L)[kOnchipData], __amdgpu_buffer_rsrc_t rs, int p0, int n) {
+  const int w = threadIdx.x >> 6;
+  const int base = (int)blockIdx.x * kPer * kOnchipData * 16;
+  for (int p = p0; p < p0 + n; ++p)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)&L[p][w * 64], 16, (int)threadIdx.x * 16,
+                                             base + p * kOnchipData * 16, 0, 0);
+}
+
+template <int kPer>
+__device__ __forceinline__ uint32_t onchip_wave_max(const u32x4 (&v)[kPer]) {
   uint32_t m = 0;
 #pragma unroll
   for (int p = 0; p < kPer; ++p) m = pk_absmax(pk_absmax(pk_absmax(pk_absmax(m, v[p].x), v[p].y), v[p].z), v[p].w);
-  m = wave_max_u32(halves_max(m));
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    uint32_t r = red[0];
-    for (int k = 1; k < kOnchipThreads / 64; ++k) r = r > red[k] ? r : red[k];
-    fused_arrive(ws, t, r, G);
-  }
+  return wave_max_u32(halves_max(m));
 }
 
-// Waits for tensor t's amax, builds its table and encodes the held values.
+// Moves tensor t+1 from LDS into nxt and refills the LDS buffer with tensor
+// t+2, a pair of pieces at a time.  kStores is the number of vector memory
+// operations issued since tensor t+1's loads (the previous step's stores):
+// before pair j, the operations younger than its second load are the
+// kPer-2-2j later loads of t+1, kStores stores and 2j loads of t+2.
+template <int kPer, int kStores>
+__device__ __forceinline__ void onchip_refill(const u32x4* __restrict__ x, int t, int batch, int64_t hb,
+                                              u32x4 (&nxt)[kPer], u32x4 (*L)[kOnchipData]) {
+  const __amdgpu_buffer_rsrc_t rs = tensor_rsrc(x, t + 2, batch, hb * 16);
+#pragma unroll
+  for (int p = 0; p < kPer; p += 2) {
+    wait_vmcnt<kPer - 2 + kStores>();
+    lds_read2(&L[p][threadIdx.x], &L[p + 1][threadIdx.x], nxt[p], nxt[p + 1]);
+    onchip_dma<kPer>(L, rs, p, 2);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// One step of a data wave: tensor t (in cur) is encoded once its amax
+// arrives, tensor t+1 moves from LDS into nxt and its maximum is published.
 template <int kPer>
-__device__ __forceinline__ void onchip_encode(const u32x4 (&v)[kPer], int64_t lo, int t,
-                                              int64_t hb_per_tensor, uint32_t* ws, float* __restrict__ gout,
-                                              uint32_t* __restrict__ q, uint8_t* __restrict__ sf, double* table,
-                                              uint32_t* sh_amax) {
-  if (threadIdx.x == 0) *sh_amax = fused_wait(ws, t);
-  __syncthreads();
-  const uint32_t a = *sh_amax;
-  const float g = a ? __uint_as_float((a & 0x7fffu) << 16) / kGlobalDiv : __builtin_nanf("");
-  if (blockIdx.x == 0 && threadIdx.x == 0) gout[t] = g;
-  const double r6 = recip_d6(g);
-  build_table(table, g);
-  __syncthreads();
-  const int64_t off = (int64_t)t * hb_per_tensor + lo;
-  const __amdgpu_buffer_rsrc_t rq =
-      __builtin_amdgcn_make_buffer_rsrc((void*)(q + off), 0, kPer * kOnchipThreads * 4, kBufferWord3);
-  const __amdgpu_buffer_rsrc_t rsf =
-      __builtin_amdgcn_make_buffer_rsrc((void*)(sf + off / 2), 0, kPer * kOnchipThreads / 2, kBufferWord3);
-  const int lane = threadIdx.x & 63;
+__device__ __forceinline__ void onchip_data_step(const u32x4* __restrict__ x, int t, int batch, int64_t hb,
+                                                 u32x4 (&cur)[kPer], u32x4 (&nxt)[kPer], u32x4 (*L)[kOnchipData],
+                                                 uint32_t* __restrict__ q, uint8_t* __restrict__ sf,
+                                                 OnchipShared& sh) {
+  if (t == 0)
+    onchip_refill<kPer, 0>(x, t, batch, hb, nxt, L);
+  else
+    onchip_refill<kPer, 2 * kPer>(x, t, batch, hb, nxt, L);
+  const uint32_t m = onchip_wave_max<kPer>(nxt);
+  if ((threadIdx.x & 63) == 0) sh.red[threadIdx.x >> 6] = m;
+  lds_barrier();                                       // maxima of t+1 -> synchronization wave
+  lds_barrier();                                       // amax of t, r6 and table <- synchronization wave
+  const double r6 = sh.r6;
+  const __amdgpu_buffer_rsrc_t rq = tensor_rsrc(q, t, batch, hb * 4);
+  const __amdgpu_buffer_rsrc_t rsf = tensor_rsrc(sf, t, batch, hb / 2);
+  const int qbase = (int)blockIdx.x * kPer * kOnchipData * 4;
+  const int sbase = (int)blockIdx.x * kPer * kOnchipData / 2;
+  // even lanes write the pair's scale byte; odd lanes aim past the extent (a
+  // dropped store), so every lane issues the same stores
+  const int sf_lane = (threadIdx.x & 1) ? (int)0x80000000u : (int)threadIdx.x >> 1;
 #pragma unroll
   for (int p = 0; p < kPer; ++p) {
-    const uint32_t sbyte = block_scale_byte(pair_max(half_absmax_bits(v[p])), r6);
-    const uint32_t code = encode_half(v[p], table[sbyte]);
-    __builtin_amdgcn_raw_buffer_store_b32(code, rq, (int)threadIdx.x * 4, p * kOnchipThreads * 4, 0);
-    if ((lane & 1) == 0)
-      __builtin_amdgcn_raw_buffer_store_b8((uint8_t)sbyte, rsf, (int)threadIdx.x >> 1, p * (kOnchipThreads / 2), 0);
+    const uint32_t sbyte = block_scale_byte(pair_max(half_absmax_bits(cur[p])), r6);
+    const uint32_t code = encode_half(cur[p], sh.table[sbyte]);
+    __builtin_amdgcn_raw_buffer_store_b32(code, rq, (int)threadIdx.x * 4, qbase + p * kOnchipData * 4, 0);
+    __builtin_amdgcn_raw_buffer_store_b8((uint8_t)sbyte, rsf, sf_lane, sbase + p * (kOnchipData / 2), 0);
     __builtin_amdgcn_sched_barrier(0);                 // one half block's temporaries at a time
   }
-  __syncthreads();                                     // the table and sh_amax are reused by the next tensor
 }
 
-// One pipeline step: issue tensor t+2's loads into nw, publish tensor t+1's
-// maximum from nx, encode tensor t from cur.
-template <int kPer>
-__device__ __forceinline__ void onchip_step(const u32x4* __restrict__ x, int batch, int64_t hb_per_tensor, int64_t lo,
-                                            int t, const u32x4 (&cur)[kPer], const u32x4 (&nx)[kPer],
-                                            u32x4 (&nw)[kPer], uint32_t* ws, int G, float* __restrict__ gout,
-                                            uint32_t* __restrict__ q, uint8_t* __restrict__ sf, double* table,
-                                            uint32_t* red, uint32_t* sh_amax) {
-  // unconditional (tensor index clamped): a skipped load would keep the
-  // buffer's previous contents alive across the step and cost registers
-  const int tl = t + 2 < batch ? t + 2 : batch - 1;
-  onchip_load<kPer>(x + (int64_t)tl * hb_per_tensor + lo, nw);
-  if (t + 1 < batch) onchip_arrive<kPer>(nx, red, ws, t + 1, G);
-  onchip_encode<kPer>(cur, lo, t, hb_per_tensor, ws, gout, q, sf, table, sh_amax);
+// Synchronization wave: slot exchange of tensor t's workgroup maxima.
+__device__ __forceinline__ void onchip_publish(uint32_t* ws, int t, uint32_t m) {
+  __hip_atomic_store(fused_line(ws, t, 0) + blockIdx.x, 0x80000000u | m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Polls every slot of tensor t until all G are filled; returns the maximum
+// (bit 31 set), or 0 after the spin limit (error flag raised).
+__device__ __forceinline__ uint32_t onchip_wait(uint32_t* ws, int t, int G) {
+  const int lane = threadIdx.x & 63;
+  const uint32_t* slots = fused_line(ws, t, 0);
+  for (uint32_t it = 0; it < kSpinLimit; ++it) {
+    uint32_t mx = 0, ok = 1;
+    for (int k = lane; k < G; k += 64) {
+      const uint32_t s = __hip_atomic_load(slots + k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      ok &= s >> 31;
+      mx = mx > s ? mx : s;
+    }
+    if (__builtin_amdgcn_ballot_w64(ok == 0) == 0) return wave_max_u32(mx);
+    __builtin_amdgcn_s_sleep(1);
+  }
+  if (lane == 0) __hip_atomic_store(&((FusedHeader*)ws)->error, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return 0u;
 }
 
 template <int kPer>
 __global__ void __launch_bounds__(kOnchipThreads) fused_onchip_kernel(const u32x4* __restrict__ x, int batch,
-                                                                      int64_t hb_per_tensor, uint32_t* ws,
+                                                                      int64_t hb, uint32_t* ws,
                                                                       float* __restrict__ gout,
                                                                       uint32_t* __restrict__ q,
                                                                       uint8_t* __restrict__ sf) {
-  __shared__ double table[128];
-  __shared__ uint32_t red[kOnchipThreads / 64];
-  __shared__ uint32_t sh_amax;
-  __shared__ uint32_t sh_last;
+  static_assert(kPer % 2 == 0 && kPer <= kOnchipMaxPer, "pieces move in pairs");
+  __shared__ OnchipShared sh;
+  __shared__ __attribute__((aligned(16))) u32x4 L[kPer][kOnchipData];
   const int G = gridDim.x;
-  const int64_t lo = (int64_t)blockIdx.x * kPer * kOnchipThreads;
-  u32x4 a[kPer], b[kPer], c[kPer];
-  onchip_load<kPer>(x + lo, a);
-  onchip_load<kPer>(x + (batch > 1 ? hb_per_tensor : 0) + lo, b);
-  onchip_arrive<kPer>(a, red, ws, 0, G);
-  for (int t = 0; t < batch; t += 3) {
-    onchip_step<kPer>(x, batch, hb_per_tensor, lo, t, a, b, c, ws, G, gout, q, sf, table, red, &sh_amax);
-    if (t + 1 >= batch) break;
-    onchip_step<kPer>(x, batch, hb_per_tensor, lo, t + 1, b, c, a, ws, G, gout, q, sf, table, red, &sh_amax);
-    if (t + 2 >= batch) break;
-    onchip_step<kPer>(x, batch, hb_per_tensor, lo, t + 2, c, a, b, ws, G, gout, q, sf, table, red, &sh_amax);
+  if (wave_id() < kOnchipDataWaves) {
+    u32x4 a[kPer], b[kPer];
+    onchip_dma<kPer>(L, tensor_rsrc(x, 0, batch, hb * 16), 0, kPer);
+    wait_vmcnt<0>();
+#pragma unroll
+    for (int p = 0; p < kPer; p += 2) lds_read2(&L[p][threadIdx.x], &L[p + 1][threadIdx.x], a[p], a[p + 1]);
+    onchip_dma<kPer>(L, tensor_rsrc(x, 1, batch, hb * 16), 0, kPer);
+    const uint32_t m = onchip_wave_max<kPer>(a);
+    if ((threadIdx.x & 63) == 0) sh.red[threadIdx.x >> 6] = m;
+    lds_barrier();                                     // maxima of tensor 0
+    int t = 0;
+    for (; t + 1 < batch; t += 2) {
+      onchip_data_step<kPer>(x, t, batch, hb, a, b, L, q, sf, sh);
+      onchip_data_step<kPer>(x, t + 1, batch, hb, b, a, L, q, sf, sh);
+    }
+    if (t < batch) onchip_data_step<kPer>(x, t, batch, hb, a, b, L, q, sf, sh);
+    return;
   }
-  // the last workgroup out restores the counters to zero (see fused_quantize_kernel)
-  if (threadIdx.x == 0) {
-    const uint32_t old = __hip_atomic_fetch_add(&((FusedHeader*)ws)->done, 1u, __ATOMIC_RELAXED,
-                                                __HIP_MEMORY_SCOPE_AGENT);
-    sh_last = old == (uint32_t)G - 1;
+  // synchronization wave
+  const int lane = threadIdx.x & 63;
+  auto red_max = [&]() {
+    uint32_t r = sh.red[0];
+#pragma unroll
+    for (int k = 1; k < kOnchipDataWaves; ++k) r = r > sh.red[k] ? r : sh.red[k];
+    return r;
+  };
+  lds_barrier();
+  if (lane == 0) onchip_publish(ws, 0, red_max());
+  for (int t = 0; t < batch; ++t) {
+    lds_barrier();                                     // maxima of t+1 are in sh.red
+    const uint32_t next = red_max();
+    if (lane == 0 && t + 1 < batch) onchip_publish(ws, t + 1, next);
+    const uint32_t v = onchip_wait(ws, t, G);
+    const float g = v ? __uint_as_float((v & 0x7fffu) << 16) / kGlobalDiv : __builtin_nanf("");
+    sh.table[lane] = recip_entry((uint32_t)lane, g);
+    if (lane < 63) sh.table[lane + 64] = recip_entry((uint32_t)lane + 64, g);
+    if (lane == 0) {
+      sh.r6 = recip_d6(g);
+      if (blockIdx.x == 0) gout[t] = g;
+    }
+    lds_barrier();                                     // publish r6 and the table
   }
-  __syncthreads();
-  if (sh_last) {
+  // the last workgroup out restores the slots and the counter to zero; every
+  // slot read of this workgroup has returned (the values were used above)
+  uint32_t last = 0;
+  if (lane == 0)
+    last = __hip_atomic_fetch_add(&((FusedHeader*)ws)->done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+           (uint32_t)G - 1;
+  if (__builtin_amdgcn_readfirstlane((int)last)) {
     const size_t words = (size_t)batch * kTensorWords;
     uint32_t* base = ws + kFusedHeaderBytes / 4;
-    for (size_t i = threadIdx.x; i < words; i += kOnchipThreads)
+    for (size_t i = lane; i < words; i += 64)
       __hip_atomic_store(base + i, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (threadIdx.x == 0)
-      __hip_atomic_store(&((FusedHeader*)ws)->done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (lane == 0) __hip_atomic_store(&((FusedHeader*)ws)->done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
@@ -533,17 +635,18 @@ int fused_grid(int64_t hb_per_tensor) {
   return (int)std::max<int64_t>(1, std::min(g, need));
 }
 
-// Half blocks per thread for the on-chip persistent launch: the smallest
-// count whose 512-thread slices tile a tensor exactly with at most one
-// workgroup per CU, or 0 when no count does (the tensor is too large to hold
-// on chip, or its size does not divide) -- the streaming launch runs then.
+// Half blocks per data thread for the on-chip persistent launch: the
+// smallest even count that covers a tensor with at most one workgroup per
+// CU, or 0 when the tensor is too large to hold on chip (the streaming
+// launch runs then).
 int onchip_per_thread(int64_t hb_per_tensor) {
+  if (hb_per_tensor <= 0) return 0;
   const int64_t cus = nvfp4host::num_cus();
-  for (int per = 1; per <= kOnchipMaxPer; ++per) {
-    const int64_t slice = (int64_t)per * kOnchipThreads;
-    if (hb_per_tensor % slice == 0 && hb_per_tensor / slice <= cus) return per;
-  }
-  return 0;
+  if (cus > (int64_t)kTensorWords) return 0;           // one exchange slot per workgroup
+  const int64_t cap = cus * kOnchipData;
+  int64_t per = (hb_per_tensor + cap - 1) / cap;
+  per += per & 1;                                       // pieces move in pairs
+  return per <= kOnchipMaxPer ? (int)per : 0;
 }
 
 }  // namespace
@@ -583,26 +686,20 @@ nvfp4_status nvfp4_quantize(const uint16_t* x, int64_t batch, int64_t rows, int6
       uint32_t* ws = (uint32_t*)workspace;
       uint32_t* qa = (uint32_t*)q;
       void* args[] = {&xa, &bt, (void*)&hb, &ws, &g, &qa, &sf};
-      const int64_t slice = (int64_t)onchip_per * kOnchipThreads;
+      const int64_t slice = (int64_t)onchip_per * kOnchipData;
       const int G = (int)((hb + slice - 1) / slice);
       const void* fn = nullptr;
-      const void* fns[kOnchipMaxPer] = {
-          (const void*)fused_onchip_kernel<1>,
+      const void* fns[kOnchipMaxPer / 2] = {
           (const void*)fused_onchip_kernel<2>,
-          (const void*)fused_onchip_kernel<3>,
           (const void*)fused_onchip_kernel<4>,
-          (const void*)fused_onchip_kernel<5>,
           (const void*)fused_onchip_kernel<6>,
-          (const void*)fused_onchip_kernel<7>,
           (const void*)fused_onchip_kernel<8>,
-          (const void*)fused_onchip_kernel<9>,
           (const void*)fused_onchip_kernel<10>,
-          (const void*)fused_onchip_kernel<11>,
           (const void*)fused_onchip_kernel<12>,
-          (const void*)fused_onchip_kernel<13>,
           (const void*)fused_onchip_kernel<14>,
+          (const void*)fused_onchip_kernel<16>,
       };
-      fn = fns[onchip_per - 1];
+      fn = fns[onchip_per / 2 - 1];
       hipError_t e = hipLaunchCooperativeKernel(fn, dim3(G), dim3(kOnchipThreads), args, 0, s);
       if (e != hipSuccess) {
         nvfp4host::set_hip_error(e);
