@@ -40,6 +40,9 @@ def parse():
     p.add_argument("--no-extras", action="store_true", help="headline step only")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--rows-only", default="", help="comma list of extra rows to run (single,acts,kv,gemm)")
+    p.add_argument("--traffic-kernels", action="store_true",
+                   help="only launch the headline kernels, the GEMM and a 1 GiB device copy, 3 times each "
+                        "(the workload for rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs)")
     return p.parse_args()
 
 
@@ -271,22 +274,65 @@ def run_extras(nv, synth, torch, which):
 
 
 def cpu_baseline(synth, torch):
-    """The oracle, untouched, on 8 of the 64 expert matrices: quantize + dequantize
-    (about 10-15 s of CPU work on a 16-core host)."""
+    """The oracle, untouched, on the whole headline workload: quantize +
+    dequantize of all 64 expert matrices, two passes (about 10 s of CPU work
+    on a 16-core host)."""
     import numpy as np
     import oracle
-    E = 8
+    E, reps = 64, 2
     x = synth.experts(E, 2048, 7168, device="cuda")
     xb = x.cpu().view(torch.int16).numpy().view(np.uint16)
     del x
+    torch.cuda.empty_cache()
     n = E * 2048 * 7168
     t0 = time.perf_counter()
-    q, sf, g = oracle.quantize(xb)
-    oracle.dequantize(q, sf, g)
+    for _ in range(reps):
+        q, sf, g = oracle.quantize(xb)
+        oracle.dequantize(q, sf, g)
+        del q, sf, g
     dt = time.perf_counter() - t0
-    nbytes = bytes_quantize(n, E) + bytes_dequant(n, E)
+    nbytes = reps * (bytes_quantize(n, E) + bytes_dequant(n, E))
     return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": oracle.max_threads(), "kind": "oracle",
-            "sample": f"quantize+dequantize of {E} of the 64 expert matrices ({E}x2048x7168), {dt:.2f} s wall"}
+            "sample": f"quantize+dequantize of all {E} expert matrices ({E}x2048x7168), {reps} passes, "
+                      f"{dt:.2f} s wall"}
+
+
+def traffic_kernels(nv, synth, torch):
+    """Three launches each of the fused quantize and the dequantize of the
+    headline workload, the two-kernel quantize, the 8192 x 2048 x 7168 GEMM,
+    and a plain 1 GiB device-to-device copy whose byte counts (1 GiB read,
+    1 GiB written) calibrate the HBM byte counters."""
+    E, R, C = 64, 2048, 7168
+    x = synth.experts(E, R, C, device="cuda")
+    ws = nv.make_workspace(E, R, C)
+    q, sf, g = nv.quantize(x, flags="fused", workspace=ws)
+    y = torch.empty_like(x)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        nv.quantize(x, flags="fused", workspace=ws, out=(q, sf, g))
+    for _ in range(3):
+        nv.dequantize(q, sf, g, out=y)
+    for _ in range(3):
+        nv.quantize(x, flags="two_kernel", workspace=ws, out=(q, sf, g))
+    torch.cuda.synchronize()
+    del x, y, q, sf, g, ws
+    torch.cuda.empty_cache()
+    a, b = synth.gemm_operands(device="cuda")
+    aq, asf, ag = nv.quantize(a)
+    bq, bsf, bg = nv.quantize(b)
+    del a, b
+    c = torch.empty((8192, 2048), dtype=torch.float32, device="cuda")
+    for _ in range(3):
+        nv.gemm(aq, asf, ag, bq, bsf, bg, out=c)
+    torch.cuda.synchronize()
+    del aq, asf, bq, bsf, c
+    torch.cuda.empty_cache()
+    src = torch.ones(2 ** 30, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log("traffic kernels done")
 
 
 def main():
@@ -300,6 +346,9 @@ def main():
     import synth
     nv.lib()                       # fail loudly if the HIP library is missing
     torch.cuda.set_device(0)
+    if args.traffic_kernels:
+        traffic_kernels(nv, synth, torch)
+        return
     head = run_headline(nv, synth, torch, args.steps, args.warmup)
     log("headline done:", json.dumps(head))
     rows = {}
