@@ -23,7 +23,30 @@ namespace nvfp4 {
 // R = head_dim/8 half blocks per token row.  Lane j of a wave chunk maps to
 // token j / R, half block j % R (shifts when kPow2).  Input rows of one head
 // are head_dim*kv_heads apart; cache rows of consecutive tokens are
-// contiguous, so the code stores of a wave form one run.
+// contiguous, so the code stores of a wave form one run.  Each wave takes
+// kKVU chunks of 64 half blocks per trip with all their loads in flight, and
+// the workgroup's first loads are issued before it builds the scale's table.
+constexpr int kKVU = 4;
+
+template <bool kPow2>
+__device__ __forceinline__ void kv_append_load(const u32x4* __restrict__ src, int64_t base, int64_t total,
+                                               uint32_t R, int log2r, int64_t in_stride, u32x4 (&v)[kKVU]) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int u = 0; u < kKVU; ++u) {
+    const int64_t j = base + u * 64 + lane;
+    uint32_t t, r;
+    if (kPow2) {
+      t = (uint32_t)(j >> log2r);
+      r = (uint32_t)j & (R - 1);
+    } else {
+      t = (uint32_t)(j / R);
+      r = (uint32_t)(j - (int64_t)t * R);
+    }
+    v[u] = j < total ? src[(int64_t)t * in_stride + r] : u32x4{0u, 0u, 0u, 0u};
+  }
+}
+
 template <bool kPow2>
 __global__ void __launch_bounds__(kThreads) kv_append_kernel(nvfp4_kv_cache c, int64_t start, int64_t n, int log2r,
                                                              const u32x4* __restrict__ k_new,
@@ -33,36 +56,34 @@ __global__ void __launch_bounds__(kThreads) kv_append_kernel(nvfp4_kv_cache c, i
   const bool is_v = blockIdx.z & 1;
   const int H = c.kv_heads;
   const uint32_t R = (uint32_t)c.head_dim / 8;
-  const float g = (is_v ? c.v_g : c.k_g)[l * H + h];
-  __shared__ double table[128];
-  for (uint32_t j = threadIdx.x; j < 127u; j += kThreads) table[j] = recip_entry(j, g);
-  __syncthreads();
-  const double r6 = recip_d6(g);
   const u32x4* src = (is_v ? v_new : k_new) + ((int64_t)l * n * H + h) * R;    // token 0 of (l, h)
   uint32_t* dq = (uint32_t*)(is_v ? c.v : c.k) + (((int64_t)l * H + h) * c.capacity + start) * R;
   uint8_t* dsf = (is_v ? c.v_sf : c.k_sf) + (((int64_t)l * H + h) * c.capacity + start) * (R / 2);
   const int64_t total = n * (int64_t)R;
   const int lane = threadIdx.x & 63;
   const int64_t in_stride = (int64_t)H * R;                                     // between tokens
-  for (int64_t base = ((int64_t)blockIdx.x * (kThreads / 64) + wave_id()) * 64; base < total;
-       base += (int64_t)gridDim.x * kThreads) {
-    const int64_t j = base + lane;
-    const bool ok = j < total;
-    uint32_t t, r;
-    if (kPow2) {
-      t = (uint32_t)(j >> log2r);
-      r = (uint32_t)j & (R - 1);
-    } else {
-      t = (uint32_t)j / R;
-      r = (uint32_t)j - t * R;
+  const int64_t span = 64 * kKVU;
+  const int64_t stride = (int64_t)gridDim.x * (kThreads / 64) * span;
+  int64_t base = ((int64_t)blockIdx.x * (kThreads / 64) + wave_id()) * span;
+  u32x4 v[kKVU];
+  kv_append_load<kPow2>(src, base, total, R, log2r, in_stride, v);
+  const float g = (is_v ? c.v_g : c.k_g)[l * H + h];
+  __shared__ double table[128];
+  for (uint32_t j = threadIdx.x; j < 127u; j += kThreads) table[j] = recip_entry(j, g);
+  __syncthreads();
+  const double r6 = recip_d6(g);
+  for (; base < total; base += stride) {
+#pragma unroll
+    for (int u = 0; u < kKVU; ++u) {
+      const int64_t j = base + u * 64 + lane;
+      const uint32_t sbyte = block_scale_byte(pair_max(half_absmax_bits(v[u])), r6);
+      const uint32_t code = encode_half(v[u], table[sbyte]);
+      if (j < total) {
+        dq[j] = code;
+        if ((lane & 1) == 0) dsf[j >> 1] = (uint8_t)sbyte;
+      }
     }
-    const u32x4 v = ok ? src[(int64_t)t * in_stride + r] : u32x4{0u, 0u, 0u, 0u};
-    const uint32_t sbyte = block_scale_byte(pair_max(half_absmax_bits(v)), r6);
-    const uint32_t code = encode_half(v, table[sbyte]);
-    if (ok) {
-      dq[j] = code;
-      if ((lane & 1) == 0) dsf[j >> 1] = (uint8_t)sbyte;
-    }
+    if (base + stride < total) kv_append_load<kPow2>(src, base + stride, total, R, log2r, in_stride, v);
   }
 }
 
@@ -319,8 +340,7 @@ nvfp4_status nvfp4_kv_append(const nvfp4_kv_cache* c, int64_t start, int64_t n, 
   const int R = c->head_dim / 8;
   if (n > INT32_MAX / R) return NVFP4_EINVAL;                      // 32-bit token index per lane
   const int64_t halves = n * R;
-  const int64_t others = (int64_t)c->kv_heads * 2 * c->layers;
-  const int tiles = tiles_for(halves / 2, others);
+  const int tiles = (int)std::min<int64_t>((halves + kThreads * kKVU - 1) / (kThreads * kKVU), 65535);
   const bool pow2 = (R & (R - 1)) == 0;
   const int log2r = __builtin_ctz((unsigned)R);
   const dim3 grid(tiles, c->kv_heads, 2 * c->layers);
