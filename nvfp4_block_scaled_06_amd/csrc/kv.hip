@@ -197,9 +197,19 @@ __global__ void __launch_bounds__(kThreads) kv_decode_qk_kernel(nvfp4_kv_cache c
 // are summed with DPP butterflies, and g is applied once per logit.
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
+constexpr int kQKGroups = 4;   // token groups per trip of kv_qk_kernel (loads in flight)
+
 template <int sel>
 __device__ __forceinline__ bf16x2 kpair(uint32_t codes) {
   return __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, 1.0f, sel);
+}
+
+// First product of a dot chain, a.x*b.x + a.y*b.y + 0, in the three-operand
+// form (the two-operand form the compiler picks needs a zeroed accumulator).
+__device__ __forceinline__ float dot2_first(bf16x2 a, bf16x2 b) {
+  float r;
+  asm("v_dot2_f32_bf16 %0, %1, %2, 0" : "=v"(r) : "v"(a), "v"(b));
+  return r;
 }
 
 template <int LPT>
@@ -214,6 +224,7 @@ template <int LPT, int GRP>
 __global__ void __launch_bounds__(kThreads) kv_qk_kernel(nvfp4_kv_cache c, const uint32_t* __restrict__ q,
                                                          int q_heads, int64_t n, float* __restrict__ logits) {
   constexpr int TPW = 64 / LPT;                        // tokens per wave
+  constexpr int U = kQKGroups;                         // token groups per trip
   const int h = blockIdx.y, l = blockIdx.z;
   const int H = c.kv_heads;
   const int lane = threadIdx.x & 63;
@@ -231,62 +242,77 @@ __global__ void __launch_bounds__(kThreads) kv_qk_kernel(nvfp4_kv_cache c, const
   }
   const float gk = c.k_g[l * H + h];
   const int64_t row0 = ((int64_t)l * H + h) * c.capacity;
-  const u32x4* kc = (const u32x4*)c.k + row0 * LPT;                 // 16 code bytes per lane
-  const uint16_t* ks = (const uint16_t*)c.k_sf + row0 * LPT;         // 2 scale bytes per lane
+  // buffer resources over tokens [0, n) of this (layer, head): loads of
+  // tokens past n read zeros, with no branch (the host keeps n*head_dim/2
+  // below 2^31)
+  const __amdgpu_buffer_rsrc_t kc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(c.k + row0 * LPT * 16), 0, (int)(n * LPT * 16), kBufferWord3);      // 16 code bytes per lane
+  const __amdgpu_buffer_rsrc_t ks = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(c.k_sf + row0 * LPT * 2), 0, (int)(n * LPT * 2), kBufferWord3);     // 2 scale bytes per lane
   float* out = logits + ((int64_t)l * q_heads + h * GRP) * n;
   const int64_t tok_step = (int64_t)gridDim.x * (kThreads / 64) * TPW;
   const int64_t t_lane = lane / LPT;
-  // two token groups per trip (independent dot chains); the next trip's codes
-  // and scales are already in flight while this trip is contracted
+  // U token groups per trip (independent dot chains); two register sets
+  // alternate, so the next trip's codes and scales are in flight while this
+  // trip is contracted
   int64_t t = ((int64_t)blockIdx.x * (kThreads / 64) + wave_id()) * TPW + t_lane;
-  u32x4 cwn[2];
-  uint32_t swn[2];
+  auto load = [&](int64_t t0, u32x4 (&cw)[U], uint32_t (&sw)[U]) {
 #pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    const int64_t tu = t + u * tok_step;
-    cwn[u] = tu < n ? kc[tu * LPT + j] : u32x4{0u, 0u, 0u, 0u};
-    swn[u] = tu < n ? ks[tu * LPT + j] : 0u;
-  }
-  for (; t - t_lane < n; t += 2 * tok_step) {
-    u32x4 cw[2];
-    uint32_t sw[2];
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      cw[u] = cwn[u];
-      sw[u] = swn[u];
-      const int64_t tn = t + (2 + u) * tok_step;
-      cwn[u] = tn < n ? kc[tn * LPT + j] : u32x4{0u, 0u, 0u, 0u};
-      swn[u] = tn < n ? ks[tn * LPT + j] : 0u;
+    for (int u = 0; u < U; ++u) {
+      const int64_t tu = t0 + u * tok_step;
+      const uint32_t e = tu < n ? (uint32_t)(tu * LPT + j) : 0x08000000u;     // past the extent: zeros
+      cw[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(kc, (int)(e * 16u), 0, 0));
+      sw[u] = __builtin_amdgcn_raw_buffer_load_b16(ks, (int)(e * 2u), 0, 0);
     }
-    float acc[2][GRP];
+  };
+  auto contract = [&](int64_t t0, const u32x4 (&cw)[U], const uint32_t (&sw)[U]) {
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const float s0 = e4m3_value(sw[u] & 0xffu), s1 = e4m3_value(sw[u] >> 8);
+    for (int u = 0; u < U; ++u) {
+      // scales from their E4M3 bytes (exact hardware decode)
+      const float s0 = __builtin_amdgcn_cvt_f32_fp8((int)sw[u], 0), s1 = __builtin_amdgcn_cvt_f32_fp8((int)sw[u], 1);
       bf16x2 kp[16];
       kp[0] = kpair<0>(cw[u].x); kp[1] = kpair<1>(cw[u].x); kp[2] = kpair<2>(cw[u].x); kp[3] = kpair<3>(cw[u].x);
       kp[4] = kpair<0>(cw[u].y); kp[5] = kpair<1>(cw[u].y); kp[6] = kpair<2>(cw[u].y); kp[7] = kpair<3>(cw[u].y);
       kp[8] = kpair<0>(cw[u].z); kp[9] = kpair<1>(cw[u].z); kp[10] = kpair<2>(cw[u].z); kp[11] = kpair<3>(cw[u].z);
       kp[12] = kpair<0>(cw[u].w); kp[13] = kpair<1>(cw[u].w); kp[14] = kpair<2>(cw[u].w); kp[15] = kpair<3>(cw[u].w);
+      const int64_t tu = t0 + u * tok_step;
+      float tot[GRP];
 #pragma unroll
       for (int g = 0; g < GRP; ++g) {
-        float p0 = 0.0f, p1 = 0.0f;
+        float p0 = dot2_first(kp[0], __builtin_bit_cast(bf16x2, qv[g][0]));
+        float p1 = dot2_first(kp[8], __builtin_bit_cast(bf16x2, qv[g][8]));
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
+        for (int i = 1; i < 8; ++i) {
           p0 = __builtin_amdgcn_fdot2_f32_bf16(kp[i], __builtin_bit_cast(bf16x2, qv[g][i]), p0, false);
           p1 = __builtin_amdgcn_fdot2_f32_bf16(kp[8 + i], __builtin_bit_cast(bf16x2, qv[g][8 + i]), p1, false);
         }
-        acc[u][g] = __builtin_fmaf(p1, s1, p0 * s0);
+        tot[g] = lane_group_sum<LPT>(__builtin_fmaf(p1, s1, p0 * s0));
+      }
+      // every lane of the token holds every head's total; lane j stores heads
+      // j, j + LPT, ... (one unmasked store per head it owns)
+      constexpr int kSPL = GRP >= LPT ? GRP / LPT : 1;
+#pragma unroll
+      for (int sidx = 0; sidx < kSPL; ++sidx) {
+        const int g = sidx * LPT + j;
+        float v = tot[0];
+#pragma unroll
+        for (int gg = 1; gg < GRP; ++gg) v = g == gg ? tot[gg] : v;
+        if (tu < n && g < GRP) out[(int64_t)g * n + tu] = v * gk;
       }
     }
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int64_t tu = t + u * tok_step;
-#pragma unroll
-      for (int g = 0; g < GRP; ++g) {
-        const float v = lane_group_sum<LPT>(acc[u][g]);
-        if (tu < n && g % LPT == j) out[(int64_t)g * n + tu] = v * gk;
-      }
-    }
+  };
+  u32x4 cwa[U], cwb[U];
+  uint32_t swa[U], swb[U];
+  const int64_t trip = U * tok_step;
+  load(t, cwa, swa);
+  while (t - t_lane < n) {
+    load(t + trip, cwb, swb);
+    contract(t, cwa, swa);
+    t += trip;
+    if (t - t_lane >= n) break;
+    load(t + trip, cwa, swa);
+    contract(t, cwb, swb);
+    t += trip;
   }
 }
 
@@ -386,8 +412,9 @@ nvfp4_status nvfp4_kv_decode_qk(const nvfp4_kv_cache* c, const uint16_t* q, int3
   if (!nvfp4host::aligned16(q) || !nvfp4host::aligned16(logits)) return NVFP4_EALIGN;
   if ((st = nvfp4host::check_device())) return st;
   const int lpt = c->head_dim / 32;
+  // 32-bit buffer offsets: n * head_dim / 2 code bytes per (layer, head)
   if (c->head_dim % 32 == 0 && (lpt == 1 || lpt == 2 || lpt == 4 || lpt == 8) &&
-      (grp == 1 || grp == 2 || grp == 4 || grp == 8)) {
+      (grp == 1 || grp == 2 || grp == 4 || grp == 8) && n * (c->head_dim / 2) < (INT64_C(1) << 27)) {
     const int64_t tpb = (kThreads / 64) * (64 / lpt);             // tokens per workgroup pass
     const int64_t need = (n + tpb - 1) / tpb;
     const int64_t per = std::max<int64_t>(1, (int64_t)nvfp4host::num_cus() * 8 / ((int64_t)c->kv_heads * c->layers));
