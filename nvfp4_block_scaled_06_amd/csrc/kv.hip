@@ -26,7 +26,7 @@ namespace nvfp4 {
 // contiguous, so the code stores of a wave form one run.  Each wave takes
 // kKVU chunks of 64 half blocks per trip with all their loads in flight, and
 // the workgroup's first loads are issued before it builds the scale's table.
-constexpr int kKVU = 4;
+constexpr int kKVU = 2;
 
 template <bool kPow2>
 __device__ __forceinline__ void kv_append_load(const u32x4* __restrict__ src, int64_t base, int64_t total,
