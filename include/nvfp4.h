@@ -155,7 +155,12 @@ nvfp4_status nvfp4_kv_read(const nvfp4_kv_cache* cache, int32_t layer0, int32_t 
  * logits[l][hq][t] = sum_d q[l][hq][d] * Khat[l][hq / (q_heads/kv_heads)][t][d]
  * (unscaled dot products, fp32 accumulation; Khat is the exact dequantized K).
  * q: [layers][q_heads][head_dim] bf16; q_heads a multiple of kv_heads (GQA).
- * logits: [layers][q_heads][n] float. */
+ * logits: [layers][q_heads][n] float.  Relative error of the logits is within
+ * fp32 accumulation of the exact fp64 sums.
+ * Errors: EINVAL (q_heads not a multiple of kv_heads, n outside
+ *   [0, capacity]), ENOTSUP (more than 16 query heads per KV head, (q_heads /
+ *   kv_heads) * head_dim above 4096, or head_dim/16 not a power of two up to
+ *   64), EALIGN, EHIP. */
 nvfp4_status nvfp4_kv_decode_qk(const nvfp4_kv_cache* cache, const uint16_t* q, int32_t q_heads,
                                 int64_t n, float* logits, void* stream);
 
@@ -165,10 +170,14 @@ nvfp4_status nvfp4_kv_decode_qk(const nvfp4_kv_cache* cache, const uint16_t* q, 
  * section 1; FP4 GEMM speed, axbrief.com, section "36% token efficiency and
  * Blackwell speed"):
  *   C[m][n] = gA * gB * sum_k deq(A)[m][k] * deq(B)[n][k]        (TN, K-major)
- * deq() = E2M1(code) * s, exact in bf16; fp32 accumulation; the tensor scales
- * are applied once in the epilogue.  Both operands use the quantize layout:
- * a_q [M][K/2], a_sf [M][K/16], b_q [N][K/2], b_sf [N][K/16]; a_g, b_g point
- * to one float each (device).  c: [M][N] float.  K % 16 == 0.
+ * deq() = E2M1(code) * s, exact in f16 (at most 6 significant bits); fp32
+ * accumulation; the tensor scales are applied once in the epilogue.  Both
+ * operands use the quantize layout: a_q [M][K/2], a_sf [M][K/16], b_q
+ * [N][K/2], b_sf [N][K/16]; a_g, b_g point to one float each (device).
+ * c: [M][N] float, fully written (zeros when K == 0).
+ * Errors: EINVAL (K % 16 != 0, K > 2^22, negative or too large M / N, null
+ *   pointers), EALIGN (a_q, b_q, c not 16-byte aligned, a_g / b_g not
+ *   4-byte aligned), ENOTSUP, EHIP.
  * ------------------------------------------------------------------------ */
 nvfp4_status nvfp4_gemm(const uint8_t* a_q, const uint8_t* a_sf, const float* a_g,
                         const uint8_t* b_q, const uint8_t* b_sf, const float* b_g,
