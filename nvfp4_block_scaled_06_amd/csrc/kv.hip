@@ -362,9 +362,9 @@ nvfp4_status nvfp4_kv_append(const nvfp4_kv_cache* c, int64_t start, int64_t n, 
   if (n == 0) return NVFP4_OK;
   if (!k_new || !v_new) return NVFP4_EINVAL;
   if (!nvfp4host::aligned16(k_new) || !nvfp4host::aligned16(v_new)) return NVFP4_EALIGN;
-  if ((st = nvfp4host::check_device())) return st;
   const int R = c->head_dim / 8;
   if (n > INT32_MAX / R) return NVFP4_EINVAL;                      // 32-bit token index per lane
+  if ((st = nvfp4host::check_device())) return st;
   const int64_t halves = n * R;
   const int tiles = (int)std::min<int64_t>((halves + kThreads * kKVU - 1) / (kThreads * kKVU), 65535);
   const bool pow2 = (R & (R - 1)) == 0;

@@ -121,6 +121,15 @@ def test_gemm_validation():
     assert L.nvfp4_gemm(*args, 64, 64, 32, P(0), None) == EINVAL
     assert L.nvfp4_gemm(*args, 64, 64, 32, P(FAKE + 4), None) == EALIGN
     assert L.nvfp4_gemm(*args, 0, 64, 32, P(FAKE), None) == 0
+    # K beyond 2^22 (32-bit offsets of a 256-row operand slab) is rejected up front
+    assert L.nvfp4_gemm(*args, 64, 64, (1 << 22) + 16, P(FAKE), None) == EINVAL
+
+
+def test_kv_append_token_count_limit():
+    """n * head_dim/8 half blocks must fit a 32-bit token index per lane."""
+    L = nv.lib()
+    d = _desc(cap=1 << 40, D=128)
+    assert L.nvfp4_kv_append(ctypes.byref(d), 0, (1 << 31) // 16 + 1, P(FAKE), P(FAKE), None) == EINVAL
 
 
 def test_valid_call_without_gpu_fails_cleanly():

@@ -57,6 +57,29 @@ def test_append_read_qk_small(D, grp):
         assert err <= QK_TOL, f"n={n}: rel Frobenius {err:.3e}"
 
 
+def test_append_read_non_pow2_head_dim():
+    """head_dim 48: three blocks per row (the non-power-of-two append path);
+    the decode sweep reports the documented ENOTSUP for it."""
+    L, H, D, cap = 2, 3, 48, 70
+    cache, kg, vg = _cache(L, H, D, cap, 48)
+    gen = torch.Generator().manual_seed(48)
+    k = (torch.randn((L, 70, H, D), generator=gen) * 3).to(torch.bfloat16)
+    v = torch.randn((L, 70, H, D), generator=gen).to(torch.bfloat16)
+    cache.append(0, k[:, :33].contiguous().cuda(), v[:, :33].contiguous().cuda())
+    cache.append(33, k[:, 33:].contiguous().cuda(), v[:, 33:].contiguous().cuda())
+    torch.cuda.synchronize()
+    okq, oks = oracle.kv_encode(bits(k), kg)
+    ovq, ovs = oracle.kv_encode(bits(v), vg)
+    assert np.array_equal(np_(cache.k), okq) and np.array_equal(np_(cache.k_sf), oks)
+    assert np.array_equal(np_(cache.v), ovq) and np.array_equal(np_(cache.v_sf), ovs)
+    kr, vr = cache.read(0, 2, 3, 60)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(kr), oracle.kv_read(okq[:, :, 3:63], oks[:, :, 3:63], kg))
+    qv = torch.randn((L, 2 * H, D), generator=gen).to(torch.bfloat16).cuda()
+    with pytest.raises(nv.NVFP4Error):
+        cache.decode_qk(qv, 10)
+
+
 def test_read_only_k_or_v():
     cache, kg, vg = _cache(2, 2, 64, 40, 3)
     k = torch.randn((2, 40, 2, 64)).to(torch.bfloat16)
