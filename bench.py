@@ -11,8 +11,9 @@ output byte written once) / wall time per step, in GB/s.
 Extra records in the same line ("rows"): the single 1024x1024 tensor, the
 16384 x 7168 activation quantize (two-kernel and fused), the 32x8x128 KV
 cache (512 appends of 256 tokens, decode QK over 131072 tokens, 32 query
-heads), and the 8192 x 2048 x 7168 block-scaled GEMM in TFLOP/s -- each with
-its roofline fraction.  Every kernel time comes from HIP events recorded on
+heads), the 8192 x 2048 x 7168 block-scaled GEMM and the grouped MoE GEMM
+(16384 tokens routed top-8 over 64 experts) in TFLOP/s -- each with its
+roofline fraction.  Every kernel time comes from HIP events recorded on
 the stream the kernels run on.
 
 cpu_baseline: the CPU oracle (the parity reference, not tuned) timed on a
@@ -39,7 +40,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--no-extras", action="store_true", help="headline step only")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    p.add_argument("--rows-only", default="", help="comma list of extra rows to run (single,acts,kv,gemm)")
+    p.add_argument("--rows-only", default="", help="comma list of extra rows to run (experts,single,acts,kv,gemm,moe)")
     p.add_argument("--traffic-kernels", action="store_true",
                    help="only launch the headline kernels, the GEMM and a 1 GiB device copy, 3 times each "
                         "(the workload for rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs)")
@@ -271,9 +272,38 @@ def run_extras(nv, synth, torch, which):
         rows["gemm_8192x2048x7168"] = {"ms": m, "bound": "mfma",
                                        **roof(flops, m, BF16_MFMA_PEAK_TFLOPS, "TFLOP/s")}
         del a, b, aq, bq, c
+    if "moe" in which:
+        rows["moe_grouped_gemm_16384x8_64x2048x7168"] = run_moe(nv, synth, torch)
     del fbuf
     torch.cuda.empty_cache()
     return rows
+
+
+def run_moe(nv, synth, torch):
+    """Grouped NVFP4 GEMM of MoE expert linears: 16384 tokens routed top-8 over
+    64 experts [2048 x 7168] (seeded uniform routing, 8 distinct experts per
+    token), routed activations sorted by expert."""
+    T, E, top, N, K = 16384, 64, 8, 2048, 7168
+    gen = torch.Generator().manual_seed(106)
+    choice = torch.rand((T, E), generator=gen).argsort(dim=1)[:, :top]       # 8 distinct experts per token
+    counts = torch.bincount(choice.flatten(), minlength=E)
+    offsets = torch.cat([torch.zeros(1, dtype=torch.int64), counts.cumsum(0)]).to(torch.int32).cuda()
+    M = int(counts.sum())
+    a = synth.activations(tokens=M, channels=K, seed=107, device="cuda")      # routed rows
+    aq, asf, ag = nv.quantize(a)
+    del a
+    w = synth.experts(E, N, K, device="cuda")
+    bq, bsf, bg = nv.quantize(w)
+    del w
+    torch.cuda.empty_cache()
+    c = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    m = timed(torch, lambda: nv.grouped_gemm(aq, asf, ag, bq, bsf, bg, offsets, out=c), 10)
+    flops = 2 * M * N * K
+    res = {"ms": m, "rows": M, "experts": E, "min_rows": int(counts.min()), "max_rows": int(counts.max()),
+           "bound": "mfma", **roof(flops, m, BF16_MFMA_PEAK_TFLOPS, "TFLOP/s")}
+    del aq, asf, bq, bsf, c
+    torch.cuda.empty_cache()
+    return res
 
 
 def cpu_baseline(synth, torch):
@@ -356,7 +386,7 @@ def main():
     log("headline done:", json.dumps(head))
     rows = {}
     if not args.no_extras:
-        which = args.rows_only.split(",") if args.rows_only else ["experts", "single", "acts", "kv", "gemm"]
+        which = args.rows_only.split(",") if args.rows_only else ["experts", "single", "acts", "kv", "gemm", "moe"]
         rows = run_extras(nv, synth, torch, which)
         log("extras done")
     cpu = None if args.no_cpu else cpu_baseline(synth, torch)

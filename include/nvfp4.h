@@ -183,6 +183,28 @@ nvfp4_status nvfp4_gemm(const uint8_t* a_q, const uint8_t* a_sf, const float* a_
                         const uint8_t* b_q, const uint8_t* b_sf, const float* b_g,
                         int64_t M, int64_t N, int64_t K, float* c, void* stream);
 
+/* ------------------------------------------------------------------------
+ * Grouped block-scaled GEMM for the MoE expert linears (iwan.kr, "NVIDIA
+ * shrank GLM-5.2 to 4 bits", section 1: the experts' weights and activations
+ * are both NVFP4).  The rows of A are the routed tokens sorted by expert:
+ * rows [offsets[e], offsets[e+1]) go through expert e's weight B_e.
+ *   C[m][n] = gA * gB[e] * sum_k deq(A)[m][k] * deq(B_e)[n][k]   (m in expert e's rows)
+ * a_q [M][K/2], a_sf [M][K/16], a_g: one float (device).
+ * b_q [experts][N][K/2], b_sf [experts][N][K/16], b_g [experts] (device).
+ * offsets: [experts+1] int32 on the device, non-decreasing from 0 to M; the
+ *   kernels clamp them to [0, M], so inconsistent offsets leave rows of C
+ *   unwritten but never access memory outside A, B or C.
+ * c: [M][N] float; every row inside some expert's range is written.
+ * Each expert's rows are computed exactly as nvfp4_gemm computes that
+ * expert's slice of A (same tiles, same accumulation order).
+ * Errors: EINVAL (experts <= 0, K % 16 != 0, K > 2^22, M / 256 + experts
+ *   above 65535, null pointers), EALIGN, ENOTSUP, EHIP.
+ * ------------------------------------------------------------------------ */
+nvfp4_status nvfp4_grouped_gemm(const uint8_t* a_q, const uint8_t* a_sf, const float* a_g,
+                                const uint8_t* b_q, const uint8_t* b_sf, const float* b_g,
+                                const int32_t* offsets, int32_t experts,
+                                int64_t M, int64_t N, int64_t K, float* c, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

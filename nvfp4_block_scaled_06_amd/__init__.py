@@ -57,6 +57,7 @@ _SIGS = {
     "nvfp4_kv_read": (_I32, [ctypes.POINTER(KVCacheDesc), _I32, _I32, _I64, _I64, _P, _P, _P]),
     "nvfp4_kv_decode_qk": (_I32, [ctypes.POINTER(KVCacheDesc), _P, _I32, _I64, _P, _P]),
     "nvfp4_gemm": (_I32, [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P, _P]),
+    "nvfp4_grouped_gemm": (_I32, [_P, _P, _P, _P, _P, _P, _P, _I32, _I64, _I64, _I64, _P, _P]),
 }
 
 _L = None
@@ -236,3 +237,23 @@ def gemm(a_q, a_sf, a_g, b_q, b_sf, b_g, out=None):
         _ptr(a_q), _ptr(a_sf), _ptr(a_g), _ptr(b_q), _ptr(b_sf), _ptr(b_g), M, N, 2 * K2, _ptr(c),
         _stream(a_q.device)))
     return c
+
+
+def grouped_gemm(a_q, a_sf, a_g, b_q, b_sf, b_g, offsets, out=None):
+    """MoE grouped GEMM: rows [offsets[e], offsets[e+1]) of A use expert e's
+    weight b[e]; C[M][N] = gA*gB[e] * sum_k deq(A)[m][k] deq(B_e)[n][k]."""
+    for t, n in ((a_q, "a_q"), (a_sf, "a_sf"), (b_q, "b_q"), (b_sf, "b_sf")):
+        _need(t, torch.uint8, n)
+    _need(a_g, torch.float32, "a_g")
+    _need(b_g, torch.float32, "b_g")
+    _need(offsets, torch.int32, "offsets")
+    M, K2 = a_q.shape
+    E, N = b_q.shape[0], b_q.shape[1]
+    if offsets.numel() != E + 1 or b_g.numel() != E:
+        raise ValueError("offsets must hold experts+1 entries and b_g one scale per expert")
+    c = out if out is not None else torch.empty((M, N), dtype=torch.float32, device=a_q.device)
+    _check("nvfp4_grouped_gemm", _lib().nvfp4_grouped_gemm(
+        _ptr(a_q), _ptr(a_sf), _ptr(a_g), _ptr(b_q), _ptr(b_sf), _ptr(b_g), _ptr(offsets), E, M, N, 2 * K2,
+        _ptr(c), _stream(a_q.device)))
+    return c
+

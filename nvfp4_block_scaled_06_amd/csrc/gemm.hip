@@ -160,18 +160,19 @@ __device__ __forceinline__ void substep(f32x16 (&acc)[4][4], f16x8 (&a)[4], f16x
   }
 }
 
+// One 256 x 256 output tile: rows [m0, m_end) of A (K-major NVFP4, at most
+// 256 of them) against rows [n0, n_end) of B, C row stride ldc, scaled by
+// gab in the epilogue.  As / Bs are the workgroup's LDS tiles.
 template <bool kAligned>
-__global__ void __launch_bounds__(GThreads) gemm_kernel(const uint8_t* __restrict__ aq, const uint8_t* __restrict__ asf,
-                                                        const float* __restrict__ ag, const uint8_t* __restrict__ bq,
-                                                        const uint8_t* __restrict__ bsf, const float* __restrict__ bg,
-                                                        int64_t M, int64_t N, int64_t K, float* __restrict__ C) {
-  __shared__ __attribute__((aligned(16))) _Float16 As[2][GTM][GLD];
-  __shared__ __attribute__((aligned(16))) _Float16 Bs[2][GTN][GLD];
-  const int64_t m0 = (int64_t)blockIdx.y * GTM, n0 = (int64_t)blockIdx.x * GTN;
+__device__ __forceinline__ void gemm_tile(const uint8_t* __restrict__ aq, const uint8_t* __restrict__ asf,
+                                          int64_t m0, int64_t m_end, const uint8_t* __restrict__ bq,
+                                          const uint8_t* __restrict__ bsf, int64_t n0, int64_t n_end, int64_t K,
+                                          float gab, float* __restrict__ C, int64_t ldc,
+                                          _Float16 (*As)[GTM][GLD], _Float16 (*Bs)[GTN][GLD]) {
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int wm = wave >> 1, wn = wave & 1;       // 2 x 2 waves of 128 x 128
-  const Operand A = make_operand(aq, asf, m0, M, K), B = make_operand(bq, bsf, n0, N, K);
+  const Operand A = make_operand(aq, asf, m0, m_end, K), B = make_operand(bq, bsf, n0, n_end, K);
 
   f32x16 acc[4][4];
 #pragma unroll
@@ -221,7 +222,6 @@ __global__ void __launch_bounds__(GThreads) gemm_kernel(const uint8_t* __restric
     rb = rb2;
     __syncthreads();
   }
-  const float gab = ag[0] * bg[0];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -230,8 +230,47 @@ __global__ void __launch_bounds__(GThreads) gemm_kernel(const uint8_t* __restric
       for (int e = 0; e < 16; ++e) {
         const int64_t row = m0 + wm * 128 + i * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
         const int64_t col = n0 + wn * 128 + j * 32 + (lane & 31);
-        if (row < M && col < N) C[row * N + col] = acc[i][j][e] * gab;
+        if (row < m_end && col < n_end) C[row * ldc + col] = acc[i][j][e] * gab;
       }
+}
+
+template <bool kAligned>
+__global__ void __launch_bounds__(GThreads) gemm_kernel(const uint8_t* __restrict__ aq, const uint8_t* __restrict__ asf,
+                                                        const float* __restrict__ ag, const uint8_t* __restrict__ bq,
+                                                        const uint8_t* __restrict__ bsf, const float* __restrict__ bg,
+                                                        int64_t M, int64_t N, int64_t K, float* __restrict__ C) {
+  __shared__ __attribute__((aligned(16))) _Float16 As[2][GTM][GLD];
+  __shared__ __attribute__((aligned(16))) _Float16 Bs[2][GTN][GLD];
+  const int64_t m0 = (int64_t)blockIdx.y * GTM, n0 = (int64_t)blockIdx.x * GTN;
+  gemm_tile<kAligned>(aq, asf, m0, M, bq, bsf, n0, N, K, ag[0] * bg[0], C, N, As, Bs);
+}
+
+// Grouped GEMM: rows of A are grouped by expert, rows [off[e], off[e+1])
+// multiplying expert e's weight B_e = b[e] ([N][K]).  grid.y enumerates the
+// (expert, 256-row tile) pairs in expert order; a workgroup finds its pair by
+// walking the offsets (clamped to [0, M], so inconsistent offsets never
+// reach outside A or C) and exits when its index is past the last tile.
+template <bool kAligned>
+__global__ void __launch_bounds__(GThreads) grouped_gemm_kernel(
+    const uint8_t* __restrict__ aq, const uint8_t* __restrict__ asf, const float* __restrict__ ag,
+    const uint8_t* __restrict__ bq, const uint8_t* __restrict__ bsf, const float* __restrict__ bg,
+    const int32_t* __restrict__ off, int experts, int64_t M, int64_t N, int64_t K, float* __restrict__ C) {
+  __shared__ __attribute__((aligned(16))) _Float16 As[2][GTM][GLD];
+  __shared__ __attribute__((aligned(16))) _Float16 Bs[2][GTN][GLD];
+  int64_t tile = blockIdx.y;
+  int e = 0;
+  int64_t lo = 0, hi = 0;
+  for (; e < experts; ++e) {
+    lo = off[e] < 0 ? 0 : (off[e] > M ? M : off[e]);
+    hi = off[e + 1] < lo ? lo : (off[e + 1] > M ? M : off[e + 1]);
+    const int64_t tiles = (hi - lo + GTM - 1) / GTM;
+    if (tile < tiles) break;
+    tile -= tiles;
+  }
+  if (e == experts) return;                            // past the last tile: no work
+  const int64_t m0 = lo + tile * GTM, n0 = (int64_t)blockIdx.x * GTN;
+  const int64_t wq = N * (K / 2), ws = N * (K / 16);   // bytes per expert weight, scales
+  gemm_tile<kAligned>(aq, asf, m0, hi, bq + e * wq, bsf + e * ws, n0, N, K, ag[0] * bg[e], C, N, As, Bs);
 }
 
 }  // namespace nvfp4
@@ -258,6 +297,39 @@ extern "C" nvfp4_status nvfp4_gemm(const uint8_t* a_q, const uint8_t* a_sf, cons
     gemm_kernel<true><<<grid, GThreads, 0, (hipStream_t)stream>>>(a_q, a_sf, a_g, b_q, b_sf, b_g, M, N, K, c);
   else
     gemm_kernel<false><<<grid, GThreads, 0, (hipStream_t)stream>>>(a_q, a_sf, a_g, b_q, b_sf, b_g, M, N, K, c);
+  NVFP4_LAUNCH_CHECK();
+  return NVFP4_OK;
+}
+
+extern "C" nvfp4_status nvfp4_grouped_gemm(const uint8_t* a_q, const uint8_t* a_sf, const float* a_g,
+                                           const uint8_t* b_q, const uint8_t* b_sf, const float* b_g,
+                                           const int32_t* offsets, int32_t experts, int64_t M, int64_t N, int64_t K,
+                                           float* c, void* stream) {
+  using namespace nvfp4;
+  if (experts <= 0 || M < 0 || N < 0 || K < 0 || K % kBlock) return NVFP4_EINVAL;
+  if (M == 0 || N == 0) return NVFP4_OK;
+  if (!a_g || !b_g || !c || !offsets) return NVFP4_EINVAL;
+  if (K > 0 && (!a_q || !a_sf || !b_q || !b_sf)) return NVFP4_EINVAL;
+  // upper bound on the (expert, row tile) pairs: every expert adds at most one partial tile
+  const int64_t tiles_y = (M + GTM - 1) / GTM + experts;
+  if (tiles_y > 65535 || (N + GTN - 1) / GTN > 2147483647LL) return NVFP4_EINVAL;
+  if (K > (1LL << 22)) return NVFP4_EINVAL;
+  if (!nvfp4host::aligned16(a_q) || !nvfp4host::aligned16(b_q) || !nvfp4host::aligned16(c)) return NVFP4_EALIGN;
+  if ((reinterpret_cast<uintptr_t>(a_g) & 3u) || (reinterpret_cast<uintptr_t>(b_g) & 3u) ||
+      (reinterpret_cast<uintptr_t>(offsets) & 3u))
+    return NVFP4_EALIGN;
+  nvfp4_status st = nvfp4host::check_device();
+  if (st) return st;
+  const dim3 grid((unsigned)((N + GTN - 1) / GTN), (unsigned)tiles_y);
+  // aligned path as for nvfp4_gemm; each expert's weight starts at a multiple
+  // of N*K/2 code bytes and N*K/16 scale bytes, aligned with K % 64 == 0
+  const bool aligned = K % GTK == 0 && nvfp4host::aligned16(a_sf) && nvfp4host::aligned16(b_sf);
+  if (aligned)
+    grouped_gemm_kernel<true><<<grid, GThreads, 0, (hipStream_t)stream>>>(a_q, a_sf, a_g, b_q, b_sf, b_g, offsets,
+                                                                          experts, M, N, K, c);
+  else
+    grouped_gemm_kernel<false><<<grid, GThreads, 0, (hipStream_t)stream>>>(a_q, a_sf, a_g, b_q, b_sf, b_g, offsets,
+                                                                           experts, M, N, K, c);
   NVFP4_LAUNCH_CHECK();
   return NVFP4_OK;
 }

@@ -258,3 +258,23 @@ def gemm_f64(a_q, a_sf, a_g, b_q, b_sf, b_g, rows=None) -> np.ndarray:
     A = dequantize_f64_unscaled(a_q, a_sf)
     B = dequantize_f64_unscaled(b_q, b_sf)
     return (float(a_g) * float(b_g)) * (A @ B.T)
+
+
+def grouped_gemm_f64(a_q, a_sf, a_g, b_q, b_sf, b_g, offsets) -> np.ndarray:
+    """fp64 grouped GEMM of MoE expert linears (iwan.kr, "NVIDIA shrank GLM-5.2
+    to 4 bits", section 1: weights and activations of the experts are NVFP4).
+
+    Rows [offsets[e], offsets[e+1]) of A are the tokens routed to expert e;
+    each such row is multiplied by expert e's weight b[e] ([N][K]):
+      C[m][n] = gA * gB[e] * sum_k deq(A)[m][k] * deq(B_e)[n][k].
+    Rows outside every expert's range stay zero.
+    """
+    offsets = np.asarray(offsets, dtype=np.int64)
+    M, N = a_q.shape[0], b_q.shape[1]
+    C = np.zeros((M, N), dtype=np.float64)
+    for e in range(b_q.shape[0]):
+        r0, r1 = int(offsets[e]), int(offsets[e + 1])
+        if r1 > r0:
+            C[r0:r1] = gemm_f64(a_q[r0:r1], a_sf[r0:r1], a_g, b_q[e], b_sf[e], b_g[e])
+    return C
+

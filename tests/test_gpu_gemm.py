@@ -113,3 +113,51 @@ def test_gemm_picks_single_elements_exactly():
     torch.cuda.synchronize()
     want = oracle.dequantize_f64_unscaled(aq, asf)[:, ks]
     np.testing.assert_array_equal(c.astype(np.float64), want)
+
+
+def _experts_and_routing(E, N, K, counts, seed):
+    gen = torch.Generator().manual_seed(seed)
+    M = int(sum(counts))
+    a = torch.randn((M, K), generator=gen).to(torch.bfloat16).cuda()
+    w = (torch.randn((E, N, K), generator=gen) * torch.linspace(0.5, 4.0, E).view(E, 1, 1)).to(torch.bfloat16).cuda()
+    aq, asf, ag = nv.quantize(a)
+    bq, bsf, bg = nv.quantize(w)                  # one tensor scale per expert
+    offsets = torch.tensor(np.concatenate([[0], np.cumsum(counts)]), dtype=torch.int32).cuda()
+    return aq, asf, ag, bq, bsf, bg, offsets
+
+
+@pytest.mark.parametrize("K", [2048, 2032])
+def test_grouped_gemm_against_oracle_and_dense(K):
+    """Ragged routing (empty experts, a single-row expert, experts spanning
+    several 256-row tiles) against the fp64 oracle, and bit-identical to one
+    dense nvfp4_gemm per expert slice."""
+    print("case: grouped gemm K", K, flush=True)
+    counts = [300, 0, 1, 513, 0, 77, 256, 2]
+    E, N = len(counts), 96
+    aq, asf, ag, bq, bsf, bg, offsets = _experts_and_routing(E, N, K, counts, K + 5)
+    c = nv.grouped_gemm(aq, asf, ag, bq, bsf, bg, offsets)
+    torch.cuda.synchronize()
+    off = np_(offsets)
+    want = oracle.grouped_gemm_f64(np_(aq), np_(asf), np_(ag)[0], np_(bq), np_(bsf), np_(bg), off)
+    err = rel_frobenius(np_(c), want)
+    assert err <= TOL, f"rel Frobenius {err:.3e}"
+    for e in range(E):
+        r0, r1 = int(off[e]), int(off[e + 1])
+        if r1 == r0:
+            continue
+        # fresh (16-byte aligned) copies of the expert's rows: K/2 need not be a multiple of 16
+        d = nv.gemm(aq[r0:r1].clone(), asf[r0:r1].clone(), ag, bq[e], bsf[e], bg[e:e + 1].clone())
+        torch.cuda.synchronize()
+        assert torch.equal(c[r0:r1], d), f"expert {e} differs from the dense GEMM of its rows"
+
+
+def test_grouped_gemm_offsets_past_m_are_clamped():
+    """A last offset beyond M is clamped to M: rows inside A are still right."""
+    counts = [40, 90]
+    aq, asf, ag, bq, bsf, bg, offsets = _experts_and_routing(2, 64, 512, counts, 9)
+    offsets[2] = 130 + 1000
+    c = nv.grouped_gemm(aq, asf, ag, bq, bsf, bg, offsets)
+    torch.cuda.synchronize()
+    want = oracle.grouped_gemm_f64(np_(aq), np_(asf), np_(ag)[0], np_(bq), np_(bsf), np_(bg),
+                                   np.array([0, 40, 130], np.int32))
+    assert rel_frobenius(np_(c), want) <= TOL

@@ -419,6 +419,32 @@ def test_gemm_f64_against_exact_triple_loop():
     assert np.allclose(Ct, C.T, rtol=1e-15)
 
 
+def test_grouped_gemm_f64_against_exact_sums():
+    """Each routed row uses its own expert's weight and scale; an empty expert
+    and rows of different experts are checked with exact rational sums."""
+    rng = np.random.default_rng(21)
+    E, N, K = 3, 2, 32
+    offsets = np.array([0, 2, 2, 5], dtype=np.int32)      # expert 1 receives no rows
+    a = bf16_bits(rng.standard_normal((5, K)))
+    aq, asf, ag = oracle.quantize(a)
+    w = [bf16_bits(rng.standard_normal((N, K)) * (e + 1) * 3) for e in range(E)]
+    enc = [oracle.quantize(x) for x in w]
+    bq = np.stack([t[0] for t in enc])
+    bsf = np.stack([t[1] for t in enc])
+    bg = np.array([t[2][0] for t in enc], dtype=np.float32)
+    C = oracle.grouped_gemm_f64(aq, asf, ag[0], bq, bsf, bg, offsets)
+    expert_of_row = [0, 0, 2, 2, 2]
+    for m in range(5):
+        e = expert_of_row[m]
+        for n in range(N):
+            s = sum(_exact_deq(aq, asf, m, k) * _exact_deq(bq[e], bsf[e], n, k) for k in range(K))
+            want = F(float(ag[0])) * F(float(bg[e])) * s
+            assert abs(F(C[m, n]) - want) <= abs(want) * F(1, 2 ** 48) + F(1, 2 ** 1000)
+    # routing a row to another expert changes its output (the expert index is used)
+    C2 = oracle.grouped_gemm_f64(aq, asf, ag[0], bq, bsf, bg, np.array([0, 3, 3, 5], np.int32))
+    assert not np.allclose(C2[2], C[2])
+
+
 def test_decode_qk_against_exact_sums():
     rng = np.random.default_rng(13)
     L, H, Hq, n, D = 2, 2, 8, 3, 32
