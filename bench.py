@@ -253,12 +253,17 @@ def run_extras(nv, synth, torch, which):
                 cache.append(c * C, k, v)
         ma = timed(torch, appends, 5, flush, warm=1)
         mqk = timed(torch, lambda: cache.decode_qk(qv, T, out=logits), 20, flush)
+        att = torch.empty((L, 4 * H, D), dtype=torch.float32, device="cuda")
+        aws = torch.empty(max(cache.attention_workspace_bytes(4 * H, T), 16), dtype=torch.uint8, device="cuda")
+        matt = timed(torch, lambda: cache.decode_attention(qv, T, D ** -0.5, out=att, workspace=aws), 20, flush)
         nvals = L * H * D * T
         app_bytes = 2 * nvals * 2 + 2 * (nvals // 2 + nvals // 16)
         qk_bytes = nvals // 2 + nvals // 16 + L * 4 * H * T * 4 + qv.numel() * 2
+        att_bytes = 2 * (nvals // 2 + nvals // 16) + qv.numel() * 2 + att.numel() * 4   # K and V once
         rows["kv_32x8x128_131072"] = {
             "append_512x256": {"ms": ma, "ms_per_chunk": ma / (T // C), **roof(app_bytes, ma, HBM_PEAK_GBS, "GB/s")},
             "decode_qk_32q": {"ms": mqk, **roof(qk_bytes, mqk, HBM_PEAK_GBS, "GB/s")},
+            "decode_attention_32q": {"ms": matt, **roof(att_bytes, matt, HBM_PEAK_GBS, "GB/s")},
             "cache_bytes": cache.nbytes()}
         del chunks, cache, logits
         torch.cuda.empty_cache()

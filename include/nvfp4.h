@@ -164,6 +164,27 @@ nvfp4_status nvfp4_kv_read(const nvfp4_kv_cache* cache, int32_t layer0, int32_t 
 nvfp4_status nvfp4_kv_decode_qk(const nvfp4_kv_cache* cache, const uint16_t* q, int32_t q_heads,
                                 int64_t n, float* logits, void* stream);
 
+/* One decode step of attention over the first n cached tokens, consuming
+ * the NVFP4 cache directly (decoding re-reads the whole cache each step:
+ * theddari.com, "What is FP4 quantization? KV cache in 4 bits", section "how
+ * does 4-bit KV change inference cost").  For layer l and query head hq
+ * (KV head h = hq / (q_heads/kv_heads)):
+ *   s_t = scale * sum_d q[l][hq][d] * Khat[l][h][t][d]            (t < n)
+ *   out[l][hq][d] = sum_t exp(s_t - max s) Vhat[l][h][t][d] / sum_t exp(s_t - max s)
+ * Khat, Vhat are the exact dequantized values; fp32 accumulation, fp32 exp.
+ * q: [layers][q_heads][head_dim] bf16; out: [layers][q_heads][head_dim] float.
+ * workspace: at least nvfp4_kv_attention_workspace_bytes(cache, q_heads, n)
+ *   bytes of device scratch (per-split partial results; no zero-fill needed).
+ * Errors: EINVAL (n < 1 or n > capacity, q_heads not a multiple of kv_heads,
+ *   non-finite scale, n * head_dim / 2 >= 2^30), ENOTSUP (head_dim/16 not a
+ *   power of two up to 16, or q_heads/kv_heads not 1, 2, 4 or 8),
+ *   EWORKSPACE, EALIGN, EHIP. */
+size_t nvfp4_kv_attention_workspace_bytes(const nvfp4_kv_cache* cache, int32_t q_heads, int64_t n);
+
+nvfp4_status nvfp4_kv_decode_attention(const nvfp4_kv_cache* cache, const uint16_t* q, int32_t q_heads,
+                                       int64_t n, float scale, float* out,
+                                       void* workspace, size_t workspace_bytes, void* stream);
+
 /* ------------------------------------------------------------------------
  * Block-scaled NVFP4 x NVFP4 GEMM for MoE expert linears, weights and
  * activations both NVFP4 (iwan.kr, "NVIDIA shrank GLM-5.2 to 4 bits",

@@ -58,6 +58,8 @@ _SIGS = {
     "nvfp4_kv_decode_qk": (_I32, [ctypes.POINTER(KVCacheDesc), _P, _I32, _I64, _P, _P]),
     "nvfp4_gemm": (_I32, [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P, _P]),
     "nvfp4_grouped_gemm": (_I32, [_P, _P, _P, _P, _P, _P, _P, _I32, _I64, _I64, _I64, _P, _P]),
+    "nvfp4_kv_attention_workspace_bytes": (ctypes.c_size_t, [_P, _I32, _I64]),
+    "nvfp4_kv_decode_attention": (_I32, [_P, _P, _I32, _I64, ctypes.c_float, _P, _P, ctypes.c_size_t, _P]),
 }
 
 _L = None
@@ -213,6 +215,22 @@ class KVCache:
         _check("nvfp4_kv_read", _lib().nvfp4_kv_read(
             ctypes.byref(self.desc), layer0, nlayers, t0, n, _ptr(k_out), _ptr(v_out), _stream(dev)))
         return k_out, v_out
+
+    def attention_workspace_bytes(self, q_heads, n):
+        return int(_lib().nvfp4_kv_attention_workspace_bytes(ctypes.byref(self.desc), q_heads, n))
+
+    def decode_attention(self, q, n, scale, out=None, workspace=None):
+        """One decode step of attention over the first n cached tokens:
+        softmax(scale * q K^T) V per query head, fp32 [layers][q_heads][head_dim]."""
+        _need(q, torch.bfloat16, "q")
+        L, Hq, D = q.shape
+        o = out if out is not None else torch.empty((L, Hq, D), dtype=torch.float32, device=q.device)
+        nb = self.attention_workspace_bytes(Hq, n)
+        ws = workspace if workspace is not None else torch.empty(max(nb, 16), dtype=torch.uint8, device=q.device)
+        _check("nvfp4_kv_decode_attention", _lib().nvfp4_kv_decode_attention(
+            ctypes.byref(self.desc), _ptr(q), Hq, n, float(scale), _ptr(o), _ptr(ws), ws.numel(),
+            _stream(q.device)))
+        return o
 
     def decode_qk(self, q, n, out=None):
         _need(q, torch.bfloat16, "q")

@@ -1,0 +1,334 @@
+// Decode-step attention over the NVFP4 KV cache: QK, softmax and P.V in one
+// pass over the cache, split over workgroups along the tokens (flash-decoding
+// style), then a small combine kernel.
+//
+// Decoding re-reads the whole KV cache every step, so storing it at 0.5625
+// bytes per value cuts the bytes each step moves (theddari.com, "What is FP4
+// quantization? KV cache in 4 bits", sections "KV cache size example" and
+// "how does 4-bit KV change inference cost").  Here the cache is consumed in
+// NVFP4 directly: K and V are decoded exactly in registers (E2M1 values from
+// the hardware conversion, block and tensor scales applied in fp32), with
+// nothing materialized in memory.
+//
+//   s_t  = scale * sum_d q[d] * Khat[t][d]
+//   out  = sum_t exp(s_t - max s) Vhat[t] / sum_t exp(s_t - max s)
+//
+// Split kernel, grid (splits, kv_heads, layers): a workgroup takes the GRP
+// query heads of one KV head (GQA) over one token range.  A token's head_dim
+// values are split over LPT = head_dim/16 lanes, 16 values (one block) per
+// lane: 8 code bytes and one scale byte of K and of V.  Each lane group keeps
+// its own running softmax state (max, sum, 16 output values per head) over
+// its tokens; the groups of a wave merge with lane shuffles and the waves of
+// the workgroup through LDS, and the workgroup writes one partial (max, sum,
+// head_dim unnormalized outputs) per query head.  The combine kernel merges
+// the splits: out = sum_s e^(m_s - M) o_s / sum_s e^(m_s - M) l_s.
+#include <algorithm>
+#include <cmath>
+
+#include "common.hpp"
+
+namespace nvfp4 {
+
+constexpr int kAttnThreads = 256;
+constexpr int kAttnWaves = kAttnThreads / 64;
+
+// Partial of one (layer, query head, split): max, sum, then head_dim outputs.
+__host__ __device__ constexpr int64_t attn_partial_floats(int head_dim) { return 2 + head_dim; }
+
+template <int LPT>
+__device__ __forceinline__ float attn_group_sum(float v) {
+  // sum over the LPT consecutive lanes of a token (LPT a power of two)
+  if (LPT >= 2) v += __shfl_xor(v, 1, 64);
+  if (LPT >= 4) v += __shfl_xor(v, 2, 64);
+  if (LPT >= 8) v += __shfl_xor(v, 4, 64);
+  if (LPT >= 16) v += __shfl_xor(v, 8, 64);
+  return v;
+}
+
+typedef __bf16 abf16x2 __attribute__((ext_vector_type(2)));
+
+// Merges softmax state (m2, l2, o2) into (m, l, o): the larger max wins and
+// the other side is rescaled (exp(-inf) = 0 covers empty states).
+template <int N>
+__device__ __forceinline__ void attn_merge(float& m, float& l, float (&o)[N], float m2, float l2, const float (&o2)[N]) {
+  const float mn = fmaxf(m, m2);
+  const float a = mn == -INFINITY ? 0.0f : __expf(m - mn);
+  const float b = mn == -INFINITY ? 0.0f : __expf(m2 - mn);
+  l = l * a + l2 * b;
+#pragma unroll
+  for (int d = 0; d < N; ++d) o[d] = o[d] * a + o2[d] * b;
+  m = mn;
+}
+
+template <int LPT, int GRP>
+__global__ void __launch_bounds__(kAttnThreads) kv_attn_split_kernel(nvfp4_kv_cache c, const uint32_t* __restrict__ q,
+                                                                     int q_heads, int64_t n, int64_t per_split,
+                                                                     float scale, float* __restrict__ part) {
+  constexpr int TPW = 64 / LPT;                          // tokens per wave
+  constexpr int D = 16 * LPT;
+  const int split = blockIdx.x, h = blockIdx.y, l = blockIdx.z;
+  const int H = c.kv_heads;
+  const int lane = threadIdx.x & 63, wave = wave_id();
+  const int j = lane % LPT;                              // this lane's block of the token
+  const int tg = lane / LPT;                             // token group within the wave
+  // query slices: 16 values (8 bf16 pairs) of block j for each of the GRP heads
+  uint32_t qv[GRP][8];
+#pragma unroll
+  for (int g = 0; g < GRP; ++g) {
+    const u32x4* qp = (const u32x4*)(q + ((int64_t)l * q_heads + h * GRP + g) * (D / 2) + j * 8);
+    const u32x4 a = qp[0], b = qp[1];
+    qv[g][0] = a.x; qv[g][1] = a.y; qv[g][2] = a.z; qv[g][3] = a.w;
+    qv[g][4] = b.x; qv[g][5] = b.y; qv[g][6] = b.z; qv[g][7] = b.w;
+  }
+  const float ks = c.k_g[l * H + h] * scale;            // tensor scale of K times the softmax scale
+  const float gv = c.v_g[l * H + h];
+  const int64_t row0 = ((int64_t)l * H + h) * c.capacity;
+  const int64_t t0 = (int64_t)split * per_split;
+  const int64_t t1 = std::min<int64_t>(n, t0 + per_split);
+  // buffer resources over this split's tokens of (layer, head): codes 8 bytes
+  // and one scale byte per lane and token; past t1 the loads read zeros
+  const int64_t cnt = t1 > t0 ? t1 - t0 : 0;
+  const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(c.k + (row0 + t0) * (D / 2)), 0, (int)(cnt * (D / 2)), kBufferWord3);
+  const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(c.v + (row0 + t0) * (D / 2)), 0, (int)(cnt * (D / 2)), kBufferWord3);
+  const __amdgpu_buffer_rsrc_t rks = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(c.k_sf + (row0 + t0) * LPT), 0, (int)(cnt * LPT), kBufferWord3);
+  const __amdgpu_buffer_rsrc_t rvs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(c.v_sf + (row0 + t0) * LPT), 0, (int)(cnt * LPT), kBufferWord3);
+
+  float m[GRP], ls[GRP], o[GRP][16];
+#pragma unroll
+  for (int g = 0; g < GRP; ++g) {
+    m[g] = -INFINITY;
+    ls[g] = 0.0f;
+#pragma unroll
+    for (int d = 0; d < 16; ++d) o[g][d] = 0.0f;
+  }
+  // token u (relative to t0) of this lane group in trip i: (i * waves + wave) * TPW + tg
+  const int64_t step = (int64_t)kAttnWaves * TPW;
+  int64_t u = (int64_t)wave * TPW + tg;
+  auto load = [&](int64_t uu, u32x2& kc, uint32_t& kb, u32x2& vc, uint32_t& vb) {
+    const uint32_t e = uu < cnt ? (uint32_t)(uu * LPT + j) : 0x10000000u;     // past the extents: zeros
+    kc = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rk, (int)(e * 8u), 0, 0));
+    vc = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rv, (int)(e * 8u), 0, 0));
+    kb = __builtin_amdgcn_raw_buffer_load_b8(rks, (int)e, 0, 0);
+    vb = __builtin_amdgcn_raw_buffer_load_b8(rvs, (int)e, 0, 0);
+  };
+  u32x2 kc, vc;
+  uint32_t kb, vb;
+  load(u, kc, kb, vc, vb);
+  // every lane of a wave runs the same trip count (the token group's own
+  // tokens end at cnt; the trailing lanes compute on zeros and are masked)
+  const int64_t trips = (cnt + step - 1) / step;
+  for (int64_t it = 0; it < trips; ++it, u += step) {
+    u32x2 kcn, vcn;
+    uint32_t kbn, vbn;
+    load(u + step, kcn, kbn, vcn, vbn);
+    const bool live = u < cnt;
+    // K block j: 16 exact E2M1 values as bf16 pairs, one scale
+    const float sk = __builtin_amdgcn_cvt_f32_fp8((int)kb, 0);
+    abf16x2 kp[8];
+    kp[0] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(kc.x, 1.0f, 0);
+    kp[1] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(kc.x, 1.0f, 1);
+    kp[2] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(kc.x, 1.0f, 2);
+    kp[3] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(kc.x, 1.0f, 3);
+    kp[4] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(kc.y, 1.0f, 0);
+    kp[5] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(kc.y, 1.0f, 1);
+    kp[6] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(kc.y, 1.0f, 2);
+    kp[7] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(kc.y, 1.0f, 3);
+    float s[GRP];
+#pragma unroll
+    for (int g = 0; g < GRP; ++g) {
+      float p = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) p = __builtin_amdgcn_fdot2_f32_bf16(kp[i], __builtin_bit_cast(abf16x2, qv[g][i]), p, false);
+      s[g] = attn_group_sum<LPT>(p * sk) * ks;          // this token's logit, in every lane of the group
+    }
+    // V block j: 16 exact E2M1 values in f32
+    const float sv = __builtin_amdgcn_cvt_f32_fp8((int)vb, 0) * gv;
+    float v[16];
+    f32x2 w;
+    w = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(vc.x, 1.0f, 0); v[0] = w.x; v[1] = w.y;
+    w = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(vc.x, 1.0f, 1); v[2] = w.x; v[3] = w.y;
+    w = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(vc.x, 1.0f, 2); v[4] = w.x; v[5] = w.y;
+    w = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(vc.x, 1.0f, 3); v[6] = w.x; v[7] = w.y;
+    w = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(vc.y, 1.0f, 0); v[8] = w.x; v[9] = w.y;
+    w = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(vc.y, 1.0f, 1); v[10] = w.x; v[11] = w.y;
+    w = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(vc.y, 1.0f, 2); v[12] = w.x; v[13] = w.y;
+    w = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(vc.y, 1.0f, 3); v[14] = w.x; v[15] = w.y;
+#pragma unroll
+    for (int g = 0; g < GRP; ++g) {
+      if (!live) continue;
+      if (s[g] > m[g]) {                                 // new running max: rescale (rare after warm-up)
+        const float r = __expf(m[g] - s[g]);
+        ls[g] *= r;
+#pragma unroll
+        for (int d = 0; d < 16; ++d) o[g][d] *= r;
+        m[g] = s[g];
+      }
+      const float p = __expf(s[g] - m[g]);
+      ls[g] += p;
+      const float pv = p * sv;
+#pragma unroll
+      for (int d = 0; d < 16; ++d) o[g][d] = __builtin_fmaf(pv, v[d], o[g][d]);
+    }
+    kc = kcn; kb = kbn; vc = vcn; vb = vbn;
+  }
+  // merge the token groups of the wave (lanes tg*LPT + j, same j)
+#pragma unroll
+  for (int sh = LPT; sh < 64; sh <<= 1) {
+#pragma unroll
+    for (int g = 0; g < GRP; ++g) {
+      const float m2 = __shfl_xor(m[g], sh, 64), l2 = __shfl_xor(ls[g], sh, 64);
+      float o2[16];
+#pragma unroll
+      for (int d = 0; d < 16; ++d) o2[d] = __shfl_xor(o[g][d], sh, 64);
+      attn_merge<16>(m[g], ls[g], o[g], m2, l2, o2);
+    }
+  }
+  // merge the waves through LDS: wave w's lanes 0..LPT-1 hold its state
+  __shared__ float st[kAttnWaves][GRP][2 + D];
+  if (lane < LPT) {
+#pragma unroll
+    for (int g = 0; g < GRP; ++g) {
+      st[wave][g][0] = m[g];
+      st[wave][g][1] = ls[g];
+#pragma unroll
+      for (int d = 0; d < 16; ++d) st[wave][g][2 + 16 * j + d] = o[g][d];
+    }
+  }
+  __syncthreads();
+  if (wave == 0 && lane < LPT) {
+#pragma unroll
+    for (int w2 = 1; w2 < kAttnWaves; ++w2)
+#pragma unroll
+      for (int g = 0; g < GRP; ++g) {
+        float o2[16];
+#pragma unroll
+        for (int d = 0; d < 16; ++d) o2[d] = st[w2][g][2 + 16 * j + d];
+        attn_merge<16>(m[g], ls[g], o[g], st[w2][g][0], st[w2][g][1], o2);
+      }
+    const int splits = gridDim.x;
+#pragma unroll
+    for (int g = 0; g < GRP; ++g) {
+      float* pp = part + (((int64_t)l * q_heads + h * GRP + g) * splits + split) * attn_partial_floats(D);
+      if (j == 0) {
+        pp[0] = m[g];
+        pp[1] = ls[g];
+      }
+#pragma unroll
+      for (int d = 0; d < 16; ++d) pp[2 + 16 * j + d] = o[g][d];
+    }
+  }
+}
+
+// grid (q_heads, layers), head_dim threads: merges the splits of one query head.
+__global__ void kv_attn_combine_kernel(const float* __restrict__ part, int splits, int head_dim,
+                                       float* __restrict__ out) {
+  const int hq = blockIdx.x, l = blockIdx.y, d = threadIdx.x;
+  const int q_heads = gridDim.x;
+  const float* pp = part + ((int64_t)l * q_heads + hq) * splits * attn_partial_floats(head_dim);
+  float M = -INFINITY;
+  for (int s = 0; s < splits; ++s) M = fmaxf(M, pp[s * attn_partial_floats(head_dim)]);
+  float num = 0.0f, den = 0.0f;
+  for (int s = 0; s < splits; ++s) {
+    const float* ps = pp + s * attn_partial_floats(head_dim);
+    const float w = ps[0] == -INFINITY ? 0.0f : __expf(ps[0] - M);
+    den = __builtin_fmaf(w, ps[1], den);
+    num = __builtin_fmaf(w, ps[2 + d], num);
+  }
+  out[((int64_t)l * q_heads + hq) * head_dim + d] = num / den;
+}
+
+}  // namespace nvfp4
+
+namespace {
+
+using namespace nvfp4;
+
+// Splits per (layer, KV head): about four workgroups per CU over the grid,
+// at least 64 tokens per split.
+int attn_splits(const nvfp4_kv_cache* c, int64_t n) {
+  const int64_t pairs = (int64_t)c->layers * c->kv_heads;
+  const int64_t want = std::max<int64_t>(1, ((int64_t)nvfp4host::num_cus() * 4 + pairs - 1) / pairs);
+  const int64_t most = std::max<int64_t>(1, (n + 63) / 64);
+  return (int)std::min<int64_t>(std::min(want, most), 1024);
+}
+
+bool attn_supported(const nvfp4_kv_cache* c, int32_t q_heads) {
+  const int lpt = c->head_dim / 16;
+  const int grp = q_heads / c->kv_heads;
+  return (lpt == 1 || lpt == 2 || lpt == 4 || lpt == 8 || lpt == 16) && (grp == 1 || grp == 2 || grp == 4 || grp == 8);
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t nvfp4_kv_attention_workspace_bytes(const nvfp4_kv_cache* c, int32_t q_heads, int64_t n) {
+  if (!c || c->layers <= 0 || c->kv_heads <= 0 || c->head_dim <= 0 || q_heads <= 0 || n <= 0) return 0;
+  return (size_t)c->layers * (size_t)q_heads * (size_t)attn_splits(c, n) *
+         (size_t)attn_partial_floats(c->head_dim) * sizeof(float);
+}
+
+nvfp4_status nvfp4_kv_decode_attention(const nvfp4_kv_cache* c, const uint16_t* q, int32_t q_heads, int64_t n,
+                                       float scale, float* out, void* workspace, size_t workspace_bytes,
+                                       void* stream) {
+  if (!c) return NVFP4_EINVAL;
+  if (c->layers <= 0 || c->kv_heads <= 0 || c->head_dim <= 0 || c->capacity < 0 || c->head_dim % kBlock)
+    return NVFP4_EINVAL;
+  if (c->kv_heads > 65535 || c->layers > 65535) return NVFP4_EINVAL;
+  if (!c->k || !c->v || !c->k_sf || !c->v_sf || !c->k_g || !c->v_g) return NVFP4_EINVAL;
+  if (q_heads <= 0 || q_heads % c->kv_heads) return NVFP4_EINVAL;
+  if (n <= 0 || n > c->capacity) return NVFP4_EINVAL;             // softmax needs at least one token
+  if (!q || !out || !std::isfinite(scale)) return NVFP4_EINVAL;
+  if (!attn_supported(c, q_heads)) return NVFP4_ENOTSUP;
+  if (n * (c->head_dim / 2) >= (INT64_C(1) << 30)) return NVFP4_EINVAL;   // 32-bit buffer offsets
+  if (!nvfp4host::aligned16(q) || !nvfp4host::aligned16(out) || !nvfp4host::aligned16(c->k) ||
+      !nvfp4host::aligned16(c->v))
+    return NVFP4_EALIGN;
+  if ((reinterpret_cast<uintptr_t>(c->k_g) & 3u) || (reinterpret_cast<uintptr_t>(c->v_g) & 3u)) return NVFP4_EALIGN;
+  if (!workspace || workspace_bytes < nvfp4_kv_attention_workspace_bytes(c, q_heads, n)) return NVFP4_EWORKSPACE;
+  if (!nvfp4host::aligned16(workspace)) return NVFP4_EALIGN;
+  nvfp4_status st = nvfp4host::check_device();
+  if (st) return st;
+  const int splits = attn_splits(c, n);
+  const int64_t per_split = (n + splits - 1) / splits;
+  const int lpt = c->head_dim / 16, grp = q_heads / c->kv_heads;
+  hipStream_t s = (hipStream_t)stream;
+  const dim3 grid(splits, c->kv_heads, c->layers);
+  const uint32_t* qa = (const uint32_t*)q;
+  float* part = (float*)workspace;
+#define NVFP4_ATTN(L, G) \
+  kv_attn_split_kernel<L, G><<<grid, kAttnThreads, 0, s>>>(*c, qa, q_heads, n, per_split, scale, part)
+  switch (lpt * 16 + grp) {
+    case 1 * 16 + 1: NVFP4_ATTN(1, 1); break;
+    case 1 * 16 + 2: NVFP4_ATTN(1, 2); break;
+    case 1 * 16 + 4: NVFP4_ATTN(1, 4); break;
+    case 1 * 16 + 8: NVFP4_ATTN(1, 8); break;
+    case 2 * 16 + 1: NVFP4_ATTN(2, 1); break;
+    case 2 * 16 + 2: NVFP4_ATTN(2, 2); break;
+    case 2 * 16 + 4: NVFP4_ATTN(2, 4); break;
+    case 2 * 16 + 8: NVFP4_ATTN(2, 8); break;
+    case 4 * 16 + 1: NVFP4_ATTN(4, 1); break;
+    case 4 * 16 + 2: NVFP4_ATTN(4, 2); break;
+    case 4 * 16 + 4: NVFP4_ATTN(4, 4); break;
+    case 4 * 16 + 8: NVFP4_ATTN(4, 8); break;
+    case 8 * 16 + 1: NVFP4_ATTN(8, 1); break;
+    case 8 * 16 + 2: NVFP4_ATTN(8, 2); break;
+    case 8 * 16 + 4: NVFP4_ATTN(8, 4); break;
+    case 8 * 16 + 8: NVFP4_ATTN(8, 8); break;
+    case 16 * 16 + 1: NVFP4_ATTN(16, 1); break;
+    case 16 * 16 + 2: NVFP4_ATTN(16, 2); break;
+    case 16 * 16 + 4: NVFP4_ATTN(16, 4); break;
+    default: NVFP4_ATTN(16, 8); break;
+  }
+#undef NVFP4_ATTN
+  NVFP4_LAUNCH_CHECK();
+  kv_attn_combine_kernel<<<dim3(q_heads, c->layers), c->head_dim, 0, s>>>(part, splits, c->head_dim, out);
+  NVFP4_LAUNCH_CHECK();
+  return NVFP4_OK;
+}
+
+}  // extern "C"

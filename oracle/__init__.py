@@ -245,6 +245,29 @@ def decode_qk_f64(q_bits: np.ndarray, kq: np.ndarray, ksf: np.ndarray, k_g: np.n
     return out
 
 
+def decode_attention_f64(q_bits, kq, ksf, k_g, vq, vsf, v_g, scale) -> np.ndarray:
+    """fp64 decode-step attention over the NVFP4 cache (decoding re-reads the
+    cache every step: theddari.com, "What is FP4 quantization? KV cache in 4
+    bits", section "how does 4-bit KV change inference cost").
+
+    For each layer l and query head hq (KV head hq // (Hq/H)):
+      s_t = scale * q . Khat_t,  p = softmax_t(s),  out = sum_t p_t Vhat_t,
+    with Khat, Vhat the exact fp64 dequantized values.  Returns [L][Hq][D].
+    """
+    logits = decode_qk_f64(q_bits, kq, ksf, k_g) * float(scale)
+    L, Hq, n = logits.shape
+    H, D = kq.shape[1], kq.shape[3] * 2
+    grp = Hq // H
+    out = np.empty((L, Hq, D), dtype=np.float64)
+    for l in range(L):
+        for h in range(H):
+            vhat = dequantize_f64_unscaled(vq[l, h], vsf[l, h]) * float(v_g[l, h])
+            s = logits[l, h * grp:(h + 1) * grp]
+            p = np.exp(s - s.max(axis=1, keepdims=True))
+            out[l, h * grp:(h + 1) * grp] = (p @ vhat) / p.sum(axis=1, keepdims=True)
+    return out
+
+
 # ---------------------------------------------------------------- GEMM
 def gemm_f64(a_q, a_sf, a_g, b_q, b_sf, b_g, rows=None) -> np.ndarray:
     """fp64 block-scaled GEMM  C[m][n] = gA*gB * sum_k deq(A)[m][k] * deq(B)[n][k].

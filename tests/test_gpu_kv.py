@@ -80,6 +80,38 @@ def test_append_read_non_pow2_head_dim():
         cache.decode_qk(qv, 10)
 
 
+@pytest.mark.parametrize("D,grp", [(128, 4), (64, 2), (32, 1), (256, 8), (16, 4), (128, 1)])
+def test_decode_attention_small(D, grp):
+    """Decode attention (QK, softmax, P.V) against the fp64 oracle for token
+    counts that leave ragged splits, including a single token."""
+    print("case: kv attention D", D, "grp", grp, flush=True)
+    L, H, cap = 2, 3, 700
+    cache, kg, vg = _cache(L, H, D, cap, 7 * D + grp)
+    gen = torch.Generator().manual_seed(3 * D + grp)
+    k = (torch.randn((L, cap, H, D), generator=gen) * 2).to(torch.bfloat16)
+    v = torch.randn((L, cap, H, D), generator=gen).to(torch.bfloat16)
+    cache.append(0, k.cuda(), v.cuda())
+    qv = torch.randn((L, H * grp, D), generator=gen).to(torch.bfloat16)
+    kq, ks, vq, vs = (np_(t) for t in (cache.k, cache.k_sf, cache.v, cache.v_sf))
+    scale = 1.0 / np.sqrt(D)
+    for n in (1, 63, 300, 700):
+        out = cache.decode_attention(qv.cuda(), n, scale)
+        torch.cuda.synchronize()
+        want = oracle.decode_attention_f64(bits(qv), kq[:, :, :n], ks[:, :, :n], kg, vq[:, :, :n], vs[:, :, :n],
+                                           vg, scale)
+        err = rel_frobenius(np_(out), want)
+        assert err <= QK_TOL, f"n={n}: rel Frobenius {err:.3e}"
+
+
+def test_decode_attention_rejects_unsupported_shapes():
+    cache, kg, vg = _cache(1, 2, 48, 10, 1)
+    with pytest.raises(nv.NVFP4Error):
+        cache.decode_attention(torch.zeros((1, 2, 48), dtype=torch.bfloat16, device="cuda"), 5, 0.1)
+    cache, kg, vg = _cache(1, 2, 64, 10, 1)
+    with pytest.raises(nv.NVFP4Error):                 # n = 0: a softmax over no tokens
+        cache.decode_attention(torch.zeros((1, 2, 64), dtype=torch.bfloat16, device="cuda"), 0, 0.1)
+
+
 def test_read_only_k_or_v():
     cache, kg, vg = _cache(2, 2, 64, 40, 3)
     k = torch.randn((2, 40, 2, 64)).to(torch.bfloat16)
@@ -129,4 +161,13 @@ def test_full_context_sampled():
     got = np_(logits[:, :, toks])
     err = rel_frobenius(got, want)
     assert err <= QK_TOL, f"rel Frobenius {err:.3e}"
+    # full decode attention over all 131072 tokens, checked on sampled (layer, KV head) pairs
+    out = np_(cache.decode_attention(qv, T, 1.0 / np.sqrt(D)))
+    for l, h in ((0, 0), (17, 5), (31, 7)):
+        want = oracle.decode_attention_f64(bits(qv)[l:l + 1, 4 * h:4 * h + 4], np_(cache.k[l:l + 1, h:h + 1]),
+                                           np_(cache.k_sf[l:l + 1, h:h + 1]), kgn[l:l + 1, h:h + 1],
+                                           np_(cache.v[l:l + 1, h:h + 1]), np_(cache.v_sf[l:l + 1, h:h + 1]),
+                                           vgn[l:l + 1, h:h + 1], 1.0 / np.sqrt(D))
+        err = rel_frobenius(out[l:l + 1, 4 * h:4 * h + 4], want)
+        assert err <= QK_TOL, f"attention l={l} h={h}: rel Frobenius {err:.3e}"
     del cache, logits

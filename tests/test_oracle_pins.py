@@ -445,6 +445,39 @@ def test_grouped_gemm_f64_against_exact_sums():
     assert not np.allclose(C2[2], C[2])
 
 
+def test_decode_attention_closed_forms():
+    """n = 1 gives the token's V exactly; q = 0 gives uniform weights (the mean
+    of the V rows); permuting tokens (K and V together) changes nothing; a
+    token whose logit dominates by far takes all the weight."""
+    rng = np.random.default_rng(31)
+    L, H, Hq, n, D = 2, 2, 4, 6, 32
+    k = bf16_bits(rng.standard_normal((L, n, H, D)))
+    v = bf16_bits(rng.standard_normal((L, n, H, D)))
+    kg = np.full((L, H), 0.002, np.float32)
+    vg = np.full((L, H), 0.0015, np.float32)
+    kq, ksf = oracle.kv_encode(k, kg)
+    vq, vsf = oracle.kv_encode(v, vg)
+    qv = bf16_bits(rng.standard_normal((L, Hq, D)))
+    vhat = np.stack([[oracle.dequantize_f64_unscaled(vq[l, h], vsf[l, h]) * float(vg[l, h])
+                      for h in range(H)] for l in range(L)])                  # [L][H][n][D]
+    one = oracle.decode_attention_f64(qv, kq[:, :, :1], ksf[:, :, :1], kg, vq[:, :, :1], vsf[:, :, :1], vg, 0.3)
+    for hq in range(Hq):
+        assert np.array_equal(one[:, hq], vhat[:, hq // 2, 0])
+    zero = oracle.decode_attention_f64(np.zeros_like(qv), kq, ksf, kg, vq, vsf, vg, 0.3)
+    for hq in range(Hq):
+        assert np.allclose(zero[:, hq], vhat[:, hq // 2].mean(axis=1), rtol=1e-14, atol=1e-15)
+    perm = rng.permutation(n)
+    a = oracle.decode_attention_f64(qv, kq, ksf, kg, vq, vsf, vg, 0.3)
+    b = oracle.decode_attention_f64(qv, kq[:, :, perm], ksf[:, :, perm], kg, vq[:, :, perm], vsf[:, :, perm], vg, 0.3)
+    assert np.allclose(a, b, rtol=1e-13, atol=1e-15)
+    big = oracle.decode_attention_f64(qv, kq, ksf, kg, vq, vsf, vg, 1e6)   # the arg-max token wins
+    logits = oracle.decode_qk_f64(qv, kq, ksf, kg)
+    for l in range(L):
+        for hq in range(Hq):
+            t = int(np.argmax(logits[l, hq]))
+            assert np.allclose(big[l, hq], vhat[l, hq // 2, t], rtol=1e-12, atol=1e-15)
+
+
 def test_decode_qk_against_exact_sums():
     rng = np.random.default_rng(13)
     L, H, Hq, n, D = 2, 2, 8, 3, 32
