@@ -35,29 +35,33 @@ constexpr int kAttnWaves = kAttnThreads / 64;
 // Partial of one (layer, query head, split): max, sum, then head_dim outputs.
 __host__ __device__ constexpr int64_t attn_partial_floats(int head_dim) { return 2 + head_dim; }
 
+template <int kCtrl>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), kCtrl, 0xF, 0xF, false));
+}
+
+// Sum over the LPT consecutive lanes of a token (LPT a power of two up to
+// 16), all in DPP: lane i ^ 1, lane i ^ 2 (quad permutations), then the
+// mirror within 8 lanes and within 16 lanes, each of which pairs the two
+// halves of the group summed so far.
 template <int LPT>
 __device__ __forceinline__ float attn_group_sum(float v) {
-  // sum over the LPT consecutive lanes of a token (LPT a power of two)
-  if (LPT >= 2) v += __shfl_xor(v, 1, 64);
-  if (LPT >= 4) v += __shfl_xor(v, 2, 64);
-  if (LPT >= 8) v += __shfl_xor(v, 4, 64);
-  if (LPT >= 16) v += __shfl_xor(v, 8, 64);
+  if (LPT >= 2) v += dpp_f<0xB1>(v);                   // quad_perm [1,0,3,2]
+  if (LPT >= 4) v += dpp_f<0x4E>(v);                   // quad_perm [2,3,0,1]
+  if (LPT >= 8) v += dpp_f<0x141>(v);                  // row_half_mirror
+  if (LPT >= 16) v += dpp_f<0x140>(v);                 // row_mirror
   return v;
 }
 
 typedef __bf16 abf16x2 __attribute__((ext_vector_type(2)));
 
-// Merges softmax state (m2, l2, o2) into (m, l, o): the larger max wins and
-// the other side is rescaled (exp(-inf) = 0 covers empty states).
-template <int N>
-__device__ __forceinline__ void attn_merge(float& m, float& l, float (&o)[N], float m2, float l2, const float (&o2)[N]) {
-  const float mn = fmaxf(m, m2);
-  const float a = mn == -INFINITY ? 0.0f : __expf(m - mn);
-  const float b = mn == -INFINITY ? 0.0f : __expf(m2 - mn);
-  l = l * a + l2 * b;
-#pragma unroll
-  for (int d = 0; d < N; ++d) o[d] = o[d] * a + o2[d] * b;
-  m = mn;
+// Weights of two softmax states with maxima m and m2 after merging:
+// a = exp(m - M), b = exp(m2 - M), M = max(m, m2) (exp(-inf) = 0 covers
+// empty states).
+__device__ __forceinline__ void attn_weights(float m, float m2, float& mn, float& a, float& b) {
+  mn = fmaxf(m, m2);
+  a = mn == -INFINITY ? 0.0f : __expf(m - mn);
+  b = mn == -INFINITY ? 0.0f : __expf(m2 - mn);
 }
 
 template <int LPT, int GRP>
@@ -159,15 +163,18 @@ __global__ void __launch_bounds__(kAttnThreads) kv_attn_split_kernel(nvfp4_kv_ca
     w = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(vc.y, 1.0f, 3); v[14] = w.x; v[15] = w.y;
 #pragma unroll
     for (int g = 0; g < GRP; ++g) {
-      if (!live) continue;
-      if (s[g] > m[g]) {                                 // new running max: rescale (rare after warm-up)
-        const float r = __expf(m[g] - s[g]);
+      const float sg = live ? s[g] : -INFINITY;         // lanes past the split add nothing
+      // a new running max somewhere in the wave: rescale (a wave-uniform
+      // branch, rare after the first tokens)
+      if (__builtin_amdgcn_ballot_w64(sg > m[g])) {
+        const float mn = fmaxf(m[g], sg);
+        const float r = mn == -INFINITY ? 1.0f : __expf(m[g] - mn);
         ls[g] *= r;
 #pragma unroll
         for (int d = 0; d < 16; ++d) o[g][d] *= r;
-        m[g] = s[g];
+        m[g] = mn;
       }
-      const float p = __expf(s[g] - m[g]);
+      const float p = sg == -INFINITY ? 0.0f : __expf(sg - m[g]);
       ls[g] += p;
       const float pv = p * sv;
 #pragma unroll
@@ -175,51 +182,55 @@ __global__ void __launch_bounds__(kAttnThreads) kv_attn_split_kernel(nvfp4_kv_ca
     }
     kc = kcn; kb = kbn; vc = vcn; vb = vbn;
   }
-  // merge the token groups of the wave (lanes tg*LPT + j, same j)
+  // merge the token groups of the wave (lanes tg*LPT + j, same j), one
+  // head and one output at a time
 #pragma unroll
   for (int sh = LPT; sh < 64; sh <<= 1) {
 #pragma unroll
     for (int g = 0; g < GRP; ++g) {
-      const float m2 = __shfl_xor(m[g], sh, 64), l2 = __shfl_xor(ls[g], sh, 64);
-      float o2[16];
+      float mn, a, b;
+      attn_weights(m[g], __shfl_xor(m[g], sh, 64), mn, a, b);
+      ls[g] = ls[g] * a + __shfl_xor(ls[g], sh, 64) * b;
 #pragma unroll
-      for (int d = 0; d < 16; ++d) o2[d] = __shfl_xor(o[g][d], sh, 64);
-      attn_merge<16>(m[g], ls[g], o[g], m2, l2, o2);
+      for (int d = 0; d < 16; ++d) o[g][d] = o[g][d] * a + __shfl_xor(o[g][d], sh, 64) * b;
+      m[g] = mn;
     }
   }
-  // merge the waves through LDS: wave w's lanes 0..LPT-1 hold its state
+  // merge the waves through LDS: lanes 0..LPT-1 of each wave hold its
+  // state; then every thread merges (head, output) pairs of the workgroup,
+  // with the loop state dead by then
   __shared__ float st[kAttnWaves][GRP][2 + D];
   if (lane < LPT) {
 #pragma unroll
     for (int g = 0; g < GRP; ++g) {
-      st[wave][g][0] = m[g];
-      st[wave][g][1] = ls[g];
+      if (j == 0) {
+        st[wave][g][0] = m[g];
+        st[wave][g][1] = ls[g];
+      }
 #pragma unroll
       for (int d = 0; d < 16; ++d) st[wave][g][2 + 16 * j + d] = o[g][d];
     }
   }
   __syncthreads();
-  if (wave == 0 && lane < LPT) {
+  const int splits = gridDim.x;
+  for (int e = threadIdx.x; e < GRP * D; e += kAttnThreads) {
+    const int g = e / D, d = e % D;
+    float mx = st[0][g][0];
 #pragma unroll
-    for (int w2 = 1; w2 < kAttnWaves; ++w2)
+    for (int w = 1; w < kAttnWaves; ++w) mx = fmaxf(mx, st[w][g][0]);
+    float num = 0.0f, den = 0.0f;
 #pragma unroll
-      for (int g = 0; g < GRP; ++g) {
-        float o2[16];
-#pragma unroll
-        for (int d = 0; d < 16; ++d) o2[d] = st[w2][g][2 + 16 * j + d];
-        attn_merge<16>(m[g], ls[g], o[g], st[w2][g][0], st[w2][g][1], o2);
-      }
-    const int splits = gridDim.x;
-#pragma unroll
-    for (int g = 0; g < GRP; ++g) {
-      float* pp = part + (((int64_t)l * q_heads + h * GRP + g) * splits + split) * attn_partial_floats(D);
-      if (j == 0) {
-        pp[0] = m[g];
-        pp[1] = ls[g];
-      }
-#pragma unroll
-      for (int d = 0; d < 16; ++d) pp[2 + 16 * j + d] = o[g][d];
+    for (int w = 0; w < kAttnWaves; ++w) {
+      const float a = st[w][g][0] == -INFINITY ? 0.0f : __expf(st[w][g][0] - mx);
+      den = __builtin_fmaf(a, st[w][g][1], den);
+      num = __builtin_fmaf(a, st[w][g][2 + d], num);
     }
+    float* pp = part + (((int64_t)l * q_heads + h * GRP + g) * splits + split) * attn_partial_floats(D);
+    if (d == 0) {
+      pp[0] = mx;
+      pp[1] = den;
+    }
+    pp[2 + d] = num;
   }
 }
 
