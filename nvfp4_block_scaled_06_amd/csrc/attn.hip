@@ -23,6 +23,7 @@
 // head_dim unnormalized outputs) per query head.  The combine kernel merges
 // the splits: out = sum_s e^(m_s - M) o_s / sum_s e^(m_s - M) l_s.
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 
 #include "common.hpp"
@@ -258,19 +259,53 @@ namespace {
 
 using namespace nvfp4;
 
-// Splits per (layer, KV head): about four workgroups per CU over the grid,
-// at least 64 tokens per split.
-int attn_splits(const nvfp4_kv_cache* c, int64_t n) {
+constexpr int kAttnMaxBlocksPerCU = 2048 / kAttnThreads;   // 32 waves per CU
+
+typedef void (*attn_kernel_t)(nvfp4_kv_cache, const uint32_t*, int, int64_t, int64_t, float, float*);
+
+// Index of (head_dim/16, q_heads/kv_heads) in the instantiation table, or
+// -1 when the shape has no kernel.
+int attn_index(const nvfp4_kv_cache* c, int32_t q_heads) {
+  const int lpt = c->head_dim / 16, grp = q_heads / c->kv_heads;
+  const int li = lpt == 1 ? 0 : lpt == 2 ? 1 : lpt == 4 ? 2 : lpt == 8 ? 3 : lpt == 16 ? 4 : -1;
+  const int gi = grp == 1 ? 0 : grp == 2 ? 1 : grp == 4 ? 2 : grp == 8 ? 3 : -1;
+  return li < 0 || gi < 0 ? -1 : li * 4 + gi;
+}
+
+const attn_kernel_t kAttnKernels[20] = {
+    kv_attn_split_kernel<1, 1>,  kv_attn_split_kernel<1, 2>,  kv_attn_split_kernel<1, 4>,  kv_attn_split_kernel<1, 8>,
+    kv_attn_split_kernel<2, 1>,  kv_attn_split_kernel<2, 2>,  kv_attn_split_kernel<2, 4>,  kv_attn_split_kernel<2, 8>,
+    kv_attn_split_kernel<4, 1>,  kv_attn_split_kernel<4, 2>,  kv_attn_split_kernel<4, 4>,  kv_attn_split_kernel<4, 8>,
+    kv_attn_split_kernel<8, 1>,  kv_attn_split_kernel<8, 2>,  kv_attn_split_kernel<8, 4>,  kv_attn_split_kernel<8, 8>,
+    kv_attn_split_kernel<16, 1>, kv_attn_split_kernel<16, 2>, kv_attn_split_kernel<16, 4>, kv_attn_split_kernel<16, 8>,
+};
+
+// Resident workgroups per CU of a split kernel (register and LDS limits),
+// asked of the runtime once per instantiation.
+int attn_blocks_per_cu(int idx) {
+  static std::atomic<int> cache[20];
+  int b = cache[idx].load(std::memory_order_relaxed);
+  if (b > 0) return b;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, reinterpret_cast<const void*>(kAttnKernels[idx]),
+                                                   kAttnThreads, 0) != hipSuccess || b <= 0)
+    b = 1;
+  b = std::min(b, kAttnMaxBlocksPerCU);
+  cache[idx].store(b, std::memory_order_relaxed);
+  return b;
+}
+
+// Splits per (layer, KV head): one full round of resident workgroups over
+// the chip (no partly filled second round), at least 64 tokens per split.
+int attn_splits(const nvfp4_kv_cache* c, int64_t n, int blocks_per_cu) {
   const int64_t pairs = (int64_t)c->layers * c->kv_heads;
-  const int64_t want = std::max<int64_t>(1, ((int64_t)nvfp4host::num_cus() * 4 + pairs - 1) / pairs);
+  const int64_t want = std::max<int64_t>(1, ((int64_t)nvfp4host::num_cus() * blocks_per_cu + pairs - 1) / pairs);
   const int64_t most = std::max<int64_t>(1, (n + 63) / 64);
   return (int)std::min<int64_t>(std::min(want, most), 1024);
 }
 
-bool attn_supported(const nvfp4_kv_cache* c, int32_t q_heads) {
-  const int lpt = c->head_dim / 16;
-  const int grp = q_heads / c->kv_heads;
-  return (lpt == 1 || lpt == 2 || lpt == 4 || lpt == 8 || lpt == 16) && (grp == 1 || grp == 2 || grp == 4 || grp == 8);
+size_t attn_workspace(const nvfp4_kv_cache* c, int32_t q_heads, int splits) {
+  return (size_t)c->layers * (size_t)q_heads * (size_t)splits * (size_t)attn_partial_floats(c->head_dim) *
+         sizeof(float);
 }
 
 }  // namespace
@@ -279,8 +314,8 @@ extern "C" {
 
 size_t nvfp4_kv_attention_workspace_bytes(const nvfp4_kv_cache* c, int32_t q_heads, int64_t n) {
   if (!c || c->layers <= 0 || c->kv_heads <= 0 || c->head_dim <= 0 || q_heads <= 0 || n <= 0) return 0;
-  return (size_t)c->layers * (size_t)q_heads * (size_t)attn_splits(c, n) *
-         (size_t)attn_partial_floats(c->head_dim) * sizeof(float);
+  // an upper bound over every occupancy the split kernels can have
+  return attn_workspace(c, q_heads, attn_splits(c, n, kAttnMaxBlocksPerCU));
 }
 
 nvfp4_status nvfp4_kv_decode_attention(const nvfp4_kv_cache* c, const uint16_t* q, int32_t q_heads, int64_t n,
@@ -294,7 +329,8 @@ nvfp4_status nvfp4_kv_decode_attention(const nvfp4_kv_cache* c, const uint16_t* 
   if (q_heads <= 0 || q_heads % c->kv_heads) return NVFP4_EINVAL;
   if (n <= 0 || n > c->capacity) return NVFP4_EINVAL;             // softmax needs at least one token
   if (!q || !out || !std::isfinite(scale)) return NVFP4_EINVAL;
-  if (!attn_supported(c, q_heads)) return NVFP4_ENOTSUP;
+  const int idx = attn_index(c, q_heads);
+  if (idx < 0) return NVFP4_ENOTSUP;
   if (n * (c->head_dim / 2) >= (INT64_C(1) << 30)) return NVFP4_EINVAL;   // 32-bit buffer offsets
   if (!nvfp4host::aligned16(q) || !nvfp4host::aligned16(out) || !nvfp4host::aligned16(c->k) ||
       !nvfp4host::aligned16(c->v))
@@ -304,38 +340,13 @@ nvfp4_status nvfp4_kv_decode_attention(const nvfp4_kv_cache* c, const uint16_t* 
   if (!nvfp4host::aligned16(workspace)) return NVFP4_EALIGN;
   nvfp4_status st = nvfp4host::check_device();
   if (st) return st;
-  const int splits = attn_splits(c, n);
+  const int splits = attn_splits(c, n, attn_blocks_per_cu(idx));
   const int64_t per_split = (n + splits - 1) / splits;
-  const int lpt = c->head_dim / 16, grp = q_heads / c->kv_heads;
   hipStream_t s = (hipStream_t)stream;
   const dim3 grid(splits, c->kv_heads, c->layers);
   const uint32_t* qa = (const uint32_t*)q;
   float* part = (float*)workspace;
-#define NVFP4_ATTN(L, G) \
-  kv_attn_split_kernel<L, G><<<grid, kAttnThreads, 0, s>>>(*c, qa, q_heads, n, per_split, scale, part)
-  switch (lpt * 16 + grp) {
-    case 1 * 16 + 1: NVFP4_ATTN(1, 1); break;
-    case 1 * 16 + 2: NVFP4_ATTN(1, 2); break;
-    case 1 * 16 + 4: NVFP4_ATTN(1, 4); break;
-    case 1 * 16 + 8: NVFP4_ATTN(1, 8); break;
-    case 2 * 16 + 1: NVFP4_ATTN(2, 1); break;
-    case 2 * 16 + 2: NVFP4_ATTN(2, 2); break;
-    case 2 * 16 + 4: NVFP4_ATTN(2, 4); break;
-    case 2 * 16 + 8: NVFP4_ATTN(2, 8); break;
-    case 4 * 16 + 1: NVFP4_ATTN(4, 1); break;
-    case 4 * 16 + 2: NVFP4_ATTN(4, 2); break;
-    case 4 * 16 + 4: NVFP4_ATTN(4, 4); break;
-    case 4 * 16 + 8: NVFP4_ATTN(4, 8); break;
-    case 8 * 16 + 1: NVFP4_ATTN(8, 1); break;
-    case 8 * 16 + 2: NVFP4_ATTN(8, 2); break;
-    case 8 * 16 + 4: NVFP4_ATTN(8, 4); break;
-    case 8 * 16 + 8: NVFP4_ATTN(8, 8); break;
-    case 16 * 16 + 1: NVFP4_ATTN(16, 1); break;
-    case 16 * 16 + 2: NVFP4_ATTN(16, 2); break;
-    case 16 * 16 + 4: NVFP4_ATTN(16, 4); break;
-    default: NVFP4_ATTN(16, 8); break;
-  }
-#undef NVFP4_ATTN
+  kAttnKernels[idx]<<<grid, kAttnThreads, 0, s>>>(*c, qa, q_heads, n, per_split, scale, part);
   NVFP4_LAUNCH_CHECK();
   kv_attn_combine_kernel<<<dim3(q_heads, c->layers), c->head_dim, 0, s>>>(part, splits, c->head_dim, out);
   NVFP4_LAUNCH_CHECK();
