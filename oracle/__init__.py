@@ -13,7 +13,10 @@ model on 10 trillion tokens", section "E2M1 format and two-level scaling";
 theddari.com, "What is FP4 quantization? KV cache in 4 bits", format table);
 the KV cache layout per token (theddari.com, same page, "KV cache size
 example"); NVFP4 for weights and activations of MoE expert linears
-(iwan.kr, "NVIDIA shrank GLM-5.2 to 4 bits", section 1).
+(iwan.kr, "NVIDIA shrank GLM-5.2 to 4 bits", section 1).  The MXFP4 variant
+(32-value blocks, one power-of-two scale each, no tensor scale; iwan.kr, same
+page, section 3; theddari.com, format table) follows the published
+Microscaling exponent rule, which the pages leave open.
 
 Parity pins live in tests/test_oracle_*.py; functions without an independent
 pin would say "parity unpinned" here -- every function below has one.
@@ -53,11 +56,20 @@ def lib():
         L.orc_decode_element.restype = ctypes.c_float
         L.orc_decode_element.argtypes = [i32, i32, ctypes.c_float]
         L.orc_max_threads.restype = i32
+        L.orc_e8m0_value.restype = ctypes.c_double
+        L.orc_e8m0_value.argtypes = [i32]
+        L.orc_mx_block_scale.restype = i32
+        L.orc_mx_block_scale.argtypes = [ctypes.c_float]
+        L.orc_mx_decode_element.restype = ctypes.c_float
+        L.orc_mx_decode_element.argtypes = [i32, i32]
         for name, args in {
             "orc_quantize": [P, i64, i64, i64, P, P, P, i32],
             "orc_quantize_with_scale": [P, i64, i64, i64, P, P, P, i32],
             "orc_dequantize": [P, P, P, i64, i64, i64, P, i32],
             "orc_dequantize_f64_unscaled": [P, P, i64, i64, P, i32],
+            "orc_mx_quantize": [P, i64, i64, P, P, i32],
+            "orc_mx_dequantize": [P, P, i64, i64, P, i32],
+            "orc_mx_dequantize_f64": [P, P, i64, i64, P, i32],
         }.items():
             getattr(L, name).restype = i32
             getattr(L, name).argtypes = args
@@ -178,6 +190,8 @@ def dequantize(q: np.ndarray, sf: np.ndarray, g: np.ndarray, nthreads: int = 0) 
         b, r = 1, q.shape[0]
     else:
         b, r = q.shape[0], q.shape[1]
+    if sf.shape != q.shape[:-1] + (c // 16,):
+        raise ValueError("oracle dequantize: scales must match the codes' rows, cols/16")
     g = np.ascontiguousarray(np.asarray(g, dtype=np.float32).reshape(b))
     y = np.empty(q.shape[:-1] + (c,), dtype=np.uint16)
     rc = lib().orc_dequantize(_p(q), _p(sf), _p(g), b, r, c, _p(y), nthreads)
@@ -192,6 +206,8 @@ def dequantize_f64_unscaled(q: np.ndarray, sf: np.ndarray, nthreads: int = 0) ->
     sf = np.ascontiguousarray(sf, dtype=np.uint8)
     rows = int(np.prod(q.shape[:-1])) if q.ndim > 1 else 1
     c = q.shape[-1] * 2
+    if sf.size != rows * (c // 16):
+        raise ValueError("oracle dequantize_f64: scales must match the codes' rows, cols/16")
     y = np.empty(q.shape[:-1] + (c,), dtype=np.float64)
     rc = lib().orc_dequantize_f64_unscaled(_p(q), _p(sf), rows, c, _p(y), nthreads)
     if rc != 0:
@@ -301,3 +317,67 @@ def grouped_gemm_f64(a_q, a_sf, a_g, b_q, b_sf, b_g, offsets) -> np.ndarray:
             C[r0:r1] = gemm_f64(a_q[r0:r1], a_sf[r0:r1], a_g, b_q[e], b_sf[e], b_g[e])
     return C
 
+
+# ---------------------------------------------------------------- MXFP4
+# 32-value blocks with one power-of-two (E8M0) scale and no tensor scale
+# (iwan.kr, "NVIDIA shrank GLM-5.2 to 4 bits", section 3; theddari.com, "What
+# is FP4 quantization? KV cache in 4 bits", format comparison table).  The
+# exponent rule is the published Microscaling definition; see nvfp4_oracle.c.
+def e8m0_value(byte: int) -> float:
+    return lib().orc_e8m0_value(int(byte))
+
+
+def mx_block_scale(bamax: float) -> int:
+    return lib().orc_mx_block_scale(float(bamax))
+
+
+def mx_decode_element(code: int, sbyte: int) -> float:
+    return lib().orc_mx_decode_element(int(code), int(sbyte))
+
+
+def mx_quantize(x_bits: np.ndarray, nthreads: int = 0):
+    """x_bits: uint16 bf16 bit patterns [rows][cols] (cols % 32 == 0).
+    Returns (q [rows][cols/2] u8, sf [rows][cols/32] u8)."""
+    x = np.ascontiguousarray(x_bits, dtype=np.uint16)
+    rows, cols = x.shape
+    q = np.empty((rows, cols // 2), dtype=np.uint8)
+    sf = np.empty((rows, cols // 32), dtype=np.uint8)
+    if lib().orc_mx_quantize(_p(x), rows, cols, _p(q), _p(sf), nthreads) != 0:
+        raise ValueError("mx_quantize: bad shape or non-finite input")
+    return q, sf
+
+
+def mx_dequantize(q: np.ndarray, sf: np.ndarray, nthreads: int = 0) -> np.ndarray:
+    """Returns bf16 bit patterns [rows][cols], cols = 2 * q.shape[1]."""
+    q = np.ascontiguousarray(q, dtype=np.uint8)
+    sf = np.ascontiguousarray(sf, dtype=np.uint8)
+    rows, cols = q.shape[0], 2 * q.shape[1]
+    if sf.shape != (rows, cols // 32):
+        raise ValueError("mx_dequantize: scales must be [rows][cols/32]")
+    y = np.empty((rows, cols), dtype=np.uint16)
+    if lib().orc_mx_dequantize(_p(q), _p(sf), rows, cols, _p(y), nthreads) != 0:
+        raise ValueError("mx_dequantize: bad shape")
+    return y
+
+
+def mx_dequantize_f64(q: np.ndarray, sf: np.ndarray, nthreads: int = 0) -> np.ndarray:
+    """Exact fp64 E2M1(code) * 2^X of every element, [rows][cols]."""
+    q = np.ascontiguousarray(q, dtype=np.uint8)
+    sf = np.ascontiguousarray(sf, dtype=np.uint8)
+    rows, cols = q.shape[0], 2 * q.shape[1]
+    if sf.shape != (rows, cols // 32):
+        raise ValueError("mx_dequantize_f64: scales must be [rows][cols/32]")
+    y = np.empty((rows, cols), dtype=np.float64)
+    if lib().orc_mx_dequantize_f64(_p(q), _p(sf), rows, cols, _p(y), nthreads) != 0:
+        raise ValueError("mx_dequantize_f64: bad shape")
+    return y
+
+
+def mx_gemm_f64(a_q, a_sf, b_q, b_sf, rows=None) -> np.ndarray:
+    """fp64 MXFP4 GEMM  C[m][n] = sum_k deq(A)[m][k] * deq(B)[n][k] (both
+    K-major, exact fp64 dequantization, library matmul).  `rows` optionally
+    restricts to a subset of A's rows."""
+    if rows is not None:
+        a_q = a_q[rows]
+        a_sf = a_sf[rows]
+    return mx_dequantize_f64(a_q, a_sf) @ mx_dequantize_f64(b_q, b_sf).T

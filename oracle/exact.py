@@ -120,3 +120,33 @@ def dequant_value(code: int, sbyte: int, g: F) -> F:
     """RN32((E2M1(code) * s) * g) with the sign of code bit 3 (exact rational)."""
     v = rn32(E2M1[code & 7] * E4M3[sbyte] * g)
     return -v if code & 8 else v
+
+
+# ---------------------------------------------------------------- MXFP4
+# 32-value blocks with one power-of-two scale 2^X (E8M0 byte X + 127) and no
+# tensor scale; X = floor(log2(block amax)) - 2 clamped to [-127, 127] (the
+# published Microscaling rule; an all-zero block takes X = -127).
+def floor_log2(a: F) -> int:
+    """The integer e with 2^e <= a < 2^(e+1), for a > 0, from the bit lengths
+    of a's numerator and denominator."""
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    return e if F(2) ** e <= a else e - 1
+
+
+def mx_quantize_rows(x_bits):
+    """x_bits: list of rows of bf16 bit patterns, len(row) % 32 == 0.
+    Returns (codes per row, scale bytes per row)."""
+    codes, scales = [], []
+    for brow in x_bits:
+        row = [bf16_to_fraction(b) for b in brow]
+        rc, rs = [], []
+        for b in range(len(row) // 32):
+            blk, bb = row[32 * b:32 * b + 32], brow[32 * b:32 * b + 32]
+            bamax = max(abs(v) for v in blk)
+            X = -127 if bamax == 0 else min(127, max(-127, floor_log2(bamax) - 2))
+            rs.append(X + 127)
+            for v, bits in zip(blk, bb):
+                rc.append((((bits >> 15) & 1) << 3) | e2m1_rne_sat(rn32(abs(v) / F(2) ** X)))
+        codes.append(rc)
+        scales.append(rs)
+    return codes, scales

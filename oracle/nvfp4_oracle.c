@@ -278,3 +278,110 @@ void orc_f32_to_bf16_array(const float* f, int64_t n, uint16_t* out, int nthread
 #pragma omp parallel for
   for (int64_t i = 0; i < n; ++i) out[i] = orc_f32_to_bf16(f[i]);
 }
+
+/* ---------- MXFP4: 32-value blocks, power-of-two scale, no tensor scale ----------
+ *
+ * The earlier microscaling format shares one power-of-two (UE8M0) scale among
+ * 32 E2M1 values, about 4.25 bits per value (iwan.kr, "NVIDIA shrank GLM-5.2
+ * to 4 bits", section 3 "Terminology"; axbrief.com, "NVFP4: how NVIDIA
+ * pre-trained a 12B model on 10 trillion tokens", sections "E2M1 format and
+ * two-level scaling" and "36% token efficiency and Blackwell speed";
+ * theddari.com, "What is FP4 quantization? KV cache in 4 bits", format
+ * comparison table).  The pages do not say how the exponent is chosen; the
+ * reading here is the published Microscaling (MX) definition of the format:
+ *   X = floor(log2(block amax)) - 2     (2 = exponent of E2M1's largest value,
+ *                                         6 = 1.5 * 2^2), clamped to [-127, 127];
+ *                                        an all-zero block takes X = -127
+ *   scale byte = X + 127                 (E8M0: value 2^(byte-127), 255 = NaN)
+ *   code = sign(x)<<3 | E2M1_RNE_SAT(RN32(|x| / 2^X))
+ *   dequant: bf16_RNE(RN32(E2M1(code) * 2^X))
+ * Values between 6 * 2^X and 8 * 2^X saturate to 6 * 2^X.  Codes are packed
+ * as for NVFP4 (element 2j in the low nibble of byte j). */
+
+double orc_e8m0_value(int byte) { return byte == 255 ? NAN : ldexp(1.0, byte - 127); }
+
+/* Scale byte of a block from its amax (>= 0, finite); -1 otherwise.  The
+ * exponent floor(log2(bamax)) is found by search: the largest e with
+ * 2^e <= bamax. */
+int orc_mx_block_scale(float bamax) {
+  if (!(bamax >= 0.0f) || isinf(bamax)) return -1;
+  if (bamax == 0.0f) return 0;
+  int e = -160;
+  while (ldexp(1.0, e + 1) <= (double)bamax) ++e;
+  int x = e - 2;
+  if (x < -127) x = -127;
+  if (x > 127) x = 127;
+  return x + 127;
+}
+
+/* One element's code given its block's scale byte (0..254). */
+int orc_mx_encode_element(uint16_t x, int sbyte) {
+  int sign = (x >> 15) & 1;
+  float sc = (float)orc_e8m0_value(sbyte);       /* exact: 2^-127 .. 2^127 */
+  float y = bf16_abs(x) / sc;
+  return (sign << 3) | orc_e2m1_encode(y);
+}
+
+/* One element's decoded fp32 value RN32(E2M1(code) * 2^X); NaN for byte 255. */
+float orc_mx_decode_element(int code, int sbyte) {
+  if (sbyte == 255) return NAN;
+  float m = (float)kE2M1Mag[code & 7];
+  float v = m * (float)orc_e8m0_value(sbyte);
+  return (code & 8) ? -v : v;
+}
+
+/* x [rows][cols] bf16 (cols % 32 == 0) -> q [rows][cols/2], sf [rows][cols/32].
+ * Returns 0, or -1 on a bad shape or a non-finite input. */
+int orc_mx_quantize(const uint16_t* x, int64_t rows, int64_t cols, uint8_t* q, uint8_t* sf, int nthreads) {
+  if (rows < 0 || cols < 0 || cols % 32) return -1;
+  set_threads(nthreads);
+  int bad = 0;
+#pragma omp parallel for reduction(| : bad)
+  for (int64_t i = 0; i < rows * cols; ++i)
+    if (!bf16_is_finite(x[i])) bad = 1;
+  if (bad) return -1;
+#pragma omp parallel for
+  for (int64_t r = 0; r < rows; ++r)
+    for (int64_t b = 0; b < cols / 32; ++b) {
+      const uint16_t* xb = x + r * cols + 32 * b;
+      float bamax = 0.0f;
+      for (int i = 0; i < 32; ++i) bamax = fmaxf(bamax, bf16_abs(xb[i]));
+      int sbyte = orc_mx_block_scale(bamax);
+      sf[r * (cols / 32) + b] = (uint8_t)sbyte;
+      for (int i = 0; i < 32; i += 2) {
+        int c0 = orc_mx_encode_element(xb[i], sbyte);
+        int c1 = orc_mx_encode_element(xb[i + 1], sbyte);
+        q[r * (cols / 2) + 16 * b + i / 2] = (uint8_t)(c0 | (c1 << 4));
+      }
+    }
+  return 0;
+}
+
+/* q [rows][cols/2], sf [rows][cols/32] -> y [rows][cols] bf16. */
+int orc_mx_dequantize(const uint8_t* q, const uint8_t* sf, int64_t rows, int64_t cols, uint16_t* y, int nthreads) {
+  if (rows < 0 || cols < 0 || cols % 32) return -1;
+  set_threads(nthreads);
+#pragma omp parallel for
+  for (int64_t r = 0; r < rows; ++r)
+    for (int64_t c = 0; c < cols; ++c) {
+      int byte = q[r * (cols / 2) + c / 2];
+      int code = (c & 1) ? (byte >> 4) : (byte & 15);
+      y[r * cols + c] = orc_f32_to_bf16(orc_mx_decode_element(code, sf[r * (cols / 32) + c / 32]));
+    }
+  return 0;
+}
+
+/* Exact fp64 value E2M1(code) * 2^X of every element (NaN for byte 255). */
+int orc_mx_dequantize_f64(const uint8_t* q, const uint8_t* sf, int64_t rows, int64_t cols, double* y,
+                          int nthreads) {
+  if (rows < 0 || cols < 0 || cols % 32) return -1;
+  set_threads(nthreads);
+#pragma omp parallel for
+  for (int64_t r = 0; r < rows; ++r)
+    for (int64_t c = 0; c < cols; ++c) {
+      int byte = q[r * (cols / 2) + c / 2];
+      int code = (c & 1) ? (byte >> 4) : (byte & 15);
+      y[r * cols + c] = orc_e2m1_value(code) * orc_e8m0_value(sf[r * (cols / 32) + c / 32]);
+    }
+  return 0;
+}

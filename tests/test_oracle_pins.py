@@ -561,3 +561,143 @@ def test_thread_count_does_not_change_results():
     b = oracle.quantize(x, nthreads=0)
     for u, v in zip(a, b):
         assert np.array_equal(u, v)
+
+
+# ------------------------------------------------------------------ MXFP4
+def _mx_rand(rng, rows, cols):
+    kind = rng.integers(0, 3)
+    if kind == 0:
+        z = rng.standard_normal((rows, cols))
+    elif kind == 1:                                          # per-block magnitudes over a wide range
+        z = rng.standard_normal((rows, cols)) * 2.0 ** rng.integers(-60, 60, (rows, cols // 32)).repeat(32, axis=1)
+    else:                                                    # tiny blocks: the clamped exponent
+        z = rng.standard_normal((rows, cols)) * 2.0 ** -128
+    return bf16_bits(np.clip(z, -3e38, 3e38))
+
+
+def test_mx_storage_is_4p25_bits_per_value():
+    gs = gold("storage.json")
+    x = bf16_bits(np.random.default_rng(31).standard_normal((8, 128)))
+    q, sf = oracle.mx_quantize(x)
+    assert 8 * (q.nbytes + sf.nbytes) / x.size == gs["mxfp4_bits_per_value"]
+    assert sf.shape == (8, 128 // 32)            # one scale per 32 values
+
+
+def test_mx_scales_are_powers_of_two():
+    """UE8M0: every finite scale is 2^k (mantissa 0.5 under frexp), byte b is
+    2^(b-127), byte 255 is NaN."""
+    import math
+    for b in range(255):
+        v = oracle.e8m0_value(b)
+        m, e = math.frexp(v)
+        assert m == 0.5 and e - 1 == b - 127
+    assert math.isnan(oracle.e8m0_value(255))
+    x = _mx_rand(np.random.default_rng(32), 16, 256)
+    _, sf = oracle.mx_quantize(x)
+    for b in np.unique(sf):
+        assert math.frexp(oracle.e8m0_value(int(b)))[0] == 0.5
+
+
+def test_mx_block_scale_against_frexp():
+    """X = floor(log2 amax) - 2, clamped; floor(log2) taken from frexp."""
+    import math
+    rng = np.random.default_rng(33)
+    vals = np.concatenate([
+        (rng.random(4000) * 2.0 ** rng.integers(-149, 128, 4000)).astype(np.float32),
+        np.float32(2.0) ** np.arange(-149, 128).astype(np.float32),
+        np.nextafter(np.float32(2.0) ** np.arange(-148, 128).astype(np.float32), np.float32(0)),
+    ])
+    for v in vals:
+        v = float(v)
+        if v == 0 or math.isinf(v):
+            continue
+        e = math.frexp(v)[1] - 1                  # v = m 2^(e+1), m in [0.5, 1)
+        want = min(127, max(-127, e - 2)) + 127
+        assert oracle.mx_block_scale(v) == want, v
+    assert oracle.mx_block_scale(0.0) == 0
+    assert oracle.mx_block_scale(6.0) == 127 and oracle.mx_block_scale(8.0) == 128
+    assert oracle.mx_block_scale(float("inf")) == -1 and oracle.mx_block_scale(-1.0) == -1
+
+
+def test_mx_roundtrip_is_exact_on_the_scaled_grid():
+    """A block whose values are E2M1 values times 2^k is stored exactly."""
+    rng = np.random.default_rng(34)
+    grid = np.array([0, 0.5, 1, 1.5, 2, 3, 4, 6])
+    for _ in range(50):
+        rows, cols = 4, 128
+        mags = grid[rng.integers(0, 8, (rows, cols))]
+        mags[:, ::32] = grid[rng.integers(1, 8, (rows, cols // 32))]     # no all-zero block
+        k = rng.integers(-120, 120, (rows, cols // 32)).repeat(32, axis=1)
+        x = bf16_bits(mags * np.where(rng.random((rows, cols)) < 0.5, -1, 1) * 2.0 ** k)
+        q, sf = oracle.mx_quantize(x)
+        y = oracle.mx_dequantize(q, sf)
+        assert np.array_equal(bits_to_f32(y), bits_to_f32(x))
+
+
+def test_mx_saturation_and_ties():
+    """With X fixed by the block max: values in (6, 8) 2^X saturate to 6 2^X;
+    5 2^X (midway between 4 and 6) goes to 4 (even code 6); 0.25 2^X to 0."""
+    row = [7.5, 7.0, 5.0, 0.25, 0.75, 2.5, -3.5, -5.0] + [0.0] * 24
+    for k in (-20, 0, 13):
+        x = bf16_bits(np.array([row]) * 2.0 ** k)
+        q, sf = oracle.mx_quantize(x)
+        assert sf[0, 0] == k + 127                  # floor(log2 7.5) - 2 = 0
+        y = bits_to_f32(oracle.mx_dequantize(q, sf))[0, :8] / 2.0 ** k
+        assert y.tolist() == [6.0, 6.0, 4.0, 0.0, 1.0, 2.0, -4.0, -4.0]
+
+
+def test_mx_quantize_matches_exact_rationals():
+    rng = np.random.default_rng(35)
+    for trial in range(30):
+        x = _mx_rand(rng, 3, 64)
+        q, sf = oracle.mx_quantize(x)
+        codes, scales = exact.mx_quantize_rows(x.tolist())
+        assert sf.tolist() == scales, f"trial {trial}"
+        qc = np.stack([q & 15, q >> 4], axis=-1).reshape(3, 64)
+        assert qc.tolist() == codes, f"trial {trial}"
+
+
+def test_mx_dequant_against_library_rounding():
+    """bf16 of E2M1 * 2^(b-127) via ldexp and torch's RNE conversion, for every
+    code and every scale byte; byte 255 gives NaN."""
+    codes = np.arange(16, dtype=np.uint8)
+    for b in range(256):
+        q = np.tile((codes[0::2] | (codes[1::2] << 4)).reshape(1, 8), (1, 2))   # 32 values
+        sf = np.full((1, 1), b, dtype=np.uint8)
+        y = bits_to_f32(oracle.mx_dequantize(q, sf))[0]
+        mags = np.array([0, 0.5, 1, 1.5, 2, 3, 4, 6])
+        vals = np.tile(np.concatenate([mags, -mags]), 2)
+        if b == 255:
+            assert np.isnan(y).all()
+            continue
+        want = torch.tensor(np.ldexp(vals, b - 127), dtype=torch.float64).to(torch.float32).to(torch.bfloat16)
+        assert np.array_equal(y, want.float().numpy()), b
+    # exact fp64 values
+    q = np.array([[0x71] * 16], dtype=np.uint8)           # codes 1 (0.5) and 7 (6)
+    assert oracle.mx_dequantize_f64(q, np.array([[130]], dtype=np.uint8))[0, :2].tolist() == [4.0, 48.0]
+
+
+def test_mx_gemm_f64_against_exact_sums():
+    rng = np.random.default_rng(36)
+    M, N, K = 3, 4, 96
+    aq, asf = oracle.mx_quantize(bf16_bits(rng.standard_normal((M, K))))
+    bq, bsf = oracle.mx_quantize(bf16_bits(rng.standard_normal((N, K)) * 40))
+
+    def deq(q, sf, r, k):
+        code = (int(q[r, k // 2]) >> (4 * (k % 2))) & 15
+        return exact.E2M1[code & 7] * (-1 if code & 8 else 1) * F(2) ** (int(sf[r, k // 32]) - 127)
+
+    C = oracle.mx_gemm_f64(aq, asf, bq, bsf)
+    for m in range(M):
+        for n in range(N):
+            want = sum(deq(aq, asf, m, k) * deq(bq, bsf, n, k) for k in range(K))
+            assert abs(F(C[m, n]) - want) <= abs(want) * F(1, 2 ** 48) + F(1, 2 ** 1000)
+
+
+def test_mx_nonfinite_and_shape_rejected():
+    x = bf16_bits(np.ones((2, 32)))
+    x[1, 5] = 0x7F80
+    with pytest.raises(ValueError):
+        oracle.mx_quantize(x)
+    with pytest.raises(ValueError):
+        oracle.mx_quantize(bf16_bits(np.ones((2, 48))))
