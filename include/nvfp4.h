@@ -226,6 +226,49 @@ nvfp4_status nvfp4_grouped_gemm(const uint8_t* a_q, const uint8_t* a_sf, const f
                                 const int32_t* offsets, int32_t experts,
                                 int64_t M, int64_t N, int64_t K, float* c, void* stream);
 
+/* ------------------------------------------------------------------------
+ * MXFP4, the earlier microscaling format: 32 consecutive E2M1 values share
+ * one power-of-two scale stored as an E8M0 byte (value 2^(byte - 127), 255
+ * is NaN); there is no tensor scale; about 4.25 bits per value (iwan.kr,
+ * "NVIDIA shrank GLM-5.2 to 4 bits", section 3 "Terminology"; axbrief.com,
+ * "NVFP4: how NVIDIA pre-trained a 12B model on 10 trillion tokens", section
+ * "36% token efficiency and Blackwell speed"; theddari.com, "What is FP4
+ * quantization? KV cache in 4 bits", format-comparison table).
+ * The pages leave the exponent rule open; it is the published Microscaling
+ * definition of the format:
+ *   X = floor(log2(block amax)) - 2, clamped to [-127, 127]
+ *       (an all-zero block takes X = -127); scale byte = X + 127
+ *   code = sign(x) << 3 | E2M1_RNE_SAT(RN32(|x| / 2^X))
+ *       (values between 6 * 2^X and 8 * 2^X saturate to 6 * 2^X)
+ *   value = bf16_RNE(RN32(E2M1(code) * 2^X))
+ * Layouts: x [rows][cols] bf16 (cols % 32 == 0; a batch is rows of one
+ * matrix, since no state is per tensor), q [rows][cols/2] uint8 (element 2j
+ * in the low nibble of byte j, as for NVFP4), sf [rows][cols/32] uint8.
+ * ------------------------------------------------------------------------ */
+
+/* Quantize bf16 x to MXFP4 in one pass.  Bit-exact to the recipe above.
+ * Errors: EINVAL (cols % 32 != 0, negative sizes, null pointers), EALIGN
+ *   (x or q not 16-byte aligned), ENOTSUP, EHIP. */
+nvfp4_status nvfp4_mxfp4_quantize(const uint16_t* x, int64_t rows, int64_t cols, uint8_t* q, uint8_t* sf,
+                                  void* stream);
+
+/* Dequantize MXFP4 to bf16 y [rows][cols].  Scale byte 255 gives NaN;
+ * products beyond bf16's range give +-inf.  Errors as nvfp4_mxfp4_quantize
+ * (EALIGN: q or y not 16-byte aligned). */
+nvfp4_status nvfp4_mxfp4_dequantize(const uint8_t* q, const uint8_t* sf, int64_t rows, int64_t cols, uint16_t* y,
+                                    void* stream);
+
+/* MXFP4 x MXFP4 GEMM on gfx950's block-scaled MFMA (the matrix cores take
+ * the E2M1 codes and E8M0 bytes as stored):
+ *   C[m][n] = sum_k deq(A)[m][k] * deq(B)[n][k]        (TN, K-major)
+ * with exact products and fp32 accumulation.  a_q [M][K/2], a_sf [M][K/32],
+ * b_q [N][K/2], b_sf [N][K/32]; c [M][N] float, fully written (zeros when
+ * K == 0).
+ * Errors: EINVAL (K % 32 != 0, K > 2^23, M above 65535 * 256, null
+ *   pointers), EALIGN (a_q, b_q, c not 16-byte aligned), ENOTSUP, EHIP. */
+nvfp4_status nvfp4_mxfp4_gemm(const uint8_t* a_q, const uint8_t* a_sf, const uint8_t* b_q, const uint8_t* b_sf,
+                              int64_t M, int64_t N, int64_t K, float* c, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -60,6 +60,9 @@ _SIGS = {
     "nvfp4_grouped_gemm": (_I32, [_P, _P, _P, _P, _P, _P, _P, _I32, _I64, _I64, _I64, _P, _P]),
     "nvfp4_kv_attention_workspace_bytes": (ctypes.c_size_t, [_P, _I32, _I64]),
     "nvfp4_kv_decode_attention": (_I32, [_P, _P, _I32, _I64, ctypes.c_float, _P, _P, ctypes.c_size_t, _P]),
+    "nvfp4_mxfp4_quantize": (_I32, [_P, _I64, _I64, _P, _P, _P]),
+    "nvfp4_mxfp4_dequantize": (_I32, [_P, _P, _I64, _I64, _P, _P]),
+    "nvfp4_mxfp4_gemm": (_I32, [_P, _P, _P, _P, _I64, _I64, _I64, _P, _P]),
 }
 
 _L = None
@@ -275,3 +278,48 @@ def grouped_gemm(a_q, a_sf, a_g, b_q, b_sf, b_g, offsets, out=None):
         _ptr(c), _stream(a_q.device)))
     return c
 
+
+# ---------------------------------------------------------------- MXFP4
+def mxfp4_quantize(x, out=None):
+    """bf16 x [..., cols] (cols % 32 == 0) -> (q [..., cols/2] u8, sf [..., cols/32] u8):
+    32-value blocks, one E8M0 (power-of-two) scale each, no tensor scale."""
+    _need(x, torch.bfloat16, "x")
+    cols = x.shape[-1]
+    rows = x.numel() // cols if cols else 0
+    lead = tuple(x.shape[:-1])
+    if out is not None:
+        q, sf = out
+    else:
+        q = torch.empty(lead + (cols // 2,), dtype=torch.uint8, device=x.device)
+        sf = torch.empty(lead + (cols // 32,), dtype=torch.uint8, device=x.device)
+    _check("nvfp4_mxfp4_quantize", _lib().nvfp4_mxfp4_quantize(
+        _ptr(x), rows, cols, _ptr(q), _ptr(sf), _stream(x.device)))
+    return q, sf
+
+
+def mxfp4_dequantize(q, sf, out=None):
+    """MXFP4 codes and scale bytes -> bf16 [..., cols]."""
+    _need(q, torch.uint8, "q")
+    _need(sf, torch.uint8, "sf")
+    cols = q.shape[-1] * 2
+    rows = q.numel() // q.shape[-1] if q.shape[-1] else 0
+    if sf.numel() != rows * (cols // 32):
+        raise ValueError("sf must hold one scale byte per 32 values")
+    y = out if out is not None else torch.empty(tuple(q.shape[:-1]) + (cols,), dtype=torch.bfloat16, device=q.device)
+    _check("nvfp4_mxfp4_dequantize", _lib().nvfp4_mxfp4_dequantize(
+        _ptr(q), _ptr(sf), rows, cols, _ptr(y), _stream(q.device)))
+    return y
+
+
+def mxfp4_gemm(a_q, a_sf, b_q, b_sf, out=None):
+    """C[M][N] = sum_k deq(A)[m][k] deq(B)[n][k] on the block-scaled MFMA; fp32 output."""
+    for t, n in ((a_q, "a_q"), (a_sf, "a_sf"), (b_q, "b_q"), (b_sf, "b_sf")):
+        _need(t, torch.uint8, n)
+    M, K2 = a_q.shape
+    N = b_q.shape[0]
+    if b_q.shape[1] != K2 or a_sf.shape != (M, K2 // 16) or b_sf.shape != (N, K2 // 16):
+        raise ValueError("operands must be q [rows][K/2] and sf [rows][K/32] with a common K")
+    c = out if out is not None else torch.empty((M, N), dtype=torch.float32, device=a_q.device)
+    _check("nvfp4_mxfp4_gemm", _lib().nvfp4_mxfp4_gemm(
+        _ptr(a_q), _ptr(a_sf), _ptr(b_q), _ptr(b_sf), M, N, 2 * K2, _ptr(c), _stream(a_q.device)))
+    return c
