@@ -11,9 +11,10 @@ output byte written once) / wall time per step, in GB/s.
 Extra records in the same line ("rows"): the single 1024x1024 tensor, the
 16384 x 7168 activation quantize (two-kernel and fused), the 32x8x128 KV
 cache (512 appends of 256 tokens, decode QK over 131072 tokens, 32 query
-heads), the 8192 x 2048 x 7168 block-scaled GEMM and the grouped MoE GEMM
-(16384 tokens routed top-8 over 64 experts) in TFLOP/s -- each with its
-roofline fraction.  Every kernel time comes from HIP events recorded on
+heads, plus decode attention), the 8192 x 2048 x 7168 block-scaled GEMM and
+the grouped MoE GEMM (16384 tokens routed top-8 over 64 experts) in TFLOP/s,
+and MXFP4 against NVFP4 on the same data (codec and GEMM speed, error) --
+each with its roofline fraction.  Every kernel time comes from HIP events recorded on
 the stream the kernels run on.
 
 cpu_baseline: the CPU oracle (the parity reference, not tuned) timed on a
@@ -31,6 +32,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
+FP4_MFMA_PEAK_TFLOPS = 10100.0  # MI355X dense fp4 MFMA, TFLOP/s
 
 
 def parse():
@@ -40,7 +42,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--no-extras", action="store_true", help="headline step only")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    p.add_argument("--rows-only", default="", help="comma list of extra rows to run (experts,single,acts,kv,gemm,moe)")
+    p.add_argument("--rows-only", default="",
+                   help="comma list of extra rows to run (experts,single,acts,kv,gemm,moe,mx)")
     p.add_argument("--traffic-kernels", action="store_true",
                    help="only launch the headline kernels, the GEMM and a 1 GiB device copy, 3 times each "
                         "(the workload for rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs)")
@@ -76,10 +79,14 @@ class EventTimer:
         self.pairs = {}
 
 
+# The sources the headline kernels (quantize and dequantize) are built from.
+HEADLINE_SOURCES = ("codec.hip", "common.hpp")
+
+
 def source_hash():
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "nvfp4_block_scaled_06_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
+    for f in HEADLINE_SOURCES:
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(f.encode() + fh.read())
     return h.hexdigest()[:16]
@@ -279,6 +286,8 @@ def run_extras(nv, synth, torch, which):
         del a, b, aq, bq, c
     if "moe" in which:
         rows["moe_grouped_gemm_16384x8_64x2048x7168"] = run_moe(nv, synth, torch)
+    if "mx" in which:
+        rows["mxfp4_vs_nvfp4"] = run_mx(nv, synth, torch)
     del fbuf
     torch.cuda.empty_cache()
     return rows
@@ -307,6 +316,61 @@ def run_moe(nv, synth, torch):
     res = {"ms": m, "rows": M, "experts": E, "min_rows": int(counts.min()), "max_rows": int(counts.max()),
            "bound": "mfma", **roof(flops, m, BF16_MFMA_PEAK_TFLOPS, "TFLOP/s")}
     del aq, asf, bq, bsf, c
+    torch.cuda.empty_cache()
+    return res
+
+
+def _rel_err(torch, y, x):
+    d = (y.float() - x.float()).double()
+    return float(d.square().sum().sqrt() / x.double().square().sum().sqrt())
+
+
+def run_mx(nv, synth, torch):
+    """MXFP4 against NVFP4 on the same synthetic data: the 64 x 2048 x 7168
+    experts tensor through quantize and dequantize (speed and round-trip
+    relative Frobenius error), and the 8192 x 2048 x 7168 GEMM (speed, and the
+    relative error of C on 64 sampled rows against the fp32 product of the
+    unquantized bf16 operands)."""
+    res = {}
+    x = synth.experts(device="cuda")
+    n = x.numel()
+    mq_bytes = 2 * n + n // 2 + n // 32
+    q, sf = nv.mxfp4_quantize(x)
+    y = nv.mxfp4_dequantize(q, sf)
+    mq = timed(torch, lambda: nv.mxfp4_quantize(x, out=(q, sf)), 10)
+    md = timed(torch, lambda: nv.mxfp4_dequantize(q, sf, out=y), 10)
+    mx_err = _rel_err(torch, y, x)
+    del q, sf
+    ws = nv.make_workspace(64, 2048, 7168)
+    nq, nsf, ng = nv.quantize(x, workspace=ws)
+    nvfp4_err = _rel_err(torch, nv.dequantize(nq, nsf, ng, out=y), x)
+    del nq, nsf, ng, y, x
+    torch.cuda.empty_cache()
+    res["experts_64x2048x7168"] = {
+        "mxfp4_quantize": {"ms": mq, **roof(mq_bytes, mq, HBM_PEAK_GBS, "GB/s")},
+        "mxfp4_dequantize": {"ms": md, **roof(mq_bytes, md, HBM_PEAK_GBS, "GB/s")},
+        "round_trip_rel_err": {"mxfp4": round(mx_err, 6), "nvfp4": round(nvfp4_err, 6)},
+        "bits_per_value": {"mxfp4": 4.25, "nvfp4": 4.5}}
+    a, b = synth.gemm_operands(device="cuda")
+    rows = torch.from_numpy(__import__("numpy").random.default_rng(4).choice(8192, 64, replace=False)).cuda()
+    ref = a[rows].float() @ b.float().T
+    c = torch.empty((8192, 2048), dtype=torch.float32, device="cuda")
+    aq, asf = nv.mxfp4_quantize(a)
+    bq, bsf = nv.mxfp4_quantize(b)
+    mg = timed(torch, lambda: nv.mxfp4_gemm(aq, asf, bq, bsf, out=c), 20)
+    mx_gerr = _rel_err(torch, c[rows], ref)
+    del aq, asf, bq, bsf
+    aq, asf, ag = nv.quantize(a)
+    bq, bsf, bg = nv.quantize(b)
+    ng = timed(torch, lambda: nv.gemm(aq, asf, ag, bq, bsf, bg, out=c), 20)
+    nv_gerr = _rel_err(torch, c[rows], ref)
+    flops = 2 * 8192 * 2048 * 7168
+    res["gemm_8192x2048x7168"] = {
+        "mxfp4": {"ms": mg, "bound": "mfma", "peak_dtype": "fp4", **roof(flops, mg, FP4_MFMA_PEAK_TFLOPS, "TFLOP/s")},
+        "nvfp4": {"ms": ng, "bound": "mfma", "peak_dtype": "bf16/f16",
+                  **roof(flops, ng, BF16_MFMA_PEAK_TFLOPS, "TFLOP/s")},
+        "rel_err_vs_bf16_inputs": {"mxfp4": round(mx_gerr, 6), "nvfp4": round(nv_gerr, 6)}}
+    del a, b, aq, asf, bq, bsf, c, ref
     torch.cuda.empty_cache()
     return res
 
@@ -391,7 +455,8 @@ def main():
     log("headline done:", json.dumps(head))
     rows = {}
     if not args.no_extras:
-        which = args.rows_only.split(",") if args.rows_only else ["experts", "single", "acts", "kv", "gemm", "moe"]
+        which = (args.rows_only.split(",") if args.rows_only
+                 else ["experts", "single", "acts", "kv", "gemm", "moe", "mx"])
         rows = run_extras(nv, synth, torch, which)
         log("extras done")
     cpu = None if args.no_cpu else cpu_baseline(synth, torch)
