@@ -177,24 +177,25 @@ struct MxStep {
   uint32_t w0, w1;                             // the row's W_0, W_1
 };
 
+// kAligned (K % 256 == 0): the caller only asks for steps inside K, so the
+// loads carry no conditions; otherwise each block is checked on its own and
+// blocks at or past K read as codes 0 with scale byte 0.
 template <bool kAligned>
 __device__ __forceinline__ MxStep mx_load_step(const MxOperand& o, int tid, int64_t K, int64_t k0) {
   MxStep st;
   const int chunk = tid & 7, rsub = tid >> 3;
-  const bool cin = k0 + 32 * chunk < K;        // this thread's block is inside K
+  const uint32_t base = (uint32_t)rsub * o.qrow + (uint32_t)(k0 / 2) + 16u * chunk;
+  const uint32_t cin = kAligned || k0 + 32 * chunk < K ? 0u : kMxOutside;   // this thread's block inside K
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const uint32_t off = cin ? (uint32_t)(rsub + 32 * j) * o.qrow + (uint32_t)(k0 / 2) + 16u * chunk : kMxOutside;
-    st.c[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(o.q, (int)off, 0, 0));
-  }
+  for (int j = 0; j < 8; ++j)
+    st.c[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(o.q, (int)((base + 32u * j * o.qrow) | cin), 0, 0));
   uint32_t lo, hi;
   const uint32_t so = (uint32_t)tid * o.srow + (uint32_t)(k0 / 32);
-  if (kAligned) {                              // K % 256 == 0: the step is wholly inside or outside
-    const bool in = k0 < K;
-    const u32x2 s = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(o.s, (int)(in ? so : kMxOutside), 0, 0));
+  if (kAligned) {
+    const u32x2 s = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(o.s, (int)so, 0, 0));
     lo = s.x;
     hi = s.y;
-  } else {                                     // ragged: blocks at or past K read as scale 0
+  } else {
     lo = hi = 0u;
 #pragma unroll
     for (int b = 0; b < 8; ++b) {
@@ -217,26 +218,45 @@ __device__ __forceinline__ void mx_store_step(const MxStep& st, int tid, uint8_t
   sc[tid][1] = st.w1;
 }
 
-template <int kk>
-__device__ __forceinline__ void mx_substep(f32x16 (&acc)[4][4], const uint8_t* Acur, const uint8_t* Bcur,
-                                           const uint32_t (&sa)[4], const uint32_t (&sb)[4]) {
+// Operand fragments of one substep: A tile rows i and B tile rows j.
+struct MxFrag {
   i32x8 a[4], b[4];
+};
+
+__device__ __forceinline__ void mx_frag_load(MxFrag& f, const uint8_t* Acur, const uint8_t* Bcur, int kk) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const u32x4 v = *(const u32x4*)(Acur + i * 32 * MROW + 32 * kk);
-    a[i] = i32x8{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
+    f.a[i] = i32x8{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
   }
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const u32x4 v = *(const u32x4*)(Bcur + j * 32 * MROW + 32 * kk);
-    b[j] = i32x8{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
+    f.b[j] = i32x8{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
   }
+}
+
+// The 16 MFMAs of substep kk on f, while the fragments of substep kk + 1
+// load from LDS into nf (kk < 3): one LDS read between every two MFMAs.
+template <int kk>
+__device__ __forceinline__ void mx_substep(f32x16 (&acc)[4][4], const MxFrag& f, MxFrag& nf, const uint8_t* Acur,
+                                           const uint8_t* Bcur, const uint32_t (&sa)[4], const uint32_t (&sb)[4]) {
+  __builtin_amdgcn_sched_barrier(0);
+  if (kk < 3) mx_frag_load(nf, Acur, Bcur, kk + 1);
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[i], b[j], acc[i][j], 4, 4, kk, (int)sa[i], kk,
+      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.a[i], f.b[j], acc[i][j], 4, 4, kk, (int)sa[i], kk,
                                                                   (int)sb[j]);
+  if (kk < 3) {
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);   // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
 }
 
 template <bool kAligned>
@@ -266,8 +286,10 @@ __global__ void __launch_bounds__(MThreads) mx_gemm_kernel(const uint8_t* __rest
   const int arow = wm * 128 + (lane & 31), brow = wn * 128 + (lane & 31), h = lane >> 5;
   for (int64_t kt = 0; kt < nk; ++kt) {
     const int buf = (int)(kt & 1);
-    ra = mx_load_step<kAligned>(A, tid, K, (kt + 1) * MTK);   // past the last step: zeros, unread buffer
-    rb = mx_load_step<kAligned>(B, tid, K, (kt + 1) * MTK);
+    // the last step reloads itself (in range) into the unread buffer
+    const int64_t knext = (kt + 1 < nk ? kt + 1 : kt) * MTK;
+    ra = mx_load_step<kAligned>(A, tid, K, knext);
+    rb = mx_load_step<kAligned>(B, tid, K, knext);
     const uint8_t* Acur = sm.a[buf] + arow * MROW + 16 * h;
     const uint8_t* Bcur = sm.b[buf] + brow * MROW + 16 * h;
     uint32_t sa[4], sb[4];
@@ -276,24 +298,36 @@ __global__ void __launch_bounds__(MThreads) mx_gemm_kernel(const uint8_t* __rest
       sa[i] = sm.as[buf][arow + 32 * i][h];
       sb[i] = sm.bs[buf][brow + 32 * i][h];
     }
-    mx_substep<0>(acc, Acur, Bcur, sa, sb);
-    mx_substep<1>(acc, Acur, Bcur, sa, sb);
-    mx_substep<2>(acc, Acur, Bcur, sa, sb);
-    mx_substep<3>(acc, Acur, Bcur, sa, sb);
+    MxFrag f0, f1;
+    mx_frag_load(f0, Acur, Bcur, 0);
+    mx_substep<0>(acc, f0, f1, Acur, Bcur, sa, sb);
+    mx_substep<1>(acc, f1, f0, Acur, Bcur, sa, sb);
+    mx_substep<2>(acc, f0, f1, Acur, Bcur, sa, sb);
+    mx_substep<3>(acc, f1, f0, Acur, Bcur, sa, sb);
     mx_store_step(ra, tid, sm.a[buf ^ 1], sm.as[buf ^ 1]);
     mx_store_step(rb, tid, sm.b[buf ^ 1], sm.bs[buf ^ 1]);
     __syncthreads();
   }
+  float* Cw = C + (m0 + wm * 128 + 4 * (lane >> 5)) * N + n0 + wn * 128 + (lane & 31);
+  if (m0 + MTM <= M && n0 + MTN <= N) {         // whole tile: no bounds checks
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < 4; ++j)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int64_t row = m0 + wm * 128 + i * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
-        const int64_t col = n0 + wn * 128 + j * 32 + (lane & 31);
-        if (row < M && col < N) C[row * N + col] = acc[i][j][e];
-      }
+        for (int e = 0; e < 16; ++e) Cw[(i * 32 + 8 * (e >> 2) + (e & 3)) * N + j * 32] = acc[i][j][e];
+  } else {
+    const int64_t rlim = M - (m0 + wm * 128 + 4 * (lane >> 5)), clim = N - (n0 + wn * 128 + (lane & 31));
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int r = i * 32 + 8 * (e >> 2) + (e & 3), cc = j * 32;
+          if (r < rlim && cc < clim) Cw[r * N + cc] = acc[i][j][e];
+        }
+  }
 }
 
 }  // namespace nvfp4
