@@ -16,7 +16,12 @@ example"); NVFP4 for weights and activations of MoE expert linears
 (iwan.kr, "NVIDIA shrank GLM-5.2 to 4 bits", section 1).  The MXFP4 variant
 (32-value blocks, one power-of-two scale each, no tensor scale; iwan.kr, same
 page, section 3; theddari.com, format table) follows the published
-Microscaling exponent rule, which the pages leave open.
+Microscaling exponent rule, which the pages leave open.  The training-recipe
+variants (16x16 2D weight scales, a random Hadamard transform of Wgrad
+inputs, stochastic rounding of gradients, the column-wise Dgrad/Wgrad
+operand layout; axbrief.com, same page, section "Four stabilizers for
+training: from RHT to stochastic rounding") run in nvfp4_oracle.c as well,
+with their random draws from Philox4x32-10.
 
 Parity pins live in tests/test_oracle_*.py; functions without an independent
 pin would say "parity unpinned" here -- every function below has one.
@@ -62,6 +67,12 @@ def lib():
         L.orc_mx_block_scale.argtypes = [ctypes.c_float]
         L.orc_mx_decode_element.restype = ctypes.c_float
         L.orc_mx_decode_element.argtypes = [i32, i32]
+        L.orc_philox4x32_10.restype = None
+        L.orc_philox4x32_10.argtypes = [P, P, P]
+        L.orc_e2m1_encode_sr.restype = i32
+        L.orc_e2m1_encode_sr.argtypes = [ctypes.c_float, ctypes.c_uint32]
+        L.orc_rht16.restype = None
+        L.orc_rht16.argtypes = [P, ctypes.c_uint32]
         for name, args in {
             "orc_quantize": [P, i64, i64, i64, P, P, P, i32],
             "orc_quantize_with_scale": [P, i64, i64, i64, P, P, P, i32],
@@ -70,6 +81,8 @@ def lib():
             "orc_mx_quantize": [P, i64, i64, P, P, i32],
             "orc_mx_dequantize": [P, P, i64, i64, P, i32],
             "orc_mx_dequantize_f64": [P, P, i64, i64, P, i32],
+            "orc_quantize_ex": [P, i64, i64, i64, ctypes.c_uint32, ctypes.c_uint32, ctypes.c_uint64,
+                                ctypes.c_uint64, P, P, P],
         }.items():
             getattr(L, name).restype = i32
             getattr(L, name).argtypes = args
@@ -381,3 +394,53 @@ def mx_gemm_f64(a_q, a_sf, b_q, b_sf, rows=None) -> np.ndarray:
         a_q = a_q[rows]
         a_sf = a_sf[rows]
     return mx_dequantize_f64(a_q, a_sf) @ mx_dequantize_f64(b_q, b_sf).T
+
+
+# ---------------------------------------------------------------- training variants
+# 16x16 2D weight scales, random Hadamard transform of Wgrad inputs and
+# stochastic rounding of gradients (axbrief.com, "NVFP4: how NVIDIA
+# pre-trained a 12B model on 10 trillion tokens", section "Four stabilizers
+# for training: from RHT to stochastic rounding"); the readings are spelled
+# out in nvfp4_oracle.c.
+COLWISE, TWO_D, RHT, SR = 1, 2, 4, 8
+
+
+def philox4x32_10(ctr, key):
+    c = np.ascontiguousarray(np.asarray(ctr, dtype=np.uint32))
+    k = np.ascontiguousarray(np.asarray(key, dtype=np.uint32))
+    out = np.empty(4, dtype=np.uint32)
+    lib().orc_philox4x32_10(_p(c), _p(k), _p(out))
+    return out
+
+
+def e2m1_encode_sr(y: float, u16: int) -> int:
+    return lib().orc_e2m1_encode_sr(float(y), int(u16))
+
+
+def rht16(v, signs: int) -> np.ndarray:
+    """fp32 RHT of one 16-value block: H16 (s .* v) / 4 by the fast
+    Walsh-Hadamard stages h = 1, 2, 4, 8."""
+    a = np.ascontiguousarray(np.asarray(v, dtype=np.float32).reshape(16)).copy()
+    lib().orc_rht16(_p(a), int(signs))
+    return a
+
+
+def quantize_ex(x_bits: np.ndarray, variant: int, signs: int = 0, seed: int = 0, offset: int = 0):
+    """Variant quantize of bf16 bits [rows][cols] or [batch][rows][cols].
+    Returns (q, sf, g); with COLWISE the outputs describe x^T
+    ([batch][cols][rows/2], [batch][cols][rows/16])."""
+    x = np.ascontiguousarray(x_bits, dtype=np.uint16)
+    squeeze = x.ndim == 2
+    if squeeze:
+        x = x[None]
+    b, r, c = x.shape
+    R, C = (c, r) if variant & COLWISE else (r, c)
+    q = np.empty((b, R, C // 2), dtype=np.uint8)
+    sf = np.empty((b, R, C // 16), dtype=np.uint8)
+    g = np.empty(b, dtype=np.float32)
+    rc = lib().orc_quantize_ex(_p(x), b, r, c, variant, signs, seed, offset, _p(q), _p(sf), _p(g))
+    if rc == -2:
+        raise ValueError("quantize_ex: 2D scaling and RHT are not combined")
+    if rc != 0:
+        raise ValueError("quantize_ex: bad shape or non-finite input")
+    return (q[0], sf[0], g) if squeeze else (q, sf, g)

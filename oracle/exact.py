@@ -150,3 +150,50 @@ def mx_quantize_rows(x_bits):
         codes.append(rc)
         scales.append(rs)
     return codes, scales
+
+
+# ---------------------------------------------------------------- variants
+def quantize_values(rows, draws=None, tiles=False):
+    """The recipe on exact rational inputs (e.g. RHT outputs, which are fp32
+    values): rows is a list of rows of Fractions (len % 16 == 0).  draws, if
+    given, holds one 16-bit uniform per element (stochastic rounding of the
+    element step); tiles=True takes each block's scale from its 16x16 tile.
+    Signs come from the values' signs (negative zero is not representable
+    here; callers avoid it).  Returns (codes, scales, g)."""
+    amax = max((abs(v) for row in rows for v in row), default=F(0))
+    g = rn32(amax / 2688)
+    d6 = rn32(6 * g)
+    codes, scales = [], []
+    for r, row in enumerate(rows):
+        rc, rs = [], []
+        for b in range(len(row) // 16):
+            if tiles:
+                r0 = r - r % 16
+                bamax = max(abs(v) for rr in range(r0, r0 + 16) for v in rows[rr][16 * b:16 * b + 16])
+            else:
+                bamax = max(abs(v) for v in row[16 * b:16 * b + 16])
+            sbyte = 0 if d6 == 0 else e4m3_rne_sat(rn32(bamax / d6))
+            d = rn32(E4M3[sbyte] * g)
+            rs.append(sbyte)
+            for i, v in enumerate(row[16 * b:16 * b + 16]):
+                sign = 8 if v < 0 else 0
+                if d == 0:
+                    rc.append(sign)
+                    continue
+                y = rn32(abs(v) / d)
+                if draws is None:
+                    rc.append(sign | e2m1_rne_sat(y))
+                else:
+                    rc.append(sign | e2m1_sr(y, draws[r][16 * b + i]))
+        codes.append(rc)
+        scales.append(rs)
+    return codes, scales, g
+
+
+def e2m1_sr(y: F, u16: int) -> int:
+    """Stochastic rounding onto the E2M1 magnitudes: up with probability
+    (y - lo) / (hi - lo), decided by u16 / 2^16; 6 and above give 6."""
+    if y >= 6:
+        return 7
+    lo = max(k for k in range(8) if E2M1[k] <= y)
+    return lo + 1 if F(u16, 65536) < (y - E2M1[lo]) / (E2M1[lo + 1] - E2M1[lo]) else lo

@@ -35,6 +35,7 @@
  */
 #include <math.h>
 #include <stdint.h>
+#include <stdlib.h>
 #include <string.h>
 
 #ifdef _OPENMP
@@ -383,5 +384,163 @@ int orc_mx_dequantize_f64(const uint8_t* q, const uint8_t* sf, int64_t rows, int
       int code = (c & 1) ? (byte >> 4) : (byte & 15);
       y[r * cols + c] = orc_e2m1_value(code) * orc_e8m0_value(sf[r * (cols / 32) + c / 32]);
     }
+  return 0;
+}
+
+/* ---------- training-recipe variants ----------
+ *
+ * The pages' training recipe (axbrief.com, "NVFP4: how NVIDIA pre-trained a
+ * 12B model on 10 trillion tokens", section "Four stabilizers for training:
+ * from RHT to stochastic rounding") quantizes the operands of the Fprop,
+ * Dgrad and Wgrad GEMMs and adds:
+ *  - 16x16 2D block scaling of weights, so a weight and its transpose have
+ *    the same quantized form;
+ *  - a random Hadamard transform of the Wgrad inputs: a 16x16 Hadamard
+ *    matrix times a random +-1 sign vector;
+ *  - stochastic rounding of gradients: a value between two neighbours
+ *    rounds up with probability equal to its distance from the lower one
+ *    over the gap (0.7 between 0 and 1 becomes 1 with probability 0.7).
+ * Readings where the pages are silent:
+ *  - COLWISE quantizes x^T (blocks run down the columns of x): the Dgrad /
+ *    Wgrad operand layout, whose contraction runs over x's rows.
+ *  - 2D: one E4M3 scale per 16x16 tile from the tile's amax; the byte is
+ *    stored for each of the tile's 16 rows in the usual [rows][cols/16]
+ *    layout, so every NVFP4 consumer reads it unchanged.
+ *  - RHT acts on each 16-value block along the block direction:
+ *    v = H16 (s .* x) / 4, H16 the Sylvester Hadamard matrix
+ *    (H[i][j] = (-1)^popcount(i & j)) and s the caller's signs (bit j of a
+ *    16-bit mask set means s_j = -1).  It is computed in fp32 as the fast
+ *    Walsh-Hadamard transform: stages h = 1, 2, 4, 8, each replacing the
+ *    pair (v[i], v[i+h]) (i & h == 0) by (v[i] + v[i+h], v[i] - v[i+h]),
+ *    then a multiply by 1/4.  The quantizer takes those fp32 values (the
+ *    recipe's amax, quotients and codes run on them unchanged).
+ *  - SR replaces only the element rounding E2M1_RNE_SAT(y): with lo the
+ *    largest E2M1 magnitude <= y and hi the next (y >= 6 gives 6), the code
+ *    rounds up when u < (y - lo) / (hi - lo), u a 16-bit uniform draw u16 /
+ *    65536.  Scales stay round-to-nearest.
+ *  - The draws come from Philox4x32-10 (Salmon et al., "Parallel random
+ *    numbers: as easy as 1, 2, 3", SC 2011): for the element at linear
+ *    index i of the output code array, counter (n mod 2^32, n >> 32, 0, 0)
+ *    with n = i / 8 + offset, key (seed mod 2^32, seed >> 32); the element
+ *    takes 16-bit half (i mod 2) of output word (i mod 8) / 2.
+ */
+
+#define ORC_COLWISE 1u
+#define ORC_2D 2u
+#define ORC_RHT 4u
+#define ORC_SR 8u
+
+void orc_philox4x32_10(const uint32_t ctr[4], const uint32_t key[2], uint32_t out[4]) {
+  uint32_t c0 = ctr[0], c1 = ctr[1], c2 = ctr[2], c3 = ctr[3], k0 = key[0], k1 = key[1];
+  for (int r = 0; r < 10; ++r) {
+    if (r > 0) {
+      k0 += 0x9E3779B9u;                 /* Weyl key schedule */
+      k1 += 0xBB67AE85u;
+    }
+    uint64_t p0 = (uint64_t)0xD2511F53u * c0, p1 = (uint64_t)0xCD9E8D57u * c2;
+    uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0, n1 = (uint32_t)p1;
+    uint32_t n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1, n3 = (uint32_t)p0;
+    c0 = n0; c1 = n1; c2 = n2; c3 = n3;
+  }
+  out[0] = c0; out[1] = c1; out[2] = c2; out[3] = c3;
+}
+
+/* 16-bit draw of the element at output index i. */
+static uint32_t sr_draw(int64_t i, uint64_t seed, uint64_t offset) {
+  uint64_t n = (uint64_t)i / 8 + offset;
+  uint32_t ctr[4] = {(uint32_t)n, (uint32_t)(n >> 32), 0u, 0u};
+  uint32_t key[2] = {(uint32_t)seed, (uint32_t)(seed >> 32)};
+  uint32_t out[4];
+  orc_philox4x32_10(ctr, key, out);
+  return (out[(i & 7) >> 1] >> (16 * (i & 1))) & 0xFFFFu;
+}
+
+/* Stochastic E2M1 magnitude code of y >= 0 with the 16-bit draw u16. */
+int orc_e2m1_encode_sr(float y, uint32_t u16) {
+  if (!(y >= 0.0f)) return -1;
+  if (y >= 6.0f) return 7;
+  int lo = 0;
+  while (lo < 7 && kE2M1Mag[lo + 1] <= (double)y) ++lo;
+  double p = ((double)y - kE2M1Mag[lo]) / (kE2M1Mag[lo + 1] - kE2M1Mag[lo]);   /* exact */
+  return (double)u16 / 65536.0 < p ? lo + 1 : lo;
+}
+
+/* In-place RHT of one 16-value block (fp32, the stage order above). */
+void orc_rht16(float v[16], uint32_t signs) {
+  for (int j = 0; j < 16; ++j)
+    if ((signs >> j) & 1u) v[j] = -v[j];
+  for (int h = 1; h < 16; h <<= 1)
+    for (int i = 0; i < 16; ++i)
+      if ((i & h) == 0) {
+        float a = v[i], b = v[i + h];
+        v[i] = a + b;
+        v[i + h] = a - b;
+      }
+  for (int j = 0; j < 16; ++j) v[j] = v[j] * 0.25f;
+}
+
+/* Element code from an fp32 value (the variant path: the value may be an
+ * RHT output), given d = RN32(s g) of its block. */
+static int encode_value(float v, float d, int sr, uint32_t u16) {
+  int sign = signbit(v) ? 1 : 0;
+  if (d == 0.0f) return sign << 3;
+  float y = fabsf(v) / d;
+  return (sign << 3) | (sr ? orc_e2m1_encode_sr(y, u16) : orc_e2m1_encode(y));
+}
+
+/* Variant quantize: x [batch][rows][cols] bf16 -> q, sf, g.  Output matrix
+ * per tensor is [R][C] = [rows][cols], or [cols][rows] with COLWISE:
+ * q [batch][R][C/2], sf [batch][R][C/16], g [batch].  Requires cols % 16 ==
+ * 0, and rows % 16 == 0 with COLWISE or 2D; 2D with RHT is not a variant
+ * (-2).  Returns 0, -1 on bad shapes / non-finite input. */
+int orc_quantize_ex(const uint16_t* x, int64_t batch, int64_t rows, int64_t cols, uint32_t variant,
+                    uint32_t signs, uint64_t seed, uint64_t offset, uint8_t* q, uint8_t* sf, float* g) {
+  const int colwise = (variant & ORC_COLWISE) != 0, two_d = (variant & ORC_2D) != 0;
+  const int rht = (variant & ORC_RHT) != 0, sr = (variant & ORC_SR) != 0;
+  if (batch < 0 || rows < 0 || cols < 0 || cols % 16) return -1;
+  if ((colwise || two_d) && rows % 16) return -1;
+  if (two_d && rht) return -2;
+  const int64_t R = colwise ? cols : rows, C = colwise ? rows : cols;
+  const int64_t n = rows * cols;
+  float* v = (float*)malloc(sizeof(float) * (size_t)(n > 0 ? n : 1));
+  if (!v) return -1;
+  for (int64_t t = 0; t < batch; ++t) {
+    const uint16_t* xt = x + t * n;
+    /* the output-oriented values v[r][c] (x or x^T), RHT per block */
+    for (int64_t r = 0; r < R; ++r)
+      for (int64_t c = 0; c < C; ++c) {
+        uint16_t b = colwise ? xt[c * cols + r] : xt[r * cols + c];
+        if (!bf16_is_finite(b)) { free(v); return -1; }
+        v[r * C + c] = orc_bf16_to_f32(b);
+      }
+    if (rht)
+      for (int64_t r = 0; r < R; ++r)
+        for (int64_t c = 0; c < C; c += 16) orc_rht16(v + r * C + c, signs);
+    float amax = 0.0f;
+    for (int64_t i = 0; i < n; ++i) amax = fmaxf(amax, fabsf(v[i]));
+    const float gt = orc_global_scale(amax);
+    g[t] = gt;
+    for (int64_t r = 0; r < R; ++r)
+      for (int64_t b = 0; b < C / 16; ++b) {
+        float bamax = 0.0f;
+        if (two_d) {                                   /* the 16x16 tile holding (r, b) */
+          int64_t r0 = r - r % 16;
+          for (int64_t rr = r0; rr < r0 + 16; ++rr)
+            for (int i = 0; i < 16; ++i) bamax = fmaxf(bamax, fabsf(v[rr * C + 16 * b + i]));
+        } else {
+          for (int i = 0; i < 16; ++i) bamax = fmaxf(bamax, fabsf(v[r * C + 16 * b + i]));
+        }
+        const int sbyte = orc_block_scale(bamax, gt);
+        sf[(t * R + r) * (C / 16) + b] = (uint8_t)sbyte;
+        const float d = (float)orc_e4m3_value(sbyte) * gt;
+        for (int i = 0; i < 16; i += 2) {
+          const int64_t i0 = (t * R + r) * C + 16 * b + i;          /* output linear index */
+          int c0 = encode_value(v[r * C + 16 * b + i], d, sr, sr ? sr_draw(i0, seed, offset) : 0u);
+          int c1 = encode_value(v[r * C + 16 * b + i + 1], d, sr, sr ? sr_draw(i0 + 1, seed, offset) : 0u);
+          q[i0 / 2] = (uint8_t)(c0 | (c1 << 4));
+        }
+      }
+  }
+  free(v);
   return 0;
 }

@@ -701,3 +701,179 @@ def test_mx_nonfinite_and_shape_rejected():
         oracle.mx_quantize(x)
     with pytest.raises(ValueError):
         oracle.mx_quantize(bf16_bits(np.ones((2, 48))))
+
+
+# ------------------------------------------------------------------ training variants
+def test_philox_known_answers():
+    """Philox4x32-10 against the known-answer vectors published with the
+    generator (Salmon et al., SC 2011, Random123 test vectors)."""
+    cases = [
+        ([0, 0, 0, 0], [0, 0], [0x6627e8d5, 0xe169c58d, 0xbc57ac4c, 0x9b00dbd8]),
+        ([0xffffffff] * 4, [0xffffffff] * 2, [0x408f276d, 0x41c83b0e, 0xa20bc7c6, 0x6d5451fd]),
+        ([0x243f6a88, 0x85a308d3, 0x13198a2e, 0x03707344], [0xa4093822, 0x299f31d0],
+         [0xd16cfe09, 0x94fdcceb, 0x5001e420, 0x24126ea1]),
+    ]
+    for ctr, key, want in cases:
+        assert oracle.philox4x32_10(ctr, key).tolist() == want
+
+
+def _hadamard16():
+    from scipy.linalg import hadamard
+    return hadamard(16).astype(np.float64)
+
+
+def test_rht_matches_the_hadamard_matrix():
+    """The fp32 butterfly equals H16 diag(s) x / 4 with scipy's Sylvester
+    Hadamard matrix: exactly on small integers, within 4 fp32 roundings
+    otherwise; H H^T = 16 I."""
+    H = _hadamard16()
+    assert np.array_equal(H @ H.T, 16 * np.eye(16))
+    rng = np.random.default_rng(41)
+    for _ in range(200):
+        signs = int(rng.integers(0, 1 << 16))
+        s = np.array([-1.0 if (signs >> j) & 1 else 1.0 for j in range(16)])
+        xi = rng.integers(-64, 64, 16).astype(np.float32)
+        assert np.array_equal(oracle.rht16(xi, signs).astype(np.float64), H @ (s * xi) / 4)
+        xf = (rng.standard_normal(16) * 2.0 ** rng.integers(-30, 30)).astype(np.float32)
+        got = oracle.rht16(xf, signs).astype(np.float64)
+        want = H @ (s * xf.astype(np.float64)) / 4
+        assert np.all(np.abs(got - want) <= 4 * 2.0 ** -24 * np.abs(xf).sum())
+
+
+def test_rht_is_orthogonal():
+    """Applying the transform twice with no signs returns s .* x, and dot
+    products survive the transform (the Wgrad contraction is unchanged)."""
+    rng = np.random.default_rng(42)
+    for _ in range(100):
+        signs = int(rng.integers(0, 1 << 16))
+        s = np.array([-1.0 if (signs >> j) & 1 else 1.0 for j in range(16)], dtype=np.float32)
+        a = rng.integers(-50, 50, 16).astype(np.float32)
+        b = rng.integers(-50, 50, 16).astype(np.float32)
+        ta, tb = oracle.rht16(a, signs), oracle.rht16(b, signs)
+        assert np.array_equal(oracle.rht16(ta, 0), s * a)
+        assert float(np.dot(ta.astype(np.float64), tb)) == float(np.dot(a.astype(np.float64), b))
+
+
+def test_sr_example_of_the_pages():
+    """A value 0.7 of the way between two neighbours rounds up with
+    probability 0.7 (to 2^-16): over all 65536 draws, on every E2M1 gap."""
+    grid = [0, 0.5, 1, 1.5, 2, 3, 4, 6]
+    for k in range(7):
+        y = np.float32(grid[k] + 0.7 * (grid[k + 1] - grid[k]))
+        p = (float(y) - grid[k]) / (grid[k + 1] - grid[k])
+        ups = sum(oracle.e2m1_encode_sr(float(y), u) == k + 1 for u in range(0, 65536, 1))
+        assert abs(ups / 65536 - 0.7) < 2 ** -15
+        assert ups == int(np.ceil(p * 65536))
+        assert all(oracle.e2m1_encode_sr(float(y), u) in (k, k + 1) for u in (0, 12345, 65535))
+
+
+def test_sr_is_unbiased_over_the_draws():
+    """The mean over all 65536 draws of the rounded value is y within one
+    part in 2^16 of the gap; grid values never move; 6 and above stay 6."""
+    grid = np.array([0, 0.5, 1, 1.5, 2, 3, 4, 6])
+    rng = np.random.default_rng(43)
+    for y in np.concatenate([rng.random(20) * 6, grid]).astype(np.float32):
+        codes = np.array([oracle.e2m1_encode_sr(float(y), u) for u in range(0, 65536, 16)])
+        mean = grid[codes].mean()
+        gap = 2.0 if y >= 4 else 1.0 if y >= 2 else 0.5
+        assert abs(mean - float(y)) <= gap * 16 / 65536 + 1e-12
+        if float(y) in grid:
+            assert np.all(grid[codes] == float(y))
+    assert oracle.e2m1_encode_sr(7.5, 0) == 7 and oracle.e2m1_encode_sr(6.0, 65535) == 7
+
+
+def test_variant_zero_is_the_plain_recipe():
+    x = _rand_tensor(np.random.default_rng(44), 32, 64)
+    q0, s0, g0 = oracle.quantize(x)
+    q1, s1, g1 = oracle.quantize_ex(x, 0)
+    assert np.array_equal(q0, q1) and np.array_equal(s0, s1) and np.array_equal(g0, g1)
+
+
+def _nibbles(q):
+    return np.stack([q & 15, q >> 4], axis=-1).reshape(q.shape[:-1] + (2 * q.shape[-1],))
+
+
+def test_2d_scaling_is_transpose_invariant():
+    """The pages' reason for 16x16 weight blocks: quantizing W^T gives the
+    transpose of quantizing W (codes and tile scales)."""
+    rng = np.random.default_rng(45)
+    for _ in range(10):
+        x = _rand_tensor(rng, 48, 80)
+        xt = np.ascontiguousarray(x.T)
+        q, sf, g = oracle.quantize_ex(x, oracle.TWO_D)
+        qt, sft, gt = oracle.quantize_ex(xt, oracle.TWO_D)
+        assert g[0] == gt[0]
+        assert np.array_equal(_nibbles(qt), _nibbles(q).T)
+        assert np.array_equal(sft[::16], sf[::16].T)          # one byte per tile, stored per row
+        assert np.all(sf.reshape(3, 16, 5)[:, :, :] == sf.reshape(3, 16, 5)[:, :1, :])
+        # COLWISE describes x^T
+        qc, sfc, gc = oracle.quantize_ex(x, oracle.TWO_D | oracle.COLWISE)
+        assert np.array_equal(qc, qt) and np.array_equal(sfc, sft)
+    # row-wise 1x16 blocks are not transpose invariant in general
+    x = _rand_tensor(np.random.default_rng(46), 32, 32)
+    q, _, _ = oracle.quantize_ex(x, 0)
+    qt, _, _ = oracle.quantize_ex(np.ascontiguousarray(x.T), 0)
+    assert not np.array_equal(_nibbles(qt), _nibbles(q).T)
+
+
+def test_colwise_quantizes_the_transpose():
+    rng = np.random.default_rng(47)
+    x = _rand_tensor(rng, 64, 48)
+    for v in (0, oracle.SR, oracle.RHT, oracle.RHT | oracle.SR):
+        a = oracle.quantize_ex(x, v | oracle.COLWISE, signs=0xA5C3, seed=9, offset=3)
+        b = oracle.quantize_ex(np.ascontiguousarray(x.T), v, signs=0xA5C3, seed=9, offset=3)
+        for u, w in zip(a, b):
+            assert np.array_equal(u, w)
+
+
+def test_variants_match_exact_rationals():
+    """2D tiles, RHT and stochastic rounding re-derived with exact rationals
+    (the RHT values from the pinned butterfly, the draws from the pinned
+    Philox stream)."""
+    rng = np.random.default_rng(48)
+    for trial in range(6):
+        x = _rand_tensor(rng, 16, 32)
+        xs = [[exact.bf16_to_fraction(int(b)) for b in row] for row in x.tolist()]
+        # 2D
+        q, sf, g = oracle.quantize_ex(x, oracle.TWO_D)
+        codes, scales, ge = exact.quantize_values(xs, tiles=True)
+        assert F(float(g[0])) == ge and sf.tolist() == scales
+        # the sign bit comes from the input bits (a bf16 -0 has no rational sign)
+        want = [[(c & 7) | (8 if (b & 0x8000) else 0) for c, b in zip(cr, br)] for cr, br in zip(codes, x.tolist())]
+        assert _nibbles(q).tolist() == want, f"2D trial {trial}"
+        # RHT (+ SR)
+        signs, seed, off = int(rng.integers(0, 1 << 16)), int(rng.integers(0, 1 << 40)), int(rng.integers(0, 99))
+        v = np.stack([np.concatenate([oracle.rht16(bits_to_f32(row[c:c + 16]), signs) for c in range(0, 32, 16)])
+                      for row in x])
+        vf = [[F(float(a)) for a in row] for row in v]
+        for variant in (oracle.RHT, oracle.RHT | oracle.SR, oracle.SR):
+            vals = vf if variant & oracle.RHT else [[F(float(a)) for a in bits_to_f32(row)] for row in x]
+            draws = None
+            if variant & oracle.SR:
+                draws = []
+                for r in range(16):
+                    dr = []
+                    for c in range(32):
+                        i = r * 32 + c
+                        n = i // 8 + off
+                        w = oracle.philox4x32_10([n & 0xffffffff, n >> 32, 0, 0], [seed & 0xffffffff, seed >> 32])
+                        dr.append(int(w[(i & 7) >> 1] >> (16 * (i & 1))) & 0xffff)
+                    draws.append(dr)
+            q, sf, g = oracle.quantize_ex(x, variant, signs=signs, seed=seed, offset=off)
+            codes, scales, ge = exact.quantize_values(vals, draws=draws)
+            src = v if variant & oracle.RHT else bits_to_f32(x)
+            neg = np.signbit(src)
+            want = [[(c & 7) | (8 if n else 0) for c, n in zip(cr, nr)] for cr, nr in zip(codes, neg.tolist())]
+            assert F(float(g[0])) == ge and sf.tolist() == scales, f"variant {variant} trial {trial}"
+            assert _nibbles(q).tolist() == want, f"variant {variant} trial {trial}"
+
+
+def test_variant_shape_rules():
+    x = _rand_tensor(np.random.default_rng(49), 24, 32)
+    with pytest.raises(ValueError):
+        oracle.quantize_ex(x, oracle.TWO_D)                  # rows % 16
+    with pytest.raises(ValueError):
+        oracle.quantize_ex(x, oracle.COLWISE)
+    with pytest.raises(ValueError):
+        oracle.quantize_ex(_rand_tensor(np.random.default_rng(50), 32, 32), oracle.TWO_D | oracle.RHT)
+    oracle.quantize_ex(x, oracle.RHT | oracle.SR)            # row-wise variants take any row count
