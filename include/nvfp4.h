@@ -227,6 +227,63 @@ nvfp4_status nvfp4_grouped_gemm(const uint8_t* a_q, const uint8_t* a_sf, const f
                                 int64_t M, int64_t N, int64_t K, float* c, void* stream);
 
 /* ------------------------------------------------------------------------
+ * Quantize variants of the NVFP4 training recipe (axbrief.com, "NVFP4: how
+ * NVIDIA pre-trained a 12B model on 10 trillion tokens", section "Four
+ * stabilizers for training: from RHT to stochastic rounding"), combinable
+ * bit flags:
+ *   NVFP4_VAR_COLWISE  quantize x^T (blocks run down x's columns): the
+ *                      Dgrad / Wgrad operand layout.  Outputs describe the
+ *                      [cols][rows] matrix.  Needs rows % 16 == 0.
+ *   NVFP4_VAR_2D       one E4M3 scale per 16 x 16 tile from the tile's amax
+ *                      (weights: W and W^T quantize to the same values); the
+ *                      byte is written for each of the tile's 16 rows, so sf
+ *                      keeps the [R][C/16] layout every consumer reads.
+ *                      Needs rows % 16 == 0; not combined with RHT (ENOTSUP).
+ *   NVFP4_VAR_RHT      each 16-value block (along the block direction) is
+ *                      replaced by H16 (s .* x) / 4 before quantizing: H16
+ *                      the Sylvester Hadamard matrix (H[i][j] =
+ *                      (-1)^popcount(i & j)), s_j = -1 where bit j of
+ *                      rht_signs is set; computed in fp32 as the fast
+ *                      Walsh-Hadamard stages h = 1, 2, 4, 8 (pairs (i, i+h)
+ *                      with i & h == 0 become (a + b, a - b)), then * 1/4.
+ *                      The tensor amax and every quotient use these fp32
+ *                      values.
+ *   NVFP4_VAR_SR       stochastic element rounding: with lo <= y < hi the
+ *                      neighbouring E2M1 magnitudes of y = RN32(|x| / d),
+ *                      the code rounds up when u16 / 65536 < (y - lo) /
+ *                      (hi - lo) (y >= 6 gives 6).  u16: Philox4x32-10
+ *                      (Salmon et al., SC 2011), key (seed, seed >> 32),
+ *                      counter (n, n >> 32, 0, 0) with n = i / 8 + offset
+ *                      for output element i (row-major index into q's
+ *                      values across the batch), 16-bit half i % 2 (low
+ *                      first) of word (i % 8) / 2.  Block scales stay
+ *                      round-to-nearest.
+ * ------------------------------------------------------------------------ */
+enum {
+  NVFP4_VAR_COLWISE = 1,
+  NVFP4_VAR_2D = 2,
+  NVFP4_VAR_RHT = 4,
+  NVFP4_VAR_SR = 8
+};
+
+/* Device scratch for nvfp4_quantize_ex: per-workgroup partial maxima (no
+ * zero-fill needed).  0 when batch <= 0. */
+size_t nvfp4_quantize_ex_workspace_bytes(int64_t batch);
+
+/* Variant quantize of x [batch][rows][cols] bf16 (cols % 16 == 0).  With
+ * (R, C) = (rows, cols), or (cols, rows) under COLWISE: q [batch][R][C/2],
+ * sf [batch][R][C/16], g [batch] (the tensor scale of the transformed
+ * values).  Two passes over x (amax, then encode).  variant 0 equals
+ * nvfp4_quantize bit for bit.
+ * Errors: EINVAL (cols % 16 != 0, rows % 16 != 0 with COLWISE or 2D, unknown
+ *   variant bits, rht_signs > 0xFFFF, batch > 65535, null pointers), ENOTSUP
+ *   (2D with RHT, or the device), EALIGN (x, q not 16-byte aligned; g,
+ *   workspace not 4-byte aligned), EWORKSPACE, EHIP. */
+nvfp4_status nvfp4_quantize_ex(const uint16_t* x, int64_t batch, int64_t rows, int64_t cols, uint32_t variant,
+                               uint32_t rht_signs, uint64_t seed, uint64_t offset, uint8_t* q, uint8_t* sf,
+                               float* g, void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
  * MXFP4, the earlier microscaling format: 32 consecutive E2M1 values share
  * one power-of-two scale stored as an E8M0 byte (value 2^(byte - 127), 255
  * is NaN); there is no tensor scale; about 4.25 bits per value (iwan.kr,

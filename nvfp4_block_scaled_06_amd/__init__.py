@@ -60,6 +60,9 @@ _SIGS = {
     "nvfp4_grouped_gemm": (_I32, [_P, _P, _P, _P, _P, _P, _P, _I32, _I64, _I64, _I64, _P, _P]),
     "nvfp4_kv_attention_workspace_bytes": (ctypes.c_size_t, [_P, _I32, _I64]),
     "nvfp4_kv_decode_attention": (_I32, [_P, _P, _I32, _I64, ctypes.c_float, _P, _P, ctypes.c_size_t, _P]),
+    "nvfp4_quantize_ex_workspace_bytes": (_SZ, [_I64]),
+    "nvfp4_quantize_ex": (_I32, [_P, _I64, _I64, _I64, ctypes.c_uint32, ctypes.c_uint32, ctypes.c_uint64,
+                                 ctypes.c_uint64, _P, _P, _P, _P, _SZ, _P]),
     "nvfp4_mxfp4_quantize": (_I32, [_P, _I64, _I64, _P, _P, _P]),
     "nvfp4_mxfp4_dequantize": (_I32, [_P, _P, _I64, _I64, _P, _P]),
     "nvfp4_mxfp4_gemm": (_I32, [_P, _P, _P, _P, _I64, _I64, _I64, _P, _P]),
@@ -277,6 +280,40 @@ def grouped_gemm(a_q, a_sf, a_g, b_q, b_sf, b_g, offsets, out=None):
         _ptr(a_q), _ptr(a_sf), _ptr(a_g), _ptr(b_q), _ptr(b_sf), _ptr(b_g), _ptr(offsets), E, M, N, 2 * K2,
         _ptr(c), _stream(a_q.device)))
     return c
+
+
+# ---------------------------------------------------------------- training variants
+VAR_COLWISE, VAR_2D, VAR_RHT, VAR_SR = 1, 2, 4, 8
+
+
+def quantize_ex(x, variant, rht_signs=0, seed=0, offset=0, workspace=None, out=None):
+    """Training-recipe quantize of bf16 x [..., rows, cols]: variant is an OR
+    of VAR_COLWISE (quantize x^T), VAR_2D (16x16 tile scales), VAR_RHT
+    (16-point random Hadamard transform with the sign mask rht_signs) and
+    VAR_SR (stochastic element rounding from Philox4x32-10 with seed,
+    offset).  Returns (q, sf, g); under VAR_COLWISE they describe x^T."""
+    _need(x, torch.bfloat16, "x")
+    if x.dim() < 2:
+        raise ValueError("x must be [..., rows, cols]")
+    rows, cols = x.shape[-2], x.shape[-1]
+    lead = tuple(x.shape[:-2])
+    batch = 1
+    for d in lead:
+        batch *= d
+    R, C = (cols, rows) if variant & VAR_COLWISE else (rows, cols)
+    if out is not None:
+        q, sf, g = out
+    else:
+        q = torch.empty(lead + (R, C // 2), dtype=torch.uint8, device=x.device)
+        sf = torch.empty(lead + (R, C // 16), dtype=torch.uint8, device=x.device)
+        g = torch.empty(lead if lead else (1,), dtype=torch.float32, device=x.device)
+    wsb = int(_lib().nvfp4_quantize_ex_workspace_bytes(batch))
+    if workspace is None:
+        workspace = torch.empty(max(wsb, 4), dtype=torch.uint8, device=x.device)
+    _check("nvfp4_quantize_ex", _lib().nvfp4_quantize_ex(
+        _ptr(x), batch, rows, cols, variant, rht_signs, seed, offset, _ptr(q), _ptr(sf), _ptr(g),
+        _ptr(workspace), workspace.numel(), _stream(x.device)))
+    return q, sf, g
 
 
 # ---------------------------------------------------------------- MXFP4

@@ -1,0 +1,115 @@
+"""GPU parity: the training-recipe quantize variants (column-wise operand
+layout, 16x16 2D scales, random Hadamard transform, stochastic rounding),
+bit-exact against the oracle."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from gpu_util import Guarded, bits, np_
+
+pytestmark = pytest.mark.gpu
+
+nv = pytest.importorskip("nvfp4_block_scaled_06_amd")
+
+VARIANTS = [0, 1, 2, 3, 4, 5, 8, 9, 10, 11, 12, 13]
+
+
+def _x(shape, seed, wide=False):
+    gen = torch.Generator().manual_seed(seed)
+    z = torch.randn(shape, generator=gen)
+    if wide:                                             # per-row magnitudes over a wide range
+        z = z * torch.exp2(torch.randint(-30, 30, shape[:-1] + (1,), generator=gen).float())
+    z.view(-1)[::97] = 0.0
+    z.view(-1)[5::211] = -0.0
+    return z.to(torch.bfloat16).cuda()
+
+
+def _check(x, variant, signs=0xB5E1, seed=0x1234_5678_9ABC, offset=17):
+    print("case: quantize_ex variant", variant, tuple(x.shape), flush=True)
+    q, sf, g = nv.quantize_ex(x, variant, rht_signs=signs, seed=seed, offset=offset)
+    torch.cuda.synchronize()
+    wq, wsf, wg = oracle.quantize_ex(bits(x), variant, signs=signs, seed=seed, offset=offset)
+    np.testing.assert_array_equal(np_(g).reshape(-1), np.asarray(wg).reshape(-1))
+    np.testing.assert_array_equal(np_(sf).reshape(wsf.shape), wsf)
+    np.testing.assert_array_equal(np_(q).reshape(wq.shape), wq)
+
+
+@pytest.mark.parametrize("variant", VARIANTS)
+@pytest.mark.parametrize("shape", [(32, 64), (48, 80), (16, 16), (3, 64, 128), (64, 1040)])
+def test_variants_match_oracle(variant, shape):
+    _check(_x(shape, sum(shape) + variant, wide=len(shape) == 3), variant)
+
+
+@pytest.mark.parametrize("variant", [0, 4, 8, 12])
+def test_rowwise_variants_any_row_count(variant):
+    _check(_x((40, 96), 5), variant)
+
+
+def test_variant_zero_equals_plain_quantize():
+    x = _x((2, 128, 256), 6, wide=True)
+    q, sf, g = nv.quantize_ex(x, 0)
+    q0, sf0, g0 = nv.quantize(x)
+    torch.cuda.synchronize()
+    assert torch.equal(q, q0) and torch.equal(sf, sf0) and torch.equal(g, g0)
+
+
+def test_sr_seed_and_offset_change_the_draws():
+    x = _x((64, 256), 7)
+    a = nv.quantize_ex(x, nv.VAR_SR, seed=1)[0]
+    b = nv.quantize_ex(x, nv.VAR_SR, seed=2)[0]
+    c = nv.quantize_ex(x, nv.VAR_SR, seed=1, offset=1)[0]
+    d = nv.quantize_ex(x, nv.VAR_SR, seed=1)[0]
+    torch.cuda.synchronize()
+    assert torch.equal(a, d) and not torch.equal(a, b) and not torch.equal(a, c)
+
+
+def test_outputs_stay_in_bounds():
+    x = _x((48, 80), 8)
+    for variant in (1, 13):
+        R, C = (80, 48) if variant & 1 else (48, 80)
+        q = Guarded((R, C // 2), torch.uint8)
+        sf = Guarded((R, C // 16), torch.uint8)
+        g = Guarded((1,), torch.float32)
+        nv.quantize_ex(x, variant, out=(q.view, sf.view, g.view))
+        torch.cuda.synchronize()
+        q.check()
+        sf.check()
+        g.check()
+
+
+def test_rejected_combinations():
+    x = _x((32, 64), 9)
+    with pytest.raises(nv.NVFP4Error):
+        nv.quantize_ex(x, nv.VAR_2D | nv.VAR_RHT)
+    with pytest.raises(nv.NVFP4Error):
+        nv.quantize_ex(_x((24, 64), 9), nv.VAR_COLWISE)
+    with pytest.raises(nv.NVFP4Error):
+        nv.quantize_ex(x, 16)
+    with pytest.raises(nv.NVFP4Error):
+        nv.quantize_ex(x, nv.VAR_RHT, rht_signs=1 << 16)
+
+
+def test_2d_weight_and_its_transpose_agree():
+    """One 2048 x 7168 expert weight: 2D scaling of W and of W^T (COLWISE)
+    give transposed codes and scales, and both match the oracle."""
+    w = synth.experts(1, 2048, 7168, device="cuda")[0]
+    print("case: 2D expert weight 2048x7168", flush=True)
+    q, sf, g = nv.quantize_ex(w, nv.VAR_2D)
+    qt, sft, gt = nv.quantize_ex(w, nv.VAR_2D | nv.VAR_COLWISE)
+    torch.cuda.synchronize()
+    wq, wsf, wg = oracle.quantize_ex(bits(w), oracle.TWO_D)
+    np.testing.assert_array_equal(np_(q), wq)
+    np.testing.assert_array_equal(np_(sf), wsf)
+    assert np_(g)[0] == wg[0] == np_(gt)[0]
+    nib = lambda a: np.stack([a & 15, a >> 4], axis=-1).reshape(a.shape[0], -1)
+    np.testing.assert_array_equal(nib(np_(qt)), nib(np_(q)).T)
+    np.testing.assert_array_equal(np_(sft)[::16], np_(sf)[::16].T)
+
+
+def test_wgrad_operand_rht_sr_colwise():
+    """A 4096 x 7168 slice of the activations as a Wgrad operand: quantized
+    along the tokens (COLWISE) with RHT and stochastic rounding."""
+    a = synth.activations(tokens=4096, device="cuda")
+    _check(a, nv.VAR_COLWISE | nv.VAR_RHT | nv.VAR_SR, signs=0x6A3C, seed=77, offset=0)
