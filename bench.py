@@ -13,7 +13,9 @@ Extra records in the same line ("rows"): the single 1024x1024 tensor, the
 cache (512 appends of 256 tokens, decode QK over 131072 tokens, 32 query
 heads, plus decode attention), the 8192 x 2048 x 7168 block-scaled GEMM and
 the grouped MoE GEMM (16384 tokens routed top-8 over 64 experts) in TFLOP/s,
-and MXFP4 against NVFP4 on the same data (codec and GEMM speed, error) --
+MXFP4 against NVFP4 on the same data (codec and GEMM speed, error), and the
+training-recipe quantize variants (2D weight scales, column-wise RHT + SR
+Wgrad operands) --
 each with its roofline fraction.  Every kernel time comes from HIP events recorded on
 the stream the kernels run on.
 
@@ -43,7 +45,7 @@ def parse():
     p.add_argument("--no-extras", action="store_true", help="headline step only")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--rows-only", default="",
-                   help="comma list of extra rows to run (experts,single,acts,kv,gemm,moe,mx)")
+                   help="comma list of extra rows to run (experts,single,acts,kv,gemm,moe,mx,train)")
     p.add_argument("--traffic-kernels", action="store_true",
                    help="only launch the headline kernels, the GEMM and a 1 GiB device copy, 3 times each "
                         "(the workload for rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs)")
@@ -288,6 +290,8 @@ def run_extras(nv, synth, torch, which):
         rows["moe_grouped_gemm_16384x8_64x2048x7168"] = run_moe(nv, synth, torch)
     if "mx" in which:
         rows["mxfp4_vs_nvfp4"] = run_mx(nv, synth, torch)
+    if "train" in which:
+        rows["training_variants"] = run_train(nv, synth, torch)
     del fbuf
     torch.cuda.empty_cache()
     return rows
@@ -375,6 +379,35 @@ def run_mx(nv, synth, torch):
     return res
 
 
+def run_train(nv, synth, torch):
+    """Training-recipe quantize variants: the 64 x 2048 x 7168 expert weights
+    with 16x16 2D scales (and their transposes), and the 16384 x 7168
+    activations as a Wgrad operand (column-wise, RHT, stochastic rounding).
+    Algorithmic bytes count one read of x and one write of the outputs; the
+    variant path reads x twice (amax pass, encode pass)."""
+    res = {}
+    x = synth.experts(device="cuda")
+    n = x.numel()
+    ws = torch.empty(nv.lib().nvfp4_quantize_ex_workspace_bytes(64), dtype=torch.uint8, device="cuda")
+    for name, v in (("2d", nv.VAR_2D), ("2d_colwise", nv.VAR_2D | nv.VAR_COLWISE)):
+        out = nv.quantize_ex(x, v, workspace=ws)
+        m = timed(torch, lambda: nv.quantize_ex(x, v, workspace=ws, out=out), 10)
+        res[f"experts_64x2048x7168_{name}"] = {"ms": m, **roof(bytes_quantize(n, 64), m, HBM_PEAK_GBS, "GB/s")}
+        del out
+    del x
+    torch.cuda.empty_cache()
+    a = synth.activations(device="cuda")
+    n = a.numel()
+    for name, v in (("rowwise_sr", nv.VAR_SR), ("colwise_rht_sr", nv.VAR_COLWISE | nv.VAR_RHT | nv.VAR_SR)):
+        out = nv.quantize_ex(a, v, rht_signs=0x6A3C, seed=77, workspace=ws)
+        m = timed(torch, lambda: nv.quantize_ex(a, v, rht_signs=0x6A3C, seed=77, workspace=ws, out=out), 10)
+        res[f"activations_16384x7168_{name}"] = {"ms": m, **roof(bytes_quantize(n, 1), m, HBM_PEAK_GBS, "GB/s")}
+        del out
+    del a, ws
+    torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline(synth, torch):
     """The oracle, untouched, on the whole headline workload: quantize +
     dequantize of all 64 expert matrices, two passes (about 10 s of CPU work
@@ -456,7 +489,7 @@ def main():
     rows = {}
     if not args.no_extras:
         which = (args.rows_only.split(",") if args.rows_only
-                 else ["experts", "single", "acts", "kv", "gemm", "moe", "mx"])
+                 else ["experts", "single", "acts", "kv", "gemm", "moe", "mx", "train"])
         rows = run_extras(nv, synth, torch, which)
         log("extras done")
     cpu = None if args.no_cpu else cpu_baseline(synth, torch)
