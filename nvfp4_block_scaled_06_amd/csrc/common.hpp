@@ -172,6 +172,17 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
 
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)); }
 
+// XCD-aware tile order.  The dispatcher hands workgroup i (linear id) to
+// XCD i % 8, in order of i; each XCD has its own L2.  Giving XCD x a
+// contiguous run of the T tiles (row-major over (m, n) tiles) makes the
+// workgroups that share an A panel run on one XCD, so that panel is fetched
+// into one L2 instead of eight.  Returns the tile index for workgroup lin.
+constexpr int kXcds = 8;
+__device__ __forceinline__ int64_t xcd_tile(int64_t lin, int64_t T) {
+  const int64_t x = lin % kXcds, slot = lin / kXcds, per = T / kXcds, extra = T % kXcds;
+  return x * per + (x < extra ? x : extra) + slot;
+}
+
 }  // namespace nvfp4
 
 // ---------------------------------------------------------------- host side

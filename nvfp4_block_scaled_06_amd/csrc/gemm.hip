@@ -241,7 +241,8 @@ __global__ void __launch_bounds__(GThreads) gemm_kernel(const uint8_t* __restric
                                                         int64_t M, int64_t N, int64_t K, float* __restrict__ C) {
   __shared__ __attribute__((aligned(16))) _Float16 As[2][GTM][GLD];
   __shared__ __attribute__((aligned(16))) _Float16 Bs[2][GTN][GLD];
-  const int64_t m0 = (int64_t)blockIdx.y * GTM, n0 = (int64_t)blockIdx.x * GTN;
+  const int64_t tile = xcd_tile((int64_t)blockIdx.y * gridDim.x + blockIdx.x, (int64_t)gridDim.x * gridDim.y);
+  const int64_t m0 = tile / gridDim.x * GTM, n0 = tile % gridDim.x * GTN;
   gemm_tile<kAligned>(aq, asf, m0, M, bq, bsf, n0, N, K, ag[0] * bg[0], C, N, As, Bs);
 }
 

@@ -267,7 +267,8 @@ __global__ void __launch_bounds__(MThreads) mx_gemm_kernel(const uint8_t* __rest
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int wm = wave >> 1, wn = wave & 1;
-  const int64_t m0 = (int64_t)blockIdx.y * MTM, n0 = (int64_t)blockIdx.x * MTN;
+  const int64_t tile = xcd_tile((int64_t)blockIdx.y * gridDim.x + blockIdx.x, (int64_t)gridDim.x * gridDim.y);
+  const int64_t m0 = tile / gridDim.x * MTM, n0 = tile % gridDim.x * MTN;
   const MxOperand A = mx_operand(aq, asf, m0, M, K), B = mx_operand(bq, bsf, n0, N, K);
 
   f32x16 acc[4][4];
