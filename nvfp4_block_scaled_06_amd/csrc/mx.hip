@@ -259,6 +259,33 @@ __device__ __forceinline__ void mx_substep(f32x16 (&acc)[4][4], const MxFrag& f,
   __builtin_amdgcn_sched_barrier(0);
 }
 
+// Writes a wave's 128 x 128 accumulators (rows wm*128.., columns wn*128..
+// of the tile at (m0, n0)); C layout of the 32 x 32 MFMA: lane l, element e
+// is row 8 (e / 4) + 4 (l / 32) + e % 4, column l % 32.
+__device__ __forceinline__ void mx_epilogue(const f32x16 (&acc)[4][4], float* __restrict__ C, int64_t m0, int64_t n0,
+                                            int64_t M, int64_t N, int wm, int wn, int lane) {
+  float* Cw = C + (m0 + wm * 128 + 4 * (lane >> 5)) * N + n0 + wn * 128 + (lane & 31);
+  if (m0 + MTM <= M && n0 + MTN <= N) {         // whole tile: no bounds checks
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) Cw[(i * 32 + 8 * (e >> 2) + (e & 3)) * N + j * 32] = acc[i][j][e];
+  } else {
+    const int64_t rlim = M - (m0 + wm * 128 + 4 * (lane >> 5)), clim = N - (n0 + wn * 128 + (lane & 31));
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int r = i * 32 + 8 * (e >> 2) + (e & 3), cc = j * 32;
+          if (r < rlim && cc < clim) Cw[r * N + cc] = acc[i][j][e];
+        }
+  }
+}
+
 template <bool kAligned>
 __global__ void __launch_bounds__(MThreads) mx_gemm_kernel(const uint8_t* __restrict__ aq, const uint8_t* __restrict__ asf,
                                                            const uint8_t* __restrict__ bq, const uint8_t* __restrict__ bsf,
@@ -309,26 +336,149 @@ __global__ void __launch_bounds__(MThreads) mx_gemm_kernel(const uint8_t* __rest
     mx_store_step(rb, tid, sm.b[buf ^ 1], sm.bs[buf ^ 1]);
     __syncthreads();
   }
-  float* Cw = C + (m0 + wm * 128 + 4 * (lane >> 5)) * N + n0 + wn * 128 + (lane & 31);
-  if (m0 + MTM <= M && n0 + MTN <= N) {         // whole tile: no bounds checks
+  mx_epilogue(acc, C, m0, n0, M, N, wm, wn, lane);
+}
+
+
+// ------------------------------------------------------------ GEMM, buffer-to-LDS loads
+// The aligned GEMM (K % 256 == 0) moves each K step straight from HBM into
+// LDS with buffer-to-LDS loads: no staging registers and no LDS writes by
+// the waves, and step k+1 streams in while step k is contracted.
+// A load instruction fills 1 KB of LDS, 16 bytes per lane in lane order, so
+// code rows are stored unpadded (128 bytes) with their 16-byte chunks
+// swizzled: chunk c of row r sits at position c ^ ((r >> 1) & 7).  The 16
+// rows that 16 lanes of an MFMA fragment read then fall on distinct bank
+// groups, and each lane loads the global chunk its LDS position holds.
+// Scale bytes are stored raw (8 per row) and rearranged when read.
+typedef __attribute__((address_space(3))) void mx_lds_t;
+
+struct MxDmaSmem {
+  uint8_t a[2][MTM * 128];
+  uint8_t b[2][MTN * 128];
+  uint32_t as[2][MTM][2];
+  uint32_t bs[2][MTN][2];
+};
+
+// s_waitcnt vmcnt(0) with the other counters unconstrained; the compiler
+// does not track the completion of buffer-to-LDS loads.
+__device__ __forceinline__ void mx_wait_vm0() {
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_waitcnt((0x7 << 4) | (0xF << 8));
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// Wave w's share of one K step of one operand: code rows [64 w, 64 w + 64)
+// (8 instructions of 8 rows) and the scale bytes of the same rows (2
+// instructions of 32 rows, 4 bytes per lane).
+__device__ __forceinline__ void mx_dma_step(const MxOperand& o, int wave, int lane, int64_t k0, uint8_t* codes,
+                                            uint32_t (*sc)[2]) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) Cw[(i * 32 + 8 * (e >> 2) + (e & 3)) * N + j * 32] = acc[i][j][e];
-  } else {
-    const int64_t rlim = M - (m0 + wm * 128 + 4 * (lane >> 5)), clim = N - (n0 + wn * 128 + (lane & 31));
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int r = i * 32 + 8 * (e >> 2) + (e & 3), cc = j * 32;
-          if (r < rlim && cc < clim) Cw[r * N + cc] = acc[i][j][e];
-        }
+  for (int j = 0; j < 8; ++j) {
+    const int r = 64 * wave + 8 * j + (lane >> 3);
+    const int c = (lane & 7) ^ ((r >> 1) & 7);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(o.q, (mx_lds_t*)(codes + (64 * wave + 8 * j) * 128), 16,
+                                             (uint32_t)r * o.qrow + (uint32_t)(k0 / 2) + 16u * c, 0, 0, 0);
   }
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int r = 64 * wave + 32 * j + (lane >> 1);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(o.s, (mx_lds_t*)&sc[64 * wave + 32 * j][0], 4,
+                                             (uint32_t)r * o.srow + (uint32_t)(k0 / 32) + 4u * (lane & 1), 0, 0, 0);
+  }
+}
+
+__device__ __forceinline__ void mx_dma_frags(MxFrag& f, const uint8_t* Acur, const uint8_t* Bcur, int kk, int h,
+                                             int sw) {
+  const int pos = ((2 * kk + h) ^ sw) * 16;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const u32x4 v = *(const u32x4*)(Acur + i * 32 * 128 + pos);
+    f.a[i] = i32x8{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const u32x4 v = *(const u32x4*)(Bcur + j * 32 * 128 + pos);
+    f.b[j] = i32x8{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
+  }
+}
+
+template <int kk>
+__device__ __forceinline__ void mx_dma_substep(f32x16 (&acc)[4][4], const MxFrag& f, MxFrag& nf, const uint8_t* Acur,
+                                               const uint8_t* Bcur, int h, int sw, const uint32_t (&sa)[4],
+                                               const uint32_t (&sb)[4]) {
+  __builtin_amdgcn_sched_barrier(0);
+  if (kk < 3) mx_dma_frags(nf, Acur, Bcur, kk + 1, h, sw);
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.a[i], f.b[j], acc[i][j], 4, 4, kk, (int)sa[i], kk,
+                                                                  (int)sb[j]);
+  if (kk < 3) {
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);   // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+__global__ void __launch_bounds__(MThreads) mx_gemm_dma_kernel(const uint8_t* __restrict__ aq,
+                                                               const uint8_t* __restrict__ asf,
+                                                               const uint8_t* __restrict__ bq,
+                                                               const uint8_t* __restrict__ bsf, int64_t M, int64_t N,
+                                                               int64_t K, float* __restrict__ C) {
+  __shared__ __attribute__((aligned(16))) MxDmaSmem sm;
+  const int tid = threadIdx.x;
+  const int wave = wave_id(), lane = tid & 63;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int64_t tile = xcd_tile((int64_t)blockIdx.y * gridDim.x + blockIdx.x, (int64_t)gridDim.x * gridDim.y);
+  const int64_t m0 = tile / gridDim.x * MTM, n0 = tile % gridDim.x * MTN;
+  const MxOperand A = mx_operand(aq, asf, m0, M, K), B = mx_operand(bq, bsf, n0, N, K);
+
+  f32x16 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+
+  const int64_t nk = K / MTK;
+  mx_dma_step(A, wave, lane, 0, sm.a[0], sm.as[0]);
+  mx_dma_step(B, wave, lane, 0, sm.b[0], sm.bs[0]);
+  mx_wait_vm0();
+  __syncthreads();
+  const int arow = wm * 128 + (lane & 31), brow = wn * 128 + (lane & 31), h = lane >> 5;
+  const int sw = ((lane & 31) >> 1) & 7;       // the swizzle of every row this lane reads
+  const uint32_t sel = h ? 0x07050301u : 0x06040200u;
+  for (int64_t kt = 0; kt < nk; ++kt) {
+    const int buf = (int)(kt & 1);
+    if (kt + 1 < nk) {                         // the next step into the other buffer
+      mx_dma_step(A, wave, lane, (kt + 1) * MTK, sm.a[buf ^ 1], sm.as[buf ^ 1]);
+      mx_dma_step(B, wave, lane, (kt + 1) * MTK, sm.b[buf ^ 1], sm.bs[buf ^ 1]);
+    }
+    const uint8_t* Acur = sm.a[buf] + arow * 128;
+    const uint8_t* Bcur = sm.b[buf] + brow * 128;
+    uint32_t sa[4], sb[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t* ra = sm.as[buf][arow + 32 * i];
+      const uint32_t* rb = sm.bs[buf][brow + 32 * i];
+      sa[i] = __builtin_amdgcn_perm(ra[1], ra[0], sel);
+      sb[i] = __builtin_amdgcn_perm(rb[1], rb[0], sel);
+    }
+    MxFrag f0, f1;
+    mx_dma_frags(f0, Acur, Bcur, 0, h, sw);
+    mx_dma_substep<0>(acc, f0, f1, Acur, Bcur, h, sw, sa, sb);
+    mx_dma_substep<1>(acc, f1, f0, Acur, Bcur, h, sw, sa, sb);
+    mx_dma_substep<2>(acc, f0, f1, Acur, Bcur, h, sw, sa, sb);
+    mx_dma_substep<3>(acc, f1, f0, Acur, Bcur, h, sw, sa, sb);
+    mx_wait_vm0();                             // step kt+1 is in LDS
+    __syncthreads();                           // ... for every wave; buffer buf is free
+  }
+  mx_epilogue(acc, C, m0, n0, M, N, wm, wn, lane);
 }
 
 }  // namespace nvfp4
@@ -394,7 +544,7 @@ nvfp4_status nvfp4_mxfp4_gemm(const uint8_t* a_q, const uint8_t* a_sf, const uin
   const bool aligned = K % MTK == 0 && (reinterpret_cast<uintptr_t>(a_sf) & 7u) == 0 &&
                        (reinterpret_cast<uintptr_t>(b_sf) & 7u) == 0;
   if (aligned)
-    mx_gemm_kernel<true><<<grid, MThreads, 0, (hipStream_t)stream>>>(a_q, a_sf, b_q, b_sf, M, N, K, c);
+    mx_gemm_dma_kernel<<<grid, MThreads, 0, (hipStream_t)stream>>>(a_q, a_sf, b_q, b_sf, M, N, K, c);
   else
     mx_gemm_kernel<false><<<grid, MThreads, 0, (hipStream_t)stream>>>(a_q, a_sf, b_q, b_sf, M, N, K, c);
   NVFP4_LAUNCH_CHECK();
