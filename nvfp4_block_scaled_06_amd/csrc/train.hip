@@ -21,12 +21,16 @@
 // The quotients use the fp64-reciprocal method of the codec: its exactness
 // argument holds for any fp32 numerator (see common.hpp).
 //
-// Work unit: one wave takes a 16-row x 64-column group of x; lane L holds
-// row L % 16 of the 16 x 16 tile L / 16 (16 values, one block).  COLWISE
-// transposes the group through LDS so that lane L then holds column
-// 16 (L / 16) + L % 16 of the group.  Two passes, each reading x once: the
-// amax pass (transformed values, per-workgroup partial maxima) and the
-// encode pass.
+// Work unit: a strip of 16 rows x 512 columns per wave.  Lane l holds
+// columns 8l..8l+7 of each of the 16 rows (16 loads of 16 bytes, each
+// instruction one contiguous kilobyte).  Row-wise, a block is the lane pair
+// (2m, 2m+1) within a row; COLWISE, a block is one column of the strip, all
+// in one lane, so x^T needs no data exchange.  2D tiles are the lane pair
+// over all 16 rows.  RHT runs in registers (across the pair for its last
+// stage row-wise).  A wave walks a run of strips down one 512-column band,
+// so COLWISE writes whole stretches of each output row in turn.  Two
+// passes, each reading x once: the amax of the quantized values, then the
+// encode.
 #include <algorithm>
 
 #include "common.hpp"
@@ -35,86 +39,14 @@ namespace nvfp4 {
 
 constexpr int kVarThreads = 256;
 constexpr int kVarMaxPartials = 2048;
-constexpr int kGroupRows = 16, kGroupCols = 64;
-constexpr int kTRow = kGroupCols + 8;          // LDS row of a transpose buffer (bf16 units, 16-byte rows)
+constexpr int kStripRows = 16, kStripCols = 512;
 
 struct VarShape {
   int64_t rows, cols, n;                       // per tensor
-  int64_t grp_r, grp_c;                        // groups down and across
   int64_t R, C;                                // output matrix per tensor
+  int64_t sr, sc;                              // strips down and across
+  int64_t seg, nseg, nitems;                   // strips per work item, items per band, items per tensor
 };
-
-// The lane's 16 values of group gidx (rows 16 gr.., columns 64 gc + 16 t4..)
-// as fp32, transposed for COLWISE, with the output row it belongs to and
-// its block index in that row; valid is false for lanes past the tensor.
-template <bool kColwise>
-__device__ __forceinline__ bool load_block(const uint16_t* __restrict__ xt, const VarShape& sh, int64_t gidx,
-                                           uint16_t (*tb)[kTRow], float (&v)[16], int64_t& orow, int64_t& oblk) {
-  const int lane = threadIdx.x & 63, r = lane & 15, t4 = lane >> 4;
-  const int64_t gr = gidx / sh.grp_c, gc = gidx % sh.grp_c;
-  const int64_t row = gr * kGroupRows + r, col0 = gc * kGroupCols + 16 * t4;
-  const bool in = row < sh.rows && col0 < sh.cols;
-  u32x4 a = {0u, 0u, 0u, 0u}, b = {0u, 0u, 0u, 0u};
-  if (in) {
-    const u32x4* p = (const u32x4*)(xt + row * sh.cols + col0);
-    a = p[0];
-    b = p[1];
-  }
-  if (!kColwise) {
-    const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      v[2 * i] = bf16_lo(w[i]);
-      v[2 * i + 1] = bf16_hi(w[i]);
-    }
-    orow = row;
-    oblk = col0 / 16;
-    return in;
-  }
-  // transpose through this wave's LDS buffer: tb[r][16 t4 + j] = x[row][col0 + j]
-  *(u32x4*)&tb[r][16 * t4] = a;
-  *(u32x4*)&tb[r][16 * t4 + 8] = b;
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  const int c = 16 * t4 + r;                    // the group column this lane now holds
-#pragma unroll
-  for (int j = 0; j < 16; ++j) v[j] = __uint_as_float((uint32_t)tb[j][c] << 16);
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();              // reads done before the next group's writes
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  orow = gc * kGroupCols + c;
-  oblk = gr;
-  return orow < sh.cols;
-}
-
-// v <- H16 (s .* v) / 4, fast Walsh-Hadamard stages h = 1, 2, 4, 8 (fp32).
-__device__ __forceinline__ void rht16(float (&v)[16], uint32_t signs) {
-#pragma unroll
-  for (int j = 0; j < 16; ++j)
-    if ((signs >> j) & 1u) v[j] = -v[j];
-#pragma unroll
-  for (int h = 1; h < 16; h <<= 1)
-#pragma unroll
-    for (int i = 0; i < 16; ++i)
-      if ((i & h) == 0) {
-        const float a = v[i], b = v[i + h];
-        v[i] = a + b;
-        v[i + h] = a - b;
-      }
-#pragma unroll
-  for (int j = 0; j < 16; ++j) v[j] = v[j] * 0.25f;
-}
-
-__device__ __forceinline__ uint32_t absmax_bits(const float (&v)[16]) {
-  uint32_t m = 0u;
-#pragma unroll
-  for (int j = 0; j < 16; ++j) {
-    const uint32_t b = __float_as_uint(v[j]) & 0x7fffffffu;   // order-preserving for |v|
-    m = m > b ? m : b;
-  }
-  return m;
-}
 
 // Philox4x32-10 (Salmon et al., SC 2011).
 __device__ __forceinline__ void philox(uint32_t c0, uint32_t c1, uint32_t k0, uint32_t k1, uint32_t (&o)[4]) {
@@ -139,6 +71,14 @@ __device__ __forceinline__ void philox(uint32_t c0, uint32_t c1, uint32_t k0, ui
   o[3] = c3;
 }
 
+// The 8 16-bit draws of output elements 8n'..8n'+7, n' = n - offset.
+__device__ __forceinline__ void draws8(uint64_t n, uint32_t key0, uint32_t key1, uint32_t (&u)[8]) {
+  uint32_t w[4];
+  philox((uint32_t)n, (uint32_t)(n >> 32), key0, key1, w);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) u[j] = (w[j >> 1] >> (16 * (j & 1))) & 0xffffu;
+}
+
 // Stochastic E2M1 magnitude code of y >= 0 with the 16-bit draw u.
 __device__ __forceinline__ uint32_t e2m1_sr(float y, uint32_t u) {
   if (y >= 6.0f) return 7u;
@@ -151,26 +91,127 @@ __device__ __forceinline__ uint32_t e2m1_sr(float y, uint32_t u) {
   return k + ((float)u < p * 65536.0f ? 1u : 0u);
 }
 
+// fp32 value of element j (0..7) of a row chunk of 8 bf16.
+__device__ __forceinline__ float chunk_val(const u32x4& c, int j) {
+  const uint32_t w = j < 2 ? c.x : j < 4 ? c.y : j < 6 ? c.z : c.w;
+  return (j & 1) ? bf16_hi(w) : bf16_lo(w);
+}
+
+__device__ __forceinline__ float dpp_swap_pair(float v) {     // lane ^ 1
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false));
+}
+__device__ __forceinline__ uint32_t pair_max_u32(uint32_t m) {
+  const uint32_t o = (uint32_t)__builtin_amdgcn_mov_dpp((int)m, 0xB1, 0xF, 0xF, false);
+  return m > o ? m : o;
+}
+__device__ __forceinline__ uint32_t fabs_bits(float v) { return __float_as_uint(v) & 0x7fffffffu; }
+
+// v <- H16 (s .* v) / 4 for a block held in one lane (fp32, stages 1, 2, 4, 8).
+__device__ __forceinline__ void rht16(float (&v)[16], uint32_t signs) {
+#pragma unroll
+  for (int j = 0; j < 16; ++j)
+    if ((signs >> j) & 1u) v[j] = -v[j];
+#pragma unroll
+  for (int h = 1; h < 16; h <<= 1)
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      if ((i & h) == 0) {
+        const float a = v[i], b = v[i + h];
+        v[i] = a + b;
+        v[i + h] = a - b;
+      }
+#pragma unroll
+  for (int j = 0; j < 16; ++j) v[j] = v[j] * 0.25f;
+}
+
+// The same for a block split over a lane pair: this lane holds elements
+// 8 (lane & 1) .. +7; stages 1, 2, 4 in registers, stage 8 across the pair.
+__device__ __forceinline__ void rht16_pair(float (&v)[8], uint32_t signs, bool odd) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+    if ((signs >> (j + (odd ? 8 : 0))) & 1u) v[j] = -v[j];
+#pragma unroll
+  for (int h = 1; h < 8; h <<= 1)
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      if ((i & h) == 0) {
+        const float a = v[i], b = v[i + h];
+        v[i] = a + b;
+        v[i + h] = a - b;
+      }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const float o = dpp_swap_pair(v[j]);          // even lane: a = own, b = o; odd lane: a = o, b = own
+    v[j] = (odd ? o - v[j] : v[j] + o) * 0.25f;
+  }
+}
+
+// Loads strip (sr_i, band) of tensor t: raw[r] = row r0 + r, columns
+// 512 band + 8 lane .. +7 (zeros past the tensor).
+__device__ __forceinline__ void load_strip(const uint16_t* __restrict__ xt, const VarShape& sh, int64_t r0,
+                                           int64_t col, u32x4 (&raw)[kStripRows]) {
+  const bool cin = col < sh.cols;
+#pragma unroll
+  for (int r = 0; r < kStripRows; ++r) {
+    raw[r] = u32x4{0u, 0u, 0u, 0u};
+    if (cin && r0 + r < sh.rows) raw[r] = __builtin_nontemporal_load((const u32x4*)(xt + (r0 + r) * sh.cols + col));
+  }
+}
+
+// Work item it -> band (512-column band) and its strips [s0, s1).
+__device__ __forceinline__ void var_item(const VarShape& sh, int64_t it, int64_t& band, int64_t& s0, int64_t& s1) {
+  band = it / sh.nseg;
+  s0 = (it % sh.nseg) * sh.seg;
+  s1 = s0 + sh.seg < sh.sr ? s0 + sh.seg : sh.sr;
+}
+
 template <bool kColwise, bool kRht>
 __global__ void __launch_bounds__(kVarThreads) var_amax_kernel(const uint16_t* __restrict__ x, VarShape sh,
                                                                uint32_t signs, uint32_t* __restrict__ partial) {
-  __shared__ __attribute__((aligned(16))) uint16_t tbuf[kVarThreads / 64][kGroupRows][kTRow];
   __shared__ uint32_t red[kVarThreads / 64];
-  const int t = blockIdx.y, wave = wave_id();
+  const int t = blockIdx.y, wave = wave_id(), lane = threadIdx.x & 63;
   const uint16_t* xt = x + (int64_t)t * sh.n;
-  const int64_t ngroups = sh.grp_r * sh.grp_c;
   uint32_t m = 0u;
-  for (int64_t gidx = (int64_t)blockIdx.x * (kVarThreads / 64) + wave; gidx < ngroups;
-       gidx += (int64_t)gridDim.x * (kVarThreads / 64)) {
-    float v[16];
-    int64_t orow, oblk;
-    const bool in = load_block<kColwise>(xt, sh, gidx, tbuf[wave], v, orow, oblk);
-    if (kRht) rht16(v, signs);
-    const uint32_t b = absmax_bits(v);
-    if (in) m = m > b ? m : b;                   // invalid lanes hold zeros anyway
+  for (int64_t it = (int64_t)blockIdx.x * (kVarThreads / 64) + wave; it < sh.nitems;
+       it += (int64_t)gridDim.x * (kVarThreads / 64)) {
+    int64_t band, s0, s1;
+    var_item(sh, it, band, s0, s1);
+    const int64_t col = band * kStripCols + 8 * lane;
+    for (int64_t si = s0; si < s1; ++si) {
+      u32x4 raw[kStripRows];
+      load_strip(xt, sh, si * kStripRows, col, raw);
+      if (!kRht) {                                     // the amax of x itself
+        uint32_t pk = 0u;
+#pragma unroll
+        for (int r = 0; r < kStripRows; ++r)
+          pk = pk_absmax(pk_absmax(pk_absmax(pk_absmax(pk, raw[r].x), raw[r].y), raw[r].z), raw[r].w);
+        const uint32_t b = halves_max(pk) << 16;       // bf16 magnitude -> fp32 bits
+        m = m > b ? m : b;
+      } else if (kColwise) {                           // blocks down the lane's 8 columns
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          float v[16];
+#pragma unroll
+          for (int r = 0; r < 16; ++r) v[r] = chunk_val(raw[r], j);
+          rht16(v, signs);
+#pragma unroll
+          for (int r = 0; r < 16; ++r) m = m > fabs_bits(v[r]) ? m : fabs_bits(v[r]);
+        }
+      } else {                                         // blocks across the lane pair of each row
+#pragma unroll
+        for (int r = 0; r < kStripRows; ++r) {
+          float v[8];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) v[j] = chunk_val(raw[r], j);
+          rht16_pair(v, signs, lane & 1);
+#pragma unroll
+          for (int j = 0; j < 8; ++j) m = m > fabs_bits(v[j]) ? m : fabs_bits(v[j]);
+        }
+      }
+    }
   }
   m = wave_max_u32(m);
-  if ((threadIdx.x & 63) == 0) red[wave] = m;
+  if (lane == 0) red[wave] = m;
   __syncthreads();
   if (threadIdx.x == 0) {
     uint32_t r = red[0];
@@ -180,16 +221,41 @@ __global__ void __launch_bounds__(kVarThreads) var_amax_kernel(const uint16_t* _
   }
 }
 
+// Codes of n values (n = 8 or 16) with reciprocal rd, RNE or stochastic
+// with draws u; packed 2 per byte (element 2i in the low nibble).
+template <int kN, bool kSr>
+__device__ __forceinline__ void encode_vals(const float (&v)[kN], double rd, const uint32_t (&u)[kN],
+                                            uint32_t (&out)[kN / 8]) {
+#pragma unroll
+  for (int w = 0; w < kN / 8; ++w) out[w] = 0u;
+  if (kSr) {
+#pragma unroll
+    for (int j = 0; j < kN; ++j) {
+      const float y = rn32((double)fabsf(v[j]) * rd);
+      const uint32_t c = (__float_as_uint(v[j]) >> 31 << 3) | e2m1_sr(y, u[j]);
+      out[j / 8] |= c << (4 * (j % 8));
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < kN; j += 8) {
+      uint32_t c = fp4_pair<0>(0u, rn32((double)v[j] * rd), rn32((double)v[j + 1] * rd));
+      c = fp4_pair<1>(c, rn32((double)v[j + 2] * rd), rn32((double)v[j + 3] * rd));
+      c = fp4_pair<2>(c, rn32((double)v[j + 4] * rd), rn32((double)v[j + 5] * rd));
+      out[j / 8] = fp4_pair<3>(c, rn32((double)v[j + 6] * rd), rn32((double)v[j + 7] * rd));
+    }
+  }
+}
+
 template <bool kColwise, bool k2D, bool kRht, bool kSr>
 __global__ void __launch_bounds__(kVarThreads) var_encode_kernel(const uint16_t* __restrict__ x, VarShape sh,
                                                                  uint32_t signs, uint64_t seed, uint64_t offset,
                                                                  const uint32_t* __restrict__ partial, int npartial,
                                                                  uint8_t* __restrict__ q, uint8_t* __restrict__ sf,
                                                                  float* __restrict__ gout) {
-  __shared__ __attribute__((aligned(16))) uint16_t tbuf[kVarThreads / 64][kGroupRows][kTRow];
   __shared__ double table[128];
   __shared__ uint32_t red[kVarThreads / 64];
   const int t = blockIdx.y, wave = wave_id(), lane = threadIdx.x & 63;
+  const bool odd = lane & 1;
   // g = RN32(amax / 2688) from the amax pass's partials (fp32 bits)
   uint32_t am = 0u;
   for (int i = threadIdx.x; i < npartial; i += kVarThreads) {
@@ -209,53 +275,90 @@ __global__ void __launch_bounds__(kVarThreads) var_encode_kernel(const uint16_t*
   __syncthreads();
 
   const uint16_t* xt = x + (int64_t)t * sh.n;
-  const int64_t ngroups = sh.grp_r * sh.grp_c;
-  const uint32_t k0 = (uint32_t)seed, k1 = (uint32_t)(seed >> 32);
-  for (int64_t gidx = (int64_t)blockIdx.x * (kVarThreads / 64) + wave; gidx < ngroups;
-       gidx += (int64_t)gridDim.x * (kVarThreads / 64)) {
-    float v[16];
-    int64_t orow, oblk;
-    const bool in = load_block<kColwise>(xt, sh, gidx, tbuf[wave], v, orow, oblk);
-    if (kRht) rht16(v, signs);
-    uint32_t bam = absmax_bits(v);
-    if (k2D) {                                   // the tile's 16 lanes: same lane / 16
+  const uint32_t key0 = (uint32_t)seed, key1 = (uint32_t)(seed >> 32);
+  for (int64_t it = (int64_t)blockIdx.x * (kVarThreads / 64) + wave; it < sh.nitems;
+       it += (int64_t)gridDim.x * (kVarThreads / 64)) {
+    int64_t band, s0, s1;
+    var_item(sh, it, band, s0, s1);
+    const int64_t col = band * kStripCols + 8 * lane;
+    const bool cin = col < sh.cols;
+    for (int64_t si = s0; si < s1; ++si) {
+      const int64_t r0 = si * kStripRows;
+      u32x4 raw[kStripRows];
+      load_strip(xt, sh, r0, col, raw);
+      uint32_t tile = 0u;                              // 2D: the tile amax (fp32 bits), pair-wide
+      if (k2D) {
+        uint32_t pk = 0u;
 #pragma unroll
-      for (int off = 1; off < 16; off <<= 1) {
-        const uint32_t o = (uint32_t)__shfl_xor((int)bam, off, 64);
-        bam = bam > o ? bam : o;
+        for (int r = 0; r < kStripRows; ++r)
+          pk = pk_absmax(pk_absmax(pk_absmax(pk_absmax(pk, raw[r].x), raw[r].y), raw[r].z), raw[r].w);
+        tile = pair_max_u32(halves_max(pk) << 16);
       }
-    }
-    const uint32_t sbyte = e4m3_rne_sat(rn32((double)__uint_as_float(bam) * r6));
-    const double rd = table[sbyte];
-    uint32_t code[16];
-    if (kSr) {
-      // output element index of this block's first value; 16 values use two counters
-      const int64_t i0 = ((int64_t)t * sh.R + orow) * sh.C + 16 * oblk;
-      const uint64_t n = (uint64_t)i0 / 8 + offset;
-      uint32_t w0[4], w1[4];
-      philox((uint32_t)n, (uint32_t)(n >> 32), k0, k1, w0);
-      philox((uint32_t)(n + 1), (uint32_t)((n + 1) >> 32), k0, k1, w1);
+      if (kColwise) {
+        // column j of the lane is output row col + j, its block r0 / 16
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const uint32_t word = j < 8 ? w0[(j & 7) >> 1] : w1[(j & 7) >> 1];
-        const uint32_t u = (word >> (16 * (j & 1))) & 0xffffu;
-        const float y = rn32((double)fabsf(v[j]) * rd);
-        code[j] = (__float_as_uint(v[j]) >> 31 << 3) | e2m1_sr(y, u);
+        for (int j = 0; j < 8; ++j) {
+          float v[16];
+#pragma unroll
+          for (int r = 0; r < 16; ++r) v[r] = chunk_val(raw[r], j);
+          if (kRht) rht16(v, signs);
+          uint32_t bam = 0u;
+          if (k2D) {
+            bam = tile;
+          } else {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) bam = bam > fabs_bits(v[r]) ? bam : fabs_bits(v[r]);
+          }
+          const uint32_t sbyte = e4m3_rne_sat(rn32((double)__uint_as_float(bam) * r6));
+          const int64_t orow = (int64_t)t * sh.R + col + j;
+          uint32_t u[16];
+          if (kSr) {
+            const uint64_t n = (uint64_t)(orow * sh.C + r0) / 8 + offset;
+            uint32_t u0[8], u1[8];
+            draws8(n, key0, key1, u0);
+            draws8(n + 1, key0, key1, u1);
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+              u[k] = u0[k];
+              u[k + 8] = u1[k];
+            }
+          }
+          uint32_t codes[2];
+          encode_vals<16, kSr>(v, table[sbyte], u, codes);
+          if (cin) {
+            *(u32x2*)(q + (orow * sh.C + r0) / 2) = u32x2{codes[0], codes[1]};
+            sf[orow * (sh.C / 16) + r0 / 16] = (uint8_t)sbyte;
+          }
+        }
+      } else {
+        // row r: this lane's half of block (col / 16), the partner holds the other half
+#pragma unroll
+        for (int r = 0; r < kStripRows; ++r) {
+          float v[8];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) v[j] = chunk_val(raw[r], j);
+          if (kRht) rht16_pair(v, signs, odd);
+          uint32_t bam;
+          if (k2D) {
+            bam = tile;
+          } else {
+            bam = 0u;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) bam = bam > fabs_bits(v[j]) ? bam : fabs_bits(v[j]);
+            bam = pair_max_u32(bam);
+          }
+          const uint32_t sbyte = e4m3_rne_sat(rn32((double)__uint_as_float(bam) * r6));
+          const int64_t orow = (int64_t)t * sh.R + r0 + r;
+          uint32_t u[8];
+          if (kSr) draws8((uint64_t)(orow * sh.C + col) / 8 + offset, key0, key1, u);
+          uint32_t codes[1];
+          encode_vals<8, kSr>(v, table[sbyte], u, codes);
+          if (cin && r0 + r < sh.rows) {
+            *(uint32_t*)(q + (orow * sh.C + col) / 2) = codes[0];
+            if (!odd) sf[orow * (sh.C / 16) + col / 16] = (uint8_t)sbyte;
+          }
+        }
       }
-    } else {
-#pragma unroll
-      for (int j = 0; j < 16; j += 2) {
-        const uint32_t pr = fp4_pair<0>(0u, rn32((double)v[j] * rd), rn32((double)v[j + 1] * rd));
-        code[j] = pr & 15u;
-        code[j + 1] = (pr >> 4) & 15u;
-      }
-    }
-    if (in) {
-      u32x2 packed = {0u, 0u};
-#pragma unroll
-      for (int j = 0; j < 8; ++j) packed[j / 4] |= (code[2 * j] | (code[2 * j + 1] << 4)) << (8 * (j % 4));
-      *(u32x2*)(q + (((int64_t)t * sh.R + orow) * sh.C + 16 * oblk) / 2) = packed;
-      sf[((int64_t)t * sh.R + orow) * (sh.C / 16) + oblk] = (uint8_t)sbyte;
     }
   }
 }
@@ -314,12 +417,16 @@ nvfp4_status nvfp4_quantize_ex(const uint16_t* x, int64_t batch, int64_t rows, i
   sh.rows = rows;
   sh.cols = cols;
   sh.n = n;
-  sh.grp_r = (rows + kGroupRows - 1) / kGroupRows;
-  sh.grp_c = (cols + kGroupCols - 1) / kGroupCols;
   sh.R = colwise ? cols : rows;
   sh.C = colwise ? rows : cols;
-  const int64_t ngroups = sh.grp_r * sh.grp_c;
-  const dim3 grid((unsigned)var_wgs(batch, ngroups), (unsigned)batch);
+  sh.sr = (rows + kStripRows - 1) / kStripRows;
+  sh.sc = (cols + kStripCols - 1) / kStripCols;
+  // strips per work item: enough items for about 16 waves per CU, at most 16 strips
+  const int64_t strips = sh.sr * sh.sc * batch;
+  sh.seg = std::max<int64_t>(1, std::min<int64_t>(16, strips / ((int64_t)nvfp4host::num_cus() * 16)));
+  sh.nseg = (sh.sr + sh.seg - 1) / sh.seg;
+  sh.nitems = sh.sc * sh.nseg;
+  const dim3 grid((unsigned)var_wgs(batch, sh.nitems), (unsigned)batch);
   hipStream_t s = (hipStream_t)stream;
   uint32_t* partial = (uint32_t*)workspace;
   // pass 1: the amax of the quantized values (the orientation matters only under RHT)
