@@ -175,9 +175,12 @@ nvfp4_status nvfp4_kv_decode_qk(const nvfp4_kv_cache* cache, const uint16_t* q, 
  * q: [layers][q_heads][head_dim] bf16; out: [layers][q_heads][head_dim] float.
  * workspace: at least nvfp4_kv_attention_workspace_bytes(cache, q_heads, n)
  *   bytes of device scratch (per-split partial results; no zero-fill needed).
+ * head_dim 64, 128 or 256 with up to 16 query heads per KV head runs both
+ * contractions on MFMA (K decoded exactly to bf16, V to f16, P split into
+ * f16 hi + lo parts); head_dim 16 or 32 with 1, 2, 4 or 8 query heads per
+ * KV head runs in VALU.
  * Errors: EINVAL (n < 1 or n > capacity, q_heads not a multiple of kv_heads,
- *   non-finite scale, n * head_dim / 2 >= 2^30), ENOTSUP (head_dim/16 not a
- *   power of two up to 16, or q_heads/kv_heads not 1, 2, 4 or 8),
+ *   non-finite scale, n * head_dim / 2 >= 2^30), ENOTSUP (any other shape),
  *   EWORKSPACE, EALIGN, EHIP. */
 size_t nvfp4_kv_attention_workspace_bytes(const nvfp4_kv_cache* cache, int32_t q_heads, int64_t n);
 

@@ -235,6 +235,292 @@ __global__ void __launch_bounds__(kAttnThreads) kv_attn_split_kernel(nvfp4_kv_ca
   }
 }
 
+// ------------------------------------------------------------ MFMA split kernel
+// The same split computation with both contractions on the matrix cores
+// (head_dim D in {64, 128, 256}, up to 16 query heads per KV head).  A wave
+// takes 32-token chunks; per chunk:
+//  - QK: two v_mfma_f32_16x16x32_bf16 tiles of 16 tokens x 16 heads, K
+//    decoded exactly to bf16 (E2M1 * s, at most 6 significant bits) as the
+//    A operand, q (bf16) as the B operand.  The K dimension order is free,
+//    so lane quarter qd takes head_dim values [qd D/4, (qd+1) D/4): one
+//    contiguous code load per token.  Lane l ends with the logits of head
+//    l % 16 for tokens 4 (l / 16) + i of each tile.
+//  - online softmax per head across those lanes (fp32, exp of s - max).
+//  - PV: v_mfma_f32_16x16x32_f16 per 16-column tile of the output, A = P
+//    (heads x 32 tokens), B = V (32 tokens x 16 columns).  Token slot s of
+//    lane l is token 16 (s / 4) + 4 (l / 16) + s % 4, so P comes straight
+//    from the lane's own logits; P is split into f16 hi + lo parts (two
+//    MFMAs) so it keeps about 22 bits.  V is decoded exactly to f16 (E2M1 *
+//    s), written token-major to LDS and read back per column.
+// The V tensor scale is applied once to the accumulated output.
+constexpr int kMChunk = 32;                              // tokens per wave step
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 h16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 h16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4v __attribute__((ext_vector_type(4)));
+
+template <int D>
+struct AttnMfmaSmem {
+  union {
+    _Float16 v[kAttnWaves][kMChunk][D + 8];              // decoded V chunk of each wave (16-byte row padding)
+    float st[kAttnWaves][16][2 + D];                     // per-wave softmax states for the final merge
+  };
+};
+
+// Raw bytes one lane loads per chunk.
+template <int D>
+struct AttnRaw {
+  uint32_t kc[2][D / 32];                                // K codes of the lane's quarter, tiles 0 and 1
+  uint32_t ks[2][D / 64];                                // K scale bytes of the token (D / 16 bytes)
+  uint32_t vc[D / 16];                                   // V codes of the lane's half token
+  uint32_t vs[D / 128 > 0 ? D / 128 : 1];                // V scale bytes of the half token (D / 32 bytes)
+};
+
+template <int W>
+__device__ __forceinline__ void load_words(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t* dst) {
+  // W words (W = 1, 2, 4, 8) from byte offset off
+  if (W == 1) {
+    dst[0] = __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0);
+  } else if (W == 2) {
+    const u32x2 v = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0));
+    dst[0] = v.x;
+    dst[1] = v.y;
+  } else {
+#pragma unroll
+    for (int i = 0; i < W; i += 4) {
+      const u32x4 v = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)(off + 4 * i), 0, 0));
+      dst[i] = v.x;
+      dst[i + 1] = v.y;
+      dst[i + 2] = v.z;
+      dst[i + 3] = v.w;
+    }
+  }
+}
+
+// Byte offsets past every extent (extents stay below 2^30) read zeros.
+constexpr uint32_t kAttnOutside = 0x80000000u;
+
+template <int D>
+__device__ __forceinline__ void attn_load(const __amdgpu_buffer_rsrc_t (&r)[4], int64_t c0, int64_t cnt, int lane,
+                                          AttnRaw<D>& raw) {
+  const int qd = lane >> 4;
+#pragma unroll
+  for (int T = 0; T < 2; ++T) {
+    const int64_t u = c0 + 16 * T + (lane & 15);
+    const bool in = u < cnt;
+    load_words<D / 32>(r[0], in ? (uint32_t)u * (D / 2) + qd * (D / 8) : kAttnOutside, raw.kc[T]);
+    if (D / 64 == 1)
+      raw.ks[T][0] = __builtin_amdgcn_raw_buffer_load_b32(r[1], (int)(in ? (uint32_t)u * (D / 16) : kAttnOutside), 0, 0);
+    else
+      load_words<D / 64>(r[1], in ? (uint32_t)u * (D / 16) : kAttnOutside, raw.ks[T]);
+  }
+  const int64_t u = c0 + (lane >> 1);
+  const bool in = u < cnt;
+  load_words<D / 16>(r[2], in ? (uint32_t)u * (D / 2) + (lane & 1) * (D / 4) : kAttnOutside, raw.vc);
+  if (D == 64)
+    raw.vs[0] = __builtin_amdgcn_raw_buffer_load_b16(r[3], (int)(in ? (uint32_t)u * (D / 16) + (lane & 1) * 2 : kAttnOutside),
+                                                     0, 0);
+  else
+    load_words<(D / 128 > 0 ? D / 128 : 1)>(r[3], in ? (uint32_t)u * (D / 16) + (lane & 1) * (D / 32) : kAttnOutside,
+                                            raw.vs);
+}
+
+// E4M3 byte b of a little-endian array of W words, decoded exactly (the
+// word is picked with selects, so the array stays in registers).
+template <int W>
+__device__ __forceinline__ float e4m3_byte(const uint32_t (&words)[W], int b) {
+  uint32_t w = words[0];
+#pragma unroll
+  for (int i = 1; i < W; ++i) w = (b >> 2) == i ? words[i] : w;
+  return __builtin_amdgcn_cvt_f32_fp8((int)(w >> (8 * (b & 3))), 0);
+}
+
+// 8 E2M1 codes times scale s, exactly, as bf16.
+__device__ __forceinline__ bf16x8 dec8_bf16(uint32_t w, float s) {
+  bf16x8 o;
+  f32x2 f;
+  f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0); o[0] = (__bf16)(f.x * s); o[1] = (__bf16)(f.y * s);
+  f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1); o[2] = (__bf16)(f.x * s); o[3] = (__bf16)(f.y * s);
+  f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2); o[4] = (__bf16)(f.x * s); o[5] = (__bf16)(f.y * s);
+  f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3); o[6] = (__bf16)(f.x * s); o[7] = (__bf16)(f.y * s);
+  return o;
+}
+
+// 8 E2M1 codes times scale s, exactly, as f16: the conversion applies s's
+// power of two, one packed multiply its mantissa factor (1 + m/8).
+__device__ __forceinline__ h16x8 dec8_f16(uint32_t w, float s) {
+  const float mfs = __uint_as_float((__float_as_uint(s) & 0x007fffffu) | 0x3f800000u);
+  const _Float16 mh = (_Float16)mfs;
+  const h16x2 mf = {mh, mh};
+  h16x8 o;
+  h16x2 p;
+  p = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, s, 0) * mf; o[0] = p.x; o[1] = p.y;
+  p = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, s, 1) * mf; o[2] = p.x; o[3] = p.y;
+  p = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, s, 2) * mf; o[4] = p.x; o[5] = p.y;
+  p = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, s, 3) * mf; o[6] = p.x; o[7] = p.y;
+  return o;
+}
+
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+template <int D>
+__global__ void __launch_bounds__(kAttnThreads) kv_attn_mfma_kernel(nvfp4_kv_cache c, const uint32_t* __restrict__ q,
+                                                                    int q_heads, int64_t n, int64_t per_split,
+                                                                    float scale, float* __restrict__ part) {
+  constexpr int KK = D / 32;                             // MFMA k steps of QK (8 values per lane each)
+  constexpr int DT = D / 16;                             // output column tiles of PV
+  const int split = blockIdx.x, h = blockIdx.y, l = blockIdx.z;
+  const int H = c.kv_heads, GRP = q_heads / H;
+  const int lane = threadIdx.x & 63, wave = wave_id();
+  const int qd = lane >> 4, hl = lane & 15;              // lane quarter; head (QK B / P A row) or column
+  __shared__ __attribute__((aligned(16))) AttnMfmaSmem<D> sm;
+  // q as the QK B operand: head hl, values [qd D/4 + 8 kk, +8) for step kk
+  bf16x8 qb[KK];
+#pragma unroll
+  for (int kk = 0; kk < KK; ++kk) {
+    u32x4 w = {0u, 0u, 0u, 0u};
+    if (hl < GRP) w = *(const u32x4*)(q + ((int64_t)l * q_heads + h * GRP + hl) * (D / 2) + qd * (D / 8) + 4 * kk);
+    qb[kk] = __builtin_bit_cast(bf16x8, w);
+  }
+  const float ks = c.k_g[l * H + h] * scale;
+  const float gv = c.v_g[l * H + h];
+  const int64_t row0 = ((int64_t)l * H + h) * c.capacity;
+  const int64_t t0 = (int64_t)split * per_split;
+  const int64_t t1 = std::min<int64_t>(n, t0 + per_split);
+  const int64_t cnt = t1 > t0 ? t1 - t0 : 0;
+  const __amdgpu_buffer_rsrc_t rs[4] = {
+      __builtin_amdgcn_make_buffer_rsrc((void*)(c.k + (row0 + t0) * (D / 2)), 0, (int)(cnt * (D / 2)), kBufferWord3),
+      __builtin_amdgcn_make_buffer_rsrc((void*)(c.k_sf + (row0 + t0) * (D / 16)), 0, (int)(cnt * (D / 16)), kBufferWord3),
+      __builtin_amdgcn_make_buffer_rsrc((void*)(c.v + (row0 + t0) * (D / 2)), 0, (int)(cnt * (D / 2)), kBufferWord3),
+      __builtin_amdgcn_make_buffer_rsrc((void*)(c.v_sf + (row0 + t0) * (D / 16)), 0, (int)(cnt * (D / 16)), kBufferWord3)};
+
+  float m = -INFINITY, lsum = 0.0f;                      // head hl: running max, this lane's partial sum
+  f32x4v o[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) o[dt] = f32x4v{0.0f, 0.0f, 0.0f, 0.0f};
+  _Float16(*vs)[D + 8] = sm.v[wave];
+  AttnRaw<D> cur;
+  int64_t c0 = (int64_t)wave * kMChunk;
+  attn_load<D>(rs, c0, cnt, lane, cur);
+  for (; c0 < cnt; c0 += kAttnWaves * kMChunk) {
+    AttnRaw<D> nxt;
+    attn_load<D>(rs, c0 + kAttnWaves * kMChunk, cnt, lane, nxt);
+    // ---- QK: logits of head hl, tokens 16 T + 4 qd + i
+    f32x4v sacc[2];
+#pragma unroll
+    for (int T = 0; T < 2; ++T) {
+      sacc[T] = f32x4v{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) {
+        const float sk = e4m3_byte(cur.ks[T], (qd * (D / 4) + 8 * kk) / 16);
+        sacc[T] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(dec8_bf16(cur.kc[T][kk], sk), qb[kk], sacc[T], 0, 0, 0);
+      }
+    }
+    // ---- V chunk into LDS: lane (token lane / 2, half lane % 2)
+    {
+      const int tk = lane >> 1, hf = lane & 1;
+#pragma unroll
+      for (int w = 0; w < D / 16; ++w) {
+        const float sv = e4m3_byte(cur.vs, w / 2);
+        *(h16x8*)&vs[tk][hf * (D / 2) + 8 * w] = dec8_f16(cur.vc[w], sv);
+      }
+    }
+    // ---- online softmax for head hl over this chunk
+    float sv8[8];
+    float cmax = -INFINITY;
+#pragma unroll
+    for (int s8 = 0; s8 < 8; ++s8) {
+      const int64_t u = c0 + 16 * (s8 >> 2) + 4 * qd + (s8 & 3);
+      sv8[s8] = u < cnt ? sacc[s8 >> 2][s8 & 3] * ks : -INFINITY;
+      cmax = fmaxf(cmax, sv8[s8]);
+    }
+    cmax = fmaxf(cmax, __shfl_xor(cmax, 16, 64));
+    cmax = fmaxf(cmax, __shfl_xor(cmax, 32, 64));
+    const float mn = fmaxf(m, cmax);
+    const float alpha = mn == -INFINITY ? 1.0f : __expf(m - mn);
+    m = mn;
+    float p8[8];
+    float psum = 0.0f;
+#pragma unroll
+    for (int s8 = 0; s8 < 8; ++s8) {
+      p8[s8] = sv8[s8] == -INFINITY ? 0.0f : __expf(sv8[s8] - mn);
+      psum += p8[s8];
+    }
+    lsum = lsum * alpha + psum;
+    if (__builtin_amdgcn_ballot_w64(hl < GRP && alpha != 1.0f)) {   // rescale the output rows (heads 4 qd + i)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float a = __shfl(alpha, 4 * qd + i, 64);
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) o[dt][i] *= a;
+      }
+    }
+    // ---- P (head hl x token slots 8 qd .. 8 qd + 7) in f16 hi + lo
+    h16x8 ph, pl;
+#pragma unroll
+    for (int s8 = 0; s8 < 8; ++s8) {
+      const float pv = hl < GRP ? p8[s8] : 0.0f;
+      const _Float16 hi = (_Float16)pv;
+      ph[s8] = hi;
+      pl[s8] = (_Float16)(pv - (float)hi);
+    }
+    wave_lds_sync();                                     // V chunk written
+    // ---- PV: column tile dt, B[slot][column hl] = V[token(slot)][16 dt + hl]
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      h16x8 vb;
+#pragma unroll
+      for (int s8 = 0; s8 < 8; ++s8) vb[s8] = vs[16 * (s8 >> 2) + 4 * qd + (s8 & 3)][16 * dt + hl];
+      o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ph, vb, o[dt], 0, 0, 0);
+      o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pl, vb, o[dt], 0, 0, 0);
+    }
+    wave_lds_sync();                                     // reads done before the next chunk's writes
+    cur = nxt;
+  }
+  // ---- this wave's state: head hl's sum over the four quarters
+  lsum += __shfl_xor(lsum, 16, 64);
+  lsum += __shfl_xor(lsum, 32, 64);
+  __syncthreads();                                       // every wave is done with its V buffer (st aliases it)
+  if (lane < GRP) {
+    sm.st[wave][lane][0] = m;
+    sm.st[wave][lane][1] = lsum;
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int hd = 4 * qd + i;                           // output row of o[.][i]
+    if (hd < GRP) {
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) sm.st[wave][hd][2 + 16 * dt + hl] = o[dt][i] * gv;
+    }
+  }
+  __syncthreads();
+  const int splits = gridDim.x;
+  for (int e = threadIdx.x; e < GRP * D; e += kAttnThreads) {
+    const int g = e / D, d = e % D;
+    float mx = sm.st[0][g][0];
+#pragma unroll
+    for (int w = 1; w < kAttnWaves; ++w) mx = fmaxf(mx, sm.st[w][g][0]);
+    float num = 0.0f, den = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kAttnWaves; ++w) {
+      const float a = sm.st[w][g][0] == -INFINITY ? 0.0f : __expf(sm.st[w][g][0] - mx);
+      den = __builtin_fmaf(a, sm.st[w][g][1], den);
+      num = __builtin_fmaf(a, sm.st[w][g][2 + d], num);
+    }
+    float* pp = part + (((int64_t)l * q_heads + h * GRP + g) * splits + split) * attn_partial_floats(D);
+    if (d == 0) {
+      pp[0] = mx;
+      pp[1] = den;
+    }
+    pp[2 + d] = num;
+  }
+}
+
 // grid (q_heads, layers), head_dim threads: merges the splits of one query head.
 __global__ void kv_attn_combine_kernel(const float* __restrict__ part, int splits, int head_dim,
                                        float* __restrict__ out) {
@@ -294,6 +580,21 @@ int attn_blocks_per_cu(int idx) {
   return b;
 }
 
+// The same for the MFMA kernels (head_dim 64, 128, 256).
+int attn_mfma_blocks_per_cu(int head_dim) {
+  static std::atomic<int> cache[3];
+  const int idx = head_dim == 64 ? 0 : head_dim == 128 ? 1 : 2;
+  int b = cache[idx].load(std::memory_order_relaxed);
+  if (b > 0) return b;
+  const void* fn = idx == 0 ? reinterpret_cast<const void*>(kv_attn_mfma_kernel<64>)
+                   : idx == 1 ? reinterpret_cast<const void*>(kv_attn_mfma_kernel<128>)
+                              : reinterpret_cast<const void*>(kv_attn_mfma_kernel<256>);
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, fn, kAttnThreads, 0) != hipSuccess || b <= 0) b = 1;
+  b = std::min(b, kAttnMaxBlocksPerCU);
+  cache[idx].store(b, std::memory_order_relaxed);
+  return b;
+}
+
 // Splits per (layer, KV head): one full round of resident workgroups over
 // the chip (no partly filled second round), at least 64 tokens per split.
 int attn_splits(const nvfp4_kv_cache* c, int64_t n, int blocks_per_cu) {
@@ -329,8 +630,10 @@ nvfp4_status nvfp4_kv_decode_attention(const nvfp4_kv_cache* c, const uint16_t* 
   if (q_heads <= 0 || q_heads % c->kv_heads) return NVFP4_EINVAL;
   if (n <= 0 || n > c->capacity) return NVFP4_EINVAL;             // softmax needs at least one token
   if (!q || !out || !std::isfinite(scale)) return NVFP4_EINVAL;
+  const int grp = q_heads / c->kv_heads;
+  const bool mfma = (c->head_dim == 64 || c->head_dim == 128 || c->head_dim == 256) && grp <= 16;
   const int idx = attn_index(c, q_heads);
-  if (idx < 0) return NVFP4_ENOTSUP;
+  if (!mfma && idx < 0) return NVFP4_ENOTSUP;
   if (n * (c->head_dim / 2) >= (INT64_C(1) << 30)) return NVFP4_EINVAL;   // 32-bit buffer offsets
   if (!nvfp4host::aligned16(q) || !nvfp4host::aligned16(out) || !nvfp4host::aligned16(c->k) ||
       !nvfp4host::aligned16(c->v))
@@ -340,13 +643,20 @@ nvfp4_status nvfp4_kv_decode_attention(const nvfp4_kv_cache* c, const uint16_t* 
   if (!nvfp4host::aligned16(workspace)) return NVFP4_EALIGN;
   nvfp4_status st = nvfp4host::check_device();
   if (st) return st;
-  const int splits = attn_splits(c, n, attn_blocks_per_cu(idx));
+  const int splits = attn_splits(c, n, mfma ? attn_mfma_blocks_per_cu(c->head_dim) : attn_blocks_per_cu(idx));
   const int64_t per_split = (n + splits - 1) / splits;
   hipStream_t s = (hipStream_t)stream;
   const dim3 grid(splits, c->kv_heads, c->layers);
   const uint32_t* qa = (const uint32_t*)q;
   float* part = (float*)workspace;
-  kAttnKernels[idx]<<<grid, kAttnThreads, 0, s>>>(*c, qa, q_heads, n, per_split, scale, part);
+  if (!mfma)
+    kAttnKernels[idx]<<<grid, kAttnThreads, 0, s>>>(*c, qa, q_heads, n, per_split, scale, part);
+  else if (c->head_dim == 64)
+    kv_attn_mfma_kernel<64><<<grid, kAttnThreads, 0, s>>>(*c, qa, q_heads, n, per_split, scale, part);
+  else if (c->head_dim == 128)
+    kv_attn_mfma_kernel<128><<<grid, kAttnThreads, 0, s>>>(*c, qa, q_heads, n, per_split, scale, part);
+  else
+    kv_attn_mfma_kernel<256><<<grid, kAttnThreads, 0, s>>>(*c, qa, q_heads, n, per_split, scale, part);
   NVFP4_LAUNCH_CHECK();
   kv_attn_combine_kernel<<<dim3(q_heads, c->layers), c->head_dim, 0, s>>>(part, splits, c->head_dim, out);
   NVFP4_LAUNCH_CHECK();

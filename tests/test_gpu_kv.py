@@ -80,7 +80,8 @@ def test_append_read_non_pow2_head_dim():
         cache.decode_qk(qv, 10)
 
 
-@pytest.mark.parametrize("D,grp", [(128, 4), (64, 2), (32, 1), (256, 8), (16, 4), (128, 1)])
+@pytest.mark.parametrize("D,grp", [(128, 4), (64, 2), (32, 1), (256, 8), (16, 4), (128, 1), (128, 16), (64, 3),
+                                   (256, 5)])
 def test_decode_attention_small(D, grp):
     """Decode attention (QK, softmax, P.V) against the fp64 oracle for token
     counts that leave ragged splits, including a single token."""
@@ -107,7 +108,12 @@ def test_decode_attention_rejects_unsupported_shapes():
     cache, kg, vg = _cache(1, 2, 48, 10, 1)
     with pytest.raises(nv.NVFP4Error):
         cache.decode_attention(torch.zeros((1, 2, 48), dtype=torch.bfloat16, device="cuda"), 5, 0.1)
+    cache, kg, vg = _cache(1, 2, 32, 10, 1)
+    with pytest.raises(nv.NVFP4Error):                 # head_dim 32 runs 1, 2, 4 or 8 query heads per KV head
+        cache.decode_attention(torch.zeros((1, 6, 32), dtype=torch.bfloat16, device="cuda"), 5, 0.1)
     cache, kg, vg = _cache(1, 2, 64, 10, 1)
+    with pytest.raises(nv.NVFP4Error):                 # more than 16 query heads per KV head
+        cache.decode_attention(torch.zeros((1, 34, 64), dtype=torch.bfloat16, device="cuda"), 5, 0.1)
     with pytest.raises(nv.NVFP4Error):                 # n = 0: a softmax over no tokens
         cache.decode_attention(torch.zeros((1, 2, 64), dtype=torch.bfloat16, device="cuda"), 0, 0.1)
 
