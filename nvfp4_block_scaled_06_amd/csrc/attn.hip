@@ -259,6 +259,9 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 h16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 h16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4v __attribute__((ext_vector_type(4)));
+typedef _Float16 h16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4_t;
 
 template <int D>
 struct AttnMfmaSmem {
@@ -470,12 +473,18 @@ __global__ void __launch_bounds__(kAttnThreads) kv_attn_mfma_kernel(nvfp4_kv_cac
       pl[s8] = (_Float16)(pv - (float)hi);
     }
     wave_lds_sync();                                     // V chunk written
-    // ---- PV: column tile dt, B[slot][column hl] = V[token(slot)][16 dt + hl]
+    // ---- PV: column tile dt, B[slot][column hl] = V[token(slot)][16 dt + hl].
+    // ds_read_b64_tr_b16 hands lane j of a 16-lane group element b of the
+    // 8-byte piece that lane 4 i + j / 4 addressed, as its element i: lane
+    // k of quarter qd addresses V[token 16 r + 4 qd + k / 4][16 dt + 4 (k % 4)]
+    // for slots 4 r .. 4 r + 3 (r = 0, 1).
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
-      h16x8 vb;
-#pragma unroll
-      for (int s8 = 0; s8 < 8; ++s8) vb[s8] = vs[16 * (s8 >> 2) + 4 * qd + (s8 & 3)][16 * dt + hl];
+      const h16x4 b0 = __builtin_bit_cast(h16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_s16x4_t*)&vs[4 * qd + (hl >> 2)][16 * dt + 4 * (hl & 3)]));
+      const h16x4 b1 = __builtin_bit_cast(h16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_s16x4_t*)&vs[16 + 4 * qd + (hl >> 2)][16 * dt + 4 * (hl & 3)]));
+      const h16x8 vb = {b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
       o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ph, vb, o[dt], 0, 0, 0);
       o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pl, vb, o[dt], 0, 0, 0);
     }
