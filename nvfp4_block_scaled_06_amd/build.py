@@ -21,12 +21,18 @@ FLAGS = [
 ]
 
 
+# Per-source additions.  attn.hip: the decode-attention MFMA kernel keeps
+# its accumulators in VGPRs (the online-softmax rescale multiplies them in
+# VALU; accumulators in AGPRs cost a read and a write of each per step).
+EXTRA = {"attn.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def sources():
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
 
 
 def _compile(src, obj):
-    cmd = [HIPCC] + FLAGS + ["-c", src, "-o", obj]
+    cmd = [HIPCC] + FLAGS + EXTRA.get(os.path.basename(src), []) + ["-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     noise = "is not a recognized feature for this target"
     err = "\n".join(l for l in r.stderr.splitlines() if noise not in l)
