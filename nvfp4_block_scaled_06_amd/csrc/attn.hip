@@ -436,12 +436,16 @@ __global__ void __launch_bounds__(kAttnThreads) kv_attn_mfma_kernel(nvfp4_kv_cac
     // ---- online softmax for head hl over this chunk
     float sv8[8];
     float cmax = -INFINITY;
+    const int rem = (int)std::min<int64_t>(cnt - c0, kMChunk);     // tokens of the chunk inside the split
 #pragma unroll
-    for (int s8 = 0; s8 < 8; ++s8) {
-      const int64_t u = c0 + 16 * (s8 >> 2) + 4 * qd + (s8 & 3);
-      sv8[s8] = u < cnt ? sacc[s8 >> 2][s8 & 3] * ks : -INFINITY;
-      cmax = fmaxf(cmax, sv8[s8]);
+    for (int s8 = 0; s8 < 8; ++s8) sv8[s8] = sacc[s8 >> 2][s8 & 3] * ks;
+    if (rem < kMChunk) {                                           // the split's last chunk
+#pragma unroll
+      for (int s8 = 0; s8 < 8; ++s8)
+        if (16 * (s8 >> 2) + 4 * qd + (s8 & 3) >= rem) sv8[s8] = -INFINITY;
     }
+#pragma unroll
+    for (int s8 = 0; s8 < 8; ++s8) cmax = fmaxf(cmax, sv8[s8]);
     cmax = fmaxf(cmax, __shfl_xor(cmax, 16, 64));
     cmax = fmaxf(cmax, __shfl_xor(cmax, 32, 64));
     const float mn = fmaxf(m, cmax);
@@ -449,9 +453,10 @@ __global__ void __launch_bounds__(kAttnThreads) kv_attn_mfma_kernel(nvfp4_kv_cac
     m = mn;
     float p8[8];
     float psum = 0.0f;
+    const float mref = mn == -INFINITY ? 0.0f : mn;               // exp(-inf - mref) = 0 for masked tokens
 #pragma unroll
     for (int s8 = 0; s8 < 8; ++s8) {
-      p8[s8] = sv8[s8] == -INFINITY ? 0.0f : __expf(sv8[s8] - mn);
+      p8[s8] = __expf(sv8[s8] - mref);
       psum += p8[s8];
     }
     lsum = lsum * alpha + psum;
