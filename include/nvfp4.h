@@ -176,9 +176,11 @@ nvfp4_status nvfp4_kv_decode_qk(const nvfp4_kv_cache* cache, const uint16_t* q, 
  * workspace: at least nvfp4_kv_attention_workspace_bytes(cache, q_heads, n)
  *   bytes of device scratch (per-split partial results; no zero-fill needed).
  * head_dim 64, 128 or 256 with up to 16 query heads per KV head runs both
- * contractions on MFMA (K decoded exactly to bf16, V to f16, P split into
- * f16 hi + lo parts); head_dim 16 or 32 with 1, 2, 4 or 8 query heads per
- * KV head runs in VALU.
+ * contractions on MFMA: K and V decoded exactly to f16, q scaled per head by
+ * a power of two (largest element in [2^14, 2^15)) and rounded to f16, which
+ * is exact for every element above 2^-28 of the head's largest; P split into
+ * f16 hi + lo parts.  head_dim 16 or 32 with 1, 2, 4 or 8 query heads per KV
+ * head runs in VALU with bf16 q.
  * Errors: EINVAL (n < 1 or n > capacity, q_heads not a multiple of kv_heads,
  *   non-finite scale, n * head_dim / 2 >= 2^30), ENOTSUP (any other shape),
  *   EWORKSPACE, EALIGN, EHIP. */

@@ -239,9 +239,11 @@ __global__ void __launch_bounds__(kAttnThreads) kv_attn_split_kernel(nvfp4_kv_ca
 // The same split computation with both contractions on the matrix cores
 // (head_dim D in {64, 128, 256}, up to 16 query heads per KV head).  A wave
 // takes 32-token chunks; per chunk:
-//  - QK: two v_mfma_f32_16x16x32_bf16 tiles of 16 tokens x 16 heads, K
-//    decoded exactly to bf16 (E2M1 * s, at most 6 significant bits) as the
-//    A operand, q (bf16) as the B operand.  The K dimension order is free,
+//  - QK: two v_mfma_f32_16x16x32_f16 tiles of 16 tokens x 16 heads, K
+//    decoded exactly to f16 (E2M1 * s: at most 6 significant bits, within
+//    f16's normal range) as the A operand; q as the B operand, scaled per
+//    head by a power of two and rounded to f16 (exact except for elements
+//    below 2^-28 of the head's largest).  The K dimension order is free,
 //    so lane quarter qd takes head_dim values [qd D/4, (qd+1) D/4): one
 //    contiguous code load per token.  Lane l ends with the logits of head
 //    l % 16 for tokens 4 (l / 16) + i of each tile.
@@ -255,7 +257,6 @@ __global__ void __launch_bounds__(kAttnThreads) kv_attn_split_kernel(nvfp4_kv_ca
 // The V tensor scale is applied once to the accumulated output.
 constexpr int kMChunk = 32;                              // tokens per wave step
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 h16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 h16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4v __attribute__((ext_vector_type(4)));
@@ -339,17 +340,6 @@ __device__ __forceinline__ float e4m3_byte(const uint32_t (&words)[W], int b) {
   return __builtin_amdgcn_cvt_f32_fp8((int)(w >> (8 * (b & 3))), 0);
 }
 
-// 8 E2M1 codes times scale s, exactly, as bf16.
-__device__ __forceinline__ bf16x8 dec8_bf16(uint32_t w, float s) {
-  bf16x8 o;
-  f32x2 f;
-  f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0); o[0] = (__bf16)(f.x * s); o[1] = (__bf16)(f.y * s);
-  f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1); o[2] = (__bf16)(f.x * s); o[3] = (__bf16)(f.y * s);
-  f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2); o[4] = (__bf16)(f.x * s); o[5] = (__bf16)(f.y * s);
-  f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3); o[6] = (__bf16)(f.x * s); o[7] = (__bf16)(f.y * s);
-  return o;
-}
-
 // 8 E2M1 codes times scale s, exactly, as f16: the conversion applies s's
 // power of two, one packed multiply its mantissa factor (1 + m/8).
 __device__ __forceinline__ h16x8 dec8_f16(uint32_t w, float s) {
@@ -383,14 +373,33 @@ __global__ void __launch_bounds__(kAttnThreads) kv_attn_mfma_kernel(nvfp4_kv_cac
   const int qd = lane >> 4, hl = lane & 15;              // lane quarter; head (QK B / P A row) or column
   __shared__ __attribute__((aligned(16))) AttnMfmaSmem<D> sm;
   // q as the QK B operand: head hl, values [qd D/4 + 8 kk, +8) for step kk
-  bf16x8 qb[KK];
+  // q as the QK B operand in f16: head hl's values times 2^cq, where cq puts
+  // the head's largest |q| in [2^14, 2^15); exact for every element above
+  // 2^-28 of that largest one.  The logits take 2^-cq back.
+  u32x4 qw[KK];
+  uint32_t qmax = 0u;
 #pragma unroll
   for (int kk = 0; kk < KK; ++kk) {
-    u32x4 w = {0u, 0u, 0u, 0u};
-    if (hl < GRP) w = *(const u32x4*)(q + ((int64_t)l * q_heads + h * GRP + hl) * (D / 2) + qd * (D / 8) + 4 * kk);
-    qb[kk] = __builtin_bit_cast(bf16x8, w);
+    qw[kk] = u32x4{0u, 0u, 0u, 0u};
+    if (hl < GRP) qw[kk] = *(const u32x4*)(q + ((int64_t)l * q_heads + h * GRP + hl) * (D / 2) + qd * (D / 8) + 4 * kk);
+    qmax = halves_max(pk_absmax(pk_absmax(pk_absmax(pk_absmax(qmax, qw[kk].x), qw[kk].y), qw[kk].z), qw[kk].w));
   }
-  const float ks = c.k_g[l * H + h] * scale;
+  qmax = max(qmax, (uint32_t)__shfl_xor((int)qmax, 16, 64));
+  qmax = max(qmax, (uint32_t)__shfl_xor((int)qmax, 32, 64));
+  const int qe = (int)(qmax >> 7);                       // biased exponent of the head's largest |q|
+  const int cq = qe == 0 ? 0 : std::min(std::max(141 - qe, -100), 100);
+  const float qs = __uint_as_float((uint32_t)(cq + 127) << 23);
+  h16x8 qb[KK];
+#pragma unroll
+  for (int kk = 0; kk < KK; ++kk) {
+    const uint32_t w[4] = {qw[kk].x, qw[kk].y, qw[kk].z, qw[kk].w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      qb[kk][2 * i] = (_Float16)(bf16_lo(w[i]) * qs);
+      qb[kk][2 * i + 1] = (_Float16)(bf16_hi(w[i]) * qs);
+    }
+  }
+  const float ks = c.k_g[l * H + h] * scale * __uint_as_float((uint32_t)(127 - cq) << 23);
   const float gv = c.v_g[l * H + h];
   const int64_t row0 = ((int64_t)l * H + h) * c.capacity;
   const int64_t t0 = (int64_t)split * per_split;
@@ -421,7 +430,7 @@ __global__ void __launch_bounds__(kAttnThreads) kv_attn_mfma_kernel(nvfp4_kv_cac
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk) {
         const float sk = e4m3_byte(cur.ks[T], (qd * (D / 4) + 8 * kk) / 16);
-        sacc[T] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(dec8_bf16(cur.kc[T][kk], sk), qb[kk], sacc[T], 0, 0, 0);
+        sacc[T] = __builtin_amdgcn_mfma_f32_16x16x32_f16(dec8_f16(cur.kc[T][kk], sk), qb[kk], sacc[T], 0, 0, 0);
       }
     }
     // ---- V chunk into LDS: lane (token lane / 2, half lane % 2)

@@ -104,6 +104,30 @@ def test_decode_attention_small(D, grp):
         assert err <= QK_TOL, f"n={n}: rel Frobenius {err:.3e}"
 
 
+@pytest.mark.parametrize("k", [-100, -20, 0, 30, 100])
+def test_decode_attention_query_magnitudes(k):
+    """Queries scaled by 2^k (with the softmax scale taking 2^-k back) and a
+    head whose elements span 40 binades: the per-head power-of-two scaling
+    of q keeps the logits exact enough for the 1e-5 bar."""
+    print("case: kv attention q magnitude 2^", k, flush=True)
+    L, H, D, grp, cap = 1, 2, 128, 4, 200
+    cache, kg, vg = _cache(L, H, D, cap, 1000 + k)
+    gen = torch.Generator().manual_seed(77 + k)
+    kk = (torch.randn((L, cap, H, D), generator=gen) * 2).to(torch.bfloat16)
+    vv = torch.randn((L, cap, H, D), generator=gen).to(torch.bfloat16)
+    cache.append(0, kk.cuda(), vv.cuda())
+    qf = torch.randn((L, H * grp, D), generator=gen) * 2.0 ** k
+    qf[0, 1] *= torch.exp2(torch.randint(-40, 1, (D,), generator=gen).float())   # mixed binades in one head
+    qv = qf.to(torch.bfloat16)
+    scale = 2.0 ** -k / np.sqrt(D)
+    out = cache.decode_attention(qv.cuda(), cap, scale)
+    torch.cuda.synchronize()
+    kq, ks, vq, vs = (np_(t) for t in (cache.k, cache.k_sf, cache.v, cache.v_sf))
+    want = oracle.decode_attention_f64(bits(qv), kq, ks, kg, vq, vs, vg, scale)
+    err = rel_frobenius(np_(out), want)
+    assert err <= QK_TOL, f"rel Frobenius {err:.3e}"
+
+
 def test_decode_attention_rejects_unsupported_shapes():
     cache, kg, vg = _cache(1, 2, 48, 10, 1)
     with pytest.raises(nv.NVFP4Error):
