@@ -367,28 +367,33 @@ __device__ __forceinline__ void mx_wait_vm0() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
-// Wave w's share of one K step of one operand: code rows [64 w, 64 w + 64)
-// (8 instructions of 8 rows) and the scale bytes of the same rows (2
-// instructions of 32 rows, 4 bytes per lane).
-__device__ __forceinline__ void mx_dma_step(const MxOperand& o, int wave, int lane, int64_t k0, uint8_t* codes,
-                                            uint32_t (*sc)[2]) {
+// 8 waves (two per SIMD), each a 128 x 64 eighth of the tile (4 x 2 MFMA
+// tiles): a second wave per SIMD keeps the matrix cores busy while the
+// other waits at the step barrier or on LDS.  Wave w loads code rows
+// [32 w, 32 w + 32) of each operand (4 instructions of 8 rows) and their
+// scale bytes (one instruction, 4 bytes per lane).
+constexpr int MThreads8 = 512;
+
+__device__ __forceinline__ void mx_dma_step8(const MxOperand& o, int wave, int lane, int64_t k0, uint8_t* codes,
+                                             uint32_t (*sc)[2]) {
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int r = 64 * wave + 8 * j + (lane >> 3);
+  for (int j = 0; j < 4; ++j) {                  // code rows [32 wave, 32 wave + 32)
+    const int r = 32 * wave + 8 * j + (lane >> 3);
     const int c = (lane & 7) ^ ((r >> 1) & 7);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(o.q, (mx_lds_t*)(codes + (64 * wave + 8 * j) * 128), 16,
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(o.q, (mx_lds_t*)(codes + (32 * wave + 8 * j) * 128), 16,
                                              (uint32_t)r * o.qrow + (uint32_t)(k0 / 2) + 16u * c, 0, 0, 0);
   }
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int r = 64 * wave + 32 * j + (lane >> 1);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(o.s, (mx_lds_t*)&sc[64 * wave + 32 * j][0], 4,
-                                             (uint32_t)r * o.srow + (uint32_t)(k0 / 32) + 4u * (lane & 1), 0, 0, 0);
-  }
+  const int r = 32 * wave + (lane >> 1);         // scale bytes of the same rows
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(o.s, (mx_lds_t*)&sc[32 * wave][0], 4,
+                                           (uint32_t)r * o.srow + (uint32_t)(k0 / 32) + 4u * (lane & 1), 0, 0, 0);
 }
 
-__device__ __forceinline__ void mx_dma_frags(MxFrag& f, const uint8_t* Acur, const uint8_t* Bcur, int kk, int h,
-                                             int sw) {
+struct MxFrag8 {
+  i32x8 a[4], b[2];
+};
+
+__device__ __forceinline__ void mx_dma_frags8(MxFrag8& f, const uint8_t* Acur, const uint8_t* Bcur, int kk, int h,
+                                              int sw) {
   const int pos = ((2 * kk + h) ^ sw) * 16;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -396,89 +401,103 @@ __device__ __forceinline__ void mx_dma_frags(MxFrag& f, const uint8_t* Acur, con
     f.a[i] = i32x8{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
   }
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
+  for (int j = 0; j < 2; ++j) {
     const u32x4 v = *(const u32x4*)(Bcur + j * 32 * 128 + pos);
     f.b[j] = i32x8{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
   }
 }
 
 template <int kk>
-__device__ __forceinline__ void mx_dma_substep(f32x16 (&acc)[4][4], const MxFrag& f, MxFrag& nf, const uint8_t* Acur,
-                                               const uint8_t* Bcur, int h, int sw, const uint32_t (&sa)[4],
-                                               const uint32_t (&sb)[4]) {
+__device__ __forceinline__ void mx_dma_substep8(f32x16 (&acc)[4][2], const MxFrag8& f, MxFrag8& nf,
+                                                const uint8_t* Acur, const uint8_t* Bcur, int h, int sw,
+                                                const uint32_t (&sa)[4], const uint32_t (&sb)[2]) {
   __builtin_amdgcn_sched_barrier(0);
-  if (kk < 3) mx_dma_frags(nf, Acur, Bcur, kk + 1, h, sw);
+  if (kk < 3) mx_dma_frags8(nf, Acur, Bcur, kk + 1, h, sw);
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < 2; ++j)
       acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.a[i], f.b[j], acc[i][j], 4, 4, kk, (int)sa[i], kk,
                                                                   (int)sb[j]);
   if (kk < 3) {
 #pragma unroll
-    for (int m = 0; m < 8; ++m) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);   // MFMA
+    for (int m = 0; m < 6; ++m) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
     }
   }
   __builtin_amdgcn_sched_barrier(0);
 }
 
-__global__ void __launch_bounds__(MThreads) mx_gemm_dma_kernel(const uint8_t* __restrict__ aq,
-                                                               const uint8_t* __restrict__ asf,
-                                                               const uint8_t* __restrict__ bq,
-                                                               const uint8_t* __restrict__ bsf, int64_t M, int64_t N,
-                                                               int64_t K, float* __restrict__ C) {
+__global__ void __launch_bounds__(MThreads8) mx_gemm_dma8_kernel(const uint8_t* __restrict__ aq,
+                                                                 const uint8_t* __restrict__ asf,
+                                                                 const uint8_t* __restrict__ bq,
+                                                                 const uint8_t* __restrict__ bsf, int64_t M,
+                                                                 int64_t N, int64_t K, float* __restrict__ C) {
   __shared__ __attribute__((aligned(16))) MxDmaSmem sm;
-  const int tid = threadIdx.x;
-  const int wave = wave_id(), lane = tid & 63;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wave = wave_id(), lane = threadIdx.x & 63;
+  const int wm = wave >> 2, wn = wave & 3;        // rows wm * 128 .., columns wn * 64 ..
   const int64_t tile = xcd_tile((int64_t)blockIdx.y * gridDim.x + blockIdx.x, (int64_t)gridDim.x * gridDim.y);
   const int64_t m0 = tile / gridDim.x * MTM, n0 = tile % gridDim.x * MTN;
   const MxOperand A = mx_operand(aq, asf, m0, M, K), B = mx_operand(bq, bsf, n0, N, K);
 
-  f32x16 acc[4][4];
+  f32x16 acc[4][2];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
   const int64_t nk = K / MTK;
-  mx_dma_step(A, wave, lane, 0, sm.a[0], sm.as[0]);
-  mx_dma_step(B, wave, lane, 0, sm.b[0], sm.bs[0]);
+  mx_dma_step8(A, wave, lane, 0, sm.a[0], sm.as[0]);
+  mx_dma_step8(B, wave, lane, 0, sm.b[0], sm.bs[0]);
   mx_wait_vm0();
   __syncthreads();
-  const int arow = wm * 128 + (lane & 31), brow = wn * 128 + (lane & 31), h = lane >> 5;
-  const int sw = ((lane & 31) >> 1) & 7;       // the swizzle of every row this lane reads
+  const int arow = wm * 128 + (lane & 31), brow = wn * 64 + (lane & 31), h = lane >> 5;
+  const int sw = ((lane & 31) >> 1) & 7;
   const uint32_t sel = h ? 0x07050301u : 0x06040200u;
   for (int64_t kt = 0; kt < nk; ++kt) {
     const int buf = (int)(kt & 1);
-    if (kt + 1 < nk) {                         // the next step into the other buffer
-      mx_dma_step(A, wave, lane, (kt + 1) * MTK, sm.a[buf ^ 1], sm.as[buf ^ 1]);
-      mx_dma_step(B, wave, lane, (kt + 1) * MTK, sm.b[buf ^ 1], sm.bs[buf ^ 1]);
+    if (kt + 1 < nk) {
+      mx_dma_step8(A, wave, lane, (kt + 1) * MTK, sm.a[buf ^ 1], sm.as[buf ^ 1]);
+      mx_dma_step8(B, wave, lane, (kt + 1) * MTK, sm.b[buf ^ 1], sm.bs[buf ^ 1]);
     }
     const uint8_t* Acur = sm.a[buf] + arow * 128;
     const uint8_t* Bcur = sm.b[buf] + brow * 128;
-    uint32_t sa[4], sb[4];
+    uint32_t sa[4], sb[2];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const uint32_t* ra = sm.as[buf][arow + 32 * i];
-      const uint32_t* rb = sm.bs[buf][brow + 32 * i];
       sa[i] = __builtin_amdgcn_perm(ra[1], ra[0], sel);
-      sb[i] = __builtin_amdgcn_perm(rb[1], rb[0], sel);
     }
-    MxFrag f0, f1;
-    mx_dma_frags(f0, Acur, Bcur, 0, h, sw);
-    mx_dma_substep<0>(acc, f0, f1, Acur, Bcur, h, sw, sa, sb);
-    mx_dma_substep<1>(acc, f1, f0, Acur, Bcur, h, sw, sa, sb);
-    mx_dma_substep<2>(acc, f0, f1, Acur, Bcur, h, sw, sa, sb);
-    mx_dma_substep<3>(acc, f1, f0, Acur, Bcur, h, sw, sa, sb);
-    mx_wait_vm0();                             // step kt+1 is in LDS
-    __syncthreads();                           // ... for every wave; buffer buf is free
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const uint32_t* rb = sm.bs[buf][brow + 32 * j];
+      sb[j] = __builtin_amdgcn_perm(rb[1], rb[0], sel);
+    }
+    MxFrag8 f0, f1;
+    mx_dma_frags8(f0, Acur, Bcur, 0, h, sw);
+    mx_dma_substep8<0>(acc, f0, f1, Acur, Bcur, h, sw, sa, sb);
+    mx_dma_substep8<1>(acc, f1, f0, Acur, Bcur, h, sw, sa, sb);
+    mx_dma_substep8<2>(acc, f0, f1, Acur, Bcur, h, sw, sa, sb);
+    mx_dma_substep8<3>(acc, f1, f0, Acur, Bcur, h, sw, sa, sb);
+    mx_wait_vm0();
+    __syncthreads();
   }
-  mx_epilogue(acc, C, m0, n0, M, N, wm, wn, lane);
+  // epilogue: rows wm * 128 + ..., columns wn * 64 + ...
+  float* Cw = C + (m0 + wm * 128 + 4 * (lane >> 5)) * N + n0 + wn * 64 + (lane & 31);
+  const int64_t rlim = M - (m0 + wm * 128 + 4 * (lane >> 5)), clim = N - (n0 + wn * 64 + (lane & 31));
+  const bool whole = m0 + MTM <= M && n0 + MTN <= N;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int r = i * 32 + 8 * (e >> 2) + (e & 3), cc = j * 32;
+        if (whole || (r < rlim && cc < clim)) Cw[r * N + cc] = acc[i][j][e];
+      }
 }
 
 }  // namespace nvfp4
@@ -544,7 +563,7 @@ nvfp4_status nvfp4_mxfp4_gemm(const uint8_t* a_q, const uint8_t* a_sf, const uin
   const bool aligned = K % MTK == 0 && (reinterpret_cast<uintptr_t>(a_sf) & 7u) == 0 &&
                        (reinterpret_cast<uintptr_t>(b_sf) & 7u) == 0;
   if (aligned)
-    mx_gemm_dma_kernel<<<grid, MThreads, 0, (hipStream_t)stream>>>(a_q, a_sf, b_q, b_sf, M, N, K, c);
+    mx_gemm_dma8_kernel<<<grid, MThreads8, 0, (hipStream_t)stream>>>(a_q, a_sf, b_q, b_sf, M, N, K, c);
   else
     mx_gemm_kernel<false><<<grid, MThreads, 0, (hipStream_t)stream>>>(a_q, a_sf, b_q, b_sf, M, N, K, c);
   NVFP4_LAUNCH_CHECK();
