@@ -434,8 +434,8 @@ def cpu_baseline(synth, torch):
 
 def traffic_kernels(nv, synth, torch):
     """Three launches each of the fused quantize and the dequantize of the
-    headline workload, the two-kernel quantize, the 8192 x 2048 x 7168 GEMM,
-    and a plain 1 GiB device-to-device copy whose byte counts (1 GiB read,
+    headline workload, the two-kernel quantize, the 8192 x 2048 x 7168 NVFP4
+    and MXFP4 GEMMs, and a plain 1 GiB device-to-device copy whose byte counts (1 GiB read,
     1 GiB written) calibrate the HBM byte counters."""
     E, R, C = 64, 2048, 7168
     x = synth.experts(E, R, C, device="cuda")
@@ -460,7 +460,15 @@ def traffic_kernels(nv, synth, torch):
     for _ in range(3):
         nv.gemm(aq, asf, ag, bq, bsf, bg, out=c)
     torch.cuda.synchronize()
-    del aq, asf, bq, bsf, c
+    del aq, asf, bq, bsf
+    a, b = synth.gemm_operands(device="cuda")
+    maq, masf = nv.mxfp4_quantize(a)
+    mbq, mbsf = nv.mxfp4_quantize(b)
+    del a, b
+    for _ in range(3):
+        nv.mxfp4_gemm(maq, masf, mbq, mbsf, out=c)
+    torch.cuda.synchronize()
+    del maq, masf, mbq, mbsf, c
     torch.cuda.empty_cache()
     src = torch.ones(2 ** 30, dtype=torch.uint8, device="cuda")
     dst = torch.empty_like(src)
