@@ -363,6 +363,140 @@ __global__ void __launch_bounds__(kVarThreads) var_encode_kernel(const uint16_t*
   }
 }
 
+// COLWISE encode, one workgroup per block of 16 strips (256 rows) of a
+// 512-column band: the four waves encode 4 strips each into LDS, then the
+// workgroup writes each output row's 128 code bytes (and 16 scale bytes) of
+// the block as whole cache lines.
+//   codes: output row r, strip k at 8-byte slot k ^ 2 ((r >> 3) & 7) of the
+//          row's 128 bytes (the XOR spreads a wave's writes, 8 rows per lane,
+//          over the banks; slot pairs 2p, 2p + 1 stay together and in order)
+//   scales: strip-major, 512 bytes per strip
+constexpr int kColStrips = 16;
+
+struct VarColSmem {
+  uint32_t codes[kStripCols][kColStrips * 2];
+  uint8_t scales[kColStrips][kStripCols];
+};
+
+__device__ __forceinline__ int col_slot(int r, int k) { return k ^ (2 * ((r >> 3) & 7)); }
+
+template <bool k2D, bool kRht, bool kSr>
+__global__ void __launch_bounds__(kVarThreads) var_encode_colwise_kernel(
+    const uint16_t* __restrict__ x, VarShape sh, uint32_t signs, uint64_t seed, uint64_t offset,
+    const uint32_t* __restrict__ partial, int npartial, uint8_t* __restrict__ q, uint8_t* __restrict__ sf,
+    float* __restrict__ gout) {
+  __shared__ double table[128];
+  __shared__ uint32_t red[kVarThreads / 64];
+  __shared__ __attribute__((aligned(16))) VarColSmem cs;
+  const int t = blockIdx.y, wave = wave_id(), lane = threadIdx.x & 63;
+  uint32_t am = 0u;
+  for (int i = threadIdx.x; i < npartial; i += kVarThreads) {
+    const uint32_t p = partial[(int64_t)t * npartial + i];
+    am = am > p ? am : p;
+  }
+  am = wave_max_u32(am);
+  if (lane == 0) red[wave] = am;
+  __syncthreads();
+  am = red[0];
+#pragma unroll
+  for (int w = 1; w < kVarThreads / 64; ++w) am = am > red[w] ? am : red[w];
+  const float g = __uint_as_float(am) / kGlobalDiv;
+  if (blockIdx.x == 0 && threadIdx.x == 0) gout[t] = g;
+  for (uint32_t j = threadIdx.x; j < 127u; j += kVarThreads) table[j] = recip_entry(j, g);
+  const double r6 = recip_d6(g);
+  __syncthreads();
+
+  const uint16_t* xt = x + (int64_t)t * sh.n;
+  const uint32_t key0 = (uint32_t)seed, key1 = (uint32_t)(seed >> 32);
+  const int64_t nblk = (sh.sr + kColStrips - 1) / kColStrips;
+  const int64_t nitems = sh.sc * nblk;
+  for (int64_t it = blockIdx.x; it < nitems; it += gridDim.x) {           // workgroup-uniform
+    const int64_t band = it / nblk, blk = it % nblk;
+    const int nstr = (int)std::min<int64_t>(kColStrips, sh.sr - blk * kColStrips);
+    const int64_t col = band * kStripCols + 8 * lane;
+    for (int k = wave; k < nstr; k += kVarThreads / 64) {
+      const int64_t r0 = (blk * kColStrips + k) * kStripRows;
+      u32x4 raw[kStripRows];
+      load_strip(xt, sh, r0, col, raw);
+      uint32_t tile = 0u;
+      if (k2D) {
+        uint32_t pk = 0u;
+#pragma unroll
+        for (int r = 0; r < kStripRows; ++r)
+          pk = pk_absmax(pk_absmax(pk_absmax(pk_absmax(pk, raw[r].x), raw[r].y), raw[r].z), raw[r].w);
+        tile = pair_max_u32(halves_max(pk) << 16);
+      }
+      uint32_t sb[2] = {0u, 0u};                   // columns j's scale bytes
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        float v[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) v[r] = chunk_val(raw[r], j);
+        if (kRht) rht16(v, signs);
+        uint32_t bam = 0u;
+        if (k2D) {
+          bam = tile;
+        } else {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) bam = bam > fabs_bits(v[r]) ? bam : fabs_bits(v[r]);
+        }
+        const uint32_t sbyte = e4m3_rne_sat(rn32((double)__uint_as_float(bam) * r6));
+        uint32_t u[16];
+        if (kSr) {
+          const int64_t orow = (int64_t)t * sh.R + col + j;
+          const uint64_t n = (uint64_t)(orow * sh.C + r0) / 8 + offset;
+          uint32_t u0[8], u1[8];
+          draws8(n, key0, key1, u0);
+          draws8(n + 1, key0, key1, u1);
+#pragma unroll
+          for (int kk = 0; kk < 8; ++kk) {
+            u[kk] = u0[kk];
+            u[kk + 8] = u1[kk];
+          }
+        }
+        uint32_t codes[2];
+        encode_vals<16, kSr>(v, table[sbyte], u, codes);
+        const int r = 8 * lane + j;                // output row within the band
+        *(u32x2*)&cs.codes[r][2 * col_slot(r, k)] = u32x2{codes[0], codes[1]};
+        sb[j / 4] |= sbyte << (8 * (j % 4));
+      }
+      *(u32x2*)&cs.scales[k][8 * lane] = u32x2{sb[0], sb[1]};
+    }
+    __syncthreads();
+    // each output row of the band gets nstr * 8 code bytes and nstr scale bytes
+    const int rows_here = (int)std::min<int64_t>(kStripCols, sh.cols - band * kStripCols);
+    const int64_t orow0 = (int64_t)t * sh.R + band * kStripCols;
+    const bool q16 = sh.C % 32 == 0;               // output rows of codes start 16-byte aligned
+#pragma unroll 4
+    for (int i = 0; i < kStripCols * 8 / kVarThreads; ++i) {
+      const int flat = i * kVarThreads + threadIdx.x;
+      const int r = flat >> 3, pc = flat & 7;      // output row, 16-byte piece (strips 2 pc, 2 pc + 1)
+      if (r < rows_here && 2 * pc < nstr) {
+        const u32x4 v = *(const u32x4*)&cs.codes[r][2 * col_slot(r, 2 * pc)];
+        uint8_t* dst = q + (orow0 + r) * (sh.C / 2) + blk * (kColStrips * 8) + 16 * pc;
+        if (2 * pc + 1 < nstr && q16) {
+          *(u32x4*)dst = v;
+        } else {
+          *(u32x2*)dst = u32x2{v.x, v.y};
+          if (2 * pc + 1 < nstr) *(u32x2*)(dst + 8) = u32x2{v.z, v.w};
+        }
+      }
+    }
+    for (int r = threadIdx.x; r < rows_here; r += kVarThreads) {
+      uint32_t w[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int k = 0; k < kColStrips; ++k) w[k / 4] |= (uint32_t)cs.scales[k][r] << (8 * (k % 4));
+      uint8_t* dst = sf + (orow0 + r) * (sh.C / 16) + blk * kColStrips;
+      if (nstr == kColStrips && !(reinterpret_cast<uintptr_t>(dst) & 15u)) {
+        *(u32x4*)dst = u32x4{w[0], w[1], w[2], w[3]};
+      } else {
+        for (int k = 0; k < nstr; ++k) dst[k] = (uint8_t)(w[k / 4] >> (8 * (k % 4)));
+      }
+    }
+    __syncthreads();                               // LDS free for the next block
+  }
+}
+
 }  // namespace nvfp4
 
 // ============================================================ host entry point
@@ -379,8 +513,12 @@ int var_wgs(int64_t batch, int64_t ngroups) {
 template <bool kColwise, bool k2D, bool kRht, bool kSr>
 void launch_encode(dim3 grid, hipStream_t s, const uint16_t* x, const VarShape& sh, uint32_t signs, uint64_t seed,
                    uint64_t offset, const uint32_t* partial, uint8_t* q, uint8_t* sf, float* g) {
-  var_encode_kernel<kColwise, k2D, kRht, kSr><<<grid, kVarThreads, 0, s>>>(x, sh, signs, seed, offset, partial,
+  if (kColwise)
+    var_encode_colwise_kernel<k2D, kRht, kSr><<<grid, kVarThreads, 0, s>>>(x, sh, signs, seed, offset, partial,
                                                                            (int)grid.x, q, sf, g);
+  else
+    var_encode_kernel<false, k2D, kRht, kSr><<<grid, kVarThreads, 0, s>>>(x, sh, signs, seed, offset, partial,
+                                                                          (int)grid.x, q, sf, g);
 }
 
 }  // namespace
@@ -426,7 +564,9 @@ nvfp4_status nvfp4_quantize_ex(const uint16_t* x, int64_t batch, int64_t rows, i
   sh.seg = std::max<int64_t>(1, std::min<int64_t>(16, strips / ((int64_t)nvfp4host::num_cus() * 16)));
   sh.nseg = (sh.sr + sh.seg - 1) / sh.seg;
   sh.nitems = sh.sc * sh.nseg;
-  const dim3 grid((unsigned)var_wgs(batch, sh.nitems), (unsigned)batch);
+  // workgroups: per-wave strip runs (row-wise), or per-workgroup blocks of 16 strips (COLWISE)
+  const int64_t wgs_need = colwise ? sh.sc * ((sh.sr + 15) / 16) * (kVarThreads / 64) : sh.nitems;
+  const dim3 grid((unsigned)var_wgs(batch, wgs_need), (unsigned)batch);
   hipStream_t s = (hipStream_t)stream;
   uint32_t* partial = (uint32_t*)workspace;
   // pass 1: the amax of the quantized values (the orientation matters only under RHT)

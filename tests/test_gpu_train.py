@@ -47,6 +47,16 @@ def test_rowwise_variants_any_row_count(variant):
     _check(_x((40, 96), 5), variant)
 
 
+@pytest.mark.parametrize("variant", [1, 3, 5, 9, 11, 13])
+@pytest.mark.parametrize("shape", [(272, 528), (528, 48), (2, 800, 1056), (256, 512)])
+def test_colwise_variants_over_several_row_blocks(variant, shape):
+    """COLWISE output is written per block of 256 input rows x 512 columns:
+    shapes with a ragged last block (rows % 256 = 16 or 32), output rows of
+    codes that start only 8-byte aligned (rows % 32 = 16), a ragged column
+    band, and one exact block."""
+    _check(_x(shape, sum(shape) * 3 + variant, wide=len(shape) == 3), variant)
+
+
 def test_variant_zero_equals_plain_quantize():
     x = _x((2, 128, 256), 6, wide=True)
     q, sf, g = nv.quantize_ex(x, 0)
