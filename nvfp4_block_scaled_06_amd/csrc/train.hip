@@ -57,8 +57,10 @@ __device__ __forceinline__ void philox(uint32_t c0, uint32_t c1, uint32_t k0, ui
       k0 += 0x9E3779B9u;
       k1 += 0xBB67AE85u;
     }
-    const uint32_t lo0 = 0xD2511F53u * c0, hi0 = __umulhi(0xD2511F53u, c0);
-    const uint32_t lo1 = 0xCD9E8D57u * c2, hi1 = __umulhi(0xCD9E8D57u, c2);
+    // one 32 x 32 -> 64-bit multiply each (a single v_mad_u64_u32)
+    const uint64_t p0 = (uint64_t)c0 * 0xD2511F53u, p1 = (uint64_t)c2 * 0xCD9E8D57u;
+    const uint32_t lo0 = (uint32_t)p0, hi0 = (uint32_t)(p0 >> 32);
+    const uint32_t lo1 = (uint32_t)p1, hi1 = (uint32_t)(p1 >> 32);
     const uint32_t n0 = hi1 ^ c1 ^ k0, n2 = hi0 ^ c3 ^ k1;
     c0 = n0;
     c1 = lo1;
@@ -81,14 +83,25 @@ __device__ __forceinline__ void draws8(uint64_t n, uint32_t key0, uint32_t key1,
 
 // Stochastic E2M1 magnitude code of y >= 0 with the 16-bit draw u.
 __device__ __forceinline__ uint32_t e2m1_sr(float y, uint32_t u) {
-  if (y >= 6.0f) return 7u;
-  const uint32_t k = (uint32_t)(y >= 0.5f) + (uint32_t)(y >= 1.0f) + (uint32_t)(y >= 1.5f) + (uint32_t)(y >= 2.0f) +
-                     (uint32_t)(y >= 3.0f) + (uint32_t)(y >= 4.0f);
-  // lower neighbour and 1 / gap (gaps are powers of two, so p is exact)
-  const float lo = k <= 4u ? 0.5f * (float)k : k == 5u ? 3.0f : 4.0f;
-  const float inv_gap = k < 4u ? 2.0f : k < 6u ? 1.0f : 0.5f;
-  const float p = (y - lo) * inv_gap;
-  return k + ((float)u < p * 65536.0f ? 1u : 0u);
+  // The probability of rounding up is (y - lo) / gap with lo the grid point
+  // at or below y; with fp32 bits b = bits(y) that fraction is a run of
+  // mantissa bits, so each regime is an integer test on b:
+  const uint32_t b = __float_as_uint(y);
+  //   y >= 1: gap = half the binade, fraction = low 22 bits m; up iff m > 64 u.
+  //   Adding 2^22 - 1 - 64 u carries into bit 22 exactly then, and bits 22
+  //   and up then read (exponent, top mantissa bit) of the result, 254 for
+  //   1.0 up to 259 for 6.0 (larger y saturate to 6)
+  const uint32_t ra = (b + (0x3FFFFFu - (u << 6))) >> 22;
+  const uint32_t ca = (ra < 259u ? ra : 259u) - 252u;
+  //   0.5 <= y < 1: lo = 0.5, gap 0.5, fraction = low 23 bits / 2^23
+  const uint32_t cb = 1u + ((b & 0x7FFFFFu) > (u << 7) ? 1u : 0u);
+  //   y < 0.5: lo = 0, gap 0.5, fraction = 2 y (u and y 2^17 are exact in fp32)
+  const uint32_t cc = (float)u < y * 131072.0f ? 1u : 0u;
+  // regime masks from the sign of a difference (b < 2^31), so the three
+  // results merge without a branch
+  const uint32_t m1 = (uint32_t)((int32_t)(0x3F7FFFFFu - b) >> 31);    // y >= 1
+  const uint32_t mh = (uint32_t)((int32_t)(0x3EFFFFFFu - b) >> 31);    // y >= 0.5
+  return (ca & m1) | (cb & mh & ~m1) | (cc & ~mh);
 }
 
 // fp32 value of element j (0..7) of a row chunk of 8 bf16.
