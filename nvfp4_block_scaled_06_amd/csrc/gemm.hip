@@ -23,6 +23,7 @@
 // pairs; the next K step's codes and scales are prefetched into registers
 // while the current step is contracted, one barrier per step.
 #include <algorithm>
+#include <type_traits>
 
 #include "common.hpp"
 
@@ -66,16 +67,24 @@ __device__ __forceinline__ Operand make_operand(const uint8_t* q, const uint8_t*
 
 constexpr uint32_t kOutside = 0x80000000u;  // offset beyond every extent (extents stay below 2^31)
 
-template <bool kAligned>
+// Operand load modes: kRagged (any K % 16 == 0: each block checked on its
+// own), kStep (K % 64 == 0: a step is wholly inside or outside), kGroup
+// (K % 256 == 0: as kStep, but the scale words of 4 steps come from one
+// 16-byte load, so each 128-byte line of scales is fetched from L2 once
+// instead of once per step; per-step 4-byte scale loads cost about as much
+// L2 traffic as all the codes).
+constexpr int kRagged = 0, kStep = 1, kGroup = 2;
+
+template <int kMode>
 __device__ __forceinline__ RowRaw load_row(const Operand& o, int lrow, int64_t K, int64_t k0) {
   RowRaw r;
   const bool in = k0 < K;
   const uint32_t qo = in ? (uint32_t)lrow * o.qrow + (uint32_t)(k0 / 2) : kOutside;
   const uint32_t so = in ? (uint32_t)lrow * o.srow + (uint32_t)(k0 / 16) : kOutside;
-  if (kAligned) {                      // K % 64 == 0: a step is wholly inside or outside
+  if (kMode != kRagged) {              // a step is wholly inside or outside
     r.c01 = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(o.q, (int)qo, 0, 0));
     r.c23 = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(o.q, (int)(in ? qo + 16 : kOutside), 0, 0));
-    r.s = __builtin_amdgcn_raw_buffer_load_b32(o.s, (int)so, 0, 0);
+    r.s = kMode == kStep ? __builtin_amdgcn_raw_buffer_load_b32(o.s, (int)so, 0, 0) : 0u;   // kGroup: set by the caller
   } else {                             // ragged last step: each block checked on its own
     u32x2 c[4];
     r.s = 0;
@@ -89,6 +98,17 @@ __device__ __forceinline__ RowRaw load_row(const Operand& o, int lrow, int64_t K
     r.c23 = u32x4{c[2].x, c[2].y, c[3].x, c[3].y};
   }
   return r;
+}
+
+// Scale words of K steps 4g .. 4g+3 of one row (kGroup; zeros past K).
+__device__ __forceinline__ u32x4 load_scale_group(const Operand& o, int lrow, int64_t K, int64_t g) {
+  const uint32_t so = g * 4 * GTK < K ? (uint32_t)lrow * o.srow + (uint32_t)(g * 16) : kOutside;
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(o.s, (int)so, 0, 0));
+}
+
+template <int i>
+__device__ __forceinline__ uint32_t word(const u32x4& v) {
+  return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
 }
 
 template <int sel>
@@ -163,7 +183,7 @@ __device__ __forceinline__ void substep(f32x16 (&acc)[4][4], f16x8 (&a)[4], f16x
 // One 256 x 256 output tile: rows [m0, m_end) of A (K-major NVFP4, at most
 // 256 of them) against rows [n0, n_end) of B, C row stride ldc, scaled by
 // gab in the epilogue.  As / Bs are the workgroup's LDS tiles.
-template <bool kAligned>
+template <int kMode>
 __device__ __forceinline__ void gemm_tile(const uint8_t* __restrict__ aq, const uint8_t* __restrict__ asf,
                                           int64_t m0, int64_t m_end, const uint8_t* __restrict__ bq,
                                           const uint8_t* __restrict__ bsf, int64_t n0, int64_t n_end, int64_t K,
@@ -187,8 +207,21 @@ __device__ __forceinline__ void gemm_tile(const uint8_t* __restrict__ aq, const 
   // other buffer (one block per substep) and the raw codes of step k+2 load.
   // Steps past the last one read zeros and write an unread buffer.
   const int64_t nk = (K + GTK - 1) / GTK;
-  RowRaw ra = load_row<kAligned>(A, tid, K, 0);
-  RowRaw rb = load_row<kAligned>(B, tid, K, 0);
+  // kGroup: scale words of the group holding the step being loaded (cur)
+  // and of the next group (nxt, in flight)
+  u32x4 sa_cur = {0u, 0u, 0u, 0u}, sb_cur = sa_cur, sa_nxt = sa_cur, sb_nxt = sa_cur;
+  if (kMode == kGroup) {
+    sa_cur = load_scale_group(A, tid, K, 0);
+    sb_cur = load_scale_group(B, tid, K, 0);
+    sa_nxt = load_scale_group(A, tid, K, 1);
+    sb_nxt = load_scale_group(B, tid, K, 1);
+  }
+  RowRaw ra = load_row<kMode>(A, tid, K, 0);
+  RowRaw rb = load_row<kMode>(B, tid, K, 0);
+  if (kMode == kGroup) {
+    ra.s = sa_cur.x;
+    rb.s = sb_cur.x;
+  }
   deq_block_to_lds<0>(ra, &As[0][tid][0]);
   deq_block_to_lds<1>(ra, &As[0][tid][0]);
   deq_block_to_lds<2>(ra, &As[0][tid][0]);
@@ -197,14 +230,32 @@ __device__ __forceinline__ void gemm_tile(const uint8_t* __restrict__ aq, const 
   deq_block_to_lds<1>(rb, &Bs[0][tid][0]);
   deq_block_to_lds<2>(rb, &Bs[0][tid][0]);
   deq_block_to_lds<3>(rb, &Bs[0][tid][0]);
-  ra = load_row<kAligned>(A, tid, K, GTK);
-  rb = load_row<kAligned>(B, tid, K, GTK);
+  ra = load_row<kMode>(A, tid, K, GTK);
+  rb = load_row<kMode>(B, tid, K, GTK);
+  if (kMode == kGroup) {
+    ra.s = sa_cur.y;
+    rb.s = sb_cur.y;
+  }
   __syncthreads();
   const int arow = wm * 128 + (lane & 31), brow = wn * 128 + (lane & 31), kof = 8 * (lane >> 5);
-  for (int64_t kt = 0; kt < nk; ++kt) {
+  // Iteration kt contracts step kt, dequantizes step kt+1 and loads step
+  // kt+2.  Unrolled by 4 so that kt+2's scale word sits at a fixed position
+  // of its group (kt is a multiple of 4 at the top of the loop).
+  auto iteration = [&](int64_t kt, auto U) {
+    constexpr int u = decltype(U)::value;          // (kt + 2) % 4 == (u + 2) % 4
     const int buf = (int)(kt & 1);
-    const RowRaw ra2 = load_row<kAligned>(A, tid, K, (kt + 2) * GTK);
-    const RowRaw rb2 = load_row<kAligned>(B, tid, K, (kt + 2) * GTK);
+    RowRaw ra2 = load_row<kMode>(A, tid, K, (kt + 2) * GTK);
+    RowRaw rb2 = load_row<kMode>(B, tid, K, (kt + 2) * GTK);
+    if (kMode == kGroup) {
+      if ((u + 2) % 4 == 0) {                      // step kt+2 opens group (kt+2)/4
+        sa_cur = sa_nxt;
+        sb_cur = sb_nxt;
+        sa_nxt = load_scale_group(A, tid, K, (kt + 2) / 4 + 1);
+        sb_nxt = load_scale_group(B, tid, K, (kt + 2) / 4 + 1);
+      }
+      ra2.s = word<(u + 2) % 4>(sa_cur);
+      rb2.s = word<(u + 2) % 4>(sb_cur);
+    }
     const _Float16* Acur = &As[buf][arow][kof];
     const _Float16* Bcur = &Bs[buf][brow][kof];
     _Float16* An = &As[buf ^ 1][tid][0];
@@ -221,6 +272,16 @@ __device__ __forceinline__ void gemm_tile(const uint8_t* __restrict__ aq, const 
     ra = ra2;
     rb = rb2;
     __syncthreads();
+  };
+  if (kMode == kGroup) {                           // nk % 4 == 0
+    for (int64_t kt = 0; kt < nk; kt += 4) {
+      iteration(kt, std::integral_constant<int, 0>());
+      iteration(kt + 1, std::integral_constant<int, 1>());
+      iteration(kt + 2, std::integral_constant<int, 2>());
+      iteration(kt + 3, std::integral_constant<int, 3>());
+    }
+  } else {
+    for (int64_t kt = 0; kt < nk; ++kt) iteration(kt, std::integral_constant<int, 0>());
   }
 #pragma unroll
   for (int i = 0; i < 4; ++i)
@@ -234,7 +295,7 @@ __device__ __forceinline__ void gemm_tile(const uint8_t* __restrict__ aq, const 
       }
 }
 
-template <bool kAligned>
+template <int kMode>
 __global__ void __launch_bounds__(GThreads) gemm_kernel(const uint8_t* __restrict__ aq, const uint8_t* __restrict__ asf,
                                                         const float* __restrict__ ag, const uint8_t* __restrict__ bq,
                                                         const uint8_t* __restrict__ bsf, const float* __restrict__ bg,
@@ -243,7 +304,7 @@ __global__ void __launch_bounds__(GThreads) gemm_kernel(const uint8_t* __restric
   __shared__ __attribute__((aligned(16))) _Float16 Bs[2][GTN][GLD];
   const int64_t tile = xcd_tile((int64_t)blockIdx.y * gridDim.x + blockIdx.x, (int64_t)gridDim.x * gridDim.y);
   const int64_t m0 = tile / gridDim.x * GTM, n0 = tile % gridDim.x * GTN;
-  gemm_tile<kAligned>(aq, asf, m0, M, bq, bsf, n0, N, K, ag[0] * bg[0], C, N, As, Bs);
+  gemm_tile<kMode>(aq, asf, m0, M, bq, bsf, n0, N, K, ag[0] * bg[0], C, N, As, Bs);
 }
 
 // Grouped GEMM: rows of A are grouped by expert, rows [off[e], off[e+1])
@@ -251,7 +312,7 @@ __global__ void __launch_bounds__(GThreads) gemm_kernel(const uint8_t* __restric
 // (expert, 256-row tile) pairs in expert order; a workgroup finds its pair by
 // walking the offsets (clamped to [0, M], so inconsistent offsets never
 // reach outside A or C) and exits when its index is past the last tile.
-template <bool kAligned>
+template <int kMode>
 __global__ void __launch_bounds__(GThreads) grouped_gemm_kernel(
     const uint8_t* __restrict__ aq, const uint8_t* __restrict__ asf, const float* __restrict__ ag,
     const uint8_t* __restrict__ bq, const uint8_t* __restrict__ bsf, const float* __restrict__ bg,
@@ -271,7 +332,7 @@ __global__ void __launch_bounds__(GThreads) grouped_gemm_kernel(
   if (e == experts) return;                            // past the last tile: no work
   const int64_t m0 = lo + tile * GTM, n0 = (int64_t)blockIdx.x * GTN;
   const int64_t wq = N * (K / 2), ws = N * (K / 16);   // bytes per expert weight, scales
-  gemm_tile<kAligned>(aq, asf, m0, hi, bq + e * wq, bsf + e * ws, n0, N, K, ag[0] * bg[e], C, N, As, Bs);
+  gemm_tile<kMode>(aq, asf, m0, hi, bq + e * wq, bsf + e * ws, n0, N, K, ag[0] * bg[e], C, N, As, Bs);
 }
 
 }  // namespace nvfp4
@@ -292,12 +353,16 @@ extern "C" nvfp4_status nvfp4_gemm(const uint8_t* a_q, const uint8_t* a_sf, cons
   nvfp4_status st = nvfp4host::check_device();
   if (st) return st;
   const dim3 grid((unsigned)((N + GTN - 1) / GTN), (unsigned)((M + GTM - 1) / GTM));
-  // aligned path: K a multiple of 64 and 4-byte aligned scale rows
+  // whole-step paths: K a multiple of 64 (of 256 for grouped scale loads)
+  // and 16-byte aligned scale bases, so scale rows are 4- (16-) byte aligned
   const bool aligned = K % GTK == 0 && nvfp4host::aligned16(a_sf) && nvfp4host::aligned16(b_sf);
-  if (aligned)
-    gemm_kernel<true><<<grid, GThreads, 0, (hipStream_t)stream>>>(a_q, a_sf, a_g, b_q, b_sf, b_g, M, N, K, c);
+  hipStream_t s = (hipStream_t)stream;
+  if (aligned && K % (4 * GTK) == 0)
+    gemm_kernel<kGroup><<<grid, GThreads, 0, s>>>(a_q, a_sf, a_g, b_q, b_sf, b_g, M, N, K, c);
+  else if (aligned)
+    gemm_kernel<kStep><<<grid, GThreads, 0, s>>>(a_q, a_sf, a_g, b_q, b_sf, b_g, M, N, K, c);
   else
-    gemm_kernel<false><<<grid, GThreads, 0, (hipStream_t)stream>>>(a_q, a_sf, a_g, b_q, b_sf, b_g, M, N, K, c);
+    gemm_kernel<kRagged><<<grid, GThreads, 0, s>>>(a_q, a_sf, a_g, b_q, b_sf, b_g, M, N, K, c);
   NVFP4_LAUNCH_CHECK();
   return NVFP4_OK;
 }
@@ -325,12 +390,14 @@ extern "C" nvfp4_status nvfp4_grouped_gemm(const uint8_t* a_q, const uint8_t* a_
   // aligned path as for nvfp4_gemm; each expert's weight starts at a multiple
   // of N*K/2 code bytes and N*K/16 scale bytes, aligned with K % 64 == 0
   const bool aligned = K % GTK == 0 && nvfp4host::aligned16(a_sf) && nvfp4host::aligned16(b_sf);
-  if (aligned)
-    grouped_gemm_kernel<true><<<grid, GThreads, 0, (hipStream_t)stream>>>(a_q, a_sf, a_g, b_q, b_sf, b_g, offsets,
-                                                                          experts, M, N, K, c);
+  hipStream_t s = (hipStream_t)stream;
+  if (aligned && K % (4 * GTK) == 0)
+    grouped_gemm_kernel<kGroup><<<grid, GThreads, 0, s>>>(a_q, a_sf, a_g, b_q, b_sf, b_g, offsets, experts, M, N, K, c);
+  else if (aligned)
+    grouped_gemm_kernel<kStep><<<grid, GThreads, 0, s>>>(a_q, a_sf, a_g, b_q, b_sf, b_g, offsets, experts, M, N, K, c);
   else
-    grouped_gemm_kernel<false><<<grid, GThreads, 0, (hipStream_t)stream>>>(a_q, a_sf, a_g, b_q, b_sf, b_g, offsets,
-                                                                           experts, M, N, K, c);
+    grouped_gemm_kernel<kRagged><<<grid, GThreads, 0, s>>>(a_q, a_sf, a_g, b_q, b_sf, b_g, offsets, experts, M, N, K,
+                                                           c);
   NVFP4_LAUNCH_CHECK();
   return NVFP4_OK;
 }

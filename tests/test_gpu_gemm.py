@@ -21,8 +21,8 @@ def _operands(M, N, K, seed, scale_a=1.0, scale_b=1.0):
     return a, b
 
 
-@pytest.mark.parametrize("M,N,K", [(128, 128, 64), (64, 96, 160), (130, 257, 48), (256, 256, 1024),
-                                   (1, 1, 16), (300, 70, 7168), (512, 384, 2048)])
+@pytest.mark.parametrize("M,N,K", [(128, 128, 64), (64, 96, 160), (130, 257, 48), (256, 256, 1024), (96, 200, 576),
+                                   (64, 64, 320), (1, 1, 16), (300, 70, 7168), (512, 384, 2048)])
 def test_gemm_small(M, N, K):
     print("case: gemm", M, N, K, flush=True)
     a, b = _operands(M, N, K, M * 7 + N * 3 + K)
