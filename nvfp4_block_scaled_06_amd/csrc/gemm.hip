@@ -20,8 +20,11 @@
 // Tiling: 256 x 256 output per workgroup (the 8192 x 2048 problem is then one
 // workgroup per CU), 4 waves of 128 x 128 (4 x 4 MFMA tiles, 256 fp32
 // accumulators per lane), K step 64 (4 blocks).  LDS holds two f16 tile
-// pairs; the next K step's codes and scales are prefetched into registers
-// while the current step is contracted, one barrier per step.
+// pairs; while step k is contracted, each thread dequantizes its A row and
+// B row of step k+1 into the other pair and step k+2's raw codes load, one
+// barrier per step.  When K % 256 == 0 the raw codes are staged in LDS by
+// buffer-to-LDS loads (gemm_tile_dma); otherwise they load into registers
+// (gemm_tile).
 #include <algorithm>
 #include <type_traits>
 
@@ -67,12 +70,10 @@ __device__ __forceinline__ Operand make_operand(const uint8_t* q, const uint8_t*
 
 constexpr uint32_t kOutside = 0x80000000u;  // offset beyond every extent (extents stay below 2^31)
 
-// Operand load modes: kRagged (any K % 16 == 0: each block checked on its
-// own), kStep (K % 64 == 0: a step is wholly inside or outside), kGroup
-// (K % 256 == 0: as kStep, but the scale words of 4 steps come from one
-// 16-byte load, so each 128-byte line of scales is fetched from L2 once
-// instead of once per step; per-step 4-byte scale loads cost about as much
-// L2 traffic as all the codes).
+// Operand paths: kRagged (any K % 16 == 0: each block checked on its own)
+// and kStep (K % 64 == 0: a step is wholly inside or outside) load a
+// thread's raw codes and scale bytes into registers; kGroup (K % 256 == 0)
+// stages the raw codes in LDS (gemm_tile_dma below).
 constexpr int kRagged = 0, kStep = 1, kGroup = 2;
 
 template <int kMode>
@@ -84,7 +85,7 @@ __device__ __forceinline__ RowRaw load_row(const Operand& o, int lrow, int64_t K
   if (kMode != kRagged) {              // a step is wholly inside or outside
     r.c01 = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(o.q, (int)qo, 0, 0));
     r.c23 = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(o.q, (int)(in ? qo + 16 : kOutside), 0, 0));
-    r.s = kMode == kStep ? __builtin_amdgcn_raw_buffer_load_b32(o.s, (int)so, 0, 0) : 0u;   // kGroup: set by the caller
+    r.s = __builtin_amdgcn_raw_buffer_load_b32(o.s, (int)so, 0, 0);
   } else {                             // ragged last step: each block checked on its own
     u32x2 c[4];
     r.s = 0;
@@ -100,7 +101,9 @@ __device__ __forceinline__ RowRaw load_row(const Operand& o, int lrow, int64_t K
   return r;
 }
 
-// Scale words of K steps 4g .. 4g+3 of one row (kGroup; zeros past K).
+// Scale words of K steps 4g .. 4g+3 of one row (kGroup; zeros past K): one
+// 16-byte load per 4 steps, so each 128-byte line of scales is fetched from
+// L2 a quarter as often as with a 4-byte load per step.
 __device__ __forceinline__ u32x4 load_scale_group(const Operand& o, int lrow, int64_t K, int64_t g) {
   const uint32_t so = g * 4 * GTK < K ? (uint32_t)lrow * o.srow + (uint32_t)(g * 16) : kOutside;
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(o.s, (int)so, 0, 0));
@@ -180,6 +183,51 @@ __device__ __forceinline__ void substep(f32x16 (&acc)[4][4], f16x8 (&a)[4], f16x
   }
 }
 
+// The last substep of a K step.  Its 16 MFMAs are split around the
+// workgroup barrier that ends the step: the first 8 run while block 3 of the
+// next step is dequantized into the other buffer; after the barrier (the
+// other buffer is complete and the current one is no longer read) the
+// fragments of the next step's first substep are read while the last 8 run,
+// so the LDS latency after the barrier is hidden behind MFMAs.
+__device__ __forceinline__ void substep_last(f32x16 (&acc)[4][4], f16x8 (&a)[4], f16x8 (&b)[4], const _Float16* Anb,
+                                             const _Float16* Bnb, const RowRaw& ra, const RowRaw& rb,
+                                             _Float16* Anext, _Float16* Bnext) {
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], b[j], acc[i][j], 0, 0, 0);
+  deq_block_to_lds<3>(ra, Anext);
+  deq_block_to_lds<3>(rb, Bnext);
+  // 8 MFMA; about 40 VALU; 4 LDS writes
+#pragma unroll
+  for (int m = 0; m < 8; ++m) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);     // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);     // VALU
+    if (m >= 4) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // DS write
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  __syncthreads();
+  __builtin_amdgcn_sched_barrier(0);
+  f16x8 an[4], bn[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) an[i] = *(const f16x8*)(Anb + i * 32 * GLD);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) bn[j] = *(const f16x8*)(Bnb + j * 32 * GLD);
+#pragma unroll
+  for (int i = 2; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], b[j], acc[i][j], 0, 0, 0);
+#pragma unroll
+  for (int m = 0; m < 8; ++m) {
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);     // DS read
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);     // MFMA
+  }
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) { a[i] = an[i]; b[i] = bn[i]; }
+}
+
 // One 256 x 256 output tile: rows [m0, m_end) of A (K-major NVFP4, at most
 // 256 of them) against rows [n0, n_end) of B, C row stride ldc, scaled by
 // gab in the epilogue.  As / Bs are the workgroup's LDS tiles.
@@ -207,21 +255,8 @@ __device__ __forceinline__ void gemm_tile(const uint8_t* __restrict__ aq, const 
   // other buffer (one block per substep) and the raw codes of step k+2 load.
   // Steps past the last one read zeros and write an unread buffer.
   const int64_t nk = (K + GTK - 1) / GTK;
-  // kGroup: scale words of the group holding the step being loaded (cur)
-  // and of the next group (nxt, in flight)
-  u32x4 sa_cur = {0u, 0u, 0u, 0u}, sb_cur = sa_cur, sa_nxt = sa_cur, sb_nxt = sa_cur;
-  if (kMode == kGroup) {
-    sa_cur = load_scale_group(A, tid, K, 0);
-    sb_cur = load_scale_group(B, tid, K, 0);
-    sa_nxt = load_scale_group(A, tid, K, 1);
-    sb_nxt = load_scale_group(B, tid, K, 1);
-  }
   RowRaw ra = load_row<kMode>(A, tid, K, 0);
   RowRaw rb = load_row<kMode>(B, tid, K, 0);
-  if (kMode == kGroup) {
-    ra.s = sa_cur.x;
-    rb.s = sb_cur.x;
-  }
   deq_block_to_lds<0>(ra, &As[0][tid][0]);
   deq_block_to_lds<1>(ra, &As[0][tid][0]);
   deq_block_to_lds<2>(ra, &As[0][tid][0]);
@@ -232,56 +267,270 @@ __device__ __forceinline__ void gemm_tile(const uint8_t* __restrict__ aq, const 
   deq_block_to_lds<3>(rb, &Bs[0][tid][0]);
   ra = load_row<kMode>(A, tid, K, GTK);
   rb = load_row<kMode>(B, tid, K, GTK);
-  if (kMode == kGroup) {
-    ra.s = sa_cur.y;
-    rb.s = sb_cur.y;
-  }
   __syncthreads();
   const int arow = wm * 128 + (lane & 31), brow = wn * 128 + (lane & 31), kof = 8 * (lane >> 5);
-  // Iteration kt contracts step kt, dequantizes step kt+1 and loads step
-  // kt+2.  Unrolled by 4 so that kt+2's scale word sits at a fixed position
-  // of its group (kt is a multiple of 4 at the top of the loop).
-  auto iteration = [&](int64_t kt, auto U) {
-    constexpr int u = decltype(U)::value;          // (kt + 2) % 4 == (u + 2) % 4
+  // fragments of step 0's first substep; later steps' are read by substep_last
+  f16x8 a[4], b[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) a[i] = *(const f16x8*)(&As[0][arow][kof] + i * 32 * GLD);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) b[j] = *(const f16x8*)(&Bs[0][brow][kof] + j * 32 * GLD);
+  // iteration kt contracts step kt, dequantizes step kt+1 and loads step kt+2
+  for (int64_t kt = 0; kt < nk; ++kt) {
     const int buf = (int)(kt & 1);
-    RowRaw ra2 = load_row<kMode>(A, tid, K, (kt + 2) * GTK);
-    RowRaw rb2 = load_row<kMode>(B, tid, K, (kt + 2) * GTK);
-    if (kMode == kGroup) {
-      if ((u + 2) % 4 == 0) {                      // step kt+2 opens group (kt+2)/4
-        sa_cur = sa_nxt;
-        sb_cur = sb_nxt;
-        sa_nxt = load_scale_group(A, tid, K, (kt + 2) / 4 + 1);
-        sb_nxt = load_scale_group(B, tid, K, (kt + 2) / 4 + 1);
-      }
-      ra2.s = word<(u + 2) % 4>(sa_cur);
-      rb2.s = word<(u + 2) % 4>(sb_cur);
-    }
+    const RowRaw ra2 = load_row<kMode>(A, tid, K, (kt + 2) * GTK);
+    const RowRaw rb2 = load_row<kMode>(B, tid, K, (kt + 2) * GTK);
     const _Float16* Acur = &As[buf][arow][kof];
     const _Float16* Bcur = &Bs[buf][brow][kof];
     _Float16* An = &As[buf ^ 1][tid][0];
     _Float16* Bn = &Bs[buf ^ 1][tid][0];
-    f16x8 a[4], b[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) a[i] = *(const f16x8*)(Acur + i * 32 * GLD);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) b[j] = *(const f16x8*)(Bcur + j * 32 * GLD);
     substep<0>(acc, a, b, Acur, Bcur, ra, rb, An, Bn);
     substep<1>(acc, a, b, Acur, Bcur, ra, rb, An, Bn);
     substep<2>(acc, a, b, Acur, Bcur, ra, rb, An, Bn);
-    substep<3>(acc, a, b, Acur, Bcur, ra, rb, An, Bn);
+    substep_last(acc, a, b, &As[buf ^ 1][arow][kof], &Bs[buf ^ 1][brow][kof], ra, rb, An, Bn);
     ra = ra2;
     rb = rb2;
-    __syncthreads();
-  };
-  if (kMode == kGroup) {                           // nk % 4 == 0
-    for (int64_t kt = 0; kt < nk; kt += 4) {
-      iteration(kt, std::integral_constant<int, 0>());
-      iteration(kt + 1, std::integral_constant<int, 1>());
-      iteration(kt + 2, std::integral_constant<int, 2>());
-      iteration(kt + 3, std::integral_constant<int, 3>());
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int64_t row = m0 + wm * 128 + i * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+        const int64_t col = n0 + wn * 128 + j * 32 + (lane & 31);
+        if (row < m_end && col < n_end) C[row * ldc + col] = acc[i][j][e] * gab;
+      }
+}
+
+// ------------------------------------------------------------ K % 256 == 0: raw codes through LDS
+// The raw codes of a K step reach LDS by buffer-to-LDS loads, which hold no
+// VGPRs and skip the register return path, two steps ahead; each thread
+// then reads its A and B rows' 32 code bytes once per step from LDS.  The
+// scale words of 4 steps come in one 16-byte register load per row.  The f16
+// tiles drop the row padding: 16-byte chunk c of row r sits at chunk
+// position c ^ ((r >> 1) & 7), which keeps the fragment reads and the
+// dequantized writes (16 consecutive rows per LDS cycle) on distinct banks.
+// Raw rows are 32 bytes; half h of row r sits at half position h ^ ((r >> 3) & 1).
+struct GemmDmaSmem {
+  _Float16 af[2][GTM * GTK];
+  _Float16 bf[2][GTN * GTK];
+  uint8_t ar[2][GTM * 32];
+  uint8_t br[2][GTN * 32];
+};
+static_assert(sizeof(GemmDmaSmem) <= 160 * 1024, "LDS budget");
+
+typedef __attribute__((address_space(3))) void gemm_lds_t;
+
+__device__ __forceinline__ int raw_swz(int r) { return (r >> 3) & 1; }
+
+// Wave w's share of one operand's raw codes of the step at k0: rows
+// [64 w, 64 w + 64), 32 rows (1 KiB) per instruction.
+__device__ __forceinline__ void dma_codes(const Operand& o, int wave, int lane, int64_t k0, uint8_t* raw) {
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int r0 = 64 * wave + 32 * j, r = r0 + (lane >> 1);
+    const int h = (lane & 1) ^ raw_swz(r);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(o.q, (gemm_lds_t*)(raw + r0 * 32), 16,
+                                             (uint32_t)r * o.qrow + (uint32_t)(k0 / 2) + 16u * h, 0, 0, 0);
+  }
+}
+
+// Row r's 32 code bytes of a step from LDS (both halves, in order).
+__device__ __forceinline__ void read_codes(const uint8_t* raw, int r, RowRaw& out) {
+  const int sz = raw_swz(r);
+  out.c01 = *(const u32x4*)(raw + r * 32 + 16 * sz);
+  out.c23 = *(const u32x4*)(raw + r * 32 + 16 * (sz ^ 1));
+}
+
+__device__ __forceinline__ void wait_vm0() {
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_waitcnt((0x7 << 4) | (0xF << 8));   // vmcnt(0)
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// Block b of a row, dequantized as in deq_block_to_lds, written to the
+// swizzled row at dst (sw = the row's swizzle).
+template <int b>
+__device__ __forceinline__ void deq_block_sw(const RowRaw& r, _Float16* dst, int sw) {
+  const float s = __builtin_amdgcn_cvt_f32_fp8((int)r.s, b);
+  const float mfs = __uint_as_float((__float_as_uint(s) & 0x007fffffu) | 0x3f800000u);
+  const _Float16 mh = (_Float16)mfs;
+  const f16x2 mf = {mh, mh};
+  const uint32_t cx = b == 0 ? r.c01.x : b == 1 ? r.c01.z : b == 2 ? r.c23.x : r.c23.z;
+  const uint32_t cy = b == 0 ? r.c01.y : b == 1 ? r.c01.w : b == 2 ? r.c23.y : r.c23.w;
+  f16x8 lo, hi;
+  f16x2 p;
+  p = deq_pair<0>(cx, s, mf); lo[0] = p.x; lo[1] = p.y;
+  p = deq_pair<1>(cx, s, mf); lo[2] = p.x; lo[3] = p.y;
+  p = deq_pair<2>(cx, s, mf); lo[4] = p.x; lo[5] = p.y;
+  p = deq_pair<3>(cx, s, mf); lo[6] = p.x; lo[7] = p.y;
+  p = deq_pair<0>(cy, s, mf); hi[0] = p.x; hi[1] = p.y;
+  p = deq_pair<1>(cy, s, mf); hi[2] = p.x; hi[3] = p.y;
+  p = deq_pair<2>(cy, s, mf); hi[4] = p.x; hi[5] = p.y;
+  p = deq_pair<3>(cy, s, mf); hi[6] = p.x; hi[7] = p.y;
+  *(f16x8*)(dst + 8 * ((2 * b) ^ sw)) = lo;
+  *(f16x8*)(dst + 8 * ((2 * b + 1) ^ sw)) = hi;
+}
+
+// Fragments of substep kk: rows fr + 32 i of a swizzled tile (fsw = their
+// common swizzle, h = the lane's K half).
+__device__ __forceinline__ void read_frags(const _Float16* tile, int fr, int kk, int h, int fsw, f16x8 (&f)[4]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) f[i] = *(const f16x8*)(tile + (fr + 32 * i) * GTK + 8 * ((2 * kk + h) ^ fsw));
+}
+
+// Substeps 0..2 of the DMA path: 16 MFMAs on a/b, the next substep's
+// fragments, and block kk of the next step dequantized into the other tile.
+template <int kk>
+__device__ __forceinline__ void dma_substep(f32x16 (&acc)[4][4], f16x8 (&a)[4], f16x8 (&b)[4], const _Float16* At,
+                                            const _Float16* Bt, int arow, int brow, int h, int fsw, const RowRaw& ra,
+                                            const RowRaw& rb, _Float16* An, _Float16* Bn, int wsw) {
+  __builtin_amdgcn_sched_barrier(0);
+  f16x8 an[4], bn[4];
+  read_frags(At, arow, kk + 1, h, fsw, an);
+  read_frags(Bt, brow, kk + 1, h, fsw, bn);
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], b[j], acc[i][j], 0, 0, 0);
+  deq_block_sw<kk>(ra, An, wsw);
+  deq_block_sw<kk>(rb, Bn, wsw);
+#pragma unroll
+  for (int m = 0; m < 16; ++m) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);     // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);     // VALU
+    if (m < 8) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
+    else if (m < 12) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // DS write
+  }
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) { a[i] = an[i]; b[i] = bn[i]; }
+}
+
+__device__ __forceinline__ void gemm_tile_dma(const uint8_t* __restrict__ aq, const uint8_t* __restrict__ asf,
+                                              int64_t m0, int64_t m_end, const uint8_t* __restrict__ bq,
+                                              const uint8_t* __restrict__ bsf, int64_t n0, int64_t n_end, int64_t K,
+                                              float gab, float* __restrict__ C, int64_t ldc, GemmDmaSmem& sm) {
+  const int tid = threadIdx.x;
+  const int wave = wave_id(), lane = tid & 63;   // wave index in an SGPR (the DMA's LDS base)
+  const int wm = wave >> 1, wn = wave & 1;       // 2 x 2 waves of 128 x 128
+  const Operand A = make_operand(aq, asf, m0, m_end, K), B = make_operand(bq, bsf, n0, n_end, K);
+
+  f32x16 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+
+  // Iteration kt contracts step kt (f16 tile kt % 2), dequantizes step kt+1
+  // from its raw codes (read from LDS at the end of iteration kt-1) into
+  // the other tile, and has the raw codes of step kt+2 loading into raw
+  // buffer kt % 2.  Each iteration ends with vmcnt(0) and a barrier, after
+  // which step kt+2's raw codes are visible to every wave.
+  const int64_t nk = K / GTK;                      // K % 256 == 0, so nk % 4 == 0
+  u32x4 sa_cur = load_scale_group(A, tid, K, 0), sb_cur = load_scale_group(B, tid, K, 0);
+  u32x4 sa_nxt = load_scale_group(A, tid, K, 1), sb_nxt = load_scale_group(B, tid, K, 1);
+  dma_codes(A, wave, lane, 0, sm.ar[0]);
+  dma_codes(B, wave, lane, 0, sm.br[0]);
+  dma_codes(A, wave, lane, GTK, sm.ar[1]);
+  dma_codes(B, wave, lane, GTK, sm.br[1]);
+  wait_vm0();
+  __syncthreads();
+  const int wsw = (tid >> 1) & 7;                  // swizzle of the row this thread dequantizes
+  RowRaw ra, rb;
+  read_codes(sm.ar[0], tid, ra);
+  read_codes(sm.br[0], tid, rb);
+  ra.s = sa_cur.x;
+  rb.s = sb_cur.x;
+  deq_block_sw<0>(ra, &sm.af[0][tid * GTK], wsw);
+  deq_block_sw<1>(ra, &sm.af[0][tid * GTK], wsw);
+  deq_block_sw<2>(ra, &sm.af[0][tid * GTK], wsw);
+  deq_block_sw<3>(ra, &sm.af[0][tid * GTK], wsw);
+  deq_block_sw<0>(rb, &sm.bf[0][tid * GTK], wsw);
+  deq_block_sw<1>(rb, &sm.bf[0][tid * GTK], wsw);
+  deq_block_sw<2>(rb, &sm.bf[0][tid * GTK], wsw);
+  deq_block_sw<3>(rb, &sm.bf[0][tid * GTK], wsw);
+  read_codes(sm.ar[1], tid, ra);
+  read_codes(sm.br[1], tid, rb);
+  __syncthreads();                                 // tile 0 complete; raw buffer 0 free
+  const int arow = wm * 128 + (lane & 31), brow = wn * 128 + (lane & 31), h = lane >> 5;
+  const int fsw = ((lane & 31) >> 1) & 7;          // swizzle of every fragment row of this lane
+  f16x8 a[4], b[4];
+  read_frags(sm.af[0], arow, 0, h, fsw, a);
+  read_frags(sm.bf[0], brow, 0, h, fsw, b);
+  auto iteration = [&](int64_t kt, auto U) {
+    constexpr int u = decltype(U)::value;          // kt % 4
+    const int buf = (int)(kt & 1);
+    if (kt + 2 < nk) {
+      dma_codes(A, wave, lane, (kt + 2) * GTK, sm.ar[buf]);
+      dma_codes(B, wave, lane, (kt + 2) * GTK, sm.br[buf]);
     }
-  } else {
-    for (int64_t kt = 0; kt < nk; ++kt) iteration(kt, std::integral_constant<int, 0>());
+    if ((u + 1) % 4 == 0) {                        // step kt+1 opens group (kt+1)/4
+      sa_cur = sa_nxt;
+      sb_cur = sb_nxt;
+      sa_nxt = load_scale_group(A, tid, K, (kt + 1) / 4 + 1);
+      sb_nxt = load_scale_group(B, tid, K, (kt + 1) / 4 + 1);
+    }
+    ra.s = word<(u + 1) % 4>(sa_cur);
+    rb.s = word<(u + 1) % 4>(sb_cur);
+    const _Float16* At = sm.af[buf];
+    const _Float16* Bt = sm.bf[buf];
+    _Float16* An = &sm.af[buf ^ 1][tid * GTK];
+    _Float16* Bn = &sm.bf[buf ^ 1][tid * GTK];
+    dma_substep<0>(acc, a, b, At, Bt, arow, brow, h, fsw, ra, rb, An, Bn, wsw);
+    dma_substep<1>(acc, a, b, At, Bt, arow, brow, h, fsw, ra, rb, An, Bn, wsw);
+    dma_substep<2>(acc, a, b, At, Bt, arow, brow, h, fsw, ra, rb, An, Bn, wsw);
+    // last substep: 8 MFMAs with block 3's dequantization, then the barrier,
+    // then the next step's first fragments and step kt+2's raw codes are
+    // read under the other 8 MFMAs
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], b[j], acc[i][j], 0, 0, 0);
+    deq_block_sw<3>(ra, An, wsw);
+    deq_block_sw<3>(rb, Bn, wsw);
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);   // VALU
+      if (m >= 4) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // DS write
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    wait_vm0();
+    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+    f16x8 an[4], bn[4];
+    read_frags(sm.af[buf ^ 1], arow, 0, h, fsw, an);
+    read_frags(sm.bf[buf ^ 1], brow, 0, h, fsw, bn);
+    read_codes(sm.ar[buf], tid, ra);
+    read_codes(sm.br[buf], tid, rb);
+#pragma unroll
+    for (int i = 2; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], b[j], acc[i][j], 0, 0, 0);
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // DS read
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+    }
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { a[i] = an[i]; b[i] = bn[i]; }
+  };
+  for (int64_t kt = 0; kt < nk; kt += 4) {
+    iteration(kt, std::integral_constant<int, 0>());
+    iteration(kt + 1, std::integral_constant<int, 1>());
+    iteration(kt + 2, std::integral_constant<int, 2>());
+    iteration(kt + 3, std::integral_constant<int, 3>());
   }
 #pragma unroll
   for (int i = 0; i < 4; ++i)
@@ -300,11 +549,16 @@ __global__ void __launch_bounds__(GThreads) gemm_kernel(const uint8_t* __restric
                                                         const float* __restrict__ ag, const uint8_t* __restrict__ bq,
                                                         const uint8_t* __restrict__ bsf, const float* __restrict__ bg,
                                                         int64_t M, int64_t N, int64_t K, float* __restrict__ C) {
-  __shared__ __attribute__((aligned(16))) _Float16 As[2][GTM][GLD];
-  __shared__ __attribute__((aligned(16))) _Float16 Bs[2][GTN][GLD];
   const int64_t tile = xcd_tile((int64_t)blockIdx.y * gridDim.x + blockIdx.x, (int64_t)gridDim.x * gridDim.y);
   const int64_t m0 = tile / gridDim.x * GTM, n0 = tile % gridDim.x * GTN;
-  gemm_tile<kMode>(aq, asf, m0, M, bq, bsf, n0, N, K, ag[0] * bg[0], C, N, As, Bs);
+  if constexpr (kMode == kGroup) {
+    __shared__ __attribute__((aligned(16))) GemmDmaSmem sm;
+    gemm_tile_dma(aq, asf, m0, M, bq, bsf, n0, N, K, ag[0] * bg[0], C, N, sm);
+  } else {
+    __shared__ __attribute__((aligned(16))) _Float16 As[2][GTM][GLD];
+    __shared__ __attribute__((aligned(16))) _Float16 Bs[2][GTN][GLD];
+    gemm_tile<kMode>(aq, asf, m0, M, bq, bsf, n0, N, K, ag[0] * bg[0], C, N, As, Bs);
+  }
 }
 
 // Grouped GEMM: rows of A are grouped by expert, rows [off[e], off[e+1])
@@ -317,8 +571,6 @@ __global__ void __launch_bounds__(GThreads) grouped_gemm_kernel(
     const uint8_t* __restrict__ aq, const uint8_t* __restrict__ asf, const float* __restrict__ ag,
     const uint8_t* __restrict__ bq, const uint8_t* __restrict__ bsf, const float* __restrict__ bg,
     const int32_t* __restrict__ off, int experts, int64_t M, int64_t N, int64_t K, float* __restrict__ C) {
-  __shared__ __attribute__((aligned(16))) _Float16 As[2][GTM][GLD];
-  __shared__ __attribute__((aligned(16))) _Float16 Bs[2][GTN][GLD];
   int64_t tile = blockIdx.y;
   int e = 0;
   int64_t lo = 0, hi = 0;
@@ -332,7 +584,14 @@ __global__ void __launch_bounds__(GThreads) grouped_gemm_kernel(
   if (e == experts) return;                            // past the last tile: no work
   const int64_t m0 = lo + tile * GTM, n0 = (int64_t)blockIdx.x * GTN;
   const int64_t wq = N * (K / 2), ws = N * (K / 16);   // bytes per expert weight, scales
-  gemm_tile<kMode>(aq, asf, m0, hi, bq + e * wq, bsf + e * ws, n0, N, K, ag[0] * bg[e], C, N, As, Bs);
+  if constexpr (kMode == kGroup) {
+    __shared__ __attribute__((aligned(16))) GemmDmaSmem sm;
+    gemm_tile_dma(aq, asf, m0, hi, bq + e * wq, bsf + e * ws, n0, N, K, ag[0] * bg[e], C, N, sm);
+  } else {
+    __shared__ __attribute__((aligned(16))) _Float16 As[2][GTM][GLD];
+    __shared__ __attribute__((aligned(16))) _Float16 Bs[2][GTN][GLD];
+    gemm_tile<kMode>(aq, asf, m0, hi, bq + e * wq, bsf + e * ws, n0, N, K, ag[0] * bg[e], C, N, As, Bs);
+  }
 }
 
 }  // namespace nvfp4
