@@ -304,36 +304,50 @@ __device__ __forceinline__ void gemm_tile(const uint8_t* __restrict__ aq, const 
 }
 
 // ------------------------------------------------------------ K % 256 == 0: raw codes through LDS
-// The raw codes of a K step reach LDS by buffer-to-LDS loads, which hold no
-// VGPRs and skip the register return path, two steps ahead; each thread
-// then reads its row's 32 code bytes once per step from LDS.  The scale
-// words of 4 steps come in one 16-byte register load per row.  The f16
-// tiles drop the row padding: 16-byte chunk c of row r sits at chunk
-// position c ^ ((r >> 1) & 7), which keeps the fragment reads and the
-// dequantized writes (16 consecutive rows per LDS cycle) on distinct banks.
-// Raw rows are 32 bytes; half h of row r sits at half position h ^ ((r >> 3) & 1).
-//
 // 8 waves of 128 x 64 (2 x 4) run two waves per SIMD, so one wave's
-// dequantization, LDS traffic and barrier wait overlap the other's MFMAs
-// (about 5% faster than 4 waves of 128 x 128, with bit-identical results).
+// dequantization, LDS traffic and barrier wait overlap the other's MFMAs.
 // Thread t dequantizes one row: A row t for t < 256, else B row t - 256.
+//
+// The raw codes of a K step reach LDS by buffer-to-LDS loads, which hold no
+// VGPRs and skip the register return path; the scale words of 4 steps come
+// in one 16-byte register load per row.  Each wave loads exactly the raw rows
+// its own threads dequantize (thread t's 32 bytes at raw + 32 t), so one raw
+// buffer suffices: a wave's next load is issued only after its own reads of
+// the buffer have returned, with no workgroup barrier involved.  Half h of
+// raw row t sits at half position h ^ ((t >> 2 ^ t >> 3) & 1), which puts 8
+// (and 16) consecutive rows' reads on distinct banks.  The f16 tiles keep
+// the 72-half row padding of gemm_tile (conflict-free reads and writes).
+constexpr int GThreads8 = 512;
+
 struct GemmDmaSmem {
-  _Float16 af[2][GTM * GTK];
-  _Float16 bf[2][GTN * GTK];
-  uint8_t ar[2][GTM * 32];
-  uint8_t br[2][GTN * 32];
+  _Float16 af[2][GTM][GLD];
+  _Float16 bf[2][GTN][GLD];
+  uint8_t raw[2 * GTM * 32];
 };
 static_assert(sizeof(GemmDmaSmem) <= 160 * 1024, "LDS budget");
 
 typedef __attribute__((address_space(3))) void gemm_lds_t;
 
-__device__ __forceinline__ int raw_swz(int r) { return (r >> 3) & 1; }
+__device__ __forceinline__ int raw_swz(int t) { return ((t >> 2) ^ (t >> 3)) & 1; }
 
-// Row r's 32 code bytes of a step from LDS (both halves, in order).
-__device__ __forceinline__ void read_codes(const uint8_t* raw, int r, RowRaw& out) {
-  const int sz = raw_swz(r);
-  out.c01 = *(const u32x4*)(raw + r * 32 + 16 * sz);
-  out.c23 = *(const u32x4*)(raw + r * 32 + 16 * (sz ^ 1));
+// Wave w's raw rows of the step at k0: rows t = 64 w .. 64 w + 63 of the raw
+// buffer (operand rows t & 255 of A for w < 4, of B otherwise), 32 rows
+// (1 KiB) per instruction.
+__device__ __forceinline__ void dma_codes8(const Operand& o, int wave, int lane, int64_t k0, uint8_t* raw) {
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int t0 = 64 * wave + 32 * j, t = t0 + (lane >> 1);
+    const int h = (lane & 1) ^ raw_swz(t);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(o.q, (gemm_lds_t*)(raw + t0 * 32), 16,
+                                             (uint32_t)(t & 255) * o.qrow + (uint32_t)(k0 / 2) + 16u * h, 0, 0, 0);
+  }
+}
+
+// Raw row t's 32 code bytes from LDS (both halves, in order).
+__device__ __forceinline__ void read_codes(const uint8_t* raw, int t, RowRaw& out) {
+  const int sz = raw_swz(t);
+  out.c01 = *(const u32x4*)(raw + t * 32 + 16 * sz);
+  out.c23 = *(const u32x4*)(raw + t * 32 + 16 * (sz ^ 1));
 }
 
 __device__ __forceinline__ void wait_vm0() {
@@ -342,56 +356,26 @@ __device__ __forceinline__ void wait_vm0() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
-// Block b of a row, dequantized as in deq_block_to_lds, written to the
-// swizzled row at dst (sw = the row's swizzle).
-template <int b>
-__device__ __forceinline__ void deq_block_sw(const RowRaw& r, _Float16* dst, int sw) {
-  const float s = __builtin_amdgcn_cvt_f32_fp8((int)r.s, b);
-  const float mfs = __uint_as_float((__float_as_uint(s) & 0x007fffffu) | 0x3f800000u);
-  const _Float16 mh = (_Float16)mfs;
-  const f16x2 mf = {mh, mh};
-  const uint32_t cx = b == 0 ? r.c01.x : b == 1 ? r.c01.z : b == 2 ? r.c23.x : r.c23.z;
-  const uint32_t cy = b == 0 ? r.c01.y : b == 1 ? r.c01.w : b == 2 ? r.c23.y : r.c23.w;
-  f16x8 lo, hi;
-  f16x2 p;
-  p = deq_pair<0>(cx, s, mf); lo[0] = p.x; lo[1] = p.y;
-  p = deq_pair<1>(cx, s, mf); lo[2] = p.x; lo[3] = p.y;
-  p = deq_pair<2>(cx, s, mf); lo[4] = p.x; lo[5] = p.y;
-  p = deq_pair<3>(cx, s, mf); lo[6] = p.x; lo[7] = p.y;
-  p = deq_pair<0>(cy, s, mf); hi[0] = p.x; hi[1] = p.y;
-  p = deq_pair<1>(cy, s, mf); hi[2] = p.x; hi[3] = p.y;
-  p = deq_pair<2>(cy, s, mf); hi[4] = p.x; hi[5] = p.y;
-  p = deq_pair<3>(cy, s, mf); hi[6] = p.x; hi[7] = p.y;
-  *(f16x8*)(dst + 8 * ((2 * b) ^ sw)) = lo;
-  *(f16x8*)(dst + 8 * ((2 * b + 1) ^ sw)) = hi;
-}
-
-constexpr int GThreads8 = 512;
-
-// Wave w's share of one operand's raw codes of the step at k0: rows
-// [32 w, 32 w + 32), one 1 KiB instruction.
-__device__ __forceinline__ void dma_codes8(const Operand& o, int wave, int lane, int64_t k0, uint8_t* raw) {
-  const int r0 = 32 * wave, r = r0 + (lane >> 1);
-  const int h = (lane & 1) ^ raw_swz(r);
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(o.q, (gemm_lds_t*)(raw + r0 * 32), 16,
-                                           (uint32_t)r * o.qrow + (uint32_t)(k0 / 2) + 16u * h, 0, 0, 0);
+__device__ __forceinline__ void wait_lgkm0() {
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_waitcnt((0x7 << 4) | 0x3F | (0x3 << 14));   // lgkmcnt(0), vmcnt at its maximum
+  __builtin_amdgcn_sched_barrier(0);
 }
 
 template <int kk>
-__device__ __forceinline__ void dma8_substep(f32x16 (&acc)[4][2], f16x8 (&a)[4], f16x8 (&b)[2], const _Float16* At,
-                                             const _Float16* Bt, int arow, int brow, int h, int fsw, const RowRaw& rr,
-                                             _Float16* Dn, int wsw) {
+__device__ __forceinline__ void dma8_substep(f32x16 (&acc)[4][2], f16x8 (&a)[4], f16x8 (&b)[2], const _Float16* Acur,
+                                             const _Float16* Bcur, const RowRaw& rr, _Float16* Dn) {
   __builtin_amdgcn_sched_barrier(0);
   f16x8 an[4], bn[2];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) an[i] = *(const f16x8*)(At + (arow + 32 * i) * GTK + 8 * ((2 * (kk + 1) + h) ^ fsw));
+  for (int i = 0; i < 4; ++i) an[i] = *(const f16x8*)(Acur + i * 32 * GLD + 16 * (kk + 1));
 #pragma unroll
-  for (int j = 0; j < 2; ++j) bn[j] = *(const f16x8*)(Bt + (brow + 32 * j) * GTK + 8 * ((2 * (kk + 1) + h) ^ fsw));
+  for (int j = 0; j < 2; ++j) bn[j] = *(const f16x8*)(Bcur + j * 32 * GLD + 16 * (kk + 1));
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], b[j], acc[i][j], 0, 0, 0);
-  deq_block_sw<kk>(rr, Dn, wsw);
+  deq_block_to_lds<kk>(rr, Dn);
 #pragma unroll
   for (int m = 0; m < 8; ++m) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);     // MFMA
@@ -406,15 +390,20 @@ __device__ __forceinline__ void dma8_substep(f32x16 (&acc)[4][2], f16x8 (&a)[4],
   for (int j = 0; j < 2; ++j) b[j] = bn[j];
 }
 
+// Iteration kt contracts step kt (tile kt % 2), dequantizes step kt+1 from
+// its raw codes (in registers since the end of iteration kt-1) into the
+// other tile, and loads step kt+2's raw codes (issued after the first
+// substep, when the wave's reads of the raw buffer have returned; waited
+// for at the end of the iteration and read back after its barrier).
 __device__ __forceinline__ void gemm_tile_dma8(const uint8_t* __restrict__ aq, const uint8_t* __restrict__ asf,
                                                int64_t m0, int64_t m_end, const uint8_t* __restrict__ bq,
                                                const uint8_t* __restrict__ bsf, int64_t n0, int64_t n_end, int64_t K,
                                                float gab, float* __restrict__ C, int64_t ldc, GemmDmaSmem& sm) {
   const int tid = threadIdx.x;
-  const int wave = wave_id(), lane = tid & 63;
-  const int wm = wave >> 2, wn = wave & 3;       // 2 x 4 waves of 128 x 64
+  const int wave = wave_id(), lane = tid & 63;    // wave index in an SGPR (the loads' LDS base)
+  const int wm = wave >> 2, wn = wave & 3;        // 2 x 4 waves of 128 x 64
   const Operand A = make_operand(aq, asf, m0, m_end, K), B = make_operand(bq, bsf, n0, n_end, K);
-  const bool isb = wave >= 4;                     // this thread dequantizes a B row
+  const bool isb = wave >= 4;                     // this wave dequantizes (and loads) B rows
   const Operand& X = isb ? B : A;
   const int row = tid & 255;
 
@@ -428,57 +417,54 @@ __device__ __forceinline__ void gemm_tile_dma8(const uint8_t* __restrict__ aq, c
 
   const int64_t nk = K / GTK;                      // K % 256 == 0, so nk % 4 == 0
   u32x4 s_cur = load_scale_group(X, row, K, 0), s_nxt = load_scale_group(X, row, K, 1);
-  dma_codes8(A, wave, lane, 0, sm.ar[0]);
-  dma_codes8(B, wave, lane, 0, sm.br[0]);
-  dma_codes8(A, wave, lane, GTK, sm.ar[1]);
-  dma_codes8(B, wave, lane, GTK, sm.br[1]);
-  wait_vm0();
-  __syncthreads();
-  const int wsw = (row >> 1) & 7;
-  uint8_t* const xr0 = isb ? sm.br[0] : sm.ar[0];
-  uint8_t* const xr1 = isb ? sm.br[1] : sm.ar[1];
-  _Float16* const xf0 = (isb ? sm.bf[0] : sm.af[0]) + row * GTK;
-  _Float16* const xf1 = (isb ? sm.bf[1] : sm.af[1]) + row * GTK;
+  _Float16* const x0 = isb ? &sm.bf[0][row][0] : &sm.af[0][row][0];
+  _Float16* const x1 = isb ? &sm.bf[1][row][0] : &sm.af[1][row][0];
   RowRaw rr;
-  read_codes(xr0, row, rr);
+  dma_codes8(X, wave, lane, 0, sm.raw);
+  wait_vm0();
+  read_codes(sm.raw, tid, rr);
   rr.s = s_cur.x;
-  deq_block_sw<0>(rr, xf0, wsw);
-  deq_block_sw<1>(rr, xf0, wsw);
-  deq_block_sw<2>(rr, xf0, wsw);
-  deq_block_sw<3>(rr, xf0, wsw);
-  read_codes(xr1, row, rr);
-  __syncthreads();
-  const int arow = wm * 128 + (lane & 31), brow = wn * 64 + (lane & 31), h = lane >> 5;
-  const int fsw = ((lane & 31) >> 1) & 7;
+  deq_block_to_lds<0>(rr, x0);
+  deq_block_to_lds<1>(rr, x0);
+  deq_block_to_lds<2>(rr, x0);
+  deq_block_to_lds<3>(rr, x0);
+  dma_codes8(X, wave, lane, GTK, sm.raw);          // after this wave's reads of step 0 (used above)
+  wait_vm0();
+  read_codes(sm.raw, tid, rr);
+  __syncthreads();                                 // tile 0 complete
+  const int arow = wm * 128 + (lane & 31), brow = wn * 64 + (lane & 31), kof = 8 * (lane >> 5);
   f16x8 a[4], b[2];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) a[i] = *(const f16x8*)(sm.af[0] + (arow + 32 * i) * GTK + 8 * (h ^ fsw));
+  for (int i = 0; i < 4; ++i) a[i] = *(const f16x8*)(&sm.af[0][arow][kof] + i * 32 * GLD);
 #pragma unroll
-  for (int j = 0; j < 2; ++j) b[j] = *(const f16x8*)(sm.bf[0] + (brow + 32 * j) * GTK + 8 * (h ^ fsw));
+  for (int j = 0; j < 2; ++j) b[j] = *(const f16x8*)(&sm.bf[0][brow][kof] + j * 32 * GLD);
   auto iteration = [&](int64_t kt, auto U) {
     constexpr int u = decltype(U)::value;          // kt % 4
     const int buf = (int)(kt & 1);
-    if (kt + 2 < nk) {
-      dma_codes8(A, wave, lane, (kt + 2) * GTK, sm.ar[buf]);
-      dma_codes8(B, wave, lane, (kt + 2) * GTK, sm.br[buf]);
-    }
-    if ((u + 1) % 4 == 0) {
+    if ((u + 1) % 4 == 0) {                        // step kt+1 opens group (kt+1)/4
       s_cur = s_nxt;
       s_nxt = load_scale_group(X, row, K, (kt + 1) / 4 + 1);
     }
     rr.s = word<(u + 1) % 4>(s_cur);
-    const _Float16* At = sm.af[buf];
-    const _Float16* Bt = sm.bf[buf];
-    _Float16* Dn = buf ? xf0 : xf1;
-    dma8_substep<0>(acc, a, b, At, Bt, arow, brow, h, fsw, rr, Dn, wsw);
-    dma8_substep<1>(acc, a, b, At, Bt, arow, brow, h, fsw, rr, Dn, wsw);
-    dma8_substep<2>(acc, a, b, At, Bt, arow, brow, h, fsw, rr, Dn, wsw);
+    const _Float16* Acur = &sm.af[buf][arow][kof];
+    const _Float16* Bcur = &sm.bf[buf][brow][kof];
+    _Float16* Dn = buf ? x0 : x1;
+    dma8_substep<0>(acc, a, b, Acur, Bcur, rr, Dn);
+    if (kt + 2 < nk) {
+      wait_lgkm0();                                // this wave's reads of the raw buffer have returned
+      dma_codes8(X, wave, lane, (kt + 2) * GTK, sm.raw);
+    }
+    dma8_substep<1>(acc, a, b, Acur, Bcur, rr, Dn);
+    dma8_substep<2>(acc, a, b, Acur, Bcur, rr, Dn);
+    // last substep: 4 MFMAs with block 3's dequantization, the barrier, then
+    // the next step's first fragments and step kt+2's raw codes are read
+    // under the other 4 MFMAs
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
       for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], b[j], acc[i][j], 0, 0, 0);
-    deq_block_sw<3>(rr, Dn, wsw);
+    deq_block_to_lds<3>(rr, Dn);
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
@@ -490,13 +476,11 @@ __device__ __forceinline__ void gemm_tile_dma8(const uint8_t* __restrict__ aq, c
     __syncthreads();
     __builtin_amdgcn_sched_barrier(0);
     f16x8 an[4], bn[2];
-    const _Float16* Af = sm.af[buf ^ 1];
-    const _Float16* Bf = sm.bf[buf ^ 1];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) an[i] = *(const f16x8*)(Af + (arow + 32 * i) * GTK + 8 * (h ^ fsw));
+    for (int i = 0; i < 4; ++i) an[i] = *(const f16x8*)(&sm.af[buf ^ 1][arow][kof] + i * 32 * GLD);
 #pragma unroll
-    for (int j = 0; j < 2; ++j) bn[j] = *(const f16x8*)(Bf + (brow + 32 * j) * GTK + 8 * (h ^ fsw));
-    read_codes(isb ? sm.br[buf] : sm.ar[buf], row, rr);
+    for (int j = 0; j < 2; ++j) bn[j] = *(const f16x8*)(&sm.bf[buf ^ 1][brow][kof] + j * 32 * GLD);
+    read_codes(sm.raw, tid, rr);
 #pragma unroll
     for (int i = 2; i < 4; ++i)
 #pragma unroll
