@@ -21,7 +21,8 @@ def _cache(L, H, D, cap, seed):
     return nv.KVCache(L, H, D, cap, kg, vg, device="cuda"), np_(kg), np_(vg)
 
 
-@pytest.mark.parametrize("D,grp", [(128, 4), (64, 2), (32, 1), (256, 8), (16, 4)])
+@pytest.mark.parametrize("D,grp", [(128, 4), (64, 2), (32, 1), (256, 8), (16, 4), (128, 16), (64, 3), (256, 5),
+                                   (128, 1)])
 def test_append_read_qk_small(D, grp):
     print("case: kv small D", D, "grp", grp, flush=True)
     L, H, cap = 3, 2, 300
@@ -125,6 +126,28 @@ def test_decode_attention_query_magnitudes(k):
     kq, ks, vq, vs = (np_(t) for t in (cache.k, cache.k_sf, cache.v, cache.v_sf))
     want = oracle.decode_attention_f64(bits(qv), kq, ks, kg, vq, vs, vg, scale)
     err = rel_frobenius(np_(out), want)
+    assert err <= QK_TOL, f"rel Frobenius {err:.3e}"
+
+
+@pytest.mark.parametrize("k", [-100, -20, 0, 30, 100])
+def test_decode_qk_query_magnitudes(k):
+    """Queries scaled by 2^k and a head whose elements span 40 binades: the
+    MFMA decode-QK scales each head by a power of two before rounding q to
+    f16, which keeps the logits within the 1e-5 bar at any magnitude."""
+    print("case: kv decode-QK q magnitude 2^", k, flush=True)
+    L, H, D, grp, cap = 1, 2, 128, 4, 200
+    cache, kg, vg = _cache(L, H, D, cap, 2000 + k)
+    gen = torch.Generator().manual_seed(99 + k)
+    kk = (torch.randn((L, cap, H, D), generator=gen) * 2).to(torch.bfloat16)
+    cache.append(0, kk.cuda(), kk.cuda())
+    qf = torch.randn((L, H * grp, D), generator=gen) * 2.0 ** k
+    qf[0, 1] *= torch.exp2(torch.randint(-40, 1, (D,), generator=gen).float())   # mixed binades in one head
+    qv = qf.to(torch.bfloat16)
+    logits = cache.decode_qk(qv.cuda(), 197)
+    torch.cuda.synchronize()
+    kq, ks = np_(cache.k), np_(cache.k_sf)
+    want = oracle.decode_qk_f64(bits(qv), kq[:, :, :197], ks[:, :, :197], kg)
+    err = rel_frobenius(np_(logits), want)
     assert err <= QK_TOL, f"rel Frobenius {err:.3e}"
 
 
