@@ -70,11 +70,11 @@ __device__ __forceinline__ Operand make_operand(const uint8_t* q, const uint8_t*
 
 constexpr uint32_t kOutside = 0x80000000u;  // offset beyond every extent (extents stay below 2^31)
 
-// Operand paths: kRagged (any K % 16 == 0: each block checked on its own)
-// and kStep (K % 64 == 0: a step is wholly inside or outside) load a
-// thread's raw codes and scale bytes into registers; kGroup (K % 256 == 0)
-// stages the raw codes in LDS (gemm_tile_dma8 below).
-constexpr int kRagged = 0, kStep = 1, kGroup = 2;
+// Register operand paths: kRagged (any K % 16 == 0: each block checked on
+// its own) and kStep (K % 64 == 0: a step is wholly inside or outside) load
+// a thread's raw codes and scale bytes into registers.  K % 256 == 0 stages
+// the raw codes in LDS instead (gemm_tile_dma8 below).
+constexpr int kRagged = 0, kStep = 1;
 
 template <int kMode>
 __device__ __forceinline__ RowRaw load_row(const Operand& o, int lrow, int64_t K, int64_t k0) {
@@ -101,7 +101,7 @@ __device__ __forceinline__ RowRaw load_row(const Operand& o, int lrow, int64_t K
   return r;
 }
 
-// Scale words of K steps 4g .. 4g+3 of one row (kGroup; zeros past K): one
+// Scale words of K steps 4g .. 4g+3 of one row (zeros past K): one
 // 16-byte load per 4 steps, so each 128-byte line of scales is fetched from
 // L2 a quarter as often as with a 4-byte load per step.
 __device__ __forceinline__ u32x4 load_scale_group(const Operand& o, int lrow, int64_t K, int64_t g) {
@@ -154,21 +154,20 @@ template <int kk>
 __device__ __forceinline__ void substep(f32x16 (&acc)[4][4], f16x8 (&a)[4], f16x8 (&b)[4], const _Float16* Acur,
                                         const _Float16* Bcur, const RowRaw& ra, const RowRaw& rb, _Float16* Anext,
                                         _Float16* Bnext) {
+  static_assert(kk < 3, "the last substep is substep_last");
   __builtin_amdgcn_sched_barrier(0);               // each substep is its own scheduling region
   f16x8 an[4], bn[4];
-  if (kk < 3) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) an[i] = *(const f16x8*)(Acur + i * 32 * GLD + 16 * (kk + 1));
+  for (int i = 0; i < 4; ++i) an[i] = *(const f16x8*)(Acur + i * 32 * GLD + 16 * (kk + 1));
 #pragma unroll
-    for (int j = 0; j < 4; ++j) bn[j] = *(const f16x8*)(Bcur + j * 32 * GLD + 16 * (kk + 1));
-  }
+  for (int j = 0; j < 4; ++j) bn[j] = *(const f16x8*)(Bcur + j * 32 * GLD + 16 * (kk + 1));
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], b[j], acc[i][j], 0, 0, 0);
   deq_block_to_lds<kk>(ra, Anext);
   deq_block_to_lds<kk>(rb, Bnext);
-  // 16 MFMA; about 40 VALU; 8 LDS reads (kk < 3) and 4 LDS writes
+  // 16 MFMA; about 40 VALU; 8 LDS reads and 4 LDS writes
 #pragma unroll
   for (int m = 0; m < 16; ++m) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);     // MFMA
@@ -177,10 +176,8 @@ __device__ __forceinline__ void substep(f32x16 (&acc)[4][4], f16x8 (&a)[4], f16x
     else if (m < 12) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // DS write
   }
   __builtin_amdgcn_sched_barrier(0);
-  if (kk < 3) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) { a[i] = an[i]; b[i] = bn[i]; }
-  }
+  for (int i = 0; i < 4; ++i) { a[i] = an[i]; b[i] = bn[i]; }
 }
 
 // The last substep of a K step.  Its 16 MFMAs are split around the
