@@ -1,7 +1,7 @@
 """Python binding for libnvfp4, the gfx950 NVFP4 two-level microscaling library.
 
 Argument marshalling only: every step of the computation runs in the HIP
-kernels of libnvfp4.so (built in-tree by __graft_entry__.build()).  PyTorch
+kernels of libnvfp4.so (built in-tree by nvfp4_block_scaled_06_amd/build.py).  PyTorch
 provides device memory and the current HIP stream.  There is no CPU path:
 if the library is missing or the device is not gfx950, calls raise.
 
@@ -75,7 +75,7 @@ def _lib():
     global _L
     if _L is None:
         if not os.path.exists(LIB_PATH):
-            raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() (hipcc, gfx950)")
+            raise ImportError(f"{LIB_PATH} is not built; run python nvfp4_block_scaled_06_amd/build.py (hipcc, gfx950)")
         L = ctypes.CDLL(LIB_PATH)
         for name, (res, args) in _SIGS.items():
             f = getattr(L, name)
