@@ -398,14 +398,43 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t tensor_rsrc(const void* base, 
                                            t < batch ? (int)bytes : 0, kBufferWord3);
 }
 
+// Where a data thread's pieces sit in a tensor: piece p of the thread is
+// the 16-byte half block at byte voff + p * pstride of the input (its 4
+// code bytes at a quarter of that offset, its block's scale byte at a 32nd).
+//  1D: the workgroup's slice is S = kPer * D consecutive half blocks; thread
+//      i's pieces are half blocks w S + p D + i.
+//  2D (16 x 16 tile scales, kPer = 16): thread i of workgroup w owns strip
+//      s = w D + i, the 8 columns [8 c, 8 c + 8) of the 16 rows [16 r,
+//      16 r + 16) with (r, c) = (s / spr, s % spr), spr = cols / 8; piece p
+//      is row 16 r + p.  Strips 2k and 2k+1 (a lane pair) form one tile.
+// Lanes past the tensor get offsets past its extent: their loads read
+// zeros and their stores are dropped.
+struct OnchipMap {
+  int voff;      // bytes: piece 0 of this thread
+  int pstride;   // bytes between consecutive pieces
+};
+
+template <int kPer, bool k2D>
+__device__ __forceinline__ OnchipMap onchip_map(int spr) {
+  OnchipMap m;
+  if (k2D) {
+    const int s = (int)blockIdx.x * kOnchipData + (int)threadIdx.x;
+    const int r = s / spr, c = s - r * spr;
+    m.voff = (r * 16 * spr + c) * 16;
+    m.pstride = spr * 16;
+  } else {
+    m.voff = ((int)blockIdx.x * kPer * kOnchipData + (int)threadIdx.x) * 16;
+    m.pstride = kOnchipData * 16;
+  }
+  return m;
+}
+
 // Issues the buffer-to-LDS loads of pieces [p0, p0 + n) of tensor t.
-template <int kPer>
-__device__ __forceinline__ void onchip_dma(u32x4 (*L)[kOnchipData], __amdgpu_buffer_rsrc_t rs, int p0, int n) {
+__device__ __forceinline__ void onchip_dma(u32x4 (*L)[kOnchipData], __amdgpu_buffer_rsrc_t rs, const OnchipMap& mp,
+                                           int p0, int n) {
   const int w = threadIdx.x >> 6;
-  const int base = (int)blockIdx.x * kPer * kOnchipData * 16;
   for (int p = p0; p < p0 + n; ++p)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)&L[p][w * 64], 16, (int)threadIdx.x * 16,
-                                             base + p * kOnchipData * 16, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)&L[p][w * 64], 16, mp.voff, p * mp.pstride, 0, 0);
 }
 
 template <int kPer>
@@ -423,28 +452,28 @@ __device__ __forceinline__ uint32_t onchip_wave_max(const u32x4 (&v)[kPer]) {
 // kPer-2-2j later loads of t+1, kStores stores and 2j loads of t+2.
 template <int kPer, int kStores>
 __device__ __forceinline__ void onchip_refill(const u32x4* __restrict__ x, int t, int batch, int64_t hb,
-                                              u32x4 (&nxt)[kPer], u32x4 (*L)[kOnchipData]) {
+                                              const OnchipMap& mp, u32x4 (&nxt)[kPer], u32x4 (*L)[kOnchipData]) {
   const __amdgpu_buffer_rsrc_t rs = tensor_rsrc(x, t + 2, batch, hb * 16);
 #pragma unroll
   for (int p = 0; p < kPer; p += 2) {
     wait_vmcnt<kPer - 2 + kStores>();
     lds_read2(&L[p][threadIdx.x], &L[p + 1][threadIdx.x], nxt[p], nxt[p + 1]);
-    onchip_dma<kPer>(L, rs, p, 2);
+    onchip_dma(L, rs, mp, p, 2);
   }
   __builtin_amdgcn_sched_barrier(0);
 }
 
 // One step of a data wave: tensor t (in cur) is encoded once its amax
 // arrives, tensor t+1 moves from LDS into nxt and its maximum is published.
-template <int kPer>
+template <int kPer, bool k2D>
 __device__ __forceinline__ void onchip_data_step(const u32x4* __restrict__ x, int t, int batch, int64_t hb,
-                                                 u32x4 (&cur)[kPer], u32x4 (&nxt)[kPer], u32x4 (*L)[kOnchipData],
-                                                 uint32_t* __restrict__ q, uint8_t* __restrict__ sf,
-                                                 OnchipShared& sh) {
+                                                 const OnchipMap& mp, u32x4 (&cur)[kPer], u32x4 (&nxt)[kPer],
+                                                 u32x4 (*L)[kOnchipData], uint32_t* __restrict__ q,
+                                                 uint8_t* __restrict__ sf, OnchipShared& sh) {
   if (t == 0)
-    onchip_refill<kPer, 0>(x, t, batch, hb, nxt, L);
+    onchip_refill<kPer, 0>(x, t, batch, hb, mp, nxt, L);
   else
-    onchip_refill<kPer, 2 * kPer>(x, t, batch, hb, nxt, L);
+    onchip_refill<kPer, 2 * kPer>(x, t, batch, hb, mp, nxt, L);
   const uint32_t m = onchip_wave_max<kPer>(nxt);
   if ((threadIdx.x & 63) == 0) sh.red[threadIdx.x >> 6] = m;
   lds_barrier();                                       // maxima of t+1 -> synchronization wave
@@ -452,17 +481,24 @@ __device__ __forceinline__ void onchip_data_step(const u32x4* __restrict__ x, in
   const double r6 = sh.r6;
   const __amdgpu_buffer_rsrc_t rq = tensor_rsrc(q, t, batch, hb * 4);
   const __amdgpu_buffer_rsrc_t rsf = tensor_rsrc(sf, t, batch, hb / 2);
-  const int qbase = (int)blockIdx.x * kPer * kOnchipData * 4;
-  const int sbase = (int)blockIdx.x * kPer * kOnchipData / 2;
   // even lanes write the pair's scale byte; odd lanes aim past the extent (a
   // dropped store), so every lane issues the same stores
-  const int sf_lane = (threadIdx.x & 1) ? (int)0x80000000u : (int)threadIdx.x >> 1;
+  const int sf_lane = (threadIdx.x & 1) ? (int)0x80000000u : mp.voff / 32;
+  uint32_t sbyte2d = 0u;
+  double rd2d = 0.0;
+  if (k2D) {                                           // one 16 x 16 tile: the lane's 16 rows and its partner's
+    uint32_t bam = 0u;
+#pragma unroll
+    for (int p = 0; p < kPer; ++p) bam = bam > half_absmax_bits(cur[p]) ? bam : half_absmax_bits(cur[p]);
+    sbyte2d = block_scale_byte(pair_max(bam), r6);
+    rd2d = sh.table[sbyte2d];
+  }
 #pragma unroll
   for (int p = 0; p < kPer; ++p) {
-    const uint32_t sbyte = block_scale_byte(pair_max(half_absmax_bits(cur[p])), r6);
-    const uint32_t code = encode_half(cur[p], sh.table[sbyte]);
-    __builtin_amdgcn_raw_buffer_store_b32(code, rq, (int)threadIdx.x * 4, qbase + p * kOnchipData * 4, 0);
-    __builtin_amdgcn_raw_buffer_store_b8((uint8_t)sbyte, rsf, sf_lane, sbase + p * (kOnchipData / 2), 0);
+    const uint32_t sbyte = k2D ? sbyte2d : block_scale_byte(pair_max(half_absmax_bits(cur[p])), r6);
+    const uint32_t code = encode_half(cur[p], k2D ? rd2d : sh.table[sbyte]);
+    __builtin_amdgcn_raw_buffer_store_b32(code, rq, mp.voff / 4, p * (mp.pstride / 4), 0);
+    __builtin_amdgcn_raw_buffer_store_b8((uint8_t)sbyte, rsf, sf_lane, p * (mp.pstride / 32), 0);
     __builtin_amdgcn_sched_barrier(0);                 // one half block's temporaries at a time
   }
 }
@@ -491,32 +527,34 @@ __device__ __forceinline__ uint32_t onchip_wait(uint32_t* ws, int t, int G) {
   return 0u;
 }
 
-template <int kPer>
+template <int kPer, bool k2D>
 __global__ void __launch_bounds__(kOnchipThreads) fused_onchip_kernel(const u32x4* __restrict__ x, int batch,
-                                                                      int64_t hb, uint32_t* ws,
+                                                                      int64_t hb, int spr, uint32_t* ws,
                                                                       float* __restrict__ gout,
                                                                       uint32_t* __restrict__ q,
                                                                       uint8_t* __restrict__ sf) {
   static_assert(kPer % 2 == 0 && kPer <= kOnchipMaxPer, "pieces move in pairs");
+  static_assert(!k2D || kPer == 16, "a 2D strip is 16 rows");
   __shared__ OnchipShared sh;
   __shared__ __attribute__((aligned(16))) u32x4 L[kPer][kOnchipData];
   const int G = gridDim.x;
   if (wave_id() < kOnchipDataWaves) {
     u32x4 a[kPer], b[kPer];
-    onchip_dma<kPer>(L, tensor_rsrc(x, 0, batch, hb * 16), 0, kPer);
+    const OnchipMap mp = onchip_map<kPer, k2D>(spr);
+    onchip_dma(L, tensor_rsrc(x, 0, batch, hb * 16), mp, 0, kPer);
     wait_vmcnt<0>();
 #pragma unroll
     for (int p = 0; p < kPer; p += 2) lds_read2(&L[p][threadIdx.x], &L[p + 1][threadIdx.x], a[p], a[p + 1]);
-    onchip_dma<kPer>(L, tensor_rsrc(x, 1, batch, hb * 16), 0, kPer);
+    onchip_dma(L, tensor_rsrc(x, 1, batch, hb * 16), mp, 0, kPer);
     const uint32_t m = onchip_wave_max<kPer>(a);
     if ((threadIdx.x & 63) == 0) sh.red[threadIdx.x >> 6] = m;
     lds_barrier();                                     // maxima of tensor 0
     int t = 0;
     for (; t + 1 < batch; t += 2) {
-      onchip_data_step<kPer>(x, t, batch, hb, a, b, L, q, sf, sh);
-      onchip_data_step<kPer>(x, t + 1, batch, hb, b, a, L, q, sf, sh);
+      onchip_data_step<kPer, k2D>(x, t, batch, hb, mp, a, b, L, q, sf, sh);
+      onchip_data_step<kPer, k2D>(x, t + 1, batch, hb, mp, b, a, L, q, sf, sh);
     }
-    if (t < batch) onchip_data_step<kPer>(x, t, batch, hb, a, b, L, q, sf, sh);
+    if (t < batch) onchip_data_step<kPer, k2D>(x, t, batch, hb, mp, a, b, L, q, sf, sh);
     return;
   }
   // synchronization wave
@@ -585,6 +623,12 @@ __global__ void __launch_bounds__(kThreads) dequant_kernel(const uint32_t* __res
   for (; i < hb_per_tensor; i += step) yt[i] = dequant_half(qt[i], e4m3_value(st[i >> 1]), g);
 }
 
+// Clears n words of scratch (the exchange header of a workspace whose
+// contents are not guaranteed, before a cooperative launch uses it).
+__global__ void __launch_bounds__(kThreads) zero_words_kernel(uint32_t* __restrict__ p, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n; i += (int64_t)gridDim.x * kThreads) p[i] = 0u;
+}
+
 }  // namespace nvfp4
 
 // ============================================================ host entry points
@@ -651,6 +695,50 @@ int onchip_per_thread(int64_t hb_per_tensor) {
 
 }  // namespace
 
+namespace nvfp4host {
+
+// Scratch bytes of quantize_2d_onchip for a batch (the exchange header).
+size_t quantize_2d_onchip_ws_bytes(int64_t batch) {
+  return batch <= 0 ? 0 : (fused_header_bytes(batch) + 255) & ~(size_t)255;
+}
+
+// 2D quantize (one E4M3 scale per 16 x 16 tile, row-major outputs) of batch
+// tensors [rows][cols] in one cooperative launch of fused_onchip_kernel<16,
+// true> when a tensor's 16-row x 8-column strips fit one per data thread on
+// the chip: every input byte is read once.  ENOTSUP when they do not (the
+// caller then runs its two-pass path).  The exchange header in ws is
+// cleared first, so the scratch needs no preparation.  The shape and
+// pointers are validated by the caller (rows % 16 == 0, cols % 16 == 0).
+nvfp4_status quantize_2d_onchip(const uint16_t* x, int64_t batch, int64_t rows, int64_t cols, uint8_t* q, uint8_t* sf,
+                                float* g, void* ws, hipStream_t s) {
+  if (batch <= 0 || rows <= 0 || cols <= 0) return NVFP4_ENOTSUP;
+  const int64_t cus = num_cus();
+  if (cus > (int64_t)kTensorWords) return NVFP4_ENOTSUP;   // one exchange slot per workgroup
+  const int64_t strips = (rows / 16) * (cols / 8);
+  const int64_t G = (strips + kOnchipData - 1) / kOnchipData;
+  if (G > cus || cols / 8 > INT32_MAX / 16) return NVFP4_ENOTSUP;
+  const int64_t words = (int64_t)(quantize_2d_onchip_ws_bytes(batch) / 4);
+  zero_words_kernel<<<(unsigned)std::min<int64_t>((words + kThreads - 1) / kThreads, 1024), kThreads, 0, s>>>(
+      (uint32_t*)ws, words);
+  NVFP4_LAUNCH_CHECK();
+  const u32x4* xa = (const u32x4*)x;
+  int bt = (int)batch;
+  int64_t hb = rows * cols / 8;
+  int spr = (int)(cols / 8);
+  uint32_t* wsa = (uint32_t*)ws;
+  uint32_t* qa = (uint32_t*)q;
+  void* args[] = {&xa, &bt, (void*)&hb, &spr, &wsa, &g, &qa, &sf};
+  const hipError_t e = hipLaunchCooperativeKernel((const void*)fused_onchip_kernel<16, true>, dim3((unsigned)G),
+                                                  dim3(kOnchipThreads), args, 0, s);
+  if (e != hipSuccess) {
+    set_hip_error(e);
+    return NVFP4_EHIP;
+  }
+  return NVFP4_OK;
+}
+
+}  // namespace nvfp4host
+
 extern "C" {
 
 size_t nvfp4_quantize_workspace_bytes(int64_t batch, int64_t rows, int64_t cols) {
@@ -685,19 +773,20 @@ nvfp4_status nvfp4_quantize(const uint16_t* x, int64_t batch, int64_t rows, int6
       int bt = (int)batch;
       uint32_t* ws = (uint32_t*)workspace;
       uint32_t* qa = (uint32_t*)q;
-      void* args[] = {&xa, &bt, (void*)&hb, &ws, &g, &qa, &sf};
+      int spr = 0;                                     // unused by the 1D layout
+      void* args[] = {&xa, &bt, (void*)&hb, &spr, &ws, &g, &qa, &sf};
       const int64_t slice = (int64_t)onchip_per * kOnchipData;
       const int G = (int)((hb + slice - 1) / slice);
       const void* fn = nullptr;
       const void* fns[kOnchipMaxPer / 2] = {
-          (const void*)fused_onchip_kernel<2>,
-          (const void*)fused_onchip_kernel<4>,
-          (const void*)fused_onchip_kernel<6>,
-          (const void*)fused_onchip_kernel<8>,
-          (const void*)fused_onchip_kernel<10>,
-          (const void*)fused_onchip_kernel<12>,
-          (const void*)fused_onchip_kernel<14>,
-          (const void*)fused_onchip_kernel<16>,
+          (const void*)fused_onchip_kernel<2, false>,
+          (const void*)fused_onchip_kernel<4, false>,
+          (const void*)fused_onchip_kernel<6, false>,
+          (const void*)fused_onchip_kernel<8, false>,
+          (const void*)fused_onchip_kernel<10, false>,
+          (const void*)fused_onchip_kernel<12, false>,
+          (const void*)fused_onchip_kernel<14, false>,
+          (const void*)fused_onchip_kernel<16, false>,
       };
       fn = fns[onchip_per / 2 - 1];
       hipError_t e = hipLaunchCooperativeKernel(fn, dim3(G), dim3(kOnchipThreads), args, 0, s);

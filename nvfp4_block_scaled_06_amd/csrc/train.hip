@@ -536,10 +536,21 @@ void launch_encode(dim3 grid, hipStream_t s, const uint16_t* x, const VarShape& 
 
 }  // namespace
 
+namespace nvfp4host {
+// The single-launch 2D quantize (codec.hip): one read of the input when a
+// tensor fits on chip; ENOTSUP otherwise.
+size_t quantize_2d_onchip_ws_bytes(int64_t batch);
+nvfp4_status quantize_2d_onchip(const uint16_t* x, int64_t batch, int64_t rows, int64_t cols, uint8_t* q, uint8_t* sf,
+                                float* g, void* ws, hipStream_t s);
+}  // namespace nvfp4host
+
 extern "C" {
 
+// Scratch: the single-launch 2D path's exchange header, then the two-pass
+// path's per-workgroup partial maxima.
 size_t nvfp4_quantize_ex_workspace_bytes(int64_t batch) {
-  return batch <= 0 ? 0 : (size_t)batch * kVarMaxPartials * sizeof(uint32_t);
+  return batch <= 0 ? 0
+                    : nvfp4host::quantize_2d_onchip_ws_bytes(batch) + (size_t)batch * kVarMaxPartials * sizeof(uint32_t);
 }
 
 nvfp4_status nvfp4_quantize_ex(const uint16_t* x, int64_t batch, int64_t rows, int64_t cols, uint32_t variant,
@@ -581,7 +592,11 @@ nvfp4_status nvfp4_quantize_ex(const uint16_t* x, int64_t batch, int64_t rows, i
   const int64_t wgs_need = colwise ? sh.sc * ((sh.sr + 15) / 16) * (kVarThreads / 64) : sh.nitems;
   const dim3 grid((unsigned)var_wgs(batch, wgs_need), (unsigned)batch);
   hipStream_t s = (hipStream_t)stream;
-  uint32_t* partial = (uint32_t*)workspace;
+  if (variant == NVFP4_VAR_2D && n > 0) {          // row-wise 2D: one launch when the tensors fit on chip
+    st = nvfp4host::quantize_2d_onchip(x, batch, rows, cols, q, sf, g, workspace, s);
+    if (st != NVFP4_ENOTSUP) return st;
+  }
+  uint32_t* partial = (uint32_t*)((char*)workspace + nvfp4host::quantize_2d_onchip_ws_bytes(batch));
   // pass 1: the amax of the quantized values (the orientation matters only under RHT)
   if (rht && colwise)
     var_amax_kernel<true, true><<<grid, kVarThreads, 0, s>>>(x, sh, rht_signs, partial);

@@ -57,6 +57,36 @@ def test_colwise_variants_over_several_row_blocks(variant, shape):
     _check(_x(shape, sum(shape) * 3 + variant, wide=len(shape) == 3), variant)
 
 
+@pytest.mark.parametrize("shape", [(5, 48, 1040), (2, 512, 7168), (1, 16, 16), (7, 32, 4096)])
+def test_2d_single_launch_shapes(shape):
+    """Row-wise 2D runs as one cooperative launch when a tensor's 16 x 8
+    strips fit one per data thread on the chip: strip rows that cross
+    workgroup boundaries (cols = 1040), 64 workgroups per tensor, a single
+    tile, and a batch of 7; per-tensor magnitudes span 60 binades."""
+    _check(_x(shape, sum(shape) * 5, wide=True), nv.VAR_2D)
+
+
+def test_2d_ignores_stale_workspace_contents():
+    """The single-launch 2D path clears its exchange words itself: a
+    workspace full of 0xFF bytes gives the same bytes as a fresh one."""
+    x = _x((3, 64, 512), 31, wide=True)
+    wsb = nv.lib().nvfp4_quantize_ex_workspace_bytes(3)
+    ws = torch.full((wsb,), 0xFF, dtype=torch.uint8, device="cuda")
+    a = nv.quantize_ex(x, nv.VAR_2D, workspace=ws)
+    b = nv.quantize_ex(x, nv.VAR_2D, workspace=ws)
+    c = nv.quantize_ex(x, nv.VAR_2D)
+    torch.cuda.synchronize()
+    for u, v, w in zip(a, b, c):
+        assert torch.equal(u, w) and torch.equal(v, w)
+
+
+def test_2d_too_large_for_one_launch():
+    """A 4096 x 7168 tensor has twice the strips the chip holds, so 2D
+    takes the two-pass path; same bytes as the oracle."""
+    print("case: 2D 4096x7168 (two-pass)", flush=True)
+    _check(_x((4096, 7168), 41), nv.VAR_2D)
+
+
 def test_variant_zero_equals_plain_quantize():
     x = _x((2, 128, 256), 6, wide=True)
     q, sf, g = nv.quantize_ex(x, 0)
