@@ -279,10 +279,12 @@ size_t nvfp4_quantize_ex_workspace_bytes(int64_t batch);
 /* Variant quantize of x [batch][rows][cols] bf16 (cols % 16 == 0).  With
  * (R, C) = (rows, cols), or (cols, rows) under COLWISE: q [batch][R][C/2],
  * sf [batch][R][C/16], g [batch] (the tensor scale of the transformed
- * values).  Two passes over x (amax, then encode); 2D alone (row-wise, no
- * RHT or SR) reads x once in a single cooperative launch when each tensor
- * has at most (compute units x 448) strips of 16 rows x 8 columns, with the
- * same bytes.  variant 0 equals nvfp4_quantize bit for bit.
+ * values).  Two passes over x (amax, then encode); 2D without RHT or SR
+ * (with or without COLWISE) reads x once in a single cooperative launch
+ * when a tensor's strips of 16 rows x 8 columns fit on the chip (at most
+ * compute units x 448 of them; COLWISE counts blocks of 8 x 8 strips, 7 per
+ * compute unit), with the same bytes.  variant 0 equals nvfp4_quantize bit
+ * for bit.
  * Errors: EINVAL (cols % 16 != 0, rows % 16 != 0 with COLWISE or 2D, unknown
  *   variant bits, rht_signs > 0xFFFF, batch > 65535, null pointers), ENOTSUP
  *   (2D with RHT, or the device), EALIGN (x, q not 16-byte aligned; g,

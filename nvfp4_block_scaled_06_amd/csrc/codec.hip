@@ -398,26 +398,55 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t tensor_rsrc(const void* base, 
                                            t < batch ? (int)bytes : 0, kBufferWord3);
 }
 
-// Where a data thread's pieces sit in a tensor: piece p of the thread is
-// the 16-byte half block at byte voff + p * pstride of the input (its 4
-// code bytes at a quarter of that offset, its block's scale byte at a 32nd).
-//  1D: the workgroup's slice is S = kPer * D consecutive half blocks; thread
-//      i's pieces are half blocks w S + p D + i.
-//  2D (16 x 16 tile scales, kPer = 16): thread i of workgroup w owns strip
-//      s = w D + i, the 8 columns [8 c, 8 c + 8) of the 16 rows [16 r,
-//      16 r + 16) with (r, c) = (s / spr, s % spr), spr = cols / 8; piece p
-//      is row 16 r + p.  Strips 2k and 2k+1 (a lane pair) form one tile.
-// Lanes past the tensor get offsets past its extent: their loads read
-// zeros and their stores are dropped.
+// Layouts of the on-chip quantize (kMode):
+//  kOn1D: the workgroup's slice is S = kPer * D consecutive half blocks;
+//      thread i's piece p is half block w S + p D + i (D data threads).
+//  kOn2D (16 x 16 tile scales, kPer = 16): thread i of workgroup w owns
+//      strip s = w D + i, the 8 columns [8 c, 8 c + 8) of the 16 rows
+//      [16 r, 16 r + 16) with (r, c) = (s / spr, s % spr), spr = cols / 8;
+//      piece p is row 16 r + p.  Strips 2k and 2k+1 (a lane pair) form one
+//      tile; codes and scales are written row-major like the input.
+//  kOn2DT (the same tiles, outputs transposed: q [cols][rows/2], sf
+//      [cols][rows/16]): data wave v of workgroup w takes the block b = 7 w
+//      + v of 8 x 8 strips (128 rows x 64 columns; blocks run down the
+//      columns), lane l the strip (8 bR + l / 8, 8 bC + l % 8).  A lane pair
+//      is again one tile; for each of its 8 columns a lane writes the 16
+//      rows' codes (8 bytes) and the tile's scale byte, so the 8 lanes of a
+//      strip column write 64 contiguous bytes of an output row.
+// Each lane's input piece p is the 16-byte half block at byte voff + p *
+// pstride.  Stores go to qoff + i * qstride and soff + i * sstride, i the
+// piece (row-major modes) or the column (kOn2DT).  Lanes past the tensor
+// get offsets past its extent: their loads read zeros, their stores are
+// dropped.
+constexpr int kOn1D = 0, kOn2D = 1, kOn2DT = 2;
+constexpr int kOnOutside = 0x70000000;          // past every on-chip tensor's extent, with room for the strides
+
 struct OnchipMap {
-  int voff;      // bytes: piece 0 of this thread
-  int pstride;   // bytes between consecutive pieces
+  int voff, pstride;                            // input bytes
+  int qoff, qstride;                            // code bytes
+  int soff, sstride;                            // scale bytes
 };
 
-template <int kPer, bool k2D>
-__device__ __forceinline__ OnchipMap onchip_map(int spr) {
+template <int kPer, int kMode>
+__device__ __forceinline__ OnchipMap onchip_map(int spr, int srows) {
   OnchipMap m;
-  if (k2D) {
+  const int lane = (int)threadIdx.x & 63;
+  if (kMode == kOn2DT) {
+    const int nbr = (srows + 7) / 8, nbc = (spr + 7) / 8;
+    const int b = (int)blockIdx.x * kOnchipDataWaves + (int)(threadIdx.x >> 6);
+    const int br = b % nbr, bc = b / nbr;
+    const int r = 8 * br + (lane >> 3), c = 8 * bc + (lane & 7);
+    const bool in = bc < nbc && r < srows && c < spr;
+    const int rows = 16 * srows;
+    m.voff = in ? (r * 16 * spr + c) * 16 : kOnOutside;
+    m.pstride = spr * 16;
+    m.qoff = in ? 8 * c * (rows / 2) + 8 * r : kOnOutside;
+    m.qstride = rows / 2;
+    m.soff = in ? 8 * c * (rows / 16) + r : kOnOutside;
+    m.sstride = rows / 16;
+    return m;
+  }
+  if (kMode == kOn2D) {
     const int s = (int)blockIdx.x * kOnchipData + (int)threadIdx.x;
     const int r = s / spr, c = s - r * spr;
     m.voff = (r * 16 * spr + c) * 16;
@@ -426,6 +455,12 @@ __device__ __forceinline__ OnchipMap onchip_map(int spr) {
     m.voff = ((int)blockIdx.x * kPer * kOnchipData + (int)threadIdx.x) * 16;
     m.pstride = kOnchipData * 16;
   }
+  m.qoff = m.voff / 4;
+  m.qstride = m.pstride / 4;
+  // even lanes write the pair's scale byte; odd lanes aim past the extent
+  // (a dropped store), so every lane issues the same stores
+  m.soff = (lane & 1) ? (int)0x80000000u : m.voff / 32;
+  m.sstride = m.pstride / 32;
   return m;
 }
 
@@ -465,7 +500,11 @@ __device__ __forceinline__ void onchip_refill(const u32x4* __restrict__ x, int t
 
 // One step of a data wave: tensor t (in cur) is encoded once its amax
 // arrives, tensor t+1 moves from LDS into nxt and its maximum is published.
-template <int kPer, bool k2D>
+// Vector memory operations the encode of one tensor issues per thread.
+template <int kPer, int kMode>
+constexpr int onchip_stores() { return kMode == kOn2DT ? 16 : 2 * kPer; }
+
+template <int kPer, int kMode>
 __device__ __forceinline__ void onchip_data_step(const u32x4* __restrict__ x, int t, int batch, int64_t hb,
                                                  const OnchipMap& mp, u32x4 (&cur)[kPer], u32x4 (&nxt)[kPer],
                                                  u32x4 (*L)[kOnchipData], uint32_t* __restrict__ q,
@@ -473,7 +512,7 @@ __device__ __forceinline__ void onchip_data_step(const u32x4* __restrict__ x, in
   if (t == 0)
     onchip_refill<kPer, 0>(x, t, batch, hb, mp, nxt, L);
   else
-    onchip_refill<kPer, 2 * kPer>(x, t, batch, hb, mp, nxt, L);
+    onchip_refill<kPer, onchip_stores<kPer, kMode>()>(x, t, batch, hb, mp, nxt, L);
   const uint32_t m = onchip_wave_max<kPer>(nxt);
   if ((threadIdx.x & 63) == 0) sh.red[threadIdx.x >> 6] = m;
   lds_barrier();                                       // maxima of t+1 -> synchronization wave
@@ -481,24 +520,42 @@ __device__ __forceinline__ void onchip_data_step(const u32x4* __restrict__ x, in
   const double r6 = sh.r6;
   const __amdgpu_buffer_rsrc_t rq = tensor_rsrc(q, t, batch, hb * 4);
   const __amdgpu_buffer_rsrc_t rsf = tensor_rsrc(sf, t, batch, hb / 2);
-  // even lanes write the pair's scale byte; odd lanes aim past the extent (a
-  // dropped store), so every lane issues the same stores
-  const int sf_lane = (threadIdx.x & 1) ? (int)0x80000000u : mp.voff / 32;
   uint32_t sbyte2d = 0u;
   double rd2d = 0.0;
-  if (k2D) {                                           // one 16 x 16 tile: the lane's 16 rows and its partner's
+  if (kMode != kOn1D) {                                // one 16 x 16 tile: the lane's 16 rows and its partner's
     uint32_t bam = 0u;
 #pragma unroll
     for (int p = 0; p < kPer; ++p) bam = bam > half_absmax_bits(cur[p]) ? bam : half_absmax_bits(cur[p]);
     sbyte2d = block_scale_byte(pair_max(bam), r6);
     rd2d = sh.table[sbyte2d];
   }
+  if (kMode == kOn2DT) {
+    // column j of the strip: rows 0..7 and 8..15 gathered into two half
+    // blocks (row p in element p), 8 code bytes down the column
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
+      uint32_t col[8];
+#pragma unroll
+      for (int p = 0; p < 16; p += 2) {
+        const uint32_t lo = j / 2 == 0 ? cur[p].x : j / 2 == 1 ? cur[p].y : j / 2 == 2 ? cur[p].z : cur[p].w;
+        const uint32_t hi = j / 2 == 0 ? cur[p + 1].x : j / 2 == 1 ? cur[p + 1].y : j / 2 == 2 ? cur[p + 1].z : cur[p + 1].w;
+        col[p / 2] = __builtin_amdgcn_perm(hi, lo, sel);
+      }
+      const uint32_t c0 = encode_half(u32x4{col[0], col[1], col[2], col[3]}, rd2d);
+      const uint32_t c1 = encode_half(u32x4{col[4], col[5], col[6], col[7]}, rd2d);
+      __builtin_amdgcn_raw_buffer_store_b64(u32x2{c0, c1}, rq, mp.qoff, j * mp.qstride, 0);
+      __builtin_amdgcn_raw_buffer_store_b8((uint8_t)sbyte2d, rsf, mp.soff, j * mp.sstride, 0);
+      __builtin_amdgcn_sched_barrier(0);               // one column's temporaries at a time
+    }
+    return;
+  }
 #pragma unroll
   for (int p = 0; p < kPer; ++p) {
-    const uint32_t sbyte = k2D ? sbyte2d : block_scale_byte(pair_max(half_absmax_bits(cur[p])), r6);
-    const uint32_t code = encode_half(cur[p], k2D ? rd2d : sh.table[sbyte]);
-    __builtin_amdgcn_raw_buffer_store_b32(code, rq, mp.voff / 4, p * (mp.pstride / 4), 0);
-    __builtin_amdgcn_raw_buffer_store_b8((uint8_t)sbyte, rsf, sf_lane, p * (mp.pstride / 32), 0);
+    const uint32_t sbyte = kMode == kOn2D ? sbyte2d : block_scale_byte(pair_max(half_absmax_bits(cur[p])), r6);
+    const uint32_t code = encode_half(cur[p], kMode == kOn2D ? rd2d : sh.table[sbyte]);
+    __builtin_amdgcn_raw_buffer_store_b32(code, rq, mp.qoff, p * mp.qstride, 0);
+    __builtin_amdgcn_raw_buffer_store_b8((uint8_t)sbyte, rsf, mp.soff, p * mp.sstride, 0);
     __builtin_amdgcn_sched_barrier(0);                 // one half block's temporaries at a time
   }
 }
@@ -527,20 +584,20 @@ __device__ __forceinline__ uint32_t onchip_wait(uint32_t* ws, int t, int G) {
   return 0u;
 }
 
-template <int kPer, bool k2D>
+template <int kPer, int kMode>
 __global__ void __launch_bounds__(kOnchipThreads) fused_onchip_kernel(const u32x4* __restrict__ x, int batch,
-                                                                      int64_t hb, int spr, uint32_t* ws,
+                                                                      int64_t hb, int spr, int srows, uint32_t* ws,
                                                                       float* __restrict__ gout,
                                                                       uint32_t* __restrict__ q,
                                                                       uint8_t* __restrict__ sf) {
   static_assert(kPer % 2 == 0 && kPer <= kOnchipMaxPer, "pieces move in pairs");
-  static_assert(!k2D || kPer == 16, "a 2D strip is 16 rows");
+  static_assert(kMode == kOn1D || kPer == 16, "a 2D strip is 16 rows");
   __shared__ OnchipShared sh;
   __shared__ __attribute__((aligned(16))) u32x4 L[kPer][kOnchipData];
   const int G = gridDim.x;
   if (wave_id() < kOnchipDataWaves) {
     u32x4 a[kPer], b[kPer];
-    const OnchipMap mp = onchip_map<kPer, k2D>(spr);
+    const OnchipMap mp = onchip_map<kPer, kMode>(spr, srows);
     onchip_dma(L, tensor_rsrc(x, 0, batch, hb * 16), mp, 0, kPer);
     wait_vmcnt<0>();
 #pragma unroll
@@ -551,10 +608,10 @@ __global__ void __launch_bounds__(kOnchipThreads) fused_onchip_kernel(const u32x
     lds_barrier();                                     // maxima of tensor 0
     int t = 0;
     for (; t + 1 < batch; t += 2) {
-      onchip_data_step<kPer, k2D>(x, t, batch, hb, mp, a, b, L, q, sf, sh);
-      onchip_data_step<kPer, k2D>(x, t + 1, batch, hb, mp, b, a, L, q, sf, sh);
+      onchip_data_step<kPer, kMode>(x, t, batch, hb, mp, a, b, L, q, sf, sh);
+      onchip_data_step<kPer, kMode>(x, t + 1, batch, hb, mp, b, a, L, q, sf, sh);
     }
-    if (t < batch) onchip_data_step<kPer, k2D>(x, t, batch, hb, mp, a, b, L, q, sf, sh);
+    if (t < batch) onchip_data_step<kPer, kMode>(x, t, batch, hb, mp, a, b, L, q, sf, sh);
     return;
   }
   // synchronization wave
@@ -702,21 +759,22 @@ size_t quantize_2d_onchip_ws_bytes(int64_t batch) {
   return batch <= 0 ? 0 : (fused_header_bytes(batch) + 255) & ~(size_t)255;
 }
 
-// 2D quantize (one E4M3 scale per 16 x 16 tile, row-major outputs) of batch
-// tensors [rows][cols] in one cooperative launch of fused_onchip_kernel<16,
-// true> when a tensor's 16-row x 8-column strips fit one per data thread on
-// the chip: every input byte is read once.  ENOTSUP when they do not (the
+// 2D quantize (one E4M3 scale per 16 x 16 tile; outputs row-major, or
+// transposed with colwise) of batch tensors [rows][cols] in one cooperative
+// launch of fused_onchip_kernel<16, kOn2D | kOn2DT> when a tensor's 16-row x
+// 8-column strips fit on the chip: every input byte is read once.  ENOTSUP when they do not (the
 // caller then runs its two-pass path).  The exchange header in ws is
 // cleared first, so the scratch needs no preparation.  The shape and
 // pointers are validated by the caller (rows % 16 == 0, cols % 16 == 0).
-nvfp4_status quantize_2d_onchip(const uint16_t* x, int64_t batch, int64_t rows, int64_t cols, uint8_t* q, uint8_t* sf,
-                                float* g, void* ws, hipStream_t s) {
+nvfp4_status quantize_2d_onchip(const uint16_t* x, int64_t batch, int64_t rows, int64_t cols, bool colwise, uint8_t* q,
+                                uint8_t* sf, float* g, void* ws, hipStream_t s) {
   if (batch <= 0 || rows <= 0 || cols <= 0) return NVFP4_ENOTSUP;
   const int64_t cus = num_cus();
   if (cus > (int64_t)kTensorWords) return NVFP4_ENOTSUP;   // one exchange slot per workgroup
-  const int64_t strips = (rows / 16) * (cols / 8);
-  const int64_t G = (strips + kOnchipData - 1) / kOnchipData;
-  if (G > cus || cols / 8 > INT32_MAX / 16) return NVFP4_ENOTSUP;
+  const int64_t srows = rows / 16, spr = cols / 8;
+  const int64_t G = colwise ? (((srows + 7) / 8) * ((spr + 7) / 8) + kOnchipDataWaves - 1) / kOnchipDataWaves
+                            : (srows * spr + kOnchipData - 1) / kOnchipData;
+  if (G > cus) return NVFP4_ENOTSUP;
   const int64_t words = (int64_t)(quantize_2d_onchip_ws_bytes(batch) / 4);
   zero_words_kernel<<<(unsigned)std::min<int64_t>((words + kThreads - 1) / kThreads, 1024), kThreads, 0, s>>>(
       (uint32_t*)ws, words);
@@ -724,12 +782,12 @@ nvfp4_status quantize_2d_onchip(const uint16_t* x, int64_t batch, int64_t rows, 
   const u32x4* xa = (const u32x4*)x;
   int bt = (int)batch;
   int64_t hb = rows * cols / 8;
-  int spr = (int)(cols / 8);
+  int spri = (int)spr, srowsi = (int)srows;       // a tensor that fits on chip has far fewer than 2^31 of either
   uint32_t* wsa = (uint32_t*)ws;
   uint32_t* qa = (uint32_t*)q;
-  void* args[] = {&xa, &bt, (void*)&hb, &spr, &wsa, &g, &qa, &sf};
-  const hipError_t e = hipLaunchCooperativeKernel((const void*)fused_onchip_kernel<16, true>, dim3((unsigned)G),
-                                                  dim3(kOnchipThreads), args, 0, s);
+  void* args[] = {&xa, &bt, (void*)&hb, &spri, &srowsi, &wsa, &g, &qa, &sf};
+  const void* fn = colwise ? (const void*)fused_onchip_kernel<16, kOn2DT> : (const void*)fused_onchip_kernel<16, kOn2D>;
+  const hipError_t e = hipLaunchCooperativeKernel(fn, dim3((unsigned)G), dim3(kOnchipThreads), args, 0, s);
   if (e != hipSuccess) {
     set_hip_error(e);
     return NVFP4_EHIP;
@@ -773,20 +831,20 @@ nvfp4_status nvfp4_quantize(const uint16_t* x, int64_t batch, int64_t rows, int6
       int bt = (int)batch;
       uint32_t* ws = (uint32_t*)workspace;
       uint32_t* qa = (uint32_t*)q;
-      int spr = 0;                                     // unused by the 1D layout
-      void* args[] = {&xa, &bt, (void*)&hb, &spr, &ws, &g, &qa, &sf};
+      int spr = 0, srows = 0;                          // unused by the 1D layout
+      void* args[] = {&xa, &bt, (void*)&hb, &spr, &srows, &ws, &g, &qa, &sf};
       const int64_t slice = (int64_t)onchip_per * kOnchipData;
       const int G = (int)((hb + slice - 1) / slice);
       const void* fn = nullptr;
       const void* fns[kOnchipMaxPer / 2] = {
-          (const void*)fused_onchip_kernel<2, false>,
-          (const void*)fused_onchip_kernel<4, false>,
-          (const void*)fused_onchip_kernel<6, false>,
-          (const void*)fused_onchip_kernel<8, false>,
-          (const void*)fused_onchip_kernel<10, false>,
-          (const void*)fused_onchip_kernel<12, false>,
-          (const void*)fused_onchip_kernel<14, false>,
-          (const void*)fused_onchip_kernel<16, false>,
+          (const void*)fused_onchip_kernel<2, kOn1D>,
+          (const void*)fused_onchip_kernel<4, kOn1D>,
+          (const void*)fused_onchip_kernel<6, kOn1D>,
+          (const void*)fused_onchip_kernel<8, kOn1D>,
+          (const void*)fused_onchip_kernel<10, kOn1D>,
+          (const void*)fused_onchip_kernel<12, kOn1D>,
+          (const void*)fused_onchip_kernel<14, kOn1D>,
+          (const void*)fused_onchip_kernel<16, kOn1D>,
       };
       fn = fns[onchip_per / 2 - 1];
       hipError_t e = hipLaunchCooperativeKernel(fn, dim3(G), dim3(kOnchipThreads), args, 0, s);

@@ -540,8 +540,8 @@ namespace nvfp4host {
 // The single-launch 2D quantize (codec.hip): one read of the input when a
 // tensor fits on chip; ENOTSUP otherwise.
 size_t quantize_2d_onchip_ws_bytes(int64_t batch);
-nvfp4_status quantize_2d_onchip(const uint16_t* x, int64_t batch, int64_t rows, int64_t cols, uint8_t* q, uint8_t* sf,
-                                float* g, void* ws, hipStream_t s);
+nvfp4_status quantize_2d_onchip(const uint16_t* x, int64_t batch, int64_t rows, int64_t cols, bool colwise, uint8_t* q,
+                                uint8_t* sf, float* g, void* ws, hipStream_t s);
 }  // namespace nvfp4host
 
 extern "C" {
@@ -592,8 +592,9 @@ nvfp4_status nvfp4_quantize_ex(const uint16_t* x, int64_t batch, int64_t rows, i
   const int64_t wgs_need = colwise ? sh.sc * ((sh.sr + 15) / 16) * (kVarThreads / 64) : sh.nitems;
   const dim3 grid((unsigned)var_wgs(batch, wgs_need), (unsigned)batch);
   hipStream_t s = (hipStream_t)stream;
-  if (variant == NVFP4_VAR_2D && n > 0) {          // row-wise 2D: one launch when the tensors fit on chip
-    st = nvfp4host::quantize_2d_onchip(x, batch, rows, cols, q, sf, g, workspace, s);
+  if ((variant == NVFP4_VAR_2D || variant == (NVFP4_VAR_2D | NVFP4_VAR_COLWISE)) && n > 0) {
+    // 2D without RHT or SR: one launch when the tensors fit on chip
+    st = nvfp4host::quantize_2d_onchip(x, batch, rows, cols, colwise, q, sf, g, workspace, s);
     if (st != NVFP4_ENOTSUP) return st;
   }
   uint32_t* partial = (uint32_t*)((char*)workspace + nvfp4host::quantize_2d_onchip_ws_bytes(batch));

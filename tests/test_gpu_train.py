@@ -57,34 +57,39 @@ def test_colwise_variants_over_several_row_blocks(variant, shape):
     _check(_x(shape, sum(shape) * 3 + variant, wide=len(shape) == 3), variant)
 
 
-@pytest.mark.parametrize("shape", [(5, 48, 1040), (2, 512, 7168), (1, 16, 16), (7, 32, 4096)])
-def test_2d_single_launch_shapes(shape):
-    """Row-wise 2D runs as one cooperative launch when a tensor's 16 x 8
-    strips fit one per data thread on the chip: strip rows that cross
+@pytest.mark.parametrize("variant", [2, 3])
+@pytest.mark.parametrize("shape", [(5, 48, 1040), (2, 512, 7168), (1, 16, 16), (7, 32, 4096), (2, 400, 80)])
+def test_2d_single_launch_shapes(shape, variant):
+    """2D (row-major or transposed outputs) runs as one cooperative launch
+    when a tensor's 16 x 8 strips fit on the chip: strip rows that cross
     workgroup boundaries (cols = 1040), 64 workgroups per tensor, a single
-    tile, and a batch of 7; per-tensor magnitudes span 60 binades."""
-    _check(_x(shape, sum(shape) * 5, wide=True), nv.VAR_2D)
+    tile, a batch of 7, and strip blocks cut by the tensor's edge in both
+    directions (400 x 80: 25 strip rows, 10 strip columns); per-tensor
+    magnitudes span 60 binades."""
+    _check(_x(shape, sum(shape) * 5 + variant, wide=True), variant)
 
 
-def test_2d_ignores_stale_workspace_contents():
+@pytest.mark.parametrize("variant", [2, 3])
+def test_2d_ignores_stale_workspace_contents(variant):
     """The single-launch 2D path clears its exchange words itself: a
     workspace full of 0xFF bytes gives the same bytes as a fresh one."""
     x = _x((3, 64, 512), 31, wide=True)
     wsb = nv.lib().nvfp4_quantize_ex_workspace_bytes(3)
     ws = torch.full((wsb,), 0xFF, dtype=torch.uint8, device="cuda")
-    a = nv.quantize_ex(x, nv.VAR_2D, workspace=ws)
-    b = nv.quantize_ex(x, nv.VAR_2D, workspace=ws)
-    c = nv.quantize_ex(x, nv.VAR_2D)
+    a = nv.quantize_ex(x, variant, workspace=ws)
+    b = nv.quantize_ex(x, variant, workspace=ws)
+    c = nv.quantize_ex(x, variant)
     torch.cuda.synchronize()
     for u, v, w in zip(a, b, c):
         assert torch.equal(u, w) and torch.equal(v, w)
 
 
-def test_2d_too_large_for_one_launch():
+@pytest.mark.parametrize("variant", [2, 3])
+def test_2d_too_large_for_one_launch(variant):
     """A 4096 x 7168 tensor has twice the strips the chip holds, so 2D
     takes the two-pass path; same bytes as the oracle."""
-    print("case: 2D 4096x7168 (two-pass)", flush=True)
-    _check(_x((4096, 7168), 41), nv.VAR_2D)
+    print("case: 2D 4096x7168 (two-pass), variant", variant, flush=True)
+    _check(_x((4096, 7168), 41 + variant), variant)
 
 
 def test_variant_zero_equals_plain_quantize():
