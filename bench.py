@@ -504,7 +504,7 @@ def main():
     dom = "quantize" if head["quantize_ms"] >= head["dequantize_ms"] else "dequantize"
     dom_bytes = head[f"{dom}_bytes"]
     dom_ms = head[f"{dom}_ms"]
-    kname = {"quantize": "fused_onchip_kernel<16, false> (nvfp4_quantize, fused)" if head["flags"] == "fused"
+    kname = {"quantize": "fused_onchip_kernel<16, 0> (nvfp4_quantize, fused)" if head["flags"] == "fused"
              else "nvfp4_quantize (two_kernel)", "dequantize": "dequant_kernel"}[dom]
     r = roof(dom_bytes, dom_ms, HBM_PEAK_GBS, "GB/s")
     line = {
