@@ -285,15 +285,15 @@ template <int W>
 __device__ __forceinline__ void load_words(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t* dst) {
   // W words (W = 1, 2, 4, 8) from byte offset off
   if (W == 1) {
-    dst[0] = __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0);
+    dst[0] = __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, kStreamLoad);
   } else if (W == 2) {
-    const u32x2 v = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0));
+    const u32x2 v = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, kStreamLoad));
     dst[0] = v.x;
     dst[1] = v.y;
   } else {
 #pragma unroll
     for (int i = 0; i < W; i += 4) {
-      const u32x4 v = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)(off + 4 * i), 0, 0));
+      const u32x4 v = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)(off + 4 * i), 0, kStreamLoad));
       dst[i] = v.x;
       dst[i + 1] = v.y;
       dst[i + 2] = v.z;
@@ -315,7 +315,7 @@ __device__ __forceinline__ void attn_load(const __amdgpu_buffer_rsrc_t (&r)[4], 
     const bool in = u < cnt;
     load_words<D / 32>(r[0], in ? (uint32_t)u * (D / 2) + qd * (D / 8) : kAttnOutside, raw.kc[T]);
     if (D / 64 == 1)
-      raw.ks[T][0] = __builtin_amdgcn_raw_buffer_load_b32(r[1], (int)(in ? (uint32_t)u * (D / 16) : kAttnOutside), 0, 0);
+      raw.ks[T][0] = __builtin_amdgcn_raw_buffer_load_b32(r[1], (int)(in ? (uint32_t)u * (D / 16) : kAttnOutside), 0, kStreamLoad);
     else
       load_words<D / 64>(r[1], in ? (uint32_t)u * (D / 16) : kAttnOutside, raw.ks[T]);
   }
@@ -324,7 +324,7 @@ __device__ __forceinline__ void attn_load(const __amdgpu_buffer_rsrc_t (&r)[4], 
   load_words<D / 16>(r[2], in ? (uint32_t)u * (D / 2) + (lane & 1) * (D / 4) : kAttnOutside, raw.vc);
   if (D == 64)
     raw.vs[0] = __builtin_amdgcn_raw_buffer_load_b16(r[3], (int)(in ? (uint32_t)u * (D / 16) + (lane & 1) * 2 : kAttnOutside),
-                                                     0, 0);
+                                                     0, kStreamLoad);
   else
     load_words<(D / 128 > 0 ? D / 128 : 1)>(r[3], in ? (uint32_t)u * (D / 16) + (lane & 1) * (D / 32) : kAttnOutside,
                                             raw.vs);

@@ -469,7 +469,7 @@ __device__ __forceinline__ void onchip_dma(u32x4 (*L)[kOnchipData], __amdgpu_buf
                                            int p0, int n) {
   const int w = threadIdx.x >> 6;
   for (int p = p0; p < p0 + n; ++p)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)&L[p][w * 64], 16, mp.voff, p * mp.pstride, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)&L[p][w * 64], 16, mp.voff, p * mp.pstride, 0, kStreamLoad);
 }
 
 template <int kPer>

@@ -160,6 +160,12 @@ __device__ __forceinline__ u32x4 dequant_half(uint32_t codes, float s, float g) 
 // stores; accesses past the resource's extent read zero and write nothing.
 constexpr int kBufferWord3 = 0x00020000;
 
+// Cache-policy operand of a buffer load that streams data read once: the
+// non-temporal bit (bit 1 on gfx950), so the lines do not displace reused
+// data in L2 and the last-level cache.  Measured on the fused quantize's
+// buffer-to-LDS loads: 0.573 -> 0.530 ms over 1.88 GB of bf16.
+constexpr int kStreamLoad = 2;
+
 // ---------------------------------------------------------------- reductions
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
 #pragma unroll

@@ -261,8 +261,8 @@ __global__ void __launch_bounds__(kThreads) kv_qk_kernel(nvfp4_kv_cache c, const
     for (int u = 0; u < U; ++u) {
       const int64_t tu = t0 + u * tok_step;
       const uint32_t e = tu < n ? (uint32_t)(tu * LPT + j) : 0x08000000u;     // past the extent: zeros
-      cw[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(kc, (int)(e * 16u), 0, 0));
-      sw[u] = __builtin_amdgcn_raw_buffer_load_b16(ks, (int)(e * 2u), 0, 0);
+      cw[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(kc, (int)(e * 16u), 0, kStreamLoad));
+      sw[u] = __builtin_amdgcn_raw_buffer_load_b16(ks, (int)(e * 2u), 0, kStreamLoad);
     }
   };
   auto contract = [&](int64_t t0, const u32x4 (&cw)[U], const uint32_t (&sw)[U]) {
