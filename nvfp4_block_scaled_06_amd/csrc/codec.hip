@@ -82,7 +82,7 @@ __device__ __forceinline__ void encode_tail(const u32x4* __restrict__ xt, uint32
   const int lane = threadIdx.x & 63;
   const int64_t hb = base + lane;
   const bool ok = hb >= lo && hb < hi;
-  const u32x4 v = ok ? xt[hb] : u32x4{0u, 0u, 0u, 0u};
+  const u32x4 v = ok ? __builtin_nontemporal_load(xt + hb) : u32x4{0u, 0u, 0u, 0u};
   const uint32_t sbyte = block_scale_byte(pair_max(half_absmax_bits(v)), r6);
   const uint32_t code = encode_half(v, table[sbyte]);
   if (ok) {
@@ -100,7 +100,7 @@ __device__ __forceinline__ void encode_chunks(const u32x4* __restrict__ xt, uint
   const int lane = threadIdx.x & 63;
   u32x4 v[kU];
 #pragma unroll
-  for (int u = 0; u < kU; ++u) v[u] = (xt + c[u])[lane];
+  for (int u = 0; u < kU; ++u) v[u] = __builtin_nontemporal_load((xt + c[u]) + lane);   // last use of x
   uint32_t sbyte[kU];
 #pragma unroll
   for (int u = 0; u < kU; ++u) sbyte[u] = block_scale_byte(pair_max(half_absmax_bits(v[u])), r6);

@@ -43,7 +43,7 @@ __device__ __forceinline__ void kv_append_load(const u32x4* __restrict__ src, in
       t = (uint32_t)(j / R);
       r = (uint32_t)(j - (int64_t)t * R);
     }
-    v[u] = j < total ? src[(int64_t)t * in_stride + r] : u32x4{0u, 0u, 0u, 0u};
+    v[u] = j < total ? __builtin_nontemporal_load(src + ((int64_t)t * in_stride + r)) : u32x4{0u, 0u, 0u, 0u};
   }
 }
 
