@@ -14,6 +14,16 @@ nv = pytest.importorskip("nvfp4_block_scaled_06_amd")
 TOL = 1e-5
 
 
+def _quantized(x):
+    """x quantized on the GPU and by the oracle.  The bytes must agree, and the
+    expected GEMM is then computed from the oracle's encoding alone."""
+    q, sf, g = nv.quantize(x)
+    oq, osf, og = oracle.quantize(bits(x))
+    assert np.array_equal(np_(q), oq) and np.array_equal(np_(sf), osf), "GPU codes differ from the oracle's"
+    assert np.array_equal(np_(g).view(np.uint32), og.view(np.uint32)), "GPU tensor scale differs from the oracle's"
+    return (q, sf, g), (oq, osf, og)
+
+
 def _operands(M, N, K, seed, scale_a=1.0, scale_b=1.0):
     gen = torch.Generator().manual_seed(seed)
     a = (torch.randn((M, K), generator=gen) * scale_a).to(torch.bfloat16).cuda()
@@ -26,11 +36,11 @@ def _operands(M, N, K, seed, scale_a=1.0, scale_b=1.0):
 def test_gemm_small(M, N, K):
     print("case: gemm", M, N, K, flush=True)
     a, b = _operands(M, N, K, M * 7 + N * 3 + K)
-    aq, asf, ag = nv.quantize(a)
-    bq, bsf, bg = nv.quantize(b)
+    (aq, asf, ag), oa = _quantized(a)
+    (bq, bsf, bg), ob = _quantized(b)
     c = nv.gemm(aq, asf, ag, bq, bsf, bg)
     torch.cuda.synchronize()
-    want = oracle.gemm_f64(np_(aq), np_(asf), np_(ag)[0], np_(bq), np_(bsf), np_(bg)[0])
+    want = oracle.gemm_f64(oa[0], oa[1], oa[2][0], ob[0], ob[1], ob[2][0])
     err = rel_frobenius(np_(c), want)
     assert err <= TOL, f"rel Frobenius {err:.3e}"
 
@@ -38,11 +48,11 @@ def test_gemm_small(M, N, K):
 def test_gemm_scales_and_outliers():
     a, b = _operands(256, 192, 512, 3, 1e-3, 40.0)
     a[:, 7] *= 300
-    aq, asf, ag = nv.quantize(a)
-    bq, bsf, bg = nv.quantize(b)
+    (aq, asf, ag), oa = _quantized(a)
+    (bq, bsf, bg), ob = _quantized(b)
     c = nv.gemm(aq, asf, ag, bq, bsf, bg)
     torch.cuda.synchronize()
-    want = oracle.gemm_f64(np_(aq), np_(asf), np_(ag)[0], np_(bq), np_(bsf), np_(bg)[0])
+    want = oracle.gemm_f64(oa[0], oa[1], oa[2][0], ob[0], ob[1], ob[2][0])
     assert rel_frobenius(np_(c), want) <= TOL
 
 
@@ -61,12 +71,12 @@ def test_gemm_full_size_sampled_rows():
     (all 2048 columns) against fp64."""
     print("case: gemm 8192x2048x7168 seed 105", flush=True)
     a, b = synth.gemm_operands(device="cuda")
-    aq, asf, ag = nv.quantize(a)
-    bq, bsf, bg = nv.quantize(b)
+    (aq, asf, ag), oa = _quantized(a)
+    (bq, bsf, bg), ob = _quantized(b)
     c = nv.gemm(aq, asf, ag, bq, bsf, bg)
     torch.cuda.synchronize()
     rows = np.sort(np.random.default_rng(1).choice(8192, 96, replace=False))
-    want = oracle.gemm_f64(np_(aq), np_(asf), np_(ag)[0], np_(bq), np_(bsf), np_(bg)[0], rows=rows)
+    want = oracle.gemm_f64(oa[0], oa[1], oa[2][0], ob[0], ob[1], ob[2][0], rows=rows)
     err = rel_frobenius(np_(c[torch.from_numpy(rows).cuda()]), want)
     assert err <= TOL, f"rel Frobenius {err:.3e}"
 
@@ -120,10 +130,10 @@ def _experts_and_routing(E, N, K, counts, seed):
     M = int(sum(counts))
     a = torch.randn((M, K), generator=gen).to(torch.bfloat16).cuda()
     w = (torch.randn((E, N, K), generator=gen) * torch.linspace(0.5, 4.0, E).view(E, 1, 1)).to(torch.bfloat16).cuda()
-    aq, asf, ag = nv.quantize(a)
-    bq, bsf, bg = nv.quantize(w)                  # one tensor scale per expert
+    (aq, asf, ag), oa = _quantized(a)
+    (bq, bsf, bg), ob = _quantized(w)             # one tensor scale per expert
     offsets = torch.tensor(np.concatenate([[0], np.cumsum(counts)]), dtype=torch.int32).cuda()
-    return aq, asf, ag, bq, bsf, bg, offsets
+    return aq, asf, ag, bq, bsf, bg, offsets, oa, ob
 
 
 @pytest.mark.parametrize("K", [2048, 2032])
@@ -134,11 +144,11 @@ def test_grouped_gemm_against_oracle_and_dense(K):
     print("case: grouped gemm K", K, flush=True)
     counts = [300, 0, 1, 513, 0, 77, 256, 2]
     E, N = len(counts), 96
-    aq, asf, ag, bq, bsf, bg, offsets = _experts_and_routing(E, N, K, counts, K + 5)
+    aq, asf, ag, bq, bsf, bg, offsets, oa, ob = _experts_and_routing(E, N, K, counts, K + 5)
     c = nv.grouped_gemm(aq, asf, ag, bq, bsf, bg, offsets)
     torch.cuda.synchronize()
     off = np_(offsets)
-    want = oracle.grouped_gemm_f64(np_(aq), np_(asf), np_(ag)[0], np_(bq), np_(bsf), np_(bg), off)
+    want = oracle.grouped_gemm_f64(oa[0], oa[1], oa[2][0], ob[0], ob[1], ob[2], off)
     err = rel_frobenius(np_(c), want)
     assert err <= TOL, f"rel Frobenius {err:.3e}"
     for e in range(E):
@@ -154,10 +164,10 @@ def test_grouped_gemm_against_oracle_and_dense(K):
 def test_grouped_gemm_offsets_past_m_are_clamped():
     """A last offset beyond M is clamped to M: rows inside A are still right."""
     counts = [40, 90]
-    aq, asf, ag, bq, bsf, bg, offsets = _experts_and_routing(2, 64, 512, counts, 9)
+    aq, asf, ag, bq, bsf, bg, offsets, oa, ob = _experts_and_routing(2, 64, 512, counts, 9)
     offsets[2] = 130 + 1000
     c = nv.grouped_gemm(aq, asf, ag, bq, bsf, bg, offsets)
     torch.cuda.synchronize()
-    want = oracle.grouped_gemm_f64(np_(aq), np_(asf), np_(ag)[0], np_(bq), np_(bsf), np_(bg),
+    want = oracle.grouped_gemm_f64(oa[0], oa[1], oa[2][0], ob[0], ob[1], ob[2],
                                    np.array([0, 40, 130], np.int32))
     assert rel_frobenius(np_(c), want) <= TOL

@@ -21,6 +21,19 @@ def _cache(L, H, D, cap, seed):
     return nv.KVCache(L, H, D, cap, kg, vg, device="cuda"), np_(kg), np_(vg)
 
 
+def _oracle_cache(cache, k, v, kg, vg):
+    """The oracle's encoding of tokens [0, n) appended from k, v ([L][n][H][D]
+    bf16).  The cache's bytes must agree, and the expected values are then
+    computed from the oracle's encoding alone."""
+    n = k.shape[1]
+    kq, ks = oracle.kv_encode(bits(k), kg)
+    vq, vs = oracle.kv_encode(bits(v), vg)
+    for got, want, what in ((cache.k, kq, "K codes"), (cache.k_sf, ks, "K scales"), (cache.v, vq, "V codes"),
+                            (cache.v_sf, vs, "V scales")):
+        assert np.array_equal(np_(got[:, :, :n]), want), what
+    return kq, ks, vq, vs
+
+
 @pytest.mark.parametrize("D,grp", [(128, 4), (64, 2), (32, 1), (256, 8), (16, 4), (128, 16), (64, 3), (256, 5),
                                    (128, 1)])
 def test_append_read_qk_small(D, grp):
@@ -94,7 +107,7 @@ def test_decode_attention_small(D, grp):
     v = torch.randn((L, cap, H, D), generator=gen).to(torch.bfloat16)
     cache.append(0, k.cuda(), v.cuda())
     qv = torch.randn((L, H * grp, D), generator=gen).to(torch.bfloat16)
-    kq, ks, vq, vs = (np_(t) for t in (cache.k, cache.k_sf, cache.v, cache.v_sf))
+    kq, ks, vq, vs = _oracle_cache(cache, k, v, kg, vg)
     scale = 1.0 / np.sqrt(D)
     for n in (1, 63, 300, 700):
         out = cache.decode_attention(qv.cuda(), n, scale)
@@ -123,7 +136,7 @@ def test_decode_attention_query_magnitudes(k):
     scale = 2.0 ** -k / np.sqrt(D)
     out = cache.decode_attention(qv.cuda(), cap, scale)
     torch.cuda.synchronize()
-    kq, ks, vq, vs = (np_(t) for t in (cache.k, cache.k_sf, cache.v, cache.v_sf))
+    kq, ks, vq, vs = _oracle_cache(cache, kk, vv, kg, vg)
     want = oracle.decode_attention_f64(bits(qv), kq, ks, kg, vq, vs, vg, scale)
     err = rel_frobenius(np_(out), want)
     assert err <= QK_TOL, f"rel Frobenius {err:.3e}"
@@ -145,7 +158,7 @@ def test_decode_qk_query_magnitudes(k):
     qv = qf.to(torch.bfloat16)
     logits = cache.decode_qk(qv.cuda(), 197)
     torch.cuda.synchronize()
-    kq, ks = np_(cache.k), np_(cache.k_sf)
+    kq, ks, _, _ = _oracle_cache(cache, kk, kk, kg, vg)
     want = oracle.decode_qk_f64(bits(qv), kq[:, :, :197], ks[:, :, :197], kg)
     err = rel_frobenius(np_(logits), want)
     assert err <= QK_TOL, f"rel Frobenius {err:.3e}"
@@ -179,8 +192,11 @@ def test_read_only_k_or_v():
 
 def test_full_context_sampled():
     """32 layers x 8 KV heads x 128 dims, 131072 tokens appended in 512 chunks of
-    256; sampled chunks checked byte for byte, decode QK for 32 query heads
-    (GQA 4:1) checked on sampled tokens against fp64."""
+    256.  Sampled chunks are checked byte for byte; decode QK for 32 query heads
+    (GQA 4:1) on those chunks' tokens and full decode attention on sampled
+    (layer, KV head) pairs against fp64; kv_read of layers 0-3 over every token
+    (the benchmarked read) bit for bit on the sampled tokens.  Every expected
+    value is computed from the oracle's own encoding of the input chunks."""
     print("case: kv full context 32x8x128x131072", flush=True)
     L, H, D, T, C = 32, 8, 128, 131072, 256
     # tensor scales: amax/2688 of a calibration pass over the whole stream is
@@ -189,12 +205,20 @@ def test_full_context_sampled():
     kg = (torch.rand((L, H), generator=gen) * 0.0004 + 0.0018).float()
     vg = (torch.rand((L, H), generator=gen) * 0.0004 + 0.0018).float()
     cache = nv.KVCache(L, H, D, T, kg, vg, device="cuda")
+    pairs = ((0, 0), (17, 5), (31, 7))
+    kin = {p: [] for p in pairs}
+    vin = {p: [] for p in pairs}
     for c in range(T // C):
         k, v = synth.kv_chunk(c, device="cuda")
         cache.append(c * C, k, v)
+        for (l, h) in pairs:                          # inputs of the attention check
+            kin[(l, h)].append(bits(k[l:l + 1, :, h:h + 1].contiguous()))
+            vin[(l, h)].append(bits(v[l:l + 1, :, h:h + 1].contiguous()))
     torch.cuda.synchronize()
     kgn, vgn = np_(kg), np_(vg)
-    for c in (0, 1, 257, 511):
+    sampled = (0, 1, 257, 511)
+    enc = {}
+    for c in sampled:
         k, v = synth.kv_chunk(c, device="cuda")
         okq, oks = oracle.kv_encode(bits(k), kgn)
         ovq, ovs = oracle.kv_encode(bits(v), vgn)
@@ -203,24 +227,27 @@ def test_full_context_sampled():
         assert np.array_equal(np_(cache.k_sf[:, :, sl]), oks), f"chunk {c} K scales"
         assert np.array_equal(np_(cache.v[:, :, sl]), ovq), f"chunk {c} V codes"
         assert np.array_equal(np_(cache.v_sf[:, :, sl]), ovs), f"chunk {c} V scales"
+        enc[c] = (okq, oks, ovq, ovs)
+    toks = np.concatenate([np.arange(c * C, (c + 1) * C) for c in sampled])
+    okq, oks, ovq, ovs = (np.concatenate([enc[c][i] for c in sampled], axis=2) for i in range(4))
     qv = synth.kv_query(device="cuda")
     logits = cache.decode_qk(qv, T)
     torch.cuda.synchronize()
-    rng = np.random.default_rng(0)
-    toks = np.sort(rng.choice(T, 2048, replace=False))
-    kq = np_(cache.k[:, :, toks])
-    ks = np_(cache.k_sf[:, :, toks])
-    want = oracle.decode_qk_f64(bits(qv), kq, ks, kgn)
-    got = np_(logits[:, :, toks])
-    err = rel_frobenius(got, want)
+    want = oracle.decode_qk_f64(bits(qv), okq, oks, kgn)
+    err = rel_frobenius(np_(logits[:, :, toks]), want)
     assert err <= QK_TOL, f"rel Frobenius {err:.3e}"
+    del logits
+    kr, vr = cache.read(0, 4, 0, T)
+    assert np.array_equal(bits(kr[:, :, toks]), oracle.kv_read(okq[0:4], oks[0:4], kgn[0:4])), "kv_read K"
+    assert np.array_equal(bits(vr[:, :, toks]), oracle.kv_read(ovq[0:4], ovs[0:4], vgn[0:4])), "kv_read V"
+    del kr, vr
     # full decode attention over all 131072 tokens, checked on sampled (layer, KV head) pairs
     out = np_(cache.decode_attention(qv, T, 1.0 / np.sqrt(D)))
-    for l, h in ((0, 0), (17, 5), (31, 7)):
-        want = oracle.decode_attention_f64(bits(qv)[l:l + 1, 4 * h:4 * h + 4], np_(cache.k[l:l + 1, h:h + 1]),
-                                           np_(cache.k_sf[l:l + 1, h:h + 1]), kgn[l:l + 1, h:h + 1],
-                                           np_(cache.v[l:l + 1, h:h + 1]), np_(cache.v_sf[l:l + 1, h:h + 1]),
-                                           vgn[l:l + 1, h:h + 1], 1.0 / np.sqrt(D))
+    for (l, h) in pairs:
+        pkq, pks = oracle.kv_encode(np.concatenate(kin[(l, h)], axis=1), kgn[l:l + 1, h:h + 1])
+        pvq, pvs = oracle.kv_encode(np.concatenate(vin[(l, h)], axis=1), vgn[l:l + 1, h:h + 1])
+        want = oracle.decode_attention_f64(bits(qv)[l:l + 1, 4 * h:4 * h + 4], pkq, pks, kgn[l:l + 1, h:h + 1],
+                                           pvq, pvs, vgn[l:l + 1, h:h + 1], 1.0 / np.sqrt(D))
         err = rel_frobenius(out[l:l + 1, 4 * h:4 * h + 4], want)
         assert err <= QK_TOL, f"attention l={l} h={h}: rel Frobenius {err:.3e}"
-    del cache, logits
+    del cache

@@ -110,25 +110,34 @@ def test_mx_rejects_bad_shapes():
     assert L.nvfp4_mxfp4_quantize(None, 0, 64, None, None, None) == 0                  # empty: no-op
 
 
+def _mx_quantized(x):
+    """x in MXFP4 on the GPU and by the oracle.  The bytes must agree, and the
+    expected GEMM is then computed from the oracle's encoding alone."""
+    q, sf = nv.mxfp4_quantize(x)
+    oq, osf = oracle.mx_quantize(bits(x))
+    assert np.array_equal(np_(q), oq) and np.array_equal(np_(sf), osf), "GPU MXFP4 bytes differ from the oracle's"
+    return (q, sf), (oq, osf)
+
+
 def _mx_operands(M, N, K, seed, sa=1.0, sb=1.0):
     gen = torch.Generator().manual_seed(seed)
     a = (torch.randn((M, K), generator=gen) * sa).to(torch.bfloat16).cuda()
     b = (torch.randn((N, K), generator=gen) * sb).to(torch.bfloat16).cuda()
-    aq, asf = nv.mxfp4_quantize(a)
-    bq, bsf = nv.mxfp4_quantize(b)
-    return aq, asf, bq, bsf
+    (aq, asf), oa = _mx_quantized(a)
+    (bq, bsf), ob = _mx_quantized(b)
+    return aq, asf, bq, bsf, oa, ob
 
 
 @pytest.mark.parametrize("M,N,K", [(256, 256, 256), (64, 96, 96), (300, 257, 544), (1, 1, 32), (512, 384, 2048),
                                    (130, 70, 7168), (256, 512, 4096)])
 def test_mx_gemm_matches_oracle(M, N, K):
     print("case: mx gemm", M, N, K, flush=True)
-    aq, asf, bq, bsf = _mx_operands(M, N, K, M * 5 + N + K)
+    aq, asf, bq, bsf, oa, ob = _mx_operands(M, N, K, M * 5 + N + K)
     c = Guarded((M, N), torch.float32)
     nv.mxfp4_gemm(aq, asf, bq, bsf, out=c.view)
     torch.cuda.synchronize()
     c.check()
-    want = oracle.mx_gemm_f64(np_(aq), np_(asf), np_(bq), np_(bsf))
+    want = oracle.mx_gemm_f64(oa[0], oa[1], ob[0], ob[1])
     err = rel_frobenius(np_(c.view), want)
     assert err <= TOL, f"rel Frobenius {err:.3e}"
 
@@ -186,11 +195,11 @@ def test_mx_gemm_full_size_sampled_rows():
     rows of C (all 2048 columns) against fp64."""
     print("case: mx gemm 8192x2048x7168 seed 105", flush=True)
     a, b = synth.gemm_operands(device="cuda")
-    aq, asf = nv.mxfp4_quantize(a)
-    bq, bsf = nv.mxfp4_quantize(b)
+    (aq, asf), oa = _mx_quantized(a)
+    (bq, bsf), ob = _mx_quantized(b)
     c = nv.mxfp4_gemm(aq, asf, bq, bsf)
     torch.cuda.synchronize()
     rows = np.sort(np.random.default_rng(3).choice(8192, 96, replace=False))
-    want = oracle.mx_gemm_f64(np_(aq), np_(asf), np_(bq), np_(bsf), rows=rows)
+    want = oracle.mx_gemm_f64(oa[0], oa[1], ob[0], ob[1], rows=rows)
     err = rel_frobenius(np_(c[torch.from_numpy(rows).cuda()]), want)
     assert err <= TOL, f"rel Frobenius {err:.3e}"
