@@ -265,14 +265,22 @@ def run_extras(nv, synth, torch, which):
         att = torch.empty((L, 4 * H, D), dtype=torch.float32, device="cuda")
         aws = torch.empty(max(cache.attention_workspace_bytes(4 * H, T), 16), dtype=torch.uint8, device="cuda")
         matt = timed(torch, lambda: cache.decode_attention(qv, T, D ** -0.5, out=att, workspace=aws), 20, flush)
+        RL = 4                                         # kv_read: K and V of 4 layers, every token, to bf16
+        kr = torch.empty((RL, H, T, D), dtype=torch.bfloat16, device="cuda")
+        vr = torch.empty_like(kr)
+        mrd = timed(torch, lambda: cache.read(0, RL, 0, T, k_out=kr, v_out=vr), 20, flush)
+        del kr, vr
         nvals = L * H * D * T
         app_bytes = 2 * nvals * 2 + 2 * (nvals // 2 + nvals // 16)
         qk_bytes = nvals // 2 + nvals // 16 + L * 4 * H * T * 4 + qv.numel() * 2
         att_bytes = 2 * (nvals // 2 + nvals // 16) + qv.numel() * 2 + att.numel() * 4   # K and V once
+        rvals = RL * H * D * T
+        rd_bytes = 2 * (rvals // 2 + rvals // 16) + 2 * rvals * 2                        # codes + scales in, bf16 out
         rows["kv_32x8x128_131072"] = {
             "append_512x256": {"ms": ma, "ms_per_chunk": ma / (T // C), **roof(app_bytes, ma, HBM_PEAK_GBS, "GB/s")},
             "decode_qk_32q": {"ms": mqk, **roof(qk_bytes, mqk, HBM_PEAK_GBS, "GB/s")},
             "decode_attention_32q": {"ms": matt, **roof(att_bytes, matt, HBM_PEAK_GBS, "GB/s")},
+            "read_4_layers_all_tokens": {"ms": mrd, **roof(rd_bytes, mrd, HBM_PEAK_GBS, "GB/s")},
             "cache_bytes": cache.nbytes()}
         del chunks, cache, logits
         torch.cuda.empty_cache()

@@ -27,6 +27,7 @@ namespace nvfp4 {
 // kKVU chunks of 64 half blocks per trip with all their loads in flight, and
 // the workgroup's first loads are issued before it builds the scale's table.
 constexpr int kKVU = 2;
+constexpr int kKVReadU = 4;   // half blocks per lane per trip of kv_read (loads in flight)
 
 template <bool kPow2>
 __device__ __forceinline__ void kv_append_load(const u32x4* __restrict__ src, int64_t base, int64_t total,
@@ -114,20 +115,30 @@ __global__ void __launch_bounds__(kThreads) kv_read_kernel(nvfp4_kv_cache c, int
   u32x4* out = is_v ? v_out : k_out;
   if (!out) return;
   const int l = layer0 + li;
-  const int H = c.kv_heads, bpr = c.head_dim / kBlock;
+  const int H = c.kv_heads, hpr = c.head_dim / 8;                  // half blocks per token
   const float g = (is_v ? c.v_g : c.k_g)[l * H + h];
-  const u32x2* sq = (const u32x2*)(is_v ? c.v : c.k);
-  const uint8_t* ssf = is_v ? c.v_sf : c.k_sf;
+  // tokens [t0, t0 + n) of (l, h) are contiguous in the cache and in the
+  // output: one lane per half block (4 code bytes in, 16 bf16 bytes out), so
+  // a wave's stores cover 1 KiB without gaps
   const int64_t row0 = ((int64_t)l * H + h) * c.capacity + t0;
-  const int64_t orow0 = ((int64_t)li * H + h) * n;
-  const int64_t nblk = n * bpr;
-  for (int64_t b = (int64_t)blockIdx.x * kThreads + threadIdx.x; b < nblk; b += (int64_t)gridDim.x * kThreads) {
-    const u32x2 cw = sq[row0 * bpr + b];
-    const float s = e4m3_value(ssf[row0 * bpr + b]);
-    const int64_t o = orow0 * bpr + b;
-    out[2 * o] = kv_dequant_half(cw.x, s, g);
-    out[2 * o + 1] = kv_dequant_half(cw.y, s, g);
+  const uint32_t* sq = (const uint32_t*)(is_v ? c.v : c.k) + row0 * hpr;
+  const uint8_t* ssf = (is_v ? c.v_sf : c.k_sf) + row0 * (hpr / 2);
+  u32x4* o = out + ((int64_t)li * H + h) * n * hpr;
+  const int64_t nh = n * hpr;
+  const int64_t step = (int64_t)gridDim.x * kThreads;
+  int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  for (; i + (kKVReadU - 1) * step < nh; i += kKVReadU * step) {
+    uint32_t cw[kKVReadU];
+    uint8_t sb[kKVReadU];
+#pragma unroll
+    for (int u = 0; u < kKVReadU; ++u) {
+      cw[u] = __builtin_nontemporal_load(sq + i + u * step);
+      sb[u] = ssf[(i + u * step) >> 1];
+    }
+#pragma unroll
+    for (int u = 0; u < kKVReadU; ++u) o[i + u * step] = kv_dequant_half(cw[u], e4m3_value(sb[u]), g);
   }
+  for (; i < nh; i += step) o[i] = kv_dequant_half(sq[i], e4m3_value(ssf[i >> 1]), g);
 }
 
 // Decode-step QK: grid (token tiles, kv_heads, layers).  The grp query heads
@@ -389,8 +400,8 @@ nvfp4_status nvfp4_kv_read(const nvfp4_kv_cache* c, int32_t layer0, int32_t nlay
   if (n == 0 || nlayers == 0 || (!k_out && !v_out)) return NVFP4_OK;
   if (!nvfp4host::aligned16(k_out) || !nvfp4host::aligned16(v_out)) return NVFP4_EALIGN;
   if ((st = nvfp4host::check_device())) return st;
-  const int64_t blocks = n * (c->head_dim / kBlock);
-  const int tiles = tiles_for(blocks, (int64_t)c->kv_heads * 2 * nlayers);
+  const int64_t halves = n * (c->head_dim / 8);
+  const int tiles = tiles_for(halves, (int64_t)c->kv_heads * 2 * nlayers);
   kv_read_kernel<<<dim3(tiles, c->kv_heads, 2 * nlayers), kThreads, 0, (hipStream_t)stream>>>(
       *c, layer0, t0, n, (u32x4*)k_out, (u32x4*)v_out);
   NVFP4_LAUNCH_CHECK();
