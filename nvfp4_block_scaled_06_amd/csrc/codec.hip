@@ -705,6 +705,16 @@ int wgs_per_tensor(int64_t batch, int64_t hb_per_tensor) {
   return (int)std::min<int64_t>(per, 65535);
 }
 
+// Workgroups per tensor when every lane takes its kU half blocks once (the
+// grid-stride loop only runs past 65535 workgroups).  Workgroups are
+// dispatched tensor by tensor, so the stores in flight stay within one or two
+// tensors; with ~16 resident workgroups per CU covering all tensors at once,
+// the dequantize of 64 x 2048 x 7168 ran 0.49 ms against 0.42 ms.
+int one_pass_wgs(int64_t hb_per_tensor) {
+  const int64_t need = (hb_per_tensor + (int64_t)kThreads * kU - 1) / ((int64_t)kThreads * kU);
+  return (int)std::max<int64_t>(1, std::min<int64_t>(need, 65535));
+}
+
 int amax_wgs_per_tensor(int64_t batch, int64_t vec_per_tensor) {
   const int64_t target = (int64_t)nvfp4host::num_cus() * 32;
   int64_t per = (target + batch - 1) / batch;
@@ -911,7 +921,7 @@ nvfp4_status nvfp4_dequantize(const uint8_t* q, const uint8_t* sf, const float* 
   if ((st = nvfp4host::check_device())) return st;
   hipStream_t s = (hipStream_t)stream;
   const int64_t hb = n / 8;
-  const int p = wgs_per_tensor(batch, hb);
+  const int p = one_pass_wgs(hb);
   dequant_kernel<<<dim3(p, (unsigned)batch), kThreads, 0, s>>>((const uint32_t*)q, sf, g, hb, (u32x4*)y);
   NVFP4_LAUNCH_CHECK();
   return NVFP4_OK;

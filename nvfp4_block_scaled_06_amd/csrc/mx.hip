@@ -507,10 +507,14 @@ namespace {
 
 using namespace nvfp4;
 
+// One pass: every lane takes its kMxU quarter blocks once (the grid-stride
+// loop only runs past 2^30 workgroups).  Workgroups are dispatched in order,
+// so the stores in flight stay close together; 16 resident workgroups per CU
+// striding over the whole tensor ran the 64 x 2048 x 7168 quantize in
+// 0.51 ms against 0.395 ms, the dequantize in 0.505 against 0.42 ms.
 int mx_grid(int64_t nq) {
-  const int64_t target = (int64_t)nvfp4host::num_cus() * 16;
   const int64_t most = std::max<int64_t>(1, (nq + (int64_t)kThreads * kMxU - 1) / ((int64_t)kThreads * kMxU));
-  return (int)std::min(target, most);
+  return (int)std::min<int64_t>(most, (int64_t)1 << 30);
 }
 
 }  // namespace
