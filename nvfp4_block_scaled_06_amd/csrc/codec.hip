@@ -569,52 +569,40 @@ __device__ __forceinline__ void onchip_publish(uint32_t* ws, int t, uint32_t m) 
 // (bit 31 set), or 0 after the spin limit (error flag raised).
 __device__ __forceinline__ uint32_t onchip_wait(uint32_t* ws, int t, int G) {
   const int lane = threadIdx.x & 63;
-  const uint32_t* slots = fused_line(ws, t, 0);
+  // One 16-byte load per lane reads 256 slots (a few cache lines per poll
+  // instead of a request per slot).  The loads carry the agent-coherent
+  // cache policy of a relaxed agent-scope atomic load (sc1), and each slot
+  // is one aligned word written by one atomic store, so no slot tears.  The
+  // resource spans the tensor's line set: words past it read as zero and
+  // words past G count as filled.
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc(fused_line(ws, t, 0), 0, (int)(kTensorWords * 4), kBufferWord3);
   for (uint32_t it = 0; it < kSpinLimit; ++it) {
     uint32_t mx = 0, ok = 1;
-    for (int k = lane; k < G; k += 64) {
-      const uint32_t s = __hip_atomic_load(slots + k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      ok &= s >> 31;
-      mx = mx > s ? mx : s;
+    for (int base = 0; base < G; base += 256) {
+      const u32x4 v = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, (base + 4 * lane) * 4, 0,
+                                                                                      kCoherentLoad));
+      const int i = base + 4 * lane;
+      ok &= (i >= G || (v.x >> 31)) && (i + 1 >= G || (v.y >> 31)) && (i + 2 >= G || (v.z >> 31)) &&
+            (i + 3 >= G || (v.w >> 31));
+      const uint32_t m2 = v.x > v.y ? v.x : v.y, m3 = v.z > v.w ? v.z : v.w;
+      const uint32_t m4 = m2 > m3 ? m2 : m3;
+      mx = mx > m4 ? mx : m4;
     }
     if (__builtin_amdgcn_ballot_w64(ok == 0) == 0) return wave_max_u32(mx);
-    __builtin_amdgcn_s_sleep(1);
+    __builtin_amdgcn_s_sleep(4);
   }
   if (lane == 0) __hip_atomic_store(&((FusedHeader*)ws)->error, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   return 0u;
 }
 
-template <int kPer, int kMode>
-__global__ void __launch_bounds__(kOnchipThreads) fused_onchip_kernel(const u32x4* __restrict__ x, int batch,
-                                                                      int64_t hb, int spr, int srows, uint32_t* ws,
-                                                                      float* __restrict__ gout,
-                                                                      uint32_t* __restrict__ q,
-                                                                      uint8_t* __restrict__ sf) {
-  static_assert(kPer % 2 == 0 && kPer <= kOnchipMaxPer, "pieces move in pairs");
-  static_assert(kMode == kOn1D || kPer == 16, "a 2D strip is 16 rows");
-  __shared__ OnchipShared sh;
-  __shared__ __attribute__((aligned(16))) u32x4 L[kPer][kOnchipData];
-  const int G = gridDim.x;
-  if (wave_id() < kOnchipDataWaves) {
-    u32x4 a[kPer], b[kPer];
-    const OnchipMap mp = onchip_map<kPer, kMode>(spr, srows);
-    onchip_dma(L, tensor_rsrc(x, 0, batch, hb * 16), mp, 0, kPer);
-    wait_vmcnt<0>();
-#pragma unroll
-    for (int p = 0; p < kPer; p += 2) lds_read2(&L[p][threadIdx.x], &L[p + 1][threadIdx.x], a[p], a[p + 1]);
-    onchip_dma(L, tensor_rsrc(x, 1, batch, hb * 16), mp, 0, kPer);
-    const uint32_t m = onchip_wave_max<kPer>(a);
-    if ((threadIdx.x & 63) == 0) sh.red[threadIdx.x >> 6] = m;
-    lds_barrier();                                     // maxima of tensor 0
-    int t = 0;
-    for (; t + 1 < batch; t += 2) {
-      onchip_data_step<kPer, kMode>(x, t, batch, hb, mp, a, b, L, q, sf, sh);
-      onchip_data_step<kPer, kMode>(x, t + 1, batch, hb, mp, b, a, L, q, sf, sh);
-    }
-    if (t < batch) onchip_data_step<kPer, kMode>(x, t, batch, hb, mp, a, b, L, q, sf, sh);
-    return;
-  }
-  // synchronization wave
+// Synchronization wave of the on-chip quantize kernels: per tensor t, it
+// publishes the workgroup's maximum of t+1 (gathered in sh.red by the data
+// waves), waits for every workgroup's maximum of t, and hands g's table and
+// r6 to the data waves; it meets them at two LDS barriers per tensor plus
+// one before the first.
+__device__ __forceinline__ void onchip_sync_wave(uint32_t* ws, int batch, int G, float* __restrict__ gout,
+                                                 OnchipShared& sh) {
   const int lane = threadIdx.x & 63;
   auto red_max = [&]() {
     uint32_t r = sh.red[0];
@@ -651,6 +639,221 @@ __global__ void __launch_bounds__(kOnchipThreads) fused_onchip_kernel(const u32x
       __hip_atomic_store(base + i, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (lane == 0) __hip_atomic_store(&((FusedHeader*)ws)->done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
+}
+
+
+template <int kPer, int kMode>
+__global__ void __launch_bounds__(kOnchipThreads) fused_onchip_kernel(const u32x4* __restrict__ x, int batch,
+                                                                      int64_t hb, int spr, int srows, uint32_t* ws,
+                                                                      float* __restrict__ gout,
+                                                                      uint32_t* __restrict__ q,
+                                                                      uint8_t* __restrict__ sf) {
+  static_assert(kPer % 2 == 0 && kPer <= kOnchipMaxPer, "pieces move in pairs");
+  static_assert(kMode == kOn1D || kPer == 16, "a 2D strip is 16 rows");
+  __shared__ OnchipShared sh;
+  __shared__ __attribute__((aligned(16))) u32x4 L[kPer][kOnchipData];
+  const int G = gridDim.x;
+  if (wave_id() < kOnchipDataWaves) {
+    u32x4 a[kPer], b[kPer];
+    const OnchipMap mp = onchip_map<kPer, kMode>(spr, srows);
+    onchip_dma(L, tensor_rsrc(x, 0, batch, hb * 16), mp, 0, kPer);
+    wait_vmcnt<0>();
+#pragma unroll
+    for (int p = 0; p < kPer; p += 2) lds_read2(&L[p][threadIdx.x], &L[p + 1][threadIdx.x], a[p], a[p + 1]);
+    onchip_dma(L, tensor_rsrc(x, 1, batch, hb * 16), mp, 0, kPer);
+    const uint32_t m = onchip_wave_max<kPer>(a);
+    if ((threadIdx.x & 63) == 0) sh.red[threadIdx.x >> 6] = m;
+    lds_barrier();                                     // maxima of tensor 0
+    int t = 0;
+    for (; t + 1 < batch; t += 2) {
+      onchip_data_step<kPer, kMode>(x, t, batch, hb, mp, a, b, L, q, sf, sh);
+      onchip_data_step<kPer, kMode>(x, t + 1, batch, hb, mp, b, a, L, q, sf, sh);
+    }
+    if (t < batch) onchip_data_step<kPer, kMode>(x, t, batch, hb, mp, a, b, L, q, sf, sh);
+    return;
+  }
+  onchip_sync_wave(ws, batch, G, gout, sh);
+}
+
+// ------------------------------------------------------------ fused, four tensors on chip
+// The 1D on-chip quantize with each tensor slice held in one of three
+// register sets and one LDS staging set: data thread i of workgroup w owns
+// half blocks w*S + p*D + i (p < kPer) of every tensor, as above.  Tensor t
+// is encoded from its register set; the set is then refilled from the LDS
+// stage with tensor t+3, whose maximum is taken right there, and the stage
+// is refilled with tensor t+4 by buffer-to-LDS loads.  A workgroup's
+// maximum of t+3 is published one step later and the amax of t+1 is
+// gathered during step t, so a tensor's maximum is published two steps
+// before any workgroup needs its amax: one slow workgroup (late data, a slow
+// fabric round trip) does not hold up the others unless it falls two steps
+// behind.  A step is one barrier:
+//   data waves:  barrier; encode t (table t); wait for own stage pieces of
+//                t+3, move them into t's register set, reduce t+3's maximum
+//                into LDS; reissue the stage pieces for t+4.
+//   sync wave:   barrier; publish the maximum of t+2 (reduced last step);
+//                gather the amax of t+1 and build its table.
+// Each data wave reads back only the stage pieces its own lanes loaded, so a
+// wave refills its part of the stage as soon as its own reads returned.
+// The compiler does not track buffer-to-LDS loads: the wait before the move
+// names the count explicitly (a step issues 2*kPer stores after the stage
+// loads it waits for).
+struct Reg3Shared {
+  double table[2][128];               // fp64 reciprocal of every block divisor, tensors of either parity
+  double r6[2];                       // reciprocal of d6 = RN32(6 g)
+  uint32_t red[2][kOnchipDataWaves];  // per-data-wave maxima of t+3, by the parity of the step t
+  uint32_t red0[3][kOnchipDataWaves]; // per-data-wave maxima of tensors 0..2 (prologue)
+};
+
+template <int kPer>
+__device__ __forceinline__ void reg3_load(u32x4 (&R)[kPer], const u32x4* __restrict__ x, int t, int batch, int64_t hb,
+                                          int voff) {
+  const __amdgpu_buffer_rsrc_t rs = tensor_rsrc(x, t, batch, hb * 16);
+#pragma unroll
+  for (int p = 0; p < kPer; ++p)
+    R[p] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, voff, p * kOnchipData * 16, kStreamLoad));
+}
+
+// One LDS read of 16 bytes, complete on return.
+__device__ __forceinline__ u32x4 lds_read1(const u32x4* a) {
+  u32x4 r;
+  asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(r) : "v"((uint32_t)(uintptr_t)a) : "memory");
+  return r;
+}
+
+// One step, piece by piece: encode piece p of tensor t and store it, then
+// move the stage's piece p (tensor t+3) into the freed registers and reissue
+// that stage slot for tensor t+4.  Per piece a wave issues two stores and
+// one stage load, so the stage load of piece p issued a step earlier has
+// exactly 3*kPer - 1 younger memory operations when piece p is moved (the
+// prologue issues its stage loads in the same pattern).  The encode (VALU),
+// the move (LDS) and the loads and stores (memory) of a wave interleave, and
+// the waves of a compute unit overlap them.
+template <int kPer>
+__device__ __forceinline__ void reg3_step(const u32x4* __restrict__ x, int t, int batch, int64_t hb, int voff,
+                                          int qoff, int soff, u32x4 (&cur)[kPer], u32x4 (*L)[kOnchipData],
+                                          uint32_t* __restrict__ q, uint8_t* __restrict__ sf, Reg3Shared& sh) {
+  lds_barrier();                                       // t's table is ready; the previous maxima were taken
+  const double r6 = sh.r6[t & 1];
+  const double* table = sh.table[t & 1];
+  const __amdgpu_buffer_rsrc_t rq = tensor_rsrc(q, t, batch, hb * 4);
+  const __amdgpu_buffer_rsrc_t rsf = tensor_rsrc(sf, t, batch, hb / 2);
+  const __amdgpu_buffer_rsrc_t rx = tensor_rsrc(x, t + 4, batch, hb * 16);   // extent zero past the batch
+  const int w = threadIdx.x >> 6;
+  uint32_t m = 0;
+#pragma unroll
+  for (int p = 0; p < kPer; ++p) {
+    const uint32_t sbyte = block_scale_byte(pair_max(half_absmax_bits(cur[p])), r6);
+    const uint32_t code = encode_half(cur[p], table[sbyte]);
+    __builtin_amdgcn_raw_buffer_store_b32(code, rq, qoff, p * kOnchipData * 4, 0);
+    __builtin_amdgcn_raw_buffer_store_b8((uint8_t)sbyte, rsf, soff, p * (kOnchipData / 2), 0);
+    wait_vmcnt<3 * kPer - 1>();                        // stage piece p of tensor t+3 has landed
+    cur[p] = lds_read1(&L[p][threadIdx.x]);
+    m = pk_absmax(pk_absmax(pk_absmax(pk_absmax(m, cur[p].x), cur[p].y), cur[p].z), cur[p].w);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void_t*)&L[p][w * 64], 16, voff, p * kOnchipData * 16, 0,
+                                             kStreamLoad);
+    __builtin_amdgcn_sched_barrier(0);                 // keep each piece's operations in this order
+  }
+  sh.red[t & 1][wave_id()] = wave_max_u32(halves_max(m));   // wave-uniform value and address
+}
+
+__device__ __forceinline__ void reg3_table(Reg3Shared& sh, int t, uint32_t v, float* __restrict__ gout) {
+  const int lane = threadIdx.x & 63;
+  const float g = v ? __uint_as_float((v & 0x7fffu) << 16) / kGlobalDiv : __builtin_nanf("");
+  sh.table[t & 1][lane] = recip_entry((uint32_t)lane, g);
+  if (lane < 63) sh.table[t & 1][lane + 64] = recip_entry((uint32_t)lane + 64, g);
+  if (lane == 0) {
+    sh.r6[t & 1] = recip_d6(g);
+    if (blockIdx.x == 0) gout[t] = g;
+  }
+}
+
+__device__ __forceinline__ uint32_t reg3_red_max(const uint32_t* red) {
+  uint32_t r = red[0];
+#pragma unroll
+  for (int k = 1; k < kOnchipDataWaves; ++k) r = r > red[k] ? r : red[k];
+  return r;
+}
+
+__device__ __forceinline__ void reg3_sync_wave(uint32_t* ws, int batch, int G, float* __restrict__ gout,
+                                               Reg3Shared& sh) {
+  const int lane = threadIdx.x & 63;
+  lds_barrier();                                       // maxima of tensors 0..2
+  if (lane == 0)
+    for (int k = 0; k < 3 && k < batch; ++k) onchip_publish(ws, k, reg3_red_max(sh.red0[k]));
+  reg3_table(sh, 0, onchip_wait(ws, 0, G), gout);
+  for (int t = 0; t < batch; ++t) {
+    lds_barrier();                                     // step t: the data waves encode t
+    if (t >= 1 && t + 2 < batch && lane == 0) onchip_publish(ws, t + 2, reg3_red_max(sh.red[(t - 1) & 1]));
+    if (t + 1 < batch) reg3_table(sh, t + 1, onchip_wait(ws, t + 1, G), gout);
+  }
+  // the last workgroup out restores the slots and the counter to zero; every
+  // slot read of this workgroup has returned (the values were used above)
+  uint32_t last = 0;
+  if (lane == 0)
+    last = __hip_atomic_fetch_add(&((FusedHeader*)ws)->done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+           (uint32_t)G - 1;
+  if (__builtin_amdgcn_readfirstlane((int)last)) {
+    const size_t words = (size_t)batch * kTensorWords;
+    uint32_t* base = ws + kFusedHeaderBytes / 4;
+    for (size_t i = lane; i < words; i += 64)
+      __hip_atomic_store(base + i, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (lane == 0) __hip_atomic_store(&((FusedHeader*)ws)->done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+// Steps run in groups of three (the register sets rotate), then one or two
+// steps finish a batch that is not a multiple of three.
+template <int kPer>
+__global__ void __launch_bounds__(kOnchipThreads) fused_reg3_kernel(const u32x4* __restrict__ x, int batch, int64_t hb,
+                                                                    uint32_t* ws, float* __restrict__ gout,
+                                                                    uint32_t* __restrict__ q,
+                                                                    uint8_t* __restrict__ sf) {
+  static_assert(kPer % 2 == 0 && kPer <= kOnchipMaxPer, "pieces move in pairs");
+  __shared__ Reg3Shared sh;
+  __shared__ __attribute__((aligned(16))) u32x4 L[kPer][kOnchipData];
+  const int G = gridDim.x;
+  if (wave_id() < kOnchipDataWaves) {
+    const int lane = (int)threadIdx.x & 63;
+    const int voff = ((int)blockIdx.x * kPer * kOnchipData + (int)threadIdx.x) * 16;
+    const int qoff = voff / 4;
+    // even lanes write the pair's scale byte; odd lanes aim past the extent
+    const int soff = (lane & 1) ? (int)0x80000000u : voff / 32;
+    u32x4 a[kPer], b[kPer], c[kPer];
+    reg3_load<kPer>(a, x, 0, batch, hb, voff);
+    reg3_load<kPer>(b, x, 1, batch, hb, voff);
+    reg3_load<kPer>(c, x, 2, batch, hb, voff);
+    __builtin_amdgcn_sched_barrier(0);
+    {
+      // tensor 3 into the stage, each piece after two stores aimed at
+      // zero-extent resources: the memory operations of a step, in order
+      const __amdgpu_buffer_rsrc_t nq = tensor_rsrc(q, batch, batch, 0), ns = tensor_rsrc(sf, batch, batch, 0);
+      const __amdgpu_buffer_rsrc_t rx = tensor_rsrc(x, 3, batch, hb * 16);
+      const int w = threadIdx.x >> 6;
+#pragma unroll
+      for (int p = 0; p < kPer; ++p) {
+        __builtin_amdgcn_raw_buffer_store_b32(0u, nq, qoff, p * kOnchipData * 4, 0);
+        __builtin_amdgcn_raw_buffer_store_b8((uint8_t)0, ns, soff, p * (kOnchipData / 2), 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void_t*)&L[p][w * 64], 16, voff, p * kOnchipData * 16, 0,
+                                                 kStreamLoad);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    sh.red0[0][wave_id()] = onchip_wave_max<kPer>(a);
+    sh.red0[1][wave_id()] = onchip_wave_max<kPer>(b);
+    sh.red0[2][wave_id()] = onchip_wave_max<kPer>(c);
+    lds_barrier();                                     // maxima of tensors 0..2
+    int t = 0;
+    for (; t + 3 <= batch; t += 3) {
+      reg3_step<kPer>(x, t, batch, hb, voff, qoff, soff, a, L, q, sf, sh);
+      reg3_step<kPer>(x, t + 1, batch, hb, voff, qoff, soff, b, L, q, sf, sh);
+      reg3_step<kPer>(x, t + 2, batch, hb, voff, qoff, soff, c, L, q, sf, sh);
+    }
+    if (t < batch) reg3_step<kPer>(x, t, batch, hb, voff, qoff, soff, a, L, q, sf, sh);
+    if (t + 1 < batch) reg3_step<kPer>(x, t + 1, batch, hb, voff, qoff, soff, b, L, q, sf, sh);
+    wait_vmcnt<0>();                                   // no stage load still writing LDS at exit
+    return;
+  }
+  reg3_sync_wave(ws, batch, G, gout, sh);
 }
 
 // ------------------------------------------------------------ dequantize
@@ -841,23 +1044,22 @@ nvfp4_status nvfp4_quantize(const uint16_t* x, int64_t batch, int64_t rows, int6
       int bt = (int)batch;
       uint32_t* ws = (uint32_t*)workspace;
       uint32_t* qa = (uint32_t*)q;
-      int spr = 0, srows = 0;                          // unused by the 1D layout
-      void* args[] = {&xa, &bt, (void*)&hb, &spr, &srows, &ws, &g, &qa, &sf};
       const int64_t slice = (int64_t)onchip_per * kOnchipData;
       const int G = (int)((hb + slice - 1) / slice);
       const void* fn = nullptr;
       const void* fns[kOnchipMaxPer / 2] = {
-          (const void*)fused_onchip_kernel<2, kOn1D>,
-          (const void*)fused_onchip_kernel<4, kOn1D>,
-          (const void*)fused_onchip_kernel<6, kOn1D>,
-          (const void*)fused_onchip_kernel<8, kOn1D>,
-          (const void*)fused_onchip_kernel<10, kOn1D>,
-          (const void*)fused_onchip_kernel<12, kOn1D>,
-          (const void*)fused_onchip_kernel<14, kOn1D>,
-          (const void*)fused_onchip_kernel<16, kOn1D>,
+          (const void*)fused_reg3_kernel<2>,
+          (const void*)fused_reg3_kernel<4>,
+          (const void*)fused_reg3_kernel<6>,
+          (const void*)fused_reg3_kernel<8>,
+          (const void*)fused_reg3_kernel<10>,
+          (const void*)fused_reg3_kernel<12>,
+          (const void*)fused_reg3_kernel<14>,
+          (const void*)fused_reg3_kernel<16>,
       };
       fn = fns[onchip_per / 2 - 1];
-      hipError_t e = hipLaunchCooperativeKernel(fn, dim3(G), dim3(kOnchipThreads), args, 0, s);
+      void* args3[] = {&xa, &bt, (void*)&hb, &ws, &g, &qa, &sf};
+      hipError_t e = hipLaunchCooperativeKernel(fn, dim3(G), dim3(kOnchipThreads), args3, 0, s);
       if (e != hipSuccess) {
         nvfp4host::set_hip_error(e);
         return NVFP4_EHIP;

@@ -166,14 +166,35 @@ constexpr int kBufferWord3 = 0x00020000;
 // buffer-to-LDS loads: 0.573 -> 0.530 ms over 1.88 GB of bf16.
 constexpr int kStreamLoad = 2;
 
+// Cache-policy operand of a load that must observe other compute units'
+// atomic stores: sc1, the policy the compiler gives a relaxed agent-scope
+// atomic load on gfx950 (the L2 of each XCD is not coherent with the others).
+constexpr int kCoherentLoad = 16;
+
 // ---------------------------------------------------------------- reductions
-__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    uint32_t o = (uint32_t)__shfl_xor((int)v, off, 64);
-    v = v > o ? v : o;
+// Maximum over the 64 lanes of a wave (every lane active), returned
+// wave-uniform.  DPP moves reduce each row of 16 lanes (quad swaps, then
+// the half-row and row mirrors); four lane reads combine the rows.  No
+// address registers are needed, unlike a shuffle through LDS permutes.
+__device__ __forceinline__ uint32_t dpp_max(uint32_t v, int ctrl) {
+  uint32_t o = 0;
+  switch (ctrl) {   // the control word must be a compile-time constant
+    case 0xB1: o = (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0xB1, 0xF, 0xF, false); break;
+    case 0x4E: o = (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x4E, 0xF, 0xF, false); break;
+    case 0x141: o = (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x141, 0xF, 0xF, false); break;
+    default: o = (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x140, 0xF, 0xF, false); break;
   }
-  return v;
+  return v > o ? v : o;
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = dpp_max(v, 0xB1);    // quad_perm(1,0,3,2)
+  v = dpp_max(v, 0x4E);    // quad_perm(2,3,0,1)
+  v = dpp_max(v, 0x141);   // row_half_mirror
+  v = dpp_max(v, 0x140);   // row_mirror: every lane holds its row's maximum
+  const uint32_t a = (uint32_t)__builtin_amdgcn_readlane((int)v, 0), b = (uint32_t)__builtin_amdgcn_readlane((int)v, 16);
+  const uint32_t c = (uint32_t)__builtin_amdgcn_readlane((int)v, 32), d = (uint32_t)__builtin_amdgcn_readlane((int)v, 48);
+  const uint32_t ab = a > b ? a : b, cd = c > d ? c : d;
+  return ab > cd ? ab : cd;
 }
 
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)); }
