@@ -25,6 +25,7 @@
 //              (agent-scope atomics), then encodes its slice of tensor t-1,
 //              read again newest-first.
 #include <algorithm>
+#include <utility>
 
 #include "common.hpp"
 
@@ -713,47 +714,116 @@ __device__ __forceinline__ void reg3_load(u32x4 (&R)[kPer], const u32x4* __restr
     R[p] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, voff, p * kOnchipData * 16, kStreamLoad));
 }
 
-// One LDS read of 16 bytes, complete on return.
-__device__ __forceinline__ u32x4 lds_read1(const u32x4* a) {
+// One LDS read of 16 bytes at base + kOff (an immediate offset), complete on
+// return.
+template <int kOff>
+__device__ __forceinline__ u32x4 lds_read_at(uint32_t base) {
+  static_assert(kOff >= 0 && kOff < 65536, "ds_read offset field");
   u32x4 r;
-  asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(r) : "v"((uint32_t)(uintptr_t)a) : "memory");
+  asm volatile("ds_read_b128 %0, %1 offset:%2\n\ts_waitcnt lgkmcnt(0)" : "=v"(r) : "v"(base), "i"(kOff) : "memory");
   return r;
 }
 
+// Block maxima kept beside a register set: the pair maximum (bf16 magnitude
+// bits of the 16-value block) of piece p in half p & 1 of word p / 2.
+template <int kPer>
+struct BlockMax {
+  uint32_t w[kPer / 2];
+};
+
+template <int kPer>
+__device__ __forceinline__ uint32_t bm_get(const BlockMax<kPer>& bm, int p) {
+  return (p & 1) ? bm.w[p / 2] >> 16 : bm.w[p / 2] & 0xffffu;
+}
+// bam << 16 as a float: the block amax (the halves' other bits are zero).
+template <int kPer>
+__device__ __forceinline__ float bm_value(const BlockMax<kPer>& bm, int p) {
+  return __uint_as_float((p & 1) ? bm.w[p / 2] & 0xffff0000u : bm.w[p / 2] << 16);
+}
+template <int kPer>
+__device__ __forceinline__ void bm_set(BlockMax<kPer>& bm, int p, uint32_t h) {
+  bm.w[p / 2] = (p & 1) ? __builtin_amdgcn_perm(h, bm.w[p / 2], 0x05040100u)    // h into the high half
+                        : __builtin_amdgcn_perm(h, bm.w[p / 2], 0x03020504u);   // h into the low half
+}
+
+// Block maxima of a whole set (prologue); returns the wave maximum.
+template <int kPer>
+__device__ __forceinline__ uint32_t reg3_block_max(const u32x4 (&R)[kPer], BlockMax<kPer>& bm) {
+  uint32_t m = 0;
+#pragma unroll
+  for (int p = 0; p < kPer; ++p) {
+    const uint32_t h = pair_max(half_absmax_bits(R[p]));
+    m = m > h ? m : h;
+    if (p & 1) bm.w[p / 2] |= h << 16;
+    else bm.w[p / 2] = h;
+  }
+  return wave_max_u32(m);
+}
+
+// The stage: 16-byte slot (p, i) at byte p * D * 16 + i * 16 of L, with D
+// data threads; read back with immediate offsets from two bases (the
+// offset field holds 16 bits).
+constexpr int kStagePiece = kOnchipData * 16;          // 7168 bytes per piece
+constexpr int kStageSplit = 65536 / kStagePiece + 1;   // pieces reachable from the first base (10)
+
+template <int kPer, int p>
+__device__ __forceinline__ u32x4 stage_read(uint32_t b0, uint32_t b1) {
+  if constexpr (p < kStageSplit) return lds_read_at<p * kStagePiece>(b0);
+  else return lds_read_at<(p - kStageSplit) * kStagePiece>(b1);
+}
+
 // One step, piece by piece: encode piece p of tensor t and store it, then
-// move the stage's piece p (tensor t+3) into the freed registers and reissue
-// that stage slot for tensor t+4.  Per piece a wave issues two stores and
-// one stage load, so the stage load of piece p issued a step earlier has
-// exactly 3*kPer - 1 younger memory operations when piece p is moved (the
-// prologue issues its stage loads in the same pattern).  The encode (VALU),
-// the move (LDS) and the loads and stores (memory) of a wave interleave, and
-// the waves of a compute unit overlap them.
+// move the stage's piece p (tensor t+3) into the freed registers (taking its
+// block maximum) and reissue that stage slot for tensor t+4.  Per piece a
+// wave issues two stores and one stage load, so the stage load of piece p
+// issued a step earlier has exactly 3*kPer - 1 younger memory operations
+// when piece p is moved (the prologue issues its stage loads in the same
+// pattern).  The encode (VALU), the move (LDS) and the loads and stores
+// (memory) of a wave interleave, and the waves of a compute unit overlap
+// them.
+template <int kPer, int p>
+__device__ __forceinline__ void reg3_piece(u32x4 (&cur)[kPer], BlockMax<kPer>& bm, uint32_t& m, double r6,
+                                           const double* table, __amdgpu_buffer_rsrc_t rq, __amdgpu_buffer_rsrc_t rsf,
+                                           __amdgpu_buffer_rsrc_t rx, int qoff, int soff, int voff, uint32_t b0,
+                                           uint32_t b1, lds_void_t* stage_w) {
+  const uint32_t sbyte = e4m3_rne_sat(rn32((double)bm_value<kPer>(bm, p) * r6));
+  const uint32_t code = encode_half(cur[p], table[sbyte]);
+  __builtin_amdgcn_raw_buffer_store_b32(code, rq, qoff, p * kOnchipData * 4, 0);
+  __builtin_amdgcn_raw_buffer_store_b8((uint8_t)sbyte, rsf, soff, p * (kOnchipData / 2), 0);
+  wait_vmcnt<3 * kPer - 1>();                          // stage piece p of tensor t+3 has landed
+  cur[p] = stage_read<kPer, p>(b0, b1);
+  const uint32_t h = pair_max(half_absmax_bits(cur[p]));
+  m = m > h ? m : h;
+  bm_set<kPer>(bm, p, h);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void_t*)((__attribute__((address_space(3))) char*)stage_w +
+                                                             p * kStagePiece),
+                                           16, voff, p * kStagePiece, 0, kStreamLoad);
+  __builtin_amdgcn_sched_barrier(0);                   // keep each piece's operations in this order
+}
+
+template <int kPer, int... P>
+__device__ __forceinline__ void reg3_pieces(std::integer_sequence<int, P...>, u32x4 (&cur)[kPer], BlockMax<kPer>& bm,
+                                            uint32_t& m, double r6, const double* table, __amdgpu_buffer_rsrc_t rq,
+                                            __amdgpu_buffer_rsrc_t rsf, __amdgpu_buffer_rsrc_t rx, int qoff, int soff,
+                                            int voff, uint32_t b0, uint32_t b1, lds_void_t* stage_w) {
+  (reg3_piece<kPer, P>(cur, bm, m, r6, table, rq, rsf, rx, qoff, soff, voff, b0, b1, stage_w), ...);
+}
+
 template <int kPer>
 __device__ __forceinline__ void reg3_step(const u32x4* __restrict__ x, int t, int batch, int64_t hb, int voff,
-                                          int qoff, int soff, u32x4 (&cur)[kPer], u32x4 (*L)[kOnchipData],
-                                          uint32_t* __restrict__ q, uint8_t* __restrict__ sf, Reg3Shared& sh) {
+                                          int qoff, int soff, u32x4 (&cur)[kPer], BlockMax<kPer>& bm, uint32_t b0,
+                                          uint32_t b1, lds_void_t* stage_w, uint32_t* __restrict__ q,
+                                          uint8_t* __restrict__ sf, Reg3Shared& sh) {
   lds_barrier();                                       // t's table is ready; the previous maxima were taken
   const double r6 = sh.r6[t & 1];
   const double* table = sh.table[t & 1];
   const __amdgpu_buffer_rsrc_t rq = tensor_rsrc(q, t, batch, hb * 4);
   const __amdgpu_buffer_rsrc_t rsf = tensor_rsrc(sf, t, batch, hb / 2);
   const __amdgpu_buffer_rsrc_t rx = tensor_rsrc(x, t + 4, batch, hb * 16);   // extent zero past the batch
-  const int w = threadIdx.x >> 6;
   uint32_t m = 0;
-#pragma unroll
-  for (int p = 0; p < kPer; ++p) {
-    const uint32_t sbyte = block_scale_byte(pair_max(half_absmax_bits(cur[p])), r6);
-    const uint32_t code = encode_half(cur[p], table[sbyte]);
-    __builtin_amdgcn_raw_buffer_store_b32(code, rq, qoff, p * kOnchipData * 4, 0);
-    __builtin_amdgcn_raw_buffer_store_b8((uint8_t)sbyte, rsf, soff, p * (kOnchipData / 2), 0);
-    wait_vmcnt<3 * kPer - 1>();                        // stage piece p of tensor t+3 has landed
-    cur[p] = lds_read1(&L[p][threadIdx.x]);
-    m = pk_absmax(pk_absmax(pk_absmax(pk_absmax(m, cur[p].x), cur[p].y), cur[p].z), cur[p].w);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void_t*)&L[p][w * 64], 16, voff, p * kOnchipData * 16, 0,
-                                             kStreamLoad);
-    __builtin_amdgcn_sched_barrier(0);                 // keep each piece's operations in this order
-  }
-  sh.red[t & 1][wave_id()] = wave_max_u32(halves_max(m));   // wave-uniform value and address
+  reg3_pieces<kPer>(std::make_integer_sequence<int, kPer>{}, cur, bm, m, r6, table, rq, rsf, rx, qoff, soff, voff, b0,
+                    b1, stage_w);
+  sh.red[t & 1][wave_id()] = wave_max_u32(m);          // wave-uniform value and address
 }
 
 __device__ __forceinline__ void reg3_table(Reg3Shared& sh, int t, uint32_t v, float* __restrict__ gout) {
@@ -819,37 +889,44 @@ __global__ void __launch_bounds__(kOnchipThreads) fused_reg3_kernel(const u32x4*
     // even lanes write the pair's scale byte; odd lanes aim past the extent
     const int soff = (lane & 1) ? (int)0x80000000u : voff / 32;
     u32x4 a[kPer], b[kPer], c[kPer];
+    BlockMax<kPer> am, bmx, cm;
     reg3_load<kPer>(a, x, 0, batch, hb, voff);
     reg3_load<kPer>(b, x, 1, batch, hb, voff);
     reg3_load<kPer>(c, x, 2, batch, hb, voff);
     __builtin_amdgcn_sched_barrier(0);
+    // the stage: this thread's slots read from two bases, this wave's slots
+    // filled through an LDS base held in scalar registers
+    const uint32_t b0 = (uint32_t)(uintptr_t)&L[0][threadIdx.x];
+    const uint32_t b1 = b0 + kStageSplit * kStagePiece;
+    lds_void_t* const stage_w =
+        (lds_void_t*)(uintptr_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uintptr_t)&L[0][threadIdx.x & ~63]);
     {
       // tensor 3 into the stage, each piece after two stores aimed at
       // zero-extent resources: the memory operations of a step, in order
       const __amdgpu_buffer_rsrc_t nq = tensor_rsrc(q, batch, batch, 0), ns = tensor_rsrc(sf, batch, batch, 0);
       const __amdgpu_buffer_rsrc_t rx = tensor_rsrc(x, 3, batch, hb * 16);
-      const int w = threadIdx.x >> 6;
 #pragma unroll
       for (int p = 0; p < kPer; ++p) {
         __builtin_amdgcn_raw_buffer_store_b32(0u, nq, qoff, p * kOnchipData * 4, 0);
         __builtin_amdgcn_raw_buffer_store_b8((uint8_t)0, ns, soff, p * (kOnchipData / 2), 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void_t*)&L[p][w * 64], 16, voff, p * kOnchipData * 16, 0,
-                                                 kStreamLoad);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rx, (lds_void_t*)((__attribute__((address_space(3))) char*)stage_w + p * kStagePiece), 16, voff,
+            p * kStagePiece, 0, kStreamLoad);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
-    sh.red0[0][wave_id()] = onchip_wave_max<kPer>(a);
-    sh.red0[1][wave_id()] = onchip_wave_max<kPer>(b);
-    sh.red0[2][wave_id()] = onchip_wave_max<kPer>(c);
+    sh.red0[0][wave_id()] = reg3_block_max<kPer>(a, am);
+    sh.red0[1][wave_id()] = reg3_block_max<kPer>(b, bmx);
+    sh.red0[2][wave_id()] = reg3_block_max<kPer>(c, cm);
     lds_barrier();                                     // maxima of tensors 0..2
     int t = 0;
     for (; t + 3 <= batch; t += 3) {
-      reg3_step<kPer>(x, t, batch, hb, voff, qoff, soff, a, L, q, sf, sh);
-      reg3_step<kPer>(x, t + 1, batch, hb, voff, qoff, soff, b, L, q, sf, sh);
-      reg3_step<kPer>(x, t + 2, batch, hb, voff, qoff, soff, c, L, q, sf, sh);
+      reg3_step<kPer>(x, t, batch, hb, voff, qoff, soff, a, am, b0, b1, stage_w, q, sf, sh);
+      reg3_step<kPer>(x, t + 1, batch, hb, voff, qoff, soff, b, bmx, b0, b1, stage_w, q, sf, sh);
+      reg3_step<kPer>(x, t + 2, batch, hb, voff, qoff, soff, c, cm, b0, b1, stage_w, q, sf, sh);
     }
-    if (t < batch) reg3_step<kPer>(x, t, batch, hb, voff, qoff, soff, a, L, q, sf, sh);
-    if (t + 1 < batch) reg3_step<kPer>(x, t + 1, batch, hb, voff, qoff, soff, b, L, q, sf, sh);
+    if (t < batch) reg3_step<kPer>(x, t, batch, hb, voff, qoff, soff, a, am, b0, b1, stage_w, q, sf, sh);
+    if (t + 1 < batch) reg3_step<kPer>(x, t + 1, batch, hb, voff, qoff, soff, b, bmx, b0, b1, stage_w, q, sf, sh);
     wait_vmcnt<0>();                                   // no stage load still writing LDS at exit
     return;
   }

@@ -56,9 +56,11 @@ __device__ __forceinline__ float e4m3_value(uint32_t b) {
   uint32_t e = b >> 3, m = b & 7u;
   return e ? __uint_as_float(((e + 120u) << 23) | (m << 20)) : (float)m * 0.001953125f;
 }
-// Nearest E4M3 byte of v >= 0 (ties to even), saturating at 448.
+// Nearest E4M3 byte of v >= 0 (ties to even), saturating at 448.  The
+// conversion writes the byte of v and that of 0.0 (0x00) into the low half
+// of a zero word, so the result is the byte itself.
 __device__ __forceinline__ uint32_t e4m3_rne_sat(float v) {
-  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(fminf(v, 448.0f), 0.0f, 0, false) & 0xffu;
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(fminf(v, 448.0f), 0.0f, 0, false);
 }
 
 // ---------------------------------------------------------------- E2M1 pairs
@@ -134,7 +136,9 @@ __device__ __forceinline__ uint32_t pair_max(uint32_t m) {
 // Encodes 8 values (one half block) into 4 code bytes (element 2i in the low
 // nibble of byte i) given the block's reciprocal r = RN64(1/d).
 __device__ __forceinline__ uint32_t encode_half(const u32x4 w, double r) {
-  uint32_t c = fp4_pair<0>(0u, q_lo(w.x, r), q_hi(w.x, r));
+  // the four conversions write all four bytes, so the first one's other
+  // bytes may start as anything (here the input word itself)
+  uint32_t c = fp4_pair<0>(w.x, q_lo(w.x, r), q_hi(w.x, r));
   c = fp4_pair<1>(c, q_lo(w.y, r), q_hi(w.y, r));
   c = fp4_pair<2>(c, q_lo(w.z, r), q_hi(w.z, r));
   return fp4_pair<3>(c, q_lo(w.w, r), q_hi(w.w, r));
