@@ -228,14 +228,16 @@ def run_extras(nv, synth, torch, which):
         x = synth.single(device="cuda")
         ws = nv.make_workspace(1, 1024, 1024)
         q, sf, g = nv.quantize(x, workspace=ws)
+        y = torch.empty_like(x)
         n = 1024 * 1024
         mq = timed(torch, lambda: nv.quantize(x, workspace=ws, out=(q, sf, g)), 50)
-        md = timed(torch, lambda: nv.dequantize(q, sf, g), 50)
+        md = timed(torch, lambda: nv.dequantize(q, sf, g, out=y), 50)
         rows["single_1024x1024"] = {
-            "note": "2.7 MB working set: launch-bound and cache-resident; warm medians",
+            "note": "2.7 MB working set: launch-bound and cache-resident; warm medians of HIP events around "
+                    "one call with preallocated outputs (host marshalling of the call included)",
             "quantize": {"ms": mq, **roof(bytes_quantize(n, 1), mq, HBM_PEAK_GBS, "GB/s")},
             "dequantize": {"ms": md, **roof(bytes_dequant(n, 1), md, HBM_PEAK_GBS, "GB/s")}}
-        del x, q, sf, g
+        del x, q, sf, g, y
     if "acts" in which:
         x = synth.activations(device="cuda")
         n = x.numel()
@@ -251,9 +253,8 @@ def run_extras(nv, synth, torch, which):
         L, H, D, T, C = 32, 8, 128, 131072, 256
         log("kv: generating 512 chunks of K/V on the GPU (16 GiB bf16)")
         chunks = [synth.kv_chunk(c, device="cuda") for c in range(T // C)]
-        gen = torch.Generator().manual_seed(104)
-        kg = (torch.rand((L, H), generator=gen) * 0.0004 + 0.0018).float()
-        cache = nv.KVCache(L, H, D, T, kg, kg.clone(), device="cuda")
+        kg, vg = calibrate_kv_scales(nv, torch, chunks, L, H)        # untimed
+        cache = nv.KVCache(L, H, D, T, kg, vg, device="cuda")
         qv = synth.kv_query(device="cuda")
         logits = torch.empty((L, 4 * H, T), dtype=torch.float32, device="cuda")
 
@@ -303,6 +304,22 @@ def run_extras(nv, synth, torch, which):
     del fbuf
     torch.cuda.empty_cache()
     return rows
+
+
+def calibrate_kv_scales(nv, torch, chunks, L, H):
+    """Per-(layer, KV head) tensor scales of K and V, fixed at cache creation
+    from a calibration pass over the whole stream: the codec's tensor-scale
+    rule g = RN32(amax / 2688), applied by nvfp4_quantize to one 16-value
+    block per (layer, head) that holds the head's amax over every chunk."""
+    kmax = torch.zeros((L, H), dtype=torch.bfloat16, device="cuda")
+    vmax = torch.zeros_like(kmax)
+    for k, v in chunks:
+        kmax = torch.maximum(kmax, k.abs().amax(dim=(1, 3)))
+        vmax = torch.maximum(vmax, v.abs().amax(dim=(1, 3)))
+    blocks = torch.zeros((2 * L * H, 1, 16), dtype=torch.bfloat16, device="cuda")
+    blocks[:, 0, 0] = torch.cat([kmax.reshape(-1), vmax.reshape(-1)])
+    _, _, g = nv.quantize(blocks)
+    return g[:L * H].reshape(L, H).clone(), g[L * H:].reshape(L, H).clone()
 
 
 def run_moe(nv, synth, torch):
@@ -416,6 +433,18 @@ def run_train(nv, synth, torch):
     return res
 
 
+def cpu_model():
+    """The host CPU's model name from /proc/cpuinfo (None if unreadable)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(synth, torch):
     """The oracle, untouched, on the whole headline workload: quantize +
     dequantize of all 64 expert matrices, two passes (about 10 s of CPU work
@@ -436,6 +465,7 @@ def cpu_baseline(synth, torch):
     dt = time.perf_counter() - t0
     nbytes = reps * (bytes_quantize(n, E) + bytes_dequant(n, E))
     return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": oracle.max_threads(), "kind": "oracle",
+            "cpu_model": cpu_model(),
             "sample": f"quantize+dequantize of all {E} expert matrices ({E}x2048x7168), {reps} passes, "
                       f"{dt:.2f} s wall"}
 
@@ -512,7 +542,7 @@ def main():
     dom = "quantize" if head["quantize_ms"] >= head["dequantize_ms"] else "dequantize"
     dom_bytes = head[f"{dom}_bytes"]
     dom_ms = head[f"{dom}_ms"]
-    kname = {"quantize": "fused_onchip_kernel<16, 0> (nvfp4_quantize, fused)" if head["flags"] == "fused"
+    kname = {"quantize": "fused_reg3_kernel<16> (nvfp4_quantize, fused)" if head["flags"] == "fused"
              else "nvfp4_quantize (two_kernel)", "dequantize": "dequant_kernel"}[dom]
     r = roof(dom_bytes, dom_ms, HBM_PEAK_GBS, "GB/s")
     line = {

@@ -29,9 +29,11 @@
  *
  * Conventions for every entry point:
  *   - All tensor pointers are DEVICE pointers owned by the caller.  The
- *     library never allocates, frees or synchronizes; every call enqueues
+ *     library never allocates or frees device memory.  Every call enqueues
  *     kernels on `stream` (a hipStream_t, NULL = the default stream) and
- *     returns.  Device-side faults surface at the caller's next sync.
+ *     returns without synchronizing, except the two calls documented as
+ *     synchronous (nvfp4_quantize_status, nvfp4_set_wait_limit).
+ *     Device-side faults surface at the caller's next sync.
  *   - Arguments are validated on the host before any launch.  On an error
  *     code nothing is launched and no output byte is written.
  *   - Inputs must be finite (not checked on the device; non-finite inputs give
@@ -40,7 +42,8 @@
  *   - Sizes are int64_t; negative sizes are NVFP4_EINVAL, zero sizes are a
  *     successful no-op.
  *   - Thread-safe; the only global state is a once-per-device architecture
- *     check and a per-thread last-HIP-error slot.
+ *     check, a per-thread last-HIP-error slot and the per-device wait limit
+ *     of nvfp4_set_wait_limit.
  */
 #ifndef NVFP4_H_
 #define NVFP4_H_
@@ -60,7 +63,8 @@ enum {
   NVFP4_EALIGN = -2,     /* a tensor base pointer is not 16-byte aligned */
   NVFP4_EWORKSPACE = -3, /* workspace missing or smaller than required */
   NVFP4_ENOTSUP = -4,    /* current device is not gfx950, or unsupported flag */
-  NVFP4_EHIP = -5        /* a HIP runtime call failed; see nvfp4_last_hip_error */
+  NVFP4_EHIP = -5,       /* a HIP runtime call failed; see nvfp4_last_hip_error */
+  NVFP4_ETIMEOUT = -6    /* nvfp4_quantize_status: a FUSED launch's bounded wait gave up */
 };
 
 /* Launch modes of nvfp4_quantize. */
@@ -94,6 +98,13 @@ int32_t nvfp4_last_hip_error(void);
  * flags: NVFP4_TWO_KERNEL or NVFP4_FUSED (same bytes either way).
  * Errors: EINVAL (null pointer with nonzero size, negative size, cols % 16),
  *   EALIGN, EWORKSPACE, ENOTSUP (unknown flag / not gfx950), EHIP.
+ * FUSED runs every workgroup of one cooperative launch through a
+ * cross-workgroup exchange of maxima; each wait is bounded (see
+ * nvfp4_set_wait_limit).  A wait that gives up -- which a cooperative launch
+ * on an otherwise idle device never needs -- does not fault: it writes NaN
+ * for the tensor scale g of that tensor, leaves its codes and scale bytes
+ * unspecified (in bounds), and sets an error word in the workspace that
+ * nvfp4_quantize_status reports.
  * ------------------------------------------------------------------------ */
 size_t nvfp4_quantize_workspace_bytes(int64_t batch, int64_t rows, int64_t cols);
 
@@ -101,6 +112,21 @@ nvfp4_status nvfp4_quantize(const uint16_t* x, int64_t batch, int64_t rows, int6
                             uint8_t* q, uint8_t* sf, float* g,
                             void* workspace, size_t workspace_bytes,
                             uint32_t flags, void* stream);
+
+/* Reports whether a FUSED nvfp4_quantize on this workspace had a bounded
+ * wait give up since the last report: synchronizes `stream` (the one the
+ * calls ran on), reads the workspace's error word, clears it, and returns
+ * NVFP4_ETIMEOUT if it was set (the affected tensors' g are NaN), else
+ * NVFP4_OK.  The only entry point that synchronizes or copies to the host.
+ * Errors: EWORKSPACE (null or too small), ENOTSUP, EHIP. */
+nvfp4_status nvfp4_quantize_status(void* workspace, size_t workspace_bytes, void* stream);
+
+/* Sets the number of polls after which every bounded wait of the
+ * cooperative kernels gives up, on the current device; returns the previous
+ * value (default 2^24, seconds of polling).  For tests and diagnostics: 0
+ * makes every wait give up at once (every kernel still runs to its end), so
+ * the timeout path can be exercised without a stalled grid.  Synchronous. */
+uint32_t nvfp4_set_wait_limit(uint32_t polls);
 
 /* Quantize with caller-supplied tensor scales g[batch] (read, not written):
  * a static or calibrated scale, no amax pass (theddari.com, "What is FP4
@@ -273,7 +299,10 @@ enum {
 
 /* Device scratch for nvfp4_quantize_ex: the single-launch 2D path's
  * exchange words, then per-workgroup partial maxima (no zero-fill needed:
- * the library clears what it relies on).  0 when batch <= 0. */
+ * the library clears what it relies on, error word included, at the start
+ * of each call; a bounded wait of that single launch that gave up is
+ * reported by nvfp4_quantize_status on the same workspace until the next
+ * nvfp4_quantize_ex call on it).  0 when batch <= 0. */
 size_t nvfp4_quantize_ex_workspace_bytes(int64_t batch);
 
 /* Variant quantize of x [batch][rows][cols] bf16 (cols % 16 == 0).  With

@@ -50,6 +50,8 @@ _SIGS = {
     "nvfp4_last_hip_error": (_I32, []),
     "nvfp4_quantize_workspace_bytes": (_SZ, [_I64, _I64, _I64]),
     "nvfp4_quantize": (_I32, [_P, _I64, _I64, _I64, _P, _P, _P, _P, _SZ, ctypes.c_uint32, _P]),
+    "nvfp4_quantize_status": (_I32, [_P, _SZ, _P]),
+    "nvfp4_set_wait_limit": (ctypes.c_uint32, [ctypes.c_uint32]),
     "nvfp4_quantize_with_scale": (_I32, [_P, _I64, _I64, _I64, _P, _P, _P, _P]),
     "nvfp4_dequantize": (_I32, [_P, _P, _P, _I64, _I64, _I64, _P, _P]),
     "nvfp4_kv_bytes": (_SZ, [ctypes.POINTER(KVCacheDesc)]),
@@ -112,9 +114,14 @@ def _need(t, dtype, name):
         raise ValueError(f"{name} must be contiguous")
 
 
-def _bits(t):
-    """bf16 tensors are passed as their uint16 bit patterns."""
-    return t
+def _shape(t, shape, name):
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _numel(t, n, name):
+    if t.numel() != n:
+        raise ValueError(f"{name} must hold {n} elements, got {t.numel()}")
 
 
 # ---------------------------------------------------------------- codec
@@ -146,12 +153,40 @@ def quantize(x, flags="two_kernel", workspace=None, out=None):
         g = torch.empty((b,), dtype=torch.float32, device=x.device)
     else:
         q, sf, g = out
+        _need(q, torch.uint8, "q")
+        _need(sf, torch.uint8, "sf")
+        _need(g, torch.float32, "g")
+        _shape(q, lead + (c // 2,), "q")
+        _shape(sf, lead + (c // 16,), "sf")
+        _numel(g, b, "g")
     if workspace is None:
         workspace = make_workspace(b, r, c, x.device)
+    _need(workspace, torch.uint8, "workspace")
     _check("nvfp4_quantize", _lib().nvfp4_quantize(
         _ptr(x), b, r, c, _ptr(q), _ptr(sf), _ptr(g), _ptr(workspace), workspace.numel(),
         _FLAGS[flags], _stream(x.device)))
     return q, sf, g
+
+
+ETIMEOUT = -6
+
+
+def quantize_status(workspace):
+    """Synchronizes the current stream and reports whether a FUSED quantize
+    on `workspace` had a bounded cross-workgroup wait give up since the last
+    report (those tensors' g are NaN).  Clears the report; returns True when
+    the calls were clean, raises NVFP4Error (status ETIMEOUT) otherwise."""
+    _need(workspace, torch.uint8, "workspace")
+    _check("nvfp4_quantize_status", _lib().nvfp4_quantize_status(
+        _ptr(workspace), workspace.numel(), _stream(workspace.device)))
+    return True
+
+
+def set_wait_limit(polls):
+    """Polls after which the cooperative kernels' bounded waits give up, on the
+    current device (default 2^24); returns the previous value.  0 makes every
+    wait give up at once: a test hook for the timeout path."""
+    return int(_lib().nvfp4_set_wait_limit(int(polls)))
 
 
 def quantize_with_scale(x, g, out=None):
@@ -166,6 +201,10 @@ def quantize_with_scale(x, g, out=None):
         sf = torch.empty(lead + (c // 16,), dtype=torch.uint8, device=x.device)
     else:
         q, sf = out
+        _need(q, torch.uint8, "q")
+        _need(sf, torch.uint8, "sf")
+        _shape(q, lead + (c // 2,), "q")
+        _shape(sf, lead + (c // 16,), "sf")
     _check("nvfp4_quantize_with_scale", _lib().nvfp4_quantize_with_scale(
         _ptr(x), b, r, c, _ptr(g), _ptr(q), _ptr(sf), _stream(x.device)))
     return q, sf
@@ -177,6 +216,11 @@ def dequantize(q, sf, g, out=None):
     _need(g, torch.float32, "g")
     c = q.shape[-1] * 2
     b, r, _ = _split(tuple(q.shape[:-1]) + (c,))
+    _shape(sf, tuple(q.shape[:-1]) + (c // 16,), "sf")
+    _numel(g, b, "g")
+    if out is not None:
+        _need(out, torch.bfloat16, "out")
+        _shape(out, tuple(q.shape[:-1]) + (c,), "out")
     y = out if out is not None else torch.empty(tuple(q.shape[:-1]) + (c,), dtype=torch.bfloat16, device=q.device)
     _check("nvfp4_dequantize", _lib().nvfp4_dequantize(
         _ptr(q), _ptr(sf), _ptr(g), b, r, c, _ptr(y), _stream(q.device)))
@@ -207,13 +251,21 @@ class KVCache:
     def append(self, start, k_new, v_new):
         _need(k_new, torch.bfloat16, "k_new")
         _need(v_new, torch.bfloat16, "v_new")
+        if k_new.dim() != 4:
+            raise ValueError("k_new must be [layers][n][kv_heads][head_dim]")
         n = k_new.shape[1]
+        _shape(k_new, (self.layers, n, self.kv_heads, self.head_dim), "k_new")
+        _shape(v_new, (self.layers, n, self.kv_heads, self.head_dim), "v_new")
         _check("nvfp4_kv_append", _lib().nvfp4_kv_append(
             ctypes.byref(self.desc), start, n, _ptr(k_new), _ptr(v_new), _stream(k_new.device)))
 
     def read(self, layer0, nlayers, t0, n, k_out=None, v_out=None, want_k=True, want_v=True):
         shp = (nlayers, self.kv_heads, n, self.head_dim)
         dev = self.k.device
+        for t, nm in ((k_out, "k_out"), (v_out, "v_out")):
+            if t is not None:
+                _need(t, torch.bfloat16, nm)
+                _shape(t, shp, nm)
         if want_k and k_out is None:
             k_out = torch.empty(shp, dtype=torch.bfloat16, device=dev)
         if want_v and v_out is None:
@@ -229,18 +281,31 @@ class KVCache:
         """One decode step of attention over the first n cached tokens:
         softmax(scale * q K^T) V per query head, fp32 [layers][q_heads][head_dim]."""
         _need(q, torch.bfloat16, "q")
-        L, Hq, D = q.shape
+        L, Hq, D = self._query_shape(q)
+        if out is not None:
+            _need(out, torch.float32, "out")
+            _shape(out, (L, Hq, D), "out")
         o = out if out is not None else torch.empty((L, Hq, D), dtype=torch.float32, device=q.device)
         nb = self.attention_workspace_bytes(Hq, n)
         ws = workspace if workspace is not None else torch.empty(max(nb, 16), dtype=torch.uint8, device=q.device)
+        _need(ws, torch.uint8, "workspace")
         _check("nvfp4_kv_decode_attention", _lib().nvfp4_kv_decode_attention(
             ctypes.byref(self.desc), _ptr(q), Hq, n, float(scale), _ptr(o), _ptr(ws), ws.numel(),
             _stream(q.device)))
         return o
 
+    def _query_shape(self, q):
+        if q.dim() != 3 or q.shape[0] != self.layers or q.shape[2] != self.head_dim:
+            raise ValueError(f"q must be [layers={self.layers}][q_heads][head_dim={self.head_dim}], "
+                             f"got {tuple(q.shape)}")
+        return tuple(q.shape)
+
     def decode_qk(self, q, n, out=None):
         _need(q, torch.bfloat16, "q")
-        L, Hq, D = q.shape
+        L, Hq, D = self._query_shape(q)
+        if out is not None:
+            _need(out, torch.float32, "out")
+            _shape(out, (L, Hq, n), "out")
         logits = out if out is not None else torch.empty((L, Hq, n), dtype=torch.float32, device=q.device)
         _check("nvfp4_kv_decode_qk", _lib().nvfp4_kv_decode_qk(
             ctypes.byref(self.desc), _ptr(q), Hq, n, _ptr(logits), _stream(q.device)))
@@ -254,8 +319,18 @@ def gemm(a_q, a_sf, a_g, b_q, b_sf, b_g, out=None):
         _need(t, torch.uint8, n)
     _need(a_g, torch.float32, "a_g")
     _need(b_g, torch.float32, "b_g")
+    if a_q.dim() != 2 or b_q.dim() != 2:
+        raise ValueError("a_q and b_q must be [rows][K/2]")
     M, K2 = a_q.shape
     N = b_q.shape[0]
+    _shape(b_q, (N, K2), "b_q")
+    _shape(a_sf, (M, K2 // 8), "a_sf")
+    _shape(b_sf, (N, K2 // 8), "b_sf")
+    _numel(a_g, 1, "a_g")
+    _numel(b_g, 1, "b_g")
+    if out is not None:
+        _need(out, torch.float32, "out")
+        _shape(out, (M, N), "out")
     c = out if out is not None else torch.empty((M, N), dtype=torch.float32, device=a_q.device)
     _check("nvfp4_gemm", _lib().nvfp4_gemm(
         _ptr(a_q), _ptr(a_sf), _ptr(a_g), _ptr(b_q), _ptr(b_sf), _ptr(b_g), M, N, 2 * K2, _ptr(c),
@@ -271,10 +346,19 @@ def grouped_gemm(a_q, a_sf, a_g, b_q, b_sf, b_g, offsets, out=None):
     _need(a_g, torch.float32, "a_g")
     _need(b_g, torch.float32, "b_g")
     _need(offsets, torch.int32, "offsets")
+    if a_q.dim() != 2 or b_q.dim() != 3:
+        raise ValueError("a_q must be [M][K/2] and b_q [experts][N][K/2]")
     M, K2 = a_q.shape
     E, N = b_q.shape[0], b_q.shape[1]
     if offsets.numel() != E + 1 or b_g.numel() != E:
         raise ValueError("offsets must hold experts+1 entries and b_g one scale per expert")
+    _shape(b_q, (E, N, K2), "b_q")
+    _shape(a_sf, (M, K2 // 8), "a_sf")
+    _shape(b_sf, (E, N, K2 // 8), "b_sf")
+    _numel(a_g, 1, "a_g")
+    if out is not None:
+        _need(out, torch.float32, "out")
+        _shape(out, (M, N), "out")
     c = out if out is not None else torch.empty((M, N), dtype=torch.float32, device=a_q.device)
     _check("nvfp4_grouped_gemm", _lib().nvfp4_grouped_gemm(
         _ptr(a_q), _ptr(a_sf), _ptr(a_g), _ptr(b_q), _ptr(b_sf), _ptr(b_g), _ptr(offsets), E, M, N, 2 * K2,
@@ -303,6 +387,12 @@ def quantize_ex(x, variant, rht_signs=0, seed=0, offset=0, workspace=None, out=N
     R, C = (cols, rows) if variant & VAR_COLWISE else (rows, cols)
     if out is not None:
         q, sf, g = out
+        _need(q, torch.uint8, "q")
+        _need(sf, torch.uint8, "sf")
+        _need(g, torch.float32, "g")
+        _shape(q, lead + (R, C // 2), "q")
+        _shape(sf, lead + (R, C // 16), "sf")
+        _numel(g, batch, "g")
     else:
         q = torch.empty(lead + (R, C // 2), dtype=torch.uint8, device=x.device)
         sf = torch.empty(lead + (R, C // 16), dtype=torch.uint8, device=x.device)
@@ -326,6 +416,10 @@ def mxfp4_quantize(x, out=None):
     lead = tuple(x.shape[:-1])
     if out is not None:
         q, sf = out
+        _need(q, torch.uint8, "q")
+        _need(sf, torch.uint8, "sf")
+        _shape(q, lead + (cols // 2,), "q")
+        _shape(sf, lead + (cols // 32,), "sf")
     else:
         q = torch.empty(lead + (cols // 2,), dtype=torch.uint8, device=x.device)
         sf = torch.empty(lead + (cols // 32,), dtype=torch.uint8, device=x.device)
@@ -342,6 +436,9 @@ def mxfp4_dequantize(q, sf, out=None):
     rows = q.numel() // q.shape[-1] if q.shape[-1] else 0
     if sf.numel() != rows * (cols // 32):
         raise ValueError("sf must hold one scale byte per 32 values")
+    if out is not None:
+        _need(out, torch.bfloat16, "out")
+        _shape(out, tuple(q.shape[:-1]) + (cols,), "out")
     y = out if out is not None else torch.empty(tuple(q.shape[:-1]) + (cols,), dtype=torch.bfloat16, device=q.device)
     _check("nvfp4_mxfp4_dequantize", _lib().nvfp4_mxfp4_dequantize(
         _ptr(q), _ptr(sf), rows, cols, _ptr(y), _stream(q.device)))
@@ -356,6 +453,9 @@ def mxfp4_gemm(a_q, a_sf, b_q, b_sf, out=None):
     N = b_q.shape[0]
     if b_q.shape[1] != K2 or a_sf.shape != (M, K2 // 16) or b_sf.shape != (N, K2 // 16):
         raise ValueError("operands must be q [rows][K/2] and sf [rows][K/32] with a common K")
+    if out is not None:
+        _need(out, torch.float32, "out")
+        _shape(out, (M, N), "out")
     c = out if out is not None else torch.empty((M, N), dtype=torch.float32, device=a_q.device)
     _check("nvfp4_mxfp4_gemm", _lib().nvfp4_mxfp4_gemm(
         _ptr(a_q), _ptr(a_sf), _ptr(b_q), _ptr(b_sf), M, N, 2 * K2, _ptr(c), _stream(a_q.device)))

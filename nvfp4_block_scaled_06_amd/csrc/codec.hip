@@ -25,6 +25,7 @@
 //              (agent-scope atomics), then encodes its slice of tensor t-1,
 //              read again newest-first.
 #include <algorithm>
+#include <cstddef>
 #include <utility>
 
 #include "common.hpp"
@@ -182,8 +183,15 @@ constexpr int kGroups = 32;
 constexpr size_t kFusedHeaderBytes = 256;
 constexpr size_t kLineWords = 16;                      // 64-byte lines
 constexpr size_t kTensorWords = (kGroups + 1) * kLineWords;
-constexpr uint32_t kSpinLimit = 1u << 24;              // ~seconds: only a non-resident grid gets there
+// Polls of a bounded wait before it gives up (~seconds at the default: only
+// a grid that is not fully resident gets there).  Per device; set by
+// nvfp4_set_wait_limit, read by every wait of the cooperative kernels.
+constexpr uint32_t kDefaultWaitLimit = 1u << 24;
+__device__ uint32_t g_wait_limit = kDefaultWaitLimit;
 
+// done counts the workgroups out of a launch (the last one restores the
+// exchange words to zero); error is set by any wait that gave up and stays
+// set until nvfp4_quantize_status reads and clears it.
 struct FusedHeader {
   uint32_t done;
   uint32_t error;
@@ -224,7 +232,8 @@ __device__ __forceinline__ void fused_arrive(uint32_t* ws, int t, uint32_t m, in
 // workgroup's group; returns it with bit 31 set, or 0 after the spin limit.
 __device__ __forceinline__ uint32_t fused_wait(uint32_t* ws, int t) {
   uint32_t* go = fused_line(ws, t, blockIdx.x % kGroups) + 2;
-  for (uint32_t it = 0; it < kSpinLimit; ++it) {
+  const uint32_t limit = g_wait_limit;
+  for (uint32_t it = 0; it < limit; ++it) {
     const uint32_t v = __hip_atomic_load(go, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (v & 0x80000000u) return v;
     __builtin_amdgcn_s_sleep(2);
@@ -578,7 +587,8 @@ __device__ __forceinline__ uint32_t onchip_wait(uint32_t* ws, int t, int G) {
   // words past G count as filled.
   const __amdgpu_buffer_rsrc_t rs =
       __builtin_amdgcn_make_buffer_rsrc(fused_line(ws, t, 0), 0, (int)(kTensorWords * 4), kBufferWord3);
-  for (uint32_t it = 0; it < kSpinLimit; ++it) {
+  const uint32_t limit = g_wait_limit;
+  for (uint32_t it = 0; it < limit; ++it) {
     uint32_t mx = 0, ok = 1;
     for (int base = 0; base < G; base += 256) {
       const u32x4 v = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, (base + 4 * lane) * 4, 0,
@@ -1167,6 +1177,32 @@ nvfp4_status nvfp4_quantize(const uint16_t* x, int64_t batch, int64_t rows, int6
                                                                       (uint32_t*)q, sf);
   NVFP4_LAUNCH_CHECK();
   return NVFP4_OK;
+}
+
+uint32_t nvfp4_set_wait_limit(uint32_t polls) {
+  uint32_t prev = kDefaultWaitLimit;
+  if (hipMemcpyFromSymbol(&prev, HIP_SYMBOL(g_wait_limit), sizeof(prev)) != hipSuccess) prev = kDefaultWaitLimit;
+  if (hipMemcpyToSymbol(HIP_SYMBOL(g_wait_limit), &polls, sizeof(polls)) != hipSuccess) return prev;
+  return prev;
+}
+
+nvfp4_status nvfp4_quantize_status(void* workspace, size_t workspace_bytes, void* stream) {
+  if (!workspace || workspace_bytes < sizeof(FusedHeader)) return NVFP4_EWORKSPACE;
+  nvfp4_status st = nvfp4host::check_device();
+  if (st) return st;
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = hipStreamSynchronize(s);
+  FusedHeader h{};
+  if (e == hipSuccess) e = hipMemcpy(&h, workspace, sizeof(h), hipMemcpyDeviceToHost);
+  if (e == hipSuccess && h.error) {
+    const uint32_t zero = 0;
+    e = hipMemcpy((char*)workspace + offsetof(FusedHeader, error), &zero, sizeof(zero), hipMemcpyHostToDevice);
+  }
+  if (e != hipSuccess) {
+    nvfp4host::set_hip_error(e);
+    return NVFP4_EHIP;
+  }
+  return h.error ? NVFP4_ETIMEOUT : NVFP4_OK;
 }
 
 nvfp4_status nvfp4_quantize_with_scale(const uint16_t* x, int64_t batch, int64_t rows, int64_t cols, const float* g,

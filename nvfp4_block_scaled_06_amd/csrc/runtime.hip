@@ -61,6 +61,7 @@ const char* nvfp4_status_string(nvfp4_status status) {
     case NVFP4_EWORKSPACE: return "NVFP4_EWORKSPACE: workspace missing or too small";
     case NVFP4_ENOTSUP: return "NVFP4_ENOTSUP: unsupported device or flag";
     case NVFP4_EHIP: return "NVFP4_EHIP: HIP runtime error";
+    case NVFP4_ETIMEOUT: return "NVFP4_ETIMEOUT: a bounded cross-workgroup wait gave up";
     default: return "NVFP4: unknown status";
   }
 }

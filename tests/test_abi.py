@@ -13,7 +13,7 @@ HEADER = os.path.join(ROOT, "include", "nvfp4.h")
 
 nv = pytest.importorskip("nvfp4_block_scaled_06_amd")
 
-EINVAL, EALIGN, EWORKSPACE, ENOTSUP, EHIP = -1, -2, -3, -4, -5
+EINVAL, EALIGN, EWORKSPACE, ENOTSUP, EHIP, ETIMEOUT = -1, -2, -3, -4, -5, -6
 FAKE = 0x7F0000000000          # aligned, never dereferenced: validation fails first
 P = ctypes.c_void_p
 
@@ -35,7 +35,7 @@ def test_every_declared_symbol_is_exported():
 def test_status_strings_and_version():
     L = nv.lib()
     assert L.nvfp4_abi_version() == 1
-    for s in (0, EINVAL, EALIGN, EWORKSPACE, ENOTSUP, EHIP, 42):
+    for s in (0, EINVAL, EALIGN, EWORKSPACE, ENOTSUP, EHIP, ETIMEOUT, 42):
         assert L.nvfp4_status_string(s)
     assert L.nvfp4_status_string(0) == b"NVFP4_OK"
 
@@ -138,3 +138,12 @@ def test_valid_call_without_gpu_fails_cleanly():
     if torch.cuda.is_available():
         pytest.skip("a GPU is present: the fake pointers would reach a kernel")
     assert _q() in (EHIP, ENOTSUP)
+
+
+def test_quantize_status_validation():
+    """The status query rejects a missing or undersized workspace before it
+    touches the device."""
+    L = nv.lib()
+    assert L.nvfp4_quantize_status(None, 1 << 20, None) == EWORKSPACE
+    assert L.nvfp4_quantize_status(P(FAKE), 4, None) == EWORKSPACE
+    assert L.nvfp4_status_string(ETIMEOUT).startswith(b"NVFP4_ETIMEOUT")

@@ -74,56 +74,113 @@ def test_edge_tensors(name):
         assert_quantize_matches(x, fl, f"{name} {fl}")
 
 
-def _sweep_input(g_value, seed):
-    """Blocks covering every bf16 magnitude below each block's max, for every
-    block-scale byte reachable with tensor scale g."""
+# Tensor scales of the conversion sweeps: round values, inexact decimals,
+# extremes whose block divisors reach the top and bottom of the fp32 range.
+SWEEP_G = [np.float32(v) for v in (0.0123, 1.0, 3.7e-5, 2.0 ** -100, 1e30, 1.0 / 3.0, 0.1, 7.77e-12)]
+ALL_MAGS = np.arange(0, 0x7F80, dtype=np.uint16)          # every finite bf16 magnitude, +0 included
+
+
+def _bf16_value(bits16):
+    return float((np.uint32(bits16) << np.uint32(16)).view(np.float32))
+
+
+def _largest_bamax_per_scale(g_value, cap=0x7F7F):
+    """For tensor scale g: each block-scale byte reachable with g, with the
+    largest bf16 magnitude (<= cap) whose block takes that byte (the oracle
+    decides which byte a block amax maps to)."""
+    out = {}
+    for m in range(0, cap + 1):
+        s = oracle.block_scale(_bf16_value(m), float(g_value))
+        out[s] = m                                      # ascending m: the last one wins
+    return out
+
+
+def _element_sweep_input(g_value, seed, cap=0x7F7F):
+    """Blocks that put every finite bf16 magnitude up to the block amax (both
+    signs drawn at random) through the element quotient and the E2M1
+    conversion, for every block-scale byte reachable with tensor scale g.
+    The block amax rotates over the 16 positions."""
     rng = np.random.default_rng(seed)
     rows = []
-    allmag = np.arange(0, 0x7F80, dtype=np.uint16)
-    allf = (allmag.astype(np.uint32) << 16).view(np.float32)
-    for sbyte in range(1, 0x7F):
-        s = oracle.e4m3_value(sbyte)
-        bam = np.float32(6.0 * s * g_value)
-        bam_bits = oracle.f32_to_bf16_array(np.array([bam], dtype=np.float32))[0]
-        lim = int(bam_bits)
-        if lim == 0 or lim >= 0x7F80:
-            continue
-        mags = allmag[:lim + 1]
-        if mags.size > 4000:            # all of the top 2^11 patterns, a random sample below
-            top = mags[-2048:]
-            rest = rng.choice(mags[:-2048], 1952, replace=False)
-            mags = np.concatenate([top, rest])
+    blk = 0
+    for sbyte, bam in sorted(_largest_bamax_per_scale(g_value, cap).items()):
+        mags = ALL_MAGS[:bam + 1]
         signs = (rng.random(mags.size) < 0.5).astype(np.uint16) << 15
         vals = mags | signs
-        pad = (-vals.size) % 15
-        vals = np.concatenate([vals, np.zeros(pad, dtype=np.uint16)]).reshape(-1, 15)
-        blk = np.concatenate([np.full((vals.shape[0], 1), bam_bits, dtype=np.uint16), vals], axis=1)
-        rows.append(blk.reshape(-1))
+        vals = np.concatenate([vals, np.zeros((-vals.size) % 15, dtype=np.uint16)]).reshape(-1, 15)
+        n = vals.shape[0]
+        out = np.empty((n, 16), dtype=np.uint16)
+        pos = (blk + np.arange(n)) % 16
+        for i in range(n):
+            out[i] = np.insert(vals[i], pos[i], np.uint16(bam))
+        blk += n
+        rows.append(out.reshape(-1))
     return np.concatenate(rows)
 
 
-@pytest.mark.parametrize("g_value", [np.float32(0.0123), np.float32(1.0), np.float32(3.7e-5),
-                                     np.float32(2.0 ** -100), np.float32(1e30)])
-def test_scale_by_magnitude_sweep(g_value):
-    """quantize_with_scale: for every E4M3 scale byte, blocks holding (nearly) every
-    bf16 magnitude up to the block max -- exercises the reciprocal fast path,
-    the danger-magnitude fix-ups and the fully exact path."""
-    print("case: sweep g", float(g_value), flush=True)
-    flat = _sweep_input(float(g_value), 17)
-    cols = 16 * 64
+def _pad_rows(flat, cols=1024):
     flat = np.concatenate([flat, np.zeros((-flat.size) % cols, dtype=np.uint16)])
-    xb = flat.reshape(1, -1, cols)
+    return flat.reshape(1, -1, cols)
+
+
+def _check_with_scale(xb, g_value, what):
     x = from_bits(xb)
     gt = torch.tensor([g_value], dtype=torch.float32, device="cuda")
     q, sf = nv.quantize_with_scale(x, gt)
     torch.cuda.synchronize()
     oq, osf = oracle.quantize_with_scale(xb, np.array([g_value], dtype=np.float32))
     bad = np.argwhere(np_(sf) != osf)
-    assert bad.size == 0, f"scale mismatch at {bad[:5].tolist()}"
+    assert bad.size == 0, f"{what}: scale mismatch at {bad[:5].tolist()}"
     bad = np.argwhere(np_(q) != oq)
-    assert bad.size == 0, f"code mismatch at {bad[:5].tolist()}: got {np_(q)[tuple(bad[0])]:#x} want {oq[tuple(bad[0])]:#x}"
+    assert bad.size == 0, f"{what}: code mismatch at {bad[:5].tolist()}: got {np_(q)[tuple(bad[0])]:#x} " \
+                          f"want {oq[tuple(bad[0])]:#x}"
     y = nv.dequantize(q, sf, gt)
-    assert np.array_equal(bits(y), oracle.dequantize(oq, osf, np.array([g_value], dtype=np.float32)))
+    assert np.array_equal(bits(y), oracle.dequantize(oq, osf, np.array([g_value], dtype=np.float32))), \
+        f"{what}: dequantize mismatch"
+
+
+@pytest.mark.parametrize("g_value", SWEEP_G)
+def test_element_conversion_sweep(g_value):
+    """quantize_with_scale, reachable domain of the element path: for every
+    E4M3 scale byte reachable with tensor scale g, blocks holding every finite
+    bf16 magnitude up to the block amax.  Every quotient RN32(|x| / RN32(s g))
+    the encode can form with this g goes through the fp64 reciprocal and the
+    hardware E2M1 conversion, and every code through the dequantize."""
+    print("case: element sweep g", float(g_value), flush=True)
+    xb = _pad_rows(_element_sweep_input(g_value, 17))
+    _check_with_scale(xb, g_value, f"g={float(g_value)}")
+
+
+@pytest.mark.parametrize("g_value", SWEEP_G)
+def test_block_scale_conversion_sweep(g_value):
+    """quantize_with_scale, reachable domain of the block-scale path: one
+    block per finite bf16 magnitude as its amax (the rest of the block drawn
+    below it), so the E4M3 conversion sees every quotient RN32(bamax /
+    RN32(6 g)) that tensor scale g allows."""
+    print("case: block-scale sweep g", float(g_value), flush=True)
+    rng = np.random.default_rng(29)
+    n = ALL_MAGS.size
+    fill = (rng.random((n, 15)) * (ALL_MAGS.astype(np.float64)[:, None] + 1)).astype(np.uint16)
+    fill = np.minimum(fill, ALL_MAGS[:, None]) | ((rng.random((n, 15)) < 0.5).astype(np.uint16) << 15)
+    pos = np.arange(n) % 16
+    blocks = np.empty((n, 16), dtype=np.uint16)
+    for i in range(n):
+        blocks[i] = np.insert(fill[i], pos[i], ALL_MAGS[i] | (np.uint16(i & 1) << 15))
+    _check_with_scale(_pad_rows(blocks.reshape(-1)), g_value, f"g={float(g_value)}")
+
+
+@pytest.mark.parametrize("flags", FLAGS)
+def test_element_sweep_through_tensor_amax(flags):
+    """The element sweep for g = 1 through nvfp4_quantize itself (amax pass,
+    tensor scale, both launch modes): block amaxes capped at 2688 and one
+    block holding 2688, so RN32(amax / 2688) = 1."""
+    print("case: element sweep through the tensor amax", flags, flush=True)
+    flat = _element_sweep_input(np.float32(1.0), 31, cap=0x4528)        # 0x4528 = bf16(2688)
+    amax_blk = np.zeros(16, dtype=np.uint16)
+    amax_blk[5] = 0x4528
+    xb = _pad_rows(np.concatenate([flat, amax_blk]))
+    q, sf, g = assert_quantize_matches(from_bits(xb), flags, f"sweep {flags}")
+    assert np_(g)[0] == np.float32(1.0)
 
 
 def test_batch_distinct_magnitudes_and_guards():
@@ -165,26 +222,24 @@ def test_deterministic_reruns():
         assert torch.equal(u, v)
 
 
-def test_experts_full_size_sampled():
-    """64 x [2048 x 7168] expert weights (N(0,0.02), 0.1% x50 outliers): all
-    64 tensor scales checked; codes, scales and dequant of 3 experts checked in full."""
+def test_experts_full_size():
+    """64 x [2048 x 7168] expert weights (N(0,0.02), 0.1% x50 outliers), the
+    headline workload: tensor scales, codes, scale bytes and dequantized values
+    of all 64 experts, both launch modes, bit for bit against one oracle pass."""
     print("case: experts 64x2048x7168 seed 102", flush=True)
     x = synth.experts(device="cuda")
+    oq, osf, og = oracle.quantize(bits(x))
+    oy = oracle.dequantize(oq, osf, og)
     ws = nv.make_workspace(64, 2048, 7168)
     for fl in FLAGS:
         q, sf, g = nv.quantize(x, flags=fl, workspace=ws)
         y = nv.dequantize(q, sf, g)
         torch.cuda.synchronize()
-        amax = x.float().abs().amax(dim=(1, 2)).cpu().numpy()
-        og_all = np.array([oracle.global_scale(a) for a in amax], dtype=np.float32)
-        assert np.array_equal(np_(g), og_all)
-        for e in (0, 31, 63):
-            xb = bits(x[e])
-            oq, osf, og = oracle.quantize(xb)
-            assert og[0] == np_(g)[e]
-            assert np.array_equal(np_(sf[e]), osf), f"expert {e} scales"
-            assert np.array_equal(np_(q[e]), oq), f"expert {e} codes"
-            assert np.array_equal(bits(y[e]), oracle.dequantize(oq, osf, og)), f"expert {e} dequant"
+        assert np.array_equal(np_(g).view(np.uint32), og.view(np.uint32)), f"{fl}: tensor scales"
+        for e in range(64):
+            assert np.array_equal(np_(sf[e]), osf[e]), f"{fl}: expert {e} scales"
+            assert np.array_equal(np_(q[e]), oq[e]), f"{fl}: expert {e} codes"
+            assert np.array_equal(bits(y[e]), oy[e]), f"{fl}: expert {e} dequant"
         del q, sf, y
     del x
 

@@ -66,18 +66,17 @@ def test_gemm_k_zero_gives_zeros():
     assert torch.count_nonzero(c).item() == 0
 
 
-def test_gemm_full_size_sampled_rows():
-    """A [8192 x 7168] x B [2048 x 7168]^T from N(0,1): 96 sampled rows of C
-    (all 2048 columns) against fp64."""
+def test_gemm_full_size():
+    """A [8192 x 7168] x B [2048 x 7168]^T from N(0,1), the benchmarked shape:
+    every element of C against the fp64 product of the oracle's encoding."""
     print("case: gemm 8192x2048x7168 seed 105", flush=True)
     a, b = synth.gemm_operands(device="cuda")
     (aq, asf, ag), oa = _quantized(a)
     (bq, bsf, bg), ob = _quantized(b)
     c = nv.gemm(aq, asf, ag, bq, bsf, bg)
     torch.cuda.synchronize()
-    rows = np.sort(np.random.default_rng(1).choice(8192, 96, replace=False))
-    want = oracle.gemm_f64(oa[0], oa[1], oa[2][0], ob[0], ob[1], ob[2][0], rows=rows)
-    err = rel_frobenius(np_(c[torch.from_numpy(rows).cuda()]), want)
+    want = oracle.gemm_f64(oa[0], oa[1], oa[2][0], ob[0], ob[1], ob[2][0])
+    err = rel_frobenius(np_(c), want)
     assert err <= TOL, f"rel Frobenius {err:.3e}"
 
 
