@@ -113,6 +113,21 @@ nvfp4_status nvfp4_quantize(const uint16_t* x, int64_t batch, int64_t rows, int6
                             void* workspace, size_t workspace_bytes,
                             uint32_t flags, void* stream);
 
+/* nvfp4_quantize for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): the same computation and bytes, with the workspace in a
+ * fixed 1 MiB device array inside the library (one copy per GPU, held until
+ * the process ends) instead of a caller buffer.  Allocates nothing.
+ * Limit: nvfp4_quantize_workspace_bytes(batch, rows, cols) <= 1 MiB, i.e.
+ * batch <= 101; larger batches return NVFP4_EWORKSPACE.  Every call on one
+ * GPU shares that array: calls that overlap in time on one GPU (different
+ * streams, or threads without ordering) race and must not be made.  A FUSED
+ * call first clears the array's exchange words with a small fill kernel.  A
+ * FUSED wait that gives up leaves NaN in g, as for nvfp4_quantize.
+ * Errors: as nvfp4_quantize (EWORKSPACE: batch above the limit). */
+nvfp4_status nvfp4_quantize_noalloc(const uint16_t* x, int64_t batch, int64_t rows, int64_t cols,
+                                    uint8_t* q, uint8_t* sf, float* g, uint32_t flags, void* stream);
+
 /* Reports whether a FUSED nvfp4_quantize on this workspace had a bounded
  * wait give up since the last report: synchronizes `stream` (the one the
  * calls ran on), reads the workspace's error word, clears it, and returns

@@ -50,6 +50,7 @@ _SIGS = {
     "nvfp4_last_hip_error": (_I32, []),
     "nvfp4_quantize_workspace_bytes": (_SZ, [_I64, _I64, _I64]),
     "nvfp4_quantize": (_I32, [_P, _I64, _I64, _I64, _P, _P, _P, _P, _SZ, ctypes.c_uint32, _P]),
+    "nvfp4_quantize_noalloc": (_I32, [_P, _I64, _I64, _I64, _P, _P, _P, ctypes.c_uint32, _P]),
     "nvfp4_quantize_status": (_I32, [_P, _SZ, _P]),
     "nvfp4_set_wait_limit": (ctypes.c_uint32, [ctypes.c_uint32]),
     "nvfp4_quantize_with_scale": (_I32, [_P, _I64, _I64, _I64, _P, _P, _P, _P]),
@@ -165,6 +166,30 @@ def quantize(x, flags="two_kernel", workspace=None, out=None):
     _check("nvfp4_quantize", _lib().nvfp4_quantize(
         _ptr(x), b, r, c, _ptr(q), _ptr(sf), _ptr(g), _ptr(workspace), workspace.numel(),
         _FLAGS[flags], _stream(x.device)))
+    return q, sf, g
+
+
+def quantize_noalloc(x, flags="two_kernel", out=None):
+    """nvfp4_quantize with the library's fixed device scratch instead of a
+    workspace (no allocation inside the call; batch <= 101).  Calls on one
+    GPU must not overlap in time."""
+    _need(x, torch.bfloat16, "x")
+    b, r, c = _split(x.shape)
+    lead = tuple(x.shape[:-1])
+    if out is None:
+        q = torch.empty(lead + (c // 2,), dtype=torch.uint8, device=x.device)
+        sf = torch.empty(lead + (c // 16,), dtype=torch.uint8, device=x.device)
+        g = torch.empty((b,), dtype=torch.float32, device=x.device)
+    else:
+        q, sf, g = out
+        _need(q, torch.uint8, "q")
+        _need(sf, torch.uint8, "sf")
+        _need(g, torch.float32, "g")
+        _shape(q, lead + (c // 2,), "q")
+        _shape(sf, lead + (c // 16,), "sf")
+        _numel(g, b, "g")
+    _check("nvfp4_quantize_noalloc", _lib().nvfp4_quantize_noalloc(
+        _ptr(x), b, r, c, _ptr(q), _ptr(sf), _ptr(g), _FLAGS[flags], _stream(x.device)))
     return q, sf, g
 
 

@@ -25,6 +25,7 @@
 //              (agent-scope atomics), then encodes its slice of tensor t-1,
 //              read again newest-first.
 #include <algorithm>
+#include <atomic>
 #include <cstddef>
 #include <utility>
 
@@ -1108,12 +1109,23 @@ size_t nvfp4_quantize_workspace_bytes(int64_t batch, int64_t rows, int64_t cols)
   return head + (size_t)batch * kMaxPartials * sizeof(uint32_t);
 }
 
-nvfp4_status nvfp4_quantize(const uint16_t* x, int64_t batch, int64_t rows, int64_t cols, uint8_t* q, uint8_t* sf,
-                            float* g, void* workspace, size_t workspace_bytes, uint32_t flags, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Host validation of nvfp4_quantize's arguments (nothing is launched).
+// Returns OK, or OK with *empty set when there is nothing to do.
+nvfp4_status quantize_validate(const uint16_t* x, int64_t batch, int64_t rows, int64_t cols, const uint8_t* q,
+                               const uint8_t* sf, const float* g, const void* workspace, size_t workspace_bytes,
+                               uint32_t flags, bool* empty) {
+  *empty = false;
   nvfp4_status st = check_shape(batch, rows, cols);
   if (st) return st;
   if (flags != NVFP4_TWO_KERNEL && flags != NVFP4_FUSED) return NVFP4_ENOTSUP;
-  if (batch == 0) return NVFP4_OK;
+  if (batch == 0) {
+    *empty = true;
+    return NVFP4_OK;
+  }
   if (!g) return NVFP4_EINVAL;
   const int64_t n = rows * cols;
   if (n > 0 && (!x || !q || !sf)) return NVFP4_EINVAL;
@@ -1121,8 +1133,13 @@ nvfp4_status nvfp4_quantize(const uint16_t* x, int64_t batch, int64_t rows, int6
     return NVFP4_EALIGN;
   if (!workspace || workspace_bytes < nvfp4_quantize_workspace_bytes(batch, rows, cols)) return NVFP4_EWORKSPACE;
   if (!nvfp4host::aligned16(workspace)) return NVFP4_EALIGN;
-  if ((st = nvfp4host::check_device())) return st;
-  hipStream_t s = (hipStream_t)stream;
+  return nvfp4host::check_device();
+}
+
+// The launches of nvfp4_quantize, arguments already validated.
+nvfp4_status quantize_launch(const uint16_t* x, int64_t batch, int64_t rows, int64_t cols, uint8_t* q, uint8_t* sf,
+                             float* g, void* workspace, uint32_t flags, hipStream_t s) {
+  const int64_t n = rows * cols;
   const int64_t hb = n / 8;
   if (flags == NVFP4_FUSED) {
     const int onchip_per = onchip_per_thread(hb);
@@ -1177,6 +1194,74 @@ nvfp4_status nvfp4_quantize(const uint16_t* x, int64_t batch, int64_t rows, int6
                                                                       (uint32_t*)q, sf);
   NVFP4_LAUNCH_CHECK();
   return NVFP4_OK;
+}
+
+// ------------------------------------------------------------ allocation-free quantize
+// The workspace of nvfp4_quantize_noalloc: a fixed device array, one copy
+// per GPU, held until the process ends.  Host code never passes the array's
+// name to a kernel (on the host it only stands for the symbol): the device
+// address comes from hipGetSymbolAddress, once per device, with that device
+// current, and is cached per device.
+constexpr size_t kNoAllocScratchBytes = size_t(1) << 20;
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxScratchDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxScratchDevices];
+
+nvfp4_status scratch_for_current_device(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) {
+    nvfp4host::set_hip_error(e);
+    return NVFP4_EHIP;
+  }
+  if (dev < 0 || dev >= kMaxScratchDevices) return NVFP4_ENOTSUP;
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) {
+      nvfp4host::set_hip_error(e != hipSuccess ? e : hipErrorInvalidSymbol);
+      return NVFP4_EHIP;
+    }
+    g_scratch_ptr[dev].store(p, std::memory_order_release);   // every caller stores the same address
+  }
+  *out = p;
+  return NVFP4_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+nvfp4_status nvfp4_quantize(const uint16_t* x, int64_t batch, int64_t rows, int64_t cols, uint8_t* q, uint8_t* sf,
+                            float* g, void* workspace, size_t workspace_bytes, uint32_t flags, void* stream) {
+  bool empty = false;
+  const nvfp4_status st =
+      quantize_validate(x, batch, rows, cols, q, sf, g, workspace, workspace_bytes, flags, &empty);
+  if (st || empty) return st;
+  return quantize_launch(x, batch, rows, cols, q, sf, g, workspace, flags, (hipStream_t)stream);
+}
+
+nvfp4_status nvfp4_quantize_noalloc(const uint16_t* x, int64_t batch, int64_t rows, int64_t cols, uint8_t* q,
+                                    uint8_t* sf, float* g, uint32_t flags, void* stream) {
+  nvfp4_status st = check_shape(batch, rows, cols);
+  if (st) return st;
+  if (batch > 0 && nvfp4_quantize_workspace_bytes(batch, rows, cols) > kNoAllocScratchBytes) return NVFP4_EWORKSPACE;
+  void* ws = nullptr;
+  if (batch > 0 && (st = scratch_for_current_device(&ws))) return st;
+  bool empty = false;
+  st = quantize_validate(x, batch, rows, cols, q, sf, g, ws, kNoAllocScratchBytes, flags, &empty);
+  if (st || empty) return st;
+  hipStream_t s = (hipStream_t)stream;
+  if (flags == NVFP4_FUSED) {
+    // the exchange words start at zero whatever an earlier call left (a fill
+    // kernel, not a memset, so the call can sit in a captured graph)
+    const int64_t words = (int64_t)(fused_header_bytes(batch) / 4);
+    zero_words_kernel<<<(unsigned)std::min<int64_t>((words + kThreads - 1) / kThreads, 1024), kThreads, 0, s>>>(
+        (uint32_t*)ws, words);
+    NVFP4_LAUNCH_CHECK();
+  }
+  return quantize_launch(x, batch, rows, cols, q, sf, g, ws, flags, s);
 }
 
 uint32_t nvfp4_set_wait_limit(uint32_t polls) {
