@@ -47,8 +47,8 @@ def parse():
     p.add_argument("--rows-only", default="",
                    help="comma list of extra rows to run (experts,single,acts,kv,gemm,moe,mx,train)")
     p.add_argument("--traffic-kernels", action="store_true",
-                   help="only launch the headline kernels, the GEMM and a 1 GiB device copy, 3 times each "
-                        "(the workload for rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs)")
+                   help="only launch every benchmarked kernel on its benchmarked shape (3 times each) and a "
+                        "1 GiB device copy: the workload of the rocprofv3 --pmc counter runs")
     return p.parse_args()
 
 
@@ -471,43 +471,110 @@ def cpu_baseline(synth, torch):
 
 
 def traffic_kernels(nv, synth, torch):
-    """Three launches each of the fused quantize and the dequantize of the
-    headline workload, the two-kernel quantize, the 8192 x 2048 x 7168 NVFP4
-    and MXFP4 GEMMs, and a plain 1 GiB device-to-device copy whose byte counts (1 GiB read,
-    1 GiB written) calibrate the HBM byte counters."""
+    """The workload of the rocprofv3 counter runs (FETCH_SIZE, WRITE_SIZE,
+    MFMA and VALU busy cycles): every benchmarked kernel on its benchmarked
+    shape, three launches each unless stated, and a plain 1 GiB
+    device-to-device copy whose byte counts (1 GiB read, 1 GiB written)
+    calibrate the HBM byte counters.  A kernel's workload is told apart in
+    the counter files by its grid size."""
     E, R, C = 64, 2048, 7168
     x = synth.experts(E, R, C, device="cuda")
     ws = nv.make_workspace(E, R, C)
     q, sf, g = nv.quantize(x, flags="fused", workspace=ws)
     y = torch.empty_like(x)
     torch.cuda.synchronize()
-    for _ in range(3):
-        nv.quantize(x, flags="fused", workspace=ws, out=(q, sf, g))
+    for fl in ("fused", "two_kernel"):
+        for _ in range(3):
+            nv.quantize(x, flags=fl, workspace=ws, out=(q, sf, g))
     for _ in range(3):
         nv.dequantize(q, sf, g, out=y)
+    xw = torch.empty(nv.lib().nvfp4_quantize_ex_workspace_bytes(64), dtype=torch.uint8, device="cuda")
+    for v in (nv.VAR_2D, nv.VAR_2D | nv.VAR_COLWISE):
+        out = nv.quantize_ex(x, v, workspace=xw)
+        for _ in range(2):
+            nv.quantize_ex(x, v, workspace=xw, out=out)
+        del out
+    mq, msf = nv.mxfp4_quantize(x)
     for _ in range(3):
-        nv.quantize(x, flags="two_kernel", workspace=ws, out=(q, sf, g))
+        nv.mxfp4_quantize(x, out=(mq, msf))
+    for _ in range(3):
+        nv.mxfp4_dequantize(mq, msf, out=y)
     torch.cuda.synchronize()
-    del x, y, q, sf, g, ws
+    del x, y, q, sf, g, ws, mq, msf
     torch.cuda.empty_cache()
+    log("traffic: experts done")
+    a = synth.activations(device="cuda")
+    ws = nv.make_workspace(1, 16384, 7168)
+    q, sf, g = nv.quantize(a, workspace=ws)
+    for fl in ("fused", "two_kernel"):
+        for _ in range(3):
+            nv.quantize(a, flags=fl, workspace=ws, out=(q, sf, g))
+    for v in (nv.VAR_SR, nv.VAR_COLWISE | nv.VAR_RHT | nv.VAR_SR):
+        out = nv.quantize_ex(a, v, rht_signs=0x6A3C, seed=77, workspace=xw)
+        for _ in range(2):
+            nv.quantize_ex(a, v, rht_signs=0x6A3C, seed=77, workspace=xw, out=out)
+        del out
+    torch.cuda.synchronize()
+    del a, q, sf, g, ws, xw
+    torch.cuda.empty_cache()
+    log("traffic: activations done")
+    L, H, D, T, CH = 32, 8, 128, 131072, 256
+    chunks = [synth.kv_chunk(c, device="cuda") for c in range(T // CH)]
+    kg, vg = calibrate_kv_scales(nv, torch, chunks, L, H)
+    cache = nv.KVCache(L, H, D, T, kg, vg, device="cuda")
+    for c, (k, v) in enumerate(chunks):                  # 512 appends
+        cache.append(c * CH, k, v)
+    del chunks
+    torch.cuda.empty_cache()
+    qv = synth.kv_query(device="cuda")
+    logits = torch.empty((L, 4 * H, T), dtype=torch.float32, device="cuda")
+    att = torch.empty((L, 4 * H, D), dtype=torch.float32, device="cuda")
+    aws = torch.empty(max(cache.attention_workspace_bytes(4 * H, T), 16), dtype=torch.uint8, device="cuda")
+    kr = torch.empty((4, H, T, D), dtype=torch.bfloat16, device="cuda")
+    vr = torch.empty_like(kr)
+    for _ in range(3):
+        cache.decode_qk(qv, T, out=logits)
+    for _ in range(3):
+        cache.decode_attention(qv, T, D ** -0.5, out=att, workspace=aws)
+    for _ in range(3):
+        cache.read(0, 4, 0, T, k_out=kr, v_out=vr)
+    torch.cuda.synchronize()
+    del cache, logits, att, aws, kr, vr
+    torch.cuda.empty_cache()
+    log("traffic: kv done")
     a, b = synth.gemm_operands(device="cuda")
     aq, asf, ag = nv.quantize(a)
     bq, bsf, bg = nv.quantize(b)
-    del a, b
     c = torch.empty((8192, 2048), dtype=torch.float32, device="cuda")
     for _ in range(3):
         nv.gemm(aq, asf, ag, bq, bsf, bg, out=c)
-    torch.cuda.synchronize()
-    del aq, asf, bq, bsf
-    a, b = synth.gemm_operands(device="cuda")
     maq, masf = nv.mxfp4_quantize(a)
     mbq, mbsf = nv.mxfp4_quantize(b)
-    del a, b
     for _ in range(3):
         nv.mxfp4_gemm(maq, masf, mbq, mbsf, out=c)
     torch.cuda.synchronize()
-    del maq, masf, mbq, mbsf, c
+    del a, b, aq, asf, bq, bsf, maq, masf, mbq, mbsf, c
     torch.cuda.empty_cache()
+    Tm, top, N, K = 16384, 8, 2048, 7168
+    gen = torch.Generator().manual_seed(106)
+    choice = torch.rand((Tm, E), generator=gen).argsort(dim=1)[:, :top]
+    counts = torch.bincount(choice.flatten(), minlength=E)
+    offsets = torch.cat([torch.zeros(1, dtype=torch.int64), counts.cumsum(0)]).to(torch.int32).cuda()
+    M = int(counts.sum())
+    ra = synth.activations(tokens=M, channels=K, seed=107, device="cuda")
+    raq, rasf, rag = nv.quantize(ra)
+    del ra
+    w = synth.experts(E, N, K, device="cuda")
+    wq, wsf, wg = nv.quantize(w)
+    del w
+    torch.cuda.empty_cache()
+    c = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    for _ in range(2):
+        nv.grouped_gemm(raq, rasf, rag, wq, wsf, wg, offsets, out=c)
+    torch.cuda.synchronize()
+    del raq, rasf, wq, wsf, c
+    torch.cuda.empty_cache()
+    log("traffic: gemms done")
     src = torch.ones(2 ** 30, dtype=torch.uint8, device="cuda")
     dst = torch.empty_like(src)
     for _ in range(3):

@@ -70,7 +70,7 @@ enum {
 /* Launch modes of nvfp4_quantize. */
 enum {
   NVFP4_TWO_KERNEL = 0,  /* pass 1: per-tensor amax kernel; pass 2: encode kernel */
-  NVFP4_FUSED = 1        /* one persistent cooperative launch, amax then encode */
+  NVFP4_FUSED = 1        /* one launch of co-resident workgroups, amax then encode */
 };
 
 #define NVFP4_ABI_VERSION 1
@@ -98,10 +98,13 @@ int32_t nvfp4_last_hip_error(void);
  * flags: NVFP4_TWO_KERNEL or NVFP4_FUSED (same bytes either way).
  * Errors: EINVAL (null pointer with nonzero size, negative size, cols % 16),
  *   EALIGN, EWORKSPACE, ENOTSUP (unknown flag / not gfx950), EHIP.
- * FUSED runs every workgroup of one cooperative launch through a
- * cross-workgroup exchange of maxima; each wait is bounded (see
- * nvfp4_set_wait_limit).  A wait that gives up -- which a cooperative launch
- * on an otherwise idle device never needs -- does not fault: it writes NaN
+ * FUSED runs every workgroup of one launch through a cross-workgroup
+ * exchange of maxima; the grid is at most one round of resident workgroups
+ * (at most one per compute unit for tensors held on chip), so FUSED calls
+ * must not overlap in time with other kernels that occupy the whole device
+ * and wait for one another (such as a FUSED call on another stream).  Each
+ * wait is bounded (see nvfp4_set_wait_limit).  A wait that gives up -- which
+ * a launch on an otherwise idle device never needs -- does not fault: it writes NaN
  * for the tensor scale g of that tensor, leaves its codes and scale bytes
  * unspecified (in bounds), and sets an error word in the workspace that
  * nvfp4_quantize_status reports.
@@ -137,7 +140,7 @@ nvfp4_status nvfp4_quantize_noalloc(const uint16_t* x, int64_t batch, int64_t ro
 nvfp4_status nvfp4_quantize_status(void* workspace, size_t workspace_bytes, void* stream);
 
 /* Sets the number of polls after which every bounded wait of the
- * cooperative kernels gives up, on the current device; returns the previous
+ * FUSED and single-launch 2D kernels gives up, on the current device; returns the previous
  * value (default 2^24, seconds of polling).  For tests and diagnostics: 0
  * makes every wait give up at once (every kernel still runs to its end), so
  * the timeout path can be exercised without a stalled grid.  Synchronous. */
@@ -324,7 +327,7 @@ size_t nvfp4_quantize_ex_workspace_bytes(int64_t batch);
  * (R, C) = (rows, cols), or (cols, rows) under COLWISE: q [batch][R][C/2],
  * sf [batch][R][C/16], g [batch] (the tensor scale of the transformed
  * values).  Two passes over x (amax, then encode); 2D without RHT or SR
- * (with or without COLWISE) reads x once in a single cooperative launch
+ * (with or without COLWISE) reads x once in a single launch
  * when a tensor's strips of 16 rows x 8 columns fit on the chip (at most
  * compute units x 448 of them; COLWISE counts blocks of 8 x 8 strips, 7 per
  * compute unit), with the same bytes.  variant 0 equals nvfp4_quantize bit

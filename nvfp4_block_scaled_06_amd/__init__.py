@@ -208,7 +208,7 @@ def quantize_status(workspace):
 
 
 def set_wait_limit(polls):
-    """Polls after which the cooperative kernels' bounded waits give up, on the
+    """Polls after which the co-resident kernels' bounded waits give up, on the
     current device (default 2^24); returns the previous value.  0 makes every
     wait give up at once: a test hook for the timeout path."""
     return int(_lib().nvfp4_set_wait_limit(int(polls)))

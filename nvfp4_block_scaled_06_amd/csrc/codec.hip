@@ -17,8 +17,8 @@
 // Launch modes of nvfp4_quantize:
 //  TWO_KERNEL  amax_partial_kernel (per-workgroup maxima, no atomics) then
 //              encode_kernel (reduces the partials, builds the table, encodes).
-//  FUSED       one cooperative launch whose workgroups walk the batch
-//              tensor by tensor.  fused_onchip_kernel when a tensor fits on
+//  FUSED       one launch of co-resident workgroups that walk the batch
+//              tensor by tensor.  fused_reg8_kernel when a tensor fits on
 //              chip (registers + LDS of the whole GPU): every input byte is
 //              read from HBM once.  Otherwise fused_quantize_kernel: each
 //              workgroup reduces its slice of tensor t, publishes it
@@ -186,7 +186,7 @@ constexpr size_t kLineWords = 16;                      // 64-byte lines
 constexpr size_t kTensorWords = (kGroups + 1) * kLineWords;
 // Polls of a bounded wait before it gives up (~seconds at the default: only
 // a grid that is not fully resident gets there).  Per device; set by
-// nvfp4_set_wait_limit, read by every wait of the cooperative kernels.
+// nvfp4_set_wait_limit, read by every wait of the co-resident kernels.
 constexpr uint32_t kDefaultWaitLimit = 1u << 24;
 __device__ uint32_t g_wait_limit = kDefaultWaitLimit;
 
@@ -687,44 +687,7 @@ __global__ void __launch_bounds__(kOnchipThreads) fused_onchip_kernel(const u32x
   onchip_sync_wave(ws, batch, G, gout, sh);
 }
 
-// ------------------------------------------------------------ fused, four tensors on chip
-// The 1D on-chip quantize with each tensor slice held in one of three
-// register sets and one LDS staging set: data thread i of workgroup w owns
-// half blocks w*S + p*D + i (p < kPer) of every tensor, as above.  Tensor t
-// is encoded from its register set; the set is then refilled from the LDS
-// stage with tensor t+3, whose maximum is taken right there, and the stage
-// is refilled with tensor t+4 by buffer-to-LDS loads.  A workgroup's
-// maximum of t+3 is published one step later and the amax of t+1 is
-// gathered during step t, so a tensor's maximum is published two steps
-// before any workgroup needs its amax: one slow workgroup (late data, a slow
-// fabric round trip) does not hold up the others unless it falls two steps
-// behind.  A step is one barrier:
-//   data waves:  barrier; encode t (table t); wait for own stage pieces of
-//                t+3, move them into t's register set, reduce t+3's maximum
-//                into LDS; reissue the stage pieces for t+4.
-//   sync wave:   barrier; publish the maximum of t+2 (reduced last step);
-//                gather the amax of t+1 and build its table.
-// Each data wave reads back only the stage pieces its own lanes loaded, so a
-// wave refills its part of the stage as soon as its own reads returned.
-// The compiler does not track buffer-to-LDS loads: the wait before the move
-// names the count explicitly (a step issues 2*kPer stores after the stage
-// loads it waits for).
-struct Reg3Shared {
-  double table[2][128];               // fp64 reciprocal of every block divisor, tensors of either parity
-  double r6[2];                       // reciprocal of d6 = RN32(6 g)
-  uint32_t red[2][kOnchipDataWaves];  // per-data-wave maxima of t+3, by the parity of the step t
-  uint32_t red0[3][kOnchipDataWaves]; // per-data-wave maxima of tensors 0..2 (prologue)
-};
-
-template <int kPer>
-__device__ __forceinline__ void reg3_load(u32x4 (&R)[kPer], const u32x4* __restrict__ x, int t, int batch, int64_t hb,
-                                          int voff) {
-  const __amdgpu_buffer_rsrc_t rs = tensor_rsrc(x, t, batch, hb * 16);
-#pragma unroll
-  for (int p = 0; p < kPer; ++p)
-    R[p] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, voff, p * kOnchipData * 16, kStreamLoad));
-}
-
+// ------------------------------------------------------------ on-chip pipeline helpers
 // One LDS read of 16 bytes at base + kOff (an immediate offset), complete on
 // return.
 template <int kOff>
@@ -759,7 +722,7 @@ __device__ __forceinline__ void bm_set(BlockMax<kPer>& bm, int p, uint32_t h) {
 
 // Block maxima of a whole set (prologue); returns the wave maximum.
 template <int kPer>
-__device__ __forceinline__ uint32_t reg3_block_max(const u32x4 (&R)[kPer], BlockMax<kPer>& bm) {
+__device__ __forceinline__ uint32_t set_block_max(const u32x4 (&R)[kPer], BlockMax<kPer>& bm) {
   uint32_t m = 0;
 #pragma unroll
   for (int p = 0; p < kPer; ++p) {
@@ -771,73 +734,91 @@ __device__ __forceinline__ uint32_t reg3_block_max(const u32x4 (&R)[kPer], Block
   return wave_max_u32(m);
 }
 
-// The stage: 16-byte slot (p, i) at byte p * D * 16 + i * 16 of L, with D
-// data threads; read back with immediate offsets from two bases (the
-// offset field holds 16 bits).
-constexpr int kStagePiece = kOnchipData * 16;          // 7168 bytes per piece
-constexpr int kStageSplit = 65536 / kStagePiece + 1;   // pieces reachable from the first base (10)
+// ------------------------------------------------------------ fused, four tensors on chip
+// The 1D FUSED quantize when one tensor fits on chip.  Data thread i (of
+// D = 512) of workgroup w owns half blocks w*S + p*D + i (p < kPer, S =
+// kPer*D) of every tensor, so every load and store instruction of a wave is
+// one contiguous run.  Four tensors are on chip at once: three in register
+// sets and one in an LDS stage.  Step t, piece by piece: encode piece p of
+// tensor t (its set) and store its codes and scale byte; move the stage's
+// piece p (tensor t+3) into the freed registers, taking its block maximum;
+// reload that stage slot with tensor t+4 by a buffer-to-LDS load (which
+// holds no registers).  The encode (VALU), the move (LDS) and the memory
+// operations of a wave interleave, and the eight waves (two per SIMD)
+// overlap them.
+//
+// A tensor's maximum is taken when it enters registers, three steps before
+// its encode.  Wave 7 does the exchange:
+//   - at the start of step t it publishes the workgroup's maximum of t+2
+//     (one agent-scope store into the workgroup's slot);
+//   - also at the start of step t it polls the slots of t+1 with a
+//     buffer-to-LDS load (so it never waits on the poll while its data loads
+//     are in flight), checks them at the end of step t and builds t+1's
+//     table of reciprocals before the step's single barrier.  Only if some
+//     workgroup has not published yet does it fall back to a bounded wait.
+// So each maximum is published a step before anyone polls it and two steps
+// before anyone needs it: a slow workgroup (late data, a slow fabric round
+// trip) holds up the others only when it falls that far behind.
+//
+// The compiler does not track buffer-to-LDS loads, so the waits are
+// explicit.  Every wave issues the same memory operations in the same order
+// (the other waves aim the exchange's store and two loads at zero-extent
+// resources), so the counts are the same constants in every wave: the stage
+// load of piece p issued a step earlier has 3*kPer + 2 younger operations
+// when piece p is moved, and the poll load 3*kPer at the end of the step.
+// Steps run in groups of three (the register sets rotate), then one or two
+// steps finish a batch that is not a multiple of three.
+constexpr int kR8Waves = 8;
+constexpr int kR8Data = 64 * kR8Waves;                 // data threads per workgroup
+constexpr int kR8MaxPer = 14;                          // 3 sets x 14 x 16 B in registers + 14 x 8 KiB of LDS
+constexpr int kR8StagePiece = kR8Data * 16;            // 8192 bytes per stage piece
+constexpr int kR8StageSplit = 65536 / kR8StagePiece;   // pieces reachable from the first base (8)
+constexpr int kR8PollSlots = 512;                      // slots one step's two poll loads cover
+
+struct Reg8Shared {
+  double table[2][128];               // fp64 reciprocal of every block divisor, tensors of either parity
+  double r6[2];                       // reciprocal of d6 = RN32(6 g)
+  uint32_t red[2][kR8Waves];          // per-wave maxima of t+3, by the parity of the step t
+  uint32_t red0[3][kR8Waves];         // per-wave maxima of tensors 0..2 (prologue)
+  u32x4 poll[kR8Waves][2][64];        // each wave's poll landing area (only wave 7's is read)
+};
 
 template <int kPer, int p>
-__device__ __forceinline__ u32x4 stage_read(uint32_t b0, uint32_t b1) {
-  if constexpr (p < kStageSplit) return lds_read_at<p * kStagePiece>(b0);
-  else return lds_read_at<(p - kStageSplit) * kStagePiece>(b1);
+__device__ __forceinline__ u32x4 r8_stage_read(uint32_t b0, uint32_t b1) {
+  if constexpr (p < kR8StageSplit) return lds_read_at<p * kR8StagePiece>(b0);
+  else return lds_read_at<(p - kR8StageSplit) * kR8StagePiece>(b1);
 }
 
-// One step, piece by piece: encode piece p of tensor t and store it, then
-// move the stage's piece p (tensor t+3) into the freed registers (taking its
-// block maximum) and reissue that stage slot for tensor t+4.  Per piece a
-// wave issues two stores and one stage load, so the stage load of piece p
-// issued a step earlier has exactly 3*kPer - 1 younger memory operations
-// when piece p is moved (the prologue issues its stage loads in the same
-// pattern).  The encode (VALU), the move (LDS) and the loads and stores
-// (memory) of a wave interleave, and the waves of a compute unit overlap
-// them.
 template <int kPer, int p>
-__device__ __forceinline__ void reg3_piece(u32x4 (&cur)[kPer], BlockMax<kPer>& bm, uint32_t& m, double r6,
-                                           const double* table, __amdgpu_buffer_rsrc_t rq, __amdgpu_buffer_rsrc_t rsf,
-                                           __amdgpu_buffer_rsrc_t rx, int qoff, int soff, int voff, uint32_t b0,
-                                           uint32_t b1, lds_void_t* stage_w) {
+__device__ __forceinline__ void r8_piece(u32x4 (&cur)[kPer], BlockMax<kPer>& bm, uint32_t& m, double r6,
+                                         const double* table, __amdgpu_buffer_rsrc_t rq, __amdgpu_buffer_rsrc_t rsf,
+                                         __amdgpu_buffer_rsrc_t rx, int qoff, int soff, int voff, uint32_t b0,
+                                         uint32_t b1, lds_void_t* stage_w) {
   const uint32_t sbyte = e4m3_rne_sat(rn32((double)bm_value<kPer>(bm, p) * r6));
   const uint32_t code = encode_half(cur[p], table[sbyte]);
-  __builtin_amdgcn_raw_buffer_store_b32(code, rq, qoff, p * kOnchipData * 4, 0);
-  __builtin_amdgcn_raw_buffer_store_b8((uint8_t)sbyte, rsf, soff, p * (kOnchipData / 2), 0);
-  wait_vmcnt<3 * kPer - 1>();                          // stage piece p of tensor t+3 has landed
-  cur[p] = stage_read<kPer, p>(b0, b1);
+  __builtin_amdgcn_raw_buffer_store_b32(code, rq, qoff, p * kR8Data * 4, 0);
+  __builtin_amdgcn_raw_buffer_store_b8((uint8_t)sbyte, rsf, soff, p * (kR8Data / 2), 0);
+  wait_vmcnt<3 * kPer + 2>();                          // stage piece p of tensor t+3 has landed
+  cur[p] = r8_stage_read<kPer, p>(b0, b1);
   const uint32_t h = pair_max(half_absmax_bits(cur[p]));
   m = m > h ? m : h;
   bm_set<kPer>(bm, p, h);
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void_t*)((__attribute__((address_space(3))) char*)stage_w +
-                                                             p * kStagePiece),
-                                           16, voff, p * kStagePiece, 0, kStreamLoad);
+                                                             p * kR8StagePiece),
+                                           16, voff, p * kR8StagePiece, 0, kStreamLoad);
   __builtin_amdgcn_sched_barrier(0);                   // keep each piece's operations in this order
 }
 
 template <int kPer, int... P>
-__device__ __forceinline__ void reg3_pieces(std::integer_sequence<int, P...>, u32x4 (&cur)[kPer], BlockMax<kPer>& bm,
-                                            uint32_t& m, double r6, const double* table, __amdgpu_buffer_rsrc_t rq,
-                                            __amdgpu_buffer_rsrc_t rsf, __amdgpu_buffer_rsrc_t rx, int qoff, int soff,
-                                            int voff, uint32_t b0, uint32_t b1, lds_void_t* stage_w) {
-  (reg3_piece<kPer, P>(cur, bm, m, r6, table, rq, rsf, rx, qoff, soff, voff, b0, b1, stage_w), ...);
+__device__ __forceinline__ void r8_pieces(std::integer_sequence<int, P...>, u32x4 (&cur)[kPer], BlockMax<kPer>& bm,
+                                          uint32_t& m, double r6, const double* table, __amdgpu_buffer_rsrc_t rq,
+                                          __amdgpu_buffer_rsrc_t rsf, __amdgpu_buffer_rsrc_t rx, int qoff, int soff,
+                                          int voff, uint32_t b0, uint32_t b1, lds_void_t* stage_w) {
+  (r8_piece<kPer, P>(cur, bm, m, r6, table, rq, rsf, rx, qoff, soff, voff, b0, b1, stage_w), ...);
 }
 
-template <int kPer>
-__device__ __forceinline__ void reg3_step(const u32x4* __restrict__ x, int t, int batch, int64_t hb, int voff,
-                                          int qoff, int soff, u32x4 (&cur)[kPer], BlockMax<kPer>& bm, uint32_t b0,
-                                          uint32_t b1, lds_void_t* stage_w, uint32_t* __restrict__ q,
-                                          uint8_t* __restrict__ sf, Reg3Shared& sh) {
-  lds_barrier();                                       // t's table is ready; the previous maxima were taken
-  const double r6 = sh.r6[t & 1];
-  const double* table = sh.table[t & 1];
-  const __amdgpu_buffer_rsrc_t rq = tensor_rsrc(q, t, batch, hb * 4);
-  const __amdgpu_buffer_rsrc_t rsf = tensor_rsrc(sf, t, batch, hb / 2);
-  const __amdgpu_buffer_rsrc_t rx = tensor_rsrc(x, t + 4, batch, hb * 16);   // extent zero past the batch
-  uint32_t m = 0;
-  reg3_pieces<kPer>(std::make_integer_sequence<int, kPer>{}, cur, bm, m, r6, table, rq, rsf, rx, qoff, soff, voff, b0,
-                    b1, stage_w);
-  sh.red[t & 1][wave_id()] = wave_max_u32(m);          // wave-uniform value and address
-}
-
-__device__ __forceinline__ void reg3_table(Reg3Shared& sh, int t, uint32_t v, float* __restrict__ gout) {
+// Table of tensor t from its amax (bit 31 set), or NaN after a wait gave up.
+__device__ __forceinline__ void r8_table(Reg8Shared& sh, int t, uint32_t v, float* __restrict__ gout) {
   const int lane = threadIdx.x & 63;
   const float g = v ? __uint_as_float((v & 0x7fffu) << 16) / kGlobalDiv : __builtin_nanf("");
   sh.table[t & 1][lane] = recip_entry((uint32_t)lane, g);
@@ -848,27 +829,146 @@ __device__ __forceinline__ void reg3_table(Reg3Shared& sh, int t, uint32_t v, fl
   }
 }
 
-__device__ __forceinline__ uint32_t reg3_red_max(const uint32_t* red) {
+__device__ __forceinline__ uint32_t r8_red_max(const uint32_t* red) {
   uint32_t r = red[0];
 #pragma unroll
-  for (int k = 1; k < kOnchipDataWaves; ++k) r = r > red[k] ? r : red[k];
+  for (int k = 1; k < kR8Waves; ++k) r = r > red[k] ? r : red[k];
   return r;
 }
 
-__device__ __forceinline__ void reg3_sync_wave(uint32_t* ws, int batch, int G, float* __restrict__ gout,
-                                               Reg3Shared& sh) {
-  const int lane = threadIdx.x & 63;
-  lds_barrier();                                       // maxima of tensors 0..2
-  if (lane == 0)
-    for (int k = 0; k < 3 && k < batch; ++k) onchip_publish(ws, k, reg3_red_max(sh.red0[k]));
-  reg3_table(sh, 0, onchip_wait(ws, 0, G), gout);
-  for (int t = 0; t < batch; ++t) {
-    lds_barrier();                                     // step t: the data waves encode t
-    if (t >= 1 && t + 2 < batch && lane == 0) onchip_publish(ws, t + 2, reg3_red_max(sh.red[(t - 1) & 1]));
-    if (t + 1 < batch) reg3_table(sh, t + 1, onchip_wait(ws, t + 1, G), gout);
+// The three memory operations that open a step: wave 7 publishes (when
+// there is a maximum to publish) and polls tensor tp's slots; every other
+// wave, and wave 7 when there is nothing to do, aims them at zero-extent
+// resources.
+__device__ __forceinline__ void r8_exchange_ops(uint32_t* ws, int G, int tpub, uint32_t mpub, int tp, bool do_poll,
+                                                Reg8Shared& sh) {
+  const int wave = wave_id(), lane = threadIdx.x & 63;
+  const bool mine = wave == kR8Waves - 1;
+  const __amdgpu_buffer_rsrc_t none = __builtin_amdgcn_make_buffer_rsrc(ws, 0, 0, kBufferWord3);
+  if (mine && tpub >= 0) {
+    if (lane == 0) onchip_publish(ws, tpub, mpub);
+  } else {
+    __builtin_amdgcn_raw_buffer_store_b32(0u, none, 0, 0, 0);
   }
+  const int ext = (mine && do_poll) ? G * 4 : 0;
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(fused_line(ws, tp < 0 ? 0 : tp, 0), 0, ext,
+                                                                      kBufferWord3);
+  lds_void_t* dst = (lds_void_t*)(uintptr_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uintptr_t)&sh.poll[wave][0][0]);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst, 16, lane * 16, 0, 0, kCoherentLoad);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)((__attribute__((address_space(3))) char*)dst + 1024), 16,
+                                           lane * 16, 1024, 0, kCoherentLoad);
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// Wave 7 at the end of step t: the polled slots of tensor tp (landed: the
+// step's wait covers them), or a bounded wait if some workgroup is behind.
+__device__ __forceinline__ uint32_t r8_gather(uint32_t* ws, int tp, int G, const Reg8Shared& sh) {
+  const int lane = threadIdx.x & 63;
+  uint32_t mx = 0, ok = 1;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const u32x4 v = sh.poll[kR8Waves - 1][h][lane];
+    const int i = h * 256 + 4 * lane;
+    ok &= (i >= G || (v.x >> 31)) && (i + 1 >= G || (v.y >> 31)) && (i + 2 >= G || (v.z >> 31)) &&
+          (i + 3 >= G || (v.w >> 31));
+    const uint32_t m2 = v.x > v.y ? v.x : v.y, m3 = v.z > v.w ? v.z : v.w;
+    const uint32_t m4 = m2 > m3 ? m2 : m3;
+    mx = mx > m4 ? mx : m4;
+  }
+  if (__builtin_amdgcn_ballot_w64(ok == 0) == 0) return wave_max_u32(mx);
+  return onchip_wait(ws, tp, G);
+}
+
+template <int kPer>
+__device__ __forceinline__ void r8_step(const u32x4* __restrict__ x, int t, int batch, int64_t hb, int voff, int qoff,
+                                        int soff, u32x4 (&cur)[kPer], BlockMax<kPer>& bm, uint32_t b0, uint32_t b1,
+                                        lds_void_t* stage_w, uint32_t* ws, int G, float* __restrict__ gout,
+                                        uint32_t* __restrict__ q, uint8_t* __restrict__ sf, Reg8Shared& sh) {
+  lds_barrier();                                       // t's table is ready; the maxima of t+2 were reduced
+  const bool pub = t >= 1 && t + 2 < batch;
+  r8_exchange_ops(ws, G, pub ? t + 2 : -1, pub ? r8_red_max(sh.red[(t - 1) & 1]) : 0u, t + 1, t + 1 < batch, sh);
+  const double r6 = sh.r6[t & 1];
+  const double* table = sh.table[t & 1];
+  const __amdgpu_buffer_rsrc_t rq = tensor_rsrc(q, t, batch, hb * 4);
+  const __amdgpu_buffer_rsrc_t rsf = tensor_rsrc(sf, t, batch, hb / 2);
+  const __amdgpu_buffer_rsrc_t rx = tensor_rsrc(x, t + 4, batch, hb * 16);   // extent zero past the batch
+  uint32_t m = 0;
+  r8_pieces<kPer>(std::make_integer_sequence<int, kPer>{}, cur, bm, m, r6, table, rq, rsf, rx, qoff, soff, voff, b0,
+                  b1, stage_w);
+  sh.red[t & 1][wave_id()] = wave_max_u32(m);          // wave-uniform value and address
+  wait_vmcnt<3 * kPer>();                              // the poll loads of this step have landed
+  if (wave_id() == kR8Waves - 1 && t + 1 < batch) r8_table(sh, t + 1, r8_gather(ws, t + 1, G, sh), gout);
+}
+
+template <int kPer>
+__global__ void __launch_bounds__(kR8Data) fused_reg8_kernel(const u32x4* __restrict__ x, int batch, int64_t hb,
+                                                             uint32_t* ws, float* __restrict__ gout,
+                                                             uint32_t* __restrict__ q, uint8_t* __restrict__ sf) {
+  static_assert(kPer % 2 == 0 && kPer <= kR8MaxPer, "pieces in pairs, within the register budget");
+  __shared__ Reg8Shared sh;
+  __shared__ __attribute__((aligned(16))) u32x4 L[kPer][kR8Data];
+  const int G = gridDim.x;
+  const int lane = (int)threadIdx.x & 63, wave = wave_id();
+  const int voff = ((int)blockIdx.x * kPer * kR8Data + (int)threadIdx.x) * 16;
+  const int qoff = voff / 4;
+  // even lanes write the pair's scale byte; odd lanes aim past the extent
+  const int soff = (lane & 1) ? (int)0x80000000u : voff / 32;
+  u32x4 a[kPer], b[kPer], c[kPer];
+  BlockMax<kPer> am, bmx, cm;
+  {
+    const __amdgpu_buffer_rsrc_t r0 = tensor_rsrc(x, 0, batch, hb * 16), r1 = tensor_rsrc(x, 1, batch, hb * 16),
+                                 r2 = tensor_rsrc(x, 2, batch, hb * 16);
+#pragma unroll
+    for (int p = 0; p < kPer; ++p)
+      a[p] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r0, voff, p * kR8StagePiece, kStreamLoad));
+#pragma unroll
+    for (int p = 0; p < kPer; ++p)
+      b[p] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r1, voff, p * kR8StagePiece, kStreamLoad));
+#pragma unroll
+    for (int p = 0; p < kPer; ++p)
+      c[p] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r2, voff, p * kR8StagePiece, kStreamLoad));
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  const uint32_t b0 = (uint32_t)(uintptr_t)&L[0][threadIdx.x];
+  const uint32_t b1 = b0 + kR8StageSplit * kR8StagePiece;
+  lds_void_t* const stage_w =
+      (lds_void_t*)(uintptr_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uintptr_t)&L[0][threadIdx.x & ~63]);
+  {
+    // tensor 3 into the stage, each piece after two stores aimed at
+    // zero-extent resources: the memory operations of a step, in order
+    const __amdgpu_buffer_rsrc_t nq = tensor_rsrc(q, batch, batch, 0), ns = tensor_rsrc(sf, batch, batch, 0);
+    const __amdgpu_buffer_rsrc_t rx = tensor_rsrc(x, 3, batch, hb * 16);
+#pragma unroll
+    for (int p = 0; p < kPer; ++p) {
+      __builtin_amdgcn_raw_buffer_store_b32(0u, nq, qoff, p * kR8Data * 4, 0);
+      __builtin_amdgcn_raw_buffer_store_b8((uint8_t)0, ns, soff, p * (kR8Data / 2), 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rx, (lds_void_t*)((__attribute__((address_space(3))) char*)stage_w + p * kR8StagePiece), 16, voff,
+          p * kR8StagePiece, 0, kStreamLoad);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  sh.red0[0][wave] = set_block_max<kPer>(a, am);
+  sh.red0[1][wave] = set_block_max<kPer>(b, bmx);
+  sh.red0[2][wave] = set_block_max<kPer>(c, cm);
+  lds_barrier();                                       // maxima of tensors 0..2
+  if (wave == kR8Waves - 1) {
+    if (lane == 0)
+      for (int k = 0; k < 3 && k < batch; ++k) onchip_publish(ws, k, r8_red_max(sh.red0[k]));
+    r8_table(sh, 0, onchip_wait(ws, 0, G), gout);
+  }
+  int t = 0;
+  for (; t + 3 <= batch; t += 3) {
+    r8_step<kPer>(x, t, batch, hb, voff, qoff, soff, a, am, b0, b1, stage_w, ws, G, gout, q, sf, sh);
+    r8_step<kPer>(x, t + 1, batch, hb, voff, qoff, soff, b, bmx, b0, b1, stage_w, ws, G, gout, q, sf, sh);
+    r8_step<kPer>(x, t + 2, batch, hb, voff, qoff, soff, c, cm, b0, b1, stage_w, ws, G, gout, q, sf, sh);
+  }
+  if (t < batch) r8_step<kPer>(x, t, batch, hb, voff, qoff, soff, a, am, b0, b1, stage_w, ws, G, gout, q, sf, sh);
+  if (t + 1 < batch) r8_step<kPer>(x, t + 1, batch, hb, voff, qoff, soff, b, bmx, b0, b1, stage_w, ws, G, gout, q, sf, sh);
+  wait_vmcnt<0>();                                     // no stage or poll load still writing LDS at exit
+  if (wave != kR8Waves - 1) return;
   // the last workgroup out restores the slots and the counter to zero; every
-  // slot read of this workgroup has returned (the values were used above)
+  // slot store of this workgroup has completed (the wait above)
   uint32_t last = 0;
   if (lane == 0)
     last = __hip_atomic_fetch_add(&((FusedHeader*)ws)->done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
@@ -880,68 +980,6 @@ __device__ __forceinline__ void reg3_sync_wave(uint32_t* ws, int batch, int G, f
       __hip_atomic_store(base + i, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (lane == 0) __hip_atomic_store(&((FusedHeader*)ws)->done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
-}
-
-// Steps run in groups of three (the register sets rotate), then one or two
-// steps finish a batch that is not a multiple of three.
-template <int kPer>
-__global__ void __launch_bounds__(kOnchipThreads) fused_reg3_kernel(const u32x4* __restrict__ x, int batch, int64_t hb,
-                                                                    uint32_t* ws, float* __restrict__ gout,
-                                                                    uint32_t* __restrict__ q,
-                                                                    uint8_t* __restrict__ sf) {
-  static_assert(kPer % 2 == 0 && kPer <= kOnchipMaxPer, "pieces move in pairs");
-  __shared__ Reg3Shared sh;
-  __shared__ __attribute__((aligned(16))) u32x4 L[kPer][kOnchipData];
-  const int G = gridDim.x;
-  if (wave_id() < kOnchipDataWaves) {
-    const int lane = (int)threadIdx.x & 63;
-    const int voff = ((int)blockIdx.x * kPer * kOnchipData + (int)threadIdx.x) * 16;
-    const int qoff = voff / 4;
-    // even lanes write the pair's scale byte; odd lanes aim past the extent
-    const int soff = (lane & 1) ? (int)0x80000000u : voff / 32;
-    u32x4 a[kPer], b[kPer], c[kPer];
-    BlockMax<kPer> am, bmx, cm;
-    reg3_load<kPer>(a, x, 0, batch, hb, voff);
-    reg3_load<kPer>(b, x, 1, batch, hb, voff);
-    reg3_load<kPer>(c, x, 2, batch, hb, voff);
-    __builtin_amdgcn_sched_barrier(0);
-    // the stage: this thread's slots read from two bases, this wave's slots
-    // filled through an LDS base held in scalar registers
-    const uint32_t b0 = (uint32_t)(uintptr_t)&L[0][threadIdx.x];
-    const uint32_t b1 = b0 + kStageSplit * kStagePiece;
-    lds_void_t* const stage_w =
-        (lds_void_t*)(uintptr_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uintptr_t)&L[0][threadIdx.x & ~63]);
-    {
-      // tensor 3 into the stage, each piece after two stores aimed at
-      // zero-extent resources: the memory operations of a step, in order
-      const __amdgpu_buffer_rsrc_t nq = tensor_rsrc(q, batch, batch, 0), ns = tensor_rsrc(sf, batch, batch, 0);
-      const __amdgpu_buffer_rsrc_t rx = tensor_rsrc(x, 3, batch, hb * 16);
-#pragma unroll
-      for (int p = 0; p < kPer; ++p) {
-        __builtin_amdgcn_raw_buffer_store_b32(0u, nq, qoff, p * kOnchipData * 4, 0);
-        __builtin_amdgcn_raw_buffer_store_b8((uint8_t)0, ns, soff, p * (kOnchipData / 2), 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rx, (lds_void_t*)((__attribute__((address_space(3))) char*)stage_w + p * kStagePiece), 16, voff,
-            p * kStagePiece, 0, kStreamLoad);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    sh.red0[0][wave_id()] = reg3_block_max<kPer>(a, am);
-    sh.red0[1][wave_id()] = reg3_block_max<kPer>(b, bmx);
-    sh.red0[2][wave_id()] = reg3_block_max<kPer>(c, cm);
-    lds_barrier();                                     // maxima of tensors 0..2
-    int t = 0;
-    for (; t + 3 <= batch; t += 3) {
-      reg3_step<kPer>(x, t, batch, hb, voff, qoff, soff, a, am, b0, b1, stage_w, q, sf, sh);
-      reg3_step<kPer>(x, t + 1, batch, hb, voff, qoff, soff, b, bmx, b0, b1, stage_w, q, sf, sh);
-      reg3_step<kPer>(x, t + 2, batch, hb, voff, qoff, soff, c, cm, b0, b1, stage_w, q, sf, sh);
-    }
-    if (t < batch) reg3_step<kPer>(x, t, batch, hb, voff, qoff, soff, a, am, b0, b1, stage_w, q, sf, sh);
-    if (t + 1 < batch) reg3_step<kPer>(x, t + 1, batch, hb, voff, qoff, soff, b, bmx, b0, b1, stage_w, q, sf, sh);
-    wait_vmcnt<0>();                                   // no stage load still writing LDS at exit
-    return;
-  }
-  reg3_sync_wave(ws, batch, G, gout, sh);
 }
 
 // ------------------------------------------------------------ dequantize
@@ -972,7 +1010,7 @@ __global__ void __launch_bounds__(kThreads) dequant_kernel(const uint32_t* __res
 }
 
 // Clears n words of scratch (the exchange header of a workspace whose
-// contents are not guaranteed, before a cooperative launch uses it).
+// contents are not guaranteed, before a co-resident launch uses it).
 __global__ void __launch_bounds__(kThreads) zero_words_kernel(uint32_t* __restrict__ p, int64_t n) {
   for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n; i += (int64_t)gridDim.x * kThreads) p[i] = 0u;
 }
@@ -1037,18 +1075,35 @@ int fused_grid(int64_t hb_per_tensor) {
   return (int)std::max<int64_t>(1, std::min(g, need));
 }
 
-// Half blocks per data thread for the on-chip persistent launch: the
-// smallest even count that covers a tensor with at most one workgroup per
-// CU, or 0 when the tensor is too large to hold on chip (the streaming
-// launch runs then).
+// Half blocks per data thread for the on-chip FUSED launch: the smallest
+// even count that covers a tensor with at most one workgroup per CU, or 0
+// when the tensor is too large to hold on chip (the streaming launch runs
+// then).
 int onchip_per_thread(int64_t hb_per_tensor) {
   if (hb_per_tensor <= 0) return 0;
   const int64_t cus = nvfp4host::num_cus();
-  if (cus > (int64_t)kTensorWords) return 0;           // one exchange slot per workgroup
-  const int64_t cap = cus * kOnchipData;
+  if (cus > kR8PollSlots || cus > (int64_t)kTensorWords) return 0;   // one exchange slot per workgroup
+  const int64_t cap = cus * kR8Data;
   int64_t per = (hb_per_tensor + cap - 1) / cap;
-  per += per & 1;                                       // pieces move in pairs
-  return per <= kOnchipMaxPer ? (int)per : 0;
+  per += per & 1;                                       // pieces pair up in the block-maximum words
+  return per <= kR8MaxPer ? (int)per : 0;
+}
+
+// Launches a kernel whose workgroups wait for one another (bounded waits):
+// the grid is at most one round of resident workgroups (the caller sizes it
+// from the device's compute units and the kernel's occupancy), so on a
+// device not filled by other persistent kernels every workgroup starts at
+// once.  A plain launch: a cooperative one guarantees the same residency but
+// costs about 16 us more per launch on this device; if some workgroup did
+// not become resident in time, the waits give up, g becomes NaN and
+// nvfp4_quantize_status reports it.
+nvfp4_status launch_resident(const void* fn, int grid, int block, void** args, hipStream_t s) {
+  const hipError_t e = hipLaunchKernel(fn, dim3((unsigned)grid), dim3((unsigned)block), args, 0, s);
+  if (e != hipSuccess) {
+    nvfp4host::set_hip_error(e);
+    return NVFP4_EHIP;
+  }
+  return NVFP4_OK;
 }
 
 }  // namespace
@@ -1061,7 +1116,7 @@ size_t quantize_2d_onchip_ws_bytes(int64_t batch) {
 }
 
 // 2D quantize (one E4M3 scale per 16 x 16 tile; outputs row-major, or
-// transposed with colwise) of batch tensors [rows][cols] in one cooperative
+// transposed with colwise) of batch tensors [rows][cols] in one
 // launch of fused_onchip_kernel<16, kOn2D | kOn2DT> when a tensor's 16-row x
 // 8-column strips fit on the chip: every input byte is read once.  ENOTSUP when they do not (the
 // caller then runs its two-pass path).  The exchange header in ws is
@@ -1088,12 +1143,7 @@ nvfp4_status quantize_2d_onchip(const uint16_t* x, int64_t batch, int64_t rows, 
   uint32_t* qa = (uint32_t*)q;
   void* args[] = {&xa, &bt, (void*)&hb, &spri, &srowsi, &wsa, &g, &qa, &sf};
   const void* fn = colwise ? (const void*)fused_onchip_kernel<16, kOn2DT> : (const void*)fused_onchip_kernel<16, kOn2D>;
-  const hipError_t e = hipLaunchCooperativeKernel(fn, dim3((unsigned)G), dim3(kOnchipThreads), args, 0, s);
-  if (e != hipSuccess) {
-    set_hip_error(e);
-    return NVFP4_EHIP;
-  }
-  return NVFP4_OK;
+  return launch_resident(fn, (int)G, kOnchipThreads, args, s);
 }
 
 }  // namespace nvfp4host
@@ -1143,45 +1193,22 @@ nvfp4_status quantize_launch(const uint16_t* x, int64_t batch, int64_t rows, int
   const int64_t hb = n / 8;
   if (flags == NVFP4_FUSED) {
     const int onchip_per = onchip_per_thread(hb);
-    if (onchip_per > 0) {
-      const u32x4* xa = (const u32x4*)x;
-      int bt = (int)batch;
-      uint32_t* ws = (uint32_t*)workspace;
-      uint32_t* qa = (uint32_t*)q;
-      const int64_t slice = (int64_t)onchip_per * kOnchipData;
-      const int G = (int)((hb + slice - 1) / slice);
-      const void* fn = nullptr;
-      const void* fns[kOnchipMaxPer / 2] = {
-          (const void*)fused_reg3_kernel<2>,
-          (const void*)fused_reg3_kernel<4>,
-          (const void*)fused_reg3_kernel<6>,
-          (const void*)fused_reg3_kernel<8>,
-          (const void*)fused_reg3_kernel<10>,
-          (const void*)fused_reg3_kernel<12>,
-          (const void*)fused_reg3_kernel<14>,
-          (const void*)fused_reg3_kernel<16>,
-      };
-      fn = fns[onchip_per / 2 - 1];
-      void* args3[] = {&xa, &bt, (void*)&hb, &ws, &g, &qa, &sf};
-      hipError_t e = hipLaunchCooperativeKernel(fn, dim3(G), dim3(kOnchipThreads), args3, 0, s);
-      if (e != hipSuccess) {
-        nvfp4host::set_hip_error(e);
-        return NVFP4_EHIP;
-      }
-      return NVFP4_OK;
-    }
-    const int G = fused_grid(hb);
     const u32x4* xa = (const u32x4*)x;
     int bt = (int)batch;
     uint32_t* ws = (uint32_t*)workspace;
     uint32_t* qa = (uint32_t*)q;
     void* args[] = {&xa, &bt, (void*)&hb, &ws, &g, &qa, &sf};
-    hipError_t e = hipLaunchCooperativeKernel((const void*)fused_quantize_kernel, dim3(G), dim3(kThreads), args, 0, s);
-    if (e != hipSuccess) {
-      nvfp4host::set_hip_error(e);
-      return NVFP4_EHIP;
+    if (onchip_per > 0) {
+      const int64_t slice = (int64_t)onchip_per * kR8Data;
+      const int G = (int)((hb + slice - 1) / slice);
+      const void* fns[kR8MaxPer / 2] = {
+          (const void*)fused_reg8_kernel<2>,  (const void*)fused_reg8_kernel<4>,  (const void*)fused_reg8_kernel<6>,
+          (const void*)fused_reg8_kernel<8>,  (const void*)fused_reg8_kernel<10>, (const void*)fused_reg8_kernel<12>,
+          (const void*)fused_reg8_kernel<14>,
+      };
+      return launch_resident(fns[onchip_per / 2 - 1], G, kR8Data, args, s);
     }
-    return NVFP4_OK;
+    return launch_resident((const void*)fused_quantize_kernel, fused_grid(hb), kThreads, args, s);
   }
   const size_t head = (fused_header_bytes(batch) + 255) & ~(size_t)255;
   uint32_t* partial = (uint32_t*)((char*)workspace + head);

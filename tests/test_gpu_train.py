@@ -60,7 +60,7 @@ def test_colwise_variants_over_several_row_blocks(variant, shape):
 @pytest.mark.parametrize("variant", [2, 3])
 @pytest.mark.parametrize("shape", [(5, 48, 1040), (2, 512, 7168), (1, 16, 16), (7, 32, 4096), (2, 400, 80)])
 def test_2d_single_launch_shapes(shape, variant):
-    """2D (row-major or transposed outputs) runs as one cooperative launch
+    """2D (row-major or transposed outputs) runs as one launch
     when a tensor's 16 x 8 strips fit on the chip: strip rows that cross
     workgroup boundaries (cols = 1040), 64 workgroups per tensor, a single
     tile, a batch of 7, and strip blocks cut by the tensor's edge in both
