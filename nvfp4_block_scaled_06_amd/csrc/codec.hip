@@ -789,7 +789,7 @@ __device__ __forceinline__ u32x4 r8_stage_read(uint32_t b0, uint32_t b1) {
   else return lds_read_at<(p - kR8StageSplit) * kR8StagePiece>(b1);
 }
 
-template <int kPer, int p>
+template <int kPer, int p, int kWait>
 __device__ __forceinline__ void r8_piece(u32x4 (&cur)[kPer], BlockMax<kPer>& bm, uint32_t& m, double r6,
                                          const double* table, __amdgpu_buffer_rsrc_t rq, __amdgpu_buffer_rsrc_t rsf,
                                          __amdgpu_buffer_rsrc_t rx, int qoff, int soff, int voff, uint32_t b0,
@@ -798,7 +798,7 @@ __device__ __forceinline__ void r8_piece(u32x4 (&cur)[kPer], BlockMax<kPer>& bm,
   const uint32_t code = encode_half(cur[p], table[sbyte]);
   __builtin_amdgcn_raw_buffer_store_b32(code, rq, qoff, p * kR8Data * 4, 0);
   __builtin_amdgcn_raw_buffer_store_b8((uint8_t)sbyte, rsf, soff, p * (kR8Data / 2), 0);
-  wait_vmcnt<3 * kPer + 2>();                          // stage piece p of tensor t+3 has landed
+  wait_vmcnt<kWait>();                                 // stage piece p (issued a step earlier) has landed
   cur[p] = r8_stage_read<kPer, p>(b0, b1);
   const uint32_t h = pair_max(half_absmax_bits(cur[p]));
   m = m > h ? m : h;
@@ -809,12 +809,12 @@ __device__ __forceinline__ void r8_piece(u32x4 (&cur)[kPer], BlockMax<kPer>& bm,
   __builtin_amdgcn_sched_barrier(0);                   // keep each piece's operations in this order
 }
 
-template <int kPer, int... P>
+template <int kPer, int kWait, int... P>
 __device__ __forceinline__ void r8_pieces(std::integer_sequence<int, P...>, u32x4 (&cur)[kPer], BlockMax<kPer>& bm,
                                           uint32_t& m, double r6, const double* table, __amdgpu_buffer_rsrc_t rq,
                                           __amdgpu_buffer_rsrc_t rsf, __amdgpu_buffer_rsrc_t rx, int qoff, int soff,
                                           int voff, uint32_t b0, uint32_t b1, lds_void_t* stage_w) {
-  (r8_piece<kPer, P>(cur, bm, m, r6, table, rq, rsf, rx, qoff, soff, voff, b0, b1, stage_w), ...);
+  (r8_piece<kPer, P, kWait>(cur, bm, m, r6, table, rq, rsf, rx, qoff, soff, voff, b0, b1, stage_w), ...);
 }
 
 // Table of tensor t from its amax (bit 31 set), or NaN after a wait gave up.
@@ -893,7 +893,8 @@ __device__ __forceinline__ void r8_step(const u32x4* __restrict__ x, int t, int 
   const __amdgpu_buffer_rsrc_t rsf = tensor_rsrc(sf, t, batch, hb / 2);
   const __amdgpu_buffer_rsrc_t rx = tensor_rsrc(x, t + 4, batch, hb * 16);   // extent zero past the batch
   uint32_t m = 0;
-  r8_pieces<kPer>(std::make_integer_sequence<int, kPer>{}, cur, bm, m, r6, table, rq, rsf, rx, qoff, soff, voff, b0,
+  r8_pieces<kPer, 3 * kPer + 2>(std::make_integer_sequence<int, kPer>{}, cur, bm, m, r6, table, rq, rsf, rx, qoff, soff,
+                                voff, b0,
                   b1, stage_w);
   sh.red[t & 1][wave_id()] = wave_max_u32(m);          // wave-uniform value and address
   wait_vmcnt<3 * kPer>();                              // the poll loads of this step have landed
@@ -969,6 +970,171 @@ __global__ void __launch_bounds__(kR8Data) fused_reg8_kernel(const u32x4* __rest
   if (wave != kR8Waves - 1) return;
   // the last workgroup out restores the slots and the counter to zero; every
   // slot store of this workgroup has completed (the wait above)
+  uint32_t last = 0;
+  if (lane == 0)
+    last = __hip_atomic_fetch_add(&((FusedHeader*)ws)->done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+           (uint32_t)G - 1;
+  if (__builtin_amdgcn_readfirstlane((int)last)) {
+    const size_t words = (size_t)batch * kTensorWords;
+    uint32_t* base = ws + kFusedHeaderBytes / 4;
+    for (size_t i = lane; i < words; i += 64)
+      __hip_atomic_store(base + i, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (lane == 0) __hip_atomic_store(&((FusedHeader*)ws)->done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+// ------------------------------------------------------------ fused, tensors larger than the chip
+// One launch for tensors of nc >= 4 chunks, a chunk being what the on-chip
+// kernel holds (D = 512 threads x kPer half blocks per workgroup, one
+// workgroup per compute unit).  Per tensor:
+//   pass 1: the last three chunks load straight into the three register
+//     sets; every other chunk streams through the LDS stage (its maximum
+//     taken as it lands, the slot reloaded with the next chunk), and chunk
+//     nc-4 stays in the stage;
+//   exchange: wave 7 publishes the workgroup's maximum and waits for the
+//     tensor's amax, then builds the table;
+//   pass 2: the encode walks the chunks in the order nc-3, nc-2, nc-1, nc-4,
+//     nc-5, ..., 0 with the register sets and the stage exactly as the
+//     on-chip kernel walks tensors: encode a set, move the stage into it,
+//     reload the stage with the chunk four places on.
+// So four chunks are read once and the others twice, newest first (the most
+// recently read data is the likeliest to still be in the last-level cache).
+template <int kPer>
+__device__ __forceinline__ void big_load_set(u32x4 (&R)[kPer], __amdgpu_buffer_rsrc_t rs, int voff) {
+#pragma unroll
+  for (int p = 0; p < kPer; ++p)
+    R[p] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, voff, p * kR8StagePiece, kStreamLoad));
+}
+
+template <int kPer>
+__device__ __forceinline__ void big_stage_issue(__amdgpu_buffer_rsrc_t rs, lds_void_t* stage_w, int voff) {
+#pragma unroll
+  for (int p = 0; p < kPer; ++p)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rs, (lds_void_t*)((__attribute__((address_space(3))) char*)stage_w + p * kR8StagePiece), 16, voff,
+        p * kR8StagePiece, 0, kStreamLoad);
+}
+
+// Pass 1 over one chunk in the stage: the maximum of each piece as it lands
+// (the load of piece p has kPer - 1 younger loads: the other pieces), then
+// the slot reloaded from `next` at voff_next.
+template <int kPer, int p>
+__device__ __forceinline__ void big_stage_piece(uint32_t& m, uint32_t b0, uint32_t b1, __amdgpu_buffer_rsrc_t next,
+                                                lds_void_t* stage_w, int voff_next) {
+  wait_vmcnt<kPer - 1>();
+  const u32x4 v = r8_stage_read<kPer, p>(b0, b1);
+  const uint32_t h = half_absmax_bits(v);
+  m = m > h ? m : h;
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(next, (lds_void_t*)((__attribute__((address_space(3))) char*)stage_w +
+                                                               p * kR8StagePiece),
+                                           16, voff_next, p * kR8StagePiece, 0, kStreamLoad);
+  __builtin_amdgcn_sched_barrier(0);
+}
+template <int kPer, int... P>
+__device__ __forceinline__ void big_stage_chunk(std::integer_sequence<int, P...>, uint32_t& m, uint32_t b0, uint32_t b1,
+                                                __amdgpu_buffer_rsrc_t next, lds_void_t* stage_w, int voff_next) {
+  (big_stage_piece<kPer, P>(m, b0, b1, next, stage_w, voff_next), ...);
+}
+template <int kPer, int p>
+__device__ __forceinline__ void big_stage_piece_max(uint32_t& m, uint32_t b0, uint32_t b1) {
+  const uint32_t h = half_absmax_bits(r8_stage_read<kPer, p>(b0, b1));
+  m = m > h ? m : h;
+}
+template <int kPer, int... P>
+__device__ __forceinline__ uint32_t big_stage_max(std::integer_sequence<int, P...>, uint32_t b0, uint32_t b1) {
+  uint32_t m = 0;
+  (big_stage_piece_max<kPer, P>(m, b0, b1), ...);
+  return m;
+}
+
+// Chunk encoded at pass-2 position s of nc chunks.
+__device__ __forceinline__ int big_chunk(int s, int nc) { return s < 3 ? nc - 3 + s : nc - 1 - s; }
+
+// Pass 2, position s: encode `cur` (chunk big_chunk(s)), move the stage
+// (position s+3) into it, reload the stage with position s+4.  The stage
+// load of piece p issued at position s-1 has 3*kPer - 1 younger operations.
+template <int kPer>
+__device__ __forceinline__ void big_step(int s, int nc, int cbytes, __amdgpu_buffer_rsrc_t rx, __amdgpu_buffer_rsrc_t rq,
+                                         __amdgpu_buffer_rsrc_t rsf, int voff, int qoff, int soff, u32x4 (&cur)[kPer],
+                                         BlockMax<kPer>& bm, uint32_t b0, uint32_t b1, lds_void_t* stage_w, double r6,
+                                         const double* table, __amdgpu_buffer_rsrc_t none) {
+  const int co = big_chunk(s, nc);
+  const bool more = s + 4 < nc;
+  const int cn = more ? big_chunk(s + 4, nc) : 0;
+  uint32_t m = 0;
+  r8_pieces<kPer, 3 * kPer - 1>(std::make_integer_sequence<int, kPer>{}, cur, bm, m, r6, table, rq, rsf,
+                                more ? rx : none, qoff + co * (cbytes / 4), soff + co * (cbytes / 32),
+                                voff + cn * cbytes, b0, b1, stage_w);
+}
+
+template <int kPer>
+__global__ void __launch_bounds__(kR8Data) fused_big_kernel(const u32x4* __restrict__ x, int batch, int64_t hb,
+                                                            uint32_t* ws, float* __restrict__ gout,
+                                                            uint32_t* __restrict__ q, uint8_t* __restrict__ sf) {
+  static_assert(kPer % 2 == 0 && kPer <= kR8MaxPer, "pieces in pairs, within the register budget");
+  __shared__ Reg8Shared sh;
+  __shared__ __attribute__((aligned(16))) u32x4 L[kPer][kR8Data];
+  const int G = gridDim.x;
+  const int lane = (int)threadIdx.x & 63, wave = wave_id();
+  const int64_t chunk_hb = (int64_t)G * kPer * kR8Data;
+  const int nc = (int)((hb + chunk_hb - 1) / chunk_hb);          // >= 4; hb * 16 < 2^31 (the host checks both)
+  const int cbytes = (int)(chunk_hb * 16);
+  const int voff = ((int)blockIdx.x * kPer * kR8Data + (int)threadIdx.x) * 16;
+  const int qoff = voff / 4;
+  // even lanes write the pair's scale byte; odd lanes aim past the extent
+  const int soff = (lane & 1) ? (int)0x80000000u : voff / 32;
+  const uint32_t b0 = (uint32_t)(uintptr_t)&L[0][threadIdx.x];
+  const uint32_t b1 = b0 + kR8StageSplit * kR8StagePiece;
+  lds_void_t* const stage_w =
+      (lds_void_t*)(uintptr_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uintptr_t)&L[0][threadIdx.x & ~63]);
+  const __amdgpu_buffer_rsrc_t none = tensor_rsrc(x, batch, batch, 0);
+  for (int t = 0; t < batch; ++t) {
+    const __amdgpu_buffer_rsrc_t rx = tensor_rsrc(x, t, batch, hb * 16);
+    const __amdgpu_buffer_rsrc_t rq = tensor_rsrc(q, t, batch, hb * 4);
+    const __amdgpu_buffer_rsrc_t rsf = tensor_rsrc(sf, t, batch, hb / 2);
+    u32x4 a[kPer], b[kPer], c[kPer];
+    BlockMax<kPer> am, bmx, cm;
+    // ---- pass 1
+    big_load_set<kPer>(a, rx, voff + (nc - 3) * cbytes);
+    big_load_set<kPer>(b, rx, voff + (nc - 2) * cbytes);
+    big_load_set<kPer>(c, rx, voff + (nc - 1) * cbytes);
+    __builtin_amdgcn_sched_barrier(0);
+    big_stage_issue<kPer>(rx, stage_w, voff);           // chunk 0
+    uint32_t m = 0;
+    for (int k = 0; k + 4 < nc; ++k)                    // chunks 0..nc-5 pass through; chunk nc-4 stays
+      big_stage_chunk<kPer>(std::make_integer_sequence<int, kPer>{}, m, b0, b1, rx, stage_w, voff + (k + 1) * cbytes);
+    wait_vmcnt<0>();                                    // chunk nc-4 and the register sets have landed
+    const uint32_t ms = big_stage_max<kPer>(std::make_integer_sequence<int, kPer>{}, b0, b1);
+    m = m > ms ? m : ms;
+    const uint32_t ma = set_block_max<kPer>(a, am), mb = set_block_max<kPer>(b, bmx), mc = set_block_max<kPer>(c, cm);
+    const uint32_t mw = wave_max_u32(m);
+    uint32_t mall = ma > mb ? ma : mb;
+    mall = mall > mc ? mall : mc;
+    sh.red0[0][wave] = mall > mw ? mall : mw;
+    lds_barrier();                                      // every wave's maximum of tensor t
+    // ---- exchange
+    if (wave == kR8Waves - 1) {
+      if (lane == 0) onchip_publish(ws, t, r8_red_max(sh.red0[0]));
+      r8_table(sh, 0, onchip_wait(ws, t, G), gout + t);
+    }
+    lds_barrier();                                      // the table of tensor t
+    // ---- pass 2
+    const double r6 = sh.r6[0];
+    const double* table = sh.table[0];
+    int s = 0;
+    for (; s + 3 <= nc; s += 3) {
+      big_step<kPer>(s, nc, cbytes, rx, rq, rsf, voff, qoff, soff, a, am, b0, b1, stage_w, r6, table, none);
+      big_step<kPer>(s + 1, nc, cbytes, rx, rq, rsf, voff, qoff, soff, b, bmx, b0, b1, stage_w, r6, table, none);
+      big_step<kPer>(s + 2, nc, cbytes, rx, rq, rsf, voff, qoff, soff, c, cm, b0, b1, stage_w, r6, table, none);
+    }
+    if (s < nc) big_step<kPer>(s, nc, cbytes, rx, rq, rsf, voff, qoff, soff, a, am, b0, b1, stage_w, r6, table, none);
+    if (s + 1 < nc) big_step<kPer>(s + 1, nc, cbytes, rx, rq, rsf, voff, qoff, soff, b, bmx, b0, b1, stage_w, r6, table, none);
+    wait_vmcnt<0>();                                    // no stage load still writing LDS
+    lds_barrier();                                      // the stage and the table are free for the next tensor
+  }
+  if (wave != kR8Waves - 1) return;
+  // the last workgroup out restores the slots and the counter to zero; every
+  // slot store of this workgroup has completed (its wait returned)
   uint32_t last = 0;
   if (lane == 0)
     last = __hip_atomic_fetch_add(&((FusedHeader*)ws)->done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
@@ -1087,6 +1253,20 @@ int onchip_per_thread(int64_t hb_per_tensor) {
   int64_t per = (hb_per_tensor + cap - 1) / cap;
   per += per & 1;                                       // pieces pair up in the block-maximum words
   return per <= kR8MaxPer ? (int)per : 0;
+}
+
+// Chunks of fused_big_kernel for a tensor (one workgroup per CU, kR8MaxPer
+// half blocks per data thread), or 0 when it does not apply: a tensor that
+// fits on chip, one of fewer than four chunks, or one whose byte offsets
+// would not fit the 32-bit buffer offsets.
+int big_chunks(int64_t hb_per_tensor) {
+  if (hb_per_tensor <= 0) return 0;
+  const int64_t cus = nvfp4host::num_cus();
+  if (cus > kR8PollSlots || cus > (int64_t)kTensorWords) return 0;
+  const int64_t chunk = cus * kR8MaxPer * kR8Data;
+  const int64_t nc = (hb_per_tensor + chunk - 1) / chunk;
+  if (nc < 4 || nc * chunk * 16 >= (INT64_C(1) << 31)) return 0;
+  return (int)nc;
 }
 
 // Launches a kernel whose workgroups wait for one another (bounded waits):
@@ -1208,6 +1388,8 @@ nvfp4_status quantize_launch(const uint16_t* x, int64_t batch, int64_t rows, int
       };
       return launch_resident(fns[onchip_per / 2 - 1], G, kR8Data, args, s);
     }
+    if (big_chunks(hb) > 0)
+      return launch_resident((const void*)fused_big_kernel<kR8MaxPer>, (int)nvfp4host::num_cus(), kR8Data, args, s);
     return launch_resident((const void*)fused_quantize_kernel, fused_grid(hb), kThreads, args, s);
   }
   const size_t head = (fused_header_bytes(batch) + 255) & ~(size_t)255;

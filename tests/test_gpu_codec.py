@@ -259,6 +259,49 @@ def test_activations_full_size():
         del q, sf
 
 
+def _chunk_elems():
+    """Elements one FUSED on-chip pass holds for a tensor too large for the
+    chip: one workgroup per CU x 512 threads x 14 half blocks of 8."""
+    return torch.cuda.get_device_properties(0).multi_processor_count * 512 * 14 * 8
+
+
+# (chunks, which chunk holds the planted maximum, batch): every pass-2 tail
+# (nc mod 3), and the maximum in a streamed chunk, the staged chunk nc-4 and
+# each register-held chunk.
+BIG_CASES = [(4, 0, 1), (5, 0, 1), (5, 3, 2), (6, 2, 1), (7, 6, 1), (8, 5, 1)]
+
+
+@pytest.mark.parametrize("nc,hot,batch", BIG_CASES)
+def test_big_tensor_chunks(nc, hot, batch):
+    """Tensors of 4..8 on-chip chunks (the single-launch path for tensors
+    larger than the chip), ragged last chunk, guarded outputs."""
+    cols = 7168
+    elems = (nc - 1) * _chunk_elems() + 3 * cols * 37   # the last chunk partly filled
+    rows = -(-elems // cols)
+    print(f"case: big tensor nc={nc} hot={hot} batch={batch} rows={rows}", flush=True)
+    gen = torch.Generator().manual_seed(1000 + 10 * nc + hot)
+    x = (torch.randn((batch, rows, cols), generator=gen) * 2).to(torch.bfloat16)
+    flat = x.view(batch, -1)
+    pos = min(hot * _chunk_elems() + 12345, rows * cols - 1)
+    flat[0, pos] = 3.0e4
+    if batch > 1:
+        flat[1, 77] = -5.0e5
+    x = x.cuda()
+    qg = Guarded((batch, rows, cols // 2), torch.uint8)
+    sg = Guarded((batch, rows, cols // 16), torch.uint8)
+    gg = Guarded((batch,), torch.float32)
+    nv.quantize(x, flags="fused", out=(qg.view, sg.view, gg.view))
+    torch.cuda.synchronize()
+    for gd in (qg, sg, gg):
+        gd.check()
+    oq, osf, og = oracle.quantize(bits(x))
+    assert np.array_equal(np_(gg.view).view(np.uint32), og.view(np.uint32)), f"g {np_(gg.view)} vs {og}"
+    bad = np.argwhere(np_(sg.view) != osf)
+    assert bad.size == 0, f"scale byte mismatch at {bad[:5].tolist()}"
+    bad = np.argwhere(np_(qg.view) != oq)
+    assert bad.size == 0, f"code mismatch at {bad[:5].tolist()}"
+
+
 def test_fused_workspace_is_left_clean():
     """The persistent launch restores its counters to zero: many back-to-back
     calls on one workspace, with different batch sizes, all give the two-kernel bytes."""
