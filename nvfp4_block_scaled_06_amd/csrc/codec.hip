@@ -1149,6 +1149,12 @@ __global__ void __launch_bounds__(kR8Data) fused_big_kernel(const u32x4* __restr
 }
 
 // ------------------------------------------------------------ dequantize
+// The bf16 output is stored non-temporal: written once and not read back
+// here, its lines then do not sit dirty in L2 and the last-level cache,
+// where the next kernel's reads would have to write them back first.
+// Measured with the fused quantize alternating with this kernel on
+// 64 x 2048 x 7168: dequantize 0.406 -> 0.400 ms, the quantize after it
+// 0.438 -> 0.415 ms.
 __global__ void __launch_bounds__(kThreads) dequant_kernel(const uint32_t* __restrict__ q,
                                                            const uint8_t* __restrict__ sf,
                                                            const float* __restrict__ gin, int64_t hb_per_tensor,
@@ -1170,9 +1176,10 @@ __global__ void __launch_bounds__(kThreads) dequant_kernel(const uint32_t* __res
       s[u] = st[(i + u * step) >> 1];
     }
 #pragma unroll
-    for (int u = 0; u < kU; ++u) yt[i + u * step] = dequant_half(c[u], e4m3_value(s[u]), g);
+    for (int u = 0; u < kU; ++u)
+      __builtin_nontemporal_store(dequant_half(c[u], e4m3_value(s[u]), g), yt + i + u * step);
   }
-  for (; i < hb_per_tensor; i += step) yt[i] = dequant_half(qt[i], e4m3_value(st[i >> 1]), g);
+  for (; i < hb_per_tensor; i += step) __builtin_nontemporal_store(dequant_half(qt[i], e4m3_value(st[i >> 1]), g), yt + i);
 }
 
 // Clears n words of scratch (the exchange header of a workspace whose

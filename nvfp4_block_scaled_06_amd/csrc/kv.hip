@@ -106,7 +106,8 @@ __device__ __forceinline__ u32x4 kv_dequant_half(uint32_t codes, float s, float 
   return o;
 }
 
-// grid (tiles, kv_heads, 2*nlayers); out [nlayers][H][n][D] bf16.
+// grid (tiles, kv_heads, 2*nlayers); out [nlayers][H][n][D] bf16, stored
+// non-temporal (written once, not read back here).
 __global__ void __launch_bounds__(kThreads) kv_read_kernel(nvfp4_kv_cache c, int layer0, int64_t t0, int64_t n,
                                                            u32x4* __restrict__ k_out, u32x4* __restrict__ v_out) {
   const int h = blockIdx.y;
@@ -136,9 +137,10 @@ __global__ void __launch_bounds__(kThreads) kv_read_kernel(nvfp4_kv_cache c, int
       sb[u] = ssf[(i + u * step) >> 1];
     }
 #pragma unroll
-    for (int u = 0; u < kKVReadU; ++u) o[i + u * step] = kv_dequant_half(cw[u], e4m3_value(sb[u]), g);
+    for (int u = 0; u < kKVReadU; ++u)
+      __builtin_nontemporal_store(kv_dequant_half(cw[u], e4m3_value(sb[u]), g), o + i + u * step);
   }
-  for (; i < nh; i += step) o[i] = kv_dequant_half(sq[i], e4m3_value(ssf[i >> 1]), g);
+  for (; i < nh; i += step) __builtin_nontemporal_store(kv_dequant_half(sq[i], e4m3_value(ssf[i >> 1]), g), o + i);
 }
 
 // Decode-step QK: grid (token tiles, kv_heads, layers).  The grp query heads

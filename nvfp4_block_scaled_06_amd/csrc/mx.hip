@@ -99,6 +99,7 @@ __device__ __forceinline__ u32x4 mx_dequant_quarter(uint32_t codes, float sc) {
   return o;
 }
 
+// bf16 output stored non-temporal, as in the NVFP4 dequantize.
 __global__ void __launch_bounds__(kThreads) mx_dequant_kernel(const uint32_t* __restrict__ q,
                                                               const uint8_t* __restrict__ sf, int64_t nq,
                                                               u32x4* __restrict__ y) {
@@ -113,9 +114,10 @@ __global__ void __launch_bounds__(kThreads) mx_dequant_kernel(const uint32_t* __
       s[u] = sf[(i + u * step) >> 2];
     }
 #pragma unroll
-    for (int u = 0; u < kMxU; ++u) y[i + u * step] = mx_dequant_quarter(c[u], e8m0_value(s[u]));
+    for (int u = 0; u < kMxU; ++u)
+      __builtin_nontemporal_store(mx_dequant_quarter(c[u], e8m0_value(s[u])), y + i + u * step);
   }
-  for (; i < nq; i += step) y[i] = mx_dequant_quarter(q[i], e8m0_value(sf[i >> 2]));
+  for (; i < nq; i += step) __builtin_nontemporal_store(mx_dequant_quarter(q[i], e8m0_value(sf[i >> 2])), y + i);
 }
 
 // ------------------------------------------------------------ GEMM
