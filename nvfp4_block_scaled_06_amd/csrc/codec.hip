@@ -796,8 +796,10 @@ __device__ __forceinline__ void r8_piece(u32x4 (&cur)[kPer], BlockMax<kPer>& bm,
                                          uint32_t b1, lds_void_t* stage_w) {
   const uint32_t sbyte = e4m3_rne_sat(rn32((double)bm_value<kPer>(bm, p) * r6));
   const uint32_t code = encode_half(cur[p], table[sbyte]);
-  __builtin_amdgcn_raw_buffer_store_b32(code, rq, qoff, p * kR8Data * 4, 0);
-  __builtin_amdgcn_raw_buffer_store_b8((uint8_t)sbyte, rsf, soff, p * (kR8Data / 2), 0);
+  // codes and scale bytes stream out non-temporal (0.431 -> 0.426 ms on the
+  // experts, alternating with the dequantize)
+  __builtin_amdgcn_raw_buffer_store_b32(code, rq, qoff, p * kR8Data * 4, kStreamLoad);
+  __builtin_amdgcn_raw_buffer_store_b8((uint8_t)sbyte, rsf, soff, p * (kR8Data / 2), kStreamLoad);
   wait_vmcnt<kWait>();                                 // stage piece p (issued a step earlier) has landed
   cur[p] = r8_stage_read<kPer, p>(b0, b1);
   const uint32_t h = pair_max(half_absmax_bits(cur[p]));
