@@ -45,7 +45,7 @@ def parse():
     p.add_argument("--no-extras", action="store_true", help="headline step only")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--rows-only", default="",
-                   help="comma list of extra rows to run (experts,single,acts,kv,gemm,moe,mx,train)")
+                   help="comma list of extra rows to run (experts,single,acts,kv,gemm,moe,mx,train,steady)")
     p.add_argument("--traffic-kernels", action="store_true",
                    help="only launch every benchmarked kernel on its benchmarked shape (3 times each) and a "
                         "1 GiB device copy: the workload of the rocprofv3 --pmc counter runs")
@@ -323,7 +323,42 @@ def run_extras(nv, synth, torch, which):
         rows["training_variants"] = run_train(nv, synth, torch)
     del fbuf
     torch.cuda.empty_cache()
+    if "steady" in which:
+        rows["experts_quantize_dequantize_steady"] = run_steady(nv, synth, torch)
     return rows
+
+
+def run_steady(nv, synth, torch, steps=60, skip=20):
+    """The headline step (fused quantize + dequantize of the 64 experts)
+    repeated 60 times back to back; per-launch event laps over the last 40.
+    A device that has just switched to this alternation runs its first few
+    tens of quantize launches up to 25% slower before settling; this row
+    reports the settled figures (and, run last, precedes the headline)."""
+    E, R, C = 64, 2048, 7168
+    x = synth.experts(E, R, C, device="cuda")
+    q = torch.empty((E, R, C // 2), dtype=torch.uint8, device="cuda")
+    sf = torch.empty((E, R, C // 16), dtype=torch.uint8, device="cuda")
+    g = torch.empty((E,), dtype=torch.float32, device="cuda")
+    y = torch.empty_like(x)
+    ws = nv.make_workspace(E, R, C)
+    timer = EventTimer(torch)
+    timer.mark()
+    for i in range(steps):
+        if i == skip:
+            timer.pairs = {}                   # drop the first laps, keep the boundary event
+        nv.quantize(x, flags="fused", workspace=ws, out=(q, sf, g))
+        timer.lap("quantize")
+        nv.dequantize(q, sf, g, out=y)
+        timer.lap("dequantize")
+    torch.cuda.synchronize()
+    mq, md = timer.mean_ms("quantize"), timer.mean_ms("dequantize")
+    n = E * R * C
+    bq, bd = bytes_quantize(n, E), bytes_dequant(n, E)
+    del x, q, sf, g, y, ws
+    torch.cuda.empty_cache()
+    return {"steps": steps, "timed": steps - skip, "quantize": {"ms": mq, **roof(bq, mq, HBM_PEAK_GBS, "GB/s")},
+            "dequantize": {"ms": md, **roof(bd, md, HBM_PEAK_GBS, "GB/s")},
+            "step": {"ms": mq + md, **roof(bq + bd, mq + md, HBM_PEAK_GBS, "GB/s")}}
 
 
 def calibrate_kv_scales(nv, torch, chunks, L, H):
@@ -627,7 +662,7 @@ def main():
     rows = {}
     if not args.no_extras:
         which = (args.rows_only.split(",") if args.rows_only
-                 else ["experts", "single", "acts", "kv", "gemm", "moe", "mx", "train"])
+                 else ["experts", "single", "acts", "kv", "gemm", "moe", "mx", "train", "steady"])
         rows = run_extras(nv, synth, torch, which)
         log("extras done")
     head = run_headline(nv, synth, torch, args.steps, args.warmup)
