@@ -129,7 +129,15 @@ def bytes_dequant(n_elem, n_tensors):
     return n_elem // 2 + n_elem // 16 + 4 * n_tensors + 2 * n_elem
 
 
-def run_headline(nv, synth, torch, steps, warmup):
+def run_headline(nv, synth, torch, steps, warmup, steady_steps=0, steady_skip=20):
+    """The headline step on the 64 experts.  With steady_steps > 0 the same
+    step first runs that many times as its own row (per-launch laps over
+    all but the first steady_skip), on the same tensors and with no other
+    GPU work between it and the headline's W + K steps: a device that has
+    just come from idle or from other kernels runs this alternation's first
+    ~20-25 quantize launches up to 45% slower before it settles, so the row
+    both reports the settled step and leaves the device settled.
+    Returns (headline, steady row or None)."""
     E, R, C = 64, 2048, 7168
     log(f"headline: experts {E}x{R}x{C}: generating inputs on the GPU")
     x = synth.experts(E, R, C, device="cuda")
@@ -140,6 +148,7 @@ def run_headline(nv, synth, torch, steps, warmup):
     y = torch.empty_like(x)
     ws = nv.make_workspace(E, R, C)
     flags = "fused"               # single persistent launch, each input byte read once; both modes are timed in "rows"
+    bq, bd = bytes_quantize(n, E), bytes_dequant(n, E)
     timer = EventTimer(torch)
 
     def step():
@@ -148,6 +157,21 @@ def run_headline(nv, synth, torch, steps, warmup):
         nv.dequantize(q, sf, g, out=y)
         timer.lap("dequantize")
 
+    steady = None
+    if steady_steps > 0:
+        timer.mark()
+        for i in range(steady_steps):
+            if i == steady_skip:
+                timer.pairs = {}              # drop the first laps, keep the boundary event
+            step()
+        torch.cuda.synchronize()
+        mq, md = timer.mean_ms("quantize"), timer.mean_ms("dequantize")
+        steady = {"steps": steady_steps, "timed": steady_steps - steady_skip,
+                  "quantize": {"ms": mq, **roof(bq, mq, HBM_PEAK_GBS, "GB/s")},
+                  "dequantize": {"ms": md, **roof(bd, md, HBM_PEAK_GBS, "GB/s")},
+                  "step": {"ms": mq + md, **roof(bq + bd, mq + md, HBM_PEAK_GBS, "GB/s")}}
+        log("steady row done:", json.dumps(steady))
+        timer.reset()
     timer.mark()
     for _ in range(warmup):
         step()
@@ -161,7 +185,6 @@ def run_headline(nv, synth, torch, steps, warmup):
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_step = (t1 - t0) * 1e3 / steps
-    bq, bd = bytes_quantize(n, E), bytes_dequant(n, E)
     res = {
         "ms_per_step": ms_step,
         "value_gbs": (bq + bd) / (ms_step * 1e-3) / 1e9,
@@ -173,7 +196,7 @@ def run_headline(nv, synth, torch, steps, warmup):
     }
     del x, q, sf, g, y, ws
     torch.cuda.empty_cache()
-    return res
+    return res, steady
 
 
 def _fused_ok(nv):
@@ -323,42 +346,7 @@ def run_extras(nv, synth, torch, which):
         rows["training_variants"] = run_train(nv, synth, torch)
     del fbuf
     torch.cuda.empty_cache()
-    if "steady" in which:
-        rows["experts_quantize_dequantize_steady"] = run_steady(nv, synth, torch)
     return rows
-
-
-def run_steady(nv, synth, torch, steps=60, skip=20):
-    """The headline step (fused quantize + dequantize of the 64 experts)
-    repeated 60 times back to back; per-launch event laps over the last 40.
-    A device that has just switched to this alternation runs its first few
-    tens of quantize launches up to 25% slower before settling; this row
-    reports the settled figures (and, run last, precedes the headline)."""
-    E, R, C = 64, 2048, 7168
-    x = synth.experts(E, R, C, device="cuda")
-    q = torch.empty((E, R, C // 2), dtype=torch.uint8, device="cuda")
-    sf = torch.empty((E, R, C // 16), dtype=torch.uint8, device="cuda")
-    g = torch.empty((E,), dtype=torch.float32, device="cuda")
-    y = torch.empty_like(x)
-    ws = nv.make_workspace(E, R, C)
-    timer = EventTimer(torch)
-    timer.mark()
-    for i in range(steps):
-        if i == skip:
-            timer.pairs = {}                   # drop the first laps, keep the boundary event
-        nv.quantize(x, flags="fused", workspace=ws, out=(q, sf, g))
-        timer.lap("quantize")
-        nv.dequantize(q, sf, g, out=y)
-        timer.lap("dequantize")
-    torch.cuda.synchronize()
-    mq, md = timer.mean_ms("quantize"), timer.mean_ms("dequantize")
-    n = E * R * C
-    bq, bd = bytes_quantize(n, E), bytes_dequant(n, E)
-    del x, q, sf, g, y, ws
-    torch.cuda.empty_cache()
-    return {"steps": steps, "timed": steps - skip, "quantize": {"ms": mq, **roof(bq, mq, HBM_PEAK_GBS, "GB/s")},
-            "dequantize": {"ms": md, **roof(bd, md, HBM_PEAK_GBS, "GB/s")},
-            "step": {"ms": mq + md, **roof(bq + bd, mq + md, HBM_PEAK_GBS, "GB/s")}}
 
 
 def calibrate_kv_scales(nv, torch, chunks, L, H):
@@ -660,12 +648,15 @@ def main():
     # the settled device.  With --no-extras it runs first.
     cpu = None if args.no_cpu else cpu_baseline(synth, torch)
     rows = {}
+    which = []
     if not args.no_extras:
         which = (args.rows_only.split(",") if args.rows_only
                  else ["experts", "single", "acts", "kv", "gemm", "moe", "mx", "train", "steady"])
         rows = run_extras(nv, synth, torch, which)
         log("extras done")
-    head = run_headline(nv, synth, torch, args.steps, args.warmup)
+    head, steady = run_headline(nv, synth, torch, args.steps, args.warmup, 60 if "steady" in which else 0)
+    if steady is not None:
+        rows["experts_quantize_dequantize_steady"] = steady
     log("headline done:", json.dumps(head))
     dom = "quantize" if head["quantize_ms"] >= head["dequantize_ms"] else "dequantize"
     dom_bytes = head[f"{dom}_bytes"]
