@@ -225,23 +225,30 @@ __device__ __forceinline__ float dot2_first(bf16x2 a, bf16x2 b) {
   return r;
 }
 
+// (old 0 with bound_ctrl lets the compiler fold each move into the add as a
+// DPP operand: one instruction per butterfly step)
 template <int LPT>
 __device__ __forceinline__ float lane_group_sum(float v) {
-  if (LPT >= 2) v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false));
-  if (LPT >= 4) v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false));
+  if (LPT >= 2)
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, true));
+  if (LPT >= 4)
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, true));
   if (LPT >= 8) v += __shfl_xor(v, 4, 64);
   return v;
 }
 
 template <int LPT, int GRP>
 __global__ void __launch_bounds__(kThreads) kv_qk_kernel(nvfp4_kv_cache c, const uint32_t* __restrict__ q,
-                                                         int q_heads, int64_t n, float* __restrict__ logits) {
+                                                         int q_heads, int64_t n64, float* __restrict__ logits) {
   constexpr int TPW = 64 / LPT;                        // tokens per wave
   constexpr int U = kQKGroups;                         // token groups per trip
   const int h = blockIdx.y, l = blockIdx.z;
   const int H = c.kv_heads;
   const int lane = threadIdx.x & 63;
   const int j = lane % LPT;                            // 32-value chunk of the token
+  // token indices and offsets are 32-bit: the host keeps n * head_dim / 2
+  // below 2^27, so n < 2^23 and the GRP * n logits stay below 2^31 bytes
+  const int n = (int)n64;
   // query slices: q[l][h*GRP + g][32 j .. 32 j + 32) as 16 bf16 pairs per head
   uint32_t qv[GRP][16];
 #pragma unroll
@@ -255,30 +262,31 @@ __global__ void __launch_bounds__(kThreads) kv_qk_kernel(nvfp4_kv_cache c, const
   }
   const float gk = c.k_g[l * H + h];
   const int64_t row0 = ((int64_t)l * H + h) * c.capacity;
-  // buffer resources over tokens [0, n) of this (layer, head): loads of
-  // tokens past n read zeros, with no branch (the host keeps n*head_dim/2
-  // below 2^31)
+  // buffer resources over tokens [0, n) of this (layer, head), and over the
+  // GRP logit rows of its query heads: loads past n read zeros, stores
+  // steered past the extent write nothing, with no branch
   const __amdgpu_buffer_rsrc_t kc = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(c.k + row0 * LPT * 16), 0, (int)(n * LPT * 16), kBufferWord3);      // 16 code bytes per lane
+      (void*)(c.k + row0 * LPT * 16), 0, n * LPT * 16, kBufferWord3);          // 16 code bytes per lane
   const __amdgpu_buffer_rsrc_t ks = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(c.k_sf + row0 * LPT * 2), 0, (int)(n * LPT * 2), kBufferWord3);     // 2 scale bytes per lane
-  float* out = logits + ((int64_t)l * q_heads + h * GRP) * n;
-  const int64_t tok_step = (int64_t)gridDim.x * (kThreads / 64) * TPW;
-  const int64_t t_lane = lane / LPT;
+      (void*)(c.k_sf + row0 * LPT * 2), 0, n * LPT * 2, kBufferWord3);         // 2 scale bytes per lane
+  const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(logits + ((int64_t)l * q_heads + h * GRP) * n64), 0, GRP * n * 4, kBufferWord3);
+  const int tok_step = (int)gridDim.x * (kThreads / 64) * TPW;
+  const int t_lane = lane / LPT;
   // U token groups per trip (independent dot chains); two register sets
   // alternate, so the next trip's codes and scales are in flight while this
   // trip is contracted
-  int64_t t = ((int64_t)blockIdx.x * (kThreads / 64) + wave_id()) * TPW + t_lane;
-  auto load = [&](int64_t t0, u32x4 (&cw)[U], uint32_t (&sw)[U]) {
+  int t = ((int)blockIdx.x * (kThreads / 64) + wave_id()) * TPW + t_lane;
+  auto load = [&](int t0, u32x4 (&cw)[U], uint32_t (&sw)[U]) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int64_t tu = t0 + u * tok_step;
+      const int tu = t0 + u * tok_step;
       const uint32_t e = tu < n ? (uint32_t)(tu * LPT + j) : 0x08000000u;     // past the extent: zeros
       cw[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(kc, (int)(e * 16u), 0, kStreamLoad));
       sw[u] = __builtin_amdgcn_raw_buffer_load_b16(ks, (int)(e * 2u), 0, kStreamLoad);
     }
   };
-  auto contract = [&](int64_t t0, const u32x4 (&cw)[U], const uint32_t (&sw)[U]) {
+  auto contract = [&](int t0, const u32x4 (&cw)[U], const uint32_t (&sw)[U]) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       // scales from their E4M3 bytes (exact hardware decode)
@@ -288,7 +296,7 @@ __global__ void __launch_bounds__(kThreads) kv_qk_kernel(nvfp4_kv_cache c, const
       kp[4] = kpair<0>(cw[u].y); kp[5] = kpair<1>(cw[u].y); kp[6] = kpair<2>(cw[u].y); kp[7] = kpair<3>(cw[u].y);
       kp[8] = kpair<0>(cw[u].z); kp[9] = kpair<1>(cw[u].z); kp[10] = kpair<2>(cw[u].z); kp[11] = kpair<3>(cw[u].z);
       kp[12] = kpair<0>(cw[u].w); kp[13] = kpair<1>(cw[u].w); kp[14] = kpair<2>(cw[u].w); kp[15] = kpair<3>(cw[u].w);
-      const int64_t tu = t0 + u * tok_step;
+      const int tu = t0 + u * tok_step;
       float tot[GRP];
 #pragma unroll
       for (int g = 0; g < GRP; ++g) {
@@ -302,7 +310,9 @@ __global__ void __launch_bounds__(kThreads) kv_qk_kernel(nvfp4_kv_cache c, const
         tot[g] = lane_group_sum<LPT>(__builtin_fmaf(p1, s1, p0 * s0));
       }
       // every lane of the token holds every head's total; lane j stores heads
-      // j, j + LPT, ... (one unmasked store per head it owns)
+      // j, j + LPT, ... (one store per head it owns).  A wave's store covers
+      // 64-byte runs of several heads' rows, which L2 merges into whole lines:
+      // non-temporal stores here ran 0.625 against 0.537 ms
       constexpr int kSPL = GRP >= LPT ? GRP / LPT : 1;
 #pragma unroll
       for (int sidx = 0; sidx < kSPL; ++sidx) {
@@ -310,13 +320,14 @@ __global__ void __launch_bounds__(kThreads) kv_qk_kernel(nvfp4_kv_cache c, const
         float v = tot[0];
 #pragma unroll
         for (int gg = 1; gg < GRP; ++gg) v = g == gg ? tot[gg] : v;
-        if (tu < n && g < GRP) out[(int64_t)g * n + tu] = v * gk;
+        const uint32_t off = (tu < n && g < GRP) ? (uint32_t)((g * n + tu) * 4) : 0x80000000u;
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v * gk), ro, (int)off, 0, 0);
       }
     }
   };
   u32x4 cwa[U], cwb[U];
   uint32_t swa[U], swb[U];
-  const int64_t trip = U * tok_step;
+  const int trip = U * tok_step;
   load(t, cwa, swa);
   while (t - t_lane < n) {
     load(t + trip, cwb, swb);
