@@ -985,6 +985,177 @@ __global__ void __launch_bounds__(kR8Data) fused_reg8_kernel(const u32x4* __rest
   }
 }
 
+// ------------------------------------------------------------ fused 2D scales, four tensors on chip
+// The 16 x 16 tile-scale quantize (2D weights) on the same pipeline as
+// fused_reg8_kernel: three register sets, one LDS stage, eight waves, the
+// exchange in wave 7 a step ahead.  Data thread i of workgroup w owns strip
+// s = 512 w + i: the 8 columns [8 c, 8 c + 8) of the 16 rows [16 r, 16 r +
+// 16), (r, c) = (s / spr, s % spr), spr = cols / 8; piece p is row 16 r + p,
+// so consecutive threads read consecutive 16-byte runs of a row.  Strips 2k
+// and 2k+1 (a lane pair) form one tile: its amax is the pair's maximum over
+// all 16 pieces, taken when the tensor enters registers, and one scale byte
+// and one reciprocal serve every piece of the step.  Codes and scale bytes
+// go out row-major like the input (every row of the tile carries the
+// tile's byte).  The memory operations of a step, and so the waits, are
+// those of the 1D kernel.
+constexpr int kR2Per = 16;                             // rows of a strip
+
+template <int p, int kWait>
+__device__ __forceinline__ void r2_piece(u32x4 (&cur)[kR2Per], uint32_t& m, double rd, uint32_t sbyte,
+                                         __amdgpu_buffer_rsrc_t rq, __amdgpu_buffer_rsrc_t rsf,
+                                         __amdgpu_buffer_rsrc_t rx, int qoff, int soff, int voff, int qstride,
+                                         int sstride, int pstride, uint32_t b0, uint32_t b1, lds_void_t* stage_w) {
+  const uint32_t code = encode_half(cur[p], rd);
+  __builtin_amdgcn_raw_buffer_store_b32(code, rq, qoff, p * qstride, kStreamLoad);
+  __builtin_amdgcn_raw_buffer_store_b8((uint8_t)sbyte, rsf, soff, p * sstride, kStreamLoad);
+  wait_vmcnt<kWait>();                                 // stage piece p (issued a step earlier) has landed
+  cur[p] = r8_stage_read<kR2Per, p>(b0, b1);
+  const uint32_t h = half_absmax_bits(cur[p]);
+  m = m > h ? m : h;
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void_t*)((__attribute__((address_space(3))) char*)stage_w +
+                                                             p * kR8StagePiece),
+                                           16, voff, p * pstride, 0, kStreamLoad);
+  __builtin_amdgcn_sched_barrier(0);                   // keep each piece's operations in this order
+}
+
+template <int kWait, int... P>
+__device__ __forceinline__ void r2_pieces(std::integer_sequence<int, P...>, u32x4 (&cur)[kR2Per], uint32_t& m,
+                                          double rd, uint32_t sbyte, __amdgpu_buffer_rsrc_t rq,
+                                          __amdgpu_buffer_rsrc_t rsf, __amdgpu_buffer_rsrc_t rx, int qoff, int soff,
+                                          int voff, int qstride, int sstride, int pstride, uint32_t b0, uint32_t b1,
+                                          lds_void_t* stage_w) {
+  (r2_piece<P, kWait>(cur, m, rd, sbyte, rq, rsf, rx, qoff, soff, voff, qstride, sstride, pstride, b0, b1, stage_w),
+   ...);
+}
+
+// Tile maximum of a register set (the pair's maximum over its pieces);
+// returns the wave maximum.
+__device__ __forceinline__ uint32_t set_tile_max(const u32x4 (&R)[kR2Per], uint32_t& tile) {
+  uint32_t m = 0;
+#pragma unroll
+  for (int p = 0; p < kR2Per; ++p) {
+    const uint32_t h = half_absmax_bits(R[p]);
+    m = m > h ? m : h;
+  }
+  tile = pair_max(m);
+  return wave_max_u32(m);
+}
+
+__device__ __forceinline__ void r2_step(const u32x4* __restrict__ x, int t, int batch, int64_t hb, int voff, int qoff,
+                                        int soff, int qstride, int sstride, int pstride, u32x4 (&cur)[kR2Per],
+                                        uint32_t& tile, uint32_t b0, uint32_t b1, lds_void_t* stage_w, uint32_t* ws,
+                                        int G, float* __restrict__ gout, uint32_t* __restrict__ q,
+                                        uint8_t* __restrict__ sf, Reg8Shared& sh) {
+  lds_barrier();                                       // t's table is ready; the maxima of t+2 were reduced
+  const bool pub = t >= 1 && t + 2 < batch;
+  r8_exchange_ops(ws, G, pub ? t + 2 : -1, pub ? r8_red_max(sh.red[(t - 1) & 1]) : 0u, t + 1, t + 1 < batch, sh);
+  const double r6 = sh.r6[t & 1];
+  const uint32_t sbyte = block_scale_byte(tile, r6);
+  const double rd = sh.table[t & 1][sbyte];
+  const __amdgpu_buffer_rsrc_t rq = tensor_rsrc(q, t, batch, hb * 4);
+  const __amdgpu_buffer_rsrc_t rsf = tensor_rsrc(sf, t, batch, hb / 2);
+  const __amdgpu_buffer_rsrc_t rx = tensor_rsrc(x, t + 4, batch, hb * 16);   // extent zero past the batch
+  uint32_t m = 0;
+  r2_pieces<3 * kR2Per + 2>(std::make_integer_sequence<int, kR2Per>{}, cur, m, rd, sbyte, rq, rsf, rx, qoff, soff, voff,
+                            qstride, sstride, pstride, b0, b1, stage_w);
+  tile = pair_max(m);                                  // tensor t+3, now in this set
+  sh.red[t & 1][wave_id()] = wave_max_u32(m);          // wave-uniform value and address
+  wait_vmcnt<3 * kR2Per>();                            // the poll loads of this step have landed
+  if (wave_id() == kR8Waves - 1 && t + 1 < batch) r8_table(sh, t + 1, r8_gather(ws, t + 1, G, sh), gout);
+}
+
+__global__ void __launch_bounds__(kR8Data) fused_2d_reg_kernel(const u32x4* __restrict__ x, int batch, int64_t hb,
+                                                               int spr, int srows, uint32_t* ws,
+                                                               float* __restrict__ gout, uint32_t* __restrict__ q,
+                                                               uint8_t* __restrict__ sf) {
+  __shared__ Reg8Shared sh;
+  __shared__ __attribute__((aligned(16))) u32x4 L[kR2Per][kR8Data];
+  const int G = gridDim.x;
+  const int lane = (int)threadIdx.x & 63, wave = wave_id();
+  // strip of this thread; strips past the tensor get offsets past every
+  // extent (their loads read zeros, their stores are dropped)
+  const int st = (int)blockIdx.x * kR8Data + (int)threadIdx.x;
+  const int r = st / spr, c = st - r * spr;
+  const bool in = r < srows;
+  const int pstride = spr * 16, qstride = spr * 4, sstride = spr / 2;
+  const int voff = in ? (r * 16 * spr + c) * 16 : kOnOutside;
+  const int qoff = in ? (r * 16 * spr + c) * 4 : kOnOutside;
+  // even lanes write the pair's scale byte; odd lanes aim past the extent
+  const int soff = (in && !(lane & 1)) ? (r * 16 * spr + c) / 2 : (int)0x80000000u;
+  u32x4 a[kR2Per], b[kR2Per], cc[kR2Per];
+  uint32_t ta, tb, tc;
+  {
+    const __amdgpu_buffer_rsrc_t r0 = tensor_rsrc(x, 0, batch, hb * 16), r1 = tensor_rsrc(x, 1, batch, hb * 16),
+                                 r2 = tensor_rsrc(x, 2, batch, hb * 16);
+#pragma unroll
+    for (int p = 0; p < kR2Per; ++p)
+      a[p] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r0, voff, p * pstride, kStreamLoad));
+#pragma unroll
+    for (int p = 0; p < kR2Per; ++p)
+      b[p] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r1, voff, p * pstride, kStreamLoad));
+#pragma unroll
+    for (int p = 0; p < kR2Per; ++p)
+      cc[p] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r2, voff, p * pstride, kStreamLoad));
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  const uint32_t b0 = (uint32_t)(uintptr_t)&L[0][threadIdx.x];
+  const uint32_t b1 = b0 + kR8StageSplit * kR8StagePiece;
+  lds_void_t* const stage_w =
+      (lds_void_t*)(uintptr_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uintptr_t)&L[0][threadIdx.x & ~63]);
+  {
+    // tensor 3 into the stage, each piece after two stores aimed at
+    // zero-extent resources: the memory operations of a step, in order
+    const __amdgpu_buffer_rsrc_t nq = tensor_rsrc(q, batch, batch, 0), ns = tensor_rsrc(sf, batch, batch, 0);
+    const __amdgpu_buffer_rsrc_t rx = tensor_rsrc(x, 3, batch, hb * 16);
+#pragma unroll
+    for (int p = 0; p < kR2Per; ++p) {
+      __builtin_amdgcn_raw_buffer_store_b32(0u, nq, qoff, p * qstride, 0);
+      __builtin_amdgcn_raw_buffer_store_b8((uint8_t)0, ns, soff, p * sstride, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rx, (lds_void_t*)((__attribute__((address_space(3))) char*)stage_w + p * kR8StagePiece), 16, voff,
+          p * pstride, 0, kStreamLoad);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  sh.red0[0][wave] = set_tile_max(a, ta);
+  sh.red0[1][wave] = set_tile_max(b, tb);
+  sh.red0[2][wave] = set_tile_max(cc, tc);
+  lds_barrier();                                       // maxima of tensors 0..2
+  if (wave == kR8Waves - 1) {
+    if (lane == 0)
+      for (int k = 0; k < 3 && k < batch; ++k) onchip_publish(ws, k, r8_red_max(sh.red0[k]));
+    r8_table(sh, 0, onchip_wait(ws, 0, G), gout);
+  }
+  int t = 0;
+  for (; t + 3 <= batch; t += 3) {
+    r2_step(x, t, batch, hb, voff, qoff, soff, qstride, sstride, pstride, a, ta, b0, b1, stage_w, ws, G, gout, q, sf, sh);
+    r2_step(x, t + 1, batch, hb, voff, qoff, soff, qstride, sstride, pstride, b, tb, b0, b1, stage_w, ws, G, gout, q, sf,
+            sh);
+    r2_step(x, t + 2, batch, hb, voff, qoff, soff, qstride, sstride, pstride, cc, tc, b0, b1, stage_w, ws, G, gout, q,
+            sf, sh);
+  }
+  if (t < batch)
+    r2_step(x, t, batch, hb, voff, qoff, soff, qstride, sstride, pstride, a, ta, b0, b1, stage_w, ws, G, gout, q, sf, sh);
+  if (t + 1 < batch)
+    r2_step(x, t + 1, batch, hb, voff, qoff, soff, qstride, sstride, pstride, b, tb, b0, b1, stage_w, ws, G, gout, q, sf,
+            sh);
+  wait_vmcnt<0>();                                     // no stage or poll load still writing LDS at exit
+  if (wave != kR8Waves - 1) return;
+  // the last workgroup out restores the slots and the counter to zero; every
+  // slot store of this workgroup has completed (the wait above)
+  uint32_t last = 0;
+  if (lane == 0)
+    last = __hip_atomic_fetch_add(&((FusedHeader*)ws)->done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+           (uint32_t)G - 1;
+  if (__builtin_amdgcn_readfirstlane((int)last)) {
+    const size_t words = (size_t)batch * kTensorWords;
+    uint32_t* base = ws + kFusedHeaderBytes / 4;
+    for (size_t i = lane; i < words; i += 64)
+      __hip_atomic_store(base + i, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (lane == 0) __hip_atomic_store(&((FusedHeader*)ws)->done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
 // ------------------------------------------------------------ fused, tensors larger than the chip
 // One launch for tensors of nc >= 4 chunks, a chunk being what the on-chip
 // kernel holds (D = 512 threads x kPer half blocks per workgroup, one
@@ -1317,9 +1488,12 @@ nvfp4_status quantize_2d_onchip(const uint16_t* x, int64_t batch, int64_t rows, 
   const int64_t cus = num_cus();
   if (cus > (int64_t)kTensorWords) return NVFP4_ENOTSUP;   // one exchange slot per workgroup
   const int64_t srows = rows / 16, spr = cols / 8;
+  // row-wise: one 16-row strip per thread of fused_2d_reg_kernel (512 per
+  // workgroup); COLWISE: fused_onchip_kernel's blocks of 8 x 8 strips
   const int64_t G = colwise ? (((srows + 7) / 8) * ((spr + 7) / 8) + kOnchipDataWaves - 1) / kOnchipDataWaves
-                            : (srows * spr + kOnchipData - 1) / kOnchipData;
-  if (G > cus) return NVFP4_ENOTSUP;
+                            : (srows * spr + kR8Data - 1) / kR8Data;
+  if (G > cus || (!colwise && G > kR8PollSlots)) return NVFP4_ENOTSUP;
+  if (rows * cols * 2 >= (INT64_C(1) << 31)) return NVFP4_ENOTSUP;   // 32-bit buffer offsets
   const int64_t words = (int64_t)(quantize_2d_onchip_ws_bytes(batch) / 4);
   zero_words_kernel<<<(unsigned)std::min<int64_t>((words + kThreads - 1) / kThreads, 1024), kThreads, 0, s>>>(
       (uint32_t*)ws, words);
@@ -1331,8 +1505,8 @@ nvfp4_status quantize_2d_onchip(const uint16_t* x, int64_t batch, int64_t rows, 
   uint32_t* wsa = (uint32_t*)ws;
   uint32_t* qa = (uint32_t*)q;
   void* args[] = {&xa, &bt, (void*)&hb, &spri, &srowsi, &wsa, &g, &qa, &sf};
-  const void* fn = colwise ? (const void*)fused_onchip_kernel<16, kOn2DT> : (const void*)fused_onchip_kernel<16, kOn2D>;
-  return launch_resident(fn, (int)G, kOnchipThreads, args, s);
+  if (!colwise) return launch_resident((const void*)fused_2d_reg_kernel, (int)G, kR8Data, args, s);
+  return launch_resident((const void*)fused_onchip_kernel<16, kOn2DT>, (int)G, kOnchipThreads, args, s);
 }
 
 }  // namespace nvfp4host

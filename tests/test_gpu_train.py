@@ -92,6 +92,21 @@ def test_2d_too_large_for_one_launch(variant):
     _check(_x((4096, 7168), 41 + variant), variant)
 
 
+@pytest.mark.parametrize("variant", [2, 3])
+def test_2d_experts_full_size(variant):
+    """2D scales on the 64 x [2048 x 7168] expert weights (the single-launch
+    path at its full size), row-major and transposed outputs, every byte
+    against the oracle."""
+    print("case: 2D experts 64x2048x7168, variant", variant, flush=True)
+    x = synth.experts(device="cuda")
+    q, sf, g = nv.quantize_ex(x, variant)
+    torch.cuda.synchronize()
+    wq, wsf, wg = oracle.quantize_ex(bits(x), variant, signs=0, seed=0, offset=0)
+    assert np.array_equal(np_(g).reshape(-1).view(np.uint32), np.asarray(wg, dtype=np.float32).reshape(-1).view(np.uint32))
+    assert np.array_equal(np_(sf).reshape(wsf.shape), wsf)
+    assert np.array_equal(np_(q).reshape(wq.shape), wq)
+
+
 def test_variant_zero_equals_plain_quantize():
     x = _x((2, 128, 256), 6, wide=True)
     q, sf, g = nv.quantize_ex(x, 0)
@@ -112,7 +127,7 @@ def test_sr_seed_and_offset_change_the_draws():
 
 def test_outputs_stay_in_bounds():
     x = _x((48, 80), 8)
-    for variant in (1, 13):
+    for variant in (1, 2, 3, 13):
         R, C = (80, 48) if variant & 1 else (48, 80)
         q = Guarded((R, C // 2), torch.uint8)
         sf = Guarded((R, C // 16), torch.uint8)
