@@ -1064,6 +1064,86 @@ __device__ __forceinline__ void r2_step(const u32x4* __restrict__ x, int t, int 
   if (wave_id() == kR8Waves - 1 && t + 1 < batch) r8_table(sh, t + 1, r8_gather(ws, t + 1, G, sh), gout);
 }
 
+// The COLWISE step (outputs transposed: q [cols][rows/2], sf [cols][rows/16]):
+// a column's 16 rows come from all 16 pieces, so the step first encodes the
+// strip's 8 columns (two half blocks each, gathered with byte permutes; 8
+// code bytes and the tile's byte per column, the 8 lanes of a strip column
+// writing 64 contiguous bytes of an output row), then moves the stage into
+// the set piece by piece and reloads it.  The stage load of piece p then has
+// 3 + 8 * 2 + 15 = 34 younger operations when it is moved, and the poll
+// loads 32 at the end of the step.
+template <int p, int kWait>
+__device__ __forceinline__ void r2t_move(u32x4 (&cur)[kR2Per], uint32_t& m, __amdgpu_buffer_rsrc_t rx, int voff,
+                                         int pstride, uint32_t b0, uint32_t b1, lds_void_t* stage_w) {
+  wait_vmcnt<kWait>();
+  cur[p] = r8_stage_read<kR2Per, p>(b0, b1);
+  const uint32_t h = half_absmax_bits(cur[p]);
+  m = m > h ? m : h;
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void_t*)((__attribute__((address_space(3))) char*)stage_w +
+                                                             p * kR8StagePiece),
+                                           16, voff, p * pstride, 0, kStreamLoad);
+  __builtin_amdgcn_sched_barrier(0);
+}
+template <int kWait, int... P>
+__device__ __forceinline__ void r2t_moves(std::integer_sequence<int, P...>, u32x4 (&cur)[kR2Per], uint32_t& m,
+                                          __amdgpu_buffer_rsrc_t rx, int voff, int pstride, uint32_t b0, uint32_t b1,
+                                          lds_void_t* stage_w) {
+  (r2t_move<P, kWait>(cur, m, rx, voff, pstride, b0, b1, stage_w), ...);
+}
+
+template <int j>
+__device__ __forceinline__ uint32_t r2t_word(const u32x4& v) {
+  return j == 0 ? v.x : j == 1 ? v.y : j == 2 ? v.z : v.w;
+}
+
+template <int j>
+__device__ __forceinline__ void r2t_column(const u32x4 (&cur)[kR2Per], double rd, uint32_t sbyte,
+                                           __amdgpu_buffer_rsrc_t rq, __amdgpu_buffer_rsrc_t rsf, int qoff, int soff,
+                                           int qstride, int sstride) {
+  // column j: element j of every row, row p into element p of the pair of
+  // half blocks
+  constexpr uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
+  uint32_t col[8];
+#pragma unroll
+  for (int p = 0; p < kR2Per; p += 2)
+    col[p / 2] = __builtin_amdgcn_perm(r2t_word<j / 2>(cur[p + 1]), r2t_word<j / 2>(cur[p]), sel);
+  const uint32_t c0 = encode_half(u32x4{col[0], col[1], col[2], col[3]}, rd);
+  const uint32_t c1 = encode_half(u32x4{col[4], col[5], col[6], col[7]}, rd);
+  __builtin_amdgcn_raw_buffer_store_b64(u32x2{c0, c1}, rq, qoff, j * qstride, 0);
+  __builtin_amdgcn_raw_buffer_store_b8((uint8_t)sbyte, rsf, soff, j * sstride, 0);
+  __builtin_amdgcn_sched_barrier(0);                   // one column's temporaries at a time
+}
+template <int... J>
+__device__ __forceinline__ void r2t_columns(std::integer_sequence<int, J...>, const u32x4 (&cur)[kR2Per], double rd,
+                                            uint32_t sbyte, __amdgpu_buffer_rsrc_t rq, __amdgpu_buffer_rsrc_t rsf,
+                                            int qoff, int soff, int qstride, int sstride) {
+  (r2t_column<J>(cur, rd, sbyte, rq, rsf, qoff, soff, qstride, sstride), ...);
+}
+
+__device__ __forceinline__ void r2t_step(const u32x4* __restrict__ x, int t, int batch, int64_t hb, int voff, int qoff,
+                                         int soff, int qstride, int sstride, int pstride, u32x4 (&cur)[kR2Per],
+                                         uint32_t& tile, uint32_t b0, uint32_t b1, lds_void_t* stage_w, uint32_t* ws,
+                                         int G, float* __restrict__ gout, uint32_t* __restrict__ q,
+                                         uint8_t* __restrict__ sf, Reg8Shared& sh) {
+  lds_barrier();                                       // t's table is ready; the maxima of t+2 were reduced
+  const bool pub = t >= 1 && t + 2 < batch;
+  r8_exchange_ops(ws, G, pub ? t + 2 : -1, pub ? r8_red_max(sh.red[(t - 1) & 1]) : 0u, t + 1, t + 1 < batch, sh);
+  const double r6 = sh.r6[t & 1];
+  const uint32_t sbyte = block_scale_byte(tile, r6);
+  const double rd = sh.table[t & 1][sbyte];
+  const __amdgpu_buffer_rsrc_t rq = tensor_rsrc(q, t, batch, hb * 4);
+  const __amdgpu_buffer_rsrc_t rsf = tensor_rsrc(sf, t, batch, hb / 2);
+  const __amdgpu_buffer_rsrc_t rx = tensor_rsrc(x, t + 4, batch, hb * 16);   // extent zero past the batch
+  r2t_columns(std::make_integer_sequence<int, 8>{}, cur, rd, sbyte, rq, rsf, qoff, soff, qstride, sstride);
+  uint32_t m = 0;
+  r2t_moves<kR2Per + 18>(std::make_integer_sequence<int, kR2Per>{}, cur, m, rx, voff, pstride, b0, b1, stage_w);
+  tile = pair_max(m);                                  // tensor t+3, now in this set
+  sh.red[t & 1][wave_id()] = wave_max_u32(m);          // wave-uniform value and address
+  wait_vmcnt<2 * kR2Per>();                            // the poll loads of this step have landed
+  if (wave_id() == kR8Waves - 1 && t + 1 < batch) r8_table(sh, t + 1, r8_gather(ws, t + 1, G, sh), gout);
+}
+
+template <bool kT>
 __global__ void __launch_bounds__(kR8Data) fused_2d_reg_kernel(const u32x4* __restrict__ x, int batch, int64_t hb,
                                                                int spr, int srows, uint32_t* ws,
                                                                float* __restrict__ gout, uint32_t* __restrict__ q,
@@ -1073,15 +1153,35 @@ __global__ void __launch_bounds__(kR8Data) fused_2d_reg_kernel(const u32x4* __re
   const int G = gridDim.x;
   const int lane = (int)threadIdx.x & 63, wave = wave_id();
   // strip of this thread; strips past the tensor get offsets past every
-  // extent (their loads read zeros, their stores are dropped)
-  const int st = (int)blockIdx.x * kR8Data + (int)threadIdx.x;
-  const int r = st / spr, c = st - r * spr;
-  const bool in = r < srows;
-  const int pstride = spr * 16, qstride = spr * 4, sstride = spr / 2;
-  const int voff = in ? (r * 16 * spr + c) * 16 : kOnOutside;
-  const int qoff = in ? (r * 16 * spr + c) * 4 : kOnOutside;
-  // even lanes write the pair's scale byte; odd lanes aim past the extent
-  const int soff = (in && !(lane & 1)) ? (r * 16 * spr + c) / 2 : (int)0x80000000u;
+  // extent (their loads read zeros, their stores are dropped).  Row-major:
+  // strip 512 w + i.  COLWISE: wave v of workgroup w takes the block b =
+  // 8 w + v of 8 x 8 strips (128 rows x 64 columns; blocks run down the
+  // columns), lane l the strip (8 bR + l / 8, 8 bC + l % 8).
+  const int pstride = spr * 16;
+  int voff, qoff, soff, qstride, sstride;
+  if (kT) {
+    const int nbr = (srows + 7) / 8, nbc = (spr + 7) / 8;
+    const int blk = (int)blockIdx.x * kR8Waves + wave;
+    const int br = blk % nbr, bc = blk / nbr;
+    const int r = 8 * br + (lane >> 3), c = 8 * bc + (lane & 7);
+    const bool in = bc < nbc && r < srows && c < spr;
+    const int rows = 16 * srows;
+    voff = in ? (r * 16 * spr + c) * 16 : kOnOutside;
+    qoff = in ? 8 * c * (rows / 2) + 8 * r : kOnOutside;
+    qstride = rows / 2;
+    soff = in ? 8 * c * (rows / 16) + r : kOnOutside;
+    sstride = rows / 16;
+  } else {
+    const int st = (int)blockIdx.x * kR8Data + (int)threadIdx.x;
+    const int r = st / spr, c = st - r * spr;
+    const bool in = r < srows;
+    voff = in ? (r * 16 * spr + c) * 16 : kOnOutside;
+    qoff = in ? (r * 16 * spr + c) * 4 : kOnOutside;
+    qstride = spr * 4;
+    // even lanes write the pair's scale byte; odd lanes aim past the extent
+    soff = (in && !(lane & 1)) ? (r * 16 * spr + c) / 2 : (int)0x80000000u;
+    sstride = spr / 2;
+  }
   u32x4 a[kR2Per], b[kR2Per], cc[kR2Per];
   uint32_t ta, tb, tc;
   {
@@ -1103,20 +1203,32 @@ __global__ void __launch_bounds__(kR8Data) fused_2d_reg_kernel(const u32x4* __re
   lds_void_t* const stage_w =
       (lds_void_t*)(uintptr_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uintptr_t)&L[0][threadIdx.x & ~63]);
   {
-    // tensor 3 into the stage, each piece after two stores aimed at
-    // zero-extent resources: the memory operations of a step, in order
+    // tensor 3 into the stage.  Row-major: each piece after two stores aimed
+    // at zero-extent resources, the memory operations of a step in order;
+    // COLWISE steps issue their stores before their loads, so the loads
+    // alone give the step's counts
     const __amdgpu_buffer_rsrc_t nq = tensor_rsrc(q, batch, batch, 0), ns = tensor_rsrc(sf, batch, batch, 0);
     const __amdgpu_buffer_rsrc_t rx = tensor_rsrc(x, 3, batch, hb * 16);
 #pragma unroll
     for (int p = 0; p < kR2Per; ++p) {
-      __builtin_amdgcn_raw_buffer_store_b32(0u, nq, qoff, p * qstride, 0);
-      __builtin_amdgcn_raw_buffer_store_b8((uint8_t)0, ns, soff, p * sstride, 0);
+      if (!kT) {
+        __builtin_amdgcn_raw_buffer_store_b32(0u, nq, qoff, p * qstride, 0);
+        __builtin_amdgcn_raw_buffer_store_b8((uint8_t)0, ns, soff, p * sstride, 0);
+      }
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           rx, (lds_void_t*)((__attribute__((address_space(3))) char*)stage_w + p * kR8StagePiece), 16, voff,
           p * pstride, 0, kStreamLoad);
     }
     __builtin_amdgcn_sched_barrier(0);
   }
+  auto step = [&](int tt, u32x4 (&cur)[kR2Per], uint32_t& tile) {
+    if (kT)
+      r2t_step(x, tt, batch, hb, voff, qoff, soff, qstride, sstride, pstride, cur, tile, b0, b1, stage_w, ws, G, gout,
+               q, sf, sh);
+    else
+      r2_step(x, tt, batch, hb, voff, qoff, soff, qstride, sstride, pstride, cur, tile, b0, b1, stage_w, ws, G, gout, q,
+              sf, sh);
+  };
   sh.red0[0][wave] = set_tile_max(a, ta);
   sh.red0[1][wave] = set_tile_max(b, tb);
   sh.red0[2][wave] = set_tile_max(cc, tc);
@@ -1128,17 +1240,12 @@ __global__ void __launch_bounds__(kR8Data) fused_2d_reg_kernel(const u32x4* __re
   }
   int t = 0;
   for (; t + 3 <= batch; t += 3) {
-    r2_step(x, t, batch, hb, voff, qoff, soff, qstride, sstride, pstride, a, ta, b0, b1, stage_w, ws, G, gout, q, sf, sh);
-    r2_step(x, t + 1, batch, hb, voff, qoff, soff, qstride, sstride, pstride, b, tb, b0, b1, stage_w, ws, G, gout, q, sf,
-            sh);
-    r2_step(x, t + 2, batch, hb, voff, qoff, soff, qstride, sstride, pstride, cc, tc, b0, b1, stage_w, ws, G, gout, q,
-            sf, sh);
+    step(t, a, ta);
+    step(t + 1, b, tb);
+    step(t + 2, cc, tc);
   }
-  if (t < batch)
-    r2_step(x, t, batch, hb, voff, qoff, soff, qstride, sstride, pstride, a, ta, b0, b1, stage_w, ws, G, gout, q, sf, sh);
-  if (t + 1 < batch)
-    r2_step(x, t + 1, batch, hb, voff, qoff, soff, qstride, sstride, pstride, b, tb, b0, b1, stage_w, ws, G, gout, q, sf,
-            sh);
+  if (t < batch) step(t, a, ta);
+  if (t + 1 < batch) step(t + 1, b, tb);
   wait_vmcnt<0>();                                     // no stage or poll load still writing LDS at exit
   if (wave != kR8Waves - 1) return;
   // the last workgroup out restores the slots and the counter to zero; every
@@ -1488,11 +1595,11 @@ nvfp4_status quantize_2d_onchip(const uint16_t* x, int64_t batch, int64_t rows, 
   const int64_t cus = num_cus();
   if (cus > (int64_t)kTensorWords) return NVFP4_ENOTSUP;   // one exchange slot per workgroup
   const int64_t srows = rows / 16, spr = cols / 8;
-  // row-wise: one 16-row strip per thread of fused_2d_reg_kernel (512 per
-  // workgroup); COLWISE: fused_onchip_kernel's blocks of 8 x 8 strips
-  const int64_t G = colwise ? (((srows + 7) / 8) * ((spr + 7) / 8) + kOnchipDataWaves - 1) / kOnchipDataWaves
+  // one 16-row strip per thread of fused_2d_reg_kernel (512 per workgroup;
+  // COLWISE: in blocks of 8 x 8 strips, one per wave)
+  const int64_t G = colwise ? (((srows + 7) / 8) * ((spr + 7) / 8) + kR8Waves - 1) / kR8Waves
                             : (srows * spr + kR8Data - 1) / kR8Data;
-  if (G > cus || (!colwise && G > kR8PollSlots)) return NVFP4_ENOTSUP;
+  if (G > cus || G > kR8PollSlots) return NVFP4_ENOTSUP;
   if (rows * cols * 2 >= (INT64_C(1) << 31)) return NVFP4_ENOTSUP;   // 32-bit buffer offsets
   const int64_t words = (int64_t)(quantize_2d_onchip_ws_bytes(batch) / 4);
   zero_words_kernel<<<(unsigned)std::min<int64_t>((words + kThreads - 1) / kThreads, 1024), kThreads, 0, s>>>(
@@ -1505,8 +1612,8 @@ nvfp4_status quantize_2d_onchip(const uint16_t* x, int64_t batch, int64_t rows, 
   uint32_t* wsa = (uint32_t*)ws;
   uint32_t* qa = (uint32_t*)q;
   void* args[] = {&xa, &bt, (void*)&hb, &spri, &srowsi, &wsa, &g, &qa, &sf};
-  if (!colwise) return launch_resident((const void*)fused_2d_reg_kernel, (int)G, kR8Data, args, s);
-  return launch_resident((const void*)fused_onchip_kernel<16, kOn2DT>, (int)G, kOnchipThreads, args, s);
+  const void* fn = colwise ? (const void*)fused_2d_reg_kernel<true> : (const void*)fused_2d_reg_kernel<false>;
+  return launch_resident(fn, (int)G, kR8Data, args, s);
 }
 
 }  // namespace nvfp4host
