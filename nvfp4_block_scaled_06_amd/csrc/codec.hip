@@ -20,10 +20,14 @@
 //  FUSED       one launch of co-resident workgroups that walk the batch
 //              tensor by tensor.  fused_reg8_kernel when a tensor fits on
 //              chip (registers + LDS of the whole GPU): every input byte is
-//              read from HBM once.  Otherwise fused_quantize_kernel: each
-//              workgroup reduces its slice of tensor t, publishes it
-//              (agent-scope atomics), then encodes its slice of tensor t-1,
-//              read again newest-first.
+//              read from HBM once.  fused_big_kernel for a tensor of four
+//              or more on-chip chunks: four chunks stay on chip between its
+//              two passes.  Otherwise fused_quantize_kernel: each workgroup
+//              reduces its slice of tensor t, publishes it (agent-scope
+//              atomics), then encodes its slice of tensor t-1, read again
+//              newest-first.
+// The 2D tile-scale variants (nvfp4_quantize_ex) run fused_2d_reg_kernel
+// when the tensors fit on chip.
 #include <algorithm>
 #include <atomic>
 #include <cstddef>
@@ -335,41 +339,15 @@ __global__ void __launch_bounds__(kThreads) fused_quantize_kernel(const u32x4* _
   }
 }
 
-// ------------------------------------------------------------ fused, tensor held on chip
-// When one tensor fits on chip (up to kOnchipMaxPer half blocks per data
-// thread, one workgroup per CU), the persistent launch reads every input
-// byte from HBM exactly once.
-//
-// Each workgroup has kOnchipDataWaves data waves and one synchronization
-// wave.  Data thread i of workgroup w owns half blocks w*S + p*D + i
-// (p < kPer, D data threads, S = D*kPer) of every tensor.  Three tensors are
-// on chip at once: t in registers (waiting for its amax, then encoded),
-// t+1 in registers (its maximum published, its amax exchange in flight
-// while t is encoded) and t+2 streaming into an LDS buffer through direct
-// buffer-to-LDS loads, which hold no registers.  A step moves t+1 from LDS
-// into registers two pieces at a time, reissuing each freed LDS slot for
-// t+2 at once, so HBM always has a tensor's worth of loads queued.
-//
-// The cross-workgroup exchange of maxima runs in the synchronization wave:
-// each workgroup stores its maximum into its own slot of the tensor's line
-// set and every synchronization wave polls all slots -- plain agent-scope
-// stores and loads, no read-modify-write chains.  Waiting on those loads
-// never waits for the data waves' loads (each wave retires its vector
-// memory operations through its own in-order counter), and data and
-// synchronization waves meet at barriers that order LDS traffic only.
-//
-// The compiler tracks neither the completion of the buffer-to-LDS loads nor
-// reads of what they wrote piecewise, so the data waves wait for them with
-// explicit counts: a step always issues the same number of vector memory
-// operations in the same order (2*kPer stores, then kPer loads; tensors
-// past the batch and slices past a tensor use buffer resources of extent
-// zero or of the tensor's size, whose accesses read zeros and write
-// nothing).
-constexpr int kOnchipDataWaves = 7;
-constexpr int kOnchipData = 64 * kOnchipDataWaves;     // data threads per workgroup
-constexpr int kOnchipThreads = kOnchipData + 64;      // + the synchronization wave
-constexpr int kOnchipMaxPer = 16;                       // 2 x 16 x 16 B registers + 16 x 7 KiB LDS
-
+// ------------------------------------------------------------ on-chip pipeline helpers
+// The on-chip kernels below hold whole tensors in registers and LDS (one
+// workgroup per CU) and exchange per-tensor maxima between workgroups
+// through one slot per workgroup in the workspace: plain agent-scope stores
+// and polled loads, no read-modify-write chains.  A wave retires its vector
+// memory operations through one in-order counter, and the compiler tracks
+// neither buffer-to-LDS loads nor reads of what they wrote piecewise, so the
+// kernels issue the same memory operations in the same order in every wave
+// and wait with explicit counts.
 typedef __attribute__((address_space(3))) void lds_void_t;
 
 // s_waitcnt with only the vector memory counter constrained (gfx9 encoding:
@@ -387,20 +365,6 @@ __device__ __forceinline__ void wait_vmcnt() {
 // side of it.
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-// Two 16-byte LDS reads, complete on return.
-__device__ __forceinline__ void lds_read2(const u32x4* a, const u32x4* b, u32x4& ra, u32x4& rb) {
-  asm volatile("ds_read_b128 %0, %2\n\tds_read_b128 %1, %3\n\ts_waitcnt lgkmcnt(0)"
-               : "=&v"(ra), "=&v"(rb)
-               : "v"((uint32_t)(uintptr_t)a), "v"((uint32_t)(uintptr_t)b)
-               : "memory");
-}
-
-struct OnchipShared {
-  double table[128];                  // fp64 reciprocal of every block divisor of the tensor
-  double r6;                          // reciprocal of d6 = RN32(6 g)
-  uint32_t red[kOnchipDataWaves];     // per-data-wave maxima of the tensor
-};
-
 // Buffer resource over tensor t's range of a per-tensor array of `bytes`
 // bytes per tensor (t >= batch: extent zero, every access is a no-op).
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t tensor_rsrc(const void* base, int t, int batch, int64_t bytes) {
@@ -409,169 +373,9 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t tensor_rsrc(const void* base, 
                                            t < batch ? (int)bytes : 0, kBufferWord3);
 }
 
-// Layouts of the on-chip quantize (kMode):
-//  kOn1D: the workgroup's slice is S = kPer * D consecutive half blocks;
-//      thread i's piece p is half block w S + p D + i (D data threads).
-//  kOn2D (16 x 16 tile scales, kPer = 16): thread i of workgroup w owns
-//      strip s = w D + i, the 8 columns [8 c, 8 c + 8) of the 16 rows
-//      [16 r, 16 r + 16) with (r, c) = (s / spr, s % spr), spr = cols / 8;
-//      piece p is row 16 r + p.  Strips 2k and 2k+1 (a lane pair) form one
-//      tile; codes and scales are written row-major like the input.
-//  kOn2DT (the same tiles, outputs transposed: q [cols][rows/2], sf
-//      [cols][rows/16]): data wave v of workgroup w takes the block b = 7 w
-//      + v of 8 x 8 strips (128 rows x 64 columns; blocks run down the
-//      columns), lane l the strip (8 bR + l / 8, 8 bC + l % 8).  A lane pair
-//      is again one tile; for each of its 8 columns a lane writes the 16
-//      rows' codes (8 bytes) and the tile's scale byte, so the 8 lanes of a
-//      strip column write 64 contiguous bytes of an output row.
-// Each lane's input piece p is the 16-byte half block at byte voff + p *
-// pstride.  Stores go to qoff + i * qstride and soff + i * sstride, i the
-// piece (row-major modes) or the column (kOn2DT).  Lanes past the tensor
-// get offsets past its extent: their loads read zeros, their stores are
-// dropped.
-constexpr int kOn1D = 0, kOn2D = 1, kOn2DT = 2;
 constexpr int kOnOutside = 0x70000000;          // past every on-chip tensor's extent, with room for the strides
 
-struct OnchipMap {
-  int voff, pstride;                            // input bytes
-  int qoff, qstride;                            // code bytes
-  int soff, sstride;                            // scale bytes
-};
-
-template <int kPer, int kMode>
-__device__ __forceinline__ OnchipMap onchip_map(int spr, int srows) {
-  OnchipMap m;
-  const int lane = (int)threadIdx.x & 63;
-  if (kMode == kOn2DT) {
-    const int nbr = (srows + 7) / 8, nbc = (spr + 7) / 8;
-    const int b = (int)blockIdx.x * kOnchipDataWaves + (int)(threadIdx.x >> 6);
-    const int br = b % nbr, bc = b / nbr;
-    const int r = 8 * br + (lane >> 3), c = 8 * bc + (lane & 7);
-    const bool in = bc < nbc && r < srows && c < spr;
-    const int rows = 16 * srows;
-    m.voff = in ? (r * 16 * spr + c) * 16 : kOnOutside;
-    m.pstride = spr * 16;
-    m.qoff = in ? 8 * c * (rows / 2) + 8 * r : kOnOutside;
-    m.qstride = rows / 2;
-    m.soff = in ? 8 * c * (rows / 16) + r : kOnOutside;
-    m.sstride = rows / 16;
-    return m;
-  }
-  if (kMode == kOn2D) {
-    const int s = (int)blockIdx.x * kOnchipData + (int)threadIdx.x;
-    const int r = s / spr, c = s - r * spr;
-    m.voff = (r * 16 * spr + c) * 16;
-    m.pstride = spr * 16;
-  } else {
-    m.voff = ((int)blockIdx.x * kPer * kOnchipData + (int)threadIdx.x) * 16;
-    m.pstride = kOnchipData * 16;
-  }
-  m.qoff = m.voff / 4;
-  m.qstride = m.pstride / 4;
-  // even lanes write the pair's scale byte; odd lanes aim past the extent
-  // (a dropped store), so every lane issues the same stores
-  m.soff = (lane & 1) ? (int)0x80000000u : m.voff / 32;
-  m.sstride = m.pstride / 32;
-  return m;
-}
-
-// Issues the buffer-to-LDS loads of pieces [p0, p0 + n) of tensor t.
-__device__ __forceinline__ void onchip_dma(u32x4 (*L)[kOnchipData], __amdgpu_buffer_rsrc_t rs, const OnchipMap& mp,
-                                           int p0, int n) {
-  const int w = threadIdx.x >> 6;
-  for (int p = p0; p < p0 + n; ++p)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)&L[p][w * 64], 16, mp.voff, p * mp.pstride, 0, kStreamLoad);
-}
-
-template <int kPer>
-__device__ __forceinline__ uint32_t onchip_wave_max(const u32x4 (&v)[kPer]) {
-  uint32_t m = 0;
-#pragma unroll
-  for (int p = 0; p < kPer; ++p) m = pk_absmax(pk_absmax(pk_absmax(pk_absmax(m, v[p].x), v[p].y), v[p].z), v[p].w);
-  return wave_max_u32(halves_max(m));
-}
-
-// Moves tensor t+1 from LDS into nxt and refills the LDS buffer with tensor
-// t+2, a pair of pieces at a time.  kStores is the number of vector memory
-// operations issued since tensor t+1's loads (the previous step's stores):
-// before pair j, the operations younger than its second load are the
-// kPer-2-2j later loads of t+1, kStores stores and 2j loads of t+2.
-template <int kPer, int kStores>
-__device__ __forceinline__ void onchip_refill(const u32x4* __restrict__ x, int t, int batch, int64_t hb,
-                                              const OnchipMap& mp, u32x4 (&nxt)[kPer], u32x4 (*L)[kOnchipData]) {
-  const __amdgpu_buffer_rsrc_t rs = tensor_rsrc(x, t + 2, batch, hb * 16);
-#pragma unroll
-  for (int p = 0; p < kPer; p += 2) {
-    wait_vmcnt<kPer - 2 + kStores>();
-    lds_read2(&L[p][threadIdx.x], &L[p + 1][threadIdx.x], nxt[p], nxt[p + 1]);
-    onchip_dma(L, rs, mp, p, 2);
-  }
-  __builtin_amdgcn_sched_barrier(0);
-}
-
-// One step of a data wave: tensor t (in cur) is encoded once its amax
-// arrives, tensor t+1 moves from LDS into nxt and its maximum is published.
-// Vector memory operations the encode of one tensor issues per thread.
-template <int kPer, int kMode>
-constexpr int onchip_stores() { return kMode == kOn2DT ? 16 : 2 * kPer; }
-
-template <int kPer, int kMode>
-__device__ __forceinline__ void onchip_data_step(const u32x4* __restrict__ x, int t, int batch, int64_t hb,
-                                                 const OnchipMap& mp, u32x4 (&cur)[kPer], u32x4 (&nxt)[kPer],
-                                                 u32x4 (*L)[kOnchipData], uint32_t* __restrict__ q,
-                                                 uint8_t* __restrict__ sf, OnchipShared& sh) {
-  if (t == 0)
-    onchip_refill<kPer, 0>(x, t, batch, hb, mp, nxt, L);
-  else
-    onchip_refill<kPer, onchip_stores<kPer, kMode>()>(x, t, batch, hb, mp, nxt, L);
-  const uint32_t m = onchip_wave_max<kPer>(nxt);
-  if ((threadIdx.x & 63) == 0) sh.red[threadIdx.x >> 6] = m;
-  lds_barrier();                                       // maxima of t+1 -> synchronization wave
-  lds_barrier();                                       // amax of t, r6 and table <- synchronization wave
-  const double r6 = sh.r6;
-  const __amdgpu_buffer_rsrc_t rq = tensor_rsrc(q, t, batch, hb * 4);
-  const __amdgpu_buffer_rsrc_t rsf = tensor_rsrc(sf, t, batch, hb / 2);
-  uint32_t sbyte2d = 0u;
-  double rd2d = 0.0;
-  if (kMode != kOn1D) {                                // one 16 x 16 tile: the lane's 16 rows and its partner's
-    uint32_t bam = 0u;
-#pragma unroll
-    for (int p = 0; p < kPer; ++p) bam = bam > half_absmax_bits(cur[p]) ? bam : half_absmax_bits(cur[p]);
-    sbyte2d = block_scale_byte(pair_max(bam), r6);
-    rd2d = sh.table[sbyte2d];
-  }
-  if (kMode == kOn2DT) {
-    // column j of the strip: rows 0..7 and 8..15 gathered into two half
-    // blocks (row p in element p), 8 code bytes down the column
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
-      uint32_t col[8];
-#pragma unroll
-      for (int p = 0; p < 16; p += 2) {
-        const uint32_t lo = j / 2 == 0 ? cur[p].x : j / 2 == 1 ? cur[p].y : j / 2 == 2 ? cur[p].z : cur[p].w;
-        const uint32_t hi = j / 2 == 0 ? cur[p + 1].x : j / 2 == 1 ? cur[p + 1].y : j / 2 == 2 ? cur[p + 1].z : cur[p + 1].w;
-        col[p / 2] = __builtin_amdgcn_perm(hi, lo, sel);
-      }
-      const uint32_t c0 = encode_half(u32x4{col[0], col[1], col[2], col[3]}, rd2d);
-      const uint32_t c1 = encode_half(u32x4{col[4], col[5], col[6], col[7]}, rd2d);
-      __builtin_amdgcn_raw_buffer_store_b64(u32x2{c0, c1}, rq, mp.qoff, j * mp.qstride, 0);
-      __builtin_amdgcn_raw_buffer_store_b8((uint8_t)sbyte2d, rsf, mp.soff, j * mp.sstride, 0);
-      __builtin_amdgcn_sched_barrier(0);               // one column's temporaries at a time
-    }
-    return;
-  }
-#pragma unroll
-  for (int p = 0; p < kPer; ++p) {
-    const uint32_t sbyte = kMode == kOn2D ? sbyte2d : block_scale_byte(pair_max(half_absmax_bits(cur[p])), r6);
-    const uint32_t code = encode_half(cur[p], kMode == kOn2D ? rd2d : sh.table[sbyte]);
-    __builtin_amdgcn_raw_buffer_store_b32(code, rq, mp.qoff, p * mp.qstride, 0);
-    __builtin_amdgcn_raw_buffer_store_b8((uint8_t)sbyte, rsf, mp.soff, p * mp.sstride, 0);
-    __builtin_amdgcn_sched_barrier(0);                 // one half block's temporaries at a time
-  }
-}
-
-// Synchronization wave: slot exchange of tensor t's workgroup maxima.
+// Slot exchange: workgroup w publishes its maximum of tensor t.
 __device__ __forceinline__ void onchip_publish(uint32_t* ws, int t, uint32_t m) {
   __hip_atomic_store(fused_line(ws, t, 0) + blockIdx.x, 0x80000000u | m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -608,86 +412,6 @@ __device__ __forceinline__ uint32_t onchip_wait(uint32_t* ws, int t, int G) {
   return 0u;
 }
 
-// Synchronization wave of the on-chip quantize kernels: per tensor t, it
-// publishes the workgroup's maximum of t+1 (gathered in sh.red by the data
-// waves), waits for every workgroup's maximum of t, and hands g's table and
-// r6 to the data waves; it meets them at two LDS barriers per tensor plus
-// one before the first.
-__device__ __forceinline__ void onchip_sync_wave(uint32_t* ws, int batch, int G, float* __restrict__ gout,
-                                                 OnchipShared& sh) {
-  const int lane = threadIdx.x & 63;
-  auto red_max = [&]() {
-    uint32_t r = sh.red[0];
-#pragma unroll
-    for (int k = 1; k < kOnchipDataWaves; ++k) r = r > sh.red[k] ? r : sh.red[k];
-    return r;
-  };
-  lds_barrier();
-  if (lane == 0) onchip_publish(ws, 0, red_max());
-  for (int t = 0; t < batch; ++t) {
-    lds_barrier();                                     // maxima of t+1 are in sh.red
-    const uint32_t next = red_max();
-    if (lane == 0 && t + 1 < batch) onchip_publish(ws, t + 1, next);
-    const uint32_t v = onchip_wait(ws, t, G);
-    const float g = v ? __uint_as_float((v & 0x7fffu) << 16) / kGlobalDiv : __builtin_nanf("");
-    sh.table[lane] = recip_entry((uint32_t)lane, g);
-    if (lane < 63) sh.table[lane + 64] = recip_entry((uint32_t)lane + 64, g);
-    if (lane == 0) {
-      sh.r6 = recip_d6(g);
-      if (blockIdx.x == 0) gout[t] = g;
-    }
-    lds_barrier();                                     // publish r6 and the table
-  }
-  // the last workgroup out restores the slots and the counter to zero; every
-  // slot read of this workgroup has returned (the values were used above)
-  uint32_t last = 0;
-  if (lane == 0)
-    last = __hip_atomic_fetch_add(&((FusedHeader*)ws)->done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-           (uint32_t)G - 1;
-  if (__builtin_amdgcn_readfirstlane((int)last)) {
-    const size_t words = (size_t)batch * kTensorWords;
-    uint32_t* base = ws + kFusedHeaderBytes / 4;
-    for (size_t i = lane; i < words; i += 64)
-      __hip_atomic_store(base + i, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (lane == 0) __hip_atomic_store(&((FusedHeader*)ws)->done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
-}
-
-
-template <int kPer, int kMode>
-__global__ void __launch_bounds__(kOnchipThreads) fused_onchip_kernel(const u32x4* __restrict__ x, int batch,
-                                                                      int64_t hb, int spr, int srows, uint32_t* ws,
-                                                                      float* __restrict__ gout,
-                                                                      uint32_t* __restrict__ q,
-                                                                      uint8_t* __restrict__ sf) {
-  static_assert(kPer % 2 == 0 && kPer <= kOnchipMaxPer, "pieces move in pairs");
-  static_assert(kMode == kOn1D || kPer == 16, "a 2D strip is 16 rows");
-  __shared__ OnchipShared sh;
-  __shared__ __attribute__((aligned(16))) u32x4 L[kPer][kOnchipData];
-  const int G = gridDim.x;
-  if (wave_id() < kOnchipDataWaves) {
-    u32x4 a[kPer], b[kPer];
-    const OnchipMap mp = onchip_map<kPer, kMode>(spr, srows);
-    onchip_dma(L, tensor_rsrc(x, 0, batch, hb * 16), mp, 0, kPer);
-    wait_vmcnt<0>();
-#pragma unroll
-    for (int p = 0; p < kPer; p += 2) lds_read2(&L[p][threadIdx.x], &L[p + 1][threadIdx.x], a[p], a[p + 1]);
-    onchip_dma(L, tensor_rsrc(x, 1, batch, hb * 16), mp, 0, kPer);
-    const uint32_t m = onchip_wave_max<kPer>(a);
-    if ((threadIdx.x & 63) == 0) sh.red[threadIdx.x >> 6] = m;
-    lds_barrier();                                     // maxima of tensor 0
-    int t = 0;
-    for (; t + 1 < batch; t += 2) {
-      onchip_data_step<kPer, kMode>(x, t, batch, hb, mp, a, b, L, q, sf, sh);
-      onchip_data_step<kPer, kMode>(x, t + 1, batch, hb, mp, b, a, L, q, sf, sh);
-    }
-    if (t < batch) onchip_data_step<kPer, kMode>(x, t, batch, hb, mp, a, b, L, q, sf, sh);
-    return;
-  }
-  onchip_sync_wave(ws, batch, G, gout, sh);
-}
-
-// ------------------------------------------------------------ on-chip pipeline helpers
 // One LDS read of 16 bytes at base + kOff (an immediate offset), complete on
 // return.
 template <int kOff>
@@ -1583,10 +1307,10 @@ size_t quantize_2d_onchip_ws_bytes(int64_t batch) {
 }
 
 // 2D quantize (one E4M3 scale per 16 x 16 tile; outputs row-major, or
-// transposed with colwise) of batch tensors [rows][cols] in one
-// launch of fused_onchip_kernel<16, kOn2D | kOn2DT> when a tensor's 16-row x
-// 8-column strips fit on the chip: every input byte is read once.  ENOTSUP when they do not (the
-// caller then runs its two-pass path).  The exchange header in ws is
+// transposed with colwise) of batch tensors [rows][cols] in one launch of
+// fused_2d_reg_kernel when a tensor's 16-row x 8-column strips fit on the
+// chip, one per thread: every input byte is read once.  ENOTSUP when they do
+// not (the caller then runs its two-pass path).  The exchange header in ws is
 // cleared first, so the scratch needs no preparation.  The shape and
 // pointers are validated by the caller (rows % 16 == 0, cols % 16 == 0).
 nvfp4_status quantize_2d_onchip(const uint16_t* x, int64_t batch, int64_t rows, int64_t cols, bool colwise, uint8_t* q,
