@@ -274,12 +274,16 @@ def run_extras(nv, synth, torch, which):
         y = torch.empty_like(x)
         n = 1024 * 1024
         mq = timed(torch, lambda: nv.quantize(x, workspace=ws, out=(q, sf, g)), 50)
+        mf = timed(torch, lambda: nv.quantize(x, flags="fused", workspace=ws, out=(q, sf, g)), 50) if fused else None
         md = timed(torch, lambda: nv.dequantize(q, sf, g, out=y), 50)
         rows["single_1024x1024"] = {
             "note": "2.7 MB working set: launch-bound and cache-resident; warm medians of HIP events around "
                     "one call with preallocated outputs (the stream held busy first, so host latency is excluded)",
             "quantize": {"ms": mq, **roof(bytes_quantize(n, 1), mq, HBM_PEAK_GBS, "GB/s")},
             "dequantize": {"ms": md, **roof(bytes_dequant(n, 1), md, HBM_PEAK_GBS, "GB/s")}}
+        if mf is not None:
+            rows["single_1024x1024"]["quantize_fused"] = {"ms": mf, **roof(bytes_quantize(n, 1), mf, HBM_PEAK_GBS,
+                                                                           "GB/s")}
         del x, q, sf, g, y
     if "acts" in which:
         x = synth.activations(device="cuda")

@@ -988,13 +988,13 @@ __global__ void __launch_bounds__(kR8Data) fused_2d_reg_kernel(const u32x4* __re
 }
 
 // ------------------------------------------------------------ fused, tensors larger than the chip
-// One launch for tensors of nc >= 4 chunks, a chunk being what the on-chip
+// One launch for tensors of nc >= 2 chunks, a chunk being what the on-chip
 // kernel holds (D = 512 threads x kPer half blocks per workgroup, one
 // workgroup per compute unit).  Per tensor:
-//   pass 1: the last three chunks load straight into the three register
-//     sets; every other chunk streams through the LDS stage (its maximum
-//     taken as it lands, the slot reloaded with the next chunk), and chunk
-//     nc-4 stays in the stage;
+//   pass 1: the last three chunks (all of them when nc < 3) load straight
+//     into the register sets; every chunk before nc-4 streams through the
+//     LDS stage (its maximum taken as it lands, the slot reloaded with the
+//     next chunk), and chunk nc-4 stays in the stage;
 //   exchange: wave 7 publishes the workgroup's maximum and waits for the
 //     tensor's amax, then builds the table;
 //   pass 2: the encode walks the chunks in the order nc-3, nc-2, nc-1, nc-4,
@@ -1002,7 +1002,8 @@ __global__ void __launch_bounds__(kR8Data) fused_2d_reg_kernel(const u32x4* __re
 //     on-chip kernel walks tensors: encode a set, move the stage into it,
 //     reload the stage with the chunk four places on.
 // So four chunks are read once and the others twice, newest first (the most
-// recently read data is the likeliest to still be in the last-level cache).
+// recently read data is the likeliest to still be in the last-level cache);
+// a tensor of at most four chunks is read once.
 template <int kPer>
 __device__ __forceinline__ void big_load_set(u32x4 (&R)[kPer], __amdgpu_buffer_rsrc_t rs, int voff) {
 #pragma unroll
@@ -1051,8 +1052,13 @@ __device__ __forceinline__ uint32_t big_stage_max(std::integer_sequence<int, P..
   return m;
 }
 
-// Chunk encoded at pass-2 position s of nc chunks.
-__device__ __forceinline__ int big_chunk(int s, int nc) { return s < 3 ? nc - 3 + s : nc - 1 - s; }
+// Chunk encoded at pass-2 position s of nc chunks: the register sets hold
+// the last nreg = min(nc, 3) chunks in order, then the stage chunks follow
+// newest first.
+__device__ __forceinline__ int big_chunk(int s, int nc) {
+  const int nreg = nc < 3 ? nc : 3;
+  return s < nreg ? nc - nreg + s : nc - 1 - s;
+}
 
 // Pass 2, position s: encode `cur` (chunk big_chunk(s)), move the stage
 // (position s+3) into it, reload the stage with position s+4.  The stage
@@ -1099,11 +1105,11 @@ __global__ void __launch_bounds__(kR8Data) fused_big_kernel(const u32x4* __restr
     u32x4 a[kPer], b[kPer], c[kPer];
     BlockMax<kPer> am, bmx, cm;
     // ---- pass 1
-    big_load_set<kPer>(a, rx, voff + (nc - 3) * cbytes);
-    big_load_set<kPer>(b, rx, voff + (nc - 2) * cbytes);
-    big_load_set<kPer>(c, rx, voff + (nc - 1) * cbytes);
+    big_load_set<kPer>(a, rx, voff + big_chunk(0, nc) * cbytes);
+    big_load_set<kPer>(b, nc >= 2 ? rx : none, voff + big_chunk(1, nc) * cbytes);
+    big_load_set<kPer>(c, nc >= 3 ? rx : none, voff + big_chunk(2, nc) * cbytes);
     __builtin_amdgcn_sched_barrier(0);
-    big_stage_issue<kPer>(rx, stage_w, voff);           // chunk 0
+    big_stage_issue<kPer>(nc >= 4 ? rx : none, stage_w, voff);   // chunk 0 (nc - 4 when nc = 4)
     uint32_t m = 0;
     for (int k = 0; k + 4 < nc; ++k)                    // chunks 0..nc-5 pass through; chunk nc-4 stays
       big_stage_chunk<kPer>(std::make_integer_sequence<int, kPer>{}, m, b0, b1, rx, stage_w, voff + (k + 1) * cbytes);
@@ -1268,15 +1274,15 @@ int onchip_per_thread(int64_t hb_per_tensor) {
 
 // Chunks of fused_big_kernel for a tensor (one workgroup per CU, kR8MaxPer
 // half blocks per data thread), or 0 when it does not apply: a tensor that
-// fits on chip, one of fewer than four chunks, or one whose byte offsets
-// would not fit the 32-bit buffer offsets.
+// fits on chip in one chunk, or one whose byte offsets would not fit the
+// 32-bit buffer offsets.
 int big_chunks(int64_t hb_per_tensor) {
   if (hb_per_tensor <= 0) return 0;
   const int64_t cus = nvfp4host::num_cus();
   if (cus > kR8PollSlots || cus > (int64_t)kTensorWords) return 0;
   const int64_t chunk = cus * kR8MaxPer * kR8Data;
   const int64_t nc = (hb_per_tensor + chunk - 1) / chunk;
-  if (nc < 4 || nc * chunk * 16 >= (INT64_C(1) << 31)) return 0;
+  if (nc < 2 || nc * chunk * 16 >= (INT64_C(1) << 31)) return 0;
   return (int)nc;
 }
 

@@ -29,11 +29,11 @@ class _WaitLimit:
         return False
 
 
-@pytest.mark.parametrize("shape", [(5, 256, 1024), (1, 8192, 2048), (1, 8192, 7168)])
+@pytest.mark.parametrize("shape", [(5, 256, 1024), (1, 8192, 7168), (1, 65536, 16384)])
 def test_fused_wait_timeout_is_reported(shape):
     """With a poll limit of 0 every wait of the FUSED launch gives up at once
-    (the on-chip kernel for the first shape, the streaming one for the
-    second, the big-tensor one for the third: four chunks on 256 CUs).  A
+    (the on-chip kernel for the first shape, the big-tensor one for the
+    second, the streaming one for the third: 2 GiB of bf16).  A
     tensor whose amax was still being gathered when its workgroups had to
     wait gets NaN for g; one whose maxima had all arrived
     when they were polled keeps its exact g.  At least one tensor waits (the

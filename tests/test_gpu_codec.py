@@ -266,14 +266,15 @@ def _chunk_elems():
 
 
 # (chunks, which chunk holds the planted maximum, batch): every pass-2 tail
-# (nc mod 3), and the maximum in a streamed chunk, the staged chunk nc-4 and
-# each register-held chunk.
-BIG_CASES = [(4, 0, 1), (5, 0, 1), (5, 3, 2), (6, 2, 1), (7, 6, 1), (8, 5, 1)]
+# (nc mod 3), the maximum in a streamed chunk, the staged chunk nc-4 and
+# each register-held chunk, and tensors of two and three chunks (read once).
+BIG_CASES = [(2, 0, 1), (2, 1, 3), (3, 2, 1), (3, 0, 2), (4, 0, 1), (5, 0, 1), (5, 3, 2), (6, 2, 1), (7, 6, 1),
+             (8, 5, 1)]
 
 
 @pytest.mark.parametrize("nc,hot,batch", BIG_CASES)
 def test_big_tensor_chunks(nc, hot, batch):
-    """Tensors of 4..8 on-chip chunks (the single-launch path for tensors
+    """Tensors of 2..8 on-chip chunks (the single-launch path for tensors
     larger than the chip), ragged last chunk, guarded outputs."""
     cols = 7168
     elems = (nc - 1) * _chunk_elems() + 3 * cols * 37   # the last chunk partly filled
@@ -300,6 +301,20 @@ def test_big_tensor_chunks(nc, hot, batch):
     assert bad.size == 0, f"scale byte mismatch at {bad[:5].tolist()}"
     bad = np.argwhere(np_(qg.view) != oq)
     assert bad.size == 0, f"code mismatch at {bad[:5].tolist()}"
+
+
+def test_streaming_fused_over_2gib():
+    """A 65536 x 16384 tensor (2 GiB of bf16) is past the 32-bit offsets of
+    the single-launch kernels, so FUSED runs the streaming kernel (pass 1 of
+    tensor t beside pass 2 of tensor t-1); bit for bit against the oracle."""
+    print("case: streaming fused, 65536x16384", flush=True)
+    x = synth.normal((1, 65536, 16384), 1.5, seed=777, device="cuda")
+    q, sf, g = nv.quantize(x, flags="fused")
+    torch.cuda.synchronize()
+    oq, osf, og = oracle.quantize(bits(x))
+    assert np.array_equal(np_(g).view(np.uint32), og.view(np.uint32))
+    assert np.array_equal(np_(sf), osf)
+    assert np.array_equal(np_(q), oq)
 
 
 def test_fused_workspace_is_left_clean():
