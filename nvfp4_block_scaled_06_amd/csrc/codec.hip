@@ -20,9 +20,9 @@
 //  FUSED       one launch of co-resident workgroups that walk the batch
 //              tensor by tensor.  fused_reg8_kernel when a tensor fits on
 //              chip (registers + LDS of the whole GPU): every input byte is
-//              read from HBM once.  fused_big_kernel for a tensor of four
-//              or more on-chip chunks: four chunks stay on chip between its
-//              two passes.  Otherwise fused_quantize_kernel: each workgroup
+//              read from HBM once.  fused_big_kernel for a larger tensor:
+//              up to four chunks stay on chip between its two passes.
+//              Past 2 GiB per tensor, fused_quantize_kernel: each workgroup
 //              reduces its slice of tensor t, publishes it (agent-scope
 //              atomics), then encodes its slice of tensor t-1, read again
 //              newest-first.
