@@ -100,7 +100,7 @@ int32_t nvfp4_last_hip_error(void);
  *   EALIGN, EWORKSPACE, ENOTSUP (unknown flag / not gfx950), EHIP.
  * FUSED runs every workgroup of one launch through a cross-workgroup
  * exchange of maxima; the grid is at most one round of resident workgroups
- * (at most one per compute unit for tensors held on chip), so FUSED calls
+ * (one per compute unit for tensors under 2 GiB), so FUSED calls
  * must not overlap in time with other kernels that occupy the whole device
  * and wait for one another (such as a FUSED call on another stream).  Each
  * wait is bounded (see nvfp4_set_wait_limit).  A wait that gives up -- which
@@ -329,9 +329,9 @@ size_t nvfp4_quantize_ex_workspace_bytes(int64_t batch);
  * values).  Two passes over x (amax, then encode); 2D without RHT or SR
  * (with or without COLWISE) reads x once in a single launch
  * when a tensor's strips of 16 rows x 8 columns fit on the chip (at most
- * compute units x 448 of them; COLWISE counts blocks of 8 x 8 strips, 7 per
- * compute unit), with the same bytes.  variant 0 equals nvfp4_quantize bit
- * for bit.
+ * compute units x 512 of them; COLWISE counts blocks of 8 x 8 strips, 8 per
+ * compute unit) and a tensor is under 2 GiB, with the same bytes.  variant 0
+ * equals nvfp4_quantize bit for bit.
  * Errors: EINVAL (cols % 16 != 0, rows % 16 != 0 with COLWISE or 2D, unknown
  *   variant bits, rht_signs > 0xFFFF, batch > 65535, null pointers), ENOTSUP
  *   (2D with RHT, or the device), EALIGN (x, q not 16-byte aligned; g,
