@@ -48,20 +48,38 @@ struct VarShape {
   int64_t seg, nseg, nitems;                   // strips per work item, items per band, items per tensor
 };
 
-// Philox4x32-10 (Salmon et al., SC 2011).
-__device__ __forceinline__ void philox(uint32_t c0, uint32_t c1, uint32_t k0, uint32_t k1, uint32_t (&o)[4]) {
+// Philox4x32-10 (Salmon et al., SC 2011).  The ten round keys are computed
+// once per thread and held in VGPRs: uniform as they are, as scalars they
+// would not fit beside the kernels' other uniform values and were spilled
+// to VGPR lanes and read back (v_readlane) inside the loops.
+struct PhiloxKeys {
+  uint32_t k0[10], k1[10];
+};
+
+__device__ __forceinline__ PhiloxKeys philox_keys(uint64_t seed) {
+  PhiloxKeys k;
+  uint32_t a = (uint32_t)seed, b = (uint32_t)(seed >> 32);
+  asm volatile("v_mov_b32 %0, %1" : "=v"(a) : "s"(a));   // keep the keys in vector registers
+  asm volatile("v_mov_b32 %0, %1" : "=v"(b) : "s"(b));
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    k.k0[r] = a;
+    k.k1[r] = b;
+    a += 0x9E3779B9u;
+    b += 0xBB67AE85u;
+  }
+  return k;
+}
+
+__device__ __forceinline__ void philox(uint32_t c0, uint32_t c1, const PhiloxKeys& k, uint32_t (&o)[4]) {
   uint32_t c2 = 0u, c3 = 0u;
 #pragma unroll
   for (int r = 0; r < 10; ++r) {
-    if (r > 0) {
-      k0 += 0x9E3779B9u;
-      k1 += 0xBB67AE85u;
-    }
     // one 32 x 32 -> 64-bit multiply each (a single v_mad_u64_u32)
     const uint64_t p0 = (uint64_t)c0 * 0xD2511F53u, p1 = (uint64_t)c2 * 0xCD9E8D57u;
     const uint32_t lo0 = (uint32_t)p0, hi0 = (uint32_t)(p0 >> 32);
     const uint32_t lo1 = (uint32_t)p1, hi1 = (uint32_t)(p1 >> 32);
-    const uint32_t n0 = hi1 ^ c1 ^ k0, n2 = hi0 ^ c3 ^ k1;
+    const uint32_t n0 = hi1 ^ c1 ^ k.k0[r], n2 = hi0 ^ c3 ^ k.k1[r];
     c0 = n0;
     c1 = lo1;
     c2 = n2;
@@ -74,9 +92,9 @@ __device__ __forceinline__ void philox(uint32_t c0, uint32_t c1, uint32_t k0, ui
 }
 
 // The 8 16-bit draws of output elements 8n'..8n'+7, n' = n - offset.
-__device__ __forceinline__ void draws8(uint64_t n, uint32_t key0, uint32_t key1, uint32_t (&u)[8]) {
+__device__ __forceinline__ void draws8(uint64_t n, const PhiloxKeys& k, uint32_t (&u)[8]) {
   uint32_t w[4];
-  philox((uint32_t)n, (uint32_t)(n >> 32), key0, key1, w);
+  philox((uint32_t)n, (uint32_t)(n >> 32), k, w);
 #pragma unroll
   for (int j = 0; j < 8; ++j) u[j] = (w[j >> 1] >> (16 * (j & 1))) & 0xffffu;
 }
@@ -288,7 +306,7 @@ __global__ void __launch_bounds__(kVarThreads) var_encode_kernel(const uint16_t*
   __syncthreads();
 
   const uint16_t* xt = x + (int64_t)t * sh.n;
-  const uint32_t key0 = (uint32_t)seed, key1 = (uint32_t)(seed >> 32);
+  const PhiloxKeys pk = philox_keys(seed);
   for (int64_t it = (int64_t)blockIdx.x * (kVarThreads / 64) + wave; it < sh.nitems;
        it += (int64_t)gridDim.x * (kVarThreads / 64)) {
     int64_t band, s0, s1;
@@ -328,8 +346,8 @@ __global__ void __launch_bounds__(kVarThreads) var_encode_kernel(const uint16_t*
           if (kSr) {
             const uint64_t n = (uint64_t)(orow * sh.C + r0) / 8 + offset;
             uint32_t u0[8], u1[8];
-            draws8(n, key0, key1, u0);
-            draws8(n + 1, key0, key1, u1);
+            draws8(n, pk, u0);
+            draws8(n + 1, pk, u1);
 #pragma unroll
             for (int k = 0; k < 8; ++k) {
               u[k] = u0[k];
@@ -363,7 +381,7 @@ __global__ void __launch_bounds__(kVarThreads) var_encode_kernel(const uint16_t*
           const uint32_t sbyte = e4m3_rne_sat(rn32((double)__uint_as_float(bam) * r6));
           const int64_t orow = (int64_t)t * sh.R + r0 + r;
           uint32_t u[8];
-          if (kSr) draws8((uint64_t)(orow * sh.C + col) / 8 + offset, key0, key1, u);
+          if (kSr) draws8((uint64_t)(orow * sh.C + col) / 8 + offset, pk, u);
           uint32_t codes[1];
           encode_vals<8, kSr>(v, table[sbyte], u, codes);
           if (cin && r0 + r < sh.rows) {
@@ -420,7 +438,7 @@ __global__ void __launch_bounds__(kVarThreads) var_encode_colwise_kernel(
   __syncthreads();
 
   const uint16_t* xt = x + (int64_t)t * sh.n;
-  const uint32_t key0 = (uint32_t)seed, key1 = (uint32_t)(seed >> 32);
+  const PhiloxKeys pk = philox_keys(seed);
   const int64_t nblk = (sh.sr + kColStrips - 1) / kColStrips;
   const int64_t nitems = sh.sc * nblk;
   for (int64_t it = blockIdx.x; it < nitems; it += gridDim.x) {           // workgroup-uniform
@@ -459,8 +477,8 @@ __global__ void __launch_bounds__(kVarThreads) var_encode_colwise_kernel(
           const int64_t orow = (int64_t)t * sh.R + col + j;
           const uint64_t n = (uint64_t)(orow * sh.C + r0) / 8 + offset;
           uint32_t u0[8], u1[8];
-          draws8(n, key0, key1, u0);
-          draws8(n + 1, key0, key1, u1);
+          draws8(n, pk, u0);
+          draws8(n + 1, pk, u1);
 #pragma unroll
           for (int kk = 0; kk < 8; ++kk) {
             u[kk] = u0[kk];
