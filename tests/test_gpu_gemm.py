@@ -160,6 +160,38 @@ def test_grouped_gemm_against_oracle_and_dense(K):
         assert torch.equal(c[r0:r1], d), f"expert {e} differs from the dense GEMM of its rows"
 
 
+def test_grouped_gemm_full_size_sampled_rows():
+    """The benchmarked MoE shape: 16384 tokens routed top-8 over 64 experts
+    [2048 x 7168] (131072 routed rows, seeded uniform routing, activations and
+    experts as the bench draws them).  Both operands' encodings are checked
+    in full against the oracle; 512 sampled rows of C (all 2048 columns, each
+    against its expert's weight) against fp64."""
+    print("case: grouped gemm 131072 rows x 64 experts", flush=True)
+    T, E, top, N, K = 16384, 64, 8, 2048, 7168
+    gen = torch.Generator().manual_seed(106)
+    choice = torch.rand((T, E), generator=gen).argsort(dim=1)[:, :top]
+    counts = torch.bincount(choice.flatten(), minlength=E)
+    off = np.concatenate([[0], np.cumsum(counts.numpy())]).astype(np.int32)
+    M = int(off[-1])
+    a = synth.activations(tokens=M, channels=K, seed=107, device="cuda")
+    (aq, asf, ag), oa = _quantized(a)
+    del a
+    w = synth.experts(E, N, K, device="cuda")
+    (bq, bsf, bg), ob = _quantized(w)
+    del w
+    c = nv.grouped_gemm(aq, asf, ag, bq, bsf, bg, torch.from_numpy(off).cuda())
+    torch.cuda.synchronize()
+    rows = np.sort(np.random.default_rng(11).choice(M, 512, replace=False))
+    got = np_(c[torch.from_numpy(rows).cuda()])
+    want = np.empty_like(got, dtype=np.float64)
+    expert = np.searchsorted(off, rows, side="right") - 1
+    for e in np.unique(expert):
+        sel = np.nonzero(expert == e)[0]
+        want[sel] = oracle.gemm_f64(oa[0], oa[1], oa[2][0], ob[0][e], ob[1][e], ob[2][e], rows=rows[sel])
+    err = rel_frobenius(got, want)
+    assert err <= TOL, f"rel Frobenius {err:.3e}"
+
+
 def test_grouped_gemm_offsets_past_m_are_clamped():
     """A last offset beyond M is clamped to M: rows inside A are still right."""
     counts = [40, 90]

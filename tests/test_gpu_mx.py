@@ -84,21 +84,18 @@ def test_mx_dequantize_random_bytes(rows, cols):
     np.testing.assert_array_equal(bits(y), oracle.mx_dequantize(q, sf))
 
 
-def test_mx_round_trip_of_the_experts_tensor_sampled():
+def test_mx_round_trip_of_the_experts_tensor():
     """The 64 x 2048 x 7168 experts tensor: quantize and dequantize on the GPU,
-    sampled rows checked bit-exactly against the oracle."""
+    every code, scale byte and dequantized value against the oracle."""
     print("case: mx experts 64x2048x7168 seed 102", flush=True)
     x = synth.experts(device="cuda")
     q, sf = nv.mxfp4_quantize(x)
     y = nv.mxfp4_dequantize(q, sf)
     torch.cuda.synchronize()
-    flat = x.reshape(-1, 7168)
-    rows = np.sort(np.random.default_rng(2).choice(flat.shape[0], 64, replace=False))
-    idx = torch.from_numpy(rows).cuda()
-    wq, wsf = oracle.mx_quantize(bits(flat[idx]))
-    np.testing.assert_array_equal(np_(q.reshape(-1, 3584)[idx]), wq)
-    np.testing.assert_array_equal(np_(sf.reshape(-1, 224)[idx]), wsf)
-    np.testing.assert_array_equal(bits(y.reshape(-1, 7168)[idx]), oracle.mx_dequantize(wq, wsf))
+    wq, wsf = oracle.mx_quantize(bits(x.reshape(-1, 7168)))
+    assert np.array_equal(np_(q.reshape(-1, 3584)), wq), "codes"
+    assert np.array_equal(np_(sf.reshape(-1, 224)), wsf), "scale bytes"
+    assert np.array_equal(bits(y.reshape(-1, 7168)), oracle.mx_dequantize(wq, wsf)), "dequantized values"
 
 
 def test_mx_rejects_bad_shapes():
@@ -190,16 +187,15 @@ def test_mx_gemm_k_zero_gives_zeros():
     assert torch.count_nonzero(c).item() == 0
 
 
-def test_mx_gemm_full_size_sampled_rows():
-    """A [8192 x 7168] x B [2048 x 7168]^T from N(0,1) in MXFP4: 96 sampled
-    rows of C (all 2048 columns) against fp64."""
+def test_mx_gemm_full_size():
+    """A [8192 x 7168] x B [2048 x 7168]^T from N(0,1) in MXFP4, the benchmarked
+    shape: every element of C against fp64."""
     print("case: mx gemm 8192x2048x7168 seed 105", flush=True)
     a, b = synth.gemm_operands(device="cuda")
     (aq, asf), oa = _mx_quantized(a)
     (bq, bsf), ob = _mx_quantized(b)
     c = nv.mxfp4_gemm(aq, asf, bq, bsf)
     torch.cuda.synchronize()
-    rows = np.sort(np.random.default_rng(3).choice(8192, 96, replace=False))
-    want = oracle.mx_gemm_f64(oa[0], oa[1], ob[0], ob[1], rows=rows)
-    err = rel_frobenius(np_(c[torch.from_numpy(rows).cuda()]), want)
+    want = oracle.mx_gemm_f64(oa[0], oa[1], ob[0], ob[1])
+    err = rel_frobenius(np_(c), want)
     assert err <= TOL, f"rel Frobenius {err:.3e}"
