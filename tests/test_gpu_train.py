@@ -168,8 +168,11 @@ def test_2d_weight_and_its_transpose_agree():
     np.testing.assert_array_equal(np_(sft)[::16], np_(sf)[::16].T)
 
 
-def test_wgrad_operand_rht_sr_colwise():
-    """A 4096 x 7168 slice of the activations as a Wgrad operand: quantized
-    along the tokens (COLWISE) with RHT and stochastic rounding."""
-    a = synth.activations(tokens=4096, device="cuda")
-    _check(a, nv.VAR_COLWISE | nv.VAR_RHT | nv.VAR_SR, signs=0x6A3C, seed=77, offset=0)
+@pytest.mark.parametrize("variant", [nv.VAR_SR, nv.VAR_COLWISE | nv.VAR_RHT | nv.VAR_SR])
+def test_sr_variants_on_the_activations_full_size(variant):
+    """The benchmarked training variants on the full 16384 x 7168 activations
+    (RHT signs 0x6A3C, SR seed 77): row-wise SR, and the Wgrad operand
+    quantized along the tokens (COLWISE) with RHT and SR; every byte against
+    the oracle."""
+    a = synth.activations(device="cuda")
+    _check(a, variant, signs=0x6A3C, seed=77, offset=0)
