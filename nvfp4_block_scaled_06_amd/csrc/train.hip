@@ -79,7 +79,9 @@ __device__ __forceinline__ void philox(uint32_t c0, uint32_t c1, const PhiloxKey
     const uint64_t p0 = (uint64_t)c0 * 0xD2511F53u, p1 = (uint64_t)c2 * 0xCD9E8D57u;
     const uint32_t lo0 = (uint32_t)p0, hi0 = (uint32_t)(p0 >> 32);
     const uint32_t lo1 = (uint32_t)p1, hi1 = (uint32_t)(p1 >> 32);
-    const uint32_t n0 = hi1 ^ c1 ^ k.k0[r], n2 = hi0 ^ c3 ^ k.k1[r];
+    // the three-way xors as single v_bitop3 (0x96 is a ^ b ^ c)
+    const uint32_t n0 = __builtin_amdgcn_bitop3_b32(hi1, c1, k.k0[r], 0x96);
+    const uint32_t n2 = __builtin_amdgcn_bitop3_b32(hi0, c3, k.k1[r], 0x96);
     c0 = n0;
     c1 = lo1;
     c2 = n2;
@@ -99,27 +101,23 @@ __device__ __forceinline__ void draws8(uint64_t n, const PhiloxKeys& k, uint32_t
   for (int j = 0; j < 8; ++j) u[j] = (w[j >> 1] >> (16 * (j & 1))) & 0xffffu;
 }
 
-// Stochastic E2M1 magnitude code of y >= 0 with the 16-bit draw u.
+// Stochastic E2M1 magnitude code of y >= 0 with the 16-bit draw u: the grid
+// point below y, plus one when u / 2^16 < (y - lo) / gap.
 __device__ __forceinline__ uint32_t e2m1_sr(float y, uint32_t u) {
-  // The probability of rounding up is (y - lo) / gap with lo the grid point
-  // at or below y; with fp32 bits b = bits(y) that fraction is a run of
-  // mantissa bits, so each regime is an integer test on b:
   const uint32_t b = __float_as_uint(y);
-  //   y >= 1: gap = half the binade, fraction = low 22 bits m; up iff m > 64 u.
-  //   Adding 2^22 - 1 - 64 u carries into bit 22 exactly then, and bits 22
-  //   and up then read (exponent, top mantissa bit) of the result, 254 for
-  //   1.0 up to 259 for 6.0 (larger y saturate to 6)
-  const uint32_t ra = (b + (0x3FFFFFu - (u << 6))) >> 22;
-  const uint32_t ca = (ra < 259u ? ra : 259u) - 252u;
-  //   0.5 <= y < 1: lo = 0.5, gap 0.5, fraction = low 23 bits / 2^23
-  const uint32_t cb = 1u + ((b & 0x7FFFFFu) > (u << 7) ? 1u : 0u);
-  //   y < 0.5: lo = 0, gap 0.5, fraction = 2 y (u and y 2^17 are exact in fp32)
-  const uint32_t cc = (float)u < y * 131072.0f ? 1u : 0u;
-  // regime masks from the sign of a difference (b < 2^31), so the three
-  // results merge without a branch
-  const uint32_t m1 = (uint32_t)((int32_t)(0x3F7FFFFFu - b) >> 31);    // y >= 1
-  const uint32_t mh = (uint32_t)((int32_t)(0x3EFFFFFFu - b) >> 31);    // y >= 0.5
-  return (ca & m1) | (cb & mh & ~m1) | (cc & ~mh);
+  // y >= 1: the gap is half the binade and the fraction is the low 22
+  // mantissa bits m, so the rule reads m > 64 u.  Adding 2^22 - 1 - 64 u
+  // carries into bit 22 exactly then; bits 22 and up then read 254 + code
+  // (1.0 is 254, 6.0 is 259, larger y saturate to code 7).  The xor forms
+  // 2^22 - 1 - 64 u and subtracts 252 << 22 in one constant.
+  uint32_t cn = (((u << 6) ^ 0xC13FFFFFu) + b) >> 22;
+  cn = cn < 7u ? cn : 7u;
+  // y < 1: the grid is 0, 0.5, 1 with gap 0.5.  With F = 2^17 y (exact) and
+  // k = floor(F / 2^16) the lower point, the rule reads u < F - 2^16 k; u is
+  // an integer, so that is u + 2^16 k <= ceil(F) - 1, and the code is
+  // (ceil(F) + 2^16 - 1 - u) >> 16 (u ^ 0xFFFF = 2^16 - 1 - u).
+  const uint32_t cf = ((u ^ 0xFFFFu) + (uint32_t)__builtin_ceilf(y * 131072.0f)) >> 16;
+  return b >= 0x3F800000u ? cn : cf;
 }
 
 // fp32 value of element j (0..7) of a row chunk of 8 bf16.
@@ -177,15 +175,26 @@ __device__ __forceinline__ void rht16_pair(float (&v)[8], uint32_t signs, bool o
   }
 }
 
+// Keeps a per-row pointer or counter a value that steps by one add per row:
+// without it the compiler precomputes all 16 rows' offsets as scalars
+// outside the loops, which spills scalar registers to vector lanes.
+template <typename T>
+__device__ __forceinline__ void step_opaque(T& v) {
+  asm volatile("" : "+v"(v));
+}
+
 // Loads strip (sr_i, band) of tensor t: raw[r] = row r0 + r, columns
 // 512 band + 8 lane .. +7 (zeros past the tensor).
 __device__ __forceinline__ void load_strip(const uint16_t* __restrict__ xt, const VarShape& sh, int64_t r0,
                                            int64_t col, u32x4 (&raw)[kStripRows]) {
   const bool cin = col < sh.cols;
+  const uint16_t* p = xt + r0 * sh.cols + col;
 #pragma unroll
   for (int r = 0; r < kStripRows; ++r) {
     raw[r] = u32x4{0u, 0u, 0u, 0u};
-    if (cin && r0 + r < sh.rows) raw[r] = __builtin_nontemporal_load((const u32x4*)(xt + (r0 + r) * sh.cols + col));
+    if (cin && r0 + r < sh.rows) raw[r] = __builtin_nontemporal_load((const u32x4*)p);
+    p += sh.cols;
+    step_opaque(p);
   }
 }
 
@@ -277,7 +286,8 @@ __device__ __forceinline__ void encode_vals(const float (&v)[kN], double rd, con
   }
 }
 
-template <bool kColwise, bool k2D, bool kRht, bool kSr>
+// Row-wise encode (the COLWISE layout has its own kernel below).
+template <bool k2D, bool kRht, bool kSr>
 __global__ void __launch_bounds__(kVarThreads) var_encode_kernel(const uint16_t* __restrict__ x, VarShape sh,
                                                                  uint32_t signs, uint64_t seed, uint64_t offset,
                                                                  const uint32_t* __restrict__ partial, int npartial,
@@ -307,6 +317,8 @@ __global__ void __launch_bounds__(kVarThreads) var_encode_kernel(const uint16_t*
 
   const uint16_t* xt = x + (int64_t)t * sh.n;
   const PhiloxKeys pk = philox_keys(seed);
+  // per output row: C / 2 code bytes, C / 16 scale bytes, C / 8 draw counters
+  const int64_t qstep = sh.C / 2, sstep = sh.C / 16, nstep = sh.C / 8;
   for (int64_t it = (int64_t)blockIdx.x * (kVarThreads / 64) + wave; it < sh.nitems;
        it += (int64_t)gridDim.x * (kVarThreads / 64)) {
     int64_t band, s0, s1;
@@ -319,76 +331,50 @@ __global__ void __launch_bounds__(kVarThreads) var_encode_kernel(const uint16_t*
       load_strip(xt, sh, r0, col, raw);
       uint32_t tile = 0u;                              // 2D: the tile amax (fp32 bits), pair-wide
       if (k2D) {
-        uint32_t pk = 0u;
+        uint32_t pm = 0u;
 #pragma unroll
         for (int r = 0; r < kStripRows; ++r)
-          pk = pk_absmax(pk_absmax(pk_absmax(pk_absmax(pk, raw[r].x), raw[r].y), raw[r].z), raw[r].w);
-        tile = pair_max_u32(halves_max(pk) << 16);
+          pm = pk_absmax(pk_absmax(pk_absmax(pk_absmax(pm, raw[r].x), raw[r].y), raw[r].z), raw[r].w);
+        tile = pair_max_u32(halves_max(pm) << 16);
       }
-      if (kColwise) {
-        // column j of the lane is output row col + j, its block r0 / 16
+      // row r0's codes, scale byte and first draw counter; the rows below
+      // step by one output row each
+      const int64_t orow0 = (int64_t)t * sh.R + r0;
+      uint8_t* qr = q + orow0 * qstep + col / 2;
+      uint8_t* sr = sf + orow0 * sstep + col / 16;
+      uint64_t n = (uint64_t)(orow0 * nstep + col / 8) + offset;
+      const int nrows = (int)(sh.rows - r0 < kStripRows ? sh.rows - r0 : kStripRows);
+      // row r: this lane's half of block (col / 16), the partner holds the other half
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          float v[16];
+      for (int r = 0; r < kStripRows; ++r) {
+        float v[8];
 #pragma unroll
-          for (int r = 0; r < 16; ++r) v[r] = chunk_val(raw[r], j);
-          if (kRht) rht16(v, signs);
-          uint32_t bam = 0u;
-          if (k2D) {
-            bam = tile;
-          } else {
+        for (int j = 0; j < 8; ++j) v[j] = chunk_val(raw[r], j);
+        if (kRht) rht16_pair(v, signs, odd);
+        uint32_t bam;
+        if (k2D) {
+          bam = tile;
+        } else {
+          bam = 0u;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) bam = bam > fabs_bits(v[r]) ? bam : fabs_bits(v[r]);
-          }
-          const uint32_t sbyte = e4m3_rne_sat(rn32((double)__uint_as_float(bam) * r6));
-          const int64_t orow = (int64_t)t * sh.R + col + j;
-          uint32_t u[16];
-          if (kSr) {
-            const uint64_t n = (uint64_t)(orow * sh.C + r0) / 8 + offset;
-            uint32_t u0[8], u1[8];
-            draws8(n, pk, u0);
-            draws8(n + 1, pk, u1);
-#pragma unroll
-            for (int k = 0; k < 8; ++k) {
-              u[k] = u0[k];
-              u[k + 8] = u1[k];
-            }
-          }
-          uint32_t codes[2];
-          encode_vals<16, kSr>(v, table[sbyte], u, codes);
-          if (cin) {
-            *(u32x2*)(q + (orow * sh.C + r0) / 2) = u32x2{codes[0], codes[1]};
-            sf[orow * (sh.C / 16) + r0 / 16] = (uint8_t)sbyte;
-          }
+          for (int j = 0; j < 8; ++j) bam = bam > fabs_bits(v[j]) ? bam : fabs_bits(v[j]);
+          bam = pair_max_u32(bam);
         }
-      } else {
-        // row r: this lane's half of block (col / 16), the partner holds the other half
-#pragma unroll
-        for (int r = 0; r < kStripRows; ++r) {
-          float v[8];
-#pragma unroll
-          for (int j = 0; j < 8; ++j) v[j] = chunk_val(raw[r], j);
-          if (kRht) rht16_pair(v, signs, odd);
-          uint32_t bam;
-          if (k2D) {
-            bam = tile;
-          } else {
-            bam = 0u;
-#pragma unroll
-            for (int j = 0; j < 8; ++j) bam = bam > fabs_bits(v[j]) ? bam : fabs_bits(v[j]);
-            bam = pair_max_u32(bam);
-          }
-          const uint32_t sbyte = e4m3_rne_sat(rn32((double)__uint_as_float(bam) * r6));
-          const int64_t orow = (int64_t)t * sh.R + r0 + r;
-          uint32_t u[8];
-          if (kSr) draws8((uint64_t)(orow * sh.C + col) / 8 + offset, pk, u);
-          uint32_t codes[1];
-          encode_vals<8, kSr>(v, table[sbyte], u, codes);
-          if (cin && r0 + r < sh.rows) {
-            *(uint32_t*)(q + (orow * sh.C + col) / 2) = codes[0];
-            if (!odd) sf[orow * (sh.C / 16) + col / 16] = (uint8_t)sbyte;
-          }
+        const uint32_t sbyte = e4m3_rne_sat(rn32((double)__uint_as_float(bam) * r6));
+        uint32_t u[8];
+        if (kSr) draws8(n, pk, u);
+        uint32_t codes[1];
+        encode_vals<8, kSr>(v, table[sbyte], u, codes);
+        if (cin && r < nrows) {
+          *(uint32_t*)qr = codes[0];
+          if (!odd) *sr = (uint8_t)sbyte;
         }
+        qr += qstep;
+        sr += sstep;
+        n += nstep;
+        step_opaque(qr);
+        step_opaque(sr);
+        step_opaque(n);
       }
     }
   }
@@ -458,6 +444,8 @@ __global__ void __launch_bounds__(kVarThreads) var_encode_colwise_kernel(
         tile = pair_max_u32(halves_max(pk) << 16);
       }
       uint32_t sb[2] = {0u, 0u};                   // columns j's scale bytes
+      // draw counter of column col's block r0 / 16; each column is one output row on
+      uint64_t n = (uint64_t)(((int64_t)t * sh.R + col) * (sh.C / 8) + r0 / 8) + offset;
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         float v[16];
@@ -474,8 +462,6 @@ __global__ void __launch_bounds__(kVarThreads) var_encode_colwise_kernel(
         const uint32_t sbyte = e4m3_rne_sat(rn32((double)__uint_as_float(bam) * r6));
         uint32_t u[16];
         if (kSr) {
-          const int64_t orow = (int64_t)t * sh.R + col + j;
-          const uint64_t n = (uint64_t)(orow * sh.C + r0) / 8 + offset;
           uint32_t u0[8], u1[8];
           draws8(n, pk, u0);
           draws8(n + 1, pk, u1);
@@ -490,6 +476,8 @@ __global__ void __launch_bounds__(kVarThreads) var_encode_colwise_kernel(
         const int r = 8 * lane + j;                // output row within the band
         *(u32x2*)&cs.codes[r][2 * col_slot(r, k)] = u32x2{codes[0], codes[1]};
         sb[j / 4] |= sbyte << (8 * (j % 4));
+        n += (uint64_t)(sh.C / 8);
+        step_opaque(n);
       }
       *(u32x2*)&cs.scales[k][8 * lane] = u32x2{sb[0], sb[1]};
     }
@@ -548,8 +536,8 @@ void launch_encode(dim3 grid, hipStream_t s, const uint16_t* x, const VarShape& 
     var_encode_colwise_kernel<k2D, kRht, kSr><<<grid, kVarThreads, 0, s>>>(x, sh, signs, seed, offset, partial,
                                                                            (int)grid.x, q, sf, g);
   else
-    var_encode_kernel<false, k2D, kRht, kSr><<<grid, kVarThreads, 0, s>>>(x, sh, signs, seed, offset, partial,
-                                                                          (int)grid.x, q, sf, g);
+    var_encode_kernel<k2D, kRht, kSr><<<grid, kVarThreads, 0, s>>>(x, sh, signs, seed, offset, partial,
+                                                                   (int)grid.x, q, sf, g);
 }
 
 }  // namespace
