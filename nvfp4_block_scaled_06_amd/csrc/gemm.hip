@@ -499,6 +499,32 @@ __device__ __forceinline__ void gemm_tile_dma8(const uint8_t* __restrict__ aq, c
     iteration(kt + 2, std::integral_constant<int, 2>());
     iteration(kt + 3, std::integral_constant<int, 3>());
   }
+  // Epilogue.  C layout of the 32 x 32 MFMA: lane l, element e is row
+  // 8 (e / 4) + 4 (l / 32) + e % 4, column l % 32.
+  if (m0 + GTM <= m_end && n0 + GTN <= n_end && ldc <= (1 << 20)) {
+    // Whole tile: a buffer resource from the tile's first element and 32-bit
+    // offsets (256 rows of at most 2^20 floats stay below 2^30 bytes).  Each
+    // accumulator's row offset is uniform, so the only per-element vector
+    // work is the gA * gB product; with 64-bit addresses and per-element
+    // bounds checks the epilogue ran about 900 vector instructions per wave.
+    // Each store writes two whole 128-byte lines of C, which is written once:
+    // non-temporal.
+    const int ld = (int)ldc;
+    const __amdgpu_buffer_rsrc_t cr =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(C + m0 * ldc + n0), 0, GTM * ld * 4, kBufferWord3);
+    const int vo = ((wm * 128 + 4 * (lane >> 5)) * ld + wn * 64 + (lane & 31)) * 4;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int so = (i * 32 + 8 * (e >> 2) + (e & 3)) * ld * 4;
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[i][j][e] * gab), cr, vo + j * 128, so,
+                                                kStreamLoad);
+      }
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll

@@ -488,9 +488,28 @@ __global__ void __launch_bounds__(MThreads8) mx_gemm_dma8_kernel(const uint8_t* 
     __syncthreads();
   }
   // epilogue: rows wm * 128 + ..., columns wn * 64 + ...
+  if (m0 + MTM <= M && n0 + MTN <= N && N <= (1 << 20)) {
+    // Whole tile: a buffer resource from the tile's first element, 32-bit
+    // offsets (256 rows of at most 2^20 floats stay below 2^30 bytes) and
+    // uniform row offsets; each store writes two whole 128-byte lines of C,
+    // which is written once: non-temporal.
+    const int ld = (int)N;
+    const __amdgpu_buffer_rsrc_t cr =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(C + m0 * N + n0), 0, MTM * ld * 4, kBufferWord3);
+    const int vo = ((wm * 128 + 4 * (lane >> 5)) * ld + wn * 64 + (lane & 31)) * 4;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int so = (i * 32 + 8 * (e >> 2) + (e & 3)) * ld * 4;
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[i][j][e]), cr, vo + j * 128, so, kStreamLoad);
+      }
+    return;
+  }
   float* Cw = C + (m0 + wm * 128 + 4 * (lane >> 5)) * N + n0 + wn * 64 + (lane & 31);
   const int64_t rlim = M - (m0 + wm * 128 + 4 * (lane >> 5)), clim = N - (n0 + wn * 64 + (lane & 31));
-  const bool whole = m0 + MTM <= M && n0 + MTN <= N;
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -498,7 +517,7 @@ __global__ void __launch_bounds__(MThreads8) mx_gemm_dma8_kernel(const uint8_t* 
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int r = i * 32 + 8 * (e >> 2) + (e & 3), cc = j * 32;
-        if (whole || (r < rlim && cc < clim)) Cw[r * N + cc] = acc[i][j][e];
+        if (r < rlim && cc < clim) Cw[r * N + cc] = acc[i][j][e];
       }
 }
 
