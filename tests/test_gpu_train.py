@@ -7,7 +7,7 @@ import torch
 
 import oracle
 import synth
-from gpu_util import Guarded, bits, np_
+from gpu_util import Guarded, bits, from_bits, np_
 
 pytestmark = pytest.mark.gpu
 
@@ -123,6 +123,49 @@ def test_sr_seed_and_offset_change_the_draws():
     d = nv.quantize_ex(x, nv.VAR_SR, seed=1)[0]
     torch.cuda.synchronize()
     assert torch.equal(a, d) and not torch.equal(a, b) and not torch.equal(a, c)
+
+
+def _every_magnitude_blocks(reps, seed):
+    """bf16 bit patterns [reps + 1][cols]: row 0 holds 2688 in a block of its
+    own, so the tensor scale is exactly 1; every other block holds 6.0 and 15
+    of the finite bf16 magnitudes in [0, 6] (all of them across a row), with
+    random signs, so its E4M3 scale is exactly 1 and each value's quotient is
+    the value itself."""
+    mags = np.arange(0, 0x40C1, dtype=np.uint16)                  # +0 .. 6.0, every finite bf16
+    nblk = -(-mags.size // 15)
+    body = np.zeros((nblk, 16), dtype=np.uint16)
+    body[:, 0] = 0x40C0                                           # 6.0
+    flat = np.zeros(nblk * 15, dtype=np.uint16)
+    flat[:mags.size] = mags
+    body[:, 1:] = flat.reshape(nblk, 15)
+    cols = 16 * (nblk + 1)
+    rng = np.random.default_rng(seed)
+    x = np.zeros((reps + 1, cols), dtype=np.uint16)
+    x[0, 0] = 0x4528                                              # 2688
+    for r in range(1, reps + 1):
+        rows = body[rng.permutation(nblk)].reshape(-1)
+        x[r, 16:] = rows | (rng.integers(0, 2, rows.size, dtype=np.uint16) << 15)
+    return x
+
+
+@pytest.mark.parametrize("variant", [nv.VAR_SR, nv.VAR_COLWISE | nv.VAR_SR])
+def test_sr_decision_every_bf16_magnitude(variant):
+    """Stochastic rounding of every finite bf16 magnitude up to 6 as the
+    quotient itself (tensor and block scales exactly 1), 64 draws each: all
+    three regimes of the rule (below 0.5, [0.5, 1), the binades from 1), the
+    grid points themselves, and ties between the draw and the fraction
+    (draws that are multiples of 1024 against 8-bit mantissas); every byte
+    against the oracle."""
+    if variant & nv.VAR_COLWISE:                                  # blocks run down the columns
+        xb = np.ascontiguousarray(_every_magnitude_blocks(63, 2024).T)
+    else:
+        xb = _every_magnitude_blocks(64, 2024)
+    x = from_bits(xb)
+    print("case: SR every bf16 magnitude, variant", variant, tuple(x.shape), flush=True)
+    _check(x, variant, signs=0, seed=0x5EED, offset=3)
+    q, sf, g = nv.quantize_ex(x, variant, seed=0x5EED, offset=3)
+    torch.cuda.synchronize()
+    assert float(np_(g).reshape(-1)[0]) == 1.0
 
 
 def test_outputs_stay_in_bounds():
