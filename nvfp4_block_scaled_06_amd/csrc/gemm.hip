@@ -416,17 +416,21 @@ __device__ __forceinline__ void gemm_tile_dma8(const uint8_t* __restrict__ aq, c
   u32x4 s_cur = load_scale_group(X, row, K, 0), s_nxt = load_scale_group(X, row, K, 1);
   _Float16* const x0 = isb ? &sm.bf[0][row][0] : &sm.af[0][row][0];
   _Float16* const x1 = isb ? &sm.bf[1][row][0] : &sm.af[1][row][0];
+  // step 0's codes straight into registers and step 1's into the raw buffer,
+  // both in flight at once (one memory round trip before the loop, not two)
   RowRaw rr;
-  dma_codes8(X, wave, lane, 0, sm.raw);
+  {
+    const uint32_t qo = (uint32_t)row * X.qrow;
+    rr.c01 = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(X.q, (int)qo, 0, 0));
+    rr.c23 = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(X.q, (int)(qo + 16), 0, 0));
+  }
+  dma_codes8(X, wave, lane, GTK, sm.raw);
   wait_vm0();
-  read_codes(sm.raw, tid, rr);
   rr.s = s_cur.x;
   deq_block_to_lds<0>(rr, x0);
   deq_block_to_lds<1>(rr, x0);
   deq_block_to_lds<2>(rr, x0);
   deq_block_to_lds<3>(rr, x0);
-  dma_codes8(X, wave, lane, GTK, sm.raw);          // after this wave's reads of step 0 (used above)
-  wait_vm0();
   read_codes(sm.raw, tid, rr);
   __syncthreads();                                 // tile 0 complete
   const int arow = wm * 128 + (lane & 31), brow = wn * 64 + (lane & 31), kof = 8 * (lane >> 5);
