@@ -309,6 +309,19 @@ def run_extras(nv, synth, torch, which):
             for c, (k, v) in enumerate(chunks):
                 cache.append(c * C, k, v)
         ma = timed(torch, appends, 5, flush, warm=1)
+        side = [torch.cuda.Stream(), torch.cuda.Stream()]       # default priority
+
+        def appends_two_streams():
+            # consecutive appends write disjoint token ranges: alternate two
+            # streams so one launch's ramp overlaps the other's tail
+            main = torch.cuda.current_stream()
+            for sd in side:
+                sd.wait_stream(main)
+            for c, (k, v) in enumerate(chunks):
+                cache.append(c * C, k, v, stream=side[c & 1])
+            for sd in side:
+                main.wait_stream(sd)
+        ma2 = timed(torch, appends_two_streams, 5, flush, warm=1)
         mqk = timed(torch, lambda: cache.decode_qk(qv, T, out=logits), 20, flush)
         att = torch.empty((L, 4 * H, D), dtype=torch.float32, device="cuda")
         aws = torch.empty(max(cache.attention_workspace_bytes(4 * H, T), 16), dtype=torch.uint8, device="cuda")
@@ -326,6 +339,8 @@ def run_extras(nv, synth, torch, which):
         rd_bytes = 2 * (rvals // 2 + rvals // 16) + 2 * rvals * 2                        # codes + scales in, bf16 out
         rows["kv_32x8x128_131072"] = {
             "append_512x256": {"ms": ma, "ms_per_chunk": ma / (T // C), **roof(app_bytes, ma, HBM_PEAK_GBS, "GB/s")},
+            "append_512x256_two_streams": {"ms": ma2, "ms_per_chunk": ma2 / (T // C),
+                                           **roof(app_bytes, ma2, HBM_PEAK_GBS, "GB/s")},
             "decode_qk_32q": {"ms": mqk, **roof(qk_bytes, mqk, HBM_PEAK_GBS, "GB/s")},
             "decode_attention_32q": {"ms": matt, **roof(att_bytes, matt, HBM_PEAK_GBS, "GB/s")},
             "read_4_layers_all_tokens": {"ms": mrd, **roof(rd_bytes, mrd, HBM_PEAK_GBS, "GB/s")},

@@ -273,7 +273,10 @@ class KVCache:
     def nbytes(self):
         return int(_lib().nvfp4_kv_bytes(ctypes.byref(self.desc)))
 
-    def append(self, start, k_new, v_new):
+    def append(self, start, k_new, v_new, stream=None):
+        """Encodes tokens [start, start + n) into the cache on `stream` (a
+        torch.cuda.Stream; default: the current stream).  Appends of disjoint
+        token ranges may run on different streams at once."""
         _need(k_new, torch.bfloat16, "k_new")
         _need(v_new, torch.bfloat16, "v_new")
         if k_new.dim() != 4:
@@ -281,8 +284,9 @@ class KVCache:
         n = k_new.shape[1]
         _shape(k_new, (self.layers, n, self.kv_heads, self.head_dim), "k_new")
         _shape(v_new, (self.layers, n, self.kv_heads, self.head_dim), "v_new")
+        st = _stream(k_new.device) if stream is None else ctypes.c_void_p(stream.cuda_stream)
         _check("nvfp4_kv_append", _lib().nvfp4_kv_append(
-            ctypes.byref(self.desc), start, n, _ptr(k_new), _ptr(v_new), _stream(k_new.device)))
+            ctypes.byref(self.desc), start, n, _ptr(k_new), _ptr(v_new), st))
 
     def read(self, layer0, nlayers, t0, n, k_out=None, v_out=None, want_k=True, want_v=True):
         shp = (nlayers, self.kv_heads, n, self.head_dim)

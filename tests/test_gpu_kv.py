@@ -71,6 +71,36 @@ def test_append_read_qk_small(D, grp):
         assert err <= QK_TOL, f"n={n}: rel Frobenius {err:.3e}"
 
 
+def test_append_on_two_streams():
+    """Consecutive 256-token appends alternating between two streams (they
+    write disjoint token ranges, so they may run at once), joined at the end:
+    every cache byte against the oracle."""
+    print("case: kv append on two streams", flush=True)
+    L, H, D, cap, C = 3, 2, 128, 16 * 256, 256
+    cache, kg, vg = _cache(L, H, D, cap, 77)
+    gen = torch.Generator().manual_seed(77)
+    ks, vs, chunks = [], [], []
+    for c in range(cap // C):
+        k = (torch.randn((L, C, H, D), generator=gen) * 2).to(torch.bfloat16)
+        v = torch.randn((L, C, H, D), generator=gen).to(torch.bfloat16)
+        chunks.append((k.cuda(), v.cuda()))
+        ks.append(bits(k))
+        vs.append(bits(v))
+    side = [torch.cuda.Stream(), torch.cuda.Stream()]
+    main = torch.cuda.current_stream()
+    for s in side:
+        s.wait_stream(main)
+    for c, (k, v) in enumerate(chunks):
+        cache.append(c * C, k, v, stream=side[c % 2])
+    for s in side:
+        main.wait_stream(s)
+    torch.cuda.synchronize()
+    okq, oks = oracle.kv_encode(np.concatenate(ks, axis=1), kg)
+    ovq, ovs = oracle.kv_encode(np.concatenate(vs, axis=1), vg)
+    assert np.array_equal(np_(cache.k), okq) and np.array_equal(np_(cache.k_sf), oks)
+    assert np.array_equal(np_(cache.v), ovq) and np.array_equal(np_(cache.v_sf), ovs)
+
+
 def test_append_read_non_pow2_head_dim():
     """head_dim 48: three blocks per row (the non-power-of-two append path);
     the decode sweep reports the documented ENOTSUP for it."""
