@@ -186,7 +186,9 @@ size_t nvfp4_kv_bytes(const nvfp4_kv_cache* cache);
 
 /* Append n tokens at positions [start, start+n).  k_new, v_new:
  * [layers][n][kv_heads][head_dim] bf16.  EINVAL if start < 0 or
- * start + n > capacity.  The caller tracks the cache length. */
+ * start + n > capacity.  The caller tracks the cache length.  An append
+ * writes only the codes and scales of its own token range, so appends of
+ * disjoint ranges may run concurrently on different streams. */
 nvfp4_status nvfp4_kv_append(const nvfp4_kv_cache* cache, int64_t start, int64_t n,
                              const uint16_t* k_new, const uint16_t* v_new, void* stream);
 
