@@ -796,6 +796,16 @@ __device__ __forceinline__ void r2_step(const u32x4* __restrict__ x, int t, int 
 // the set piece by piece and reloads it.  The stage load of piece p then has
 // 3 + 8 * 2 + 15 = 34 younger operations when it is moved, and the poll
 // loads 32 at the end of the step.
+//
+// Staged scale bytes (kS, every 8 x 8 block whole): a strip's tile byte
+// belongs to 8 output rows, one per column, and a wave's 8 strip rows give 8
+// consecutive bytes of each.  Written directly that is 64 runs of 8 bytes
+// per wave and step.  Instead each wave writes its bytes into an LDS tile of
+// the workgroup's 64 output rows x 8 blocks x 8 bytes, and after the next
+// step's barrier every thread stores one 8-byte run (the 8 blocks of a
+// workgroup run down the columns, so a row's runs are adjacent): one store
+// per thread instead of 8, 64-byte runs per row.  Counts per step then: 3 +
+// 1 + 8 + 15 = 27 younger operations at a move, 1 + 8 + 16 = 25 at the poll.
 template <int p, int kWait>
 __device__ __forceinline__ void r2t_move(u32x4 (&cur)[kR2Per], uint32_t& m, __amdgpu_buffer_rsrc_t rx, int voff,
                                          int pstride, uint32_t b0, uint32_t b1, lds_void_t* stage_w) {
@@ -820,7 +830,7 @@ __device__ __forceinline__ uint32_t r2t_word(const u32x4& v) {
   return j == 0 ? v.x : j == 1 ? v.y : j == 2 ? v.z : v.w;
 }
 
-template <int j>
+template <int j, bool kS>
 __device__ __forceinline__ void r2t_column(const u32x4 (&cur)[kR2Per], double rd, uint32_t sbyte,
                                            __amdgpu_buffer_rsrc_t rq, __amdgpu_buffer_rsrc_t rsf, int qoff, int soff,
                                            int qstride, int sstride) {
@@ -834,46 +844,73 @@ __device__ __forceinline__ void r2t_column(const u32x4 (&cur)[kR2Per], double rd
   const uint32_t c0 = encode_half(u32x4{col[0], col[1], col[2], col[3]}, rd);
   const uint32_t c1 = encode_half(u32x4{col[4], col[5], col[6], col[7]}, rd);
   __builtin_amdgcn_raw_buffer_store_b64(u32x2{c0, c1}, rq, qoff, j * qstride, 0);
-  __builtin_amdgcn_raw_buffer_store_b8((uint8_t)sbyte, rsf, soff, j * sstride, 0);
+  if (!kS) __builtin_amdgcn_raw_buffer_store_b8((uint8_t)sbyte, rsf, soff, j * sstride, 0);
   __builtin_amdgcn_sched_barrier(0);                   // one column's temporaries at a time
 }
-template <int... J>
+template <bool kS, int... J>
 __device__ __forceinline__ void r2t_columns(std::integer_sequence<int, J...>, const u32x4 (&cur)[kR2Per], double rd,
                                             uint32_t sbyte, __amdgpu_buffer_rsrc_t rq, __amdgpu_buffer_rsrc_t rsf,
                                             int qoff, int soff, int qstride, int sstride) {
-  (r2t_column<J>(cur, rd, sbyte, rq, rsf, qoff, soff, qstride, sstride), ...);
+  (r2t_column<J, kS>(cur, rd, sbyte, rq, rsf, qoff, soff, qstride, sstride), ...);
 }
 
+// Staged scale bytes: tile bytes at stile[buf][wave][row][k], row = 8 c + j
+// the output row within the workgroup's 64, k the strip row within the block.
+constexpr int kSTileBytes = 8 * 64 * 8;                // one buffer
+
+// Thread T stores the 8 bytes of output row T / 8 from block T % 8 of
+// tensor t's tile (buffer t & 1) at offset fso (past the extent when the
+// block is outside the tensor); t < 0 stores nothing (zero extent).
+__device__ __forceinline__ void r2t_flush_scales(const uint8_t* stile, int t, int batch, int64_t hb,
+                                                 uint8_t* __restrict__ sf, int fso) {
+  const int T = (int)threadIdx.x;
+  const u32x2 v = *(const u32x2*)(stile + (t & 1) * kSTileBytes + ((T & 7) * 64 + (T >> 3)) * 8);
+  const __amdgpu_buffer_rsrc_t rs = tensor_rsrc(sf, t < 0 ? batch : t, batch, hb / 2);
+  __builtin_amdgcn_raw_buffer_store_b64(v, rs, fso, 0, 0);
+}
+
+template <bool kS>
 __device__ __forceinline__ void r2t_step(const u32x4* __restrict__ x, int t, int batch, int64_t hb, int voff, int qoff,
                                          int soff, int qstride, int sstride, int pstride, u32x4 (&cur)[kR2Per],
                                          uint32_t& tile, uint32_t b0, uint32_t b1, lds_void_t* stage_w, uint32_t* ws,
                                          int G, float* __restrict__ gout, uint32_t* __restrict__ q,
-                                         uint8_t* __restrict__ sf, Reg8Shared& sh) {
+                                         uint8_t* __restrict__ sf, Reg8Shared& sh, uint8_t* stile, int fso) {
   lds_barrier();                                       // t's table is ready; the maxima of t+2 were reduced
   const bool pub = t >= 1 && t + 2 < batch;
   r8_exchange_ops(ws, G, pub ? t + 2 : -1, pub ? r8_red_max(sh.red[(t - 1) & 1]) : 0u, t + 1, t + 1 < batch, sh);
   const double r6 = sh.r6[t & 1];
   const uint32_t sbyte = block_scale_byte(tile, r6);
   const double rd = sh.table[t & 1][sbyte];
+  if (kS) {
+    r2t_flush_scales(stile, t - 1, batch, hb, sf, fso);   // tensor t-1's tile (the barrier above)
+    const int lane = (int)threadIdx.x & 63;
+    uint8_t* dst = stile + (t & 1) * kSTileBytes + (wave_id() * 64 + 8 * (lane & 7)) * 8 + (lane >> 3);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) dst[8 * j] = (uint8_t)sbyte;
+    __builtin_amdgcn_sched_barrier(0);
+  }
   const __amdgpu_buffer_rsrc_t rq = tensor_rsrc(q, t, batch, hb * 4);
   const __amdgpu_buffer_rsrc_t rsf = tensor_rsrc(sf, t, batch, hb / 2);
   const __amdgpu_buffer_rsrc_t rx = tensor_rsrc(x, t + 4, batch, hb * 16);   // extent zero past the batch
-  r2t_columns(std::make_integer_sequence<int, 8>{}, cur, rd, sbyte, rq, rsf, qoff, soff, qstride, sstride);
+  r2t_columns<kS>(std::make_integer_sequence<int, 8>{}, cur, rd, sbyte, rq, rsf, qoff, soff, qstride, sstride);
   uint32_t m = 0;
-  r2t_moves<kR2Per + 18>(std::make_integer_sequence<int, kR2Per>{}, cur, m, rx, voff, pstride, b0, b1, stage_w);
+  r2t_moves<kS ? kR2Per + 11 : kR2Per + 18>(std::make_integer_sequence<int, kR2Per>{}, cur, m, rx, voff, pstride, b0,
+                                            b1, stage_w);
   tile = pair_max(m);                                  // tensor t+3, now in this set
   sh.red[t & 1][wave_id()] = wave_max_u32(m);          // wave-uniform value and address
-  wait_vmcnt<2 * kR2Per>();                            // the poll loads of this step have landed
+  wait_vmcnt<kS ? 2 * kR2Per - 7 : 2 * kR2Per>();      // the poll loads of this step have landed
   if (wave_id() == kR8Waves - 1 && t + 1 < batch) r8_table(sh, t + 1, r8_gather(ws, t + 1, G, sh), gout);
 }
 
-template <bool kT>
+template <bool kT, bool kS>
 __global__ void __launch_bounds__(kR8Data) fused_2d_reg_kernel(const u32x4* __restrict__ x, int batch, int64_t hb,
                                                                int spr, int srows, uint32_t* ws,
                                                                float* __restrict__ gout, uint32_t* __restrict__ q,
                                                                uint8_t* __restrict__ sf) {
+  static_assert(kT || !kS, "staged scale bytes are a COLWISE layout");
   __shared__ Reg8Shared sh;
   __shared__ __attribute__((aligned(16))) u32x4 L[kR2Per][kR8Data];
+  __shared__ __attribute__((aligned(16))) uint8_t stile[kS ? 2 * kSTileBytes : 16];
   const int G = gridDim.x;
   const int lane = (int)threadIdx.x & 63, wave = wave_id();
   // strip of this thread; strips past the tensor get offsets past every
@@ -882,7 +919,7 @@ __global__ void __launch_bounds__(kR8Data) fused_2d_reg_kernel(const u32x4* __re
   // 8 w + v of 8 x 8 strips (128 rows x 64 columns; blocks run down the
   // columns), lane l the strip (8 bR + l / 8, 8 bC + l % 8).
   const int pstride = spr * 16;
-  int voff, qoff, soff, qstride, sstride;
+  int voff, qoff, soff, qstride, sstride, fso = 0;
   if (kT) {
     const int nbr = (srows + 7) / 8, nbc = (spr + 7) / 8;
     const int blk = (int)blockIdx.x * kR8Waves + wave;
@@ -895,6 +932,11 @@ __global__ void __launch_bounds__(kR8Data) fused_2d_reg_kernel(const u32x4* __re
     qstride = rows / 2;
     soff = in ? 8 * c * (rows / 16) + r : kOnOutside;
     sstride = rows / 16;
+    if (kS) {                                          // this thread's 8-byte run of the staged scales
+      const int sb = (int)blockIdx.x * kR8Waves + ((int)threadIdx.x & 7);
+      const int sbr = sb % nbr, sbc = sb / nbr;
+      fso = sbc < nbc ? (64 * sbc + ((int)threadIdx.x >> 3)) * sstride + 8 * sbr : (int)0x80000000u;
+    }
   } else {
     const int st = (int)blockIdx.x * kR8Data + (int)threadIdx.x;
     const int r = st / spr, c = st - r * spr;
@@ -947,8 +989,8 @@ __global__ void __launch_bounds__(kR8Data) fused_2d_reg_kernel(const u32x4* __re
   }
   auto step = [&](int tt, u32x4 (&cur)[kR2Per], uint32_t& tile) {
     if (kT)
-      r2t_step(x, tt, batch, hb, voff, qoff, soff, qstride, sstride, pstride, cur, tile, b0, b1, stage_w, ws, G, gout,
-               q, sf, sh);
+      r2t_step<kS>(x, tt, batch, hb, voff, qoff, soff, qstride, sstride, pstride, cur, tile, b0, b1, stage_w, ws, G,
+                   gout, q, sf, sh, stile, fso);
     else
       r2_step(x, tt, batch, hb, voff, qoff, soff, qstride, sstride, pstride, cur, tile, b0, b1, stage_w, ws, G, gout, q,
               sf, sh);
@@ -970,6 +1012,10 @@ __global__ void __launch_bounds__(kR8Data) fused_2d_reg_kernel(const u32x4* __re
   }
   if (t < batch) step(t, a, ta);
   if (t + 1 < batch) step(t + 1, b, tb);
+  if (kS) {
+    lds_barrier();                                     // the last tensor's scale tile
+    r2t_flush_scales(stile, batch - 1, batch, hb, sf, fso);
+  }
   wait_vmcnt<0>();                                     // no stage or poll load still writing LDS at exit
   if (wave != kR8Waves - 1) return;
   // the last workgroup out restores the slots and the counter to zero; every
@@ -1393,7 +1439,11 @@ nvfp4_status quantize_2d_onchip(const uint16_t* x, int64_t batch, int64_t rows, 
   uint32_t* wsa = (uint32_t*)ws;
   uint32_t* qa = (uint32_t*)q;
   void* args[] = {&xa, &bt, (void*)&hb, &spri, &srowsi, &wsa, &g, &qa, &sf};
-  const void* fn = colwise ? (const void*)fused_2d_reg_kernel<true> : (const void*)fused_2d_reg_kernel<false>;
+  // COLWISE with every 8 x 8 block whole stages its scale bytes
+  const bool staged = colwise && srows % 8 == 0 && spr % 8 == 0;
+  const void* fn = staged ? (const void*)fused_2d_reg_kernel<true, true>
+                   : colwise ? (const void*)fused_2d_reg_kernel<true, false>
+                             : (const void*)fused_2d_reg_kernel<false, false>;
   return launch_resident(fn, (int)G, kR8Data, args, s);
 }
 

@@ -58,14 +58,18 @@ def test_colwise_variants_over_several_row_blocks(variant, shape):
 
 
 @pytest.mark.parametrize("variant", [2, 3])
-@pytest.mark.parametrize("shape", [(5, 48, 1040), (2, 512, 7168), (1, 16, 16), (7, 32, 4096), (2, 400, 80)])
+@pytest.mark.parametrize("shape", [(5, 48, 1040), (2, 512, 7168), (1, 16, 16), (7, 32, 4096), (2, 400, 80),
+                                   (3, 128, 512), (2, 256, 1024), (1, 128, 192)])
 def test_2d_single_launch_shapes(shape, variant):
     """2D (row-major or transposed outputs) runs as one launch
     when a tensor's 16 x 8 strips fit on the chip: strip rows that cross
     workgroup boundaries (cols = 1040), 64 workgroups per tensor, a single
     tile, a batch of 7, and strip blocks cut by the tensor's edge in both
     directions (400 x 80: 25 strip rows, 10 strip columns); per-tensor
-    magnitudes span 60 binades."""
+    magnitudes span 60 binades.  The transposed layout stages its scale
+    bytes through LDS when every 8 x 8 block of strips is whole: a
+    workgroup's blocks in 8 column bands (128 x 512), alternating between two
+    bands (256 x 1024), and 3 blocks in the last workgroup's 8 (128 x 192)."""
     _check(_x(shape, sum(shape) * 5 + variant, wide=True), variant)
 
 
