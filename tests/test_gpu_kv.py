@@ -35,7 +35,7 @@ def _oracle_cache(cache, k, v, kg, vg):
 
 
 @pytest.mark.parametrize("D,grp", [(128, 4), (64, 2), (32, 1), (256, 8), (16, 4), (128, 16), (64, 3), (256, 5),
-                                   (128, 1)])
+                                   (128, 1), (128, 8), (64, 4), (64, 8), (128, 2)])
 def test_append_read_qk_small(D, grp):
     print("case: kv small D", D, "grp", grp, flush=True)
     L, H, cap = 3, 2, 300
