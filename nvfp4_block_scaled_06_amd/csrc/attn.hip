@@ -252,7 +252,7 @@ __global__ void __launch_bounds__(kAttnThreads) kv_attn_split_kernel(nvfp4_kv_ca
 //    (heads x 32 tokens), B = V (32 tokens x 16 columns).  Token slot s of
 //    lane l is token 16 (s / 4) + 4 (l / 16) + s % 4, so P comes straight
 //    from the lane's own logits; P is split into f16 hi + lo parts (two
-//    MFMAs) so it keeps about 22 bits.  V is decoded exactly to f16 (E2M1 *
+//    MFMAs) so it keeps about 21 bits.  V is decoded exactly to f16 (E2M1 *
 //    s), written token-major to LDS and read back per column.
 // The V tensor scale is applied once to the accumulated output.
 constexpr int kMChunk = 32;                              // tokens per wave step
@@ -276,7 +276,7 @@ struct AttnMfmaSmem {
 template <int D>
 struct AttnRaw {
   uint32_t kc[2][D / 32];                                // K codes of the lane's quarter, tiles 0 and 1
-  uint32_t ks[2][D / 64];                                // K scale bytes of the token (D / 16 bytes)
+  uint32_t ks[2];                                        // the D / 64 K scale bytes of the lane's quarter
   uint32_t vc[D / 16];                                   // V codes of the lane's half token
   uint32_t vs[D / 128 > 0 ? D / 128 : 1];                // V scale bytes of the half token (D / 32 bytes)
 };
@@ -314,10 +314,14 @@ __device__ __forceinline__ void attn_load(const __amdgpu_buffer_rsrc_t (&r)[4], 
     const int64_t u = c0 + 16 * T + (lane & 15);
     const bool in = u < cnt;
     load_words<D / 32>(r[0], in ? (uint32_t)u * (D / 2) + qd * (D / 8) : kAttnOutside, raw.kc[T]);
-    if (D / 64 == 1)
-      raw.ks[T][0] = __builtin_amdgcn_raw_buffer_load_b32(r[1], (int)(in ? (uint32_t)u * (D / 16) : kAttnOutside), 0, kStreamLoad);
+    // the quarter's values [qd D/4, (qd+1) D/4) span blocks qd D/64 .. (qd+1) D/64 - 1
+    const int so = (int)(in ? (uint32_t)u * (D / 16) + qd * (D / 64) : kAttnOutside);
+    if (D == 64)
+      raw.ks[T] = __builtin_amdgcn_raw_buffer_load_b8(r[1], so, 0, kStreamLoad);
+    else if (D == 128)
+      raw.ks[T] = __builtin_amdgcn_raw_buffer_load_b16(r[1], so, 0, kStreamLoad);
     else
-      load_words<D / 64>(r[1], in ? (uint32_t)u * (D / 16) : kAttnOutside, raw.ks[T]);
+      raw.ks[T] = __builtin_amdgcn_raw_buffer_load_b32(r[1], so, 0, kStreamLoad);
   }
   const int64_t u = c0 + (lane >> 1);
   const bool in = u < cnt;
@@ -429,7 +433,7 @@ __global__ void __launch_bounds__(kAttnThreads) kv_attn_mfma_kernel(nvfp4_kv_cac
       sacc[T] = f32x4v{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk) {
-        const float sk = e4m3_byte(cur.ks[T], (qd * (D / 4) + 8 * kk) / 16);
+        const float sk = __builtin_amdgcn_cvt_f32_fp8((int)(cur.ks[T] >> (8 * (kk / 2))), 0);   // block kk / 2 of the quarter
         sacc[T] = __builtin_amdgcn_mfma_f32_16x16x32_f16(dec8_f16(cur.kc[T][kk], sk), qb[kk], sacc[T], 0, 0, 0);
       }
     }
@@ -461,13 +465,12 @@ __global__ void __launch_bounds__(kAttnThreads) kv_attn_mfma_kernel(nvfp4_kv_cac
     const float alpha = mn == -INFINITY ? 1.0f : __expf(m - mn);
     m = mn;
     float p8[8];
-    float psum = 0.0f;
     const float mref = mn == -INFINITY ? 0.0f : mn;               // exp(-inf - mref) = 0 for masked tokens
 #pragma unroll
-    for (int s8 = 0; s8 < 8; ++s8) {
-      p8[s8] = __expf(sv8[s8] - mref);
-      psum += p8[s8];
-    }
+    for (int s8 = 0; s8 < 8; ++s8) p8[s8] = __expf(sv8[s8] - mref);
+    float psum = p8[0];
+#pragma unroll
+    for (int s8 = 1; s8 < 8; ++s8) psum += p8[s8];
     lsum = lsum * alpha + psum;
     if (__builtin_amdgcn_ballot_w64(hl < GRP && alpha != 1.0f)) {   // rescale the output rows (heads 4 qd + i)
 #pragma unroll
@@ -477,14 +480,20 @@ __global__ void __launch_bounds__(kAttnThreads) kv_attn_mfma_kernel(nvfp4_kv_cac
         for (int dt = 0; dt < DT; ++dt) o[dt][i] *= a;
       }
     }
-    // ---- P (head hl x token slots 8 qd .. 8 qd + 7) in f16 hi + lo
+    // ---- P (head hl x token slots 8 qd .. 8 qd + 7) in f16 hi + lo: hi is
+    // p with its low 13 mantissa bits cleared (exact in f16 for p >= 2^-14),
+    // lo = p - hi is exact in fp32 and rounds to f16 with error at most 2^-22 p.
+    // Rows of heads hl >= GRP (zero queries) hold finite values and feed only
+    // output rows that are never stored.
     h16x8 ph, pl;
 #pragma unroll
-    for (int s8 = 0; s8 < 8; ++s8) {
-      const float pv = hl < GRP ? p8[s8] : 0.0f;
-      const _Float16 hi = (_Float16)pv;
-      ph[s8] = hi;
-      pl[s8] = (_Float16)(pv - (float)hi);
+    for (int s8 = 0; s8 < 8; s8 += 2) {
+      const float h0 = __uint_as_float(__float_as_uint(p8[s8]) & 0xFFFFE000u);
+      const float h1 = __uint_as_float(__float_as_uint(p8[s8 + 1]) & 0xFFFFE000u);
+      ph[s8] = (_Float16)h0;
+      ph[s8 + 1] = (_Float16)h1;
+      pl[s8] = (_Float16)(p8[s8] - h0);
+      pl[s8 + 1] = (_Float16)(p8[s8 + 1] - h1);
     }
     wave_lds_sync();                                     // V chunk written
     // ---- PV: column tile dt, B[slot][column hl] = V[token(slot)][16 dt + hl].
