@@ -1102,6 +1102,19 @@ __device__ __forceinline__ uint32_t big_stage_max(std::integer_sequence<int, P..
   return m;
 }
 
+// Largest magnitude bits over a register set's pieces (pass 2 takes the
+// block maxima again as it encodes, so none are kept here).
+template <int kPer>
+__device__ __forceinline__ uint32_t big_set_max(const u32x4 (&R)[kPer]) {
+  uint32_t m = 0;
+#pragma unroll
+  for (int p = 0; p < kPer; ++p) {
+    const uint32_t h = half_absmax_bits(R[p]);
+    m = m > h ? m : h;
+  }
+  return m;
+}
+
 // Chunk held by register set s (0, 1, 2) after pass 1: the last
 // nreg = min(nc, 3) chunks in order.
 __device__ __forceinline__ int big_chunk(int s, int nc) {
@@ -1181,24 +1194,22 @@ __global__ void __launch_bounds__(kR8Data) fused_big_kernel(const u32x4* __restr
     const __amdgpu_buffer_rsrc_t rq = tensor_rsrc(q, t, batch, hb * 4);
     const __amdgpu_buffer_rsrc_t rsf = tensor_rsrc(sf, t, batch, hb / 2);
     u32x4 a[kPer], b[kPer], c[kPer];
-    BlockMax<kPer> am, bmx, cm;
     // ---- pass 1
     big_load_set<kPer>(a, rx, voff + big_chunk(0, nc) * cbytes);
     big_load_set<kPer>(b, nc >= 2 ? rx : none, voff + big_chunk(1, nc) * cbytes);
     big_load_set<kPer>(c, nc >= 3 ? rx : none, voff + big_chunk(2, nc) * cbytes);
     __builtin_amdgcn_sched_barrier(0);
     big_stage_issue<kPer>(nc >= 4 ? rx : none, stage_w, voff);   // chunk 0 (nc - 4 when nc = 4)
-    uint32_t m = 0;
+    // the register sets' maxima while the stage's first chunk streams in (its
+    // kPer loads are the youngest), not after the last load of pass 1 lands
+    wait_vmcnt<kPer>();
+    uint32_t m = max(max(big_set_max<kPer>(a), big_set_max<kPer>(b)), big_set_max<kPer>(c));
     for (int k = 0; k + 4 < nc; ++k)                    // chunks 0..nc-5 pass through; chunk nc-4 stays
       big_stage_chunk<kPer>(std::make_integer_sequence<int, kPer>{}, m, b0, b1, rx, stage_w, voff + (k + 1) * cbytes);
-    wait_vmcnt<0>();                                    // chunk nc-4 and the register sets have landed
+    wait_vmcnt<0>();                                    // chunk nc-4 has landed
     const uint32_t ms = big_stage_max<kPer>(std::make_integer_sequence<int, kPer>{}, b0, b1);
     m = m > ms ? m : ms;
-    const uint32_t ma = set_block_max<kPer>(a, am), mb = set_block_max<kPer>(b, bmx), mc = set_block_max<kPer>(c, cm);
-    const uint32_t mw = wave_max_u32(m);
-    uint32_t mall = ma > mb ? ma : mb;
-    mall = mall > mc ? mall : mc;
-    sh.red0[0][wave] = mall > mw ? mall : mw;
+    sh.red0[0][wave] = wave_max_u32(m);
     lds_barrier();                                      // every wave's maximum of tensor t
     // ---- exchange
     if (wave == kR8Waves - 1) {
