@@ -306,12 +306,12 @@ __device__ __forceinline__ void load_words(__amdgpu_buffer_rsrc_t r, uint32_t of
 constexpr uint32_t kAttnOutside = 0x80000000u;
 
 template <int D>
-__device__ __forceinline__ void attn_load(const __amdgpu_buffer_rsrc_t (&r)[4], int64_t c0, int64_t cnt, int lane,
+__device__ __forceinline__ void attn_load(const __amdgpu_buffer_rsrc_t (&r)[4], int c0, int cnt, int lane,
                                           AttnRaw<D>& raw) {
   const int qd = lane >> 4;
 #pragma unroll
   for (int T = 0; T < 2; ++T) {
-    const int64_t u = c0 + 16 * T + (lane & 15);
+    const int u = c0 + 16 * T + (lane & 15);
     const bool in = u < cnt;
     load_words<D / 32>(r[0], in ? (uint32_t)u * (D / 2) + qd * (D / 8) : kAttnOutside, raw.kc[T]);
     // the quarter's values [qd D/4, (qd+1) D/4) span blocks qd D/64 .. (qd+1) D/64 - 1
@@ -323,7 +323,7 @@ __device__ __forceinline__ void attn_load(const __amdgpu_buffer_rsrc_t (&r)[4], 
     else
       raw.ks[T] = __builtin_amdgcn_raw_buffer_load_b32(r[1], so, 0, kStreamLoad);
   }
-  const int64_t u = c0 + (lane >> 1);
+  const int u = c0 + (lane >> 1);
   const bool in = u < cnt;
   load_words<D / 16>(r[2], in ? (uint32_t)u * (D / 2) + (lane & 1) * (D / 4) : kAttnOutside, raw.vc);
   if (D == 64)
@@ -392,7 +392,10 @@ __global__ void __launch_bounds__(kAttnThreads) kv_attn_mfma_kernel(nvfp4_kv_cac
   qmax = max(qmax, (uint32_t)__shfl_xor((int)qmax, 32, 64));
   const int qe = (int)(qmax >> 7);                       // biased exponent of the head's largest |q|
   const int cq = qe == 0 ? 0 : std::min(std::max(141 - qe, -100), 100);
-  const float qs = __uint_as_float((uint32_t)(cq + 127) << 23);
+  // the sign of the softmax scale goes into q (exact), so the logits in
+  // MFMA units order like the scaled ones and the running max is taken on
+  // them directly
+  const float qs = __uint_as_float((uint32_t)(cq + 127) << 23 | (scale < 0.0f ? 0x80000000u : 0u));
   h16x8 qb[KK];
 #pragma unroll
   for (int kk = 0; kk < KK; ++kk) {
@@ -403,7 +406,9 @@ __global__ void __launch_bounds__(kAttnThreads) kv_attn_mfma_kernel(nvfp4_kv_cac
       qb[kk][2 * i + 1] = (_Float16)(bf16_hi(w[i]) * qs);
     }
   }
-  const float ks = c.k_g[l * H + h] * scale * __uint_as_float((uint32_t)(127 - cq) << 23);
+  // logit = ks * (MFMA sum); exp(logit - max) = exp2((sum - max sum) * kl)
+  const float ks = c.k_g[l * H + h] * fabsf(scale) * __uint_as_float((uint32_t)(127 - cq) << 23);
+  const float kl = fmaxf(ks * 1.44269504f, 1.17549435e-38f);   // > 0: masked tokens give -inf, not NaN
   const float gv = c.v_g[l * H + h];
   const int64_t row0 = ((int64_t)l * H + h) * c.capacity;
   const int64_t t0 = (int64_t)split * per_split;
@@ -421,11 +426,14 @@ __global__ void __launch_bounds__(kAttnThreads) kv_attn_mfma_kernel(nvfp4_kv_cac
   for (int dt = 0; dt < DT; ++dt) o[dt] = f32x4v{0.0f, 0.0f, 0.0f, 0.0f};
   _Float16(*vs)[D + 8] = sm.v[wave];
   AttnRaw<D> cur;
-  int64_t c0 = (int64_t)wave * kMChunk;
-  attn_load<D>(rs, c0, cnt, lane, cur);
-  for (; c0 < cnt; c0 += kAttnWaves * kMChunk) {
+  // token counts and offsets within a split are 32-bit: the host keeps
+  // n * head_dim / 2 below 2^30
+  const int cnt32 = (int)cnt;
+  int c0 = wave * kMChunk;
+  attn_load<D>(rs, c0, cnt32, lane, cur);
+  for (; c0 < cnt32; c0 += kAttnWaves * kMChunk) {
     AttnRaw<D> nxt;
-    attn_load<D>(rs, c0 + kAttnWaves * kMChunk, cnt, lane, nxt);
+    attn_load<D>(rs, c0 + kAttnWaves * kMChunk, cnt32, lane, nxt);
     // ---- QK: logits of head hl, tokens 16 T + 4 qd + i
     f32x4v sacc[2];
 #pragma unroll
@@ -446,12 +454,13 @@ __global__ void __launch_bounds__(kAttnThreads) kv_attn_mfma_kernel(nvfp4_kv_cac
         *(h16x8*)&vs[tk][hf * (D / 2) + 8 * w] = dec8_f16(cur.vc[w], sv);
       }
     }
-    // ---- online softmax for head hl over this chunk
+    // ---- online softmax for head hl over this chunk, in MFMA units (the
+    // running max m too); kl turns differences into base-2 exponents
     float sv8[8];
     float cmax = -INFINITY;
-    const int rem = (int)std::min<int64_t>(cnt - c0, kMChunk);     // tokens of the chunk inside the split
+    const int rem = std::min(cnt32 - c0, kMChunk);                 // tokens of the chunk inside the split
 #pragma unroll
-    for (int s8 = 0; s8 < 8; ++s8) sv8[s8] = sacc[s8 >> 2][s8 & 3] * ks;
+    for (int s8 = 0; s8 < 8; ++s8) sv8[s8] = sacc[s8 >> 2][s8 & 3];
     if (rem < kMChunk) {                                           // the split's last chunk
 #pragma unroll
       for (int s8 = 0; s8 < 8; ++s8)
@@ -462,12 +471,12 @@ __global__ void __launch_bounds__(kAttnThreads) kv_attn_mfma_kernel(nvfp4_kv_cac
     cmax = fmaxf(cmax, __shfl_xor(cmax, 16, 64));
     cmax = fmaxf(cmax, __shfl_xor(cmax, 32, 64));
     const float mn = fmaxf(m, cmax);
-    const float alpha = mn == -INFINITY ? 1.0f : __expf(m - mn);
+    const float alpha = mn == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f((m - mn) * kl);
     m = mn;
     float p8[8];
     const float mref = mn == -INFINITY ? 0.0f : mn;               // exp(-inf - mref) = 0 for masked tokens
 #pragma unroll
-    for (int s8 = 0; s8 < 8; ++s8) p8[s8] = __expf(sv8[s8] - mref);
+    for (int s8 = 0; s8 < 8; ++s8) p8[s8] = __builtin_amdgcn_exp2f((sv8[s8] - mref) * kl);
     float psum = p8[0];
 #pragma unroll
     for (int s8 = 1; s8 < 8; ++s8) psum += p8[s8];
@@ -519,7 +528,7 @@ __global__ void __launch_bounds__(kAttnThreads) kv_attn_mfma_kernel(nvfp4_kv_cac
   lsum += __shfl_xor(lsum, 32, 64);
   __syncthreads();                                       // every wave is done with its V buffer (st aliases it)
   if (lane < GRP) {
-    sm.st[wave][lane][0] = m;
+    sm.st[wave][lane][0] = m == -INFINITY ? m : m * ks;   // the max logit, for the merges
     sm.st[wave][lane][1] = lsum;
   }
 #pragma unroll
