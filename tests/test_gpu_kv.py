@@ -148,6 +148,32 @@ def test_decode_attention_small(D, grp):
         assert err <= QK_TOL, f"n={n}: rel Frobenius {err:.3e}"
 
 
+@pytest.mark.parametrize("D,grp", [(128, 4), (64, 2), (32, 2)])
+@pytest.mark.parametrize("scale_kind", ["negative", "zero", "large"])
+def test_decode_attention_scale_sign_and_size(D, grp, scale_kind):
+    """Softmax scales that are negative (the running max is then taken on
+    the negated logits), zero (uniform weights over the tokens) or large
+    (near one-hot weights), against the fp64 oracle, on the MFMA kernel
+    (head_dim 64, 128) and the VALU kernel (head_dim 32)."""
+    print("case: kv attention scale", scale_kind, "D", D, "grp", grp, flush=True)
+    L, H, cap = 2, 2, 333
+    cache, kg, vg = _cache(L, H, D, cap, 5 * D + grp)
+    gen = torch.Generator().manual_seed(13 * D + grp)
+    k = (torch.randn((L, cap, H, D), generator=gen) * 2).to(torch.bfloat16)
+    v = torch.randn((L, cap, H, D), generator=gen).to(torch.bfloat16)
+    cache.append(0, k.cuda(), v.cuda())
+    qv = torch.randn((L, H * grp, D), generator=gen).to(torch.bfloat16)
+    kq, ks, vq, vs = _oracle_cache(cache, k, v, kg, vg)
+    scale = {"negative": -1.0 / np.sqrt(D), "zero": 0.0, "large": 8.0}[scale_kind]
+    for n in (1, 200, 333):
+        out = cache.decode_attention(qv.cuda(), n, scale)
+        torch.cuda.synchronize()
+        want = oracle.decode_attention_f64(bits(qv), kq[:, :, :n], ks[:, :, :n], kg, vq[:, :, :n], vs[:, :, :n],
+                                           vg, scale)
+        err = rel_frobenius(np_(out), want)
+        assert err <= QK_TOL, f"n={n}: rel Frobenius {err:.3e}"
+
+
 @pytest.mark.parametrize("k", [-100, -20, 0, 30, 100])
 def test_decode_attention_query_magnitudes(k):
     """Queries scaled by 2^k (with the softmax scale taking 2^-k back) and a
